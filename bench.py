@@ -1,0 +1,193 @@
+"""Benchmark of one LatentMoE layer with MXFP4 expert weights on one GPU.
+
+A step is one pass of the whole layer (route -> permute -> gate/up + act ->
+down -> combine) over one batch of seeded synthetic tokens already resident
+in HBM. Prints one JSON line: whole-layer tokens/s, the dominant kernel's
+roofline fraction (from HIP events recorded on the launch stream inside the
+timed steps), and the oracle's CPU rate on a bounded token sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|...]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % of MFMA/HBM roofline, 896 experts top-16 MXFP4"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 matrix
+STAGES = ("route", "permute", "gate_up", "down", "combine")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--mode", type=int, default=0, help="GEMM schedule: 0 auto, 1 stream, 2 tiled")
+    ap.add_argument("--cpu-tokens", type=int, default=24,
+                    help="tokens the oracle CPU baseline evaluates (0 = skip)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes of the dominant kernel")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, A, U, out_bytes=2):
+    """Bytes and FLOPs the layer must move / compute (never the dense work it
+    avoids): touched experts' MXFP4 weights, tokens in and out, router weights
+    and the routing arrays; router GEMM plus 3 expert projections."""
+    T, d, E, k, I = cfg.T, cfg.d, cfg.E, cfg.k, cfg.I
+    mx = 0.5 + 1.0 / 32  # bytes per MXFP4 weight, codes + scales
+    layer_bytes = U * 3 * I * d * mx + T * d * 2 + E * d * 4 + T * d * out_bytes + T * k * 8
+    layer_flops = 2 * T * E * d + 6 * A * I * d
+    # the gate/up kernel: two [I, d] matrices per touched expert, the token
+    # rows it gathers, the bf16 activations it writes
+    gu_bytes = U * 2 * I * d * mx + T * d * 2 + A * I * 2
+    gu_flops = 4 * A * I * d
+    return layer_bytes, layer_flops, gu_bytes, gu_flops
+
+
+def cpu_baseline(inp, n_tokens):
+    """The oracle, as it stands, on `n_tokens` seeded tokens of the same
+    workload: router scores, top-k, softmax and every selected expert's FFN
+    and the weighted combine of each token. Single-threaded."""
+    import oracle
+    from tests.parity_util import host_weights
+
+    cfg = inp.cfg
+    rng = np.random.default_rng(1)
+    toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    xs = inp.x[torch.as_tensor(toks, device=inp.x.device)].cpu()
+    w_r = inp.w_router.cpu().numpy()
+    bias = None if inp.bias is None else inp.bias.cpu().numpy()
+    # the weights the sampled tokens need, copied to the host beforehand
+    lg_probe = oracle.router_logits(xs, w_r, bias)
+    idx_probe, _ = oracle.topk_softmax(lg_probe, cfg.k)
+    loc = idx_probe - cfg.expert_begin
+    used = np.unique(loc[(loc >= 0) & (loc < cfg.num_local)])
+    wts = host_weights(inp.weights, used)
+    remap = np.full(cfg.num_local, -1, np.int64)
+    remap[used] = np.arange(len(used))
+
+    t0 = time.perf_counter()
+    lg = oracle.router_logits(xs, w_r, bias)
+    idx, w = oracle.topk_softmax(lg, cfg.k)
+    loc = idx - cfg.expert_begin
+    cidx = np.full(idx.shape, -1, np.int32)
+    ok = (loc >= 0) & (loc < cfg.num_local)
+    cidx[ok] = remap[loc[ok]]
+    oracle.token_rows(xs, cidx, w, np.arange(len(toks)), wts, I=cfg.I, e0=0,
+                      n_local=max(len(used), 1))
+    dt = time.perf_counter() - t0
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.T} tokens of the same workload, whole layer per "
+                      f"token (router scores over {cfg.E} experts, top-{cfg.k}, softmax, "
+                      f"{cfg.k} MXFP4 expert FFNs with I={cfg.I}, weighted combine), "
+                      f"single-threaded fp32 C; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this layer runs on one GPU; --gpus must be 1 "
+                          "(multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import mxfp4_expert_top_amd as m
+    from synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    inp = make_inputs(cfg, dev)
+    p = m.layer_params(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.expert_begin, cfg.num_local,
+                       mode=args.mode)
+    ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
+    out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
+    idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        m.moe_layer(p, inp.x, inp.w_router, inp.bias, inp.weights, out, ws, topk_idx_out=idx,
+                    stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for ev in evs:  # create the underlying events before the timed region
+        for e in ev:
+            e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    stage_ms = {s: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]))
+                for j, s in enumerate(STAGES)}
+
+    # measured load of this batch
+    ii = idx.cpu().numpy() - cfg.expert_begin
+    local = (ii >= 0) & (ii < cfg.num_local)
+    A = int(local.sum())
+    counts = np.bincount(ii[local], minlength=cfg.num_local)
+    U = int((counts > 0).sum())
+    lb, lf, gb, gf = algorithmic(cfg, A, U)
+
+    gu_s = stage_ms["gate_up"] / 1e3
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    roof = {"kernel": "gemm_stream_kernel<SILU_MUL> (gate/up projection)", "bound": "hbm",
+            "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(gb),
+            "avg_launch_ms": round(stage_ms["gate_up"], 4)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(cfg.T / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "experts_computed": cfg.num_local, "weights": "mxfp4-e2m1-e8m0-b32",
+                   "activations": "bf16", "routing_bias": cfg.bias},
+        "roofline": roof,
+        "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),
+                  "algorithmic_bytes": int(lb), "algorithmic_flops": int(lf),
+                  "hbm_frac": round(lb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "bf16_mfma_frac": round(lf / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                  "mxfp4_mfma_frac": round(lf / (ms_step / 1e3) / 1e12 / MXFP4_PEAK_TFLOPS, 5),
+                  "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()}},
+        "cpu_baseline": None,
+    }
+    if args.cpu_tokens > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

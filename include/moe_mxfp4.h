@@ -1,0 +1,223 @@
+/*
+ * moe_mxfp4.h -- C ABI of a single-GPU LatentMoE layer with MXFP4 expert
+ * weights for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the sources describe it:
+ *   P1  "从Kimi K3到MiniMax-H3：国产大模型竞争进入“推理系统战”", section 一: tokens
+ *       are routed and computed in a 3584-wide latent space, 896 experts with
+ *       16 active per token, with a K3-specific activation path; section
+ *       二/第一层: weights ship as MXFP4 (4-bit elements sharing a scale per
+ *       block) and meet higher-precision activations in the kernels.
+ *   P2  "SGLang 0.5.17：Kimi K3 原生 MXFP4 推理架构解析", section "MoE 稀疏激活":
+ *       a router scores every token against every expert, the top 16 are
+ *       kept, and their outputs are summed with weights; section "MXFP4 原生
+ *       支持": per-block scales and dequantisation fused into the GEMM.
+ *   P3  "Kimi K3 Day-0 适配剖析:KDA/Gated MLA 混合注意力、MXFP4 在线量化与 896
+ *       专家 MoE", section 四: dispatch -> expert compute -> combine, with
+ *       dispatch's index computation and buffer planning re-done for 896
+ *       experts / top-16.
+ *   OCP-MX  OCP Microscaling Formats (MX) v1.0: E2M1 elements, one E8M0 scale
+ *       per 32 consecutive elements.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named as device arrays point to device memory (HBM) owned by
+ *    the caller; the library never keeps them after the call returns and never
+ *    allocates or frees device memory. Scratch memory comes in through `ws`
+ *    (device, 256-byte aligned, at least the queried size).
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *    stream) and return; nothing synchronises the host.
+ *  - Argument checks run on the host before any HIP call and return
+ *    MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE without
+ *    touching the device. A failed launch returns MOE_ERR_HIP and the HIP
+ *    message is kept per thread (moe_last_error()). T == 0 is a no-op.
+ *  - bf16 arrays are passed as void* (16-bit payloads). Row starts of bf16
+ *    activation rows must be 16-byte aligned (row strides multiple of 8).
+ *  - Determinism: no floating-point atomics; two calls on the same inputs give
+ *    bitwise-equal outputs.
+ *
+ * MXFP4 weight layout (one matrix [N, K], K the contraction dim): codes
+ * [N][K/2] bytes, element 2i in bits 0-3 and element 2i+1 in bits 4-7 of
+ * byte i; scales [N][K/32] bytes (E8M0: value 2^(s-127); the contract is
+ * 2 <= s <= 252, the codes of every finite fp32 block whose largest
+ * magnitude is at least 2^-123: s = 255 is NaN, s >= 253 can overflow,
+ * s <= 1 reaches subnormals). Element value =
+ * E2M1(code) * 2^(s-127). Experts are stacked: [num_local][N][...].
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moe_stream_t; /* hipStream_t */
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* a size out of range or a required pointer NULL */
+    MOE_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle     */
+    MOE_ERR_WORKSPACE = 3,   /* ws smaller than the queried size, or misaligned */
+    MOE_ERR_HIP = 4          /* a HIP runtime call or launch failed              */
+};
+
+enum moe_dtype { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 };
+
+/* Elementwise stage between the two expert projections. P1 (section 一)
+ * names a K3-specific activation path without defining it, so the stage is
+ * selectable: SILU_MUL = silu(gate) * up (default), GELU_TANH_MUL =
+ * gelu_tanh(gate) * up, NONE = plain GEMM output (no second weight). */
+enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2 };
+
+/* Limits of this build. */
+#define MOE_MX_BLOCK 32
+#define MOE_MAX_TOPK 32
+#define MOE_MAX_EXPERTS 2048
+
+/* ------------------------------------------------------------------------
+ * moe_route -- router scores, top-k select, softmax over the selected scores,
+ * expert histogram (P2 "MoE 稀疏激活": score every expert, keep the best 16,
+ * weight their outputs).
+ *
+ *   x        [T][d] bf16          latent tokens
+ *   w_router [E][d] fp32          router weights
+ *   bias     [E] fp32 or NULL     added to every token's scores
+ *   logits   [T][E] fp32          if logits_given: read (replayed scores);
+ *                                 else written: logits[t][e] =
+ *                                 sum_i x[t][i]*w_router[e][i] + bias[e]
+ *                                 (fp32 accumulation; each product exact)
+ *   topk_idx [T][k] int32 (out)   best expert first; a larger score wins, an
+ *                                 equal score goes to the lower index, -0 == +0
+ *   topk_w   [T][k] fp32 (out)    w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ *   expert_counts [E] int32 (out) assignments per expert over all T*k
+ * Preconditions: finite scores. Errors: k < 1, k > E, NULL required pointer
+ * -> INVALID_ARG; k > 32, E > 2048 or (scores computed) d % 128 != 0 ->
+ * UNSUPPORTED. With T == 0 only expert_counts is written (zeros).
+ * ------------------------------------------------------------------------ */
+int moe_route(const void *x, const float *w_router, const float *bias, float *logits,
+              int logits_given, int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
+              int32_t *expert_counts, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- dispatch planning (P3 section 四: index computation and
+ * buffer planning): offsets of each local expert's rows and a stable counting
+ * sort of the row-major (t, j) assignment list by expert.
+ *
+ *   topk_idx [T][k] int32, expert_counts [E] int32  (from moe_route)
+ *   local experts are ids [expert_begin, expert_begin + num_local)
+ *   expert_offsets [num_local + 1] int32 (out): off[0] = 0,
+ *                  off[i+1] = off[i] + expert_counts[expert_begin + i]
+ *   perm_token [T*k] int32 (out): rows off[i]..off[i+1]-1 hold the tokens
+ *                  routed to local expert i in increasing token order; entries
+ *                  at and after off[num_local] are left untouched
+ *   inv [T][k] int32 (out): the row of assignment (t, j), or -1 if its
+ *                  expert is not local (dropped)
+ *   ws / ws_bytes: scratch of moe_permute_workspace_size(T, num_local) bytes
+ * ------------------------------------------------------------------------ */
+size_t moe_permute_workspace_size(int T, int num_local);
+int moe_permute(const int32_t *topk_idx, const int32_t *expert_counts, int T, int k, int E,
+                int expert_begin, int num_local, int32_t *expert_offsets, int32_t *perm_token,
+                int32_t *inv, void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_mxfp4_dequant -- decode an MXFP4 matrix to bf16 (OCP-MX element value
+ * E2M1(code) * 2^(s-127), exact in bf16 for scale codes 2..252; codes 0 and 1
+ * reach bf16 subnormals, which the hardware may flush to zero).
+ *   codes [N][K/2], scales [N][K/32] -> out [N][K] bf16
+ * ------------------------------------------------------------------------ */
+int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K, void *out,
+                      moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_gemm_mxfp4 -- one grouped expert projection with MXFP4 weights
+ * dequantised in registers and fed to bf16 matrix cores with fp32
+ * accumulation (P2 "MXFP4 原生支持": dequantisation fused into the GEMM).
+ *
+ * For local expert e and each row r in [off[e], off[e+1]):
+ *   a_row  = a + (a_rows ? a_rows[r] : r) * lda          (bf16, K elements)
+ *   acc1[n] = sum_k a_row[k] * W1[e][n][k],  n < N
+ *   act == MOE_ACT_NONE:  out[r][n] = acc1[n]                     (w2 NULL)
+ *   otherwise:            out[r][n] = act(acc1[n], acc2[n]), acc2 from W2
+ *   out + r * ldo, dtype out_dtype (bf16 rounding is to nearest even)
+ *
+ *   w1_codes/w1_scales, w2_codes/w2_scales: [num_local][N][K/2], [..][K/32]
+ *   expert_offsets [num_local + 1] int32 on the device
+ *   max_rows: a host-side upper bound on off[num_local] (e.g. T*k); it sizes
+ *             the launch, rows beyond off[num_local] are never touched
+ *   mode: 0 = choose from max_rows/num_local, 1 = weight-streaming schedule
+ *         (few rows per expert), 2 = tiled schedule (many rows per expert)
+ *   ws / ws_bytes: scratch of moe_grouped_gemm_workspace_size(...) bytes (the
+ *         device-built work list)
+ * Requirements: lda >= K and ldo >= N, both multiples of 8; a_rows entries
+ * index valid rows of `a`.
+ * Errors: block_size != 32, K % 128 != 0 or N % 64 != 0 -> UNSUPPORTED;
+ * a GLU act without w2, or w2 with MOE_ACT_NONE -> INVALID_ARG.
+ * ------------------------------------------------------------------------ */
+size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode);
+int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
+                           const uint8_t *w1_codes, const uint8_t *w1_scales,
+                           const uint8_t *w2_codes, const uint8_t *w2_scales,
+                           const int32_t *expert_offsets, int num_local, int max_rows, int N,
+                           int K, int block_size, int act, void *out, int out_dtype,
+                           int64_t ldo, int mode, void *ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- weighted unpermute (P3 section 四, combine: results come back
+ * weighted; P2 "MoE 稀疏激活": weighted sum of the selected experts):
+ *   out[t][m] = sum_{j=0..k-1, inv[t][j] >= 0} topk_w[t][j] * y[inv[t][j]][m]
+ * summed in j order in fp32; a token with no local assignment gets zeros.
+ *   y [rows][d] (y_dtype, row stride ldy), out [T][d] (out_dtype, stride ldo)
+ * ------------------------------------------------------------------------ */
+int moe_combine(const void *y, int y_dtype, int64_t ldy, const int32_t *inv,
+                const float *topk_w, int T, int d, int k, void *out, int out_dtype, int64_t ldo,
+                moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer -- the whole layer in one call: route -> permute -> gate/up
+ * projection with activation -> down projection -> combine, enqueued as
+ * kernels on `stream` with no host synchronisation.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int T;            /* tokens                                   */
+    int d;            /* latent width (3584 for the K3 layer)     */
+    int E;            /* routed experts (896)                     */
+    int k;            /* experts per token (16)                   */
+    int I;            /* expert intermediate width                */
+    int block_size;   /* MX block size, must be 32                */
+    int expert_begin; /* first local expert id                    */
+    int num_local;    /* local experts computed; others dropped   */
+    int act;          /* enum moe_act, MOE_ACT_SILU_MUL default   */
+    int out_dtype;    /* enum moe_dtype of `out`                  */
+    int mode;         /* GEMM schedule, as moe_grouped_gemm_mxfp4 */
+} moe_layer_params;
+
+/* Scratch bytes moe_layer needs for these parameters (0 if invalid). */
+size_t moe_layer_workspace_size(const moe_layer_params *p);
+
+/*   gate/up codes [num_local][I][d/2], scales [num_local][I][d/32]
+ *   down codes    [num_local][d][I/2], scales [num_local][d][I/32]
+ *   out [T][d] (p->out_dtype)
+ *   logits_out [T][E] f32, topk_idx_out / topk_w_out [T][k]: optional copies
+ *   of the routing (NULL to skip)
+ *   stage_events: NULL, or 6 hipEvent_t recorded on `stream` before the
+ *   route, permute, gate/up, down and combine stages and after the last one
+ *   (for per-stage timing). */
+int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, const float *bias,
+              const uint8_t *gate_codes, const uint8_t *gate_scales, const uint8_t *up_codes,
+              const uint8_t *up_scales, const uint8_t *down_codes, const uint8_t *down_scales,
+              void *out, float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+              size_t ws_bytes, void **stage_events, moe_stream_t stream);
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+/* The calling thread's last HIP error message ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MXFP4_H */

@@ -1,0 +1,284 @@
+"""Python binding of libmoe_mxfp4.so (the C ABI in include/moe_mxfp4.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+the library. Tensors are PyTorch device tensors (PyTorch supplies device
+memory and streams); each function checks devices, dtypes, contiguity and
+shapes on the host -- the C ABI cannot see buffer sizes -- then passes raw
+pointers and the current stream. There is no CPU fallback: if the library is
+missing, importing this package raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmoe_mxfp4.so"
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+DT_BF16, DT_F32 = 0, 1
+ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
+MODE_AUTO, MODE_STREAM, MODE_TILED = 0, 1, 2
+MX_BLOCK = 32
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not _LIB_PATH.exists():
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m mxfp4_expert_top_amd.build` "
+            "(there is no fallback path)")
+    L = C.CDLL(str(_LIB_PATH))
+    p, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
+    L.moe_status_string.restype = C.c_char_p
+    L.moe_status_string.argtypes = [i32]
+    L.moe_last_error.restype = C.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_route.restype = i32
+    L.moe_route.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, p, p, p, p]
+    L.moe_permute_workspace_size.restype = sz
+    L.moe_permute_workspace_size.argtypes = [i32, i32]
+    L.moe_permute.restype = i32
+    L.moe_permute.argtypes = [p, p, i32, i32, i32, i32, i32, p, p, p, p, sz, p]
+    L.moe_mxfp4_dequant.restype = i32
+    L.moe_mxfp4_dequant.argtypes = [p, p, i64, i32, p, p]
+    L.moe_grouped_gemm_workspace_size.restype = sz
+    L.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32]
+    L.moe_grouped_gemm_mxfp4.restype = i32
+    L.moe_grouped_gemm_mxfp4.argtypes = [p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                         p, i32, i64, i32, p, sz, p]
+    L.moe_combine.restype = i32
+    L.moe_combine.argtypes = [p, i32, i64, p, p, i32, i32, i32, p, i32, i64, p]
+    L.moe_layer_workspace_size.restype = sz
+    L.moe_layer_workspace_size.argtypes = [p]
+    L.moe_layer.restype = i32
+    L.moe_layer.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, sz, p, p]
+    return L
+
+
+lib = _load()
+
+EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4_dequant",
+            "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size", "moe_combine",
+            "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error")
+
+
+class LayerParams(C.Structure):
+    _fields_ = [(n, C.c_int) for n in ("T", "d", "E", "k", "I", "block_size", "expert_begin",
+                                        "num_local", "act", "out_dtype", "mode")]
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        msg = lib.moe_status_string(status).decode()
+        if status == MOE_ERR_HIP:
+            msg += ": " + lib.moe_last_error().decode()
+        raise MoeError(fn, status, msg)
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices")
+    return dev
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _want(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def moe_route(x, w_router, bias, logits, logits_given, topk_idx, topk_w, expert_counts,
+              stream=None):
+    """Router scores (unless ``logits_given``), top-k, softmax, histogram."""
+    T, k = topk_idx.shape
+    E = expert_counts.shape[0]
+    d = x.shape[1] if x is not None else 0
+    _dev(x, w_router, bias, logits, topk_idx, topk_w, expert_counts)
+    _want(logits, torch.float32, (T, E), "logits")
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(topk_w, torch.float32, (T, k), "topk_w")
+    _want(expert_counts, torch.int32, (E,), "expert_counts")
+    if not logits_given:
+        _want(x, torch.bfloat16, (T, d), "x")
+        _want(w_router, torch.float32, (E, d), "w_router")
+        if bias is not None:
+            _want(bias, torch.float32, (E,), "bias")
+    st = lib.moe_route(_ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits), int(bool(logits_given)),
+                       T, d, E, k, _ptr(topk_idx), _ptr(topk_w), _ptr(expert_counts),
+                       _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_permute_workspace_size(T, num_local):
+    return int(lib.moe_permute_workspace_size(T, num_local))
+
+
+def moe_permute(topk_idx, expert_counts, expert_begin, num_local, expert_offsets, perm_token,
+                inv, ws, stream=None):
+    T, k = topk_idx.shape
+    E = expert_counts.shape[0]
+    _dev(topk_idx, expert_counts, expert_offsets, perm_token, inv, ws)
+    _want(topk_idx, torch.int32, (T, k), "topk_idx")
+    _want(expert_offsets, torch.int32, (num_local + 1,), "expert_offsets")
+    _want(perm_token, torch.int32, (T * k,), "perm_token")
+    _want(inv, torch.int32, (T, k), "inv")
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.moe_permute(_ptr(topk_idx), _ptr(expert_counts), T, k, E, expert_begin, num_local,
+                         _ptr(expert_offsets), _ptr(perm_token), _ptr(inv), _ptr(ws), nbytes,
+                         _stream(stream))
+    _check("moe_permute", st)
+
+
+def moe_mxfp4_dequant(codes, scales, out, stream=None):
+    N, K = out.shape
+    _dev(codes, scales, out)
+    _want(codes, torch.uint8, (N, K // 2), "codes")
+    _want(scales, torch.uint8, (N, K // 32), "scales")
+    _want(out, torch.bfloat16, (N, K), "out")
+    _check("moe_mxfp4_dequant",
+           lib.moe_mxfp4_dequant(_ptr(codes), _ptr(scales), N, K, _ptr(out), _stream(stream)))
+
+
+def moe_grouped_gemm_workspace_size(num_local, max_rows, N, mode=MODE_AUTO):
+    return int(lib.moe_grouped_gemm_workspace_size(num_local, max_rows, N, mode))
+
+
+def moe_grouped_gemm_mxfp4(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
+                           expert_offsets, max_rows, act, out, ws, mode=MODE_AUTO, stream=None):
+    """out[r] = act(a_row(r) @ W1[e].T, a_row(r) @ W2[e].T) for the rows r of
+    each local expert e (see the header). ``out`` is [>= rows, N]."""
+    num_local = expert_offsets.shape[0] - 1
+    N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
+    _dev(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets, out, ws)
+    if a.dtype != torch.bfloat16 or a.dim() != 2 or a.shape[1] != K:
+        raise ValueError("a must be [rows, K] bf16")
+    _want(w1_codes, torch.uint8, (num_local, N, K // 2), "w1_codes")
+    _want(w1_scales, torch.uint8, (num_local, N, K // 32), "w1_scales")
+    if w2_codes is not None:
+        _want(w2_codes, torch.uint8, (num_local, N, K // 2), "w2_codes")
+        _want(w2_scales, torch.uint8, (num_local, N, K // 32), "w2_scales")
+    if out.dim() != 2 or out.shape[1] != N or out.shape[0] < max_rows:
+        raise ValueError("out must be [>= max_rows, N]")
+    if a_rows is not None:
+        if a_rows.dtype != torch.int32 or a_rows.numel() < max_rows:
+            raise ValueError("a_rows must be int32 with >= max_rows entries")
+    elif a.shape[0] < max_rows:
+        raise ValueError("a must hold >= max_rows rows")
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.moe_grouped_gemm_mxfp4(
+        _ptr(a), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K, MX_BLOCK, act,
+        _ptr(out), _dt(out), N, mode, _ptr(ws), nbytes, _stream(stream))
+    _check("moe_grouped_gemm_mxfp4", st)
+
+
+def moe_combine(y, inv, topk_w, out, stream=None):
+    T, k = inv.shape
+    d = out.shape[1]
+    _dev(y, inv, topk_w, out)
+    _want(inv, torch.int32, (T, k), "inv")
+    _want(topk_w, torch.float32, (T, k), "topk_w")
+    if y.dim() != 2 or y.shape[1] != d or out.shape[0] != T:
+        raise ValueError("y must be [rows, d] and out [T, d]")
+    st = lib.moe_combine(_ptr(y), _dt(y), d, _ptr(inv), _ptr(topk_w), T, d, k, _ptr(out), _dt(out),
+                         d, _stream(stream))
+    _check("moe_combine", st)
+
+
+def layer_params(T, d, E, k, I, expert_begin=0, num_local=None, act=ACT_SILU_MUL,
+                 out_dtype=DT_BF16, mode=MODE_AUTO):
+    return LayerParams(T, d, E, k, I, MX_BLOCK, expert_begin,
+                       E - expert_begin if num_local is None else num_local, act, out_dtype, mode)
+
+
+def moe_layer_workspace_size(params: LayerParams) -> int:
+    n = int(lib.moe_layer_workspace_size(C.byref(params)))
+    if n == 0:
+        raise MoeError("moe_layer_workspace_size", MOE_ERR_INVALID_ARG, "invalid parameters")
+    return n
+
+
+def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_out=None,
+              topk_idx_out=None, topk_w_out=None, stage_events=None, stream=None):
+    """The fused layer. ``weights`` holds gate/up/down codes and scales
+    (local experts stacked). ``stage_events``: None or 6 torch.cuda.Event."""
+    p = params
+    _dev(x, w_router, bias, out, ws, logits_out, topk_idx_out, topk_w_out,
+         *[weights[n] for n in _WNAMES])
+    _want(x, torch.bfloat16, (p.T, p.d), "x")
+    _want(w_router, torch.float32, (p.E, p.d), "w_router")
+    if bias is not None:
+        _want(bias, torch.float32, (p.E,), "bias")
+    for n, shape in (("gate_codes", (p.num_local, p.I, p.d // 2)),
+                     ("gate_scales", (p.num_local, p.I, p.d // 32)),
+                     ("up_codes", (p.num_local, p.I, p.d // 2)),
+                     ("up_scales", (p.num_local, p.I, p.d // 32)),
+                     ("down_codes", (p.num_local, p.d, p.I // 2)),
+                     ("down_scales", (p.num_local, p.d, p.I // 32))):
+        _want(weights[n], torch.uint8, shape, n)
+    _want(out, torch.float32 if p.out_dtype == DT_F32 else torch.bfloat16, (p.T, p.d), "out")
+    if logits_out is not None:
+        _want(logits_out, torch.float32, (p.T, p.E), "logits_out")
+    if topk_idx_out is not None:
+        _want(topk_idx_out, torch.int32, (p.T, p.k), "topk_idx_out")
+    if topk_w_out is not None:
+        _want(topk_w_out, torch.float32, (p.T, p.k), "topk_w_out")
+    nbytes = ws.numel() * ws.element_size()
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        for e_ in stage_events:
+            e_.record(torch.cuda.current_stream() if stream is None else stream)  # materialise
+        ev = (C.c_void_p * 6)(*[e_.cuda_event for e_ in stage_events])
+    st = lib.moe_layer(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                       *[_ptr(weights[n]) for n in _WNAMES], _ptr(out), _ptr(logits_out),
+                       _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), nbytes, ev,
+                       _stream(stream))
+    _check("moe_layer", st)
+
+
+_WNAMES = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer (torch's allocator returns 256-byte aligned blocks)."""
+    ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws

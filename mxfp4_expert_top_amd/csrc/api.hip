@@ -1,0 +1,314 @@
+// C ABI of the MXFP4 LatentMoE layer: argument checks (on the host, before
+// any HIP call), workspace carving and the launch sequence. Declarations and
+// the contract of every entry point are in include/moe_mxfp4.h.
+#include <string>
+
+#include "moe_mxfp4.h"
+#include "launch.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e)
+{
+    g_last_error = hipGetErrorString(e);
+    return MOE_ERR_HIP;
+}
+
+#define HIP_TRY(expr)                                   \
+    do {                                                \
+        hipError_t e_ = (expr);                         \
+        if (e_ != hipSuccess) return hip_fail(e_);      \
+    } while (0)
+
+#define CHECK(cond, code)          \
+    do {                           \
+        if (!(cond)) return (code); \
+    } while (0)
+
+inline hipStream_t as_stream(moe_stream_t s) { return (hipStream_t)s; }
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline size_t round_up(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int check_route(const void *x, const float *w_router, const float *logits, int logits_given,
+                int T, int d, int E, int k, const int32_t *idx, const float *w,
+                const int32_t *counts)
+{
+    CHECK(T >= 0 && E >= 1 && k >= 1 && k <= E, MOE_ERR_INVALID_ARG);
+    CHECK(counts, MOE_ERR_INVALID_ARG);
+    CHECK(k <= MOE_MAX_TOPK && E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
+    if (T == 0) return MOE_OK;
+    CHECK(logits && idx && w, MOE_ERR_INVALID_ARG);
+    if (!logits_given) {
+        CHECK(x && w_router && d >= 1, MOE_ERR_INVALID_ARG);
+        CHECK(d % 128 == 0, MOE_ERR_UNSUPPORTED);
+        CHECK(aligned(x, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG);
+    }
+    return MOE_OK;
+}
+
+int check_permute(const int32_t *idx, const int32_t *counts, int T, int k, int E, int e0, int nl,
+                  const int32_t *off, const int32_t *perm, const int32_t *inv)
+{
+    CHECK(T >= 0 && k >= 1 && k <= E && E >= 1, MOE_ERR_INVALID_ARG);
+    CHECK(e0 >= 0 && nl >= 1 && e0 + nl <= E, MOE_ERR_INVALID_ARG);
+    CHECK(k <= MOE_MAX_TOPK && E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
+    CHECK(counts && off, MOE_ERR_INVALID_ARG);
+    if (T > 0) CHECK(idx && perm && inv, MOE_ERR_INVALID_ARG);
+    return MOE_OK;
+}
+
+int check_gemm(const void *a, int64_t lda, const uint8_t *w1c, const uint8_t *w1s,
+               const uint8_t *w2c, const uint8_t *w2s, const int32_t *off, int nl, int max_rows,
+               int N, int K, int block_size, int act, const void *out, int out_dtype, int64_t ldo)
+{
+    CHECK(nl >= 1 && max_rows >= 0 && N >= 1 && K >= 1, MOE_ERR_INVALID_ARG);
+    CHECK(act == MOE_ACT_NONE || act == MOE_ACT_SILU_MUL || act == MOE_ACT_GELU_TANH_MUL,
+          MOE_ERR_INVALID_ARG);
+    CHECK(out_dtype == MOE_DT_BF16 || out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
+    CHECK(block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
+    CHECK(K % 128 == 0 && N % 64 == 0, MOE_ERR_UNSUPPORTED);
+    if (act == MOE_ACT_NONE)
+        CHECK(!w2c && !w2s, MOE_ERR_INVALID_ARG);
+    else
+        CHECK(w2c && w2s, MOE_ERR_INVALID_ARG);
+    if (max_rows == 0) return MOE_OK;
+    CHECK(a && w1c && w1s && off && out, MOE_ERR_INVALID_ARG);
+    CHECK(lda >= K && lda % 8 == 0 && ldo >= N && ldo % 8 == 0, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(a, 16) && aligned(w1c, 16) && aligned(w1s, 4), MOE_ERR_INVALID_ARG);
+    if (w2c) CHECK(aligned(w2c, 16) && aligned(w2s, 4), MOE_ERR_INVALID_ARG);
+    return MOE_OK;
+}
+
+int check_ws(const void *ws, size_t ws_bytes, size_t need)
+{
+    if (need == 0) return MOE_OK;
+    CHECK(ws && ws_bytes >= need && aligned(ws, 256), MOE_ERR_WORKSPACE);
+    return MOE_OK;
+}
+
+// Workspace layout of moe_layer; every region 256-byte aligned.
+struct LayerWs {
+    size_t logits, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
+};
+
+LayerWs layer_ws(const moe_layer_params *p)
+{
+    LayerWs L{};
+    const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
+    const size_t A = T * k;
+    size_t o = 0;
+    L.logits = o; o += round_up(T * E * 4);
+    L.idx = o;    o += round_up(A * 4);
+    L.w = o;      o += round_up(A * 4);
+    L.counts = o; o += round_up(E * 4);
+    L.off = o;    o += round_up(((size_t)p->num_local + 1) * 4);
+    L.perm = o;   o += round_up(A * 4);
+    L.inv = o;    o += round_up(A * 4);
+    L.pws = o;    o += round_up(permute_ws_bytes(p->T, p->num_local));
+    L.gws = o;
+    o += round_up(grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
+    L.h = o;      o += round_up(A * (size_t)p->I * 2);
+    L.y = o;      o += round_up(A * (size_t)p->d * 4);
+    L.total = o;
+    return L;
+}
+
+int check_layer_params(const moe_layer_params *p)
+{
+    CHECK(p, MOE_ERR_INVALID_ARG);
+    CHECK(p->T >= 0 && p->d >= 1 && p->E >= 1 && p->k >= 1 && p->k <= p->E && p->I >= 1,
+          MOE_ERR_INVALID_ARG);
+    CHECK(p->expert_begin >= 0 && p->num_local >= 1 && p->expert_begin + p->num_local <= p->E,
+          MOE_ERR_INVALID_ARG);
+    CHECK(p->act == MOE_ACT_SILU_MUL || p->act == MOE_ACT_GELU_TANH_MUL, MOE_ERR_INVALID_ARG);
+    CHECK(p->out_dtype == MOE_DT_BF16 || p->out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
+    CHECK(p->mode >= 0 && p->mode <= 2, MOE_ERR_INVALID_ARG);
+    CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
+    CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
+    CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
+    CHECK((int64_t)p->T * p->k <= INT32_MAX / 2, MOE_ERR_UNSUPPORTED);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported by this build";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_route(const void *x, const float *w_router, const float *bias, float *logits,
+              int logits_given, int T, int d, int E, int k, int32_t *topk_idx, float *topk_w,
+              int32_t *expert_counts, moe_stream_t stream)
+{
+    int rc = check_route(x, w_router, logits, logits_given, T, d, E, k, topk_idx, topk_w,
+                         expert_counts);
+    if (rc) return rc;
+    hipStream_t s = as_stream(stream);
+    HIP_TRY(launch_fill_i32(expert_counts, E, 0, s));
+    if (T == 0) return MOE_OK;
+    if (!logits_given)
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, s));
+    HIP_TRY(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, expert_counts, s));
+    return MOE_OK;
+}
+
+size_t moe_permute_workspace_size(int T, int num_local)
+{
+    if (T < 0 || num_local < 1) return 0;
+    return permute_ws_bytes(T, num_local);
+}
+
+int moe_permute(const int32_t *topk_idx, const int32_t *expert_counts, int T, int k, int E,
+                int expert_begin, int num_local, int32_t *expert_offsets, int32_t *perm_token,
+                int32_t *inv, void *ws, size_t ws_bytes, moe_stream_t stream)
+{
+    int rc = check_permute(topk_idx, expert_counts, T, k, E, expert_begin, num_local,
+                           expert_offsets, perm_token, inv);
+    if (rc) return rc;
+    rc = check_ws(ws, ws_bytes, permute_ws_bytes(T, num_local));
+    if (rc) return rc;
+    HIP_TRY(launch_permute(topk_idx, expert_counts, T, k, expert_begin, num_local, expert_offsets,
+                           perm_token, inv, ws, as_stream(stream)));
+    return MOE_OK;
+}
+
+int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K, void *out,
+                      moe_stream_t stream)
+{
+    CHECK(N >= 0 && K >= 0, MOE_ERR_INVALID_ARG);
+    CHECK(K % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (N == 0 || K == 0) return MOE_OK;
+    CHECK(codes && scales && out, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(codes, 4) && aligned(out, 16), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_mxfp4_dequant(codes, scales, N, K, (bf16 *)out, as_stream(stream)));
+    return MOE_OK;
+}
+
+size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode)
+{
+    if (num_local < 1 || max_rows < 0 || mode < 0 || mode > 2) return 0;
+    return grouped_gemm_ws_bytes(num_local, max_rows, N, mode);
+}
+
+int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
+                           const uint8_t *w1_codes, const uint8_t *w1_scales,
+                           const uint8_t *w2_codes, const uint8_t *w2_scales,
+                           const int32_t *expert_offsets, int num_local, int max_rows, int N,
+                           int K, int block_size, int act, void *out, int out_dtype,
+                           int64_t ldo, int mode, void *ws, size_t ws_bytes,
+                           moe_stream_t stream)
+{
+    CHECK(mode >= 0 && mode <= 2, MOE_ERR_INVALID_ARG);
+    int rc = check_gemm(a, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
+                        num_local, max_rows, N, K, block_size, act, out, out_dtype, ldo);
+    if (rc) return rc;
+    if (max_rows == 0) return MOE_OK;
+    rc = check_ws(ws, ws_bytes, grouped_gemm_ws_bytes(num_local, max_rows, N, mode));
+    if (rc) return rc;
+    HIP_TRY(launch_grouped_gemm((const bf16 *)a, lda, a_rows, w1_codes, w1_scales, w2_codes,
+                                w2_scales, expert_offsets, num_local, max_rows, N, K, act, out,
+                                out_dtype == MOE_DT_F32, ldo, mode, ws, as_stream(stream)));
+    return MOE_OK;
+}
+
+int moe_combine(const void *y, int y_dtype, int64_t ldy, const int32_t *inv,
+                const float *topk_w, int T, int d, int k, void *out, int out_dtype, int64_t ldo,
+                moe_stream_t stream)
+{
+    CHECK(T >= 0 && d >= 1 && k >= 1, MOE_ERR_INVALID_ARG);
+    CHECK(y_dtype == MOE_DT_BF16 || y_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
+    CHECK(out_dtype == MOE_DT_BF16 || out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
+    CHECK(k <= MOE_MAX_TOPK, MOE_ERR_UNSUPPORTED);
+    CHECK(d % 8 == 0, MOE_ERR_UNSUPPORTED);
+    if (T == 0) return MOE_OK;
+    CHECK(y && inv && topk_w && out, MOE_ERR_INVALID_ARG);
+    CHECK(ldy >= d && ldy % 8 == 0 && ldo >= d && ldo % 8 == 0, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(y, 16) && aligned(out, 16), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_combine(y, y_dtype == MOE_DT_F32, ldy, inv, topk_w, T, d, k, out,
+                           out_dtype == MOE_DT_F32, ldo, as_stream(stream)));
+    return MOE_OK;
+}
+
+size_t moe_layer_workspace_size(const moe_layer_params *p)
+{
+    if (check_layer_params(p) != MOE_OK) return 0;
+    return layer_ws(p).total;
+}
+
+int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, const float *bias,
+              const uint8_t *gate_codes, const uint8_t *gate_scales, const uint8_t *up_codes,
+              const uint8_t *up_scales, const uint8_t *down_codes, const uint8_t *down_scales,
+              void *out, float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+              size_t ws_bytes, void **stage_events, moe_stream_t stream)
+{
+    int rc = check_layer_params(p);
+    if (rc) return rc;
+    if (p->T == 0) return MOE_OK;
+    CHECK(x && w_router && out && gate_codes && gate_scales && up_codes && up_scales &&
+              down_codes && down_scales,
+          MOE_ERR_INVALID_ARG);
+    CHECK(aligned(x, 16) && aligned(out, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG);
+    CHECK(aligned(gate_codes, 16) && aligned(up_codes, 16) && aligned(down_codes, 16) &&
+              aligned(gate_scales, 4) && aligned(up_scales, 4) && aligned(down_scales, 4),
+          MOE_ERR_INVALID_ARG);
+    const LayerWs L = layer_ws(p);
+    rc = check_ws(ws, ws_bytes, L.total);
+    if (rc) return rc;
+
+    char *base = (char *)ws;
+    float *logits = logits_out ? logits_out : (float *)(base + L.logits);
+    int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + L.idx);
+    float *w = topk_w_out ? topk_w_out : (float *)(base + L.w);
+    int32_t *counts = (int32_t *)(base + L.counts);
+    int32_t *off = (int32_t *)(base + L.off);
+    int32_t *perm = (int32_t *)(base + L.perm);
+    int32_t *inv = (int32_t *)(base + L.inv);
+    bf16 *h = (bf16 *)(base + L.h);
+    float *y = (float *)(base + L.y);
+    const int A = p->T * p->k;
+    hipStream_t s = as_stream(stream);
+    hipEvent_t *ev = (hipEvent_t *)stage_events;
+
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    HIP_TRY(launch_fill_i32(counts, p->E, 0, s));
+    HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, p->T, p->d, p->E, s));
+    HIP_TRY(launch_topk_softmax(logits, p->T, p->E, p->k, idx, w, counts, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm, inv,
+                           base + L.pws, s));
+    // one work plan serves both projections (same offsets, bound and schedule)
+    HIP_TRY(launch_gemm_plan(off, p->num_local, A, p->mode, base + L.gws, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
+                            up_scales, off, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
+                            p->mode, base + L.gws, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr, off,
+                            p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
+                            base + L.gws, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+    HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                           p->out_dtype == MOE_DT_F32, p->d, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[5], s));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Weighted unpermute / combine (P3 "Kimi K3 Day-0 适配剖析", section 四: the
+// combine step gathers expert results back by weight; P2 "SGLang 0.5.17", section
+// "MoE 稀疏激活": a weighted sum over the selected experts).
+//
+// out[t][m] = sum_{j < k, inv[t][j] >= 0} w[t][j] * y[inv[t][j]][m], summed in
+// slot order j in fp32. A gather, not a scatter: every output element is
+// written once, without atomics. Bandwidth-bound: one workgroup per token,
+// 8 contiguous elements per thread per step.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+template <typename YT>
+__device__ __forceinline__ void load8(const YT *p, float v[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float v[8])
+{
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8<bf16>(const bf16 *p, float v[8])
+{
+    const bf16x8 a = *(const bf16x8 *)p;
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = (float)a[i];
+}
+
+template <typename OT>
+__device__ __forceinline__ void store8(OT *p, const float v[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float v[8])
+{
+    *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4 *)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16 *p, const float v[8])
+{
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = to_bf16(v[i]);
+    *(bf16x8 *)p = o;
+}
+
+template <typename YT, typename OT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, int64_t ldy,
+                                                      const int32_t *__restrict__ inv,
+                                                      const float *__restrict__ w, int d, int k,
+                                                      OT *__restrict__ out, int64_t ldo)
+{
+    const int t = blockIdx.x;
+    __shared__ int32_t rows[MOE_MAX_TOPK_DEV];
+    __shared__ float wts[MOE_MAX_TOPK_DEV];
+    if (threadIdx.x < k) {
+        rows[threadIdx.x] = inv[(int64_t)t * k + threadIdx.x];
+        wts[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < k; j++) {
+            const int r = rows[j];
+            if (r < 0) continue;
+            float v[8];
+            load8<YT>(y + (int64_t)r * ldy + c, v);
+            const float wj = wts[j];
+#pragma unroll
+            for (int i = 0; i < 8; i++) acc[i] += wj * v[i];
+        }
+        store8<OT>(out + (int64_t)t * ldo + c, acc);
+    }
+}
+
+hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,
+                          const float *w, int T, int d, int k, void *out, int out_f32,
+                          int64_t ldo, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    dim3 grid(T), block(256);
+    if (y_f32 && out_f32)
+        hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, (const float *)y,
+                           ldy, inv, w, d, k, (float *)out, ldo);
+    else if (y_f32)
+        hipLaunchKernelGGL((combine_kernel<float, bf16>), grid, block, 0, s, (const float *)y,
+                           ldy, inv, w, d, k, (bf16 *)out, ldo);
+    else if (out_f32)
+        hipLaunchKernelGGL((combine_kernel<bf16, float>), grid, block, 0, s, (const bf16 *)y, ldy,
+                           inv, w, d, k, (float *)out, ldo);
+    else
+        hipLaunchKernelGGL((combine_kernel<bf16, bf16>), grid, block, 0, s, (const bf16 *)y, ldy,
+                           inv, w, d, k, (bf16 *)out, ldo);
+    return hipGetLastError();
+}
+
+}  // namespace moe

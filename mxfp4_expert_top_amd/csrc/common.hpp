@@ -1,0 +1,100 @@
+// Device-side building blocks shared by the gfx950 kernels of the MXFP4
+// LatentMoE layer: vector types, the bf16 matrix-core instruction, MXFP4
+// decode, and bf16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// D = A * B + C on one 16x16 fp32 tile with K = 32 bf16 products.
+// Operand lanes: lane L supplies row (L % 16) of A and column (L % 16) of B,
+// 8 consecutive contraction elements of the lane group L / 16. Any mapping of
+// contraction indices to (lane group, element) gives the same sum as long as A
+// and B use the same one, so kernels choose the mapping that makes their loads
+// contiguous. Result: lane L holds C[4 * (L / 16) + i][L % 16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// E8M0 scale code -> fp32 2^(s-127). Code 0 is the fp32 subnormal 2^-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Decode 8 E2M1 codes (one dword: element 2i in the low nibble of byte i) and
+// multiply by `scale` (a power of two), giving 8 bf16 values. Products of an
+// E2M1 value and 2^n are exact in bf16 unless they leave its normal range.
+__device__ __forceinline__ bf16x8 mx_decode8(uint32_t codes, float scale)
+{
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ bf16 to_bf16(float f)
+{
+    return (bf16)f;
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16 b)
+{
+    return (float)b;
+}
+
+// Split an fp32 value into three bf16 parts whose exact sum is the value:
+// hi keeps the top 8 significant bits (truncated), mid the next 8 of the
+// remainder, lo the rest (at most 8 bits, so exact in bf16). Each product of
+// a bf16 with a part is exact in fp32.
+__device__ __forceinline__ void split3_bf16(float v, bf16 &hi, bf16 &mid, bf16 &lo)
+{
+    float h = __uint_as_float(__float_as_uint(v) & 0xffff0000u);
+    float r1 = v - h;
+    float m = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+    float r2 = r1 - m;
+    hi = (bf16)h;
+    mid = (bf16)m;
+    lo = (bf16)r2;
+}
+
+// Activation stages (the elementwise step between the two projections).
+enum { ACT_NONE = 0, ACT_SILU_MUL = 1, ACT_GELU_TANH_MUL = 2 };
+
+template <int ACT>
+__device__ __forceinline__ float act_apply(float g, float u)
+{
+    if constexpr (ACT == ACT_SILU_MUL) {
+        return g / (1.0f + expf(-g)) * u;
+    } else if constexpr (ACT == ACT_GELU_TANH_MUL) {
+        float inner = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+        return 0.5f * g * (1.0f + tanhf(inner)) * u;
+    } else {
+        return g;
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T *p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<bf16>(bf16 *p, float v) { *p = to_bf16(v); }
+
+}  // namespace moe

@@ -1,0 +1,62 @@
+// Internal launchers of the gfx950 kernels (host side). Every launcher
+// enqueues on `s` and returns the launch status; arguments are assumed
+// validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOE_MAX_EXPERTS_DEV 2048
+#define MOE_MAX_TOPK_DEV 32
+
+typedef __bf16 bf16;
+
+namespace moe {
+
+// route.hip
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
+                                int T, int d, int E, hipStream_t s);
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
+                               int32_t *counts, hipStream_t s);
+
+// permute.hip
+// Tokens per permutation block (one bitmap of local experts x tokens in LDS).
+constexpr int PERM_TB = 256;
+inline int perm_blocks(int T) { return (T + PERM_TB - 1) / PERM_TB; }
+size_t permute_ws_bytes(int T, int num_local);
+hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int k, int e0,
+                          int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
+                          hipStream_t s);
+
+// gemm.hip
+// Work items of the grouped GEMMs: (expert, first row) groups of `rows`
+// consecutive permuted rows, built on the device from the expert offsets.
+size_t gemm_plan_ws_bytes(int num_local, int max_rows, int rows_per_group);
+hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows,
+                               const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                               const uint8_t *w2s, const int32_t *off, int num_local,
+                               int max_rows, int N, int K, int act, void *out, int out_f32,
+                               int64_t ldo, int mode, void *ws, hipStream_t s);
+size_t grouped_gemm_ws_bytes(int num_local, int max_rows, int N, int mode);
+// The two halves of launch_grouped_gemm: build the work plan into `ws`, then
+// run the GEMM from a plan built for the same (offsets, max_rows, mode).
+hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int mode, void *ws,
+                            hipStream_t s);
+hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, const uint8_t *w1c,
+                           const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
+                           const int32_t *off, int num_local, int max_rows, int N, int K, int act,
+                           void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
+                           hipStream_t s);
+int resolve_mode(int mode, int num_local, int max_rows);
+
+hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,
+                                bf16 *out, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,
+                          const float *w, int T, int d, int k, void *out, int out_f32,
+                          int64_t ldo, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,147 @@
+// Dispatch planning on one GPU (P3 "Kimi K3 Day-0 适配剖析", section 四: the
+// index computation and buffer planning of dispatch, re-done for 896 experts
+// and top-16): expert offsets and a deterministic stable counting sort of the
+// row-major (token, slot) list by expert.
+//
+// A token selects k distinct experts, so inside one expert's segment the rows
+// are exactly the tokens that chose it, in increasing token order. Tokens are
+// cut into blocks of PERM_TB; per block an LDS bitmap bits[expert][token] is
+// built with integer ORs (order-independent). Popcounts of the bitmap give
+// (a) each block's per-expert count, and (b) each assignment's rank among the
+// earlier tokens of its block. A column scan over blocks turns (a) into each
+// block's base row per expert. No step depends on atomic ordering, so the
+// permutation is the same on every run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int PERM_WORDS = PERM_TB / 32;  // bitmap words per expert
+
+__device__ __forceinline__ void build_bitmap(uint32_t *bits, const int32_t *__restrict__ idx,
+                                             int T, int k, int e0, int nl, int t0)
+{
+    for (int i = threadIdx.x; i < nl * PERM_WORDS; i += blockDim.x) bits[i] = 0u;
+    __syncthreads();
+    const int tl = threadIdx.x;
+    const int t = t0 + tl;
+    if (t < T) {
+        for (int j = 0; j < k; j++) {
+            int le = idx[(int64_t)t * k + j] - e0;
+            if (le >= 0 && le < nl) atomicOr(&bits[le * PERM_WORDS + tl / 32], 1u << (tl % 32));
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(PERM_TB) void permute_count_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int e0, int nl, int32_t *__restrict__ blk)
+{
+    extern __shared__ uint32_t bits[];
+    build_bitmap(bits, idx, T, k, e0, nl, blockIdx.x * PERM_TB);
+    for (int le = threadIdx.x; le < nl; le += blockDim.x) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < PERM_WORDS; w++) c += __popc(bits[le * PERM_WORDS + w]);
+        blk[(int64_t)blockIdx.x * nl + le] = c;
+    }
+}
+
+// One workgroup: offsets over the local range, then per expert a scan of the
+// block counts (in place: blk[b][e] becomes block b's first row for e).
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    const int32_t *__restrict__ counts, int e0, int nl, int nblk, int32_t *__restrict__ off,
+    int32_t *__restrict__ blk)
+{
+    __shared__ int32_t part[1024];
+    const int tid = threadIdx.x;
+    // each thread sums a contiguous run of experts
+    const int per = (nl + 1023) / 1024;
+    const int lo = tid * per, hi = min(lo + per, nl);
+    int s = 0;
+    for (int i = lo; i < hi; i++) s += counts[e0 + i];
+    part[tid] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the 1024 partial sums
+    for (int o = 1; o < 1024; o <<= 1) {
+        int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - s;  // exclusive prefix of this thread's run
+    for (int i = lo; i < hi; i++) {
+        off[i] = run;
+        run += counts[e0 + i];
+    }
+    if (tid == 1023) off[nl] = part[1023];
+    __syncthreads();
+    for (int le = tid; le < nl; le += 1024) {
+        int r = off[le];
+        for (int b = 0; b < nblk; b++) {
+            int c = blk[(int64_t)b * nl + le];
+            blk[(int64_t)b * nl + le] = r;
+            r += c;
+        }
+    }
+}
+
+__global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
+    const int32_t *__restrict__ idx, int T, int k, int e0, int nl,
+    const int32_t *__restrict__ base, int32_t *__restrict__ perm, int32_t *__restrict__ inv)
+{
+    extern __shared__ uint32_t bits[];
+    const int t0 = blockIdx.x * PERM_TB;
+    build_bitmap(bits, idx, T, k, e0, nl, t0);
+    const int tl = threadIdx.x, t = t0 + tl;
+    if (t >= T) return;
+    const int64_t cap = (int64_t)T * k;
+    const int w = tl / 32;
+    const uint32_t below = (1u << (tl % 32)) - 1u;
+    for (int j = 0; j < k; j++) {
+        int le = idx[(int64_t)t * k + j] - e0;
+        int pos = -1;
+        if (le >= 0 && le < nl) {
+            const uint32_t *row = bits + le * PERM_WORDS;
+            int rank = __popc(row[w] & below);
+            for (int i = 0; i < w; i++) rank += __popc(row[i]);
+            int64_t p = (int64_t)base[(int64_t)blockIdx.x * nl + le] + rank;
+            if (p >= 0 && p < cap) {
+                pos = (int)p;
+                perm[pos] = t;
+            }
+        }
+        inv[(int64_t)t * k + j] = pos;
+    }
+}
+
+size_t permute_ws_bytes(int T, int num_local)
+{
+    size_t n = (size_t)perm_blocks(T) * (size_t)num_local * sizeof(int32_t);
+    return (n + 255) & ~(size_t)255;
+}
+
+hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int k, int e0,
+                          int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
+                          hipStream_t s)
+{
+    const int nblk = perm_blocks(T);
+    int32_t *blk = (int32_t *)ws;
+    const size_t lds = (size_t)num_local * PERM_WORDS * sizeof(uint32_t);
+    hipError_t e;
+    if (nblk > 0) {
+        hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k, e0,
+                           num_local, blk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, counts, e0, num_local,
+                       nblk, off, blk);
+    e = hipGetLastError();
+    if (e != hipSuccess || nblk == 0) return e;
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k, e0,
+                       num_local, (const int32_t *)blk, perm, inv);
+    return hipGetLastError();
+}
+
+}  // namespace moe

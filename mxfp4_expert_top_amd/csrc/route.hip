@@ -1,0 +1,227 @@
+// Routing kernels: router scores (a dense GEMM on the bf16 matrix cores with
+// the fp32 router weights split into three exact bf16 parts), and a
+// wavefront-per-token top-k select with softmax weights and the expert
+// histogram.
+//
+// Sources: P2 "SGLang 0.5.17：Kimi K3 原生 MXFP4 推理架构解析", section
+// "MoE 稀疏激活" (score every token against every expert, keep the best 16,
+// weight the kept experts' outputs); P1 "从Kimi K3到MiniMax-H3", section 一
+// (896 experts, 16 active, routing in the 3584-wide latent space).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router scores: logits[t][e] = sum_i x[t][i] * W[e][i] + bias[e].
+//
+// W (fp32) = hi + mid + lo exactly, each part bf16, so every product with a
+// bf16 token element is exact in fp32; the matrix cores accumulate in fp32.
+// Workgroup tile: 64 tokens x 64 experts, 4 waves, each wave 16 tokens x 64
+// experts (4 accumulator tiles). The W tile of one 128-wide K step is split
+// once into LDS (3 parts) and shared by the 4 waves; token rows come straight
+// from global memory (each row is read by one wave only).
+//
+// Contraction mapping inside a 128-wide K step: lane group g = L / 16 owns
+// K offsets [32 g, 32 g + 32); MFMA step s (0..3) takes the 8 elements
+// 32 g + 8 s .. +8, for both operands.
+// ---------------------------------------------------------------------------
+constexpr int RT_TOK = 64, RT_EXP = 64, RT_K = 128;
+
+__global__ __launch_bounds__(256) void router_logits_kernel(
+    const bf16 *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ logits, int T, int d, int E)
+{
+    // LDS: [part][expert][K] bf16, padded rows to spread banks.
+    constexpr int LDK = RT_K + 8;
+    __shared__ bf16 wpart[3][RT_EXP][LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * RT_TOK, e0 = blockIdx.y * RT_EXP;
+    const int m = lane & 15, g = lane >> 4;
+    const int tok = t0 + wave * 16 + m;
+    const bool tok_ok = tok < T;
+    const bf16 *xrow = x + (int64_t)(tok_ok ? tok : 0) * d;
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = 0; k0 < d; k0 += RT_K) {
+        // Stage and split the W tile: 64 experts x 128 K fp32 = 8192 values,
+        // 32 per thread as 8 float4 loads.
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 8; it++) {
+            int idx4 = it * 256 + tid;         // float4 index inside the tile
+            int er = idx4 / (RT_K / 4);        // expert row 0..63
+            int kc = (idx4 % (RT_K / 4)) * 4;  // K offset
+            int e = e0 + er;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < E) v = *(const float4 *)(w + (int64_t)e * d + k0 + kc);
+            float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                bf16 h, md, lo;
+                split3_bf16(vv[c], h, md, lo);
+                wpart[0][er][kc + c] = h;
+                wpart[1][er][kc + c] = md;
+                wpart[2][er][kc + c] = lo;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int kk = 32 * g + 8 * s;
+            bf16x8 a = bf16x8{};
+            if (tok_ok) a = *(const bf16x8 *)(xrow + k0 + kk);
+#pragma unroll
+            for (int nb = 0; nb < 4; nb++) {
+                const int er = nb * 16 + m;
+#pragma unroll
+                for (int p = 0; p < 3; p++) {
+                    bf16x8 b = *(const bf16x8 *)(&wpart[p][er][kk]);
+                    acc[nb] = mfma16x16x32(a, b, acc[nb]);
+                }
+            }
+        }
+    }
+    // C layout: lane holds C[4*g + i][m] for its 16x16 tile: token row
+    // 4*g+i of the wave's 16, expert column m of n-block nb.
+#pragma unroll
+    for (int nb = 0; nb < 4; nb++) {
+        const int e = e0 + nb * 16 + m;
+        if (e >= E) continue;
+        const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = t0 + wave * 16 + 4 * g + i;
+            if (t < T) logits[(int64_t)t * E + e] = acc[nb][i] + b;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k select, softmax, histogram: one wavefront per token.
+//
+// A score maps to a 64-bit key that orders (score desc, expert asc):
+// the fp32 bits made monotone (with -0 folded onto +0) in the high word, the
+// complemented expert id in the low word. k rounds of a wave-wide max pick
+// the winners best first; the winning lane retires its element.
+// ---------------------------------------------------------------------------
+constexpr int TK_MAX_PER_LANE = MOE_MAX_EXPERTS_DEV / 64;
+
+__device__ __forceinline__ uint64_t score_key(float v, int e)
+{
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) == 0) u = 0;  // -0 == +0
+    uint32_t mono = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)mono << 32) | (uint32_t)(~(uint32_t)e);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, int32_t *__restrict__ counts)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float *l = logits + (int64_t)t * E;
+
+    uint64_t key[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+        int e = i * 64 + lane;
+        key[i] = (e < E) ? score_key(l[e], e) : 0ull;  // 0 never wins over a real key
+    }
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < NPL; i++) best = key[i] > best ? key[i] : best;
+
+    float my_score = 0.f;
+    int my_idx = 0;
+    for (int j = 0; j < k; j++) {
+        uint64_t win = wave_max_u64(best);
+        int e = (int)(~(uint32_t)win);
+        if (lane == j) my_idx = e;
+        if ((e & 63) == lane) {
+            // retire the winner and recompute this lane's best
+            best = 0;
+#pragma unroll
+            for (int i = 0; i < NPL; i++) {
+                if (key[i] == win) key[i] = 0;
+                best = key[i] > best ? key[i] : best;
+            }
+        }
+    }
+    // The winners' scores, read back exactly.
+    if (lane < k) my_score = l[my_idx];
+    const float top = __shfl(my_score, 0, 64);
+    const float z = (lane < k) ? expf(my_score - top) : 0.f;
+    float sum = 0.f;
+    for (int j = 0; j < k; j++) sum += __shfl(z, j, 64);  // j order, as a plain loop
+    if (lane < k) {
+        topk_idx[(int64_t)t * k + lane] = my_idx;
+        topk_w[(int64_t)t * k + lane] = z / sum;
+        atomicAdd(&counts[my_idx], 1);
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n,
+                       v);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
+                                int T, int d, int E, hipStream_t s)
+{
+    dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
+                               int32_t *counts, hipStream_t s)
+{
+    dim3 grid((T + 3) / 4);
+    const int npl = (E + 63) / 64;
+#define TK_CASE(N)                                                                            \
+    if (npl <= N) {                                                                           \
+        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, logits, T, E, k, idx, \
+                           w, counts);                                                        \
+        return hipGetLastError();                                                             \
+    }
+    TK_CASE(2)
+    TK_CASE(4)
+    TK_CASE(8)
+    TK_CASE(14)
+    TK_CASE(16)
+    TK_CASE(TK_MAX_PER_LANE)
+#undef TK_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

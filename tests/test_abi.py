@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every entry point include/moe_mxfp4.h
+declares, and rejects bad arguments on the host before any HIP call (these
+tests need no GPU: every call here fails validation first)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import mxfp4_expert_top_amd as m
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "moe_mxfp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_layer_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_gemm_mxfp4", "moe_combine", "moe_layer"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    for n in declared_functions():
+        assert hasattr(m.lib, n), n
+    assert set(m.EXPORTED) <= set(declared_functions())
+
+
+def test_status_strings():
+    for s in range(5):
+        assert m.lib.moe_status_string(s)
+    assert m.lib.moe_status_string(99) == b"unknown status"
+    assert m.lib.moe_last_error() == b""
+
+
+P = C.c_void_p
+FAKE = C.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def test_route_validation():
+    L = m.lib
+    # k > E
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 8, 9, FAKE, FAKE, FAKE, None) == 1
+    # k < 1
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 8, 0, FAKE, FAKE, FAKE, None) == 1
+    # k > 32 unsupported
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 896, 33, FAKE, FAKE, FAKE, None) == 2
+    # E too large
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 4096, 16, FAKE, FAKE, FAKE, None) == 2
+    # d not a multiple of 128 when scores are computed
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 96, 64, 4, FAKE, FAKE, FAKE, None) == 2
+    # missing outputs
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 64, 4, None, FAKE, FAKE, None) == 1
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, 4, 128, 64, 4, FAKE, FAKE, None, None) == 1
+    # negative T
+    assert L.moe_route(FAKE, FAKE, None, FAKE, 0, -1, 128, 64, 4, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_permute_validation():
+    L = m.lib
+    ws = m.moe_permute_workspace_size(100, 64)
+    assert ws >= 64 * 4
+    # local range outside [0, E)
+    assert L.moe_permute(FAKE, FAKE, 100, 4, 64, 60, 8, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    # workspace too small
+    assert L.moe_permute(FAKE, FAKE, 100, 4, 64, 0, 64, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    # misaligned workspace
+    assert L.moe_permute(FAKE, FAKE, 100, 4, 64, 0, 64, FAKE, FAKE, FAKE, C.c_void_p(0x10004),
+                         ws, None) == 3
+
+
+def _gemm(**kw):
+    a = dict(a=FAKE, lda=256, a_rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE, off=FAKE,
+             nl=8, max_rows=64, N=128, K=256, bs=32, act=1, out=FAKE, odt=0, ldo=128, mode=0,
+             ws=None, wsb=0)
+    a.update(kw)
+    return m.lib.moe_grouped_gemm_mxfp4(*a.values(), None)
+
+
+def test_grouped_gemm_validation():
+    assert _gemm(bs=64) == 2                 # MX block must be 32
+    assert _gemm(K=96, lda=96) == 2          # K % 128
+    assert _gemm(N=96, ldo=96) == 2          # N % 64
+    assert _gemm(w2c=None, w2s=None) == 1    # GLU without the up weight
+    assert _gemm(act=0) == 1                 # plain GEMM with a second weight
+    assert _gemm(act=7) == 1
+    assert _gemm(odt=5) == 1
+    assert _gemm(lda=100) == 1               # stride not a multiple of 8
+    assert _gemm(mode=3) == 1
+    assert _gemm() == 3                      # no workspace given
+    need = m.moe_grouped_gemm_workspace_size(8, 64, 128, 0)
+    assert need > 0
+    assert _gemm(ws=C.c_void_p(0x10040), wsb=need) == 3  # misaligned
+
+
+def test_combine_and_dequant_validation():
+    L = m.lib
+    assert L.moe_combine(FAKE, 0, 96, FAKE, FAKE, 4, 90, 4, FAKE, 0, 96, None) == 2  # d % 8
+    assert L.moe_combine(FAKE, 0, 96, FAKE, FAKE, 4, 96, 33, FAKE, 0, 96, None) == 2  # k > 32
+    assert L.moe_combine(FAKE, 3, 96, FAKE, FAKE, 4, 96, 4, FAKE, 0, 96, None) == 1
+    assert L.moe_combine(FAKE, 0, 90, FAKE, FAKE, 4, 96, 4, FAKE, 0, 96, None) == 1  # ldy < d
+    assert L.moe_mxfp4_dequant(FAKE, FAKE, 4, 48, FAKE, None) == 2
+    assert L.moe_mxfp4_dequant(FAKE, FAKE, -1, 64, FAKE, None) == 1
+    # zero-size requests are no-ops that touch nothing
+    assert L.moe_mxfp4_dequant(None, None, 0, 64, None, None) == 0
+    assert L.moe_combine(None, 0, 96, None, None, 0, 96, 4, None, 0, 96, None) == 0
+
+
+def test_layer_params_and_workspace():
+    p = m.layer_params(8, 3584, 896, 16, 128)
+    n = m.moe_layer_workspace_size(p)
+    assert n >= 8 * 896 * 4 + 8 * 16 * 3584 * 4
+    bad = m.layer_params(8, 3584, 896, 16, 96)  # I % 128
+    assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    bad = m.layer_params(8, 3584, 896, 16, 128, expert_begin=800, num_local=112)
+    assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    bad = m.layer_params(8, 3584, 896, 16, 128, act=0)
+    assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    # T == 0 is a no-op: returns before looking at any pointer
+    p0 = m.layer_params(0, 3584, 896, 16, 128)
+    assert m.lib.moe_layer(C.byref(p0), *([None] * 14), 0, None, None) == 0
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.moe_combine(x, torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2), x)

@@ -1,0 +1,140 @@
+"""GPU parity of the fused layer (moe_layer) against the oracle.
+
+Small shapes: the whole oracle layer on all tokens, routing replayed on the
+GPU's fp32 scores (routing arrays bit-exact) and the output within the layer
+tolerance. Full-size workloads (the launch configuration the benchmark times):
+routing of every token replayed bit-exactly, and the output of sampled tokens
+(random, segment edges, hottest expert, no local expert) computed one by one
+by the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, LayerConfig, make_inputs
+from tests.parity_util import (LOGIT_TOL, W_TOL, assert_close_layer, host_weights, np_,
+                               oracle_rows, run_gpu_layer)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check_routing(inp, g):
+    """Replay the oracle's routing on the GPU's scores; compare bit for bit."""
+    c = inp.cfg
+    lg = np_(g["logits"])
+    r_idx, r_w = oracle.topk_softmax(lg, c.k)
+    assert np.array_equal(np_(g["idx"]), r_idx)
+    assert np.abs(np_(g["w"]) - r_w).max() <= W_TOL
+    return lg, r_idx, r_w
+
+
+def _check_scores(inp, lg, rows=None):
+    xb = inp.x if rows is None else inp.x[torch.as_tensor(rows, device=inp.x.device)]
+    ref = oracle.router_logits(xb, np_(inp.w_router), None if inp.bias is None else np_(inp.bias))
+    got = lg if rows is None else lg[rows]
+    assert (np.abs(got - ref) <= LOGIT_TOL * np.maximum(1, np.abs(ref))).all()
+
+
+SMALL = [
+    LayerConfig("g0", T=37, I=128, d=256, E=64, k=8),
+    LayerConfig("g1", T=300, I=256, d=384, E=16, k=4),
+    LayerConfig("g2", T=50, I=128, d=256, E=40, k=6, expert_begin=8, num_local=20, bias="normal"),
+    LayerConfig("g3", T=1, I=128, d=3584, E=896, k=16),
+    LayerConfig("g4", T=129, I=256, d=512, E=8, k=8),  # k == E: every expert
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_small_layer_vs_oracle(cfg, mode):
+    inp = make_inputs(cfg)
+    g = run_gpu_layer(inp.to(DEV), mode=mode)
+    lg, _, _ = _check_routing(inp, g)
+    _check_scores(inp, lg)
+    ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                       host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                       e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg)
+    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], cfg.name)
+
+
+@pytest.mark.parametrize("act", [1, 2])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_layer_act_and_dtype(act, out_dtype):
+    cfg = SMALL[0]
+    inp = make_inputs(cfg)
+    g = run_gpu_layer(inp.to(DEV), out_dtype=out_dtype, act=act)
+    lg, _, _ = _check_routing(inp, g)
+    ref = oracle.layer(inp.x, np_(inp.w_router), None, host_weights(inp.weights), E=cfg.E,
+                       k=cfg.k, I=cfg.I, logits=lg, act=act)
+    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], f"act={act}")
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    return make_inputs(CONFIGS["tiny"])
+
+
+def test_tiny_workload_full_oracle(tiny):
+    cfg = tiny.cfg
+    g = run_gpu_layer(tiny.to(DEV))
+    lg, _, _ = _check_routing(tiny, g)
+    _check_scores(tiny, lg)
+    ref = oracle.layer(tiny.x, np_(tiny.w_router), None, host_weights(tiny.weights), E=cfg.E,
+                       k=cfg.k, I=cfg.I, logits=lg)
+    assert ref["A"] == cfg.T * cfg.k
+    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], "tiny")
+
+
+def test_determinism_bitwise(tiny):
+    gi = tiny.to(DEV)
+    a = run_gpu_layer(gi)
+    b = run_gpu_layer(gi)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------- full sizes
+def _sample_tokens(cfg, idx, n_random, seed=0):
+    """Random tokens, first/last tokens, the first and last token of the
+    hottest local expert's segment, and a token with no local expert."""
+    rng = np.random.default_rng(seed)
+    toks = set(rng.choice(cfg.T, size=min(n_random, cfg.T), replace=False).tolist())
+    toks |= {0, cfg.T - 1}
+    loc = idx - cfg.expert_begin
+    is_loc = (loc >= 0) & (loc < cfg.num_local)
+    counts = np.bincount(loc[is_loc], minlength=cfg.num_local)
+    hot = int(counts.argmax())
+    users = np.nonzero((loc == hot).any(1))[0]
+    toks |= {int(users[0]), int(users[-1])}
+    none = np.nonzero(~is_loc.any(1))[0]
+    if len(none):
+        toks.add(int(none[0]))
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("name,n_random", [("decode", 10), ("prefill", 6), ("ep_share", 6),
+                                           ("long_skewed_prefill", 3)])
+def test_full_size_workload(name, n_random):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, DEV)
+    g = run_gpu_layer(inp)
+    lg, r_idx, _ = _check_routing(inp, g)
+    # scores of a few tokens against the oracle's own router product
+    _check_scores(inp, lg, rows=[0, cfg.T // 2, cfg.T - 1])
+    # dispatch arrays: the oracle's permutation of the replayed routing
+    cnt = oracle.histogram(r_idx, cfg.E)
+    off = oracle.offsets(cnt, cfg.expert_begin, cfg.num_local)
+    assert off[-1] > 0
+    toks = _sample_tokens(cfg, r_idx, n_random)
+    ref = oracle_rows(inp, r_idx, np_(g["w"]), toks)
+    got = g["out"].float().cpu().numpy()[toks]
+    assert_close_layer(got, ref, name)
+    # rows with no local expert are exact zeros
+    loc = r_idx - cfg.expert_begin
+    none = ~((loc >= 0) & (loc < cfg.num_local)).any(1)
+    if none.any():
+        assert (g["out"][torch.as_tensor(np.nonzero(none)[0], device=DEV)] == 0).all()
+    del inp, g
+    torch.cuda.empty_cache()

@@ -1,0 +1,214 @@
+"""GPU parity of each C-ABI entry point against the oracle, on seeded inputs
+that span several tiles with ragged tails, plus the degenerate cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import LayerConfig, quantize_mxfp4
+from tests.dense_ref import ACTS
+from tests.parity_util import W_TOL, LOGIT_TOL, np_, rel_l2, max_abs_rms
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mxfp4_expert_top_amd as mod
+    return mod
+
+
+# ---------------------------------------------------------------- decode
+def test_dequant_every_code_and_scale_bitexact(m):
+    # row s-2 uses scale code s (2..252); its 32-element blocks cycle all codes
+    S = np.arange(2, 253)
+    N, K = len(S), 128
+    nib = np.tile(np.arange(16), (N, K // 16))
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.repeat(S[:, None], K // 32, axis=1).astype(np.uint8)
+    out = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
+    m.moe_mxfp4_dequant(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), out)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    want = oracle.mxfp4_decode(codes, scales)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))  # -0 stays -0
+
+
+def test_dequant_random_weights_bitexact(m):
+    g = torch.Generator().manual_seed(5)
+    w = torch.randn(300, 512, generator=g) * 0.02
+    c, s = quantize_mxfp4(w)
+    out = torch.empty(300, 512, dtype=torch.bfloat16, device=DEV)
+    m.moe_mxfp4_dequant(c.to(DEV), s.to(DEV), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().numpy(), oracle.mxfp4_decode(c.numpy(), s.numpy()))
+
+
+# ---------------------------------------------------------------- routing
+def _route_gpu(m, logits_np, k, x=None, w_router=None, bias=None, given=True):
+    T, E = logits_np.shape
+    lg = torch.from_numpy(np.ascontiguousarray(logits_np)).to(DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    cnt = torch.full((E,), 12345, dtype=torch.int32, device=DEV)
+    m.moe_route(x, w_router, bias, lg, given, idx, w, cnt)
+    torch.cuda.synchronize()
+    return np_(lg), np_(idx), np_(w), np_(cnt)
+
+
+def _tie_logits(T, E, seed):
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    lg[1] = np.round(lg[1] * 2) / 2         # many exact ties
+    lg[2] = 0.0
+    lg[2, ::3] = -0.0                       # +-0: all tie
+    lg[3] = 0.75                            # all equal
+    lg[4] = rng.integers(-3, 3, size=E)
+    lg[5, E // 2:] = lg[5, : E - E // 2]    # duplicated halves
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 896, 16), (77, 64, 8), (40, 17, 1), (33, 2048, 32),
+                                   (6, 16, 16), (1, 896, 16)])
+def test_route_injected_logits_bitexact(m, T, E, k):
+    lg = _tie_logits(max(T, 6), E, T * 7 + E)[:T]
+    _, idx, w, cnt = _route_gpu(m, lg, k)
+    oi, ow = oracle.topk_softmax(lg, k)
+    assert np.array_equal(idx, oi)
+    assert np.abs(w - ow).max() <= W_TOL
+    assert np.array_equal(cnt, oracle.histogram(oi, E))
+    if k == 1:
+        assert (w == 1.0).all()
+
+
+def test_route_t0_zeroes_counts(m):
+    cnt = torch.full((64,), 7, dtype=torch.int32, device=DEV)
+    e = torch.empty(0, 4, dtype=torch.int32, device=DEV)
+    m.moe_route(None, None, None, torch.empty(0, 64, device=DEV), True, e,
+                torch.empty(0, 4, device=DEV), cnt)
+    torch.cuda.synchronize()
+    assert (np_(cnt) == 0).all()
+
+
+@pytest.mark.parametrize("T,d,E,bias", [(77, 3584, 896, False), (130, 256, 40, True),
+                                        (1, 3584, 896, True)])
+def test_router_scores_and_replay(m, T, d, E, bias):
+    from synth import make_router, make_tokens
+    cfg = LayerConfig("r", T=T, I=128, d=d, E=E, bias="normal" if bias else None)
+    x = make_tokens(cfg)
+    w_r, b = make_router(cfg)
+    lg_ref = oracle.router_logits(x, w_r.numpy(), None if b is None else b.numpy())
+    k = min(16, E)
+    lg, idx, w, cnt = _route_gpu(m, np.zeros((T, E), np.float32), k, x=x.to(DEV),
+                                 w_router=w_r.to(DEV), bias=None if b is None else b.to(DEV),
+                                 given=False)
+    assert (np.abs(lg - lg_ref) <= LOGIT_TOL * np.maximum(1, np.abs(lg_ref))).all()
+    oi, ow = oracle.topk_softmax(lg, k)  # replay on the GPU's scores
+    assert np.array_equal(idx, oi)
+    assert np.abs(w - ow).max() <= W_TOL
+    assert np.array_equal(cnt, oracle.histogram(oi, E))
+
+
+# ---------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,E,k,e0,nl", [(0, 64, 4, 0, 64), (1, 896, 16, 0, 896),
+                                         (7, 8, 2, 0, 8), (257, 896, 16, 0, 896),
+                                         (1000, 64, 4, 16, 20), (5000, 896, 16, 0, 112),
+                                         (700, 896, 16, 784, 112), (513, 32, 32, 0, 32)])
+def test_permute_bitexact(m, T, E, k, e0, nl):
+    rng = np.random.default_rng(T + E + k)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    oi, _ = oracle.topk_softmax(lg, k) if T else (np.zeros((0, k), np.int32), None)
+    cnt = oracle.histogram(oi, E) if T else np.zeros(E, np.int32)
+    off = oracle.offsets(cnt, e0, nl)
+    perm, inv = oracle.permute(oi, off, e0, nl) if T else (np.zeros(0, np.int32),
+                                                          np.zeros((0, k), np.int32))
+    g_off = torch.full((nl + 1,), -7, dtype=torch.int32, device=DEV)
+    g_perm = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+    g_inv = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    ws = m.alloc_workspace(m.moe_permute_workspace_size(T, nl), DEV)
+    m.moe_permute(torch.from_numpy(oi).to(DEV), torch.from_numpy(cnt).to(DEV), e0, nl, g_off,
+                  g_perm, g_inv, ws)
+    torch.cuda.synchronize()
+    A = int(off[-1])
+    assert np.array_equal(np_(g_off), off)
+    assert np.array_equal(np_(g_perm)[:A], perm)
+    assert (np_(g_perm)[A:] == -7).all()  # untouched beyond the local rows
+    assert np.array_equal(np_(g_inv), inv)
+
+
+# ---------------------------------------------------------------- grouped GEMM
+def _experts(num_local, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for _ in range(num_local):
+        c, s = quantize_mxfp4(torch.randn(N, K, generator=g) / np.sqrt(K))
+        out.append((c, s))
+    return torch.stack([c for c, _ in out]), torch.stack([s for _, s in out])
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("act", [0, 1, 2])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_grouped_gemm_vs_definition(m, mode, act, out_dtype):
+    rng = np.random.default_rng(act * 10 + mode)
+    nl, N, K, T = 6, 192, 384, 90
+    counts = np.array([0, 37, 1, 16, 70, 17], np.int32)  # empty, ragged, exact tiles
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16)
+    a_rows = rng.integers(0, T, size=A).astype(np.int32)
+    w1c, w1s = _experts(nl, N, K, 1)
+    w2c, w2s = _experts(nl, N, K, 2) if act else (None, None)
+    out = torch.full((A + 5, N), 7.0, dtype=out_dtype, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_workspace_size(nl, A, N, mode), DEV)
+    m.moe_grouped_gemm_mxfp4(x.to(DEV), torch.from_numpy(a_rows).to(DEV), w1c.to(DEV),
+                             w1s.to(DEV), None if w2c is None else w2c.to(DEV),
+                             None if w2s is None else w2s.to(DEV),
+                             torch.from_numpy(off).to(DEV), A, act, out, ws, mode=mode)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert (got[A:] == 7.0).all()  # rows past the last expert untouched
+    xa = x.float().numpy().astype(np.float64)[a_rows]
+    ref = np.zeros((A, N))
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        if r0 == r1:
+            continue
+        g1 = xa[r0:r1] @ oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64).T
+        if act == 0:
+            ref[r0:r1] = g1
+        else:
+            u = xa[r0:r1] @ oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64).T
+            ref[r0:r1] = ACTS[act](g1, u)
+    tol = 4e-3 if out_dtype == torch.bfloat16 else 1e-5
+    assert rel_l2(got[:A], ref) <= tol, rel_l2(got[:A], ref)
+    assert max_abs_rms(got[:A], ref) <= (3e-2 if out_dtype == torch.bfloat16 else 1e-4)
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("y_dtype,out_dtype", [(torch.float32, torch.float32),
+                                               (torch.float32, torch.bfloat16),
+                                               (torch.bfloat16, torch.float32),
+                                               (torch.bfloat16, torch.bfloat16)])
+def test_combine_vs_oracle(m, y_dtype, out_dtype):
+    rng = np.random.default_rng(3)
+    T, k, d, R = 50, 16, 3584, 600
+    y = torch.from_numpy(rng.standard_normal((R, d)).astype(np.float32)).to(y_dtype)
+    inv = rng.integers(0, R, size=(T, k)).astype(np.int32)
+    inv[rng.random((T, k)) < 0.3] = -1
+    inv[7] = -1  # a token with no local assignment
+    w = rng.random((T, k)).astype(np.float32)
+    out = torch.empty(T, d, dtype=out_dtype, device=DEV)
+    m.moe_combine(y.to(DEV), torch.from_numpy(inv).to(DEV), torch.from_numpy(w).to(DEV), out)
+    torch.cuda.synchronize()
+    ref = oracle.combine(y.float().numpy(), inv, w)
+    got = out.float().cpu().numpy()
+    assert (got[7] == 0).all()
+    if out_dtype == torch.float32:
+        assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+    else:
+        assert np.abs(got - ref).max() <= 2 ** -8 * np.abs(ref).max()
