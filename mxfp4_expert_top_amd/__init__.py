@@ -30,12 +30,13 @@ class MoeError(RuntimeError):
         self.status = status
 
 
-def _load():
-    if not _LIB_PATH.exists():
+def _load(path=None):
+    path = Path(path) if path is not None else _LIB_PATH
+    if not path.exists():
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m mxfp4_expert_top_amd.build` "
+            f"{path} is not built; run `python -m mxfp4_expert_top_amd.build` "
             "(there is no fallback path)")
-    L = C.CDLL(str(_LIB_PATH))
+    L = C.CDLL(str(path))
     p, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
     L.moe_status_string.restype = C.c_char_p
     L.moe_status_string.argtypes = [i32]

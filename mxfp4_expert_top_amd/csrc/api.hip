@@ -94,7 +94,8 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 
 // Workspace layout of moe_layer; every region 256-byte aligned.
 struct LayerWs {
-    size_t logits, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
+    size_t logits, planes, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
+    int splits;
 };
 
 LayerWs layer_ws(const moe_layer_params *p)
@@ -103,7 +104,9 @@ LayerWs layer_ws(const moe_layer_params *p)
     const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
     const size_t A = T * k;
     size_t o = 0;
+    L.splits = router_splits(p->T, p->d, p->E, 512);
     L.logits = o; o += round_up(T * E * 4);
+    L.planes = o; o += L.splits > 1 ? round_up((size_t)L.splits * T * E * 4) : 0;
     L.idx = o;    o += round_up(A * 4);
     L.w = o;      o += round_up(A * 4);
     L.counts = o; o += round_up(E * 4);
@@ -165,8 +168,9 @@ int moe_route(const void *x, const float *w_router, const float *bias, float *lo
     HIP_TRY(launch_fill_i32(expert_counts, E, 0, s));
     if (T == 0) return MOE_OK;
     if (!logits_given)
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, s));
-    HIP_TRY(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, expert_counts, s));
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, 1, s));
+    HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, T, E, k, topk_idx, topk_w,
+                                expert_counts, s));
     return MOE_OK;
 }
 
@@ -289,13 +293,25 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     HIP_TRY(launch_fill_i32(counts, p->E, 0, s));
-    HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, p->T, p->d, p->E, s));
-    HIP_TRY(launch_topk_softmax(logits, p->T, p->E, p->k, idx, w, counts, s));
+    if (L.splits > 1) {
+        // split-K router: partial planes, summed (with the bias) by the top-k
+        float *planes = (float *)(base + L.planes);
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, nullptr, planes, p->T, p->d, p->E,
+                                     L.splits, s));
+        HIP_TRY(launch_sum_planes(planes, L.splits, bias, logits, p->T, p->E, s));
+        HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w,
+                                    counts, s));
+    } else {
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, p->T, p->d, p->E,
+                                     1, s));
+        HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w,
+                                    counts, s));
+    }
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
-    HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm, inv,
-                           base + L.pws, s));
     // one work plan serves both projections (same offsets, bound and schedule)
-    HIP_TRY(launch_gemm_plan(off, p->num_local, A, p->mode, base + L.gws, s));
+    const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);
+    HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm, inv,
+                           base + L.pws, s, &plan));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
                             up_scales, off, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,

@@ -51,27 +51,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, 
                                                       const float *__restrict__ w, int d, int k,
                                                       OT *__restrict__ out, int64_t ldo)
 {
+    // blockIdx.x = token, blockIdx.y = a slice of 2048 columns; 8 columns per
+    // thread. The token's local (row, weight) pairs are compacted in slot
+    // order first, so the sum loop has no per-slot branch and its loads can
+    // be issued ahead.
     const int t = blockIdx.x;
     __shared__ int32_t rows[MOE_MAX_TOPK_DEV];
     __shared__ float wts[MOE_MAX_TOPK_DEV];
-    if (threadIdx.x < k) {
-        rows[threadIdx.x] = inv[(int64_t)t * k + threadIdx.x];
-        wts[threadIdx.x] = w[(int64_t)t * k + threadIdx.x];
+    __shared__ int n_rows;
+    if (threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        const int r = j < k ? inv[(int64_t)t * k + j] : -1;
+        const uint64_t valid = __ballot(r >= 0);
+        const int slot = __popcll(valid & ((1ull << j) - 1ull));
+        if (r >= 0) {
+            rows[slot] = r;
+            wts[slot] = w[(int64_t)t * k + j];
+        }
+        if (j == 0) n_rows = __popcll(valid);
     }
     __syncthreads();
-    for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < k; j++) {
-            const int r = rows[j];
-            if (r < 0) continue;
-            float v[8];
-            load8<YT>(y + (int64_t)r * ldy + c, v);
-            const float wj = wts[j];
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (c >= d) return;
+    const int n = n_rows;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int j = 0; j < n; j++) {
+        float v[8];
+        load8<YT>(y + (int64_t)rows[j] * ldy + c, v);
+        const float wj = wts[j];
 #pragma unroll
-            for (int i = 0; i < 8; i++) acc[i] += wj * v[i];
-        }
-        store8<OT>(out + (int64_t)t * ldo + c, acc);
+        for (int i = 0; i < 8; i++) acc[i] += wj * v[i];
     }
+    store8<OT>(out + (int64_t)t * ldo + c, acc);
 }
 
 hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,
@@ -79,7 +91,7 @@ hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *
                           int64_t ldo, hipStream_t s)
 {
     if (T <= 0) return hipSuccess;
-    dim3 grid(T), block(256);
+    dim3 grid(T, (d + 8 * 256 - 1) / (8 * 256)), block(256);
     if (y_f32 && out_f32)
         hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, (const float *)y,
                            ldy, inv, w, d, k, (float *)out, ldo);

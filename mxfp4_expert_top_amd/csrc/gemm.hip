@@ -52,22 +52,41 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int32_t *__restri
 // ---------------------------------------------------------------------------
 // Weight-streaming schedule (few rows per expert: decode batches).
 //
-// Work item = (row group of <= 16 rows of expert e, 64 weight rows). Each of
-// the 4 waves owns 16 weight rows and streams them over all of K; every
-// weight byte is read once per row group. Lane L: token row m = L % 16 of
-// the group (A operand), weight row L % 16 of the wave (B operand), lane
-// group g = L / 16.
+// Work item = (row group of <= 16 rows of expert e, a block of output
+// columns); one workgroup per item. Each wave streams ST_NS weight streams of
+// 16 rows over all of K; every weight byte is read once per row group. For a
+// GLU stage the streams pair up as (W1 rows, W2 rows) of the same output
+// columns, so act(gate, up) is applied in registers; for a plain stage each
+// stream is 16 more output columns.
 //
-// Contraction mapping per 128-wide K chunk at kc: lane group g holds the
-// 32 elements kc + 32 g .. +32, i.e. exactly one MX block, so one 16-byte
-// code load and one scale byte per lane per matrix. MFMA step s (0..3) takes
-// elements kc + 32 g + 8 s .. +8 of both operands.
+// Lane L: token row m = L % 16 of the group (A operand), weight row L % 16 of
+// each stream (B operand), lane group g = L / 16. Per 128-wide K chunk at kc,
+// lane group g holds K elements kc + 32 g .. +32 -- exactly one MX block:
+// one 16-byte code load and one scale byte per stream. MFMA step s (0..3)
+// takes elements kc + 32 g + 8 s .. +8 of both operands.
 //
-// GLU (act != NONE): the wave streams the same 16 rows of both W1 (gate) and
-// W2 (up); the two accumulators of a (token, n) pair sit in the same lane and
-// register, so act(gate, up) is applied in registers.
+// Latency: loads of chunk c + ST_D are issued right after chunk c is
+// consumed, into a ring of ST_D register slots holding codes, scales and the
+// A fragments. Vector loads complete in issue order, so the A loads ride in
+// the same ring rather than behind the code prefetch.
+//
+// Rows past the group's end load a valid row of the group instead (no branch,
+// and the repeated address coalesces); their outputs are never stored.
 // ---------------------------------------------------------------------------
-template <int ACT, typename OutT>
+#ifndef ST_NS
+#define ST_NS 4
+#endif
+#ifndef ST_DMAX
+#define ST_DMAX 4
+#endif
+
+template <int ACT>
+__host__ __device__ constexpr int stream_cols_per_wave()
+{
+    return ACT != ACT_NONE ? 8 * ST_NS : 16 * ST_NS;
+}
+
+template <int ACT, typename OutT, int D>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
@@ -76,59 +95,91 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     OutT *__restrict__ out, int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
-    const int n_groups = plan[0];
-    const int2 *items = (const int2 *)(plan + PLAN_HDR);
-    const int nblk = N / ST_NB;
-    const int total = n_groups * nblk;
+    constexpr int NS = ST_NS;
+    constexpr int COLS_W = stream_cols_per_wave<ACT>();
+    constexpr int COLS_B = 4 * COLS_W;
+    const int nblk = (N + COLS_B - 1) / COLS_B;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
+
+    const int wi = blockIdx.x;
+    if (wi >= plan[0] * nblk) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int n0 = nb * COLS_B + wave * COLS_W;
+    if (n0 >= N) return;  // N is a multiple of COLS_W, so a started wave is whole
+    const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
+    const int e = it.x, r0 = it.y;
+    const int rend = min(r0 + ST_ROWS, off[e + 1]);
+    const int rc = min(r0 + m, rend - 1);
+    const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+    const bf16 *ap = a + arow * lda + 32 * g;
+
     const int64_t code_row = K / 2, scale_row = K / 32;
-
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
-        const int grp = w / nblk, nb = w - grp * nblk;
-        const int2 it = items[grp];
-        const int e = it.x, r0 = it.y;
-        const int rend = min(r0 + ST_ROWS, off[e + 1]);
-        const int r = r0 + m;
-        const bool rv = r < rend;
-        const int64_t arow = rv ? (a_rows ? (int64_t)a_rows[r] : (int64_t)r) : 0;
-        const bf16 *ap = a + arow * lda + 32 * g;
-        const int n = nb * ST_NB + wave * 16 + m;
-        const int64_t wrow = (int64_t)e * N + n;
-        const uint8_t *c1 = w1c + wrow * code_row + 16 * g;
-        const uint8_t *s1 = w1s + wrow * scale_row;
-        const uint8_t *c2 = GLU ? w2c + wrow * code_row + 16 * g : nullptr;
-        const uint8_t *s2 = GLU ? w2s + wrow * scale_row : nullptr;
-
-        f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int kc = 0; kc < K; kc += 128) {
-            const u32x4 q1 = *(const u32x4 *)(c1 + kc / 2);
-            const float f1 = e8m0_to_f32((*(const uint32_t *)(s1 + kc / 32) >> (8 * g)) & 0xffu);
-            u32x4 q2;
-            float f2 = 0.f;
-            if constexpr (GLU) {
-                q2 = *(const u32x4 *)(c2 + kc / 2);
-                f2 = e8m0_to_f32((*(const uint32_t *)(s2 + kc / 32) >> (8 * g)) & 0xffu);
-            }
-            bf16x8 af[4];
+    const uint8_t *cp[NS];
+    const uint8_t *sp[NS];
 #pragma unroll
-            for (int s = 0; s < 4; s++)
-                af[s] = rv ? *(const bf16x8 *)(ap + kc + 8 * s) : bf16x8{};
+    for (int j = 0; j < NS; j++) {
+        const int wr = GLU ? n0 + 16 * (j / 2) + m : n0 + 16 * j + m;
+        const bool second = GLU && (j & 1);
+        const int64_t row = (int64_t)e * N + wr;
+        cp[j] = (second ? w2c : w1c) + row * code_row + 16 * g;
+        sp[j] = (second ? w2s : w1s) + row * scale_row;
+    }
+
+    const int nch = K / 128;  // a multiple of D (the launcher picks D)
+    u32x4 q[D][NS];
+    uint32_t sc[D][NS];
+    bf16x8 af[D][4];
+    f32x4 acc[NS];
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                acc1 = mfma16x16x32(af[s], mx_decode8(q1[s], f1), acc1);
-                if constexpr (GLU) acc2 = mfma16x16x32(af[s], mx_decode8(q2[s], f2), acc2);
-            }
+    for (int j = 0; j < NS; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int slot_unused, int c, u32x4 *qd, uint32_t *sd, bf16x8 *ad) {
+        (void)slot_unused;
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            qd[j] = *(const u32x4 *)(cp[j] + c * 64);
+            sd[j] = *(const uint32_t *)(sp[j] + c * 4);
         }
-        // lane holds C[4 g + i][m]: token row r0 + 4 g + i, output column n
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int row = r0 + 4 * g + i;
-            if (row < rend) {
-                float v = GLU ? act_apply<ACT>(acc1[i], acc2[i]) : acc1[i];
-                store_out<OutT>(out + (int64_t)row * ldo + n, v);
-            }
+        for (int s = 0; s < 4; s++) ad[s] = *(const bf16x8 *)(ap + c * 128 + 8 * s);
+    };
+    auto consume = [&](const u32x4 *qd, const uint32_t *sd, const bf16x8 *ad) {
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            const float f = e8m0_to_f32((sd[j] >> (8 * g)) & 0xffu);
+#pragma unroll
+            for (int s = 0; s < 4; s++) acc[j] = mfma16x16x32(ad[s], mx_decode8(qd[j][s], f), acc[j]);
+        }
+    };
+    // prologue: chunks 0 .. D-1 in flight
+#pragma unroll
+    for (int d = 0; d < D; d++) issue(d, d, q[d], sc[d], af[d]);
+    // steady state: consume chunk c, refill its slot with chunk c + D
+    for (int c0 = 0; c0 < nch - D; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+            consume(q[d], sc[d], af[d]);
+            issue(d, c0 + d + D, q[d], sc[d], af[d]);
+        }
+    }
+    // drain the last D chunks
+#pragma unroll
+    for (int d = 0; d < D; d++) consume(q[d], sc[d], af[d]);
+    // lane holds C[4 g + i][m] of each stream: token row r0 + 4 g + i
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = r0 + 4 * g + i;
+        if (row >= rend) continue;
+        OutT *orow = out + (int64_t)row * ldo;
+        if constexpr (GLU) {
+#pragma unroll
+            for (int jp = 0; jp < NS / 2; jp++)
+                store_out<OutT>(orow + n0 + 16 * jp + m,
+                                act_apply<ACT>(acc[2 * jp][i], acc[2 * jp + 1][i]));
+        } else {
+#pragma unroll
+            for (int j = 0; j < NS; j++) store_out<OutT>(orow + n0 + 16 * j + m, acc[j][i]);
         }
     }
 }
@@ -200,12 +251,24 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
                                 int max_groups, int N, int K, OutT *out, int64_t ldo,
                                 hipStream_t s)
 {
-    const int64_t bound = (int64_t)max_groups * (N / ST_NB);
-    const int64_t cap = (int64_t)device_cus() * 8;
-    const int grid = (int)(bound < cap ? bound : cap);
+    // one workgroup per (row group, column block); groups past the device-side
+    // count exit at once
+    constexpr int COLS_B = 4 * stream_cols_per_wave<ACT>();
+    const int64_t grid = (int64_t)max_groups * ((N + COLS_B - 1) / COLS_B);
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT>), dim3(grid), dim3(256), 0, s, a, lda,
-                       a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo);
+    // prefetch depth: the largest of ST_DMAX, 2, 1 that divides the chunk count
+    const int nch = K / 128;
+    const int D = (nch % ST_DMAX == 0) ? ST_DMAX : (nch % 2 == 0 ? 2 : 1);
+#define ST_LAUNCH(DD)                                                                            \
+    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD>), dim3((unsigned)grid), dim3(256), 0, s, \
+                       a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo)
+    if (D == ST_DMAX)
+        ST_LAUNCH(ST_DMAX);
+    else if (D == 2)
+        ST_LAUNCH(2);
+    else
+        ST_LAUNCH(1);
+#undef ST_LAUNCH
     return hipGetLastError();
 }
 
@@ -231,13 +294,24 @@ static hipError_t dispatch_act(int act, const bf16 *a, int64_t lda, const int32_
     }
 }
 
+GemmPlanArgs gemm_plan_args(int num_local, int max_rows, int mode, void *ws)
+{
+    const int R = rows_per_group(resolve_mode(mode, num_local, max_rows));
+    return GemmPlanArgs{(int32_t *)ws, R, max_groups_for(num_local, max_rows, R), PLAN_HDR};
+}
+
+hipError_t launch_gemm_plan_into(const int32_t *off, int num_local, const GemmPlanArgs &a,
+                                 hipStream_t s)
+{
+    hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, off, num_local,
+                       a.rows_per_group, a.max_groups, a.plan);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int mode, void *ws,
                             hipStream_t s)
 {
-    const int R = rows_per_group(resolve_mode(mode, num_local, max_rows));
-    hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, off, num_local, R,
-                       max_groups_for(num_local, max_rows, R), (int32_t *)ws);
-    return hipGetLastError();
+    return launch_gemm_plan_into(off, num_local, gemm_plan_args(num_local, max_rows, mode, ws), s);
 }
 
 hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, const uint8_t *w1c,

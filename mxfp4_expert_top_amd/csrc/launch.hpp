@@ -16,9 +16,19 @@ namespace moe {
 
 // route.hip
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+// Router scores into `splits` planes of [T][E] partial sums (splits == 1:
+// the final scores, bias included); splits must divide d / 128.
 hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
-                                int T, int d, int E, hipStream_t s);
-hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
+                                int T, int d, int E, int splits, hipStream_t s);
+// logits = sum of the planes in order + bias (E % 4 == 0).
+hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
+                             int T, int E, hipStream_t s);
+// K splits that give the router about `target_blocks` workgroups.
+int router_splits(int T, int d, int E, int target_blocks);
+// Top-k over the sum of `n_planes` score planes plus `bias` (NULL: none);
+// the summed scores go to `logits_out` when not NULL.
+hipError_t launch_topk_softmax(const float *planes, int n_planes, const float *bias,
+                               float *logits_out, int T, int E, int k, int32_t *idx, float *w,
                                int32_t *counts, hipStream_t s);
 
 // permute.hip
@@ -26,9 +36,18 @@ hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t
 constexpr int PERM_TB = 256;
 inline int perm_blocks(int T) { return (T + PERM_TB - 1) / PERM_TB; }
 size_t permute_ws_bytes(int T, int num_local);
+// Where a grouped-GEMM work plan goes and how it is cut (see gemm.hip).
+struct GemmPlanArgs {
+    int32_t *plan;
+    int rows_per_group;
+    int max_groups;
+    int hdr;
+};
+// Offsets, permutation and inverse; with `plan` also the GEMM work plan
+// (built inside the same kernel for small T).
 hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int k, int e0,
                           int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
-                          hipStream_t s);
+                          hipStream_t s, const GemmPlanArgs *plan = nullptr);
 
 // gemm.hip
 // Work items of the grouped GEMMs: (expert, first row) groups of `rows`
@@ -40,6 +59,9 @@ hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows
                                int max_rows, int N, int K, int act, void *out, int out_f32,
                                int64_t ldo, int mode, void *ws, hipStream_t s);
 size_t grouped_gemm_ws_bytes(int num_local, int max_rows, int N, int mode);
+GemmPlanArgs gemm_plan_args(int num_local, int max_rows, int mode, void *ws);
+hipError_t launch_gemm_plan_into(const int32_t *off, int num_local, const GemmPlanArgs &a,
+                                 hipStream_t s);
 // The two halves of launch_grouped_gemm: build the work plan into `ws`, then
 // run the GEMM from a plan built for the same (offsets, max_rows, mode).
 hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int mode, void *ws,

@@ -115,6 +115,89 @@ __global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
     }
 }
 
+// Small batches (T <= PERM_TB): the whole plan in one workgroup -- bitmap,
+// offsets, ranks and, when `plan` is given, the grouped-GEMM work list
+// (groups of R rows, as gemm_plan_kernel builds it).
+__device__ __forceinline__ int block_exclusive_scan_1024(int v, int *part, int &total)
+{
+    const int tid = threadIdx.x;
+    part[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        int u = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += u;
+        __syncthreads();
+    }
+    total = part[1023];
+    const int ex = part[tid] - v;
+    __syncthreads();
+    return ex;
+}
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t *__restrict__ idx, const int32_t *__restrict__ counts, int T, int k, int e0,
+    int nl, int32_t *__restrict__ off, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
+    int R, int max_groups, int32_t *__restrict__ plan, int plan_hdr)
+{
+    extern __shared__ uint32_t bits[];  // nl * PERM_WORDS
+    __shared__ int32_t part[1024];
+    __shared__ int32_t soff[MOE_MAX_EXPERTS_DEV + 1];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < nl * PERM_WORDS; i += 1024) bits[i] = 0u;
+    __syncthreads();
+    if (tid < T) {
+        for (int j = 0; j < k; j++) {
+            int le = idx[(int64_t)tid * k + j] - e0;
+            if (le >= 0 && le < nl) atomicOr(&bits[le * PERM_WORDS + tid / 32], 1u << (tid % 32));
+        }
+    }
+    // offsets: each thread owns two consecutive local experts (nl <= 2048)
+    const int i0 = 2 * tid;
+    const int c0 = i0 < nl ? counts[e0 + i0] : 0, c1 = i0 + 1 < nl ? counts[e0 + i0 + 1] : 0;
+    int total;
+    const int ex = block_exclusive_scan_1024(c0 + c1, part, total);
+    if (i0 < nl) soff[i0] = ex;
+    if (i0 + 1 < nl) soff[i0 + 1] = ex + c0;
+    if (tid == 0) soff[nl] = total;
+    __syncthreads();
+    for (int i = tid; i <= nl; i += 1024) off[i] = soff[i];
+    if (tid < T) {
+        const int64_t cap = (int64_t)T * k;
+        const int w = tid / 32;
+        const uint32_t below = (1u << (tid % 32)) - 1u;
+        for (int j = 0; j < k; j++) {
+            int le = idx[(int64_t)tid * k + j] - e0;
+            int pos = -1;
+            if (le >= 0 && le < nl) {
+                const uint32_t *row = bits + le * PERM_WORDS;
+                int rank = __popc(row[w] & below);
+                for (int i = 0; i < w; i++) rank += __popc(row[i]);
+                const int64_t p = (int64_t)soff[le] + rank;
+                if (p < cap) {
+                    pos = (int)p;
+                    perm[pos] = tid;
+                }
+            }
+            inv[(int64_t)tid * k + j] = pos;
+        }
+    }
+    if (!plan) return;
+    // grouped-GEMM work list: ceil(count / R) groups per expert, expert-major
+    const int g0 = i0 < nl ? (c0 + R - 1) / R : 0, g1 = i0 + 1 < nl ? (c1 + R - 1) / R : 0;
+    int ngroups;
+    int pos = block_exclusive_scan_1024(g0 + g1, part, ngroups);
+    int2 *items = (int2 *)(plan + plan_hdr);
+    for (int h = 0; h < 2; h++) {
+        const int i = i0 + h;
+        if (i >= nl) break;
+        const int c = h ? c1 : c0;
+        for (int r = 0; r < c; r += R, pos++)
+            if (pos < max_groups) items[pos] = make_int2(i, soff[i] + r);
+    }
+    if (tid == 0) plan[0] = min(ngroups, max_groups);
+}
+
 size_t permute_ws_bytes(int T, int num_local)
 {
     size_t n = (size_t)perm_blocks(T) * (size_t)num_local * sizeof(int32_t);
@@ -123,12 +206,19 @@ size_t permute_ws_bytes(int T, int num_local)
 
 hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int k, int e0,
                           int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
-                          hipStream_t s)
+                          hipStream_t s, const GemmPlanArgs *plan)
 {
     const int nblk = perm_blocks(T);
     int32_t *blk = (int32_t *)ws;
     const size_t lds = (size_t)num_local * PERM_WORDS * sizeof(uint32_t);
     hipError_t e;
+    if (nblk == 1 && num_local <= 1024) {  // bitmap <= 32 KB of LDS
+        hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, idx, counts, T, k, e0,
+                           num_local, off, perm, inv, plan ? plan->rows_per_group : 0,
+                           plan ? plan->max_groups : 0, plan ? plan->plan : nullptr,
+                           plan ? plan->hdr : 0);
+        return hipGetLastError();
+    }
     if (nblk > 0) {
         hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k, e0,
                            num_local, blk);
@@ -138,10 +228,15 @@ hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int 
     hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, counts, e0, num_local,
                        nblk, off, blk);
     e = hipGetLastError();
-    if (e != hipSuccess || nblk == 0) return e;
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k, e0,
-                       num_local, (const int32_t *)blk, perm, inv);
-    return hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (nblk > 0) {
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k,
+                           e0, num_local, (const int32_t *)blk, perm, inv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (plan) return launch_gemm_plan_into(off, num_local, *plan, s);
+    return hipSuccess;
 }
 
 }  // namespace moe

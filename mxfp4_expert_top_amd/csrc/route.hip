@@ -30,8 +30,14 @@ constexpr int RT_TOK = 64, RT_EXP = 64, RT_K = 128;
 
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const bf16 *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
-    float *__restrict__ logits, int T, int d, int E)
+    float *__restrict__ logits, int T, int d, int E, int k_per_split)
 {
+    // blockIdx.z selects a K range; with more than one range each writes its
+    // partial sums to its own [T][E] plane (no bias) and the top-k kernel adds
+    // the planes in order.
+    const int kbeg = blockIdx.z * k_per_split, kend = kbeg + k_per_split;
+    logits += (int64_t)blockIdx.z * T * E;
+    if (gridDim.z > 1) bias = nullptr;
     // LDS: [part][expert][K] bf16, padded rows to spread banks.
     constexpr int LDK = RT_K + 8;
     __shared__ bf16 wpart[3][RT_EXP][LDK];
@@ -47,7 +53,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 #pragma unroll
     for (int nb = 0; nb < 4; nb++) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = 0; k0 < d; k0 += RT_K) {
+    for (int k0 = kbeg; k0 < kend; k0 += RT_K) {
         // Stage and split the W tile: 64 experts x 128 K fp32 = 8192 values,
         // 32 per thread as 8 float4 loads.
         __syncthreads();
@@ -119,33 +125,69 @@ __device__ __forceinline__ uint64_t score_key(float v, int e)
     return ((uint64_t)mono << 32) | (uint32_t)(~(uint32_t)e);
 }
 
+// The score a key was built from (exact; -0 comes back as +0, which changes
+// neither the order nor exp(l - max)).
+__device__ __forceinline__ float key_score(uint64_t key)
+{
+    uint32_t mono = (uint32_t)(key >> 32);
+    uint32_t u = (mono & 0x80000000u) ? (mono & 0x7fffffffu) : ~mono;
+    return __uint_as_float(u);
+}
+
+// One DPP step: v = max(v, v taken from the lane `ctrl` names); lanes the
+// pattern leaves without a source keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false);
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
+}
+
+// Maximum over the 64 lanes, returned to every lane (wave-uniform). Within
+// each row of 16 lanes: quad swaps, half-row and row mirrors; then rows are
+// chained with the row broadcasts so lane 63 holds the maximum, which is read
+// back as a scalar.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-        uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max_step<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+    v = dpp_max_step<0x141, 0xf>(v);  // row_half_mirror
+    v = dpp_max_step<0x140, 0xf>(v);  // row_mirror
+    v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(
-    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
+    const float *__restrict__ planes, int n_planes, const float *__restrict__ bias,
+    float *__restrict__ logits_out, int T, int E, int k, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int32_t *__restrict__ counts)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *l = logits + (int64_t)t * E;
+    const float *l = planes + (int64_t)t * E;
+    const int64_t plane = (int64_t)T * E;
 
+    // scores: the planes summed in order, then the bias
     uint64_t key[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
         int e = i * 64 + lane;
-        key[i] = (e < E) ? score_key(l[e], e) : 0ull;  // 0 never wins over a real key
+        float acc = 0.f;
+        if (e < E) {
+            acc = l[e];
+            for (int p = 1; p < n_planes; p++) acc += l[p * plane + e];
+            if (bias) acc += bias[e];
+            if (logits_out) logits_out[(int64_t)t * E + e] = acc;
+        }
+        key[i] = (e < E) ? score_key(acc, e) : 0ull;  // 0 never wins over a real key
     }
     uint64_t best = 0;
 #pragma unroll
@@ -156,7 +198,10 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     for (int j = 0; j < k; j++) {
         uint64_t win = wave_max_u64(best);
         int e = (int)(~(uint32_t)win);
-        if (lane == j) my_idx = e;
+        if (lane == j) {
+            my_idx = e;
+            my_score = key_score(win);
+        }
         if ((e & 63) == lane) {
             // retire the winner and recompute this lane's best
             best = 0;
@@ -167,8 +212,6 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
             }
         }
     }
-    // The winners' scores, read back exactly.
-    if (lane < k) my_score = l[my_idx];
     const float top = __shfl(my_score, 0, 64);
     const float z = (lane < k) ? expf(my_score - top) : 0.f;
     float sum = 0.f;
@@ -178,6 +221,39 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
         topk_w[(int64_t)t * k + lane] = z / sum;
         atomicAdd(&counts[my_idx], 1);
     }
+}
+
+// Router scores from split-K planes: logits = sum of the planes in order +
+// bias. Four consecutive scores per thread, every plane's load issued before
+// the sums.
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float *__restrict__ planes,
+                                                         int n_planes, int64_t plane, int E,
+                                                         const float *__restrict__ bias,
+                                                         float *__restrict__ logits)
+{
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 >= plane) return;
+    float4 acc = *(const float4 *)(planes + i4);
+    int p = 1;
+    for (; p + 4 <= n_planes; p += 4) {
+        const float4 a = *(const float4 *)(planes + p * plane + i4);
+        const float4 b = *(const float4 *)(planes + (p + 1) * plane + i4);
+        const float4 c = *(const float4 *)(planes + (p + 2) * plane + i4);
+        const float4 d = *(const float4 *)(planes + (p + 3) * plane + i4);
+        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+        acc.x += b.x; acc.y += b.y; acc.z += b.z; acc.w += b.w;
+        acc.x += c.x; acc.y += c.y; acc.z += c.z; acc.w += c.w;
+        acc.x += d.x; acc.y += d.y; acc.z += d.z; acc.w += d.w;
+    }
+    for (; p < n_planes; p++) {
+        const float4 a = *(const float4 *)(planes + p * plane + i4);
+        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
+    }
+    if (bias) {
+        const int e = (int)(i4 % E);  // E % 4 == 0: the four scores share a row
+        acc.x += bias[e]; acc.y += bias[e + 1]; acc.z += bias[e + 2]; acc.w += bias[e + 3];
+    }
+    *(float4 *)(logits + i4) = acc;
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -196,23 +272,52 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s)
 }
 
 hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
-                                int T, int d, int E, hipStream_t s)
+                                int T, int d, int E, int splits, hipStream_t s)
 {
-    dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E);
+    dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP, splits);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E,
+                       d / splits);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
+hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
+                             int T, int E, hipStream_t s)
+{
+    const int64_t plane = (int64_t)T * E;
+    const int64_t threads = plane / 4;
+    if (threads <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       planes, n_planes, plane, E, bias, logits);
+    return hipGetLastError();
+}
+
+int router_splits(int T, int d, int E, int target_blocks)
+{
+    if (E % 4) return 1;  // the plane sum reads scores four at a time
+    // Split K while the token x expert tiles alone leave the chip idle. Each
+    // split is a whole number of 128-wide K steps.
+    const int tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
+    const int steps = d / RT_K;
+    int best = 1;
+    for (int sp = 1; sp <= steps; sp++) {
+        if (steps % sp) continue;
+        if ((int64_t)tiles * sp > target_blocks) break;
+        best = sp;
+    }
+    return best;
+}
+
+hipError_t launch_topk_softmax(const float *planes, int n_planes, const float *bias,
+                               float *logits_out, int T, int E, int k, int32_t *idx, float *w,
                                int32_t *counts, hipStream_t s)
 {
     dim3 grid((T + 3) / 4);
     const int npl = (E + 63) / 64;
-#define TK_CASE(N)                                                                            \
-    if (npl <= N) {                                                                           \
-        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, logits, T, E, k, idx, \
-                           w, counts);                                                        \
-        return hipGetLastError();                                                             \
+#define TK_CASE(N)                                                                             \
+    if (npl <= N) {                                                                            \
+        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, planes, n_planes, bias, \
+                           logits_out, T, E, k, idx, w, counts);                               \
+        return hipGetLastError();                                                              \
     }
     TK_CASE(2)
     TK_CASE(4)

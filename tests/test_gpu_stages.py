@@ -117,7 +117,9 @@ def test_router_scores_and_replay(m, T, d, E, bias):
 @pytest.mark.parametrize("T,E,k,e0,nl", [(0, 64, 4, 0, 64), (1, 896, 16, 0, 896),
                                          (7, 8, 2, 0, 8), (257, 896, 16, 0, 896),
                                          (1000, 64, 4, 16, 20), (5000, 896, 16, 0, 112),
-                                         (700, 896, 16, 784, 112), (513, 32, 32, 0, 32)])
+                                         (700, 896, 16, 784, 112), (513, 32, 32, 0, 32),
+                                         (200, 896, 16, 0, 896), (256, 64, 4, 8, 40),
+                                         (256, 1100, 16, 0, 1100), (300, 2048, 32, 0, 2048)])
 def test_permute_bitexact(m, T, E, k, e0, nl):
     rng = np.random.default_rng(T + E + k)
     lg = rng.standard_normal((T, E)).astype(np.float32)
