@@ -117,6 +117,8 @@ LayerWs layer_ws(const moe_layer_params *p)
     L.gws = o;
     o += round_up(grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
     L.h = o;      o += round_up(A * (size_t)p->I * 2);
+    // fp32 expert outputs: bf16 here would spend most of the max-abs error
+    // budget of the layer (measured 3.05e-2 rms against the 3e-2 bound)
     L.y = o;      o += round_up(A * (size_t)p->d * 4);
     L.total = o;
     return L;

@@ -185,6 +185,199 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Tiled schedule (many rows per expert: prefill).
+//
+// Workgroup tile: TL_BM = 128 permuted rows of one expert x TL_BN = 256 weight
+// rows, K step TL_BK = 64 (two MX blocks), 8 waves as 2 (rows) x 4 (weight
+// rows), each wave 64 x 64 on v_mfma_f32_32x32x16_bf16 (2 x 2 tiles). A GLU
+// tile holds 128 W1 rows and the same 128 W2 rows (128 output columns); each
+// wave takes 32 of each, so act(gate, up) is applied in registers. A plain
+// tile is 256 output columns.
+//
+// LDS per stage: the A rows as bf16 and the weight rows still as 4-bit codes
+// plus scales; each wave decodes the codes it needs into registers. Two
+// stages; the next step's global loads are in flight during the MFMAs and
+// land in the other stage, so one barrier per K step.
+//
+// MFMA operands (32x32x16): lane L supplies row L % 32 of A and column
+// L % 32 of B, 8 contraction elements of lane group h = L / 32. Inside a K
+// step, lane group h takes MX block h (elements 32 h .. 32 h + 31) and
+// sub-step s (0..3) its elements 32 h + 8 s .. +8 -- one 16-byte code read
+// and one scale byte per lane per weight tile. Result: lane L holds
+// C[8 (v / 4) + 4 h + v % 4][L % 32], v = 0..15.
+//
+// Rows past the expert's end repeat the last row (never stored); 32-row
+// sub-tiles wholly past the end skip their MFMAs.
+// ---------------------------------------------------------------------------
+constexpr int TL_BM = 128, TL_BN = 256, TL_BK = 64;
+constexpr int TL_THREADS = 512;
+constexpr int TL_APAD = 8;                   // bf16 pad per A row in LDS
+constexpr int TL_ALD = TL_BK + TL_APAD;      // 72 bf16 = 144 bytes per row
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int ACT>
+__host__ __device__ constexpr int tile_cols()
+{
+    return ACT != ACT_NONE ? TL_BN / 2 : TL_BN;
+}
+
+template <int ACT, typename OutT>
+__global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
+    const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
+    const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
+    const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
+    const int32_t *__restrict__ off, const int32_t *__restrict__ plan, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int COLS = tile_cols<ACT>();
+    __shared__ __attribute__((aligned(16))) bf16 As[2][TL_BM][TL_ALD];
+    __shared__ __attribute__((aligned(16))) uint8_t Bq[2][TL_BN][TL_BK / 2];
+    __shared__ uint8_t Bs[2][TL_BN][TL_BK / 32];
+
+    const int nblk = (N + COLS - 1) / COLS;
+    const int total = plan[0] * nblk;
+    // XCD-aware order: workgroup b runs on XCD b % 8; each XCD takes a
+    // contiguous eighth of the actual work (the device-side count, not the
+    // launch bound), so a row group's column blocks share one L2.
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int wi = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || wi >= total) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
+    const int e = it.x, r0 = it.y;
+    const int rend = min(r0 + TL_BM, off[e + 1]);
+    const int mrows = rend - r0;
+    const int n0 = nb * COLS;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t code_row = K / 2, scale_row = K / 32;
+
+    // ---- global -> LDS assignment
+    // A: thread -> row tid / 4, 32 bytes at column 16 * (tid % 4)
+    const int ar = tid >> 2, ac = (tid & 3) * 16;
+    const int arc = min(r0 + ar, rend - 1);
+    const int64_t arow = a_rows ? (int64_t)a_rows[arc] : (int64_t)arc;
+    const bf16 *ag = a + arow * lda + ac;
+    // B: thread -> weight row tid / 2 of the tile, 16 code bytes (one MX block)
+    const int br = tid >> 1, bh = tid & 1;
+    int wrow;
+    const uint8_t *wcb, *wsb;
+    if (GLU) {
+        const int n = min(n0 + (br & 127), N - 1);
+        wrow = n;
+        wcb = br < 128 ? w1c : w2c;
+        wsb = br < 128 ? w1s : w2s;
+    } else {
+        wrow = min(n0 + br, N - 1);
+        wcb = w1c;
+        wsb = w1s;
+    }
+    const int64_t wr64 = (int64_t)e * N + wrow;
+    const uint8_t *bg = wcb + wr64 * code_row + 16 * bh;
+    const uint8_t *sg = wsb + wr64 * scale_row + bh;
+
+    u32x4 ra0, ra1, rb;
+    uint8_t rs;
+    auto gload = [&](int k0) {
+        ra0 = *(const u32x4 *)(ag + k0);
+        ra1 = *(const u32x4 *)(ag + k0 + 8);
+        rb = *(const u32x4 *)(bg + k0 / 2);
+        rs = sg[k0 / 32];
+    };
+    auto lstore = [&](int st) {
+        *(u32x4 *)(&As[st][ar][ac]) = ra0;
+        *(u32x4 *)(&As[st][ar][ac + 8]) = ra1;
+        *(u32x4 *)(&Bq[st][br][16 * bh]) = rb;
+        Bs[st][br][bh] = rs;
+    };
+
+    // ---- wave tiles
+    const int h = lane >> 5, l32 = lane & 31;
+    // weight-row tiles of this wave inside the LDS tile
+    int bt[2];
+    if (GLU) {
+        bt[0] = 32 * wn;        // W1 rows -> output columns n0 + 32 wn + l32
+        bt[1] = 128 + 32 * wn;  // the same columns of W2
+    } else {
+        bt[0] = 64 * wn;
+        bt[1] = 64 * wn + 32;
+    }
+    const bool mt_on[2] = {wm * 64 < mrows, wm * 64 + 32 < mrows};
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+    const int nk = K / TL_BK;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+        const int st = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * TL_BK);
+        if (mt_on[0]) {
+            u32x4 q[2];
+            float f[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int row = bt[j] + l32;
+                q[j] = *(const u32x4 *)(&Bq[st][row][16 * h]);
+                f[j] = e8m0_to_f32(Bs[st][row][h]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const bf16x8 b0 = mx_decode8(q[0][s], f[0]), b1 = mx_decode8(q[1][s], f[1]);
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    if (!mt_on[i]) continue;
+                    const bf16x8 af =
+                        *(const bf16x8 *)(&As[st][wm * 64 + 32 * i + l32][32 * h + 8 * s]);
+                    acc[i][0] = mfma32x32x16(af, b0, acc[i][0]);
+                    acc[i][1] = mfma32x32x16(af, b1, acc[i][1]);
+                }
+            }
+        }
+        if (kt + 1 < nk) lstore(st ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        if (!mt_on[i]) continue;
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int rl = wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (rl >= mrows) continue;
+            OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+            if constexpr (GLU) {
+                const int col = n0 + 32 * wn + l32;
+                if (col < N) store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int col = n0 + 64 * wn + 32 * j + l32;
+                    if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone decode of an MXFP4 matrix to bf16 (8 elements per thread).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint8_t *__restrict__ codes,
@@ -216,15 +409,18 @@ static int device_cus()
     return cus;
 }
 
+// Schedule choice from host-known sizes only: the mean rows per local expert.
+// Below TILE_MIN_ROWS the weight-streaming schedule (weights read once per 16
+// rows) wins; above it the tiled schedule (once per 128 rows, LDS reuse).
+constexpr int TILE_MIN_ROWS = 48;
+
 int resolve_mode(int mode, int num_local, int max_rows)
 {
-    (void)num_local;
-    (void)max_rows;
-    if (mode == 1 || mode == 2) return 1;
-    return 1;
+    if (mode == 1 || mode == 2) return mode;
+    return (int64_t)max_rows >= (int64_t)TILE_MIN_ROWS * num_local ? 2 : 1;
 }
 
-static int rows_per_group(int mode) { return mode == 2 ? 128 : ST_ROWS; }
+static int rows_per_group(int mode) { return mode == 2 ? TL_BM : ST_ROWS; }
 
 static int max_groups_for(int num_local, int max_rows, int R)
 {
@@ -272,26 +468,45 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
     return hipGetLastError();
 }
 
+template <int ACT, typename OutT>
+static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
+                              const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                              const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                              int max_groups, int N, int K, OutT *out, int64_t ldo, hipStream_t s)
+{
+    constexpr int COLS = tile_cols<ACT>();
+    const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
+    if (grid <= 0) return hipSuccess;
+    // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
+    // a grid of 8 * ceil(bound / 8) blocks covers every work item
+    const int64_t G = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT>), dim3((unsigned)G), dim3(TL_THREADS), 0, s, a,
+                       lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo);
+    return hipGetLastError();
+}
+
 template <typename OutT>
-static hipError_t dispatch_act(int act, const bf16 *a, int64_t lda, const int32_t *a_rows,
+static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, const int32_t *a_rows,
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                const uint8_t *w2s, const int32_t *off, const int32_t *plan,
                                int max_groups, int N, int K, OutT *out, int64_t ldo,
                                hipStream_t s)
 {
+#define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups, N, K, out, ldo, s
     switch (act) {
     case ACT_NONE:
-        return launch_stream<ACT_NONE, OutT>(a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,
-                                             max_groups, N, K, out, ldo, s);
+        return md == 2 ? launch_tile<ACT_NONE, OutT>(MOE_GEMM_ARGS)
+                       : launch_stream<ACT_NONE, OutT>(MOE_GEMM_ARGS);
     case ACT_SILU_MUL:
-        return launch_stream<ACT_SILU_MUL, OutT>(a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,
-                                                 max_groups, N, K, out, ldo, s);
+        return md == 2 ? launch_tile<ACT_SILU_MUL, OutT>(MOE_GEMM_ARGS)
+                       : launch_stream<ACT_SILU_MUL, OutT>(MOE_GEMM_ARGS);
     case ACT_GELU_TANH_MUL:
-        return launch_stream<ACT_GELU_TANH_MUL, OutT>(a, lda, a_rows, w1c, w1s, w2c, w2s, off,
-                                                      plan, max_groups, N, K, out, ldo, s);
+        return md == 2 ? launch_tile<ACT_GELU_TANH_MUL, OutT>(MOE_GEMM_ARGS)
+                       : launch_stream<ACT_GELU_TANH_MUL, OutT>(MOE_GEMM_ARGS);
     default:
         return hipErrorInvalidValue;
     }
+#undef MOE_GEMM_ARGS
 }
 
 GemmPlanArgs gemm_plan_args(int num_local, int max_rows, int mode, void *ws)
@@ -324,10 +539,10 @@ hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, co
     const int max_groups = max_groups_for(num_local, max_rows, rows_per_group(md));
     const int32_t *plan = (const int32_t *)plan_ws;
     if (out_f32)
-        return dispatch_act<float>(act, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups,
-                                   N, K, (float *)out, ldo, s);
-    return dispatch_act<bf16>(act, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups, N,
-                              K, (bf16 *)out, ldo, s);
+        return dispatch_act<float>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,
+                                   max_groups, N, K, (float *)out, ldo, s);
+    return dispatch_act<bf16>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups,
+                              N, K, (bf16 *)out, ldo, s);
 }
 
 hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows,
