@@ -39,8 +39,8 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="GEMM schedule: 0 auto, 1 stream, 2 tiled")
     ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens the oracle CPU baseline evaluates (0 = skip)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes of the dominant kernel")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -98,8 +98,46 @@ def cpu_baseline(inp, n_tokens):
                       f"single-threaded fp32 C; {dt:.1f} s"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_stream_gate_up_decode_traffic.txt")
+GEMM_SRC = os.path.join(ROOT, "mxfp4_expert_top_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, or None if the kernel source changed since it was taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != src or "bytes_per_launch" not in fields:
+        return None
+    return int(float(fields["bytes_per_launch"]))
+
+
+def copy_probe(mib):
+    """A plain device-to-device copy of `mib` MiB, five times: the reference
+    the HBM byte counters are scaled by."""
+    n = mib * 2**20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+
+
 def main():
     args = parse()
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this layer runs on one GPU; --gpus must be 1 "
                           "(multi-GPU sharding is described, not built)"}))
@@ -150,9 +188,7 @@ def main():
     lb, lf, gb, gf = algorithmic(cfg, A, U)
 
     gu_s = stage_ms["gate_up"] / 1e3
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get("bytes_per_launch")
+    traffic = measured_traffic()
     roof = {"kernel": "gemm_stream_kernel<SILU_MUL> (gate/up projection)", "bound": "hbm",
             "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic,

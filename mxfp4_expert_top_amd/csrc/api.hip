@@ -94,8 +94,9 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 
 // Workspace layout of moe_layer; every region 256-byte aligned.
 struct LayerWs {
-    size_t logits, planes, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
+    size_t logits, planes, wsplit, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
     int splits;
+    bool tiled_router;
 };
 
 LayerWs layer_ws(const moe_layer_params *p)
@@ -104,9 +105,12 @@ LayerWs layer_ws(const moe_layer_params *p)
     const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
     const size_t A = T * k;
     size_t o = 0;
-    L.splits = router_splits(p->T, p->d, p->E, 512);
+    L.tiled_router = p->T >= ROUTER_TILE_MIN_T && p->d % 64 == 0;
+    L.splits = L.tiled_router ? router_tile_splits(p->T, p->d, p->E, 512)
+                              : router_splits(p->T, p->d, p->E, 512);
     L.logits = o; o += round_up(T * E * 4);
     L.planes = o; o += L.splits > 1 ? round_up((size_t)L.splits * T * E * 4) : 0;
+    L.wsplit = o; o += L.tiled_router ? round_up(3 * E * (size_t)p->d * 2) : 0;
     L.idx = o;    o += round_up(A * 4);
     L.w = o;      o += round_up(A * 4);
     L.counts = o; o += round_up(E * 4);
@@ -295,20 +299,20 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
     HIP_TRY(launch_fill_i32(counts, p->E, 0, s));
-    if (L.splits > 1) {
-        // split-K router: partial planes, summed (with the bias) by the top-k
-        float *planes = (float *)(base + L.planes);
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, nullptr, planes, p->T, p->d, p->E,
-                                     L.splits, s));
-        HIP_TRY(launch_sum_planes(planes, L.splits, bias, logits, p->T, p->E, s));
-        HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w,
-                                    counts, s));
+    float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
+    const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
+    if (L.tiled_router) {
+        bf16 *wp = (bf16 *)(base + L.wsplit);
+        HIP_TRY(launch_split_router(w_router, p->E, p->d, wp, s));
+        HIP_TRY(launch_router_tile((const bf16 *)x, wp, b_in_gemm, planes, p->T, p->d, p->E,
+                                   L.splits, s));
     } else {
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, p->T, p->d, p->E,
-                                     1, s));
-        HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w,
-                                    counts, s));
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
+                                     p->E, L.splits, s));
     }
+    // split-K planes are summed in a fixed order (bias added there)
+    if (L.splits > 1) HIP_TRY(launch_sum_planes(planes, L.splits, bias, logits, p->T, p->E, s));
+    HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w, counts, s));
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);

@@ -23,6 +23,14 @@ hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias
 // logits = sum of the planes in order + bias (E % 4 == 0).
 hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
                              int T, int E, hipStream_t s);
+// Larger batches: fp32 router weights -> three exact bf16 planes [3][E][d],
+// then a tiled bf16 GEMM over K' = 3 d into `splits` planes of [T][E].
+hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s);
+int router_tile_splits(int T, int d, int E, int target_blocks);
+hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, float *logits,
+                              int T, int d, int E, int splits, hipStream_t s);
+// Batches at or above this many tokens use the tiled router.
+constexpr int ROUTER_TILE_MIN_T = 512;
 // K splits that give the router about `target_blocks` workgroups.
 int router_splits(int T, int d, int E, int target_blocks);
 // Top-k over the sum of `n_planes` score planes plus `bias` (NULL: none);

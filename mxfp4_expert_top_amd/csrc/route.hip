@@ -108,6 +108,131 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Router scores for larger batches: the fp32 weights are split once into
+// three bf16 planes Wp[p][e][i] (hi, mid, lo; exact sum), then
+//   logits[t][e] = sum_p sum_i x[t][i] * Wp[p][e][i]  (+ bias)
+// is one bf16 GEMM over K' = 3 d on the 32x32x16 matrix cores. Workgroup
+// tile 128 tokens x 128 experts, K step 64, both operands double-buffered in
+// LDS, 4 waves of 64 x 64. blockIdx.y splits K' into planes of partial sums
+// when the tile grid alone is too small for the chip.
+// ---------------------------------------------------------------------------
+constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 64, RG_LD = RG_BK + 8;
+
+__global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ w,
+                                                           int64_t n, bf16 *__restrict__ wp)
+{
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= n) return;
+    const float4 v = *(const float4 *)(w + i);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        bf16 h, md, lo;
+        split3_bf16(vv[c], h, md, lo);
+        wp[i + c] = h;
+        wp[n + i + c] = md;
+        wp[2 * n + i + c] = lo;
+    }
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 2) void router_tile_kernel(
+    const bf16 *__restrict__ x, const bf16 *__restrict__ wp, const float *__restrict__ bias,
+    float *__restrict__ logits, int T, int d, int E, int ksteps_per_split)
+{
+    __shared__ __attribute__((aligned(16))) bf16 As[2][RG_BM][RG_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Bs[2][RG_BN][RG_LD];
+    const int n_nb = (E + RG_BN - 1) / RG_BN;
+    const int mb = blockIdx.x / n_nb, nb = blockIdx.x - mb * n_nb;
+    const int t0 = mb * RG_BM, e0 = nb * RG_BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int steps_d = d / RG_BK;
+    const int kt0 = blockIdx.y * ksteps_per_split, kt1 = kt0 + ksteps_per_split;
+    logits += (int64_t)blockIdx.y * T * E;
+    if (gridDim.y > 1) bias = nullptr;
+
+    // global -> LDS: thread -> row tid / 2, 64 bytes at column 32 * (tid % 2)
+    const int lr = tid >> 1, lc = (tid & 1) * 32;
+    const bf16 *xa = x + (int64_t)min(t0 + lr, T - 1) * d + lc;
+    const int eb = min(e0 + lr, E - 1);
+    u32x4 ra[4], rb[4];
+    auto gload = [&](int kt) {
+        const int p = kt / steps_d, k0 = (kt - p * steps_d) * RG_BK;
+        const bf16 *wb = wp + ((int64_t)p * E + eb) * d + lc + k0;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            ra[c] = *(const u32x4 *)(xa + k0 + 8 * c);
+            rb[c] = *(const u32x4 *)(wb + 8 * c);
+        }
+    };
+    auto lstore = [&](int st) {
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            *(u32x4 *)(&As[st][lr][lc + 8 * c]) = ra[c];
+            *(u32x4 *)(&Bs[st][lr][lc + 8 * c]) = rb[c];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+    const bool mt_on[2] = {t0 + wm * 64 < T, t0 + wm * 64 + 32 < T};
+
+    gload(kt0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; kt++) {
+        const int st = (kt - kt0) & 1;
+        if (kt + 1 < kt1) gload(kt + 1);
+        if (mt_on[0]) {
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                bf16x8 b[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    b[j] = *(const bf16x8 *)(&Bs[st][wn * 64 + 32 * j + l32][32 * h + 8 * s]);
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+                    if (!mt_on[i]) continue;
+                    const bf16x8 a = *(const bf16x8 *)(&As[st][wm * 64 + 32 * i + l32][32 * h + 8 * s]);
+#pragma unroll
+                    for (int j = 0; j < 2; j++) acc[i][j] = mfma32x32x16(a, b[j], acc[i][j]);
+                }
+            }
+        }
+        if (kt + 1 < kt1) lstore(st ^ 1);
+        __syncthreads();
+    }
+    // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        if (!mt_on[i]) continue;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int e = e0 + wn * 64 + 32 * j + l32;
+            if (e >= E) continue;
+            const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int t = t0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (t < T) logits[(int64_t)t * E + e] = acc[i][j][v] + b;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Top-k select, softmax, histogram: one wavefront per token.
 //
 // A score maps to a 64-bit key that orders (score desc, expert asc):
@@ -288,6 +413,38 @@ hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bia
     if (threads <= 0) return hipSuccess;
     hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                        planes, n_planes, plane, E, bias, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s)
+{
+    const int64_t n = (int64_t)E * d;
+    hipLaunchKernelGGL(split_router_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                       w, n, wp);
+    return hipGetLastError();
+}
+
+int router_tile_splits(int T, int d, int E, int target_blocks)
+{
+    const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
+    const int steps = 3 * (d / RG_BK);
+    if (E % 4) return 1;
+    int best = 1;
+    for (int sp = 1; sp <= steps; sp++) {
+        if (steps % sp) continue;
+        if ((int64_t)tiles * sp > target_blocks) break;
+        best = sp;
+    }
+    return best;
+}
+
+hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, float *logits,
+                              int T, int d, int E, int splits, hipStream_t s)
+{
+    const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
+    const int steps = 3 * (d / RG_BK);
+    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), 0, s, x, wp, bias,
+                       logits, T, d, E, steps / splits);
     return hipGetLastError();
 }
 

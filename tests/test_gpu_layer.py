@@ -43,6 +43,9 @@ SMALL = [
     LayerConfig("g2", T=50, I=128, d=256, E=40, k=6, expert_begin=8, num_local=20, bias="normal"),
     LayerConfig("g3", T=1, I=128, d=3584, E=896, k=16),
     LayerConfig("g4", T=129, I=256, d=512, E=8, k=8),  # k == E: every expert
+    # T >= 512: the tiled router (split-K planes, bias, E not a tile multiple)
+    LayerConfig("g5", T=700, I=128, d=256, E=100, k=6, bias="normal"),
+    LayerConfig("g6", T=1030, I=256, d=384, E=40, k=4, expert_begin=4, num_local=30),
 ]
 
 
