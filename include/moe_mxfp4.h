@@ -42,7 +42,8 @@
  * 2 <= s <= 252, the codes of every finite fp32 block whose largest
  * magnitude is at least 2^-123: s = 255 is NaN, s >= 253 can overflow,
  * s <= 1 reaches subnormals). Element value =
- * E2M1(code) * 2^(s-127). Experts are stacked: [num_local][N][...].
+ * E2M1(code) * 2^(s-127). Experts are stacked: [num_local][N][...]; code and
+ * scale arrays start 16-byte aligned.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -76,6 +77,7 @@ enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2
 #define MOE_MX_BLOCK 32
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_EXPERTS 2048
+#define MOE_MAX_K 8192 /* contraction length of one expert projection (d and I) */
 
 /* ------------------------------------------------------------------------
  * moe_route -- router scores, top-k select, softmax over the selected scores,
@@ -152,8 +154,9 @@ int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, in
  *   ws / ws_bytes: scratch of moe_grouped_gemm_workspace_size(...) bytes (the
  *         device-built work list)
  * Requirements: lda >= K and ldo >= N, both multiples of 8; a_rows entries
- * index valid rows of `a`.
- * Errors: block_size != 32, K % 128 != 0 or N % 64 != 0 -> UNSUPPORTED;
+ * index valid rows of `a`; code and scale arrays 16-byte aligned.
+ * Errors: block_size != 32, K % 128 != 0, N % 64 != 0 or K > MOE_MAX_K ->
+ * UNSUPPORTED;
  * a GLU act without w2, or w2 with MOE_ACT_NONE -> INVALID_ARG.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode);

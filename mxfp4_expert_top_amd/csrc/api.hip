@@ -72,7 +72,7 @@ int check_gemm(const void *a, int64_t lda, const uint8_t *w1c, const uint8_t *w1
           MOE_ERR_INVALID_ARG);
     CHECK(out_dtype == MOE_DT_BF16 || out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
     CHECK(block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
-    CHECK(K % 128 == 0 && N % 64 == 0, MOE_ERR_UNSUPPORTED);
+    CHECK(K % 128 == 0 && N % 64 == 0 && K <= MOE_MAX_K, MOE_ERR_UNSUPPORTED);
     if (act == MOE_ACT_NONE)
         CHECK(!w2c && !w2s, MOE_ERR_INVALID_ARG);
     else
@@ -80,8 +80,8 @@ int check_gemm(const void *a, int64_t lda, const uint8_t *w1c, const uint8_t *w1
     if (max_rows == 0) return MOE_OK;
     CHECK(a && w1c && w1s && off && out, MOE_ERR_INVALID_ARG);
     CHECK(lda >= K && lda % 8 == 0 && ldo >= N && ldo % 8 == 0, MOE_ERR_INVALID_ARG);
-    CHECK(aligned(a, 16) && aligned(w1c, 16) && aligned(w1s, 4), MOE_ERR_INVALID_ARG);
-    if (w2c) CHECK(aligned(w2c, 16) && aligned(w2s, 4), MOE_ERR_INVALID_ARG);
+    CHECK(aligned(a, 16) && aligned(w1c, 16) && aligned(w1s, 16), MOE_ERR_INVALID_ARG);
+    if (w2c) CHECK(aligned(w2c, 16) && aligned(w2s, 16), MOE_ERR_INVALID_ARG);
     return MOE_OK;
 }
 
@@ -141,6 +141,7 @@ int check_layer_params(const moe_layer_params *p)
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
     CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
     CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
+    CHECK(p->d <= MOE_MAX_K && p->I <= MOE_MAX_K, MOE_ERR_UNSUPPORTED);
     CHECK((int64_t)p->T * p->k <= INT32_MAX / 2, MOE_ERR_UNSUPPORTED);
     return MOE_OK;
 }
@@ -277,7 +278,7 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
           MOE_ERR_INVALID_ARG);
     CHECK(aligned(x, 16) && aligned(out, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG);
     CHECK(aligned(gate_codes, 16) && aligned(up_codes, 16) && aligned(down_codes, 16) &&
-              aligned(gate_scales, 4) && aligned(up_scales, 4) && aligned(down_scales, 4),
+              aligned(gate_scales, 16) && aligned(up_scales, 16) && aligned(down_scales, 16),
           MOE_ERR_INVALID_ARG);
     const LayerWs L = layer_ws(p);
     rc = check_ws(ws, ws_bytes, L.total);

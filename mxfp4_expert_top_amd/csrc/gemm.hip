@@ -15,7 +15,6 @@ namespace moe {
 
 constexpr int PLAN_HDR = 64;  // int32 slots before the work items
 constexpr int ST_ROWS = 16;   // streaming schedule: permuted rows per group
-constexpr int ST_NB = 64;     // streaming schedule: weight rows per workgroup
 
 // ---------------------------------------------------------------------------
 // Work plan: groups of up to R consecutive rows of one expert, expert-major.
@@ -79,6 +78,19 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int32_t *__restri
 #ifndef ST_DMAX
 #define ST_DMAX 4
 #endif
+#ifndef ST_NT
+#define ST_NT 0
+#endif
+
+// Weight codes and scales are read once per row group: with ST_NT they are
+// loaded with the non-temporal hint so the stream does not push the reused
+// token rows out of the caches.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T *p)
+{
+    if constexpr (ST_NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
 
 template <int ACT>
 __host__ __device__ constexpr int stream_cols_per_wave()
@@ -98,6 +110,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     constexpr int NS = ST_NS;
     constexpr int COLS_W = stream_cols_per_wave<ACT>();
     constexpr int COLS_B = 4 * COLS_W;
+    // the scales of the workgroup's weight rows, staged in LDS (see below)
+    extern __shared__ uint32_t sscale[];
     const int nblk = (N + COLS_B - 1) / COLS_B;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m = lane & 15, g = lane >> 4;
@@ -105,8 +119,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const int wi = blockIdx.x;
     if (wi >= plan[0] * nblk) return;
     const int grp = wi / nblk, nb = wi - grp * nblk;
-    const int n0 = nb * COLS_B + wave * COLS_W;
-    if (n0 >= N) return;  // N is a multiple of COLS_W, so a started wave is whole
+    const int nb0 = nb * COLS_B;                 // first output column of the workgroup
+    const int n0 = nb0 + wave * COLS_W;          // first output column of the wave
+    const bool wave_on = n0 < N;                 // N is a multiple of COLS_W
     const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
     const int e = it.x, r0 = it.y;
     const int rend = min(r0 + ST_ROWS, off[e + 1]);
@@ -114,58 +129,77 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
     const bf16 *ap = a + arow * lda + 32 * g;
 
-    const int64_t code_row = K / 2, scale_row = K / 32;
+    // Scales: one E8M0 byte per 32 weights. Read piecemeal inside the K loop
+    // they would be fetched many times over (a 128-byte line holds about one
+    // row's worth and the code stream evicts it between reads), so the
+    // workgroup first copies the scales of all its weight rows -- one
+    // contiguous block per weight matrix -- into LDS with 16-byte loads.
+    const int sbw = K / 128;                                    // scale dwords per row
+    const int rows_b = COLS_B;                                  // weight rows per matrix block
+    const int rows_v = min(rows_b, N - nb0);                    // rows inside the matrix
+    const int nmat = GLU ? 2 : 1;
+    {
+        const int per_mat4 = rows_v * sbw / 4;                  // uint4 per matrix (rows_v*sbw % 4 == 0)
+        for (int i = threadIdx.x; i < nmat * per_mat4; i += blockDim.x) {
+            const int mat = i / per_mat4, r = i - mat * per_mat4;
+            const uint8_t *base = (mat ? w2s : w1s) + ((int64_t)e * N + nb0) * (K / 32);
+            *(u32x4 *)(&sscale[mat * rows_b * sbw + 4 * r]) = *(const u32x4 *)(base + 16 * r);
+        }
+    }
+
+    const int64_t code_row = K / 2;
     const uint8_t *cp[NS];
-    const uint8_t *sp[NS];
+    int srow[NS];  // dword offset of each stream's scale row in LDS
 #pragma unroll
     for (int j = 0; j < NS; j++) {
         const int wr = GLU ? n0 + 16 * (j / 2) + m : n0 + 16 * j + m;
         const bool second = GLU && (j & 1);
-        const int64_t row = (int64_t)e * N + wr;
+        const int64_t row = (int64_t)e * N + (wave_on ? wr : 0);
         cp[j] = (second ? w2c : w1c) + row * code_row + 16 * g;
-        sp[j] = (second ? w2s : w1s) + row * scale_row;
+        srow[j] = ((second ? 1 : 0) * rows_b + (wr - nb0)) * sbw;
     }
 
     const int nch = K / 128;  // a multiple of D (the launcher picks D)
     u32x4 q[D][NS];
-    uint32_t sc[D][NS];
     bf16x8 af[D][4];
     f32x4 acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int slot_unused, int c, u32x4 *qd, uint32_t *sd, bf16x8 *ad) {
-        (void)slot_unused;
+    auto issue = [&](int c, u32x4 *qd, bf16x8 *ad) {
 #pragma unroll
-        for (int j = 0; j < NS; j++) {
-            qd[j] = *(const u32x4 *)(cp[j] + c * 64);
-            sd[j] = *(const uint32_t *)(sp[j] + c * 4);
-        }
+        for (int j = 0; j < NS; j++) qd[j] = *(const u32x4 *)(cp[j] + c * 64);
 #pragma unroll
         for (int s = 0; s < 4; s++) ad[s] = *(const bf16x8 *)(ap + c * 128 + 8 * s);
     };
-    auto consume = [&](const u32x4 *qd, const uint32_t *sd, const bf16x8 *ad) {
+    auto consume = [&](int c, const u32x4 *qd, const bf16x8 *ad) {
 #pragma unroll
         for (int j = 0; j < NS; j++) {
-            const float f = e8m0_to_f32((sd[j] >> (8 * g)) & 0xffu);
+            const uint32_t sw = sscale[srow[j] + c];
+            const float f = e8m0_to_f32((sw >> (8 * g)) & 0xffu);
 #pragma unroll
             for (int s = 0; s < 4; s++) acc[j] = mfma16x16x32(ad[s], mx_decode8(qd[j][s], f), acc[j]);
         }
     };
-    // prologue: chunks 0 .. D-1 in flight
+    // prologue: chunks 0 .. D-1 in flight (behind the scale copy's loads)
+    if (wave_on) {
 #pragma unroll
-    for (int d = 0; d < D; d++) issue(d, d, q[d], sc[d], af[d]);
+        for (int d = 0; d < D; d++) issue(d, q[d], af[d]);
+    }
+    __syncthreads();  // scales in LDS
+    if (!wave_on) return;
     // steady state: consume chunk c, refill its slot with chunk c + D
     for (int c0 = 0; c0 < nch - D; c0 += D) {
 #pragma unroll
         for (int d = 0; d < D; d++) {
-            consume(q[d], sc[d], af[d]);
-            issue(d, c0 + d + D, q[d], sc[d], af[d]);
+            consume(c0 + d, q[d], af[d]);
+            issue(c0 + d + D, q[d], af[d]);
         }
     }
     // drain the last D chunks
 #pragma unroll
-    for (int d = 0; d < D; d++) consume(q[d], sc[d], af[d]);
+    for (int d = 0; d < D; d++) consume(nch - D + d, q[d], af[d]);
+
     // lane holds C[4 g + i][m] of each stream: token row r0 + 4 g + i
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -455,9 +489,10 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
     // prefetch depth: the largest of ST_DMAX, 2, 1 that divides the chunk count
     const int nch = K / 128;
     const int D = (nch % ST_DMAX == 0) ? ST_DMAX : (nch % 2 == 0 ? 2 : 1);
+    const size_t lds = (size_t)(ACT != ACT_NONE ? 2 : 1) * COLS_B * (K / 32);
 #define ST_LAUNCH(DD)                                                                            \
-    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD>), dim3((unsigned)grid), dim3(256), 0, s, \
-                       a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo)
+    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD>), dim3((unsigned)grid), dim3(256), lds, \
+                       s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo)
     if (D == ST_DMAX)
         ST_LAUNCH(ST_DMAX);
     else if (D == 2)

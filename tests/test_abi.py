@@ -93,6 +93,8 @@ def test_grouped_gemm_validation():
     assert _gemm(odt=5) == 1
     assert _gemm(lda=100) == 1               # stride not a multiple of 8
     assert _gemm(mode=3) == 1
+    assert _gemm(K=8320, lda=8320) == 2      # K > MOE_MAX_K
+    assert _gemm(w1s=C.c_void_p(0x10004)) == 1  # scales not 16-byte aligned
     assert _gemm() == 3                      # no workspace given
     need = m.moe_grouped_gemm_workspace_size(8, 64, 128, 0)
     assert need > 0
@@ -119,6 +121,8 @@ def test_layer_params_and_workspace():
     bad = m.layer_params(8, 3584, 896, 16, 96)  # I % 128
     assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
     bad = m.layer_params(8, 3584, 896, 16, 128, expert_begin=800, num_local=112)
+    assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
+    bad = m.layer_params(8, 3584, 896, 16, 8320)  # I > MOE_MAX_K
     assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
     bad = m.layer_params(8, 3584, 896, 16, 128, act=0)
     assert m.lib.moe_layer_workspace_size(C.byref(bad)) == 0
