@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--mode", type=int, default=0, help="GEMM schedule: 0 auto, 1 stream, 2 tiled")
     ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens the oracle CPU baseline evaluates (0 = skip)")
+    ap.add_argument("--weights", default="packed", choices=["packed", "ocp"],
+                    help="expert weight layout: converted at load (packed) or canonical")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -149,15 +151,23 @@ def main():
     torch.cuda.set_device(0)
     dev = "cuda:0"
     inp = make_inputs(cfg, dev)
+    packed = args.weights == "packed"
+    canonical = inp.weights  # the oracle reads the canonical layout
+    if packed:  # the load-time conversion, outside the timed region
+        layer_weights = m.prepack_weights(inp.weights)
+        torch.cuda.synchronize()
+    else:
+        layer_weights = inp.weights
     p = m.layer_params(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.expert_begin, cfg.num_local,
-                       mode=args.mode)
+                       mode=args.mode,
+                       weight_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
     out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        m.moe_layer(p, inp.x, inp.w_router, inp.bias, inp.weights, out, ws, topk_idx_out=idx,
+        m.moe_layer(p, inp.x, inp.w_router, inp.bias, layer_weights, out, ws, topk_idx_out=idx,
                     stage_events=ev)
 
     for _ in range(args.warmup):
@@ -209,7 +219,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
-                   "I": cfg.I, "experts_computed": cfg.num_local, "weights": "mxfp4-e2m1-e8m0-b32",
+                   "I": cfg.I, "experts_computed": cfg.num_local,
+                   "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
                    "activations": "bf16", "routing_bias": cfg.bias},
         "roofline": roof,
         "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),
@@ -221,6 +232,7 @@ def main():
         "cpu_baseline": None,
     }
     if args.cpu_tokens > 0:
+        inp.weights = canonical
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(res), flush=True)
 

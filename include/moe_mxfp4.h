@@ -73,6 +73,11 @@ enum moe_dtype { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 };
  * gelu_tanh(gate) * up, NONE = plain GEMM output (no second weight). */
 enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2 };
 
+/* Storage layout of MXFP4 expert weights. OCP: the canonical row-major
+ * layout described above. PACKED: the streaming layout moe_mxfp4_prepack
+ * produces (same codes and scales, permuted for the kernels). */
+enum moe_weight_layout { MOE_LAYOUT_OCP = 0, MOE_LAYOUT_PACKED = 1 };
+
 /* Limits of this build. */
 #define MOE_MX_BLOCK 32
 #define MOE_MAX_TOPK 32
@@ -134,6 +139,25 @@ int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, in
                       moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_mxfp4_prepack -- load-time conversion of MXFP4 weights into the
+ * streaming layout (P3 section 三: the MXFP4 checkpoint is converted layer by
+ * layer at load into a form the hardware runs efficiently, no offline copy).
+ * A byte permutation: values are unchanged. For n_mats stacked [N][K]
+ * matrices (N % 16 == 0, K % 128 == 0), with nch = K/128, nc4 = ceil(nch/4),
+ * per matrix:
+ *   packed codes  [N/16][nch][4][16][16 bytes]: row block, 128-wide chunk,
+ *       MX block g of the chunk, row m of the block, the 16 code bytes of
+ *       row 16 rb + m, block 4 c + g  (N*K/2 bytes, as the input)
+ *   packed scales [N/16][nc4][4][16][4]: the scale of row 16 rb + m, block
+ *       4 (4 c4 + cc) + g at byte cc; 0 past the last chunk
+ *       (moe_mxfp4_packed_scale_bytes(N, K) bytes; = N*K/32 when K % 512 == 0)
+ * Inputs and outputs are device arrays that must not overlap.
+ * ------------------------------------------------------------------------ */
+size_t moe_mxfp4_packed_scale_bytes(int N, int K);
+int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, int N, int K,
+                      uint8_t *packed_codes, uint8_t *packed_scales, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_gemm_mxfp4 -- one grouped expert projection with MXFP4 weights
  * dequantised in registers and fed to bf16 matrix cores with fp32
  * accumulation (P2 "MXFP4 原生支持": dequantisation fused into the GEMM).
@@ -146,6 +170,8 @@ int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, in
  *   out + r * ldo, dtype out_dtype (bf16 rounding is to nearest even)
  *
  *   w1_codes/w1_scales, w2_codes/w2_scales: [num_local][N][K/2], [..][K/32]
+ *         in layout w_layout (MOE_LAYOUT_PACKED: each expert's arrays as
+ *         moe_mxfp4_prepack lays them out, experts stacked)
  *   expert_offsets [num_local + 1] int32 on the device
  *   max_rows: a host-side upper bound on off[num_local] (e.g. T*k); it sizes
  *             the launch, rows beyond off[num_local] are never touched
@@ -164,8 +190,8 @@ int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
                            const uint8_t *w1_codes, const uint8_t *w1_scales,
                            const uint8_t *w2_codes, const uint8_t *w2_scales,
                            const int32_t *expert_offsets, int num_local, int max_rows, int N,
-                           int K, int block_size, int act, void *out, int out_dtype,
-                           int64_t ldo, int mode, void *ws, size_t ws_bytes,
+                           int K, int block_size, int w_layout, int act, void *out,
+                           int out_dtype, int64_t ldo, int mode, void *ws, size_t ws_bytes,
                            moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -196,6 +222,7 @@ typedef struct {
     int act;          /* enum moe_act, MOE_ACT_SILU_MUL default   */
     int out_dtype;    /* enum moe_dtype of `out`                  */
     int mode;         /* GEMM schedule, as moe_grouped_gemm_mxfp4 */
+    int weight_layout; /* enum moe_weight_layout of all six weight arrays */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

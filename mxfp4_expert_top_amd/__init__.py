@@ -21,6 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 DT_BF16, DT_F32 = 0, 1
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
 MODE_AUTO, MODE_STREAM, MODE_TILED = 0, 1, 2
+LAYOUT_OCP, LAYOUT_PACKED = 0, 1
 MX_BLOCK = 32
 
 
@@ -54,7 +55,11 @@ def _load(path=None):
     L.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32]
     L.moe_grouped_gemm_mxfp4.restype = i32
     L.moe_grouped_gemm_mxfp4.argtypes = [p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
-                                         p, i32, i64, i32, p, sz, p]
+                                         i32, p, i32, i64, i32, p, sz, p]
+    L.moe_mxfp4_packed_scale_bytes.restype = sz
+    L.moe_mxfp4_packed_scale_bytes.argtypes = [i32, i32]
+    L.moe_mxfp4_prepack.restype = i32
+    L.moe_mxfp4_prepack.argtypes = [p, p, i32, i32, i32, p, p, p]
     L.moe_combine.restype = i32
     L.moe_combine.argtypes = [p, i32, i64, p, p, i32, i32, i32, p, i32, i64, p]
     L.moe_layer_workspace_size.restype = sz
@@ -67,13 +72,15 @@ def _load(path=None):
 lib = _load()
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4_dequant",
+            "moe_mxfp4_prepack", "moe_mxfp4_packed_scale_bytes",
             "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size", "moe_combine",
             "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error")
 
 
 class LayerParams(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("T", "d", "E", "k", "I", "block_size", "expert_begin",
-                                        "num_local", "act", "out_dtype", "mode")]
+                                        "num_local", "act", "out_dtype", "mode",
+                                        "weight_layout")]
 
 
 def _check(fn, status):
@@ -176,12 +183,46 @@ def moe_mxfp4_dequant(codes, scales, out, stream=None):
            lib.moe_mxfp4_dequant(_ptr(codes), _ptr(scales), N, K, _ptr(out), _stream(stream)))
 
 
+def packed_scale_cols(N, K):
+    """Per-row width of the packed scale array: moe_mxfp4_packed_scale_bytes / N."""
+    return int(lib.moe_mxfp4_packed_scale_bytes(N, K)) // N
+
+
+def scale_shape(n_mats, N, K, layout):
+    return (n_mats, N, K // 32 if layout == LAYOUT_OCP else packed_scale_cols(N, K))
+
+
+def moe_mxfp4_prepack(codes, scales, stream=None):
+    """Streaming layout of stacked MXFP4 matrices: codes [n, N, K/2], scales
+    [n, N, K/32] -> new (codes, scales) tensors on the same device."""
+    n, N, K2 = codes.shape
+    K = 2 * K2
+    _dev(codes, scales)
+    _want(codes, torch.uint8, (n, N, K // 2), "codes")
+    _want(scales, torch.uint8, (n, N, K // 32), "scales")
+    pc = torch.empty_like(codes)
+    ps = torch.empty(scale_shape(n, N, K, LAYOUT_PACKED), dtype=torch.uint8, device=codes.device)
+    _check("moe_mxfp4_prepack", lib.moe_mxfp4_prepack(_ptr(codes), _ptr(scales), n, N, K,
+                                                      _ptr(pc), _ptr(ps), _stream(stream)))
+    return pc, ps
+
+
+def prepack_weights(weights, stream=None):
+    """The six expert weight arrays of a layer in the streaming layout."""
+    out = {}
+    for name in ("gate", "up", "down"):
+        out[name + "_codes"], out[name + "_scales"] = moe_mxfp4_prepack(
+            weights[name + "_codes"], weights[name + "_scales"], stream)
+    return out
+
+
 def moe_grouped_gemm_workspace_size(num_local, max_rows, N, mode=MODE_AUTO):
     return int(lib.moe_grouped_gemm_workspace_size(num_local, max_rows, N, mode))
 
 
 def moe_grouped_gemm_mxfp4(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
-                           expert_offsets, max_rows, act, out, ws, mode=MODE_AUTO, stream=None):
+                           expert_offsets, max_rows, act, out, ws, mode=MODE_AUTO,
+                           w_layout=LAYOUT_OCP, stream=None):
     """out[r] = act(a_row(r) @ W1[e].T, a_row(r) @ W2[e].T) for the rows r of
     each local expert e (see the header). ``out`` is [>= rows, N]."""
     num_local = expert_offsets.shape[0] - 1
@@ -190,10 +231,10 @@ def moe_grouped_gemm_mxfp4(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
     if a.dtype != torch.bfloat16 or a.dim() != 2 or a.shape[1] != K:
         raise ValueError("a must be [rows, K] bf16")
     _want(w1_codes, torch.uint8, (num_local, N, K // 2), "w1_codes")
-    _want(w1_scales, torch.uint8, (num_local, N, K // 32), "w1_scales")
+    _want(w1_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w1_scales")
     if w2_codes is not None:
         _want(w2_codes, torch.uint8, (num_local, N, K // 2), "w2_codes")
-        _want(w2_scales, torch.uint8, (num_local, N, K // 32), "w2_scales")
+        _want(w2_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w2_scales")
     if out.dim() != 2 or out.shape[1] != N or out.shape[0] < max_rows:
         raise ValueError("out must be [>= max_rows, N]")
     if a_rows is not None:
@@ -204,7 +245,7 @@ def moe_grouped_gemm_mxfp4(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib.moe_grouped_gemm_mxfp4(
         _ptr(a), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
-        _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K, MX_BLOCK, act,
+        _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K, MX_BLOCK, w_layout, act,
         _ptr(out), _dt(out), N, mode, _ptr(ws), nbytes, _stream(stream))
     _check("moe_grouped_gemm_mxfp4", st)
 
@@ -223,9 +264,10 @@ def moe_combine(y, inv, topk_w, out, stream=None):
 
 
 def layer_params(T, d, E, k, I, expert_begin=0, num_local=None, act=ACT_SILU_MUL,
-                 out_dtype=DT_BF16, mode=MODE_AUTO):
+                 out_dtype=DT_BF16, mode=MODE_AUTO, weight_layout=LAYOUT_OCP):
     return LayerParams(T, d, E, k, I, MX_BLOCK, expert_begin,
-                       E - expert_begin if num_local is None else num_local, act, out_dtype, mode)
+                       E - expert_begin if num_local is None else num_local, act, out_dtype, mode,
+                       weight_layout)
 
 
 def moe_layer_workspace_size(params: LayerParams) -> int:
@@ -246,12 +288,13 @@ def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_o
     _want(w_router, torch.float32, (p.E, p.d), "w_router")
     if bias is not None:
         _want(bias, torch.float32, (p.E,), "bias")
+    lay = p.weight_layout
     for n, shape in (("gate_codes", (p.num_local, p.I, p.d // 2)),
-                     ("gate_scales", (p.num_local, p.I, p.d // 32)),
+                     ("gate_scales", scale_shape(p.num_local, p.I, p.d, lay)),
                      ("up_codes", (p.num_local, p.I, p.d // 2)),
-                     ("up_scales", (p.num_local, p.I, p.d // 32)),
+                     ("up_scales", scale_shape(p.num_local, p.I, p.d, lay)),
                      ("down_codes", (p.num_local, p.d, p.I // 2)),
-                     ("down_scales", (p.num_local, p.d, p.I // 32))):
+                     ("down_scales", scale_shape(p.num_local, p.d, p.I, lay))):
         _want(weights[n], torch.uint8, shape, n)
     _want(out, torch.float32 if p.out_dtype == DT_F32 else torch.bfloat16, (p.T, p.d), "out")
     if logits_out is not None:

@@ -65,8 +65,10 @@ int check_permute(const int32_t *idx, const int32_t *counts, int T, int k, int E
 
 int check_gemm(const void *a, int64_t lda, const uint8_t *w1c, const uint8_t *w1s,
                const uint8_t *w2c, const uint8_t *w2s, const int32_t *off, int nl, int max_rows,
-               int N, int K, int block_size, int act, const void *out, int out_dtype, int64_t ldo)
+               int N, int K, int block_size, int w_layout, int act, const void *out,
+               int out_dtype, int64_t ldo)
 {
+    CHECK(w_layout == MOE_LAYOUT_OCP || w_layout == MOE_LAYOUT_PACKED, MOE_ERR_INVALID_ARG);
     CHECK(nl >= 1 && max_rows >= 0 && N >= 1 && K >= 1, MOE_ERR_INVALID_ARG);
     CHECK(act == MOE_ACT_NONE || act == MOE_ACT_SILU_MUL || act == MOE_ACT_GELU_TANH_MUL,
           MOE_ERR_INVALID_ARG);
@@ -138,6 +140,8 @@ int check_layer_params(const moe_layer_params *p)
     CHECK(p->act == MOE_ACT_SILU_MUL || p->act == MOE_ACT_GELU_TANH_MUL, MOE_ERR_INVALID_ARG);
     CHECK(p->out_dtype == MOE_DT_BF16 || p->out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
     CHECK(p->mode >= 0 && p->mode <= 2, MOE_ERR_INVALID_ARG);
+    CHECK(p->weight_layout == MOE_LAYOUT_OCP || p->weight_layout == MOE_LAYOUT_PACKED,
+          MOE_ERR_INVALID_ARG);
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
     CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
     CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
@@ -213,6 +217,25 @@ int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, in
     return MOE_OK;
 }
 
+size_t moe_mxfp4_packed_scale_bytes(int N, int K)
+{
+    if (N < 0 || K < 0 || N % 16 || K % 128) return 0;
+    return packed_scale_bytes(N, K);
+}
+
+int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, int N, int K,
+                      uint8_t *packed_codes, uint8_t *packed_scales, moe_stream_t stream)
+{
+    CHECK(n_mats >= 0 && N >= 0 && K >= 0, MOE_ERR_INVALID_ARG);
+    CHECK(N % 16 == 0 && K % 128 == 0, MOE_ERR_UNSUPPORTED);
+    if (n_mats == 0 || N == 0 || K == 0) return MOE_OK;
+    CHECK(codes && scales && packed_codes && packed_scales, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(codes, 16) && aligned(packed_codes, 16), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_prepack(codes, scales, (int64_t)n_mats * N, K, packed_codes, packed_scales,
+                           as_stream(stream)));
+    return MOE_OK;
+}
+
 size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode)
 {
     if (num_local < 1 || max_rows < 0 || mode < 0 || mode > 2) return 0;
@@ -223,20 +246,22 @@ int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
                            const uint8_t *w1_codes, const uint8_t *w1_scales,
                            const uint8_t *w2_codes, const uint8_t *w2_scales,
                            const int32_t *expert_offsets, int num_local, int max_rows, int N,
-                           int K, int block_size, int act, void *out, int out_dtype,
-                           int64_t ldo, int mode, void *ws, size_t ws_bytes,
+                           int K, int block_size, int w_layout, int act, void *out,
+                           int out_dtype, int64_t ldo, int mode, void *ws, size_t ws_bytes,
                            moe_stream_t stream)
 {
     CHECK(mode >= 0 && mode <= 2, MOE_ERR_INVALID_ARG);
     int rc = check_gemm(a, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
-                        num_local, max_rows, N, K, block_size, act, out, out_dtype, ldo);
+                        num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
+                        ldo);
     if (rc) return rc;
     if (max_rows == 0) return MOE_OK;
     rc = check_ws(ws, ws_bytes, grouped_gemm_ws_bytes(num_local, max_rows, N, mode));
     if (rc) return rc;
     HIP_TRY(launch_grouped_gemm((const bf16 *)a, lda, a_rows, w1_codes, w1_scales, w2_codes,
                                 w2_scales, expert_offsets, num_local, max_rows, N, K, act, out,
-                                out_dtype == MOE_DT_F32, ldo, mode, ws, as_stream(stream)));
+                                out_dtype == MOE_DT_F32, ldo, mode, ws,
+                                w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
     return MOE_OK;
 }
 
@@ -295,6 +320,7 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     bf16 *h = (bf16 *)(base + L.h);
     float *y = (float *)(base + L.y);
     const int A = p->T * p->k;
+    const int packed = p->weight_layout == MOE_LAYOUT_PACKED;
     hipStream_t s = as_stream(stream);
     hipEvent_t *ev = (hipEvent_t *)stage_events;
 
@@ -322,11 +348,11 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
                             up_scales, off, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
-                            p->mode, base + L.gws, s));
+                            p->mode, base + L.gws, packed, s));
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
     HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr, off,
                             p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
-                            base + L.gws, s));
+                            base + L.gws, packed, s));
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));
     HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
                            p->out_dtype == MOE_DT_F32, p->d, s));

@@ -98,7 +98,7 @@ __host__ __device__ constexpr int stream_cols_per_wave()
     return ACT != ACT_NONE ? 8 * ST_NS : 16 * ST_NS;
 }
 
-template <int ACT, typename OutT, int D>
+template <int ACT, typename OutT, int D, bool PACKED>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     constexpr int NS = ST_NS;
     constexpr int COLS_W = stream_cols_per_wave<ACT>();
     constexpr int COLS_B = 4 * COLS_W;
-    // the scales of the workgroup's weight rows, staged in LDS (see below)
+    // canonical layout: the scales of the workgroup's weight rows, staged in LDS
     extern __shared__ uint32_t sscale[];
     const int nblk = (N + COLS_B - 1) / COLS_B;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -129,54 +129,74 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
     const bf16 *ap = a + arow * lda + 32 * g;
 
-    // Scales: one E8M0 byte per 32 weights. Read piecemeal inside the K loop
-    // they would be fetched many times over (a 128-byte line holds about one
-    // row's worth and the code stream evicts it between reads), so the
-    // workgroup first copies the scales of all its weight rows -- one
-    // contiguous block per weight matrix -- into LDS with 16-byte loads.
-    const int sbw = K / 128;                                    // scale dwords per row
-    const int rows_b = COLS_B;                                  // weight rows per matrix block
-    const int rows_v = min(rows_b, N - nb0);                    // rows inside the matrix
-    const int nmat = GLU ? 2 : 1;
-    {
-        const int per_mat4 = rows_v * sbw / 4;                  // uint4 per matrix (rows_v*sbw % 4 == 0)
-        for (int i = threadIdx.x; i < nmat * per_mat4; i += blockDim.x) {
+    const int nch = K / 128;  // a multiple of D (the launcher picks D)
+    const int nc4 = (nch + 3) / 4;
+    const int sbw = K / 128;  // canonical: scale dwords per row
+    if constexpr (!PACKED) {
+        // Canonical scales: one E8M0 byte per 32 weights. Read piecemeal inside
+        // the K loop they would be fetched many times over (a 128-byte line
+        // holds about one row's worth and the code stream evicts it between
+        // reads), so the workgroup first copies the scales of all its weight
+        // rows -- one contiguous block per weight matrix -- into LDS.
+        const int rows_v = min(COLS_B, N - nb0);
+        const int per_mat4 = rows_v * sbw / 4;  // uint4 per matrix (rows_v % 64 == 0)
+        for (int i = threadIdx.x; i < (GLU ? 2 : 1) * per_mat4; i += blockDim.x) {
             const int mat = i / per_mat4, r = i - mat * per_mat4;
             const uint8_t *base = (mat ? w2s : w1s) + ((int64_t)e * N + nb0) * (K / 32);
-            *(u32x4 *)(&sscale[mat * rows_b * sbw + 4 * r]) = *(const u32x4 *)(base + 16 * r);
+            *(u32x4 *)(&sscale[mat * COLS_B * sbw + 4 * r]) = *(const u32x4 *)(base + 16 * r);
         }
     }
 
-    const int64_t code_row = K / 2;
+    // Per stream: code pointer (chunk stride 64 canonical, 1024 packed) and the
+    // scale source (LDS dword row canonical; global dword packed).
     const uint8_t *cp[NS];
-    int srow[NS];  // dword offset of each stream's scale row in LDS
+    const uint8_t *spk[NS];
+    int srow[NS];
 #pragma unroll
     for (int j = 0; j < NS; j++) {
-        const int wr = GLU ? n0 + 16 * (j / 2) + m : n0 + 16 * j + m;
+        const int wr0 = GLU ? n0 + 16 * (j / 2) : n0 + 16 * j;  // first row of the 16
         const bool second = GLU && (j & 1);
-        const int64_t row = (int64_t)e * N + (wave_on ? wr : 0);
-        cp[j] = (second ? w2c : w1c) + row * code_row + 16 * g;
-        srow[j] = ((second ? 1 : 0) * rows_b + (wr - nb0)) * sbw;
+        const int wr = wave_on ? wr0 : 0;
+        if constexpr (PACKED) {
+            const int64_t rb = ((int64_t)e * N + wr) / 16;
+            cp[j] = (second ? w2c : w1c) + rb * nch * 1024 + lane * 16;
+            spk[j] = (second ? w2s : w1s) + rb * nc4 * 256 + lane * 4;
+            srow[j] = 0;
+        } else {
+            const int64_t row = (int64_t)e * N + wr + m;
+            cp[j] = (second ? w2c : w1c) + row * (K / 2) + 16 * g;
+            spk[j] = nullptr;
+            srow[j] = ((second ? 1 : 0) * COLS_B + (wr0 - nb0) + m) * sbw;
+        }
     }
 
-    const int nch = K / 128;  // a multiple of D (the launcher picks D)
     u32x4 q[D][NS];
+    uint32_t sq[D][NS];  // packed: the scale dword of each slot's chunk group
     bf16x8 af[D][4];
     f32x4 acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto issue = [&](int c, u32x4 *qd, bf16x8 *ad) {
+    auto issue = [&](int c, u32x4 *qd, uint32_t *sd, bf16x8 *ad) {
 #pragma unroll
-        for (int j = 0; j < NS; j++) qd[j] = *(const u32x4 *)(cp[j] + c * 64);
+        for (int j = 0; j < NS; j++) {
+            if constexpr (PACKED) {
+                qd[j] = *(const u32x4 *)(cp[j] + c * 1024);
+                sd[j] = *(const uint32_t *)(spk[j] + (c >> 2) * 256);
+            } else {
+                qd[j] = *(const u32x4 *)(cp[j] + c * 64);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 4; s++) ad[s] = *(const bf16x8 *)(ap + c * 128 + 8 * s);
     };
-    auto consume = [&](int c, const u32x4 *qd, const bf16x8 *ad) {
+    auto consume = [&](int c, const u32x4 *qd, const uint32_t *sd, const bf16x8 *ad) {
 #pragma unroll
         for (int j = 0; j < NS; j++) {
-            const uint32_t sw = sscale[srow[j] + c];
-            const float f = e8m0_to_f32((sw >> (8 * g)) & 0xffu);
+            uint32_t sb;
+            if constexpr (PACKED) sb = (sd[j] >> (8 * (c & 3))) & 0xffu;
+            else sb = (sscale[srow[j] + c] >> (8 * g)) & 0xffu;
+            const float f = e8m0_to_f32(sb);
 #pragma unroll
             for (int s = 0; s < 4; s++) acc[j] = mfma16x16x32(ad[s], mx_decode8(qd[j][s], f), acc[j]);
         }
@@ -184,21 +204,21 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     // prologue: chunks 0 .. D-1 in flight (behind the scale copy's loads)
     if (wave_on) {
 #pragma unroll
-        for (int d = 0; d < D; d++) issue(d, q[d], af[d]);
+        for (int d = 0; d < D; d++) issue(d, q[d], sq[d], af[d]);
     }
-    __syncthreads();  // scales in LDS
+    if constexpr (!PACKED) __syncthreads();  // scales in LDS
     if (!wave_on) return;
     // steady state: consume chunk c, refill its slot with chunk c + D
     for (int c0 = 0; c0 < nch - D; c0 += D) {
 #pragma unroll
         for (int d = 0; d < D; d++) {
-            consume(c0 + d, q[d], af[d]);
-            issue(c0 + d + D, q[d], af[d]);
+            consume(c0 + d, q[d], sq[d], af[d]);
+            issue(c0 + d + D, q[d], sq[d], af[d]);
         }
     }
     // drain the last D chunks
 #pragma unroll
-    for (int d = 0; d < D; d++) consume(nch - D + d, q[d], af[d]);
+    for (int d = 0; d < D; d++) consume(nch - D + d, q[d], sq[d], af[d]);
 
     // lane holds C[4 g + i][m] of each stream: token row r0 + 4 g + i
 #pragma unroll
@@ -261,7 +281,7 @@ __host__ __device__ constexpr int tile_cols()
     return ACT != ACT_NONE ? TL_BN / 2 : TL_BN;
 }
 
-template <int ACT, typename OutT>
+template <int ACT, typename OutT, bool PACKED>
 __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
@@ -316,16 +336,33 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
         wsb = w1s;
     }
     const int64_t wr64 = (int64_t)e * N + wrow;
-    const uint8_t *bg = wcb + wr64 * code_row + 16 * bh;
-    const uint8_t *sg = wsb + wr64 * scale_row + bh;
+    // canonical: row-major codes/scales; packed: 16-row blocks x 128-wide
+    // chunks (a K step of 64 is half a chunk: MX blocks g = 2 (kt % 2) + bh)
+    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const uint8_t *bg, *sg;
+    if constexpr (PACKED) {
+        const int64_t rb = wr64 / 16;
+        const int mm = (int)(wr64 % 16);
+        bg = wcb + rb * nch * 1024 + mm * 16;
+        sg = wsb + rb * nc4 * 256 + mm * 4;
+    } else {
+        bg = wcb + wr64 * code_row + 16 * bh;
+        sg = wsb + wr64 * scale_row + bh;
+    }
 
     u32x4 ra0, ra1, rb;
     uint8_t rs;
     auto gload = [&](int k0) {
         ra0 = *(const u32x4 *)(ag + k0);
         ra1 = *(const u32x4 *)(ag + k0 + 8);
-        rb = *(const u32x4 *)(bg + k0 / 2);
-        rs = sg[k0 / 32];
+        if constexpr (PACKED) {
+            const int kt = k0 / TL_BK, c = kt >> 1, gg = 2 * (kt & 1) + bh;
+            rb = *(const u32x4 *)(bg + c * 1024 + gg * 256);
+            rs = sg[(c >> 2) * 256 + gg * 64 + (c & 3)];
+        } else {
+            rb = *(const u32x4 *)(bg + k0 / 2);
+            rs = sg[k0 / 32];
+        }
     };
     auto lstore = [&](int st) {
         *(u32x4 *)(&As[st][ar][ac]) = ra0;
@@ -474,7 +511,7 @@ size_t grouped_gemm_ws_bytes(int num_local, int max_rows, int N, int mode)
     return gemm_plan_ws_bytes(num_local, max_rows, rows_per_group(md));
 }
 
-template <int ACT, typename OutT>
+template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_rows,
                                 const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                 const uint8_t *w2s, const int32_t *off, const int32_t *plan,
@@ -489,10 +526,11 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
     // prefetch depth: the largest of ST_DMAX, 2, 1 that divides the chunk count
     const int nch = K / 128;
     const int D = (nch % ST_DMAX == 0) ? ST_DMAX : (nch % 2 == 0 ? 2 : 1);
-    const size_t lds = (size_t)(ACT != ACT_NONE ? 2 : 1) * COLS_B * (K / 32);
-#define ST_LAUNCH(DD)                                                                            \
-    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD>), dim3((unsigned)grid), dim3(256), lds, \
-                       s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo)
+    const size_t lds = PACKED ? 0 : (size_t)(ACT != ACT_NONE ? 2 : 1) * COLS_B * (K / 32);
+#define ST_LAUNCH(DD)                                                                         \
+    hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD, PACKED>), dim3((unsigned)grid),     \
+                       dim3(256), lds, s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, \
+                       out, ldo)
     if (D == ST_DMAX)
         ST_LAUNCH(ST_DMAX);
     else if (D == 2)
@@ -503,7 +541,7 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
     return hipGetLastError();
 }
 
-template <int ACT, typename OutT>
+template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
                               const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                               const uint8_t *w2s, const int32_t *off, const int32_t *plan,
@@ -515,12 +553,12 @@ static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
     // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT>), dim3((unsigned)G), dim3(TL_THREADS), 0, s, a,
-                       lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo);
+    hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(TL_THREADS),
+                       0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo);
     return hipGetLastError();
 }
 
-template <typename OutT>
+template <typename OutT, bool PACKED>
 static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, const int32_t *a_rows,
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                const uint8_t *w2s, const int32_t *off, const int32_t *plan,
@@ -528,19 +566,18 @@ static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, cons
                                hipStream_t s)
 {
 #define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups, N, K, out, ldo, s
+#define MOE_GEMM_CASE(A)                                                     \
+    case A:                                                                  \
+        return md == 2 ? launch_tile<A, OutT, PACKED>(MOE_GEMM_ARGS)         \
+                       : launch_stream<A, OutT, PACKED>(MOE_GEMM_ARGS);
     switch (act) {
-    case ACT_NONE:
-        return md == 2 ? launch_tile<ACT_NONE, OutT>(MOE_GEMM_ARGS)
-                       : launch_stream<ACT_NONE, OutT>(MOE_GEMM_ARGS);
-    case ACT_SILU_MUL:
-        return md == 2 ? launch_tile<ACT_SILU_MUL, OutT>(MOE_GEMM_ARGS)
-                       : launch_stream<ACT_SILU_MUL, OutT>(MOE_GEMM_ARGS);
-    case ACT_GELU_TANH_MUL:
-        return md == 2 ? launch_tile<ACT_GELU_TANH_MUL, OutT>(MOE_GEMM_ARGS)
-                       : launch_stream<ACT_GELU_TANH_MUL, OutT>(MOE_GEMM_ARGS);
+        MOE_GEMM_CASE(ACT_NONE)
+        MOE_GEMM_CASE(ACT_SILU_MUL)
+        MOE_GEMM_CASE(ACT_GELU_TANH_MUL)
     default:
         return hipErrorInvalidValue;
     }
+#undef MOE_GEMM_CASE
 #undef MOE_GEMM_ARGS
 }
 
@@ -568,28 +605,33 @@ hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, co
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
                            const int32_t *off, int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
-                           hipStream_t s)
+                           int packed, hipStream_t s)
 {
     const int md = resolve_mode(mode, num_local, max_rows);
     const int max_groups = max_groups_for(num_local, max_rows, rows_per_group(md));
     const int32_t *plan = (const int32_t *)plan_ws;
-    if (out_f32)
-        return dispatch_act<float>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,
-                                   max_groups, N, K, (float *)out, ldo, s);
-    return dispatch_act<bf16>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups,
-                              N, K, (bf16 *)out, ldo, s);
+#define MOE_RUN(OT, PK)                                                                    \
+    return dispatch_act<OT, PK>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,    \
+                                max_groups, N, K, (OT *)out, ldo, s)
+    if (out_f32) {
+        if (packed) MOE_RUN(float, true);
+        MOE_RUN(float, false);
+    }
+    if (packed) MOE_RUN(bf16, true);
+    MOE_RUN(bf16, false);
+#undef MOE_RUN
 }
 
 hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows,
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                const uint8_t *w2s, const int32_t *off, int num_local,
                                int max_rows, int N, int K, int act, void *out, int out_f32,
-                               int64_t ldo, int mode, void *ws, hipStream_t s)
+                               int64_t ldo, int mode, void *ws, int packed, hipStream_t s)
 {
     hipError_t e = launch_gemm_plan(off, num_local, max_rows, mode, ws, s);
     if (e != hipSuccess) return e;
     return launch_gemm_run(a, lda, a_rows, w1c, w1s, w2c, w2s, off, num_local, max_rows, N, K,
-                           act, out, out_f32, ldo, mode, ws, s);
+                           act, out, out_f32, ldo, mode, ws, packed, s);
 }
 
 hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,

@@ -65,7 +65,7 @@ hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                const uint8_t *w2s, const int32_t *off, int num_local,
                                int max_rows, int N, int K, int act, void *out, int out_f32,
-                               int64_t ldo, int mode, void *ws, hipStream_t s);
+                               int64_t ldo, int mode, void *ws, int packed, hipStream_t s);
 size_t grouped_gemm_ws_bytes(int num_local, int max_rows, int N, int mode);
 GemmPlanArgs gemm_plan_args(int num_local, int max_rows, int mode, void *ws);
 hipError_t launch_gemm_plan_into(const int32_t *off, int num_local, const GemmPlanArgs &a,
@@ -78,11 +78,16 @@ hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, co
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
                            const int32_t *off, int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
-                           hipStream_t s);
+                           int packed, hipStream_t s);
 int resolve_mode(int mode, int num_local, int max_rows);
 
 hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,
                                 bf16 *out, hipStream_t s);
+
+// prepack.hip: the streaming weight layout (see prepack.hip)
+size_t packed_scale_bytes(int64_t N, int K);
+hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int64_t n_rows, int K,
+                          uint8_t *pcodes, uint8_t *pscales, hipStream_t s);
 
 // combine.hip
 hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,

@@ -38,20 +38,23 @@ def assert_close_layer(got, ref, what=""):
     return r, m
 
 
-def run_gpu_layer(inp, *, mode=0, out_dtype=torch.bfloat16, act=1):
-    """The fused entry on ``inp`` (tensors already on the GPU). Returns dict of
-    GPU tensors: out, logits, idx, w."""
+def run_gpu_layer(inp, *, mode=0, out_dtype=torch.bfloat16, act=1, packed=None):
+    """The fused entry on ``inp`` (tensors already on the GPU). ``packed``: the
+    weights already in the streaming layout (``inp.weights`` stay canonical).
+    Returns dict of GPU tensors: out, logits, idx, w."""
     import mxfp4_expert_top_amd as m
     c = inp.cfg
     p = m.layer_params(c.T, c.d, c.E, c.k, c.I, c.expert_begin, c.num_local, act=act,
-                       out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16, mode=mode)
+                       out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16, mode=mode,
+                       weight_layout=m.LAYOUT_OCP if packed is None else m.LAYOUT_PACKED)
     dev = inp.x.device
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
     out = torch.empty(c.T, c.d, dtype=out_dtype, device=dev)
     logits = torch.empty(c.T, c.E, dtype=torch.float32, device=dev)
     idx = torch.empty(c.T, c.k, dtype=torch.int32, device=dev)
     w = torch.empty(c.T, c.k, dtype=torch.float32, device=dev)
-    m.moe_layer(p, inp.x, inp.w_router, inp.bias, inp.weights, out, ws, logits, idx, w)
+    m.moe_layer(p, inp.x, inp.w_router, inp.bias, inp.weights if packed is None else packed, out,
+                ws, logits, idx, w)
     torch.cuda.synchronize()
     return dict(out=out, logits=logits, idx=idx, w=w)
 

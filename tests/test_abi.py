@@ -77,7 +77,7 @@ def test_permute_validation():
 
 def _gemm(**kw):
     a = dict(a=FAKE, lda=256, a_rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE, off=FAKE,
-             nl=8, max_rows=64, N=128, K=256, bs=32, act=1, out=FAKE, odt=0, ldo=128, mode=0,
+             nl=8, max_rows=64, N=128, K=256, bs=32, lay=0, act=1, out=FAKE, odt=0, ldo=128, mode=0,
              ws=None, wsb=0)
     a.update(kw)
     return m.lib.moe_grouped_gemm_mxfp4(*a.values(), None)
@@ -93,6 +93,7 @@ def test_grouped_gemm_validation():
     assert _gemm(odt=5) == 1
     assert _gemm(lda=100) == 1               # stride not a multiple of 8
     assert _gemm(mode=3) == 1
+    assert _gemm(lay=2) == 1                 # unknown weight layout
     assert _gemm(K=8320, lda=8320) == 2      # K > MOE_MAX_K
     assert _gemm(w1s=C.c_void_p(0x10004)) == 1  # scales not 16-byte aligned
     assert _gemm() == 3                      # no workspace given
@@ -112,6 +113,18 @@ def test_combine_and_dequant_validation():
     # zero-size requests are no-ops that touch nothing
     assert L.moe_mxfp4_dequant(None, None, 0, 64, None, None) == 0
     assert L.moe_combine(None, 0, 96, None, None, 0, 96, 4, None, 0, 96, None) == 0
+
+
+def test_prepack_validation():
+    L = m.lib
+    assert L.moe_mxfp4_prepack(FAKE, FAKE, 2, 24, 256, FAKE, FAKE, None) == 2   # N % 16
+    assert L.moe_mxfp4_prepack(FAKE, FAKE, 2, 32, 96, FAKE, FAKE, None) == 2    # K % 128
+    assert L.moe_mxfp4_prepack(None, None, 0, 32, 256, None, None, None) == 0   # nothing to do
+    assert L.moe_mxfp4_prepack(FAKE, FAKE, 2, 32, 256, None, FAKE, None) == 1
+    assert m.lib.moe_mxfp4_packed_scale_bytes(1024, 3584) == 1024 * 3584 // 32
+    assert m.lib.moe_mxfp4_packed_scale_bytes(3584, 1024) == 3584 * 1024 // 32
+    assert m.lib.moe_mxfp4_packed_scale_bytes(128, 128) == 128 * 16  # one padded group
+    assert m.lib.moe_mxfp4_packed_scale_bytes(100, 128) == 0
 
 
 def test_layer_params_and_workspace():

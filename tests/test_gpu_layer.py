@@ -90,6 +90,17 @@ def test_tiny_workload_full_oracle(tiny):
     assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], "tiny")
 
 
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], SMALL[2], SMALL[5]], ids=lambda c: c.name)
+@pytest.mark.parametrize("mode", [1, 2])
+def test_packed_layout_layer_bitwise(cfg, mode):
+    import mxfp4_expert_top_amd as m
+    inp = make_inputs(cfg).to(DEV)
+    a = run_gpu_layer(inp, mode=mode)
+    b = run_gpu_layer(inp, mode=mode, packed=m.prepack_weights(inp.weights))
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
 def test_determinism_bitwise(tiny):
     gi = tiny.to(DEV)
     a = run_gpu_layer(gi)
@@ -120,9 +131,12 @@ def _sample_tokens(cfg, idx, n_random, seed=0):
 @pytest.mark.parametrize("name,n_random", [("decode", 10), ("prefill", 6), ("ep_share", 6),
                                            ("long_skewed_prefill", 3)])
 def test_full_size_workload(name, n_random):
+    """The benchmark's launch configuration: weights converted to the streaming
+    layout at load, schedule chosen automatically, bf16 output."""
+    import mxfp4_expert_top_amd as m
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, DEV)
-    g = run_gpu_layer(inp)
+    g = run_gpu_layer(inp, packed=m.prepack_weights(inp.weights))
     lg, r_idx, _ = _check_routing(inp, g)
     # scores of a few tokens against the oracle's own router product
     _check_scores(inp, lg, rows=[0, cfg.T // 2, cfg.T - 1])

@@ -214,3 +214,57 @@ def test_combine_vs_oracle(m, y_dtype, out_dtype):
         assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
     else:
         assert np.abs(got - ref).max() <= 2 ** -8 * np.abs(ref).max()
+
+
+# ---------------------------------------------------------------- prepack
+def _unpack_reference(pc, ps, n, N, K):
+    """Inverse of the streaming layout, written from the layout's definition:
+    codes [N/16][K/128][4][16][16], scales [N/16][ceil(K/512)][4][16][4]."""
+    nch, nc4 = K // 128, (K // 128 + 3) // 4
+    codes = pc.reshape(n, N // 16, nch, 4, 16, 16)           # rb, c, g, m, byte
+    codes = codes.transpose(0, 1, 4, 2, 3, 5).reshape(n, N, K // 2)  # rb, m, c, g, byte
+    sc = ps.reshape(n, N // 16, nc4, 4, 16, 4)               # rb, c4, g, m, cc
+    sc = sc.transpose(0, 1, 4, 2, 5, 3).reshape(n, N, nc4 * 16)  # rb, m, c4, cc, g
+    return codes, sc[:, :, : K // 32], sc[:, :, K // 32:]
+
+
+@pytest.mark.parametrize("n,N,K", [(3, 48, 384), (2, 64, 1024), (1, 16, 128), (2, 1024, 3584)])
+def test_prepack_is_a_permutation(m, n, N, K):
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 256, size=(n, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(2, 253, size=(n, N, K // 32), dtype=np.uint8)
+    pc, ps = m.moe_mxfp4_prepack(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    c2, s2, pad = _unpack_reference(np_(pc), np_(ps), n, N, K)
+    assert np.array_equal(c2, codes)
+    assert np.array_equal(s2, scales)
+    assert (pad == 0).all()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("act", [0, 1])
+def test_grouped_gemm_packed_equals_canonical(m, mode, act):
+    rng = np.random.default_rng(11 + act)
+    nl, N, K, T = 5, 192, 384, 80
+    counts = np.array([3, 0, 40, 17, 60], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    a_rows = torch.from_numpy(rng.integers(0, T, size=A).astype(np.int32)).to(DEV)
+    w1c, w1s = [t.to(DEV) for t in _experts(nl, N, K, 3)]
+    w2c, w2s = [t.to(DEV) for t in _experts(nl, N, K, 4)] if act else (None, None)
+    offd = torch.from_numpy(off).to(DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_workspace_size(nl, A, N, mode), DEV)
+    outs = []
+    for lay in (m.LAYOUT_OCP, m.LAYOUT_PACKED):
+        if lay == m.LAYOUT_PACKED:
+            p1c, p1s = m.moe_mxfp4_prepack(w1c, w1s)
+            p2c, p2s = m.moe_mxfp4_prepack(w2c, w2s) if act else (None, None)
+        else:
+            p1c, p1s, p2c, p2s = w1c, w1s, w2c, w2s
+        out = torch.empty(A, N, dtype=torch.float32, device=DEV)
+        m.moe_grouped_gemm_mxfp4(x, a_rows, p1c, p1s, p2c, p2s, offd, A, act, out, ws, mode=mode,
+                                 w_layout=lay)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
