@@ -176,12 +176,12 @@ int moe_route(const void *x, const float *w_router, const float *bias, float *lo
                          expert_counts);
     if (rc) return rc;
     hipStream_t s = as_stream(stream);
-    HIP_TRY(launch_fill_i32(expert_counts, E, 0, s));
+    if (T == 0 || logits_given) HIP_TRY(launch_fill_i32(expert_counts, E, 0, s));
     if (T == 0) return MOE_OK;
     if (!logits_given)
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, 1, s));
-    HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, T, E, k, topk_idx, topk_w,
-                                expert_counts, s));
+        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, 1,
+                                     expert_counts, s));
+    HIP_TRY(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, expert_counts, s));
     return MOE_OK;
 }
 
@@ -325,21 +325,20 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     hipEvent_t *ev = (hipEvent_t *)stage_events;
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
-    HIP_TRY(launch_fill_i32(counts, p->E, 0, s));
     float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
     const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
     if (L.tiled_router) {
         bf16 *wp = (bf16 *)(base + L.wsplit);
         HIP_TRY(launch_split_router(w_router, p->E, p->d, wp, s));
         HIP_TRY(launch_router_tile((const bf16 *)x, wp, b_in_gemm, planes, p->T, p->d, p->E,
-                                   L.splits, s));
+                                   L.splits, counts, s));
     } else {
         HIP_TRY(launch_router_logits((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
-                                     p->E, L.splits, s));
+                                     p->E, L.splits, counts, s));
     }
     // split-K planes are summed in a fixed order (bias added there)
     if (L.splits > 1) HIP_TRY(launch_sum_planes(planes, L.splits, bias, logits, p->T, p->E, s));
-    HIP_TRY(launch_topk_softmax(logits, 1, nullptr, nullptr, p->T, p->E, p->k, idx, w, counts, s));
+    HIP_TRY(launch_topk_softmax(logits, p->T, p->E, p->k, idx, w, counts, s));
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);

@@ -90,6 +90,34 @@ __device__ __forceinline__ float act_apply(float g, float u)
     }
 }
 
+// Exclusive prefix sum over the threads of a workgroup of `nthreads`
+// (a multiple of 64, at most 1024) threads: an inclusive scan inside each
+// wavefront with lane shuffles, one exchange of the wave totals through LDS.
+// `scratch` holds 16 ints of LDS; `total` receives the sum of all values.
+// Every thread of the workgroup must call it.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nwaves = blockDim.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+    }
+    if (lane == 63) scratch[wave] = inc;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < nwaves; w++) {
+        const int t = scratch[w];
+        before += w < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();  // scratch may be reused by the caller
+    total = all;
+    return before + inc - v;
+}
+
 template <typename T>
 __device__ __forceinline__ void store_out(T *p, float v);
 template <>

@@ -24,28 +24,21 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int32_t *__restri
                                                          int R, int max_groups,
                                                          int32_t *__restrict__ plan)
 {
-    __shared__ int32_t part[1024];
+    __shared__ int32_t part[16];
     const int tid = threadIdx.x;
     const int per = (nl + 1023) / 1024;
     const int lo = tid * per, hi = min(lo + per, nl);
     int s = 0;
     for (int i = lo; i < hi; i++) s += (off[i + 1] - off[i] + R - 1) / R;
-    part[tid] = s;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        int v = tid >= o ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int pos = part[tid] - s;
+    int ngroups;
+    int pos = block_exclusive_scan(s, part, ngroups);
     int2 *items = (int2 *)(plan + PLAN_HDR);
     for (int i = lo; i < hi; i++) {
         const int c = off[i + 1] - off[i];
         for (int r = 0; r < c; r += R, pos++)
             if (pos < max_groups) items[pos] = make_int2(i, off[i] + r);
     }
-    if (tid == 1023) plan[0] = min(part[1023], max_groups);
+    if (tid == 0) plan[0] = min(ngroups, max_groups);
 }
 
 // ---------------------------------------------------------------------------

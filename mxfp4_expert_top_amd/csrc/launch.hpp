@@ -18,8 +18,10 @@ namespace moe {
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // Router scores into `splits` planes of [T][E] partial sums (splits == 1:
 // the final scores, bias included); splits must divide d / 128.
+// zero_counts: an [E] histogram zeroed by the launch (NULL: none).
 hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
-                                int T, int d, int E, int splits, hipStream_t s);
+                                int T, int d, int E, int splits, int32_t *zero_counts,
+                                hipStream_t s);
 // logits = sum of the planes in order + bias (E % 4 == 0).
 hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
                              int T, int E, hipStream_t s);
@@ -28,15 +30,14 @@ hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bia
 hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s);
 int router_tile_splits(int T, int d, int E, int target_blocks);
 hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, float *logits,
-                              int T, int d, int E, int splits, hipStream_t s);
+                              int T, int d, int E, int splits, int32_t *zero_counts,
+                              hipStream_t s);
 // Batches at or above this many tokens use the tiled router.
 constexpr int ROUTER_TILE_MIN_T = 512;
 // K splits that give the router about `target_blocks` workgroups.
 int router_splits(int T, int d, int E, int target_blocks);
-// Top-k over the sum of `n_planes` score planes plus `bias` (NULL: none);
-// the summed scores go to `logits_out` when not NULL.
-hipError_t launch_topk_softmax(const float *planes, int n_planes, const float *bias,
-                               float *logits_out, int T, int E, int k, int32_t *idx, float *w,
+// Top-k, softmax weights and histogram from final scores [T][E].
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
                                int32_t *counts, hipStream_t s);
 
 // permute.hip

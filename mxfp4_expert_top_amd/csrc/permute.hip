@@ -53,28 +53,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     const int32_t *__restrict__ counts, int e0, int nl, int nblk, int32_t *__restrict__ off,
     int32_t *__restrict__ blk)
 {
-    __shared__ int32_t part[1024];
+    __shared__ int32_t part[16];
     const int tid = threadIdx.x;
     // each thread sums a contiguous run of experts
     const int per = (nl + 1023) / 1024;
     const int lo = tid * per, hi = min(lo + per, nl);
     int s = 0;
     for (int i = lo; i < hi; i++) s += counts[e0 + i];
-    part[tid] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan of the 1024 partial sums
-    for (int o = 1; o < 1024; o <<= 1) {
-        int v = tid >= o ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
-    }
-    int run = part[tid] - s;  // exclusive prefix of this thread's run
+    int total;
+    int run = block_exclusive_scan(s, part, total);  // exclusive prefix of this thread's run
     for (int i = lo; i < hi; i++) {
         off[i] = run;
         run += counts[e0 + i];
     }
-    if (tid == 1023) off[nl] = part[1023];
+    if (tid == 0) off[nl] = total;
     __syncthreads();
     for (int le = tid; le < nl; le += 1024) {
         int r = off[le];
@@ -118,30 +110,13 @@ __global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
 // Small batches (T <= PERM_TB): the whole plan in one workgroup -- bitmap,
 // offsets, ranks and, when `plan` is given, the grouped-GEMM work list
 // (groups of R rows, as gemm_plan_kernel builds it).
-__device__ __forceinline__ int block_exclusive_scan_1024(int v, int *part, int &total)
-{
-    const int tid = threadIdx.x;
-    part[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        int u = tid >= o ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += u;
-        __syncthreads();
-    }
-    total = part[1023];
-    const int ex = part[tid] - v;
-    __syncthreads();
-    return ex;
-}
-
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ counts, int T, int k, int e0,
     int nl, int32_t *__restrict__ off, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
     int R, int max_groups, int32_t *__restrict__ plan, int plan_hdr)
 {
     extern __shared__ uint32_t bits[];  // nl * PERM_WORDS
-    __shared__ int32_t part[1024];
+    __shared__ int32_t part[16];
     __shared__ int32_t soff[MOE_MAX_EXPERTS_DEV + 1];
     const int tid = threadIdx.x;
     for (int i = tid; i < nl * PERM_WORDS; i += 1024) bits[i] = 0u;
@@ -156,7 +131,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int i0 = 2 * tid;
     const int c0 = i0 < nl ? counts[e0 + i0] : 0, c1 = i0 + 1 < nl ? counts[e0 + i0 + 1] : 0;
     int total;
-    const int ex = block_exclusive_scan_1024(c0 + c1, part, total);
+    const int ex = block_exclusive_scan(c0 + c1, part, total);
     if (i0 < nl) soff[i0] = ex;
     if (i0 + 1 < nl) soff[i0 + 1] = ex + c0;
     if (tid == 0) soff[nl] = total;
@@ -186,7 +161,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     // grouped-GEMM work list: ceil(count / R) groups per expert, expert-major
     const int g0 = i0 < nl ? (c0 + R - 1) / R : 0, g1 = i0 + 1 < nl ? (c1 + R - 1) / R : 0;
     int ngroups;
-    int pos = block_exclusive_scan_1024(g0 + g1, part, ngroups);
+    int pos = block_exclusive_scan(g0 + g1, part, ngroups);
     int2 *items = (int2 *)(plan + plan_hdr);
     for (int h = 0; h < 2; h++) {
         const int i = i0 + h;

@@ -30,8 +30,12 @@ constexpr int RT_TOK = 64, RT_EXP = 64, RT_K = 128;
 
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const bf16 *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
-    float *__restrict__ logits, int T, int d, int E, int k_per_split)
+    float *__restrict__ logits, int T, int d, int E, int k_per_split,
+    int32_t *__restrict__ zero_counts)
 {
+    // the histogram the top-k kernel fills next starts from zero
+    if (zero_counts && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+        for (int i = threadIdx.x; i < E; i += blockDim.x) zero_counts[i] = 0;
     // blockIdx.z selects a K range; with more than one range each writes its
     // partial sums to its own [T][E] plane (no bias) and the top-k kernel adds
     // the planes in order.
@@ -144,8 +148,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
 
 __global__ __launch_bounds__(256, 2) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wp, const float *__restrict__ bias,
-    float *__restrict__ logits, int T, int d, int E, int ksteps_per_split)
+    float *__restrict__ logits, int T, int d, int E, int ksteps_per_split,
+    int32_t *__restrict__ zero_counts)
 {
+    if (zero_counts && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < E; i += blockDim.x) zero_counts[i] = 0;
     __shared__ __attribute__((aligned(16))) bf16 As[2][RG_BM][RG_LD];
     __shared__ __attribute__((aligned(16))) bf16 Bs[2][RG_BN][RG_LD];
     const int n_nb = (E + RG_BN - 1) / RG_BN;
@@ -290,51 +297,42 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(
-    const float *__restrict__ planes, int n_planes, const float *__restrict__ bias,
-    float *__restrict__ logits_out, int T, int E, int k, int32_t *__restrict__ topk_idx,
+    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int32_t *__restrict__ counts)
 {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *l = planes + (int64_t)t * E;
-    const int64_t plane = (int64_t)T * E;
+    const float *l = logits + (int64_t)t * E;
 
-    // scores: the planes summed in order, then the bias
-    uint64_t key[NPL];
+    // all of the token's scores in flight at once (indices clamped, keys of
+    // padding lanes zeroed afterwards)
+    float v[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; i++) {
-        int e = i * 64 + lane;
-        float acc = 0.f;
-        if (e < E) {
-            acc = l[e];
-            for (int p = 1; p < n_planes; p++) acc += l[p * plane + e];
-            if (bias) acc += bias[e];
-            if (logits_out) logits_out[(int64_t)t * E + e] = acc;
-        }
-        key[i] = (e < E) ? score_key(acc, e) : 0ull;  // 0 never wins over a real key
-    }
+    for (int i = 0; i < NPL; i++) v[i] = l[min(i * 64 + lane, E - 1)];
+    uint64_t key[NPL];
     uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < NPL; i++) best = key[i] > best ? key[i] : best;
+    for (int i = 0; i < NPL; i++) {
+        const int e = i * 64 + lane;
+        key[i] = e < E ? score_key(v[i], e) : 0ull;  // 0 never wins over a real key
+        best = key[i] > best ? key[i] : best;
+    }
 
     float my_score = 0.f;
     int my_idx = 0;
     for (int j = 0; j < k; j++) {
-        uint64_t win = wave_max_u64(best);
-        int e = (int)(~(uint32_t)win);
+        const uint64_t win = wave_max_u64(best);  // wave-uniform
         if (lane == j) {
-            my_idx = e;
+            my_idx = (int)(~(uint32_t)win);
             my_score = key_score(win);
         }
-        if ((e & 63) == lane) {
-            // retire the winner and recompute this lane's best
-            best = 0;
+        // retire the winner (exactly one element matches) and refresh maxima
+        best = 0;
 #pragma unroll
-            for (int i = 0; i < NPL; i++) {
-                if (key[i] == win) key[i] = 0;
-                best = key[i] > best ? key[i] : best;
-            }
+        for (int i = 0; i < NPL; i++) {
+            key[i] = key[i] == win ? 0ull : key[i];
+            best = key[i] > best ? key[i] : best;
         }
     }
     const float top = __shfl(my_score, 0, 64);
@@ -397,11 +395,12 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s)
 }
 
 hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
-                                int T, int d, int E, int splits, hipStream_t s)
+                                int T, int d, int E, int splits, int32_t *zero_counts,
+                                hipStream_t s)
 {
     dim3 grid((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP, splits);
     hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, s, x, w, bias, logits, T, d, E,
-                       d / splits);
+                       d / splits, zero_counts);
     return hipGetLastError();
 }
 
@@ -439,12 +438,13 @@ int router_tile_splits(int T, int d, int E, int target_blocks)
 }
 
 hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, float *logits,
-                              int T, int d, int E, int splits, hipStream_t s)
+                              int T, int d, int E, int splits, int32_t *zero_counts,
+                              hipStream_t s)
 {
     const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
     const int steps = 3 * (d / RG_BK);
     hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), 0, s, x, wp, bias,
-                       logits, T, d, E, steps / splits);
+                       logits, T, d, E, steps / splits, zero_counts);
     return hipGetLastError();
 }
 
@@ -464,17 +464,16 @@ int router_splits(int T, int d, int E, int target_blocks)
     return best;
 }
 
-hipError_t launch_topk_softmax(const float *planes, int n_planes, const float *bias,
-                               float *logits_out, int T, int E, int k, int32_t *idx, float *w,
+hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
                                int32_t *counts, hipStream_t s)
 {
     dim3 grid((T + 3) / 4);
     const int npl = (E + 63) / 64;
-#define TK_CASE(N)                                                                             \
-    if (npl <= N) {                                                                            \
-        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, planes, n_planes, bias, \
-                           logits_out, T, E, k, idx, w, counts);                               \
-        return hipGetLastError();                                                              \
+#define TK_CASE(N)                                                                            \
+    if (npl <= N) {                                                                           \
+        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, logits, T, E, k, idx, \
+                           w, counts);                                                        \
+        return hipGetLastError();                                                             \
     }
     TK_CASE(2)
     TK_CASE(4)
