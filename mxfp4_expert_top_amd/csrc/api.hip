@@ -98,8 +98,15 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 struct LayerWs {
     size_t logits, planes, wsplit, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
     int splits;
-    bool tiled_router;
+    int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
 };
+enum { ROUTER_SKINNY = 0, ROUTER_SMALL = 1, ROUTER_TILED = 2 };
+
+static int router_kind(int T, int d)
+{
+    if (T <= ROUTER_SKINNY_MAX_T) return ROUTER_SKINNY;
+    return T >= ROUTER_TILE_MIN_T && d % 64 == 0 ? ROUTER_TILED : ROUTER_SMALL;
+}
 
 LayerWs layer_ws(const moe_layer_params *p)
 {
@@ -107,12 +114,13 @@ LayerWs layer_ws(const moe_layer_params *p)
     const size_t T = (size_t)p->T, E = (size_t)p->E, k = (size_t)p->k;
     const size_t A = T * k;
     size_t o = 0;
-    L.tiled_router = p->T >= ROUTER_TILE_MIN_T && p->d % 64 == 0;
-    L.splits = L.tiled_router ? router_tile_splits(p->T, p->d, p->E, 512)
-                              : router_splits(p->T, p->d, p->E, 512);
+    L.router = router_kind(p->T, p->d);
+    L.splits = L.router == ROUTER_TILED   ? router_tile_splits(p->T, p->d, p->E, 512)
+               : L.router == ROUTER_SMALL ? router_splits(p->T, p->d, p->E, 512)
+                                          : router_skinny_splits(p->T, p->d, p->E, 256);
     L.logits = o; o += round_up(T * E * 4);
     L.planes = o; o += L.splits > 1 ? round_up((size_t)L.splits * T * E * 4) : 0;
-    L.wsplit = o; o += L.tiled_router ? round_up(3 * E * (size_t)p->d * 2) : 0;
+    L.wsplit = o; o += L.router == ROUTER_TILED ? round_up(3 * E * (size_t)p->d * 2) : 0;
     L.idx = o;    o += round_up(A * 4);
     L.w = o;      o += round_up(A * 4);
     L.counts = o; o += round_up(E * 4);
@@ -178,10 +186,16 @@ int moe_route(const void *x, const float *w_router, const float *bias, float *lo
     hipStream_t s = as_stream(stream);
     if (T == 0 || logits_given) HIP_TRY(launch_fill_i32(expert_counts, E, 0, s));
     if (T == 0) return MOE_OK;
-    if (!logits_given)
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, 1,
-                                     expert_counts, s));
-    HIP_TRY(launch_topk_softmax(logits, T, E, k, topk_idx, topk_w, expert_counts, s));
+    if (!logits_given) {
+        if (router_kind(T, d) == ROUTER_SKINNY)
+            HIP_TRY(launch_router_skinny((const bf16 *)x, w_router, bias, logits, T, d, E, 1,
+                                         expert_counts, s));
+        else
+            HIP_TRY(launch_router_logits((const bf16 *)x, w_router, bias, logits, T, d, E, 1,
+                                         expert_counts, s));
+    }
+    HIP_TRY(launch_topk_softmax(logits, 1, nullptr, logits, T, E, k, topk_idx, topk_w,
+                                expert_counts, s));
     return MOE_OK;
 }
 
@@ -325,20 +339,23 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     hipEvent_t *ev = (hipEvent_t *)stage_events;
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    // with split-K planes the top-k kernel adds them in a fixed order, then the bias
     float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
     const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
-    if (L.tiled_router) {
+    if (L.router == ROUTER_TILED) {
         bf16 *wp = (bf16 *)(base + L.wsplit);
         HIP_TRY(launch_split_router(w_router, p->E, p->d, wp, s));
         HIP_TRY(launch_router_tile((const bf16 *)x, wp, b_in_gemm, planes, p->T, p->d, p->E,
                                    L.splits, counts, s));
-    } else {
+    } else if (L.router == ROUTER_SMALL) {
         HIP_TRY(launch_router_logits((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
                                      p->E, L.splits, counts, s));
+    } else {
+        HIP_TRY(launch_router_skinny((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
+                                     p->E, L.splits, counts, s));
     }
-    // split-K planes are summed in a fixed order (bias added there)
-    if (L.splits > 1) HIP_TRY(launch_sum_planes(planes, L.splits, bias, logits, p->T, p->E, s));
-    HIP_TRY(launch_topk_softmax(logits, p->T, p->E, p->k, idx, w, counts, s));
+    HIP_TRY(launch_topk_softmax(planes, L.splits, bias, logits, p->T, p->E, p->k, idx, w, counts,
+                                s));
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);

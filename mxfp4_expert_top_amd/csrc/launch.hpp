@@ -22,9 +22,14 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias, float *logits,
                                 int T, int d, int E, int splits, int32_t *zero_counts,
                                 hipStream_t s);
-// logits = sum of the planes in order + bias (E % 4 == 0).
-hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
-                             int T, int E, hipStream_t s);
+// Small batches (T <= ROUTER_SKINNY_MAX_T): weight-streaming router into
+// `splits` planes (splits == 1: final scores, bias included); splits must
+// divide d / 128.
+constexpr int ROUTER_SKINNY_MAX_T = 64;
+int router_skinny_splits(int T, int d, int E, int target_blocks);
+hipError_t launch_router_skinny(const bf16 *x, const float *w, const float *bias, float *out,
+                                int T, int d, int E, int splits, int32_t *zero_counts,
+                                hipStream_t s);
 // Larger batches: fp32 router weights -> three exact bf16 planes [3][E][d],
 // then a tiled bf16 GEMM over K' = 3 d into `splits` planes of [T][E].
 hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s);
@@ -36,9 +41,13 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
 constexpr int ROUTER_TILE_MIN_T = 512;
 // K splits that give the router about `target_blocks` workgroups.
 int router_splits(int T, int d, int E, int target_blocks);
-// Top-k, softmax weights and histogram from final scores [T][E].
-hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
-                               int32_t *counts, hipStream_t s);
+// Top-k, softmax weights and histogram. src holds n_planes planes [T][E];
+// with n_planes > 1 the scores are plane 0 + plane 1 + ... (in that order)
+// + bias, and are written to `logits`; with one plane src is the final scores
+// (bias and logits unused).
+hipError_t launch_topk_softmax(const float *src, int n_planes, const float *bias, float *logits,
+                               int T, int E, int k, int32_t *idx, float *w, int32_t *counts,
+                               hipStream_t s);
 
 // permute.hip
 // Tokens per permutation block (one bitmap of local experts x tokens in LDS).

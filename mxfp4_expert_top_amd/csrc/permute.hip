@@ -26,10 +26,14 @@ __device__ __forceinline__ void build_bitmap(uint32_t *bits, const int32_t *__re
     const int tl = threadIdx.x;
     const int t = t0 + tl;
     if (t < T) {
-        for (int j = 0; j < k; j++) {
-            int le = idx[(int64_t)t * k + j] - e0;
-            if (le >= 0 && le < nl) atomicOr(&bits[le * PERM_WORDS + tl / 32], 1u << (tl % 32));
-        }
+        int le[MOE_MAX_TOPK_DEV];
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK_DEV; j++)
+            if (j < k) le[j] = idx[(int64_t)t * k + j] - e0;
+#pragma unroll
+        for (int j = 0; j < MOE_MAX_TOPK_DEV; j++)
+            if (j < k && le[j] >= 0 && le[j] < nl)
+                atomicOr(&bits[le[j] * PERM_WORDS + tl / 32], 1u << (tl % 32));
     }
     __syncthreads();
 }
@@ -90,26 +94,36 @@ __global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
     const int64_t cap = (int64_t)T * k;
     const int w = tl / 32;
     const uint32_t below = (1u << (tl % 32)) - 1u;
-    for (int j = 0; j < k; j++) {
-        int le = idx[(int64_t)t * k + j] - e0;
-        int pos = -1;
-        if (le >= 0 && le < nl) {
-            const uint32_t *row = bits + le * PERM_WORDS;
-            int rank = __popc(row[w] & below);
-            for (int i = 0; i < w; i++) rank += __popc(row[i]);
-            int64_t p = (int64_t)base[(int64_t)blockIdx.x * nl + le] + rank;
-            if (p >= 0 && p < cap) {
-                pos = (int)p;
-                perm[pos] = t;
+    int lej[MOE_MAX_TOPK_DEV];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK_DEV; j++)
+        if (j < k) lej[j] = idx[(int64_t)t * k + j] - e0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK_DEV; j++) {
+        if (j < k) {
+            const int le = lej[j];
+            int pos = -1;
+            if (le >= 0 && le < nl) {
+                const uint32_t *row = bits + le * PERM_WORDS;
+                int rank = __popc(row[w] & below);
+                for (int i = 0; i < w; i++) rank += __popc(row[i]);
+                int64_t p = (int64_t)base[(int64_t)blockIdx.x * nl + le] + rank;
+                if (p >= 0 && p < cap) {
+                    pos = (int)p;
+                    perm[pos] = t;
+                }
             }
+            inv[(int64_t)t * k + j] = pos;
         }
-        inv[(int64_t)t * k + j] = pos;
     }
 }
 
 // Small batches (T <= PERM_TB): the whole plan in one workgroup -- bitmap,
 // offsets, ranks and, when `plan` is given, the grouped-GEMM work list
-// (groups of R rows, as gemm_plan_kernel builds it).
+// (groups of R rows, as gemm_plan_kernel builds it). One thread per
+// (token, slot) assignment, all of a thread's index loads issued together.
+constexpr int PS_PER = PERM_TB * MOE_MAX_TOPK_DEV / 1024;  // assignments per thread
+
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ counts, int T, int k, int e0,
     int nl, int32_t *__restrict__ off, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
@@ -119,42 +133,52 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     __shared__ int32_t part[16];
     __shared__ int32_t soff[MOE_MAX_EXPERTS_DEV + 1];
     const int tid = threadIdx.x;
+    const int A = T * k;
+    int le[PS_PER];
+    if (A > 0) {
+#pragma unroll
+        for (int u = 0; u < PS_PER; u++) le[u] = idx[min(tid + 1024 * u, A - 1)] - e0;
+    }
+#pragma unroll
+    for (int u = 0; u < PS_PER; u++)
+        if (A == 0 || tid + 1024 * u >= A || le[u] < 0 || le[u] >= nl) le[u] = -1;
     for (int i = tid; i < nl * PERM_WORDS; i += 1024) bits[i] = 0u;
     __syncthreads();
-    if (tid < T) {
-        for (int j = 0; j < k; j++) {
-            int le = idx[(int64_t)tid * k + j] - e0;
-            if (le >= 0 && le < nl) atomicOr(&bits[le * PERM_WORDS + tid / 32], 1u << (tid % 32));
-        }
+#pragma unroll
+    for (int u = 0; u < PS_PER; u++) {
+        if (le[u] < 0) continue;
+        const int t = (tid + 1024 * u) / k;
+        atomicOr(&bits[le[u] * PERM_WORDS + t / 32], 1u << (t % 32));
     }
     // offsets: each thread owns two consecutive local experts (nl <= 2048)
     const int i0 = 2 * tid;
     const int c0 = i0 < nl ? counts[e0 + i0] : 0, c1 = i0 + 1 < nl ? counts[e0 + i0 + 1] : 0;
     int total;
-    const int ex = block_exclusive_scan(c0 + c1, part, total);
+    const int ex = block_exclusive_scan(c0 + c1, part, total);  // also orders the bitmap ORs
     if (i0 < nl) soff[i0] = ex;
     if (i0 + 1 < nl) soff[i0 + 1] = ex + c0;
     if (tid == 0) soff[nl] = total;
     __syncthreads();
     for (int i = tid; i <= nl; i += 1024) off[i] = soff[i];
-    if (tid < T) {
-        const int64_t cap = (int64_t)T * k;
-        const int w = tid / 32;
-        const uint32_t below = (1u << (tid % 32)) - 1u;
-        for (int j = 0; j < k; j++) {
-            int le = idx[(int64_t)tid * k + j] - e0;
+    const int64_t cap = (int64_t)A;
+#pragma unroll
+    for (int u = 0; u < PS_PER; u++) {
+        const int a = tid + 1024 * u;
+        if (a < A) {
+            const int t = a / k;
             int pos = -1;
-            if (le >= 0 && le < nl) {
-                const uint32_t *row = bits + le * PERM_WORDS;
-                int rank = __popc(row[w] & below);
+            if (le[u] >= 0) {
+                const uint32_t *row = bits + le[u] * PERM_WORDS;
+                const int w = t / 32;
+                int rank = __popc(row[w] & ((1u << (t % 32)) - 1u));
                 for (int i = 0; i < w; i++) rank += __popc(row[i]);
-                const int64_t p = (int64_t)soff[le] + rank;
+                const int64_t p = (int64_t)soff[le[u]] + rank;
                 if (p < cap) {
                     pos = (int)p;
-                    perm[pos] = tid;
+                    perm[pos] = t;
                 }
             }
-            inv[(int64_t)tid * k + j] = pos;
+            inv[a] = pos;
         }
     }
     if (!plan) return;

@@ -112,6 +112,102 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Router scores for small batches (T <= 16 NT, NT <= 4): weight streaming.
+//
+// The fp32 router weights are the streamed operand. Lane (m, g) of a wave
+// reads 8 consecutive K elements of expert e0 + m per 32-wide K step, splits
+// them into the three exact bf16 parts in registers and multiplies each part
+// against every token (NT tiles of 16 rows) on the 16x16x32 matrix cores.
+// Workgroup = 16 experts x one K range (blockIdx.y) that its four waves split
+// four ways; their partial tiles are added in LDS in wave order. With more
+// than one K range each range writes a plane [T][E] of partial sums (no bias)
+// and the top-k kernel adds the planes in order.
+// ---------------------------------------------------------------------------
+constexpr int RS_STEP = 32, RS_BATCH = 8;
+
+template <int NT>
+__global__ __launch_bounds__(256) void router_skinny_kernel(
+    const bf16 *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ out, int T, int d, int E, int steps, int32_t *__restrict__ zero_counts)
+{
+    if (zero_counts && blockIdx.x == 0 && blockIdx.y == 0)
+        for (int i = threadIdx.x; i < E; i += blockDim.x) zero_counts[i] = 0;
+    __shared__ f32x4 red[4][NT][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int e0 = blockIdx.x * 16;
+    out += (int64_t)blockIdx.y * T * E;
+    // this wave's K range: steps x 32 elements; the lane's 8 at offset 8 g
+    const int64_t k0 = ((int64_t)blockIdx.y * 4 + wave) * steps * RS_STEP + 8 * g;
+    const float *wp = w + (int64_t)min(e0 + m, E - 1) * d + k0;
+    const bf16 *xp[NT];
+#pragma unroll
+    for (int i = 0; i < NT; i++) xp[i] = x + (int64_t)min(16 * i + m, T - 1) * d + k0;
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; i++) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < steps; s0 += RS_BATCH) {
+        // a batch of steps in flight at once (steps past the end repeat the
+        // last one and are not used)
+        float4 wa[RS_BATCH], wb[RS_BATCH];
+        bf16x8 xa[RS_BATCH][NT];
+#pragma unroll
+        for (int b = 0; b < RS_BATCH; b++) {
+            const int st = min(s0 + b, steps - 1) * RS_STEP;
+            wa[b] = *(const float4 *)(wp + st);
+            wb[b] = *(const float4 *)(wp + st + 4);
+#pragma unroll
+            for (int i = 0; i < NT; i++) xa[b][i] = *(const bf16x8 *)(xp[i] + st);
+        }
+#pragma unroll
+        for (int b = 0; b < RS_BATCH; b++) {
+            if (s0 + b < steps) {
+                const float v[8] = {wa[b].x, wa[b].y, wa[b].z, wa[b].w,
+                                    wb[b].x, wb[b].y, wb[b].z, wb[b].w};
+                bf16x8 hi, mid, lo;
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                    bf16 h_, m_, l_;
+                    split3_bf16(v[c], h_, m_, l_);
+                    hi[c] = h_;
+                    mid[c] = m_;
+                    lo[c] = l_;
+                }
+#pragma unroll
+                for (int i = 0; i < NT; i++) {
+                    acc[i] = mfma16x16x32(xa[b][i], hi, acc[i]);
+                    acc[i] = mfma16x16x32(xa[b][i], mid, acc[i]);
+                    acc[i] = mfma16x16x32(xa[b][i], lo, acc[i]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; i++) red[wave][i][lane] = acc[i];
+    __syncthreads();
+    // lane l of tile i holds C[4 (l / 16) + q][l % 16]: token 16 i + 4 (l / 16) + q,
+    // expert e0 + l % 16
+    for (int j = threadIdx.x; j < NT * 64; j += 256) {
+        const int i = j >> 6, l = j & 63;
+        f32x4 r = red[0][i][l];
+#pragma unroll
+        for (int wv = 1; wv < 4; wv++) {
+            const f32x4 o = red[wv][i][l];
+            r[0] += o[0]; r[1] += o[1]; r[2] += o[2]; r[3] += o[3];
+        }
+        const int e = e0 + (l & 15);
+        if (e >= E) continue;
+        const float bb = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int t = 16 * i + 4 * (l >> 4) + q;
+            if (t < T) out[(int64_t)t * E + e] = r[q] + bb;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Router scores for larger batches: the fp32 weights are split once into
 // three bf16 planes Wp[p][e][i] (hi, mid, lo; exact sum), then
 //   logits[t][e] = sum_p sum_i x[t][i] * Wp[p][e][i]  (+ bias)
@@ -242,10 +338,19 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
 // ---------------------------------------------------------------------------
 // Top-k select, softmax, histogram: one wavefront per token.
 //
-// A score maps to a 64-bit key that orders (score desc, expert asc):
-// the fp32 bits made monotone (with -0 folded onto +0) in the high word, the
-// complemented expert id in the low word. k rounds of a wave-wide max pick
-// the winners best first; the winning lane retires its element.
+// A score maps to a 64-bit key that orders (score desc, expert asc): the fp32
+// bits made monotone (with -0 folded onto +0) in the high word, the
+// complemented expert id in the low word. Keys are distinct, so the k winners
+// are the keys of rank 0..k-1, where a key's rank is the number of larger
+// keys. A token's 14 keys per lane are too many to rank directly, so:
+//   1. each lane's largest key is ranked among the 64 lane maxima; tau, the
+//      maximum of rank k-1, is a lower bound of the winners (k lanes hold a
+//      key >= tau);
+//   2. the keys >= tau (usually about 20) are packed into LDS and ranked
+//      among themselves: ranks 0..k-1 are the winners, best first.
+// More than 64 candidates (only for unusual score patterns) take k rounds of
+// a wave-wide maximum instead. Every step is a short fixed sequence: no
+// chains of k or 32 dependent rounds.
 // ---------------------------------------------------------------------------
 constexpr int TK_MAX_PER_LANE = MOE_MAX_EXPERTS_DEV / 64;
 
@@ -295,88 +400,149 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
     return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Number of the 64 keys in LDS that are larger than `mine`.
+__device__ __forceinline__ int rank64(const uint64_t *s, uint64_t mine)
+{
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 64; j++) r += s[j] > mine ? 1 : 0;
+    return r;
+}
+
+// With n_planes > 1 the scores are first assembled from split-K planes of
+// partial sums: plane 0 + plane 1 + ... in that order, then the bias, and
+// written to `logits`; with one plane `src` already holds the final scores.
 template <int NPL>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(
-    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
+    const float *__restrict__ src, int n_planes, const float *__restrict__ bias,
+    float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int32_t *__restrict__ counts)
 {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float *l = logits + (int64_t)t * E;
+    constexpr int PB = NPL <= 16 ? 8 : 2;  // planes loaded per batch
+    __shared__ uint64_t s_key[4][64];
+    __shared__ uint64_t s_ord[4][MOE_MAX_TOPK_DEV];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    // a wave past the last token repeats it and stores nothing (every wave
+    // reaches the barriers)
+    const bool t_ok = t < T;
+    const int tt = t_ok ? t : T - 1;
+    const int64_t plane = (int64_t)T * E;
+    const float *l = src + (int64_t)tt * E;
 
-    // all of the token's scores in flight at once (indices clamped, keys of
-    // padding lanes zeroed afterwards)
+    // the token's scores: one batch of loads per PB planes (indices clamped)
     float v[NPL];
+    if (n_planes == 1) {
 #pragma unroll
-    for (int i = 0; i < NPL; i++) v[i] = l[min(i * 64 + lane, E - 1)];
+        for (int i = 0; i < NPL; i++) v[i] = l[min(i * 64 + lane, E - 1)];
+    } else {
+        for (int p = 0; p < n_planes; p += PB) {
+            float u[PB][NPL];
+#pragma unroll
+            for (int q = 0; q < PB; q++)
+#pragma unroll
+                for (int i = 0; i < NPL; i++)
+                    u[q][i] = l[min(p + q, n_planes - 1) * plane + min(i * 64 + lane, E - 1)];
+#pragma unroll
+            for (int i = 0; i < NPL; i++) v[i] = p == 0 ? u[0][i] : v[i] + u[0][i];
+#pragma unroll
+            for (int q = 1; q < PB; q++)
+                if (p + q < n_planes)
+#pragma unroll
+                    for (int i = 0; i < NPL; i++) v[i] += u[q][i];
+        }
+        float *lo = logits + (int64_t)tt * E;
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+            const int e = i * 64 + lane;
+            if (e < E) {
+                if (bias) v[i] += bias[e];
+                if (t_ok) lo[e] = v[i];
+            }
+        }
+    }
     uint64_t key[NPL];
     uint64_t best = 0;
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
         const int e = i * 64 + lane;
-        key[i] = e < E ? score_key(v[i], e) : 0ull;  // 0 never wins over a real key
+        key[i] = e < E ? score_key(v[i], e) : 0ull;  // 0 ranks below every real key
         best = key[i] > best ? key[i] : best;
     }
 
-    float my_score = 0.f;
-    int my_idx = 0;
-    for (int j = 0; j < k; j++) {
-        const uint64_t win = wave_max_u64(best);  // wave-uniform
-        if (lane == j) {
-            my_idx = (int)(~(uint32_t)win);
-            my_score = key_score(win);
-        }
-        // retire the winner (exactly one element matches) and refresh maxima
-        best = 0;
+    // candidates, one per lane (0 past the count)
+    uint64_t cand = best;
+    int ncand = 64;
+    if constexpr (NPL > 1) {
+        // E > 64: every lane holds a real key, so the 64 maxima are distinct
+        s_key[wv][lane] = best;
+        __syncthreads();
+        const int r0 = rank64(s_key[wv], best);
+        const uint64_t at = __ballot(r0 == k - 1);  // exactly one lane
+        const uint64_t tau = readlane_u64(best, (int)__builtin_ctzll(at));
+        __syncthreads();
+        int base = 0;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
-            key[i] = key[i] == win ? 0ull : key[i];
-            best = key[i] > best ? key[i] : best;
+            const bool p = key[i] >= tau;
+            const uint64_t msk = __ballot(p);
+            const int pos = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                       (uint32_t)(msk >> 32),
+                                       __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+            if (p && pos < 64) s_key[wv][pos] = key[i];
+            base += __popcll(msk);
+        }
+        ncand = base;
+        if (lane >= ncand) s_key[wv][lane] = 0ull;
+        __syncthreads();
+        cand = lane < ncand ? s_key[wv][lane] : 0ull;
+    } else {
+        s_key[wv][lane] = cand;
+        __syncthreads();
+    }
+    // rank the candidates (zeros past the count rank below all of them)
+    if (ncand <= 64) {
+        const int r = rank64(s_key[wv], cand);
+        if (lane < ncand && r < k) s_ord[wv][r] = cand;
+    }
+    __syncthreads();
+    uint64_t my = 0;
+    if (ncand <= 64) {
+        if (lane < k) my = s_ord[wv][lane];
+    } else {
+        // k rounds of a wave-wide maximum; the winner's slot is retired
+        for (int j = 0; j < k; j++) {
+            const uint64_t win = wave_max_u64(best);
+            if (lane == j) my = win;
+            best = 0;
+#pragma unroll
+            for (int i = 0; i < NPL; i++) {
+                key[i] = key[i] == win ? 0ull : key[i];
+                best = key[i] > best ? key[i] : best;
+            }
         }
     }
-    const float top = __shfl(my_score, 0, 64);
+    const int my_idx = (int)(~(uint32_t)my);
+    const float my_score = key_score(my);
+
+    // softmax over the selected scores, summed best first
+    const float top = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(my_score)));
     const float z = (lane < k) ? expf(my_score - top) : 0.f;
     float sum = 0.f;
-    for (int j = 0; j < k; j++) sum += __shfl(z, j, 64);  // j order, as a plain loop
-    if (lane < k) {
+    for (int j = 0; j < k; j++)
+        sum += __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(z), j));
+    if (t_ok && lane < k) {
         topk_idx[(int64_t)t * k + lane] = my_idx;
         topk_w[(int64_t)t * k + lane] = z / sum;
         atomicAdd(&counts[my_idx], 1);
     }
-}
-
-// Router scores from split-K planes: logits = sum of the planes in order +
-// bias. Four consecutive scores per thread, every plane's load issued before
-// the sums.
-__global__ __launch_bounds__(256) void sum_planes_kernel(const float *__restrict__ planes,
-                                                         int n_planes, int64_t plane, int E,
-                                                         const float *__restrict__ bias,
-                                                         float *__restrict__ logits)
-{
-    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (i4 >= plane) return;
-    float4 acc = *(const float4 *)(planes + i4);
-    int p = 1;
-    for (; p + 4 <= n_planes; p += 4) {
-        const float4 a = *(const float4 *)(planes + p * plane + i4);
-        const float4 b = *(const float4 *)(planes + (p + 1) * plane + i4);
-        const float4 c = *(const float4 *)(planes + (p + 2) * plane + i4);
-        const float4 d = *(const float4 *)(planes + (p + 3) * plane + i4);
-        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-        acc.x += b.x; acc.y += b.y; acc.z += b.z; acc.w += b.w;
-        acc.x += c.x; acc.y += c.y; acc.z += c.z; acc.w += c.w;
-        acc.x += d.x; acc.y += d.y; acc.z += d.z; acc.w += d.w;
-    }
-    for (; p < n_planes; p++) {
-        const float4 a = *(const float4 *)(planes + p * plane + i4);
-        acc.x += a.x; acc.y += a.y; acc.z += a.z; acc.w += a.w;
-    }
-    if (bias) {
-        const int e = (int)(i4 % E);  // E % 4 == 0: the four scores share a row
-        acc.x += bias[e]; acc.y += bias[e + 1]; acc.z += bias[e + 2]; acc.w += bias[e + 3];
-    }
-    *(float4 *)(logits + i4) = acc;
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v)
@@ -404,17 +570,6 @@ hipError_t launch_router_logits(const bf16 *x, const float *w, const float *bias
     return hipGetLastError();
 }
 
-hipError_t launch_sum_planes(const float *planes, int n_planes, const float *bias, float *logits,
-                             int T, int E, hipStream_t s)
-{
-    const int64_t plane = (int64_t)T * E;
-    const int64_t threads = plane / 4;
-    if (threads <= 0) return hipSuccess;
-    hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       planes, n_planes, plane, E, bias, logits);
-    return hipGetLastError();
-}
-
 hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s)
 {
     const int64_t n = (int64_t)E * d;
@@ -427,7 +582,6 @@ int router_tile_splits(int T, int d, int E, int target_blocks)
 {
     const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
     const int steps = 3 * (d / RG_BK);
-    if (E % 4) return 1;
     int best = 1;
     for (int sp = 1; sp <= steps; sp++) {
         if (steps % sp) continue;
@@ -448,9 +602,44 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
     return hipGetLastError();
 }
 
+int router_skinny_splits(int T, int d, int E, int target_blocks)
+{
+    (void)T;
+    // K ranges of 4 x 32 x steps elements; the largest count whose grid
+    // stays within target_blocks, at most 4 planes for the top-k kernel
+    const int tiles = (E + 15) / 16;
+    const int units = d / (4 * RS_STEP);
+    int best = 1;
+    for (int sp = 1; sp <= 4; sp++) {
+        if (units % sp) continue;
+        if ((int64_t)tiles * sp > target_blocks) break;
+        best = sp;
+    }
+    return best;
+}
+
+hipError_t launch_router_skinny(const bf16 *x, const float *w, const float *bias, float *out,
+                                int T, int d, int E, int splits, int32_t *zero_counts,
+                                hipStream_t s)
+{
+    dim3 grid((E + 15) / 16, splits);
+    const int steps = d / (4 * RS_STEP * splits);
+    const float *b = splits > 1 ? nullptr : bias;
+#define RS_CASE(N)                                                                          \
+    if (T <= 16 * N) {                                                                      \
+        hipLaunchKernelGGL(router_skinny_kernel<N>, grid, dim3(256), 0, s, x, w, b, out, T, \
+                           d, E, steps, zero_counts);                                       \
+        return hipGetLastError();                                                           \
+    }
+    RS_CASE(1)
+    RS_CASE(2)
+    RS_CASE(4)
+#undef RS_CASE
+    return hipErrorInvalidValue;
+}
+
 int router_splits(int T, int d, int E, int target_blocks)
 {
-    if (E % 4) return 1;  // the plane sum reads scores four at a time
     // Split K while the token x expert tiles alone leave the chip idle. Each
     // split is a whole number of 128-wide K steps.
     const int tiles = ((T + RT_TOK - 1) / RT_TOK) * ((E + RT_EXP - 1) / RT_EXP);
@@ -464,16 +653,18 @@ int router_splits(int T, int d, int E, int target_blocks)
     return best;
 }
 
-hipError_t launch_topk_softmax(const float *logits, int T, int E, int k, int32_t *idx, float *w,
-                               int32_t *counts, hipStream_t s)
+hipError_t launch_topk_softmax(const float *src, int n_planes, const float *bias, float *logits,
+                               int T, int E, int k, int32_t *idx, float *w, int32_t *counts,
+                               hipStream_t s)
 {
+    if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4);
     const int npl = (E + 63) / 64;
-#define TK_CASE(N)                                                                            \
-    if (npl <= N) {                                                                           \
-        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, logits, T, E, k, idx, \
-                           w, counts);                                                        \
-        return hipGetLastError();                                                             \
+#define TK_CASE(N)                                                                        \
+    if (npl <= N) {                                                                       \
+        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, s, src, n_planes,  \
+                           bias, logits, T, E, k, idx, w, counts);                        \
+        return hipGetLastError();                                                         \
     }
     TK_CASE(2)
     TK_CASE(4)

@@ -69,13 +69,19 @@ def _tie_logits(T, E, seed):
     lg[3] = 0.75                            # all equal
     lg[4] = rng.integers(-3, 3, size=E)
     lg[5, E // 2:] = lg[5, : E - E // 2]    # duplicated halves
+    if T > 7:
+        # experts e with e % 64 < 16 far ahead: many large scores share the
+        # same lanes of a 64-wide layout (a kernel that packs candidates per
+        # lane sees more than 64 of them)
+        lg[6, (np.arange(E) % 64) < 16] += 10.0
+        lg[7] = np.arange(E, dtype=np.float32)[::-1] / E  # strictly decreasing by id
     return lg
 
 
 @pytest.mark.parametrize("T,E,k", [(300, 896, 16), (77, 64, 8), (40, 17, 1), (33, 2048, 32),
                                    (6, 16, 16), (1, 896, 16)])
 def test_route_injected_logits_bitexact(m, T, E, k):
-    lg = _tie_logits(max(T, 6), E, T * 7 + E)[:T]
+    lg = _tie_logits(max(T, 8), E, T * 7 + E)[:T]
     _, idx, w, cnt = _route_gpu(m, lg, k)
     oi, ow = oracle.topk_softmax(lg, k)
     assert np.array_equal(idx, oi)
@@ -95,7 +101,9 @@ def test_route_t0_zeroes_counts(m):
 
 
 @pytest.mark.parametrize("T,d,E,bias", [(77, 3584, 896, False), (130, 256, 40, True),
-                                        (1, 3584, 896, True)])
+                                        (1, 3584, 896, True), (16, 3584, 896, False),
+                                        (20, 512, 40, True), (64, 3584, 896, True),
+                                        (33, 128, 17, False)])
 def test_router_scores_and_replay(m, T, d, E, bias):
     from synth import make_router, make_tokens
     cfg = LayerConfig("r", T=T, I=128, d=d, E=E, bias="normal" if bias else None)
