@@ -78,6 +78,24 @@ enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2
  * produces (same codes and scales, permuted for the kernels). */
 enum moe_weight_layout { MOE_LAYOUT_OCP = 0, MOE_LAYOUT_PACKED = 1 };
 
+/* Schedules of the grouped expert GEMMs (the `mode` argument). All give the
+ * same results up to fp32 summation order; they differ in how work is cut:
+ *   STREAM:   groups of 16 rows, each weight streamed once per group
+ *             (few rows per expert: decode)
+ *   TILE128:  128-row x 256-weight-row tiles, two workgroups per CU
+ *   TILE256:  256-row x 256-weight-row tiles, an expert's rows cut into
+ *             nearly equal groups (an expert of up to 256 rows reads its
+ *             weights once)
+ *   TILED:    TILE256 when max_rows / num_local <= 192, else TILE128
+ *   AUTO:     STREAM when max_rows / num_local < 48, else TILED */
+enum moe_sched {
+    MOE_SCHED_AUTO = 0,
+    MOE_SCHED_STREAM = 1,
+    MOE_SCHED_TILED = 2,
+    MOE_SCHED_TILE128 = 3,
+    MOE_SCHED_TILE256 = 4
+};
+
 /* Limits of this build. */
 #define MOE_MX_BLOCK 32
 #define MOE_MAX_TOPK 32
@@ -175,8 +193,7 @@ int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, i
  *   expert_offsets [num_local + 1] int32 on the device
  *   max_rows: a host-side upper bound on off[num_local] (e.g. T*k); it sizes
  *             the launch, rows beyond off[num_local] are never touched
- *   mode: 0 = choose from max_rows/num_local, 1 = weight-streaming schedule
- *         (few rows per expert), 2 = tiled schedule (many rows per expert)
+ *   mode: enum moe_sched (0 = choose from max_rows / num_local)
  *   ws / ws_bytes: scratch of moe_grouped_gemm_workspace_size(...) bytes (the
  *         device-built work list)
  * Requirements: lda >= K and ldo >= N, both multiples of 8; a_rows entries

@@ -20,7 +20,7 @@ _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mxfp4.so"
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 DT_BF16, DT_F32 = 0, 1
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
-MODE_AUTO, MODE_STREAM, MODE_TILED = 0, 1, 2
+MODE_AUTO, MODE_STREAM, MODE_TILED, MODE_TILE128, MODE_TILE256 = 0, 1, 2, 3, 4
 LAYOUT_OCP, LAYOUT_PACKED = 0, 1
 MX_BLOCK = 32
 

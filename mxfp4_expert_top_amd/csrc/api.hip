@@ -147,7 +147,7 @@ int check_layer_params(const moe_layer_params *p)
           MOE_ERR_INVALID_ARG);
     CHECK(p->act == MOE_ACT_SILU_MUL || p->act == MOE_ACT_GELU_TANH_MUL, MOE_ERR_INVALID_ARG);
     CHECK(p->out_dtype == MOE_DT_BF16 || p->out_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
-    CHECK(p->mode >= 0 && p->mode <= 2, MOE_ERR_INVALID_ARG);
+    CHECK(p->mode >= MOE_SCHED_AUTO && p->mode <= MOE_SCHED_TILE256, MOE_ERR_INVALID_ARG);
     CHECK(p->weight_layout == MOE_LAYOUT_OCP || p->weight_layout == MOE_LAYOUT_PACKED,
           MOE_ERR_INVALID_ARG);
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
@@ -252,7 +252,8 @@ int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, i
 
 size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode)
 {
-    if (num_local < 1 || max_rows < 0 || mode < 0 || mode > 2) return 0;
+    if (num_local < 1 || max_rows < 0 || mode < MOE_SCHED_AUTO || mode > MOE_SCHED_TILE256)
+        return 0;
     return grouped_gemm_ws_bytes(num_local, max_rows, N, mode);
 }
 
@@ -264,7 +265,7 @@ int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
                            int out_dtype, int64_t ldo, int mode, void *ws, size_t ws_bytes,
                            moe_stream_t stream)
 {
-    CHECK(mode >= 0 && mode <= 2, MOE_ERR_INVALID_ARG);
+    CHECK(mode >= MOE_SCHED_AUTO && mode <= MOE_SCHED_TILE256, MOE_ERR_INVALID_ARG);
     int rc = check_gemm(a, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
                         num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
                         ldo);

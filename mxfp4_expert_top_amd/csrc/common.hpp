@@ -77,14 +77,24 @@ __device__ __forceinline__ void split3_bf16(float v, bf16 &hi, bf16 &mid, bf16 &
 // Activation stages (the elementwise step between the two projections).
 enum { ACT_NONE = 0, ACT_SILU_MUL = 1, ACT_GELU_TANH_MUL = 2 };
 
+// g * u / (1 + exp(-z)) with the hardware exp2 and reciprocal (each within
+// about 1 ulp); exp overflowing to inf gives 0, the limit.
+__device__ __forceinline__ float gated_sigmoid(float g, float u, float z)
+{
+    const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+    return g * u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// silu(g) * u = g * sigmoid(g) * u; gelu_tanh(g) * u =
+// 0.5 g (1 + tanh(y)) u = g * sigmoid(2 y) * u with y = sqrt(2/pi) (g + 0.044715 g^3).
 template <int ACT>
 __device__ __forceinline__ float act_apply(float g, float u)
 {
     if constexpr (ACT == ACT_SILU_MUL) {
-        return g / (1.0f + expf(-g)) * u;
+        return gated_sigmoid(g, u, g);
     } else if constexpr (ACT == ACT_GELU_TANH_MUL) {
-        float inner = 0.7978845608028654f * (g + 0.044715f * g * g * g);
-        return 0.5f * g * (1.0f + tanhf(inner)) * u;
+        const float y = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+        return gated_sigmoid(g, u, 2.0f * y);
     } else {
         return g;
     }
@@ -116,6 +126,19 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int &to
     __syncthreads();  // scratch may be reused by the caller
     total = all;
     return before + inc - v;
+}
+
+// Work items of the grouped GEMMs: an expert's c rows in g = ceil(c / R)
+// groups, either R rows each (the last one shorter) or, `balanced`, of
+// nearly equal size (sizes differ by at most one), so that no group is a
+// short tail that streams a whole weight tile for a few rows.
+// Item = {expert | rows << 16, first row} (experts < 2^16, rows <= R).
+__device__ __forceinline__ int2 plan_item(int e, int off_e, int c, int g, int i, int R,
+                                          bool balanced)
+{
+    const int s = balanced ? (int)((int64_t)i * c / g) : i * R;
+    const int t = balanced ? (int)((int64_t)(i + 1) * c / g) : min((i + 1) * R, c);
+    return make_int2(e | ((t - s) << 16), off_e + s);
 }
 
 template <typename T>

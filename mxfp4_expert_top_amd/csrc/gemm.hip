@@ -8,6 +8,8 @@
 // scaled FP4->bf16 convert (exact: an E2M1 value times a power of two), and
 // feed v_mfma_f32_16x16x32_bf16 with fp32 accumulation. No dequantised copy of
 // a weight ever reaches memory.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -17,11 +19,11 @@ constexpr int PLAN_HDR = 64;  // int32 slots before the work items
 constexpr int ST_ROWS = 16;   // streaming schedule: permuted rows per group
 
 // ---------------------------------------------------------------------------
-// Work plan: groups of up to R consecutive rows of one expert, expert-major.
-// plan[0] = number of groups; items (expert, first row) from plan[PLAN_HDR].
+// Work plan: each expert's rows in ceil(count / R) groups (plan_item),
+// expert-major. plan[0] = number of groups; items from plan[PLAN_HDR].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int32_t *__restrict__ off, int nl,
-                                                         int R, int max_groups,
+                                                         int R, int max_groups, int balanced,
                                                          int32_t *__restrict__ plan)
 {
     __shared__ int32_t part[16];
@@ -34,9 +36,9 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(const int32_t *__restri
     int pos = block_exclusive_scan(s, part, ngroups);
     int2 *items = (int2 *)(plan + PLAN_HDR);
     for (int i = lo; i < hi; i++) {
-        const int c = off[i + 1] - off[i];
-        for (int r = 0; r < c; r += R, pos++)
-            if (pos < max_groups) items[pos] = make_int2(i, off[i] + r);
+        const int c = off[i + 1] - off[i], g = (c + R - 1) / R;
+        for (int j = 0; j < g; j++, pos++)
+            if (pos < max_groups) items[pos] = plan_item(i, off[i], c, g, j, R, balanced);
     }
     if (tid == 0) plan[0] = min(ngroups, max_groups);
 }
@@ -116,8 +118,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const int n0 = nb0 + wave * COLS_W;          // first output column of the wave
     const bool wave_on = n0 < N;                 // N is a multiple of COLS_W
     const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
-    const int e = it.x, r0 = it.y;
-    const int rend = min(r0 + ST_ROWS, off[e + 1]);
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
     const int rc = min(r0 + m, rend - 1);
     const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
     const bf16 *ap = a + arow * lda + 32 * g;
@@ -299,8 +300,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
     if (local >= per_xcd || wi >= total) return;
     const int grp = wi / nblk, nb = wi - grp * nblk;
     const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
-    const int e = it.x, r0 = it.y;
-    const int rend = min(r0 + TL_BM, off[e + 1]);
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
     const int mrows = rend - r0;
     const int n0 = nb * COLS;
 
@@ -442,6 +442,234 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Tiled schedule with 256-row tiles (many rows per expert: prefill).
+//
+// Workgroup tile: TB_BM = 256 permuted rows of one expert x TB_BN = 256
+// weight rows, K step 64. 8 waves as 4 row quarters x 2 weight halves; a wave
+// owns 2 row tiles of 32 x 4 weight tiles of 32 on v_mfma_f32_32x32x16_bf16.
+// Per MFMA sub-step a wave reads 2 A fragments and 4 decoded weight
+// fragments (the weights stay 4-bit in LDS), so LDS traffic per MFMA is about
+// 3/8 of a bf16 x bf16 tile of the same shape. A GLU tile holds 128 W1 rows
+// and the same 128 W2 rows (128 output columns): weight half ch takes W1 and
+// W2 rows 64 ch .. 64 ch + 63, and act(gate, up) is applied in registers.
+//
+// An expert with up to 256 rows is one tile row, so each weight byte is read
+// once per expert. Row quarter q owns row tiles q and q + 4 (rows 32 q .. and
+// 128 + 32 q ..); tiles wholly past the expert's end are skipped (the K loop
+// is specialised on the wave's count of active tiles, so its MFMA stream has
+// no branches). Wave w = 2 q + ch runs on SIMD w % 4, which spreads a short
+// tile's active row tiles over the four SIMDs.
+//
+// Pipeline: two LDS stages and two register stages; global loads run two K
+// steps ahead of the MFMAs (the last steps repeat step nk - 1, so the count
+// of loads in flight is fixed); one barrier per K step.
+//
+// MFMA operands: lane L supplies row L % 32 and 8 contraction elements of
+// lane group h = L / 32; in a K step lane group h takes MX block h, sub-step
+// s its elements 32 h + 8 s .. +8.
+// ---------------------------------------------------------------------------
+constexpr int TB_BM = 256, TB_BN = 256, TB_BK = 64, TB_THREADS = 512;
+constexpr int TB_ALD = TB_BK + 8;  // 72 bf16 = 144 bytes per A row in LDS
+constexpr size_t TB_LDS = (size_t)2 * TB_BM * TB_ALD * 2 + (size_t)2 * TB_BN * (TB_BK / 2) +
+                          (size_t)2 * TB_BN * (TB_BK / 32);
+
+template <int ACT, typename OutT, bool PACKED>
+__global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
+    const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
+    const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
+    const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
+    const int32_t *__restrict__ off, const int32_t *__restrict__ plan, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int COLS = GLU ? TB_BN / 2 : TB_BN;
+    extern __shared__ __attribute__((aligned(16))) uint8_t tb_lds[];
+    bf16 (*As)[TB_BM][TB_ALD] = (bf16 (*)[TB_BM][TB_ALD])tb_lds;
+    uint8_t (*Bq)[TB_BN][TB_BK / 2] =
+        (uint8_t (*)[TB_BN][TB_BK / 2])(tb_lds + (size_t)2 * TB_BM * TB_ALD * 2);
+    uint8_t (*Bs)[TB_BN][TB_BK / 32] = (uint8_t (*)[TB_BN][TB_BK / 32])(
+        tb_lds + (size_t)2 * TB_BM * TB_ALD * 2 + (size_t)2 * TB_BN * (TB_BK / 2));
+
+    const int nblk = (N + COLS - 1) / COLS;
+    const int total = plan[0] * nblk;
+    // XCD-aware order (as in the 128-row tiled schedule)
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int wi = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || wi >= total) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int2 it = ((const int2 *)(plan + PLAN_HDR))[grp];
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
+    const int mrows = rend - r0;
+    const int n0 = nb * COLS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ch = wave & 1, q = wave >> 1;
+
+    // ---- global -> LDS assignment
+    // A: 4 loads per thread, each wave instruction covers 8 whole rows of the
+    // K step: row 32 wave + 8 j + lane / 8, 16 bytes at column 8 (lane % 8)
+    const int acol = 8 * (lane & 7);
+    const bf16 *ag[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int rc = min(r0 + 32 * wave + 8 * j + (lane >> 3), rend - 1);
+        const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+        ag[j] = a + arow * lda + acol;
+    }
+    // B: thread -> weight row tid / 2 of the tile, 16 code bytes (one MX block)
+    const int br = tid >> 1, bh = tid & 1;
+    int wrow;
+    const uint8_t *wcb, *wsb;
+    if (GLU) {
+        wrow = min(n0 + (br & 127), N - 1);
+        wcb = br < 128 ? w1c : w2c;
+        wsb = br < 128 ? w1s : w2s;
+    } else {
+        wrow = min(n0 + br, N - 1);
+        wcb = w1c;
+        wsb = w1s;
+    }
+    const int64_t wr64 = (int64_t)e * N + wrow;
+    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const uint8_t *bg, *sg;
+    if constexpr (PACKED) {
+        const int64_t rb = wr64 / 16;
+        const int mm = (int)(wr64 % 16);
+        bg = wcb + rb * nch * 1024 + mm * 16;
+        sg = wsb + rb * nc4 * 256 + mm * 4;
+    } else {
+        bg = wcb + wr64 * (K / 2) + 16 * bh;
+        sg = wsb + wr64 * (K / 32) + bh;
+    }
+
+    u32x4 ra0[4], ra1[4], rb0, rb1;
+    uint8_t rs0, rs1;
+    auto gload = [&](u32x4 *ra, u32x4 &rbv, uint8_t &rsv, int kt) {
+        const int k0 = kt * TB_BK;
+#pragma unroll
+        for (int j = 0; j < 4; j++) ra[j] = *(const u32x4 *)(ag[j] + k0);
+        if constexpr (PACKED) {
+            const int c = kt >> 1, gg = 2 * (kt & 1) + bh;
+            rbv = *(const u32x4 *)(bg + c * 1024 + gg * 256);
+            rsv = sg[(c >> 2) * 256 + gg * 64 + (c & 3)];
+        } else {
+            rbv = *(const u32x4 *)(bg + k0 / 2);
+            rsv = sg[k0 / 32];
+        }
+    };
+    auto lstore = [&](int st, const u32x4 *ra, const u32x4 &rbv, uint8_t rsv) {
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            *(u32x4 *)(&As[st][32 * wave + 8 * j + (lane >> 3)][acol]) = ra[j];
+        *(u32x4 *)(&Bq[st][br][16 * bh]) = rbv;
+        Bs[st][br][bh] = rsv;
+    };
+
+    // ---- wave tiles
+    const int h = lane >> 5, l32 = lane & 31;
+    // weight tiles j = 0..3 of this wave inside the LDS tile
+    int bt[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (GLU) bt[j] = (j >= 2 ? 128 : 0) + 64 * ch + 32 * (j & 1);  // W1 x2, then W2 x2
+        else bt[j] = 128 * ch + 32 * j;
+    }
+    // active row tiles: q (rows 32 q ..) and q + 4 (rows 128 + 32 q ..)
+    const int n_on = (32 * q < mrows ? 1 : 0) + (128 + 32 * q < mrows ? 1 : 0);
+    const int nk = K / TB_BK;  // even: K is a multiple of 128
+
+    auto run = [&](auto ni_c) {
+        constexpr int NI = decltype(ni_c)::value;
+        f32x16 acc[NI > 0 ? NI : 1][4];
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+        auto compute = [&](int st) {
+            if constexpr (NI > 0) {
+                u32x4 qd[4];
+                float f[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int row = bt[j] + l32;
+                    qd[j] = *(const u32x4 *)(&Bq[st][row][16 * h]);
+                    f[j] = e8m0_to_f32(Bs[st][row][h]);
+                }
+#pragma unroll
+                for (int s = 0; s < 4; s++) {
+                    bf16x8 af[NI];
+#pragma unroll
+                    for (int i = 0; i < NI; i++)
+                        af[i] = *(const bf16x8 *)(&As[st][32 * q + 128 * i + l32][32 * h + 8 * s]);
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const bf16x8 bv = mx_decode8(qd[j][s], f[j]);
+#pragma unroll
+                        for (int i = 0; i < NI; i++) acc[i][j] = mfma32x32x16(af[i], bv, acc[i][j]);
+                    }
+                }
+            }
+        };
+
+        gload(ra0, rb0, rs0, 0);
+        gload(ra1, rb1, rs1, 1);
+        lstore(0, ra0, rb0, rs0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            // stage 0 holds step kt; registers set 1 hold step kt + 1
+            gload(ra0, rb0, rs0, min(kt + 2, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+            compute(0);
+            lstore(1, ra1, rb1, rs1);
+            __syncthreads();
+            // stage 1 holds step kt + 1; registers set 0 hold step kt + 2
+            gload(ra1, rb1, rs1, min(kt + 3, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            lstore(0, ra0, rb0, rs0);  // past the end: a copy of the last step, unused
+            __syncthreads();
+        }
+
+        // epilogue: lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int rl = 32 * q + 128 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (rl >= mrows) continue;
+                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                if constexpr (GLU) {
+#pragma unroll
+                    for (int jj = 0; jj < 2; jj++) {
+                        const int col = n0 + 64 * ch + 32 * jj + l32;
+                        if (col < N)
+                            store_out<OutT>(orow + col,
+                                            act_apply<ACT>(acc[i][jj][v], acc[i][2 + jj][v]));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int col = n0 + 128 * ch + 32 * j + l32;
+                        if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                    }
+                }
+            }
+        }
+    };
+    // every branch runs the same barriers (1 + nk)
+    switch (__builtin_amdgcn_readfirstlane(n_on)) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Standalone decode of an MXFP4 matrix to bf16 (8 elements per thread).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint8_t *__restrict__ codes,
@@ -473,18 +701,28 @@ static int device_cus()
     return cus;
 }
 
-// Schedule choice from host-known sizes only: the mean rows per local expert.
-// Below TILE_MIN_ROWS the weight-streaming schedule (weights read once per 16
-// rows) wins; above it the tiled schedule (once per 128 rows, LDS reuse).
-constexpr int TILE_MIN_ROWS = 48;
+// Schedule choice from host-known sizes only: the mean rows per local expert
+// (max_rows / num_local). Below TILE_MIN_ROWS the weight-streaming schedule
+// (weights read once per 16 rows) wins. Up to TILE256_MAX_MEAN a typical
+// expert fits one 256-row tile, so the 256-row schedule reads each weight
+// byte once per expert; above it the 128-row schedule (two workgroups per
+// CU) keeps the matrix cores busier.
+constexpr int TILE_MIN_ROWS = 48, TILE256_MAX_MEAN = 192;
 
 int resolve_mode(int mode, int num_local, int max_rows)
 {
-    if (mode == 1 || mode == 2) return mode;
-    return (int64_t)max_rows >= (int64_t)TILE_MIN_ROWS * num_local ? 2 : 1;
+    if (mode == MOE_SCHED_STREAM || mode == MOE_SCHED_TILE128 || mode == MOE_SCHED_TILE256)
+        return mode;
+    if (mode == 0 && (int64_t)max_rows < (int64_t)TILE_MIN_ROWS * num_local)
+        return MOE_SCHED_STREAM;
+    return (int64_t)max_rows <= (int64_t)TILE256_MAX_MEAN * num_local ? MOE_SCHED_TILE256
+                                                                        : MOE_SCHED_TILE128;
 }
 
-static int rows_per_group(int mode) { return mode == 2 ? TL_BM : ST_ROWS; }
+static int rows_per_group(int md)
+{
+    return md == MOE_SCHED_TILE256 ? TB_BM : md == MOE_SCHED_TILE128 ? TL_BM : ST_ROWS;
+}
 
 static int max_groups_for(int num_local, int max_rows, int R)
 {
@@ -551,6 +789,30 @@ static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
     return hipGetLastError();
 }
 
+template <int ACT, typename OutT, bool PACKED>
+static hipError_t launch_tile256(const bf16 *a, int64_t lda, const int32_t *a_rows,
+                                 const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                                 const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                                 int max_groups, int N, int K, OutT *out, int64_t ldo,
+                                 hipStream_t s)
+{
+    constexpr int COLS = ACT != ACT_NONE ? TB_BN / 2 : TB_BN;
+    const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
+    if (grid <= 0) return hipSuccess;
+    auto kern = gemm_tile256_kernel<ACT, OutT, PACKED>;
+    static bool attr_set = false;  // per template instance; the limit is a property of the code
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)TB_LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t G = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(TB_THREADS), TB_LDS, s, a, lda, a_rows, w1c,
+                       w1s, w2c, w2s, off, plan, N, K, out, ldo);
+    return hipGetLastError();
+}
+
 template <typename OutT, bool PACKED>
 static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, const int32_t *a_rows,
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
@@ -561,8 +823,9 @@ static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, cons
 #define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups, N, K, out, ldo, s
 #define MOE_GEMM_CASE(A)                                                     \
     case A:                                                                  \
-        return md == 2 ? launch_tile<A, OutT, PACKED>(MOE_GEMM_ARGS)         \
-                       : launch_stream<A, OutT, PACKED>(MOE_GEMM_ARGS);
+        return md == MOE_SCHED_TILE256   ? launch_tile256<A, OutT, PACKED>(MOE_GEMM_ARGS) \
+               : md == MOE_SCHED_TILE128 ? launch_tile<A, OutT, PACKED>(MOE_GEMM_ARGS)    \
+                                         : launch_stream<A, OutT, PACKED>(MOE_GEMM_ARGS);
     switch (act) {
         MOE_GEMM_CASE(ACT_NONE)
         MOE_GEMM_CASE(ACT_SILU_MUL)
@@ -576,15 +839,17 @@ static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, cons
 
 GemmPlanArgs gemm_plan_args(int num_local, int max_rows, int mode, void *ws)
 {
-    const int R = rows_per_group(resolve_mode(mode, num_local, max_rows));
-    return GemmPlanArgs{(int32_t *)ws, R, max_groups_for(num_local, max_rows, R), PLAN_HDR};
+    const int md = resolve_mode(mode, num_local, max_rows);
+    const int R = rows_per_group(md);
+    return GemmPlanArgs{(int32_t *)ws, R, max_groups_for(num_local, max_rows, R), PLAN_HDR,
+                        md == MOE_SCHED_TILE256};
 }
 
 hipError_t launch_gemm_plan_into(const int32_t *off, int num_local, const GemmPlanArgs &a,
                                  hipStream_t s)
 {
     hipLaunchKernelGGL(gemm_plan_kernel, dim3(1), dim3(1024), 0, s, off, num_local,
-                       a.rows_per_group, a.max_groups, a.plan);
+                       a.rows_per_group, a.max_groups, a.balanced, a.plan);
     return hipGetLastError();
 }
 

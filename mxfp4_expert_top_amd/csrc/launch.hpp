@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe_mxfp4.h"
+
 #define MOE_MAX_EXPERTS_DEV 2048
 #define MOE_MAX_TOPK_DEV 32
 
@@ -60,6 +62,7 @@ struct GemmPlanArgs {
     int rows_per_group;
     int max_groups;
     int hdr;
+    int balanced;  // nearly equal groups instead of rows_per_group-row groups
 };
 // Offsets, permutation and inverse; with `plan` also the GEMM work plan
 // (built inside the same kernel for small T).

@@ -127,7 +127,7 @@ constexpr int PS_PER = PERM_TB * MOE_MAX_TOPK_DEV / 1024;  // assignments per th
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t *__restrict__ idx, const int32_t *__restrict__ counts, int T, int k, int e0,
     int nl, int32_t *__restrict__ off, int32_t *__restrict__ perm, int32_t *__restrict__ inv,
-    int R, int max_groups, int32_t *__restrict__ plan, int plan_hdr)
+    int R, int max_groups, int balanced, int32_t *__restrict__ plan, int plan_hdr)
 {
     extern __shared__ uint32_t bits[];  // nl * PERM_WORDS
     __shared__ int32_t part[16];
@@ -190,9 +190,9 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     for (int h = 0; h < 2; h++) {
         const int i = i0 + h;
         if (i >= nl) break;
-        const int c = h ? c1 : c0;
-        for (int r = 0; r < c; r += R, pos++)
-            if (pos < max_groups) items[pos] = make_int2(i, soff[i] + r);
+        const int c = h ? c1 : c0, g = (c + R - 1) / R;
+        for (int j = 0; j < g; j++, pos++)
+            if (pos < max_groups) items[pos] = plan_item(i, soff[i], c, g, j, R, balanced);
     }
     if (tid == 0) plan[0] = min(ngroups, max_groups);
 }
@@ -214,7 +214,8 @@ hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int 
     if (nblk == 1 && num_local <= 1024) {  // bitmap <= 32 KB of LDS
         hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), lds, s, idx, counts, T, k, e0,
                            num_local, off, perm, inv, plan ? plan->rows_per_group : 0,
-                           plan ? plan->max_groups : 0, plan ? plan->plan : nullptr,
+                           plan ? plan->max_groups : 0, plan ? plan->balanced : 0,
+                           plan ? plan->plan : nullptr,
                            plan ? plan->hdr : 0);
         return hipGetLastError();
     }

@@ -32,6 +32,16 @@ def max_abs_rms(a, ref):
     return float(np.max(np.abs(a - ref)) / max(rms, 1e-300))
 
 
+def bf16_rounding_ok(got, ref, rel_slack=1e-5):
+    """Elementwise check of a bf16 output against the exact result: rounding to
+    nearest with 8 significant bits moves a value by at most 2^-8 of itself;
+    the slack covers fp32 summation-order differences (rel_slack of each value
+    plus 1e-5 of the rms)."""
+    a, r = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    return bool(np.all(np.abs(a - r) <= (2.0 ** -8 + rel_slack) * np.abs(r) + 1e-5 * rms))
+
+
 def assert_close_layer(got, ref, what=""):
     r, m = rel_l2(got, ref), max_abs_rms(got, ref)
     assert r <= REL_L2 and m <= MAX_ABS_RMS, f"{what}: rel_l2={r:.3e} max_abs/rms={m:.3e}"

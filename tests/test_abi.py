@@ -92,7 +92,7 @@ def test_grouped_gemm_validation():
     assert _gemm(act=7) == 1
     assert _gemm(odt=5) == 1
     assert _gemm(lda=100) == 1               # stride not a multiple of 8
-    assert _gemm(mode=3) == 1
+    assert _gemm(mode=5) == 1
     assert _gemm(lay=2) == 1                 # unknown weight layout
     assert _gemm(K=8320, lda=8320) == 2      # K > MOE_MAX_K
     assert _gemm(w1s=C.c_void_p(0x10004)) == 1  # scales not 16-byte aligned

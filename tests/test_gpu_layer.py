@@ -50,7 +50,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
 def test_small_layer_vs_oracle(cfg, mode):
     inp = make_inputs(cfg)
     g = run_gpu_layer(inp.to(DEV), mode=mode)
@@ -91,7 +91,7 @@ def test_tiny_workload_full_oracle(tiny):
 
 
 @pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], SMALL[2], SMALL[5]], ids=lambda c: c.name)
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 3, 4])
 def test_packed_layout_layer_bitwise(cfg, mode):
     import mxfp4_expert_top_amd as m
     inp = make_inputs(cfg).to(DEV)

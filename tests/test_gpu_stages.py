@@ -8,7 +8,7 @@ import torch
 import oracle
 from synth import LayerConfig, quantize_mxfp4
 from tests.dense_ref import ACTS
-from tests.parity_util import W_TOL, LOGIT_TOL, np_, rel_l2, max_abs_rms
+from tests.parity_util import W_TOL, LOGIT_TOL, bf16_rounding_ok, np_, rel_l2, max_abs_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -160,7 +160,7 @@ def _experts(num_local, N, K, seed):
     return torch.stack([c for c, _ in out]), torch.stack([s for _, s in out])
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 3, 4])
 @pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_grouped_gemm_vs_definition(m, mode, act, out_dtype):
@@ -196,7 +196,54 @@ def test_grouped_gemm_vs_definition(m, mode, act, out_dtype):
             ref[r0:r1] = ACTS[act](g1, u)
     tol = 4e-3 if out_dtype == torch.bfloat16 else 1e-5
     assert rel_l2(got[:A], ref) <= tol, rel_l2(got[:A], ref)
-    assert max_abs_rms(got[:A], ref) <= (3e-2 if out_dtype == torch.bfloat16 else 1e-4)
+    if out_dtype == torch.bfloat16:
+        # elementwise: bf16 keeps 8 significant bits, so rounding to nearest
+        # moves a value by at most 2^-8 of itself (the GLU output is heavy
+        # tailed, so a bound relative to its rms would not hold)
+        assert bf16_rounding_ok(got[:A], ref)
+    else:
+        assert max_abs_rms(got[:A], ref) <= 1e-4
+
+
+@pytest.mark.parametrize("mode", [1, 3, 4])
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("K", [128, 640])
+def test_grouped_gemm_many_rows(m, mode, act, K):
+    """Experts with more rows than one tile (300, 513, 256, 257 rows), an
+    empty and a single-row expert, a column count that is not a tile multiple,
+    and the shortest contraction (one 128-wide chunk)."""
+    rng = np.random.default_rng(K + act + 7 * mode)
+    nl, N, T = 6, 320, 700
+    counts = np.array([300, 0, 513, 1, 256, 257], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16)
+    a_rows = rng.integers(0, T, size=A).astype(np.int32)
+    w1c, w1s = _experts(nl, N, K, 3)
+    w2c, w2s = _experts(nl, N, K, 4) if act else (None, None)
+    out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_workspace_size(nl, A, N, mode), DEV)
+    m.moe_grouped_gemm_mxfp4(x.to(DEV), torch.from_numpy(a_rows).to(DEV), w1c.to(DEV),
+                             w1s.to(DEV), None if w2c is None else w2c.to(DEV),
+                             None if w2s is None else w2s.to(DEV),
+                             torch.from_numpy(off).to(DEV), A, act, out, ws, mode=mode)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[A:] == 7.0).all()
+    xa = x.float().numpy().astype(np.float64)[a_rows]
+    ref = np.zeros((A, N))
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        if r0 == r1:
+            continue
+        g1 = xa[r0:r1] @ oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64).T
+        if act == 0:
+            ref[r0:r1] = g1
+        else:
+            u = xa[r0:r1] @ oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64).T
+            ref[r0:r1] = ACTS[act](g1, u)
+    assert rel_l2(got[:A], ref) <= 1e-5, rel_l2(got[:A], ref)
+    assert max_abs_rms(got[:A], ref) <= 1e-4
 
 
 # ---------------------------------------------------------------- combine
@@ -249,7 +296,7 @@ def test_prepack_is_a_permutation(m, n, N, K):
     assert (pad == 0).all()
 
 
-@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("mode", [1, 3, 4])
 @pytest.mark.parametrize("act", [0, 1])
 def test_grouped_gemm_packed_equals_canonical(m, mode, act):
     rng = np.random.default_rng(11 + act)
