@@ -131,7 +131,9 @@ int moe_route(const void *x, const float *w_router, const float *bias, float *lo
  * buffer planning): offsets of each local expert's rows and a stable counting
  * sort of the row-major (t, j) assignment list by expert.
  *
- *   topk_idx [T][k] int32, expert_counts [E] int32  (from moe_route)
+ *   topk_idx [T][k] int32, expert_counts [E] int32  (from moe_route; or
+ *            NULL: each local expert's rows are then counted from topk_idx,
+ *            with no atomics, which suits heavily skewed routing)
  *   local experts are ids [expert_begin, expert_begin + num_local)
  *   expert_offsets [num_local + 1] int32 (out): off[0] = 0,
  *                  off[i+1] = off[i] + expert_counts[expert_begin + i]

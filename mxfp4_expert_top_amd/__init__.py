@@ -158,9 +158,15 @@ def moe_permute_workspace_size(T, num_local):
 
 
 def moe_permute(topk_idx, expert_counts, expert_begin, num_local, expert_offsets, perm_token,
-                inv, ws, stream=None):
+                inv, ws, stream=None, E=None):
+    """expert_counts may be None (counts are then taken from topk_idx); E, the
+    expert count, is then required."""
     T, k = topk_idx.shape
-    E = expert_counts.shape[0]
+    if expert_counts is not None:
+        E = expert_counts.shape[0]
+        _want(expert_counts, torch.int32, (E,), "expert_counts")
+    elif E is None:
+        raise ValueError("E is required when expert_counts is None")
     _dev(topk_idx, expert_counts, expert_offsets, perm_token, inv, ws)
     _want(topk_idx, torch.int32, (T, k), "topk_idx")
     _want(expert_offsets, torch.int32, (num_local + 1,), "expert_offsets")

@@ -58,7 +58,7 @@ int check_permute(const int32_t *idx, const int32_t *counts, int T, int k, int E
     CHECK(T >= 0 && k >= 1 && k <= E && E >= 1, MOE_ERR_INVALID_ARG);
     CHECK(e0 >= 0 && nl >= 1 && e0 + nl <= E, MOE_ERR_INVALID_ARG);
     CHECK(k <= MOE_MAX_TOPK && E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
-    CHECK(counts && off, MOE_ERR_INVALID_ARG);
+    CHECK(off, MOE_ERR_INVALID_ARG);  // counts may be NULL: taken from idx
     if (T > 0) CHECK(idx && perm && inv, MOE_ERR_INVALID_ARG);
     return MOE_OK;
 }
@@ -96,7 +96,7 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 
 // Workspace layout of moe_layer; every region 256-byte aligned.
 struct LayerWs {
-    size_t logits, planes, wsplit, idx, w, counts, off, perm, inv, pws, gws, h, y, total;
+    size_t logits, planes, wsplit, idx, w, off, perm, inv, pws, gws, h, y, total;
     int splits;
     int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
 };
@@ -123,7 +123,6 @@ LayerWs layer_ws(const moe_layer_params *p)
     L.wsplit = o; o += L.router == ROUTER_TILED ? round_up(3 * E * (size_t)p->d * 2) : 0;
     L.idx = o;    o += round_up(A * 4);
     L.w = o;      o += round_up(A * 4);
-    L.counts = o; o += round_up(E * 4);
     L.off = o;    o += round_up(((size_t)p->num_local + 1) * 4);
     L.perm = o;   o += round_up(A * 4);
     L.inv = o;    o += round_up(A * 4);
@@ -328,7 +327,6 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     float *logits = logits_out ? logits_out : (float *)(base + L.logits);
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + L.idx);
     float *w = topk_w_out ? topk_w_out : (float *)(base + L.w);
-    int32_t *counts = (int32_t *)(base + L.counts);
     int32_t *off = (int32_t *)(base + L.off);
     int32_t *perm = (int32_t *)(base + L.perm);
     int32_t *inv = (int32_t *)(base + L.inv);
@@ -340,7 +338,11 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     hipEvent_t *ev = (hipEvent_t *)stage_events;
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
-    // with split-K planes the top-k kernel adds them in a fixed order, then the bias
+    // With split-K planes the top-k kernel adds them in a fixed order, then the
+    // bias. No expert histogram here: the permute kernels count each expert's
+    // rows from their dispatch bitmaps (a histogram of skewed routing would
+    // serialise atomics on the hot experts).
+    int32_t *counts = nullptr;
     float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
     const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
     if (L.router == ROUTER_TILED) {

@@ -43,7 +43,8 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
 constexpr int ROUTER_TILE_MIN_T = 512;
 // K splits that give the router about `target_blocks` workgroups.
 int router_splits(int T, int d, int E, int target_blocks);
-// Top-k, softmax weights and histogram. src holds n_planes planes [T][E];
+// Top-k, softmax weights and (counts != NULL) histogram by integer atomics.
+// src holds n_planes planes [T][E];
 // with n_planes > 1 the scores are plane 0 + plane 1 + ... (in that order)
 // + bias, and are written to `logits`; with one plane src is the final scores
 // (bias and logits unused).
@@ -65,7 +66,8 @@ struct GemmPlanArgs {
     int balanced;  // nearly equal groups instead of rows_per_group-row groups
 };
 // Offsets, permutation and inverse; with `plan` also the GEMM work plan
-// (built inside the same kernel for small T).
+// (built inside the same kernel for small T). counts: the expert histogram,
+// or NULL to count from the dispatch bitmaps (no atomics anywhere).
 hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int k, int e0,
                           int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
                           hipStream_t s, const GemmPlanArgs *plan = nullptr);

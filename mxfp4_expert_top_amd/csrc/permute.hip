@@ -53,23 +53,28 @@ __global__ __launch_bounds__(PERM_TB) void permute_count_kernel(
 
 // One workgroup: offsets over the local range, then per expert a scan of the
 // block counts (in place: blk[b][e] becomes block b's first row for e).
+// Expert counts come from `counts` (the histogram) or, when it is NULL, from
+// the block counts themselves.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     const int32_t *__restrict__ counts, int e0, int nl, int nblk, int32_t *__restrict__ off,
     int32_t *__restrict__ blk)
 {
     __shared__ int32_t part[16];
     const int tid = threadIdx.x;
-    // each thread sums a contiguous run of experts
+    // each thread owns a contiguous run of at most two experts (nl <= 2048)
     const int per = (nl + 1023) / 1024;
     const int lo = tid * per, hi = min(lo + per, nl);
-    int s = 0;
-    for (int i = lo; i < hi; i++) s += counts[e0 + i];
+    auto count = [&](int i) {
+        if (counts) return counts[e0 + i];
+        int c = 0;
+        for (int b = 0; b < nblk; b++) c += blk[(int64_t)b * nl + i];
+        return c;
+    };
+    const int c0 = lo < hi ? count(lo) : 0, c1 = lo + 1 < hi ? count(lo + 1) : 0;
     int total;
-    int run = block_exclusive_scan(s, part, total);  // exclusive prefix of this thread's run
-    for (int i = lo; i < hi; i++) {
-        off[i] = run;
-        run += counts[e0 + i];
-    }
+    const int run = block_exclusive_scan(c0 + c1, part, total);  // exclusive prefix of the run
+    if (lo < hi) off[lo] = run;
+    if (lo + 1 < hi) off[lo + 1] = run + c0;
     if (tid == 0) off[nl] = total;
     __syncthreads();
     for (int le = tid; le < nl; le += 1024) {
@@ -150,9 +155,19 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
         const int t = (tid + 1024 * u) / k;
         atomicOr(&bits[le[u] * PERM_WORDS + t / 32], 1u << (t % 32));
     }
-    // offsets: each thread owns two consecutive local experts (nl <= 2048)
+    // offsets: each thread owns two consecutive local experts (nl <= 2048);
+    // counts from the histogram or, when it is NULL, from the bitmap
     const int i0 = 2 * tid;
-    const int c0 = i0 < nl ? counts[e0 + i0] : 0, c1 = i0 + 1 < nl ? counts[e0 + i0 + 1] : 0;
+    if (!counts) __syncthreads();  // the bitmap is complete
+    auto count = [&](int i) {
+        if (i >= nl) return 0;
+        if (counts) return (int)counts[e0 + i];
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < PERM_WORDS; w++) c += __popc(bits[i * PERM_WORDS + w]);
+        return c;
+    };
+    const int c0 = count(i0), c1 = count(i0 + 1);
     int total;
     const int ex = block_exclusive_scan(c0 + c1, part, total);  // also orders the bitmap ORs
     if (i0 < nl) soff[i0] = ex;

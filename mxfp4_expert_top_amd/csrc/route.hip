@@ -210,13 +210,15 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 // ---------------------------------------------------------------------------
 // Router scores for larger batches: the fp32 weights are split once into
 // three bf16 planes Wp[p][e][i] (hi, mid, lo; exact sum), then
-//   logits[t][e] = sum_p sum_i x[t][i] * Wp[p][e][i]  (+ bias)
-// is one bf16 GEMM over K' = 3 d on the 32x32x16 matrix cores. Workgroup
-// tile 128 tokens x 128 experts, K step 64, both operands double-buffered in
-// LDS, 4 waves of 64 x 64. blockIdx.y splits K' into planes of partial sums
-// when the tile grid alone is too small for the chip.
+//   logits[t][e] = sum_i sum_p x[t][i] * Wp[p][e][i]  (+ bias)
+// on the 32x32x16 matrix cores. Workgroup tile 128 tokens x 128 experts, K
+// step 32 of d covering all three planes: each token fragment read from LDS
+// feeds three MFMAs (one per plane). Both operands double-buffered in LDS
+// (80 KB, two workgroups per CU), 4 waves of 64 x 64. blockIdx.y splits d
+// into ranges whose partial sums go to separate planes when the tile grid
+// alone is too small for the chip.
 // ---------------------------------------------------------------------------
-constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 64, RG_LD = RG_BK + 8;
+constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 32, RG_LD = RG_BK + 8;
 
 __global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ w,
                                                            int64_t n, bf16 *__restrict__ wp)
@@ -242,6 +244,8 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+constexpr size_t RG_LDS = (size_t)2 * RG_BM * RG_LD * 2 + (size_t)2 * 3 * RG_BN * RG_LD * 2;
+
 __global__ __launch_bounds__(256, 2) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wp, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int ksteps_per_split,
@@ -249,39 +253,48 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
 {
     if (zero_counts && blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = threadIdx.x; i < E; i += blockDim.x) zero_counts[i] = 0;
-    __shared__ __attribute__((aligned(16))) bf16 As[2][RG_BM][RG_LD];
-    __shared__ __attribute__((aligned(16))) bf16 Bs[2][RG_BN][RG_LD];
+    extern __shared__ __attribute__((aligned(16))) uint8_t rg_lds[];
+    bf16 (*As)[RG_BM][RG_LD] = (bf16 (*)[RG_BM][RG_LD])rg_lds;
+    bf16 (*Bs)[3][RG_BN][RG_LD] =
+        (bf16 (*)[3][RG_BN][RG_LD])(rg_lds + (size_t)2 * RG_BM * RG_LD * 2);
     const int n_nb = (E + RG_BN - 1) / RG_BN;
     const int mb = blockIdx.x / n_nb, nb = blockIdx.x - mb * n_nb;
     const int t0 = mb * RG_BM, e0 = nb * RG_BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
-    const int steps_d = d / RG_BK;
     const int kt0 = blockIdx.y * ksteps_per_split, kt1 = kt0 + ksteps_per_split;
     logits += (int64_t)blockIdx.y * T * E;
     if (gridDim.y > 1) bias = nullptr;
 
-    // global -> LDS: thread -> row tid / 2, 64 bytes at column 32 * (tid % 2)
-    const int lr = tid >> 1, lc = (tid & 1) * 32;
-    const bf16 *xa = x + (int64_t)min(t0 + lr, T - 1) * d + lc;
-    const int eb = min(e0 + lr, E - 1);
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const int p = kt / steps_d, k0 = (kt - p * steps_d) * RG_BK;
-        const bf16 *wb = wp + ((int64_t)p * E + eb) * d + lc + k0;
+    // global -> LDS. A: thread -> token row tid / 2, 16 bf16 at 16 (tid % 2).
+    // B: 6 units of 8 bf16 per thread, unit u = tid + 256 i -> plane u / 512,
+    // expert row (u % 512) / 4, column 8 (u % 4).
+    const int ar = tid >> 1, ac = 16 * (tid & 1);
+    const bf16 *xa = x + (int64_t)min(t0 + ar, T - 1) * d + ac;
+    const bf16 *wb[6];
+    int bp[6], brow[6], bq[6];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            ra[c] = *(const u32x4 *)(xa + k0 + 8 * c);
-            rb[c] = *(const u32x4 *)(wb + 8 * c);
-        }
+    for (int i = 0; i < 6; i++) {
+        const int u = tid + 256 * i;
+        bp[i] = u >> 9;
+        brow[i] = (u & 511) >> 2;
+        bq[i] = u & 3;
+        wb[i] = wp + ((int64_t)bp[i] * E + min(e0 + brow[i], E - 1)) * d + 8 * bq[i];
+    }
+    u32x4 ra[2], rb[6];
+    auto gload = [&](int kt) {
+        const int k0 = kt * RG_BK;
+        ra[0] = *(const u32x4 *)(xa + k0);
+        ra[1] = *(const u32x4 *)(xa + k0 + 8);
+#pragma unroll
+        for (int i = 0; i < 6; i++) rb[i] = *(const u32x4 *)(wb[i] + k0);
     };
     auto lstore = [&](int st) {
+        *(u32x4 *)(&As[st][ar][ac]) = ra[0];
+        *(u32x4 *)(&As[st][ar][ac + 8]) = ra[1];
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-            *(u32x4 *)(&As[st][lr][lc + 8 * c]) = ra[c];
-            *(u32x4 *)(&Bs[st][lr][lc + 8 * c]) = rb[c];
-        }
+        for (int i = 0; i < 6; i++) *(u32x4 *)(&Bs[st][bp[i]][brow[i]][8 * bq[i]]) = rb[i];
     };
     f32x16 acc[2][2];
 #pragma unroll
@@ -290,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
-    const bool mt_on[2] = {t0 + wm * 64 < T, t0 + wm * 64 + 32 < T};
+    const bool mt_on = t0 + wm * 64 < T;  // the wave's 64 tokens hold at least one real row
 
     gload(kt0);
     lstore(0);
@@ -298,19 +311,22 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
     for (int kt = kt0; kt < kt1; kt++) {
         const int st = (kt - kt0) & 1;
         if (kt + 1 < kt1) gload(kt + 1);
-        if (mt_on[0]) {
+        if (mt_on) {
 #pragma unroll
-            for (int s = 0; s < 4; s++) {
-                bf16x8 b[2];
+            for (int s = 0; s < 2; s++) {
+                bf16x8 a[2];
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    b[j] = *(const bf16x8 *)(&Bs[st][wn * 64 + 32 * j + l32][32 * h + 8 * s]);
+                for (int i = 0; i < 2; i++)
+                    a[i] = *(const bf16x8 *)(&As[st][wm * 64 + 32 * i + l32][16 * s + 8 * h]);
 #pragma unroll
-                for (int i = 0; i < 2; i++) {
-                    if (!mt_on[i]) continue;
-                    const bf16x8 a = *(const bf16x8 *)(&As[st][wm * 64 + 32 * i + l32][32 * h + 8 * s]);
+                for (int p = 0; p < 3; p++) {
 #pragma unroll
-                    for (int j = 0; j < 2; j++) acc[i][j] = mfma32x32x16(a, b[j], acc[i][j]);
+                    for (int j = 0; j < 2; j++) {
+                        const bf16x8 b =
+                            *(const bf16x8 *)(&Bs[st][p][wn * 64 + 32 * j + l32][16 * s + 8 * h]);
+#pragma unroll
+                        for (int i = 0; i < 2; i++) acc[i][j] = mfma32x32x16(a[i], b, acc[i][j]);
+                    }
                 }
             }
         }
@@ -318,18 +334,18 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
         __syncthreads();
     }
     // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
+    if (!mt_on) return;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        if (!mt_on[i]) continue;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int e = e0 + wn * 64 + 32 * j + l32;
             if (e >= E) continue;
-            const float b = bias ? bias[e] : 0.f;
+            const float bb = bias ? bias[e] : 0.f;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int t = t0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (t < T) logits[(int64_t)t * E + e] = acc[i][j][v] + b;
+                if (t < T) logits[(int64_t)t * E + e] = acc[i][j][v] + bb;
             }
         }
     }
@@ -541,7 +557,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     if (t_ok && lane < k) {
         topk_idx[(int64_t)t * k + lane] = my_idx;
         topk_w[(int64_t)t * k + lane] = z / sum;
-        atomicAdd(&counts[my_idx], 1);
+        if (counts) atomicAdd(&counts[my_idx], 1);
     }
 }
 
@@ -581,7 +597,7 @@ hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream
 int router_tile_splits(int T, int d, int E, int target_blocks)
 {
     const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
-    const int steps = 3 * (d / RG_BK);
+    const int steps = d / RG_BK;
     int best = 1;
     for (int sp = 1; sp <= steps; sp++) {
         if (steps % sp) continue;
@@ -596,8 +612,15 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
                               hipStream_t s)
 {
     const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
-    const int steps = 3 * (d / RG_BK);
-    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), 0, s, x, wp, bias,
+    const int steps = d / RG_BK;
+    static bool attr_set = false;  // the limit is a property of the code
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)router_tile_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)RG_LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), RG_LDS, s, x, wp, bias,
                        logits, T, d, E, steps / splits, zero_counts);
     return hipGetLastError();
 }

@@ -128,7 +128,8 @@ def test_router_scores_and_replay(m, T, d, E, bias):
                                          (700, 896, 16, 784, 112), (513, 32, 32, 0, 32),
                                          (200, 896, 16, 0, 896), (256, 64, 4, 8, 40),
                                          (256, 1100, 16, 0, 1100), (300, 2048, 32, 0, 2048)])
-def test_permute_bitexact(m, T, E, k, e0, nl):
+@pytest.mark.parametrize("with_counts", [True, False])
+def test_permute_bitexact(m, T, E, k, e0, nl, with_counts):
     rng = np.random.default_rng(T + E + k)
     lg = rng.standard_normal((T, E)).astype(np.float32)
     oi, _ = oracle.topk_softmax(lg, k) if T else (np.zeros((0, k), np.int32), None)
@@ -140,8 +141,9 @@ def test_permute_bitexact(m, T, E, k, e0, nl):
     g_perm = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
     g_inv = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
     ws = m.alloc_workspace(m.moe_permute_workspace_size(T, nl), DEV)
-    m.moe_permute(torch.from_numpy(oi).to(DEV), torch.from_numpy(cnt).to(DEV), e0, nl, g_off,
-                  g_perm, g_inv, ws)
+    m.moe_permute(torch.from_numpy(oi).to(DEV),
+                  torch.from_numpy(cnt).to(DEV) if with_counts else None, e0, nl, g_off,
+                  g_perm, g_inv, ws, E=E)
     torch.cuda.synchronize()
     A = int(off[-1])
     assert np.array_equal(np_(g_off), off)
