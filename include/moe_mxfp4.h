@@ -205,6 +205,9 @@ int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, i
  * a GLU act without w2, or w2 with MOE_ACT_NONE -> INVALID_ARG.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode);
+/* The schedule `mode` resolves to for these sizes (MOE_SCHED_STREAM,
+ * MOE_SCHED_TILE128 or MOE_SCHED_TILE256), or -1 for invalid arguments. */
+int moe_grouped_gemm_schedule(int num_local, int max_rows, int mode);
 int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
                            const uint8_t *w1_codes, const uint8_t *w1_scales,
                            const uint8_t *w2_codes, const uint8_t *w2_scales,

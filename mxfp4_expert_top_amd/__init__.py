@@ -35,7 +35,7 @@ def _load(path=None):
     path = Path(path) if path is not None else _LIB_PATH
     if not path.exists():
         raise ImportError(
-            f"{path} is not built; run `python -m mxfp4_expert_top_amd.build` "
+            f"{path} is not built; run `python mxfp4_expert_top_amd/build.py` "
             "(there is no fallback path)")
     L = C.CDLL(str(path))
     p, i32, i64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_size_t
@@ -51,6 +51,8 @@ def _load(path=None):
     L.moe_permute.argtypes = [p, p, i32, i32, i32, i32, i32, p, p, p, p, sz, p]
     L.moe_mxfp4_dequant.restype = i32
     L.moe_mxfp4_dequant.argtypes = [p, p, i64, i32, p, p]
+    L.moe_grouped_gemm_schedule.restype = i32
+    L.moe_grouped_gemm_schedule.argtypes = [i32, i32, i32]
     L.moe_grouped_gemm_workspace_size.restype = sz
     L.moe_grouped_gemm_workspace_size.argtypes = [i32, i32, i32, i32]
     L.moe_grouped_gemm_mxfp4.restype = i32
@@ -73,7 +75,8 @@ lib = _load()
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4_dequant",
             "moe_mxfp4_prepack", "moe_mxfp4_packed_scale_bytes",
-            "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size", "moe_combine",
+            "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size",
+            "moe_grouped_gemm_schedule", "moe_combine",
             "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error")
 
 
@@ -220,6 +223,14 @@ def prepack_weights(weights, stream=None):
         out[name + "_codes"], out[name + "_scales"] = moe_mxfp4_prepack(
             weights[name + "_codes"], weights[name + "_scales"], stream)
     return out
+
+
+def moe_grouped_gemm_schedule(num_local, max_rows, mode=MODE_AUTO):
+    """The schedule (MODE_STREAM, MODE_TILE128 or MODE_TILE256) `mode` resolves to."""
+    r = lib.moe_grouped_gemm_schedule(num_local, max_rows, mode)
+    if r < 0:
+        raise MoeError("moe_grouped_gemm_schedule", MOE_ERR_INVALID_ARG, "invalid argument")
+    return r
 
 
 def moe_grouped_gemm_workspace_size(num_local, max_rows, N, mode=MODE_AUTO):

@@ -2,7 +2,8 @@
 
 Every HIP source under csrc/ is compiled to an object in _build/ (in
 parallel) and linked into mxfp4_expert_top_amd/libmoe_mxfp4.so next to this
-file. Run as ``python -m mxfp4_expert_top_amd.build``.
+file. Run as ``python mxfp4_expert_top_amd/build.py`` (as a script: importing
+the package would first load the library it is about to build).
 """
 
 from __future__ import annotations

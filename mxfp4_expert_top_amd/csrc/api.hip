@@ -249,6 +249,13 @@ int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, i
     return MOE_OK;
 }
 
+int moe_grouped_gemm_schedule(int num_local, int max_rows, int mode)
+{
+    if (num_local < 1 || max_rows < 0 || mode < MOE_SCHED_AUTO || mode > MOE_SCHED_TILE256)
+        return -1;
+    return resolve_mode(mode, num_local, max_rows);
+}
+
 size_t moe_grouped_gemm_workspace_size(int num_local, int max_rows, int N, int mode)
 {
     if (num_local < 1 || max_rows < 0 || mode < MOE_SCHED_AUTO || mode > MOE_SCHED_TILE256)

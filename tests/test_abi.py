@@ -32,6 +32,25 @@ def test_library_exports_every_declared_function():
     assert set(m.EXPORTED) <= set(declared_functions())
 
 
+def test_schedule_choice():
+    # the decode, prefill, EP-share and long skewed workloads of this repository
+    assert m.moe_grouped_gemm_schedule(896, 64 * 16) == m.MODE_STREAM
+    assert m.moe_grouped_gemm_schedule(896, 8192 * 16) == m.MODE_TILE256
+    assert m.moe_grouped_gemm_schedule(112, 16384 * 16) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(896, 65536 * 16) == m.MODE_TILE128
+    # explicit schedules are kept; TILED never streams
+    for md in (m.MODE_STREAM, m.MODE_TILE128, m.MODE_TILE256):
+        assert m.moe_grouped_gemm_schedule(896, 64, md) == md
+    assert m.moe_grouped_gemm_schedule(896, 64, m.MODE_TILED) == m.MODE_TILE256
+    # the thresholds: mean rows 48 (stream below) and 192 (256-row tiles up to)
+    assert m.moe_grouped_gemm_schedule(10, 479) == m.MODE_STREAM
+    assert m.moe_grouped_gemm_schedule(10, 480) == m.MODE_TILE256
+    assert m.moe_grouped_gemm_schedule(10, 1920) == m.MODE_TILE256
+    assert m.moe_grouped_gemm_schedule(10, 1921) == m.MODE_TILE128
+    assert m.lib.moe_grouped_gemm_schedule(0, 10, 0) == -1
+    assert m.lib.moe_grouped_gemm_schedule(4, 10, 5) == -1
+
+
 def test_status_strings():
     for s in range(5):
         assert m.lib.moe_status_string(s)
