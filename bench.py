@@ -43,6 +43,9 @@ def parse():
                     help="tokens the oracle CPU baseline evaluates (0 = skip)")
     ap.add_argument("--weights", default="packed", choices=["packed", "ocp"],
                     help="expert weight layout: converted at load (packed) or canonical")
+    ap.add_argument("--quantize-probe-mib", type=int, default=0,
+                    help="time the device fp32 -> MXFP4 quantiser on this many MiB of fp32 "
+                         "weights (a [N, 3584] matrix) and print its own JSON line")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -137,10 +140,42 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
 
 
+def quantize_probe(mib, steps=20):
+    """Throughput of moe_mxfp4_quantize (the load-time weight conversion):
+    reads 4 bytes and writes 17/32 bytes per weight, HBM bound."""
+    import mxfp4_expert_top_amd as m
+    K = 3584
+    N = max(1, mib * 2**20 // (4 * K))
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    w = torch.randn(N, K, generator=g, device="cuda:0") * 0.02
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty(N, K // 32, dtype=torch.uint8, device="cuda:0")
+    for _ in range(3):
+        m.moe_mxfp4_quantize(w, codes, scales)
+    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s_.record()
+    for _ in range(steps):
+        m.moe_mxfp4_quantize(w, codes, scales)
+    e_.record()
+    torch.cuda.synchronize()
+    ms = s_.elapsed_time(e_) / steps
+    nbytes = N * K * (4 + 0.5 + 1 / 32)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({"metric": "MXFP4 quantise (fp32 -> E2M1 + E8M0) GB/s", "value": round(gbs, 1),
+                      "unit": "GB/s", "ms_per_call": round(ms, 4), "weights": N * K,
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
+        return
+    if args.quantize_probe_mib:
+        quantize_probe(args.quantize_probe_mib)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this layer runs on one GPU; --gpus must be 1 "

@@ -150,6 +150,22 @@ int moe_permute(const int32_t *topk_idx, const int32_t *expert_counts, int T, in
                 int32_t *inv, void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_mxfp4_quantize -- fp32 -> MXFP4 on the device, for weights converted
+ * online at load time (P3 section 三: MXFP4 online quantisation at load;
+ * OCP-MX: E2M1 elements, one E8M0 scale per 32 elements).
+ *   w [N][K] fp32 (device, 16-byte aligned) -> codes [N][K/2], scales
+ *   [N][K/32] in the canonical layout (codes 16-byte aligned).
+ * Per 32-element block: amax = max|v|; all zero -> scale code 0, codes 0;
+ * else s = clamp(floor(log2 amax) - 2 + 127, 0, 254) and each element is
+ * v / 2^(s-127) rounded to the nearest E2M1 value (ties to the even code,
+ * magnitudes above 6 saturate to 6), sign bit from v (-0 keeps it).
+ * Preconditions: finite w. Errors: K % 32 != 0 -> UNSUPPORTED; NULL or
+ * misaligned pointers -> INVALID_ARG. N == 0 or K == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+int moe_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes, uint8_t *scales,
+                       moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_mxfp4_dequant -- decode an MXFP4 matrix to bf16 (OCP-MX element value
  * E2M1(code) * 2^(s-127), exact in bf16 for scale codes 2..252; codes 0 and 1
  * reach bf16 subnormals, which the hardware may flush to zero).

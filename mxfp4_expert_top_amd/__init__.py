@@ -49,6 +49,8 @@ def _load(path=None):
     L.moe_permute_workspace_size.argtypes = [i32, i32]
     L.moe_permute.restype = i32
     L.moe_permute.argtypes = [p, p, i32, i32, i32, i32, i32, p, p, p, p, sz, p]
+    L.moe_mxfp4_quantize.restype = i32
+    L.moe_mxfp4_quantize.argtypes = [p, i64, i32, p, p, p]
     L.moe_mxfp4_dequant.restype = i32
     L.moe_mxfp4_dequant.argtypes = [p, p, i64, i32, p, p]
     L.moe_grouped_gemm_schedule.restype = i32
@@ -74,6 +76,7 @@ def _load(path=None):
 lib = _load()
 
 EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4_dequant",
+            "moe_mxfp4_quantize",
             "moe_mxfp4_prepack", "moe_mxfp4_packed_scale_bytes",
             "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size",
             "moe_grouped_gemm_schedule", "moe_combine",
@@ -180,6 +183,26 @@ def moe_permute(topk_idx, expert_counts, expert_begin, num_local, expert_offsets
                          _ptr(expert_offsets), _ptr(perm_token), _ptr(inv), _ptr(ws), nbytes,
                          _stream(stream))
     _check("moe_permute", st)
+
+
+def moe_mxfp4_quantize(w, codes=None, scales=None, stream=None):
+    """fp32 [N, K] (or [..., N, K]) on the GPU -> (codes uint8 [..., N, K/2],
+    scales uint8 [..., N, K/32]) in the canonical MXFP4 layout."""
+    if w.dtype != torch.float32:
+        raise TypeError(f"w: expected torch.float32, got {w.dtype}")
+    K = w.shape[-1]
+    N = w.numel() // K if K else 0
+    lead = tuple(w.shape[:-1])
+    if codes is None:
+        codes = torch.empty(*lead, K // 2, dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(*lead, K // 32, dtype=torch.uint8, device=w.device)
+    _dev(w, codes, scales)
+    _want(codes, torch.uint8, lead + (K // 2,), "codes")
+    _want(scales, torch.uint8, lead + (K // 32,), "scales")
+    _check("moe_mxfp4_quantize", lib.moe_mxfp4_quantize(_ptr(w), N, K, _ptr(codes),
+                                                        _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 def moe_mxfp4_dequant(codes, scales, out, stream=None):

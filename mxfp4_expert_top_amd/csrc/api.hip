@@ -218,6 +218,18 @@ int moe_permute(const int32_t *topk_idx, const int32_t *expert_counts, int T, in
     return MOE_OK;
 }
 
+int moe_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes, uint8_t *scales,
+                       moe_stream_t stream)
+{
+    CHECK(N >= 0 && K >= 0, MOE_ERR_INVALID_ARG);
+    CHECK(K % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (N == 0 || K == 0) return MOE_OK;
+    CHECK(w && codes && scales, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(w, 16) && aligned(codes, 16), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_mxfp4_quantize(w, N, K, codes, scales, as_stream(stream)));
+    return MOE_OK;
+}
+
 int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K, void *out,
                       moe_stream_t stream)
 {

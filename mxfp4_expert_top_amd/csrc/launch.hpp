@@ -99,7 +99,10 @@ int resolve_mode(int mode, int num_local, int max_rows);
 hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,
                                 bf16 *out, hipStream_t s);
 
-// prepack.hip: the streaming weight layout (see prepack.hip)
+// prepack.hip: the streaming weight layout (see prepack.hip) and the fp32 ->
+// MXFP4 quantiser (canonical layout out)
+hipError_t launch_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes,
+                                 uint8_t *scales, hipStream_t s);
 size_t packed_scale_bytes(int64_t N, int K);
 hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int64_t n_rows, int K,
                           uint8_t *pcodes, uint8_t *pscales, hipStream_t s);

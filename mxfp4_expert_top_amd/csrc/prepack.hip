@@ -59,6 +59,78 @@ __global__ __launch_bounds__(256) void prepack_scales_kernel(const uint8_t *__re
     dst[i] = v;
 }
 
+// ---------------------------------------------------------------------------
+// fp32 -> MXFP4 on the device (P3 "Kimi K3 Day-0 适配剖析", section 三: the
+// weights are quantised to MXFP4 online, when the model is loaded; OCP MX
+// v1.0: one E8M0 scale per 32 elements, E2M1 elements). One thread per
+// 32-element block:
+//   amax = max |v|; all zero -> scale code 0 and codes 0;
+//   else s = clamp(floor(log2 amax) - 2 + 127, 0, 254), with floor(log2)
+//   read from the exponent bits (subnormals included);
+//   q = v * 2^(127 - s) (a power of two: exact), |q| rounded to the nearest
+//   E2M1 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even code and
+//   |q| > 5 to 6; the sign bit of v gives bit 3 (so -0 and small negatives
+//   that round to 0 keep their sign).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_code(float q)
+{
+    const float a = fabsf(q);
+    uint32_t m;
+    if (a > 5.0f) m = 7;         // 6
+    else if (a >= 3.5f) m = 6;   // 4 (3.5 ties to the even code)
+    else if (a > 2.5f) m = 5;    // 3
+    else if (a >= 1.75f) m = 4;  // 2 (1.75 up, 2.5 down: even)
+    else if (a > 1.25f) m = 3;   // 1.5
+    else if (a >= 0.75f) m = 2;  // 1 (0.75 up, 1.25 down: even)
+    else if (a > 0.25f) m = 1;   // 0.5
+    else m = 0;                  // 0 (0.25 down: even)
+    return m | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const float *__restrict__ w,
+                                                             int64_t nblocks,
+                                                             uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nblocks) return;
+    const float4 *v4 = (const float4 *)(w + i * 32);
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float4 t = v4[j];
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+    const uint32_t u = __float_as_uint(amax);
+    const int ex = (int)((u >> 23) & 0xffu);
+    const int e = ex ? ex - 127 : (31 - __clz((int)(u & 0x7fffffu))) - 149;  // floor(log2 amax)
+    const int s = amax == 0.0f ? 0 : min(254, max(0, e - 2 + 127));
+    const float inv = __uint_as_float((uint32_t)(254 - s) << 23);  // 2^(127 - s), s <= 253
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) word |= e2m1_code(v[8 * d + j] * inv) << (4 * j);
+        out[d] = amax == 0.0f ? 0u : word;
+    }
+    *(u32x4 *)(codes + i * 16) = out;
+    scales[i] = (uint8_t)s;
+}
+
+hipError_t launch_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes,
+                                 uint8_t *scales, hipStream_t s)
+{
+    const int64_t nb = N * (K / 32);
+    if (nb <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mxfp4_quantize_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                       w, nb, codes, scales);
+    return hipGetLastError();
+}
+
 size_t packed_scale_bytes(int64_t N, int K)
 {
     const int nch = K / 128, nc4 = (nch + 3) / 4;

@@ -131,6 +131,11 @@ def test_combine_and_dequant_validation():
     assert L.moe_mxfp4_dequant(FAKE, FAKE, -1, 64, FAKE, None) == 1
     # zero-size requests are no-ops that touch nothing
     assert L.moe_mxfp4_dequant(None, None, 0, 64, None, None) == 0
+    assert L.moe_mxfp4_quantize(FAKE, 4, 48, FAKE, FAKE, None) == 2
+    assert L.moe_mxfp4_quantize(FAKE, -1, 64, FAKE, FAKE, None) == 1
+    assert L.moe_mxfp4_quantize(None, 4, 64, FAKE, FAKE, None) == 1
+    assert L.moe_mxfp4_quantize(C.c_void_p(0x10004), 4, 64, FAKE, FAKE, None) == 1
+    assert L.moe_mxfp4_quantize(None, 0, 64, None, None, None) == 0
     assert L.moe_combine(None, 0, 96, None, None, 0, 96, 4, None, 0, 96, None) == 0
 
 

@@ -38,6 +38,67 @@ def test_dequant_every_code_and_scale_bitexact(m):
     assert np.array_equal(np.signbit(got), np.signbit(want))  # -0 stays -0
 
 
+def _quantize_cases():
+    """Rows of 64 (two MX blocks each) that reach every branch of the
+    encoding: scales from subnormal to huge, exact rounding ties, saturation,
+    all-zero and signed-zero blocks."""
+    rng = np.random.default_rng(11)
+    rows = []
+    for k in range(-149, 126, 5):  # amax around 2^k, subnormal to near the fp32 top
+        r = rng.standard_normal(64) * np.float64(2.0) ** k
+        rows.append(r)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.2499, 0.2501, 0.7499, 5.0001,
+                     4.9999, 1.7501, 2.4999, 3.4999, 1.2501])
+    for k in (-120, -3, 0, 7, 100):
+        for sgn in (1.0, -1.0):
+            blk = np.concatenate([[6.0], sgn * ties, -ties[:15]]) * 2.0 ** k  # amax 6 * 2^k
+            rows.append(np.concatenate([blk, blk[::-1]]))
+    sat = np.array([7.9, 7.0, 6.5, 6.0, 5.9, 5.1, -7.5, -6.01] * 4) * 2.0 ** -5  # |q| up to 7.9
+    rows.append(np.concatenate([sat, -sat]))
+    rows.append(np.zeros(64))
+    rows.append(-np.zeros(64))
+    mixed = np.zeros(64)
+    mixed[::2] = -0.0
+    mixed[5] = 1e-3
+    mixed[40] = -3.0
+    rows.append(mixed)
+    big = np.full(64, 3.0e38)
+    big[1::2] = -1.7e38
+    rows.append(big)
+    sub = np.full(64, 1.4e-45)
+    sub[7] = -2.8e-45
+    rows.append(sub)
+    return np.ascontiguousarray(np.stack(rows).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [64, 3584])
+def test_quantize_bitexact(m, K):
+    w = _quantize_cases()
+    if K != 64:  # the same rows spread over long rows, plus random ones
+        g = np.random.default_rng(12).standard_normal((9, K)).astype(np.float32) * 0.02
+        tiled = np.resize(w, (w.size // K + 1) * K)[: (w.size // K) * K].reshape(-1, K)
+        w = np.ascontiguousarray(np.concatenate([tiled, g]))
+    codes, scales = m.moe_mxfp4_quantize(torch.from_numpy(w).to(DEV))
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mxfp4_quantize(w)
+    assert np.array_equal(np_(scales), want_s)
+    assert np.array_equal(np_(codes), want_c)
+
+
+def test_quantize_then_decode_round_trip(m):
+    # decoding what was quantised gives the nearest grid value: within half an
+    # E2M1 step (relative to the block scale) of each input
+    g = torch.Generator().manual_seed(13)
+    w = (torch.randn(64, 256, generator=g) * 0.05).to(DEV)
+    codes, scales = m.moe_mxfp4_quantize(w)
+    out = torch.empty(64, 256, dtype=torch.bfloat16, device=DEV)
+    m.moe_mxfp4_dequant(codes, scales, out)
+    torch.cuda.synchronize()
+    err = (out.float() - w).abs().view(64, 8, 32)
+    step = torch.pow(2.0, scales.float() - 127).view(64, 8, 1)  # the scale: grid spacing 0.5 .. 2
+    assert bool((err <= step * 2.0).all())  # |q| in [6, 8) saturates to 6
+
+
 def test_dequant_random_weights_bitexact(m):
     g = torch.Generator().manual_seed(5)
     w = torch.randn(300, 512, generator=g) * 0.02
