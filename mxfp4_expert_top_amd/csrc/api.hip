@@ -6,6 +6,10 @@
 #include "moe_mxfp4.h"
 #include "launch.hpp"
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 using namespace moe;
 
 namespace {
@@ -158,6 +162,24 @@ int check_layer_params(const moe_layer_params *p)
 }
 
 }  // namespace
+
+namespace moe {
+
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes)
+{
+    static std::mutex mu;
+    static std::set<std::pair<const void *, int>> done;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if (done.count({kernel, dev})) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.insert({kernel, dev});
+    return e;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -385,10 +407,10 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
                            base + L.pws, s, &plan));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
-                            up_scales, off, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
+                            up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
                             p->mode, base + L.gws, packed, s));
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-    HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr, off,
+    HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
                             p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
                             base + L.gws, packed, s));
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
-    const int32_t *__restrict__ off, const int32_t *__restrict__ plan, int N, int K,
+    const int32_t *__restrict__ plan, int N, int K,
     OutT *__restrict__ out, int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
-    const int32_t *__restrict__ off, const int32_t *__restrict__ plan, int N, int K,
+    const int32_t *__restrict__ plan, int N, int K,
     OutT *__restrict__ out, int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
-    const int32_t *__restrict__ off, const int32_t *__restrict__ plan, int N, int K,
+    const int32_t *__restrict__ plan, int N, int K,
     OutT *__restrict__ out, int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
@@ -745,7 +745,7 @@ size_t grouped_gemm_ws_bytes(int num_local, int max_rows, int N, int mode)
 template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_rows,
                                 const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                                const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                                const uint8_t *w2s, const int32_t *plan,
                                 int max_groups, int N, int K, OutT *out, int64_t ldo,
                                 hipStream_t s)
 {
@@ -760,7 +760,7 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
     const size_t lds = PACKED ? 0 : (size_t)(ACT != ACT_NONE ? 2 : 1) * COLS_B * (K / 32);
 #define ST_LAUNCH(DD)                                                                         \
     hipLaunchKernelGGL((gemm_stream_kernel<ACT, OutT, DD, PACKED>), dim3((unsigned)grid),     \
-                       dim3(256), lds, s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, \
+                       dim3(256), lds, s, a, lda, a_rows, w1c, w1s, w2c, w2s, plan, N, K, \
                        out, ldo)
     if (D == ST_DMAX)
         ST_LAUNCH(ST_DMAX);
@@ -775,7 +775,7 @@ static hipError_t launch_stream(const bf16 *a, int64_t lda, const int32_t *a_row
 template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
                               const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                              const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                              const uint8_t *w2s, const int32_t *plan,
                               int max_groups, int N, int K, OutT *out, int64_t ldo, hipStream_t s)
 {
     constexpr int COLS = tile_cols<ACT>();
@@ -785,14 +785,14 @@ static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(TL_THREADS),
-                       0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, N, K, out, ldo);
+                       0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, plan, N, K, out, ldo);
     return hipGetLastError();
 }
 
 template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_tile256(const bf16 *a, int64_t lda, const int32_t *a_rows,
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                                 const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                                 const uint8_t *w2s, const int32_t *plan,
                                  int max_groups, int N, int K, OutT *out, int64_t ldo,
                                  hipStream_t s)
 {
@@ -800,27 +800,22 @@ static hipError_t launch_tile256(const bf16 *a, int64_t lda, const int32_t *a_ro
     const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
     if (grid <= 0) return hipSuccess;
     auto kern = gemm_tile256_kernel<ACT, OutT, PACKED>;
-    static bool attr_set = false;  // per template instance; the limit is a property of the code
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)TB_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t err = ensure_dynamic_lds((const void *)kern, (int)TB_LDS);
+    if (err != hipSuccess) return err;
     const int64_t G = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(TB_THREADS), TB_LDS, s, a, lda, a_rows, w1c,
-                       w1s, w2c, w2s, off, plan, N, K, out, ldo);
+                       w1s, w2c, w2s, plan, N, K, out, ldo);
     return hipGetLastError();
 }
 
 template <typename OutT, bool PACKED>
 static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, const int32_t *a_rows,
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                               const uint8_t *w2s, const int32_t *off, const int32_t *plan,
+                               const uint8_t *w2s, const int32_t *plan,
                                int max_groups, int N, int K, OutT *out, int64_t ldo,
                                hipStream_t s)
 {
-#define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan, max_groups, N, K, out, ldo, s
+#define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, plan, max_groups, N, K, out, ldo, s
 #define MOE_GEMM_CASE(A)                                                     \
     case A:                                                                  \
         return md == MOE_SCHED_TILE256   ? launch_tile256<A, OutT, PACKED>(MOE_GEMM_ARGS) \
@@ -861,7 +856,7 @@ hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int
 
 hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, const uint8_t *w1c,
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
-                           const int32_t *off, int num_local, int max_rows, int N, int K, int act,
+                           int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
                            int packed, hipStream_t s)
 {
@@ -869,7 +864,7 @@ hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, co
     const int max_groups = max_groups_for(num_local, max_rows, rows_per_group(md));
     const int32_t *plan = (const int32_t *)plan_ws;
 #define MOE_RUN(OT, PK)                                                                    \
-    return dispatch_act<OT, PK>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, off, plan,    \
+    return dispatch_act<OT, PK>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, plan,         \
                                 max_groups, N, K, (OT *)out, ldo, s)
     if (out_f32) {
         if (packed) MOE_RUN(float, true);
@@ -888,7 +883,7 @@ hipError_t launch_grouped_gemm(const bf16 *a, int64_t lda, const int32_t *a_rows
 {
     hipError_t e = launch_gemm_plan(off, num_local, max_rows, mode, ws, s);
     if (e != hipSuccess) return e;
-    return launch_gemm_run(a, lda, a_rows, w1c, w1s, w2c, w2s, off, num_local, max_rows, N, K,
+    return launch_gemm_run(a, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N, K,
                            act, out, out_f32, ldo, mode, ws, packed, s);
 }
 

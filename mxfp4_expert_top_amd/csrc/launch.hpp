@@ -16,6 +16,10 @@ typedef __bf16 bf16;
 
 namespace moe {
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device); thread-safe (api.hip).
+hipError_t ensure_dynamic_lds(const void *kernel, int bytes);
+
 // route.hip
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 // Router scores into `splits` planes of [T][E] partial sums (splits == 1:
@@ -91,7 +95,7 @@ hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int
                             hipStream_t s);
 hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, const uint8_t *w1c,
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
-                           const int32_t *off, int num_local, int max_rows, int N, int K, int act,
+                           int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
                            int packed, hipStream_t s);
 int resolve_mode(int mode, int num_local, int max_rows);

@@ -613,13 +613,8 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
 {
     const int tiles = ((T + RG_BM - 1) / RG_BM) * ((E + RG_BN - 1) / RG_BN);
     const int steps = d / RG_BK;
-    static bool attr_set = false;  // the limit is a property of the code
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)router_tile_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)RG_LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    hipError_t err = ensure_dynamic_lds((const void *)router_tile_kernel, (int)RG_LDS);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), RG_LDS, s, x, wp, bias,
                        logits, T, d, E, steps / splits, zero_counts);
     return hipGetLastError();
