@@ -273,11 +273,14 @@ def test_grouped_gemm_vs_definition(m, mode, act, out_dtype):
 @pytest.mark.parametrize("K", [128, 640])
 def test_grouped_gemm_many_rows(m, mode, act, K):
     """Experts with more rows than one tile (300, 513, 256, 257 rows), an
-    empty and a single-row expert, a column count that is not a tile multiple,
-    and the shortest contraction (one 128-wide chunk)."""
+    empty and a single-row expert, one of 200 rows, a column count that is not
+    a tile multiple, and the shortest contraction (one 128-wide chunk). With
+    256-row tiles the groups hold 1, 128, 129, 150, 171, 200 and 256 rows:
+    every count of active 32-row tiles but 2 and 3, and both ways of sharing a
+    fifth or sixth row tile between the waves."""
     rng = np.random.default_rng(K + act + 7 * mode)
-    nl, N, T = 6, 320, 700
-    counts = np.array([300, 0, 513, 1, 256, 257], np.int32)
+    nl, N, T = 7, 320, 700
+    counts = np.array([300, 0, 513, 1, 256, 257, 200], np.int32)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     A = int(off[-1])
     x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16)
