@@ -65,6 +65,16 @@ def lib():
         L.oracle_token_rows.restype = i32
         L.oracle_token_rows.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, i64,
                                         p, p, p, p, p, p, i32, p]
+        L.oracle_e4m3_value.restype = C.c_float
+        L.oracle_e4m3_value.argtypes = [i32]
+        L.oracle_mxfp8_quantize.argtypes = [p, i64, i64, p, p]
+        L.oracle_mxfp8_decode.argtypes = [p, p, i64, i64, p]
+        L.oracle_expert_compute_mx8.restype = i32
+        L.oracle_expert_compute_mx8.argtypes = L.oracle_expert_compute.argtypes
+        L.oracle_layer_mx8.restype = i64
+        L.oracle_layer_mx8.argtypes = L.oracle_layer.argtypes
+        L.oracle_token_rows_mx8.restype = i32
+        L.oracle_token_rows_mx8.argtypes = L.oracle_token_rows.argtypes
         _lib = L
     return _lib
 
@@ -113,6 +123,31 @@ def mxfp4_quantize(w):
     scales = np.empty((N, K // 32), np.uint8)
     lib().oracle_mxfp4_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def e4m3_value(code: int) -> float:
+    """OCP-MX E4M3 element value of a code (NaN for S.1111.111)."""
+    return float(lib().oracle_e4m3_value(int(code)))
+
+
+def mxfp8_quantize(v):
+    """[N, K] fp32 -> MXFP8: codes [N, K] u8 (E4M3), scales [N, K/32] u8 (E8M0)."""
+    v = _arr(v, np.float32)
+    N, K = v.shape
+    assert K % 32 == 0
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    lib().oracle_mxfp8_quantize(_ptr(v), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mxfp8_decode(codes, scales) -> np.ndarray:
+    codes, scales = _arr(codes, np.uint8), _arr(scales, np.uint8)
+    N, K = codes.shape
+    assert scales.shape == (N, K // 32)
+    out = np.empty((N, K), np.float32)
+    lib().oracle_mxfp8_decode(_ptr(codes), _ptr(scales), N, K, _ptr(out))
+    return out
 
 
 def router_logits(x, w_router, bias=None) -> np.ndarray:
@@ -165,7 +200,10 @@ def _weights(wts):
     return [_arr(wts[n], np.uint8) for n in names]
 
 
-def expert_compute(x, I, off, perm, wts, act=ACT_SILU_MUL):
+def expert_compute(x, I, off, perm, wts, act=ACT_SILU_MUL, mx8=False):
+    """Grouped expert FFNs over the permuted rows: h [A, I] and y [A, d] fp32.
+    With mx8 the tokens and h are MXFP8-quantised (h is returned decoded, as
+    it feeds the down projection)."""
     xb = bf16_bits(x)
     T, d = xb.shape
     off, perm = _arr(off, np.int32), _arr(perm, np.int32)
@@ -174,8 +212,9 @@ def expert_compute(x, I, off, perm, wts, act=ACT_SILU_MUL):
     w6 = _weights(wts)
     h = np.empty((A, I), np.float32)
     y = np.empty((A, d), np.float32)
-    rc = lib().oracle_expert_compute(_ptr(xb), d, I, _ptr(off), _ptr(perm), n_local,
-                                     *[_ptr(a) for a in w6], act, _ptr(h), _ptr(y))
+    fn = lib().oracle_expert_compute_mx8 if mx8 else lib().oracle_expert_compute
+    rc = fn(_ptr(xb), d, I, _ptr(off), _ptr(perm), n_local, *[_ptr(a) for a in w6], act,
+            _ptr(h), _ptr(y))
     if rc != 0:
         raise MemoryError("oracle_expert_compute failed")
     return h, y
@@ -191,9 +230,10 @@ def combine(y, inv, w) -> np.ndarray:
 
 
 def layer(x, w_router, bias, wts, *, E, k, I, e0=0, n_local=None, act=ACT_SILU_MUL,
-          logits=None):
+          logits=None, mx8=False):
     """The whole layer. If ``logits`` is given it is used instead of the router
-    GEMM (routing replayed on another implementation's fp32 scores).
+    GEMM (routing replayed on another implementation's fp32 scores). With mx8
+    the expert FFNs run in the block-scaled precision mode (MXFP8 tokens and h).
 
     Returns a dict: out [T,d] f32, logits, idx, w, counts, off, perm, inv, A.
     """
@@ -217,7 +257,8 @@ def layer(x, w_router, bias, wts, *, E, k, I, e0=0, n_local=None, act=ACT_SILU_M
     perm = np.empty(T * k, np.int32)
     inv = np.empty((T, k), np.int32)
     out = np.empty((T, d), np.float32)
-    A = lib().oracle_layer(_ptr(xb), _ptr(w_router), _ptr(bias), _ptr(lg), given,
+    fn = lib().oracle_layer_mx8 if mx8 else lib().oracle_layer
+    A = fn(_ptr(xb), _ptr(w_router), _ptr(bias), _ptr(lg), given,
                            T, d, E, k, I, e0, n_local, *[_ptr(a) for a in w6], act,
                            _ptr(idx), _ptr(w), _ptr(counts), _ptr(off), _ptr(perm),
                            _ptr(inv), _ptr(out))
@@ -227,7 +268,7 @@ def layer(x, w_router, bias, wts, *, E, k, I, e0=0, n_local=None, act=ACT_SILU_M
                 perm=perm[:A], inv=inv, A=int(A))
 
 
-def token_rows(x, idx, w, tokens, wts, *, I, e0=0, n_local, act=ACT_SILU_MUL):
+def token_rows(x, idx, w, tokens, wts, *, I, e0=0, n_local, act=ACT_SILU_MUL, mx8=False):
     """Layer output rows for the listed tokens only, from their routing."""
     xb = bf16_bits(x)
     T, d = xb.shape
@@ -236,7 +277,8 @@ def token_rows(x, idx, w, tokens, wts, *, I, e0=0, n_local, act=ACT_SILU_MUL):
     tokens = _arr(np.asarray(tokens, np.int64), np.int64)
     w6 = _weights(wts)
     out = np.empty((tokens.shape[0], d), np.float32)
-    rc = lib().oracle_token_rows(_ptr(xb), d, I, k, _ptr(idx), _ptr(w), _ptr(tokens),
+    fn = lib().oracle_token_rows_mx8 if mx8 else lib().oracle_token_rows
+    rc = fn(_ptr(xb), d, I, k, _ptr(idx), _ptr(w), _ptr(tokens),
                                  tokens.shape[0], e0, n_local, *[_ptr(a) for a in w6],
                                  act, _ptr(out))
     if rc != 0:

@@ -16,8 +16,18 @@
  *   P2  "SGLang 0.5.17：Kimi K3 原生 MXFP4 推理架构解析" (mindlynx.top)
  *   P3  "Kimi K3 Day-0 适配剖析:KDA/Gated MLA 混合注意力、MXFP4 在线量化与
  *        896 专家 MoE" (7yue.com MUSA learning center, m8-l14)
- *   OCP-MX  OCP Microscaling Formats (MX) Specification v1.0: the E2M1 element
- *        type and the E8M0 shared scale with 32-element blocks.
+ *   OCP-MX  OCP Microscaling Formats (MX) Specification v1.0: the E2M1 and
+ *        E4M3 element types, the E8M0 shared scale with 32-element blocks, and
+ *        the conversion to MX (shared exponent floor(log2 amax) minus the
+ *        element type's emax, elements rounded to nearest-even and clamped).
+ *
+ * Two precision modes. The default one keeps the latent tokens and h in
+ * bf16/fp32 against MXFP4 weights, as the pages describe (4-bit weights
+ * combined with higher-precision activations, P1 §二 第一层). The MX8 mode
+ * (functions ending in _mx8) quantises the tokens and h to MXFP8 (E4M3) before
+ * each projection, the input contract of block-scaled 8-bit x 4-bit matrix
+ * instructions; it is a separate accuracy contract, not an approximation of
+ * the default mode.
  *
  * Pins (tests/test_oracle_*.py): the E2M1 table against its bit-field
  * definition; every E8M0 scale; every (code, scale) decode; hand-built
@@ -26,7 +36,12 @@
  * all-equal closed forms; permutation invariants and permute-then-unpermute
  * identity; the layer against a dense, mask-weighted fp64 evaluation of every
  * expert that bypasses the permutation; E=1,k=1 against a textbook MLP; and
- * the all-ones closed form out = I*S*silu(S).
+ * the all-ones closed form out = I*S*silu(S). MX8 mode: every E4M3 code
+ * against torch's float8_e4m3fn and the spec's landmark values; the MXFP8
+ * quantiser against frexp plus torch's round-to-nearest-even fp8 conversion
+ * on tie, clamp, zero and extreme-exponent blocks; the layer against a dense
+ * fp64 evaluation with its own quantisation; closed forms of all-ones
+ * weights whose h lands on the E4M3 grid, on a tie and on the 448 clamp.
  */
 #include <math.h>
 #include <stdint.h>
@@ -132,6 +147,87 @@ void oracle_mxfp4_quantize(const float *w, int64_t N, int64_t K,
             }
         }
     }
+}
+
+/* ------------------------------------------------------------------ */
+/* MXFP8 activations (the block-scaled precision mode)                 */
+/* ------------------------------------------------------------------ */
+
+/* OCP-MX E4M3 (FP8): sign bit 7, exponent bits 6-3 (bias 7), mantissa bits
+ * 2-0; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN, so the
+ * largest finite magnitude is S.1111.110 = 448. No infinities. */
+float oracle_e4m3_value(int code)
+{
+    code &= 0xff;
+    int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    float v = (e == 0) ? ldexpf((float)m / 8.0f, -6) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -v : v;
+}
+
+/* Round a magnitude in [0, 448] to the nearest finite E4M3 magnitude
+ * (codes 0x00..0x7E); on a tie take the even code. An argmin over the grid. */
+static int e4m3_round_magnitude(float a)
+{
+    int best = 0;
+    float best_dist = fabsf(a - oracle_e4m3_value(0));
+    for (int c = 1; c <= 0x7E; c++) {
+        float dist = fabsf(a - oracle_e4m3_value(c));
+        if (dist < best_dist || (dist == best_dist && (c % 2) == 0 && (best % 2) != 0)) {
+            best = c;
+            best_dist = dist;
+        }
+    }
+    return best;
+}
+
+/* OCP-MX conversion of [N, K] fp32 to MXFP8 (E4M3 elements, E8M0 scale per
+ * 32-element block along K): shared exponent floor(log2 amax) - emax(E4M3)=8,
+ * taken exactly from frexp and clamped to the E8M0 range; elements divided by
+ * the scale (a power of two, so exactly) and rounded to nearest-even, with
+ * magnitudes beyond 448 clamped to 448. All-zero block: scale 0, codes 0.
+ * A negative element that rounds to zero keeps its sign (code 0x80).
+ * codes [N, K] (one byte per element), scales [N, K/32]. */
+void oracle_mxfp8_quantize(const float *v, int64_t N, int64_t K,
+                           uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < K / 32; b++) {
+            const float *blk = v + n * K + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; i++)
+                if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+            int s = 0;
+            if (amax != 0.0f) {
+                int e2;
+                frexpf(amax, &e2); /* amax = m * 2^e2, m in [0.5, 1) */
+                s = (e2 - 1) - 8 + 127;
+                if (s < 0) s = 0;
+                if (s > 254) s = 254;
+            }
+            scales[n * (K / 32) + b] = (uint8_t)s;
+            for (int i = 0; i < 32; i++) {
+                int c = 0;
+                if (amax != 0.0f) {
+                    float q = blk[i] / ldexpf(1.0f, s - 127);
+                    float a = fabsf(q);
+                    int mag = (a >= 448.0f) ? 0x7E : e4m3_round_magnitude(a);
+                    c = mag | (signbit(q) ? 0x80 : 0);
+                }
+                codes[n * K + b * 32 + i] = (uint8_t)c;
+            }
+        }
+    }
+}
+
+/* Decode [N, K] MXFP8: element value times its block's scale (exact). */
+void oracle_mxfp8_decode(const uint8_t *codes, const uint8_t *scales,
+                         int64_t N, int64_t K, float *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t i = 0; i < K; i++)
+            out[n * K + i] = ldexpf(oracle_e4m3_value(codes[n * K + i]),
+                                    (int)scales[n * (K / 32) + i / 32] - 127);
 }
 
 /* ------------------------------------------------------------------ */
@@ -283,6 +379,75 @@ static void expert_ffn(const float *xt, const float *wg, const float *wu, const 
     }
 }
 
+/* The same FFN in the block-scaled precision mode (MX8): the latent token
+ * arrives quantised to MXFP8 (xq, decoded values), and h is quantised to
+ * MXFP8 along I before the down projection. A product of two MX values is
+ * exact, so each projection sums in fp64 and rounds to fp32 once; h is
+ * act(g, u) in fp32 as above. hq receives the decoded quantised h; hc, hs are
+ * scratch for its codes [I] and scales [I/32]. */
+static void expert_ffn_mx8(const float *xq, const float *wg, const float *wu, const float *wd,
+                           int64_t d, int64_t I, int act, float *h, uint8_t *hc, uint8_t *hs,
+                           float *hq, float *y)
+{
+    for (int64_t n = 0; n < I; n++) {
+        double g = 0.0, u = 0.0;
+        for (int64_t i = 0; i < d; i++) g += (double)xq[i] * (double)wg[n * d + i];
+        for (int64_t i = 0; i < d; i++) u += (double)xq[i] * (double)wu[n * d + i];
+        h[n] = act_apply(act, (float)g, (float)u);
+    }
+    oracle_mxfp8_quantize(h, 1, I, hc, hs);
+    oracle_mxfp8_decode(hc, hs, 1, I, hq);
+    for (int64_t m = 0; m < d; m++) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < I; n++) acc += (double)hq[n] * (double)wd[m * I + n];
+        y[m] = (float)acc;
+    }
+}
+
+/* One token's latent row as the FFN input: bf16 widened to fp32, and in the
+ * MX8 mode quantised to MXFP8 along d and decoded again. xc, xs: scratch of
+ * d and d/32 bytes. */
+static void token_input(const uint16_t *x, int64_t t, int64_t d, int mx8, uint8_t *xc,
+                        uint8_t *xs, float *xt)
+{
+    for (int64_t i = 0; i < d; i++) xt[i] = bf16_bits_to_float(x[t * d + i]);
+    if (mx8) {
+        oracle_mxfp8_quantize(xt, 1, d, xc, xs);
+        oracle_mxfp8_decode(xc, xs, 1, d, xt);
+    }
+}
+
+/* Scratch for one FFN evaluation. */
+typedef struct {
+    float *xt, *h, *hq, *y;
+    uint8_t *xc, *xs, *hc, *hs;
+} ffn_scratch;
+
+static int scratch_alloc(ffn_scratch *sc, int64_t d, int64_t I)
+{
+    sc->xt = (float *)malloc((size_t)d * sizeof(float));
+    sc->h = (float *)malloc((size_t)I * sizeof(float));
+    sc->hq = (float *)malloc((size_t)I * sizeof(float));
+    sc->y = (float *)malloc((size_t)d * sizeof(float));
+    sc->xc = (uint8_t *)malloc((size_t)d);
+    sc->xs = (uint8_t *)malloc((size_t)(d / 32 > 0 ? d / 32 : 1));
+    sc->hc = (uint8_t *)malloc((size_t)I);
+    sc->hs = (uint8_t *)malloc((size_t)(I / 32 > 0 ? I / 32 : 1));
+    return (sc->xt && sc->h && sc->hq && sc->y && sc->xc && sc->xs && sc->hc && sc->hs) ? 0 : -1;
+}
+
+static void scratch_free(ffn_scratch *sc)
+{
+    free(sc->xt);
+    free(sc->h);
+    free(sc->hq);
+    free(sc->y);
+    free(sc->xc);
+    free(sc->xs);
+    free(sc->hc);
+    free(sc->hs);
+}
+
 typedef struct {
     float *wg, *wu, *wd;
 } decoded_expert;
@@ -314,30 +479,59 @@ static void free_expert(decoded_expert *e)
  * Weight arrays index local experts: gate/up codes [n_local][I][d/2],
  * scales [n_local][I][d/32]; down codes [n_local][d][I/2], scales
  * [n_local][d][I/32]. */
+static int expert_compute_impl(const uint16_t *x, int64_t d, int64_t I,
+                               const int32_t *off, const int32_t *perm_token, int64_t n_local,
+                               const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                               const uint8_t *us, const uint8_t *dc, const uint8_t *ds,
+                               int act, int mx8, float *h, float *y)
+{
+    ffn_scratch sc;
+    if (scratch_alloc(&sc, d, I)) {
+        scratch_free(&sc);
+        return -1;
+    }
+    for (int64_t le = 0; le < n_local; le++) {
+        if (off[le + 1] == off[le]) continue;
+        decoded_expert we;
+        if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) {
+            scratch_free(&sc);
+            return -1;
+        }
+        for (int64_t pos = off[le]; pos < off[le + 1]; pos++) {
+            token_input(x, perm_token[pos], d, mx8, sc.xc, sc.xs, sc.xt);
+            if (mx8) {
+                expert_ffn_mx8(sc.xt, we.wg, we.wu, we.wd, d, I, act, sc.h, sc.hc, sc.hs,
+                               h + pos * I, y + pos * d);
+            } else {
+                expert_ffn(sc.xt, we.wg, we.wu, we.wd, d, I, act, h + pos * I, y + pos * d);
+            }
+        }
+        free_expert(&we);
+    }
+    scratch_free(&sc);
+    return 0;
+}
+
 int oracle_expert_compute(const uint16_t *x, int64_t d, int64_t I,
                           const int32_t *off, const int32_t *perm_token, int64_t n_local,
                           const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
                           const uint8_t *us, const uint8_t *dc, const uint8_t *ds,
                           int act, float *h, float *y)
 {
-    float *xt = (float *)malloc((size_t)d * sizeof(float));
-    if (!xt) return -1;
-    for (int64_t le = 0; le < n_local; le++) {
-        if (off[le + 1] == off[le]) continue;
-        decoded_expert we;
-        if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) {
-            free(xt);
-            return -1;
-        }
-        for (int64_t pos = off[le]; pos < off[le + 1]; pos++) {
-            int64_t t = perm_token[pos];
-            for (int64_t i = 0; i < d; i++) xt[i] = bf16_bits_to_float(x[t * d + i]);
-            expert_ffn(xt, we.wg, we.wu, we.wd, d, I, act, h + pos * I, y + pos * d);
-        }
-        free_expert(&we);
-    }
-    free(xt);
-    return 0;
+    return expert_compute_impl(x, d, I, off, perm_token, n_local, gc, gs, uc, us, dc, ds, act,
+                               0, h, y);
+}
+
+/* The MX8 mode of the grouped expert compute; h receives the decoded
+ * MXFP8-quantised h that feeds the down projection. */
+int oracle_expert_compute_mx8(const uint16_t *x, int64_t d, int64_t I,
+                              const int32_t *off, const int32_t *perm_token, int64_t n_local,
+                              const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                              const uint8_t *us, const uint8_t *dc, const uint8_t *ds,
+                              int act, float *h, float *y)
+{
+    return expert_compute_impl(x, d, I, off, perm_token, n_local, gc, gs, uc, us, dc, ds, act,
+                               1, h, y);
 }
 
 /* Combine (P3 §四: results come back weighted; P2 §MoE稀疏激活: the weighted
@@ -370,14 +564,14 @@ void oracle_combine(const float *y, const int32_t *inv, const float *w,
  * scores); otherwise it is written. Outputs: out [T, d] fp32, idx/w [T, k],
  * counts [E], off [n_local+1], perm_token [T*k], inv [T, k]. Returns the
  * number of local assignments A, or -1 on allocation failure. */
-int64_t oracle_layer(const uint16_t *x, const float *w_router, const float *bias,
-                     float *logits, int logits_given,
-                     int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
-                     int64_t e0, int64_t n_local,
-                     const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
-                     const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
-                     int32_t *idx, float *w, int32_t *counts, int32_t *off,
-                     int32_t *perm_token, int32_t *inv, float *out)
+static int64_t layer_impl(const uint16_t *x, const float *w_router, const float *bias,
+                          float *logits, int logits_given,
+                          int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                          int64_t e0, int64_t n_local,
+                          const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                          const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                          int mx8, int32_t *idx, float *w, int32_t *counts, int32_t *off,
+                          int32_t *perm_token, int32_t *inv, float *out)
 {
     if (!logits_given) oracle_router_logits(x, w_router, bias, T, d, E, logits);
     oracle_topk_softmax(logits, T, E, k, idx, w);
@@ -392,18 +586,90 @@ int64_t oracle_layer(const uint16_t *x, const float *w_router, const float *bias
         free(y);
         return -1;
     }
-    int rc = oracle_expert_compute(x, d, I, off, perm_token, n_local, gc, gs, uc, us, dc, ds,
-                                   act, h, y);
+    int rc = expert_compute_impl(x, d, I, off, perm_token, n_local, gc, gs, uc, us, dc, ds,
+                                 act, mx8, h, y);
     if (rc == 0) oracle_combine(y, inv, w, T, k, d, out);
     free(h);
     free(y);
     return rc == 0 ? A : -1;
 }
 
+/* Route -> dispatch -> expert compute -> combine, in the pages' order
+ * (P3 §四: the three MoE steps). If logits_given, `logits` is read instead of
+ * computed (so routing can be replayed from another implementation's fp32
+ * scores); otherwise it is written. Outputs: out [T, d] fp32, idx/w [T, k],
+ * counts [E], off [n_local+1], perm_token [T*k], inv [T, k]. Returns the
+ * number of local assignments A, or -1 on allocation failure. */
+int64_t oracle_layer(const uint16_t *x, const float *w_router, const float *bias,
+                     float *logits, int logits_given,
+                     int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                     int64_t e0, int64_t n_local,
+                     const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                     const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                     int32_t *idx, float *w, int32_t *counts, int32_t *off,
+                     int32_t *perm_token, int32_t *inv, float *out)
+{
+    return layer_impl(x, w_router, bias, logits, logits_given, T, d, E, k, I, e0, n_local, gc,
+                      gs, uc, us, dc, ds, act, 0, idx, w, counts, off, perm_token, inv, out);
+}
+
+/* The whole layer in the MX8 mode: routing as above (the router reads the
+ * bf16 tokens), expert FFNs as expert_ffn_mx8. */
+int64_t oracle_layer_mx8(const uint16_t *x, const float *w_router, const float *bias,
+                         float *logits, int logits_given,
+                         int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                         int64_t e0, int64_t n_local,
+                         const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                         const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                         int32_t *idx, float *w, int32_t *counts, int32_t *off,
+                         int32_t *perm_token, int32_t *inv, float *out)
+{
+    return layer_impl(x, w_router, bias, logits, logits_given, T, d, E, k, I, e0, n_local, gc,
+                      gs, uc, us, dc, ds, act, 1, idx, w, counts, off, perm_token, inv, out);
+}
+
 /* The same arithmetic for chosen tokens only, given their routing: for each
  * listed token t, out_rows[r, :] = sum_j w[t,j] * FFN_{idx[t,j]}(x[t]) over
  * local experts, in j order. This is what the layer computes for row t,
  * evaluated one token at a time (used where the full layer is too slow). */
+static int token_rows_impl(const uint16_t *x, int64_t d, int64_t I, int64_t k,
+                           const int32_t *idx, const float *w, const int64_t *tokens,
+                           int64_t n_tokens, int64_t e0, int64_t n_local,
+                           const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                           const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                           int mx8, float *out_rows)
+{
+    ffn_scratch sc;
+    if (scratch_alloc(&sc, d, I)) {
+        scratch_free(&sc);
+        return -1;
+    }
+    for (int64_t r = 0; r < n_tokens; r++) {
+        int64_t t = tokens[r];
+        float *o = out_rows + r * d;
+        for (int64_t m = 0; m < d; m++) o[m] = 0.0f;
+        token_input(x, t, d, mx8, sc.xc, sc.xs, sc.xt);
+        for (int64_t j = 0; j < k; j++) {
+            int64_t le = (int64_t)idx[t * k + j] - e0;
+            if (le < 0 || le >= n_local) continue;
+            decoded_expert we;
+            if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) {
+                scratch_free(&sc);
+                return -1;
+            }
+            if (mx8)
+                expert_ffn_mx8(sc.xt, we.wg, we.wu, we.wd, d, I, act, sc.h, sc.hc, sc.hs, sc.hq,
+                               sc.y);
+            else
+                expert_ffn(sc.xt, we.wg, we.wu, we.wd, d, I, act, sc.h, sc.y);
+            free_expert(&we);
+            for (int64_t m = 0; m < d; m++) o[m] += w[t * k + j] * sc.y[m];
+        }
+    }
+    scratch_free(&sc);
+    return 0;
+}
+
 int oracle_token_rows(const uint16_t *x, int64_t d, int64_t I, int64_t k,
                       const int32_t *idx, const float *w, const int64_t *tokens,
                       int64_t n_tokens, int64_t e0, int64_t n_local,
@@ -411,27 +677,17 @@ int oracle_token_rows(const uint16_t *x, int64_t d, int64_t I, int64_t k,
                       const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
                       float *out_rows)
 {
-    float *xt = (float *)malloc((size_t)d * sizeof(float));
-    float *h = (float *)malloc((size_t)I * sizeof(float));
-    float *y = (float *)malloc((size_t)d * sizeof(float));
-    if (!xt || !h || !y) return -1;
-    for (int64_t r = 0; r < n_tokens; r++) {
-        int64_t t = tokens[r];
-        float *o = out_rows + r * d;
-        for (int64_t m = 0; m < d; m++) o[m] = 0.0f;
-        for (int64_t i = 0; i < d; i++) xt[i] = bf16_bits_to_float(x[t * d + i]);
-        for (int64_t j = 0; j < k; j++) {
-            int64_t le = (int64_t)idx[t * k + j] - e0;
-            if (le < 0 || le >= n_local) continue;
-            decoded_expert we;
-            if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) return -1;
-            expert_ffn(xt, we.wg, we.wu, we.wd, d, I, act, h, y);
-            free_expert(&we);
-            for (int64_t m = 0; m < d; m++) o[m] += w[t * k + j] * y[m];
-        }
-    }
-    free(xt);
-    free(h);
-    free(y);
-    return 0;
+    return token_rows_impl(x, d, I, k, idx, w, tokens, n_tokens, e0, n_local, gc, gs, uc, us,
+                           dc, ds, act, 0, out_rows);
+}
+
+int oracle_token_rows_mx8(const uint16_t *x, int64_t d, int64_t I, int64_t k,
+                          const int32_t *idx, const float *w, const int64_t *tokens,
+                          int64_t n_tokens, int64_t e0, int64_t n_local,
+                          const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                          const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                          float *out_rows)
+{
+    return token_rows_impl(x, d, I, k, idx, w, tokens, n_tokens, e0, n_local, gc, gs, uc, us,
+                           dc, ds, act, 1, out_rows);
 }
