@@ -77,6 +77,7 @@ enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2
  * layout described above. PACKED: the streaming layout moe_mxfp4_prepack
  * produces (same codes and scales, permuted for the kernels). */
 enum moe_weight_layout { MOE_LAYOUT_OCP = 0, MOE_LAYOUT_PACKED = 1 };
+enum moe_precision { MOE_PREC_BF16 = 0, MOE_PREC_MX8 = 1 };
 
 /* Schedules of the grouped expert GEMMs (the `mode` argument). All give the
  * same results up to fp32 summation order; they differ in how work is cut:
@@ -233,6 +234,47 @@ int moe_grouped_gemm_mxfp4(const void *a, int64_t lda, const int32_t *a_rows,
                            moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The block-scaled precision mode (MX8). The pages' layer pairs 4-bit weights
+ * with higher-precision activations (P1 section 二, 第一层); this mode instead
+ * rounds the activations to MXFP8 so that both operands and their scales go
+ * to the gfx950 block-scaled matrix instruction as stored (8-bit rate, no
+ * decode). It is a separate accuracy contract, defined with OCP-MX v1.0
+ * formats: E4M3 elements (bias 7, largest magnitude 448), one E8M0 scale per
+ * 32 elements along the contraction.
+ * ------------------------------------------------------------------------ */
+
+/* moe_mxfp8_quantize -- rows of v (bf16 or fp32, row stride ldv elements) to
+ * MXFP8: codes [N][K] (one E4M3 byte per element), scales [N][K/32].
+ * Per 32-element block: amax = max|v|; all zero -> scale code 0, codes 0;
+ * else s = clamp(floor(log2 amax) - 8 + 127, 0, 254), and each element is
+ * v / 2^(s-127) rounded to the nearest E4M3 value (ties to the even code),
+ * magnitudes from 448 up clamped to 448, sign bit from v (-0 keeps it).
+ * Preconditions: finite v. Errors: K % 32 != 0 -> UNSUPPORTED; v_dtype not
+ * a moe_dtype, ldv < K, ldv % 8 != 0, NULL or misaligned (16-byte) pointers
+ * -> INVALID_ARG. N == 0 is a no-op. */
+int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K,
+                       uint8_t *codes, uint8_t *scales, moe_stream_t stream);
+
+/* moe_grouped_gemm_mx8 -- moe_grouped_gemm_mxfp4 with MXFP8 rows:
+ *   a_row  = (a_rows ? a_rows[r] : r)
+ *   acc1[n] = sum_k A(a_row, k) * W1[e][n][k], A(r, k) = E4M3(a_codes[r *
+ *             lda + k]) * 2^(a_scales[r * (lda/32) + k/32] - 127)
+ * on v_mfma_scale_f32_32x32x64_f8f6f4 (exact products; each 64-long partial
+ * sum is formed inside the instruction, then accumulated in fp32); out as in
+ * moe_grouped_gemm_mxfp4. 256-row tiles only; ws holds
+ * moe_grouped_gemm_mx8_workspace_size(...) bytes.
+ * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0; 16-byte
+ * aligned code and scale arrays. Errors as moe_grouped_gemm_mxfp4. */
+size_t moe_grouped_gemm_mx8_workspace_size(int num_local, int max_rows);
+int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_t lda,
+                         const int32_t *a_rows, const uint8_t *w1_codes,
+                         const uint8_t *w1_scales, const uint8_t *w2_codes,
+                         const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
+                         int max_rows, int N, int K, int block_size, int w_layout, int act,
+                         void *out, int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine -- weighted unpermute (P3 section 四, combine: results come back
  * weighted; P2 "MoE 稀疏激活": weighted sum of the selected experts):
  *   out[t][m] = sum_{j=0..k-1, inv[t][j] >= 0} topk_w[t][j] * y[inv[t][j]][m]
@@ -261,6 +303,9 @@ typedef struct {
     int out_dtype;    /* enum moe_dtype of `out`                  */
     int mode;         /* GEMM schedule, as moe_grouped_gemm_mxfp4 */
     int weight_layout; /* enum moe_weight_layout of all six weight arrays */
+    int precision;    /* enum moe_precision: MOE_PREC_BF16 (the pages' bf16
+                         activations) or MOE_PREC_MX8 (tokens and h rounded to
+                         MXFP8 before each projection; `mode` is then ignored) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

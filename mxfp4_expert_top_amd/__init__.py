@@ -22,6 +22,7 @@ DT_BF16, DT_F32 = 0, 1
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
 MODE_AUTO, MODE_STREAM, MODE_TILED, MODE_TILE128, MODE_TILE256 = 0, 1, 2, 3, 4
 LAYOUT_OCP, LAYOUT_PACKED = 0, 1
+PREC_BF16, PREC_MX8 = 0, 1
 MX_BLOCK = 32
 
 
@@ -70,6 +71,13 @@ def _load(path=None):
     L.moe_layer_workspace_size.argtypes = [p]
     L.moe_layer.restype = i32
     L.moe_layer.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, sz, p, p]
+    L.moe_mxfp8_quantize.restype = i32
+    L.moe_mxfp8_quantize.argtypes = [p, i32, i64, i64, i32, p, p, p]
+    L.moe_grouped_gemm_mx8_workspace_size.restype = sz
+    L.moe_grouped_gemm_mx8_workspace_size.argtypes = [i32, i32]
+    L.moe_grouped_gemm_mx8.restype = i32
+    L.moe_grouped_gemm_mx8.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                       i32, p, i32, i64, p, sz, p]
     return L
 
 
@@ -80,13 +88,14 @@ EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4
             "moe_mxfp4_prepack", "moe_mxfp4_packed_scale_bytes",
             "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size",
             "moe_grouped_gemm_schedule", "moe_combine",
-            "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error")
+            "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error",
+            "moe_mxfp8_quantize", "moe_grouped_gemm_mx8", "moe_grouped_gemm_mx8_workspace_size")
 
 
 class LayerParams(C.Structure):
     _fields_ = [(n, C.c_int) for n in ("T", "d", "E", "k", "I", "block_size", "expert_begin",
                                         "num_local", "act", "out_dtype", "mode",
-                                        "weight_layout")]
+                                        "weight_layout", "precision")]
 
 
 def _check(fn, status):
@@ -205,6 +214,29 @@ def moe_mxfp4_quantize(w, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+def moe_mxfp8_quantize(v, codes=None, scales=None, stream=None):
+    """bf16 or fp32 [N, K] on the GPU -> MXFP8 (codes uint8 [N, K] E4M3,
+    scales uint8 [N, K/32] E8M0)."""
+    if v.dtype not in (torch.bfloat16, torch.float32) or v.dim() != 2:
+        raise TypeError("v must be a 2-D bf16 or fp32 tensor")
+    N, K = v.shape
+    if v.stride(1) != 1:
+        raise ValueError("v rows must be contiguous")
+    if codes is None:
+        codes = torch.empty(N, K, dtype=torch.uint8, device=v.device)
+    if scales is None:
+        scales = torch.empty(N, K // 32, dtype=torch.uint8, device=v.device)
+    _dev(codes, scales)
+    if not v.is_cuda or v.device != codes.device:
+        raise ValueError("v must be on the GPU of codes and scales")
+    _want(codes, torch.uint8, (N, K), "codes")
+    _want(scales, torch.uint8, (N, K // 32), "scales")
+    _check("moe_mxfp8_quantize", lib.moe_mxfp8_quantize(_ptr(v), _dt(v), v.stride(0), N, K,
+                                                        _ptr(codes), _ptr(scales),
+                                                        _stream(stream)))
+    return codes, scales
+
+
 def moe_mxfp4_dequant(codes, scales, out, stream=None):
     N, K = out.shape
     _dev(codes, scales, out)
@@ -290,6 +322,42 @@ def moe_grouped_gemm_mxfp4(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
     _check("moe_grouped_gemm_mxfp4", st)
 
 
+def moe_grouped_gemm_mx8_workspace_size(num_local, max_rows):
+    return int(lib.moe_grouped_gemm_mx8_workspace_size(num_local, max_rows))
+
+
+def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
+                         expert_offsets, max_rows, act, out, ws, w_layout=LAYOUT_OCP,
+                         stream=None):
+    """moe_grouped_gemm_mxfp4 with MXFP8 rows (a_codes uint8 [rows, K] E4M3,
+    a_scales uint8 [rows, K/32]) on the block-scaled matrix cores."""
+    num_local = expert_offsets.shape[0] - 1
+    N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
+    _dev(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
+         out, ws)
+    if a_codes.dtype != torch.uint8 or a_codes.dim() != 2 or a_codes.shape[1] != K:
+        raise ValueError("a_codes must be [rows, K] uint8")
+    _want(a_scales, torch.uint8, (a_codes.shape[0], K // 32), "a_scales")
+    _want(w1_codes, torch.uint8, (num_local, N, K // 2), "w1_codes")
+    _want(w1_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w1_scales")
+    if w2_codes is not None:
+        _want(w2_codes, torch.uint8, (num_local, N, K // 2), "w2_codes")
+        _want(w2_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w2_scales")
+    if out.dim() != 2 or out.shape[1] != N or out.shape[0] < max_rows:
+        raise ValueError("out must be [>= max_rows, N]")
+    if a_rows is not None:
+        if a_rows.dtype != torch.int32 or a_rows.numel() < max_rows:
+            raise ValueError("a_rows must be int32 with >= max_rows entries")
+    elif a_codes.shape[0] < max_rows:
+        raise ValueError("a_codes must hold >= max_rows rows")
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    st = lib.moe_grouped_gemm_mx8(
+        _ptr(a_codes), _ptr(a_scales), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
+        _ptr(w2_codes), _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K,
+        MX_BLOCK, w_layout, act, _ptr(out), _dt(out), N, _ptr(ws), nbytes, _stream(stream))
+    _check("moe_grouped_gemm_mx8", st)
+
+
 def moe_combine(y, inv, topk_w, out, stream=None):
     T, k = inv.shape
     d = out.shape[1]
@@ -304,10 +372,11 @@ def moe_combine(y, inv, topk_w, out, stream=None):
 
 
 def layer_params(T, d, E, k, I, expert_begin=0, num_local=None, act=ACT_SILU_MUL,
-                 out_dtype=DT_BF16, mode=MODE_AUTO, weight_layout=LAYOUT_OCP):
+                 out_dtype=DT_BF16, mode=MODE_AUTO, weight_layout=LAYOUT_OCP,
+                 precision=PREC_BF16):
     return LayerParams(T, d, E, k, I, MX_BLOCK, expert_begin,
                        E - expert_begin if num_local is None else num_local, act, out_dtype, mode,
-                       weight_layout)
+                       weight_layout, precision)
 
 
 def moe_layer_workspace_size(params: LayerParams) -> int:

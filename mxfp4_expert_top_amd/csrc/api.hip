@@ -101,6 +101,7 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 // Workspace layout of moe_layer; every region 256-byte aligned.
 struct LayerWs {
     size_t logits, planes, wsplit, idx, w, off, perm, inv, pws, gws, h, y, total;
+    size_t xq, xs, hq, hs;  // MX8 mode: MXFP8 tokens and h (codes, scales)
     int splits;
     int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
 };
@@ -132,8 +133,18 @@ LayerWs layer_ws(const moe_layer_params *p)
     L.inv = o;    o += round_up(A * 4);
     L.pws = o;    o += round_up(permute_ws_bytes(p->T, p->num_local));
     L.gws = o;
-    o += round_up(grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
-    L.h = o;      o += round_up(A * (size_t)p->I * 2);
+    const bool mx8 = p->precision == MOE_PREC_MX8;
+    o += round_up(mx8 ? mx8_gemm_ws_bytes(p->num_local, (int)A)
+                      : grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
+    // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
+    // from there to MXFP8
+    L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
+    if (mx8) {
+        L.xq = o; o += round_up(T * (size_t)p->d);
+        L.xs = o; o += round_up(T * (size_t)(p->d / 32));
+        L.hq = o; o += round_up(A * (size_t)p->I);
+        L.hs = o; o += round_up(A * (size_t)(p->I / 32));
+    }
     // fp32 expert outputs: bf16 here would spend most of the max-abs error
     // budget of the layer (measured 3.05e-2 rms against the 3e-2 bound)
     L.y = o;      o += round_up(A * (size_t)p->d * 4);
@@ -153,6 +164,7 @@ int check_layer_params(const moe_layer_params *p)
     CHECK(p->mode >= MOE_SCHED_AUTO && p->mode <= MOE_SCHED_TILE256, MOE_ERR_INVALID_ARG);
     CHECK(p->weight_layout == MOE_LAYOUT_OCP || p->weight_layout == MOE_LAYOUT_PACKED,
           MOE_ERR_INVALID_ARG);
+    CHECK(p->precision == MOE_PREC_BF16 || p->precision == MOE_PREC_MX8, MOE_ERR_INVALID_ARG);
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
     CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
     CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
@@ -249,6 +261,50 @@ int moe_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes, uint8_t
     CHECK(w && codes && scales, MOE_ERR_INVALID_ARG);
     CHECK(aligned(w, 16) && aligned(codes, 16), MOE_ERR_INVALID_ARG);
     HIP_TRY(launch_mxfp4_quantize(w, N, K, codes, scales, as_stream(stream)));
+    return MOE_OK;
+}
+
+int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K,
+                       uint8_t *codes, uint8_t *scales, moe_stream_t stream)
+{
+    CHECK(N >= 0 && K >= 0, MOE_ERR_INVALID_ARG);
+    CHECK(v_dtype == MOE_DT_BF16 || v_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
+    CHECK(K % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (N == 0 || K == 0) return MOE_OK;
+    CHECK(v && codes && scales, MOE_ERR_INVALID_ARG);
+    CHECK(ldv >= K && ldv % 8 == 0, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(v, 16) && aligned(codes, 16), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_mxfp8_quantize(v, v_dtype == MOE_DT_F32, ldv, N, K, codes, scales,
+                                  as_stream(stream)));
+    return MOE_OK;
+}
+
+size_t moe_grouped_gemm_mx8_workspace_size(int num_local, int max_rows)
+{
+    if (num_local < 1 || max_rows < 0) return 0;
+    return mx8_gemm_ws_bytes(num_local, max_rows);
+}
+
+int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_t lda,
+                         const int32_t *a_rows, const uint8_t *w1_codes,
+                         const uint8_t *w1_scales, const uint8_t *w2_codes,
+                         const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
+                         int max_rows, int N, int K, int block_size, int w_layout, int act,
+                         void *out, int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
+                         moe_stream_t stream)
+{
+    int rc = check_gemm(a_codes, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
+                        num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
+                        ldo);
+    if (rc) return rc;
+    if (max_rows == 0) return MOE_OK;
+    CHECK(a_scales && lda % 32 == 0, MOE_ERR_INVALID_ARG);
+    rc = check_ws(ws, ws_bytes, mx8_gemm_ws_bytes(num_local, max_rows));
+    if (rc) return rc;
+    HIP_TRY(launch_grouped_gemm_mx8(a_codes, a_scales, lda, a_rows, w1_codes, w1_scales,
+                                    w2_codes, w2_scales, expert_offsets, num_local, max_rows, N,
+                                    K, act, out, out_dtype == MOE_DT_F32, ldo, ws,
+                                    w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
     return MOE_OK;
 }
 
@@ -403,6 +459,31 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);
+    if (p->precision == MOE_PREC_MX8) {
+        const GemmPlanArgs pm = mx8_plan_args(p->num_local, A, base + L.gws);
+        HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm,
+                               inv, base + L.pws, s, &pm));
+        uint8_t *xq = (uint8_t *)(base + L.xq), *xs = (uint8_t *)(base + L.xs);
+        uint8_t *hq = (uint8_t *)(base + L.hq), *hs = (uint8_t *)(base + L.hs);
+        float *h32 = (float *)(base + L.h);
+        if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+        // gate/up stage: the tokens to MXFP8, then the projection with act
+        HIP_TRY(launch_mxfp8_quantize(x, 0, p->d, p->T, p->d, xq, xs, s));
+        HIP_TRY(launch_gemm_mx8_run(xq, xs, p->d, perm, gate_codes, gate_scales, up_codes,
+                                    up_scales, p->num_local, A, p->I, p->d, p->act, h32, 1, p->I,
+                                    base + L.gws, packed, s));
+        if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+        // down stage: h to MXFP8, then the projection
+        HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s));
+        HIP_TRY(launch_gemm_mx8_run(hq, hs, p->I, nullptr, down_codes, down_scales, nullptr,
+                                    nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1,
+                                    p->d, base + L.gws, packed, s));
+        if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+        HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                               p->out_dtype == MOE_DT_F32, p->d, s));
+        if (ev) HIP_TRY(hipEventRecord(ev[5], s));
+        return MOE_OK;
+    }
     HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm, inv,
                            base + L.pws, s, &plan));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));

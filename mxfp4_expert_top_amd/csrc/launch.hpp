@@ -103,6 +103,24 @@ int resolve_mode(int mode, int num_local, int max_rows);
 hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,
                                 bf16 *out, hipStream_t s);
 
+// mx8.hip: the block-scaled precision mode (MXFP8 activations x MXFP4
+// weights on v_mfma_scale_f32_32x32x64_f8f6f4)
+hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
+                                 uint8_t *codes, uint8_t *scales, hipStream_t s);
+size_t mx8_gemm_ws_bytes(int num_local, int max_rows);
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, void *ws);
+// A: codes [rows][lda] bytes, scales [rows][lda / 32]
+hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                               const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                               const uint8_t *w2c, const uint8_t *w2s, int num_local,
+                               int max_rows, int N, int K, int act, void *out, int out_f32,
+                               int64_t ldo, void *plan_ws, int packed, hipStream_t s);
+hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                                   const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                                   const uint8_t *w2c, const uint8_t *w2s, const int32_t *off,
+                                   int num_local, int max_rows, int N, int K, int act, void *out,
+                                   int out_f32, int64_t ldo, void *ws, int packed, hipStream_t s);
+
 // prepack.hip: the streaming weight layout (see prepack.hip) and the fp32 ->
 // MXFP4 quantiser (canonical layout out)
 hipError_t launch_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes,

@@ -1,0 +1,440 @@
+// The block-scaled precision mode (MX8): activations as MXFP8 (E4M3 elements,
+// one E8M0 scale per 32) against MXFP4 weights on the gfx950 block-scaled
+// matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4, which takes both
+// operands and both scale sets as stored and runs at the 8-bit rate, twice
+// the bf16 one, with no decode instructions.
+//
+// The formats are OCP Microscaling (MX) v1.0; the pages' layer (P1 section
+// 二, 第一层: 4-bit weights meet higher-precision activations in hardware
+// matrix kernels; P2 "MXFP4 原生支持": dequantisation fused into the GEMM)
+// keeps bf16 activations, so MX8 is a separate accuracy contract: tokens and
+// h are rounded to E4M3 before each projection.
+//
+//   mxfp8_quantize_kernel  bf16 or fp32 rows -> MXFP8 (codes [N][K], scales
+//                          [N][K/32]); one thread per 32-element block
+//   gemm_mx8_kernel        grouped projection, 256 x 256 tiles, MXFP8 rows x
+//                          MXFP4 weights, fp32 accumulation
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// fp32 -> MXFP8. Per block: s = clamp(floor(log2 amax) - 8 + 127, 0, 254)
+// (8 = emax of E4M3), q = v * 2^(127 - s) (exact), E4M3 code of q rounded to
+// nearest-even with magnitudes from 448 up clamped to 448 (0x7E); an all-zero
+// block gets scale 0 and codes 0; the sign bit comes from q, so -0 and
+// negatives rounding to zero give 0x80.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code(float q)
+{
+    const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+    const float a = fabsf(q);
+    uint32_t mag;
+    if (a >= 448.0f) {
+        mag = 0x7Eu;
+    } else if (a < 0.015625f) {
+        // below 2^-6 the grid is k * 2^-9, k = 0..8 (k = 8 is the smallest
+        // normal, whose code is also 8); the scaling is exact
+        mag = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        // round the 23-bit fp32 mantissa to 3 bits, nearest-even; a carry
+        // moves into the exponent field
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        mag = ((((b >> 23) & 0xFFu) - 127u + 7u) << 3) | ((b >> 20) & 7u);
+    }
+    return sign | mag;
+}
+
+template <typename InT>
+__device__ __forceinline__ void load32(const InT *p, float v[32]);
+template <>
+__device__ __forceinline__ void load32<float>(const float *p, float v[32])
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float4 t = ((const float4 *)p)[j];
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+}
+template <>
+__device__ __forceinline__ void load32<bf16>(const bf16 *p, float v[32])
+{
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const bf16x8 t = ((const bf16x8 *)p)[j];
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[8 * j + i] = (float)t[i];
+    }
+}
+
+template <typename InT>
+__global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const InT *__restrict__ v,
+                                                             int64_t ldv, int64_t N, int K,
+                                                             uint8_t *__restrict__ codes,
+                                                             uint8_t *__restrict__ scales)
+{
+    const int nb = K / 32;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N * nb) return;
+    const int64_t n = i / nb;
+    const int b = (int)(i - n * nb);
+    float x[32];
+    load32<InT>(v + n * ldv + 32 * b, x);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(x[j]));
+    const uint32_t u = __float_as_uint(amax);
+    const int ex = (int)((u >> 23) & 0xffu);
+    // floor(log2 amax); an fp32 subnormal amax is below 2^-126 and clamps to 0
+    const int s = (amax == 0.0f || ex == 0) ? 0 : min(254, max(0, ex - 127 - 8 + 127));
+    // 2^(127 - s): s <= 246 for finite input, so the exponent field is >= 8
+    const float inv = __uint_as_float((uint32_t)(254 - s) << 23);
+    uint8_t *c = codes + n * (int64_t)K + 32 * b;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        u32x4 w;
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++) word |= e4m3_code(x[16 * h + 4 * d + j] * inv) << (8 * j);
+            w[d] = amax == 0.0f ? 0u : word;
+        }
+        *(u32x4 *)(c + 16 * h) = w;
+    }
+    scales[n * nb + b] = (uint8_t)s;
+}
+
+hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
+                                 uint8_t *codes, uint8_t *scales, hipStream_t s)
+{
+    const int64_t nb = N * (K / 32);
+    if (nb <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+    if (v_f32)
+        hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, block, 0, s, (const float *)v, ldv,
+                           N, K, codes, scales);
+    else
+        hipLaunchKernelGGL(mxfp8_quantize_kernel<bf16>, grid, block, 0, s, (const bf16 *)v, ldv,
+                           N, K, codes, scales);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped projection on the block-scaled matrix cores.
+//
+// Workgroup tile: 256 permuted rows of one expert x 256 weight rows, K step
+// 64 (two MX blocks). 8 waves as 4 row quarters x 2 weight halves; quarter q
+// owns row tiles q and q + 4 of 32 (those holding rows of the group), each
+// against the 4 weight tiles of 32 of its half; one 32 x 32 x 64 MFMA per
+// (row tile, weight tile) per K step. A GLU tile holds 128 W1 rows and the
+// same 128 W2 rows (weight half ch: rows 64 ch .. 64 ch + 63 of each), so
+// act(gate, up) is applied in registers.
+//
+// Operands, as the instruction takes them (lane L, l = L % 32, g = L / 32):
+//   B (E2M1, 16 bytes): weight row l, K 32 g .. 32 g + 31 of the step, i.e.
+//     MX block g, exactly the 16 stored code bytes (low nibble = even K);
+//   A (E4M3, 32 bytes): row l, K 16 g .. 16 g + 15 in bytes 0-15 and
+//     32 + 16 g .. 32 + 16 g + 15 in bytes 16-31;
+//   scales: lane L gives the E8M0 scale of its row (A) or weight row (B)
+//     for MX block g of the step.
+// A rows sit in LDS at an 80-byte stride (64 code bytes + 16), so the 16
+// lanes of a 16-byte read land on distinct banks; weights stay 4-bit in LDS.
+//
+// Pipeline: two LDS stages and two register stages, global loads two K steps
+// ahead (the last steps repeat step nk - 1), one barrier per K step.
+// ---------------------------------------------------------------------------
+constexpr int M8_BM = 256, M8_BN = 256, M8_BK = 64, M8_THREADS = 512, M8_ALD = 80;
+
+template <int ACT, typename OutT, bool PACKED>
+__global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t lda,
+    const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
+    const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
+    const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
+    __shared__ __attribute__((aligned(16))) uint8_t Aq[2][M8_BM][M8_ALD];
+    __shared__ uint8_t Asc[2][M8_BM][2];
+    __shared__ __attribute__((aligned(16))) uint8_t Bq[2][M8_BN][M8_BK / 2];
+    __shared__ uint8_t Bsc[2][M8_BN][2];
+
+    const int nblk = (N + COLS - 1) / COLS;
+    const int total = plan[0] * nblk;
+    // XCD-aware order: each XCD takes a contiguous run of work items, so the
+    // column blocks of one row group share an L2
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int wi = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || wi >= total) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int2 it = ((const int2 *)(plan + hdr))[grp];
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
+    const int mrows = rend - r0;
+    const int n0 = nb * COLS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ch = wave & 1, q = wave >> 1;
+
+    // ---- global -> LDS assignment
+    // A codes: 16-byte chunks c = tid and tid + 512 of the 256 x 64-byte
+    // step, row c / 4, bytes 16 (c % 4); A scales: row tid / 2, block tid % 2
+    const int64_t lds_ = lda / 32;
+    const uint8_t *ag[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int c = tid + 512 * j;
+        const int rc = min(r0 + (c >> 2), rend - 1);
+        const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+        ag[j] = ac + arow * lda + 16 * (c & 3);
+    }
+    const uint8_t *asg;
+    {
+        const int rc = min(r0 + (tid >> 1), rend - 1);
+        const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+        asg = as + arow * lds_ + (tid & 1);
+    }
+    // B: weight row tid / 2 of the tile, MX block tid % 2 of the step
+    const int br = tid >> 1, bh = tid & 1;
+    int wrow;
+    const uint8_t *wcb, *wsb;
+    if (GLU) {
+        wrow = min(n0 + (br & 127), N - 1);
+        wcb = br < 128 ? w1c : w2c;
+        wsb = br < 128 ? w1s : w2s;
+    } else {
+        wrow = min(n0 + br, N - 1);
+        wcb = w1c;
+        wsb = w1s;
+    }
+    const int64_t wr64 = (int64_t)e * N + wrow;
+    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const uint8_t *bg, *sg;
+    if constexpr (PACKED) {
+        const int64_t rb = wr64 / 16;
+        const int mm = (int)(wr64 % 16);
+        bg = wcb + rb * nch * 1024 + mm * 16;
+        sg = wsb + rb * nc4 * 256 + mm * 4;
+    } else {
+        bg = wcb + wr64 * (K / 2) + 16 * bh;
+        sg = wsb + wr64 * (K / 32) + bh;
+    }
+
+    u32x4 ra0[2], ra1[2], rb0, rb1;
+    uint8_t rsa0, rsa1, rsb0, rsb1;
+    auto gload = [&](u32x4 *ra, uint8_t &rsa, u32x4 &rbv, uint8_t &rsb, int kt) {
+        const int k0 = kt * M8_BK;
+#pragma unroll
+        for (int j = 0; j < 2; j++) ra[j] = *(const u32x4 *)(ag[j] + k0);
+        rsa = asg[k0 / 32];
+        if constexpr (PACKED) {
+            const int c = kt >> 1, gg = 2 * (kt & 1) + bh;
+            rbv = *(const u32x4 *)(bg + c * 1024 + gg * 256);
+            rsb = sg[(c >> 2) * 256 + gg * 64 + (c & 3)];
+        } else {
+            rbv = *(const u32x4 *)(bg + k0 / 2);
+            rsb = sg[k0 / 32];
+        }
+    };
+    auto lstore = [&](int st, const u32x4 *ra, uint8_t rsa, const u32x4 &rbv, uint8_t rsb) {
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int c = tid + 512 * j;
+            *(u32x4 *)(&Aq[st][c >> 2][16 * (c & 3)]) = ra[j];
+        }
+        Asc[st][tid >> 1][tid & 1] = rsa;
+        *(u32x4 *)(&Bq[st][br][16 * bh]) = rbv;
+        Bsc[st][br][bh] = rsb;
+    };
+
+    // ---- wave tiles
+    const int g = lane >> 5, l32 = lane & 31;
+    int bt[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        if (GLU) bt[j] = (j >= 2 ? 128 : 0) + 64 * ch + 32 * (j & 1);  // W1 x2, then W2 x2
+        else bt[j] = 128 * ch + 32 * j;
+    }
+    const int n_on = (32 * q < mrows ? 1 : 0) + (128 + 32 * q < mrows ? 1 : 0);
+    const int nk = K / M8_BK;  // even: K is a multiple of 128
+
+    auto run = [&](auto ni_c) {
+        constexpr int NI = decltype(ni_c)::value;
+        f32x16 acc[NI > 0 ? NI : 1][4];
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+        auto compute = [&](int st) {
+            if constexpr (NI > 0) {
+                i32x8 bv[4];
+                int sb[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int row = bt[j] + l32;
+                    const u32x4 w = *(const u32x4 *)(&Bq[st][row][16 * g]);
+                    bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+                    sb[j] = Bsc[st][row][g];
+                }
+#pragma unroll
+                for (int i = 0; i < NI; i++) {
+                    const int row = 32 * q + 128 * i + l32;
+                    const u32x4 lo = *(const u32x4 *)(&Aq[st][row][16 * g]);
+                    const u32x4 hi = *(const u32x4 *)(&Aq[st][row][32 + 16 * g]);
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    const int sa = Asc[st][row][g];
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        // A format 0: E4M3; B format 4: E2M1; scale byte 0 of each
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av, bv[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+                }
+            }
+        };
+
+        gload(ra0, rsa0, rb0, rsb0, 0);
+        gload(ra1, rsa1, rb1, rsb1, 1);
+        lstore(0, ra0, rsa0, rb0, rsb0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            // stage 0 holds step kt; registers set 1 hold step kt + 1
+            gload(ra0, rsa0, rb0, rsb0, min(kt + 2, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+            compute(0);
+            lstore(1, ra1, rsa1, rb1, rsb1);
+            __syncthreads();
+            // stage 1 holds step kt + 1; registers set 0 hold step kt + 2
+            gload(ra1, rsa1, rb1, rsb1, min(kt + 3, nk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            compute(1);
+            lstore(0, ra0, rsa0, rb0, rsb0);  // past the end: a copy of the last step, unused
+            __syncthreads();
+        }
+
+        // epilogue: lane holds C[8 (v / 4) + 4 g + v % 4][l32] of each tile
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int rl = 32 * q + 128 * i + 8 * (v >> 2) + 4 * g + (v & 3);
+                if (rl >= mrows) continue;
+                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                if constexpr (GLU) {
+#pragma unroll
+                    for (int jj = 0; jj < 2; jj++) {
+                        const int col = n0 + 64 * ch + 32 * jj + l32;
+                        if (col < N)
+                            store_out<OutT>(orow + col,
+                                            act_apply<ACT>(acc[i][jj][v], acc[i][2 + jj][v]));
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const int col = n0 + 128 * ch + 32 * j + l32;
+                        if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                    }
+                }
+            }
+        }
+    };
+    // every branch runs the same barriers (1 + nk)
+    switch (__builtin_amdgcn_readfirstlane(n_on)) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+    }
+}
+
+template <int ACT, typename OutT, bool PACKED>
+static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                             const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                             const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa,
+                             int N, int K, OutT *out, int64_t ldo, hipStream_t s)
+{
+    constexpr int COLS = ACT != ACT_NONE ? M8_BN / 2 : M8_BN;
+    const int64_t grid = (int64_t)pa.max_groups * ((N + COLS - 1) / COLS);
+    if (grid <= 0) return hipSuccess;
+    // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
+    // a grid of 8 * ceil(bound / 8) blocks covers every work item
+    const int64_t G = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(M8_THREADS),
+                       0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out,
+                       ldo);
+    return hipGetLastError();
+}
+
+template <typename OutT, bool PACKED>
+static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t lda,
+                          const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                          const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa, int N,
+                          int K, OutT *out, int64_t ldo, hipStream_t s)
+{
+    switch (act) {
+    case ACT_NONE:
+        return launch_mx8<ACT_NONE, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N,
+                                                  K, out, ldo, s);
+    case ACT_SILU_MUL:
+        return launch_mx8<ACT_SILU_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa,
+                                                      N, K, out, ldo, s);
+    case ACT_GELU_TANH_MUL:
+        return launch_mx8<ACT_GELU_TANH_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c,
+                                                           w2s, pa, N, K, out, ldo, s);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, void *ws)
+{
+    // the 256-row tiles take the 256-row grouping of the bf16 schedule
+    return gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws);
+}
+
+size_t mx8_gemm_ws_bytes(int num_local, int max_rows)
+{
+    return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE256);
+}
+
+hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                               const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                               const uint8_t *w2c, const uint8_t *w2s, int num_local,
+                               int max_rows, int N, int K, int act, void *out, int out_f32,
+                               int64_t ldo, void *plan_ws, int packed, hipStream_t s)
+{
+    const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, plan_ws);
+#define MX8_RUN(OT, PK) \
+    return mx8_act<OT, PK>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, (OT *)out, ldo, s)
+    if (out_f32) {
+        if (packed) MX8_RUN(float, true);
+        MX8_RUN(float, false);
+    }
+    if (packed) MX8_RUN(bf16, true);
+    MX8_RUN(bf16, false);
+#undef MX8_RUN
+}
+
+hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                                   const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                                   const uint8_t *w2c, const uint8_t *w2s, const int32_t *off,
+                                   int num_local, int max_rows, int N, int K, int act, void *out,
+                                   int out_f32, int64_t ldo, void *ws, int packed, hipStream_t s)
+{
+    hipError_t e = launch_gemm_plan_into(off, num_local, mx8_plan_args(num_local, max_rows, ws), s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_mx8_run(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
+                               K, act, out, out_f32, ldo, ws, packed, s);
+}
+
+}  // namespace moe

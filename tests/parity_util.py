@@ -48,7 +48,7 @@ def assert_close_layer(got, ref, what=""):
     return r, m
 
 
-def run_gpu_layer(inp, *, mode=0, out_dtype=torch.bfloat16, act=1, packed=None):
+def run_gpu_layer(inp, *, mode=0, out_dtype=torch.bfloat16, act=1, packed=None, precision=0):
     """The fused entry on ``inp`` (tensors already on the GPU). ``packed``: the
     weights already in the streaming layout (``inp.weights`` stay canonical).
     Returns dict of GPU tensors: out, logits, idx, w."""
@@ -56,7 +56,8 @@ def run_gpu_layer(inp, *, mode=0, out_dtype=torch.bfloat16, act=1, packed=None):
     c = inp.cfg
     p = m.layer_params(c.T, c.d, c.E, c.k, c.I, c.expert_begin, c.num_local, act=act,
                        out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16, mode=mode,
-                       weight_layout=m.LAYOUT_OCP if packed is None else m.LAYOUT_PACKED)
+                       weight_layout=m.LAYOUT_OCP if packed is None else m.LAYOUT_PACKED,
+                       precision=precision)
     dev = inp.x.device
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
     out = torch.empty(c.T, c.d, dtype=out_dtype, device=dev)
@@ -77,7 +78,7 @@ def host_weights(weights, local_ids=None):
     return out
 
 
-def oracle_rows(inp, idx, w, tokens, act=1):
+def oracle_rows(inp, idx, w, tokens, act=1, mx8=False):
     """Oracle output rows for `tokens`, given routing (idx, w) as numpy. Only
     the experts these tokens use are copied to the host."""
     c = inp.cfg
@@ -94,7 +95,7 @@ def oracle_rows(inp, idx, w, tokens, act=1):
     cidx[local] = remap[(idx - c.expert_begin)[local]]
     cidx[cidx < 0] = -1
     return oracle.token_rows(inp.x, cidx, np.asarray(w, np.float32), tokens, wts, I=c.I,
-                             e0=0, n_local=max(len(used), 1), act=act) if len(used) else \
+                             e0=0, n_local=max(len(used), 1), act=act, mx8=mx8) if len(used) else \
         np.zeros((len(tokens), c.d), np.float32)
 
 

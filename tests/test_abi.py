@@ -168,6 +168,43 @@ def test_layer_params_and_workspace():
     assert m.lib.moe_layer(C.byref(p0), *([None] * 14), 0, None, None) == 0
 
 
+def test_mx8_validation():
+    L = m.lib
+    # quantiser: K % 32, dtype, stride, alignment; empty input is a no-op
+    assert L.moe_mxfp8_quantize(FAKE, 0, 64, 4, 48, FAKE, FAKE, None) == 2
+    assert L.moe_mxfp8_quantize(FAKE, 2, 64, 4, 64, FAKE, FAKE, None) == 1
+    assert L.moe_mxfp8_quantize(FAKE, 0, 60, 4, 64, FAKE, FAKE, None) == 1   # ldv < K
+    assert L.moe_mxfp8_quantize(FAKE, 0, 68, 4, 64, FAKE, FAKE, None) == 1   # ldv % 8
+    assert L.moe_mxfp8_quantize(C.c_void_p(0x10004), 0, 64, 4, 64, FAKE, FAKE, None) == 1
+    assert L.moe_mxfp8_quantize(FAKE, 0, 64, 4, 64, None, FAKE, None) == 1
+    assert L.moe_mxfp8_quantize(None, 0, 64, 0, 64, None, None, None) == 0
+    # grouped GEMM: the bf16 checks plus the scale stride (lda % 32) and scales
+    need = m.moe_grouped_gemm_mx8_workspace_size(8, 64)
+    assert need > 0 and m.moe_grouped_gemm_mx8_workspace_size(0, 64) == 0
+
+    def gemm(**kw):
+        a = dict(ac=FAKE, asc=FAKE, lda=256, rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE,
+                 off=FAKE, nl=8, maxr=64, N=128, K=256, bs=32, lay=0, act=1, out=FAKE, odt=1,
+                 ldo=128, ws=FAKE, wsb=need)
+        a.update(kw)
+        return L.moe_grouped_gemm_mx8(*a.values(), None)
+    assert gemm(bs=64) == 2
+    assert gemm(K=96, lda=96) == 2
+    assert gemm(lda=264) == 1                 # scale stride lda / 32 not whole
+    assert gemm(asc=None) == 1
+    assert gemm(w2c=None, w2s=None) == 1
+    assert gemm(wsb=need - 1) == 3
+    assert gemm(maxr=0, ac=None, asc=None, out=None, ws=None, wsb=0) == 0
+    # the layer's precision field
+    p = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8)
+    n_mx8 = m.moe_layer_workspace_size(p)
+    n_bf16 = m.moe_layer_workspace_size(m.layer_params(8, 3584, 896, 16, 128))
+    # fp32 h plus MXFP8 tokens and h
+    assert n_mx8 >= n_bf16 + 8 * 16 * 128 * 2 + 8 * 3584
+    bad = m.layer_params(8, 3584, 896, 16, 128, precision=2)
+    assert L.moe_layer_workspace_size(C.byref(bad)) == 0
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.bfloat16)

@@ -1,0 +1,221 @@
+"""GPU parity of the block-scaled precision mode (MX8: MXFP8 tokens and h,
+MXFP4 weights, v_mfma_scale_f32_32x32x64_f8f6f4) against the oracle's MX8
+definition.
+
+Stage by stage: the quantiser byte for byte; the grouped projection
+elementwise against the exact sum of exactly decoded operands, within the
+instruction's summation bound; the layer against the oracle's MX8 layer on
+the GPU's routing. The bound of the projection comes from the instruction:
+its products are exact and a one-wave measurement of its 64-long sums put
+them within 1.1e-4 of sum|products| (about 13 bits); fp32 accumulation over
+K/64 of them adds at most K/64 * 2^-24 of sum|products|. The tests allow
+2e-4 * sum|a w|."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, LayerConfig, make_inputs, quantize_mxfp4
+from tests.parity_util import (assert_close_layer, host_weights, np_, oracle_rows, rel_l2,
+                               run_gpu_layer)
+from tests.test_oracle_mx8 import _blocks
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MMA_TOL = 2e-4
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mxfp4_expert_top_amd as mod
+    return mod
+
+
+# ---------------------------------------------------------------- quantiser
+@pytest.mark.parametrize("K", [32, 128, 3584])
+def test_mxfp8_quantize_fp32_bitexact(m, K):
+    v = _blocks().reshape(-1)
+    v = np.resize(v, ((v.size + K - 1) // K) * K).reshape(-1, K).astype(np.float32)
+    rnd = np.random.default_rng(K).standard_normal((7, K)).astype(np.float32)
+    v = np.ascontiguousarray(np.concatenate([v, rnd * 3.0, rnd * 1e-30]))
+    c, s = m.moe_mxfp8_quantize(torch.from_numpy(v).to(DEV))
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp8_quantize(v)
+    assert np.array_equal(np_(s), rs)
+    assert np.array_equal(np_(c), rc), np.argwhere(np_(c) != rc)[:5]
+
+
+def test_mxfp8_quantize_bf16_rows_with_stride(m):
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((33, 3584 + 64)).astype(np.float32)).to(torch.bfloat16)
+    x[3, :64] = 0
+    x[4] *= 1e-20
+    xv = x[:, :3584]
+    c, s = m.moe_mxfp8_quantize(x.to(DEV)[:, :3584])  # rows of 3584 at a stride of 3648
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp8_quantize(xv.float().numpy())
+    assert np.array_equal(np_(s), rs) and np.array_equal(np_(c), rc)
+
+
+# ---------------------------------------------------------------- projection
+def _experts(num_local, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    cs = [quantize_mxfp4(torch.randn(N, K, generator=g) / np.sqrt(K)) for _ in range(num_local)]
+    return torch.stack([c for c, _ in cs]), torch.stack([s for _, s in cs])
+
+
+def _mx8_rows(rng, R, K):
+    v = (rng.standard_normal((R, K)) * np.exp2(rng.integers(-3, 4, (R, 1)))).astype(np.float32)
+    return oracle.mxfp8_quantize(v)
+
+
+def _bound(a, w):
+    """sum_k |a_k w_k| for every (row, weight row)."""
+    return np.abs(a) @ np.abs(w).T
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("K", [128, 640])
+def test_grouped_gemm_mx8_vs_definition(m, act, packed, K):
+    """Experts with 0, 1, 37, 150, 257 and 513 rows (empty, one row, ragged,
+    several 256-row groups), a column count that is not a tile multiple,
+    gathered rows, fp32 output."""
+    rng = np.random.default_rng(K + 3 * act + 7 * packed)
+    nl, N, T = 6, 320, 700
+    counts = np.array([37, 0, 513, 1, 257, 150], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    xc, xs = _mx8_rows(rng, T, K)
+    a_rows = rng.integers(0, T, size=A).astype(np.int32)
+    w1c, w1s = _experts(nl, N, K, 3)
+    w2c, w2s = _experts(nl, N, K, 4) if act else (None, None)
+    dev = lambda t: None if t is None else t.to(DEV)
+    pk = lambda c, s: m.moe_mxfp4_prepack(dev(c), dev(s)) if packed else (dev(c), dev(s))
+    g1c, g1s = pk(w1c, w1s)
+    g2c, g2s = pk(w2c, w2s) if act else (None, None)
+    out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
+    m.moe_grouped_gemm_mx8(torch.from_numpy(xc).to(DEV), torch.from_numpy(xs).to(DEV),
+                           torch.from_numpy(a_rows).to(DEV), g1c, g1s, g2c, g2s,
+                           torch.from_numpy(off).to(DEV), A, act, out, ws,
+                           w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
+    torch.cuda.synchronize()
+    got = np_(out).astype(np.float64)
+    assert (got[A:] == 7.0).all()
+    xa = oracle.mxfp8_decode(xc, xs).astype(np.float64)[a_rows]
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        if r0 == r1:
+            continue
+        w1 = oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64)
+        g = xa[r0:r1] @ w1.T
+        bg = MMA_TOL * _bound(xa[r0:r1], w1)
+        if act == 0:
+            assert (np.abs(got[r0:r1] - g) <= bg).all(), np.abs(got[r0:r1] - g).max()
+        else:
+            w2 = oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64)
+            u = xa[r0:r1] @ w2.T
+            bu = MMA_TOL * _bound(xa[r0:r1], w2)
+            sg = 1.0 / (1.0 + np.exp(-g))
+            h = g * sg * u
+            # first-order propagation: |d silu/dg| <= 1.1, |silu(g)| <= |g| + 0.28
+            tol = 1.1 * np.abs(u) * bg + (np.abs(g) + 0.28) * bu + 1e-5 * np.abs(h) + 1e-30
+            assert (np.abs(got[r0:r1] - h) <= tol).all(), np.abs(got[r0:r1] - h).max()
+
+
+def test_grouped_gemm_mx8_bf16_out_and_direct_rows(m):
+    """No gathered rows (a_rows NULL), bf16 output, the down-projection shape
+    (K = 1024, N = 3584 not a tile multiple of 256)."""
+    rng = np.random.default_rng(9)
+    nl, N, K = 3, 3584, 1024
+    counts = np.array([200, 3, 70], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    hc, hs = _mx8_rows(rng, A, K)
+    wc, wsc = _experts(nl, N, K, 8)
+    out = torch.empty(A, N, dtype=torch.bfloat16, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
+    m.moe_grouped_gemm_mx8(torch.from_numpy(hc).to(DEV), torch.from_numpy(hs).to(DEV), None,
+                           wc.to(DEV), wsc.to(DEV), None, None, torch.from_numpy(off).to(DEV),
+                           A, 0, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ha = oracle.mxfp8_decode(hc, hs).astype(np.float64)
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        w = oracle.mxfp4_decode(wc[e].numpy(), wsc[e].numpy()).astype(np.float64)
+        ref = ha[r0:r1] @ w.T
+        # bf16 rounding of a value within the summation bound of the exact sum
+        err = np.abs(got[r0:r1] - ref)
+        assert (err <= 2.0 ** -8 * (np.abs(ref) + MMA_TOL * _bound(ha[r0:r1], w))
+                + MMA_TOL * _bound(ha[r0:r1], w)).all()
+
+
+# ---------------------------------------------------------------- layer
+SMALL = [
+    LayerConfig("x0", T=37, I=128, d=256, E=64, k=8),
+    LayerConfig("x1", T=300, I=256, d=384, E=16, k=4),
+    LayerConfig("x2", T=50, I=128, d=256, E=40, k=6, expert_begin=8, num_local=20, bias="normal"),
+    LayerConfig("x3", T=700, I=128, d=256, E=100, k=6, bias="normal"),
+]
+
+
+def _routing(inp, g):
+    c = inp.cfg
+    lg = np_(g["logits"])
+    r_idx, r_w = oracle.topk_softmax(lg, c.k)
+    assert np.array_equal(np_(g["idx"]), r_idx)
+    return lg, r_idx, r_w
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("packed", [False, True])
+def test_small_layer_mx8_vs_oracle(m, cfg, packed):
+    """The whole MX8 layer against the oracle's MX8 layer on the GPU's scores.
+    Both round h to E4M3 from fp32 values that differ by the instruction's
+    summation error, so a few h codes may sit one E4M3 step apart; the layer
+    bounds (rel-L2 1e-2, max-abs 3e-2 rms) cover that. The routing is the
+    bf16 path's, bit for bit."""
+    inp = make_inputs(cfg).to(DEV)
+    g = run_gpu_layer(inp, precision=m.PREC_MX8,
+                      packed=m.prepack_weights(inp.weights) if packed else None)
+    lg, _, _ = _routing(inp, g)
+    ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                       host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                       e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg, mx8=True)
+    got = g["out"].float().cpu().numpy()
+    assert_close_layer(got, ref["out"], cfg.name)
+    # the bf16-activation layer differs by the activation rounding (E4M3 steps
+    # are 2^-3 of the value): far more than the parity gap above
+    ref16 = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                         host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                         e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg)
+    assert rel_l2(got, ref16["out"]) > 2 * rel_l2(got, ref["out"])
+
+
+def test_mx8_layer_determinism_bitwise(m):
+    inp = make_inputs(SMALL[1]).to(DEV)
+    a = run_gpu_layer(inp, precision=m.PREC_MX8)
+    b = run_gpu_layer(inp, precision=m.PREC_MX8)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_full_size_mx8(m, name):
+    """The prefill workload (and the decode batch) in the MX8 mode, in the
+    benchmark's launch configuration: sampled tokens' rows against the
+    oracle's MX8 rows on the GPU's routing."""
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, DEV)
+    g = run_gpu_layer(inp, precision=m.PREC_MX8, packed=m.prepack_weights(inp.weights))
+    _, r_idx, _ = _routing(inp, g)
+    rng = np.random.default_rng(1)
+    toks = sorted(set(rng.choice(cfg.T, size=min(5, cfg.T), replace=False).tolist())
+                  | {0, cfg.T - 1})
+    ref = oracle_rows(inp, r_idx, np_(g["w"]), toks, mx8=True)
+    assert_close_layer(g["out"].float().cpu().numpy()[toks], ref, name)
+    del inp, g
+    torch.cuda.empty_cache()
