@@ -27,6 +27,7 @@ METRIC = "MoE-layer tokens/s + % of MFMA/HBM roofline, 896 experts top-16 MXFP4"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 matrix
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix (the fp8 x fp4 block-scaled rate)
 STAGES = ("route", "permute", "gate_up", "down", "combine")
 
 
@@ -39,6 +40,10 @@ def parse():
     ap.add_argument("--mode", type=int, default=0,
                     help="GEMM schedule (enum moe_sched): 0 auto, 1 stream, 2 tiled, "
                          "3 128-row tiles, 4 256-row tiles")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "mx8"],
+                    help="bf16: bf16 tokens and h against MXFP4 weights (the pages' layer); "
+                         "mx8: tokens and h rounded to MXFP8 for the block-scaled fp8 x fp4 "
+                         "matrix instruction (a separate accuracy contract)")
     ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens the oracle CPU baseline evaluates (0 = skip)")
     ap.add_argument("--weights", default="packed", choices=["packed", "ocp"],
@@ -66,7 +71,7 @@ def algorithmic(cfg, A, U, out_bytes=2):
     return layer_bytes, layer_flops, gu_bytes, gu_flops
 
 
-def cpu_baseline(inp, n_tokens):
+def cpu_baseline(inp, n_tokens, mx8=False):
     """The oracle, as it stands, on `n_tokens` seeded tokens of the same
     workload: router scores, top-k, softmax and every selected expert's FFN
     and the weighted combine of each token. Single-threaded."""
@@ -96,12 +101,13 @@ def cpu_baseline(inp, n_tokens):
     ok = (loc >= 0) & (loc < cfg.num_local)
     cidx[ok] = remap[loc[ok]]
     oracle.token_rows(xs, cidx, w, np.arange(len(toks)), wts, I=cfg.I, e0=0,
-                      n_local=max(len(used), 1))
+                      n_local=max(len(used), 1), mx8=mx8)
     dt = time.perf_counter() - t0
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} tokens of the same workload, whole layer per "
                       f"token (router scores over {cfg.E} experts, top-{cfg.k}, softmax, "
-                      f"{cfg.k} MXFP4 expert FFNs with I={cfg.I}, weighted combine), "
+                      f"{cfg.k} MXFP4 expert FFNs with I={cfg.I}"
+                      f"{' on MXFP8 tokens and h' if mx8 else ''}, weighted combine), "
                       f"single-threaded fp32 C; {dt:.1f} s"}
 
 
@@ -189,6 +195,7 @@ def main():
     dev = "cuda:0"
     inp = make_inputs(cfg, dev)
     packed = args.weights == "packed"
+    mx8 = args.precision == "mx8"
     canonical = inp.weights  # the oracle reads the canonical layout
     if packed:  # the load-time conversion, outside the timed region
         layer_weights = m.prepack_weights(inp.weights)
@@ -197,7 +204,8 @@ def main():
         layer_weights = inp.weights
     p = m.layer_params(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.expert_begin, cfg.num_local,
                        mode=args.mode,
-                       weight_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
+                       weight_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP,
+                       precision=m.PREC_MX8 if mx8 else m.PREC_BF16)
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
     out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
@@ -252,7 +260,14 @@ def main():
     # bound) for few rows per expert, a tiled bf16 GEMM (MFMA bound) otherwise.
     gu_s = stage_ms["gate_up"] / 1e3
     sched = m.moe_grouped_gemm_schedule(cfg.num_local, cfg.T * cfg.k, args.mode)
-    if sched == m.MODE_STREAM:
+    if mx8:
+        # the stage is the token quantiser plus the block-scaled GEMM
+        roof = {"kernel": "mxfp8_quantize_kernel + gemm_mx8_kernel<SILU_MUL> (gate/up stage)",
+                "bound": "mfma", "achieved": round(gf / gu_s / 1e12, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+                "traffic": None, "algorithmic_flops_per_launch": int(gf),
+                "avg_launch_ms": round(stage_ms["gate_up"], 4)}
+    elif sched == m.MODE_STREAM:
         roof = {"kernel": "gemm_stream_kernel<SILU_MUL> (gate/up projection)", "bound": "hbm",
                 "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
@@ -277,17 +292,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8" if mx8 else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "experts_computed": cfg.num_local,
                    "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
-                   "activations": "bf16", "routing_bias": cfg.bias},
+                   "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else "bf16",
+                   "routing_bias": cfg.bias},
         "roofline": roof,
         "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),
                   "algorithmic_bytes": int(lb), "algorithmic_flops": int(lf),
                   "hbm_frac": round(lb / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                   "bf16_mfma_frac": round(lf / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                  "fp8_mfma_frac": round(lf / (ms_step / 1e3) / 1e12 / FP8_PEAK_TFLOPS, 5),
                   "mxfp4_mfma_frac": round(lf / (ms_step / 1e3) / 1e12 / MXFP4_PEAK_TFLOPS, 5),
                   "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
                   "ms_per_step_with_stage_events": round(ms_step_staged, 4)},
@@ -295,7 +312,7 @@ def main():
     }
     if args.cpu_tokens > 0:
         inp.weights = canonical
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens, mx8=mx8)
     print(json.dumps(res), flush=True)
 
 
