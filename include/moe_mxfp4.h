@@ -65,7 +65,7 @@ enum moe_status {
     MOE_ERR_HIP = 4          /* a HIP runtime call or launch failed              */
 };
 
-enum moe_dtype { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 };
+enum moe_dtype { MOE_DT_BF16 = 0, MOE_DT_F32 = 1, MOE_DT_MXFP8 = 2 /* moe_grouped_gemm_mx8 output only */ };
 
 /* Elementwise stage between the two expert projections. P1 (section 一)
  * names a K3-specific activation path without defining it, so the stage is
@@ -261,18 +261,22 @@ int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K
  *             lda + k]) * 2^(a_scales[r * (lda/32) + k/32] - 127)
  * on v_mfma_scale_f32_32x32x64_f8f6f4 (exact products; each 64-long partial
  * sum is formed inside the instruction, then accumulated in fp32); out as in
- * moe_grouped_gemm_mxfp4. 256-row tiles only; ws holds
+ * moe_grouped_gemm_mxfp4, or with out_dtype MOE_DT_MXFP8 the fp32 results
+ * converted as moe_mxfp8_quantize does (blocks of 32 along N): codes to out
+ * [rows][ldo] (bytes), scales to out_scales [rows][ldo/32] (NULL for the
+ * other dtypes). 256-row tiles only; ws holds
  * moe_grouped_gemm_mx8_workspace_size(...) bytes.
- * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0; 16-byte
- * aligned code and scale arrays. Errors as moe_grouped_gemm_mxfp4. */
+ * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0 (% 32 for
+ * MXFP8 output); 16-byte aligned code and scale arrays. Errors as
+ * moe_grouped_gemm_mxfp4. */
 size_t moe_grouped_gemm_mx8_workspace_size(int num_local, int max_rows);
 int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_t lda,
                          const int32_t *a_rows, const uint8_t *w1_codes,
                          const uint8_t *w1_scales, const uint8_t *w2_codes,
                          const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
                          int max_rows, int N, int K, int block_size, int w_layout, int act,
-                         void *out, int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
-                         moe_stream_t stream);
+                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, void *ws,
+                         size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- weighted unpermute (P3 section 四, combine: results come back

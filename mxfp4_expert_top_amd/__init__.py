@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mxfp4.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-DT_BF16, DT_F32 = 0, 1
+DT_BF16, DT_F32, DT_MXFP8 = 0, 1, 2
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
 MODE_AUTO, MODE_STREAM, MODE_TILED, MODE_TILE128, MODE_TILE256 = 0, 1, 2, 3, 4
 LAYOUT_OCP, LAYOUT_PACKED = 0, 1
@@ -77,7 +77,7 @@ def _load(path=None):
     L.moe_grouped_gemm_mx8_workspace_size.argtypes = [i32, i32]
     L.moe_grouped_gemm_mx8.restype = i32
     L.moe_grouped_gemm_mx8.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
-                                       i32, p, i32, i64, p, sz, p]
+                                       i32, p, i32, p, i64, p, sz, p]
     return L
 
 
@@ -328,9 +328,11 @@ def moe_grouped_gemm_mx8_workspace_size(num_local, max_rows):
 
 def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
                          expert_offsets, max_rows, act, out, ws, w_layout=LAYOUT_OCP,
-                         stream=None):
+                         out_scales=None, stream=None):
     """moe_grouped_gemm_mxfp4 with MXFP8 rows (a_codes uint8 [rows, K] E4M3,
-    a_scales uint8 [rows, K/32]) on the block-scaled matrix cores."""
+    a_scales uint8 [rows, K/32]) on the block-scaled matrix cores. ``out`` is
+    bf16 or fp32, or uint8 (MXFP8 codes) with ``out_scales`` uint8
+    [>= max_rows, N/32]."""
     num_local = expert_offsets.shape[0] - 1
     N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
     _dev(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
@@ -350,11 +352,22 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
             raise ValueError("a_rows must be int32 with >= max_rows entries")
     elif a_codes.shape[0] < max_rows:
         raise ValueError("a_codes must hold >= max_rows rows")
+    if out.dtype == torch.uint8:
+        if out_scales is None:
+            raise ValueError("MXFP8 output needs out_scales")
+        _dev(out_scales)
+        _want(out_scales, torch.uint8, (out.shape[0], N // 32), "out_scales")
+        odt = DT_MXFP8
+    else:
+        if out_scales is not None:
+            raise ValueError("out_scales is only for MXFP8 (uint8) output")
+        odt = _dt(out)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib.moe_grouped_gemm_mx8(
         _ptr(a_codes), _ptr(a_scales), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K,
-        MX_BLOCK, w_layout, act, _ptr(out), _dt(out), N, _ptr(ws), nbytes, _stream(stream))
+        MX_BLOCK, w_layout, act, _ptr(out), odt, _ptr(out_scales), N, _ptr(ws), nbytes,
+        _stream(stream))
     _check("moe_grouped_gemm_mx8", st)
 
 

@@ -137,7 +137,7 @@ LayerWs layer_ws(const moe_layer_params *p)
     o += round_up(mx8 ? mx8_gemm_ws_bytes(p->num_local, (int)A)
                       : grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
     // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
-    // from there to MXFP8
+    // from there to MXFP8 (hq, hs)
     L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
     if (mx8) {
         L.xq = o; o += round_up(T * (size_t)p->d);
@@ -290,21 +290,27 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                          const uint8_t *w1_scales, const uint8_t *w2_codes,
                          const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
                          int max_rows, int N, int K, int block_size, int w_layout, int act,
-                         void *out, int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
-                         moe_stream_t stream)
+                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, void *ws,
+                         size_t ws_bytes, moe_stream_t stream)
 {
+    const bool q_out = out_dtype == MOE_DT_MXFP8;
     int rc = check_gemm(a_codes, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
-                        num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
-                        ldo);
+                        num_local, max_rows, N, K, block_size, w_layout, act, out,
+                        q_out ? MOE_DT_BF16 : out_dtype, ldo);
     if (rc) return rc;
+    CHECK(q_out == (out_scales != nullptr), MOE_ERR_INVALID_ARG);
     if (max_rows == 0) return MOE_OK;
     CHECK(a_scales && lda % 32 == 0, MOE_ERR_INVALID_ARG);
+    if (q_out) CHECK(ldo % 32 == 0 && aligned(out, 16), MOE_ERR_INVALID_ARG);
     rc = check_ws(ws, ws_bytes, mx8_gemm_ws_bytes(num_local, max_rows));
     if (rc) return rc;
     HIP_TRY(launch_grouped_gemm_mx8(a_codes, a_scales, lda, a_rows, w1_codes, w1_scales,
                                     w2_codes, w2_scales, expert_offsets, num_local, max_rows, N,
-                                    K, act, out, out_dtype == MOE_DT_F32, ldo, ws,
-                                    w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
+                                    K, act, out,
+                                    q_out ? MX8_OUT_MXFP8
+                                          : out_dtype == MOE_DT_F32 ? MX8_OUT_F32 : MX8_OUT_BF16,
+                                    out_scales, ldo, ws, w_layout == MOE_LAYOUT_PACKED,
+                                    as_stream(stream)));
     return MOE_OK;
 }
 
@@ -468,16 +474,19 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
         float *h32 = (float *)(base + L.h);
         if (ev) HIP_TRY(hipEventRecord(ev[2], s));
         // gate/up stage: the tokens to MXFP8, then the projection with act
+        // (h in fp32). A separate pass converts h: quantising in the GEMM
+        // epilogue (MX8_OUT_MXFP8) measured slower, as its per-element
+        // reduction and rounding work sits on the MFMA-bound kernel.
         HIP_TRY(launch_mxfp8_quantize(x, 0, p->d, p->T, p->d, xq, xs, s));
         HIP_TRY(launch_gemm_mx8_run(xq, xs, p->d, perm, gate_codes, gate_scales, up_codes,
-                                    up_scales, p->num_local, A, p->I, p->d, p->act, h32, 1, p->I,
-                                    base + L.gws, packed, s));
+                                    up_scales, p->num_local, A, p->I, p->d, p->act, h32,
+                                    MX8_OUT_F32, nullptr, p->I, base + L.gws, packed, s));
         if (ev) HIP_TRY(hipEventRecord(ev[3], s));
         // down stage: h to MXFP8, then the projection
         HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s));
         HIP_TRY(launch_gemm_mx8_run(hq, hs, p->I, nullptr, down_codes, down_scales, nullptr,
-                                    nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1,
-                                    p->d, base + L.gws, packed, s));
+                                    nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y,
+                                    MX8_OUT_F32, nullptr, p->d, base + L.gws, packed, s));
         if (ev) HIP_TRY(hipEventRecord(ev[4], s));
         HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
                                p->out_dtype == MOE_DT_F32, p->d, s));

@@ -14,6 +14,8 @@
 //                          [N][K/32]); one thread per 32-element block
 //   gemm_mx8_kernel        grouped projection, 256 x 256 tiles, MXFP8 rows x
 //                          MXFP4 weights, fp32 accumulation
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -48,6 +50,25 @@ __device__ __forceinline__ uint32_t e4m3_code(float q)
         mag = ((((b >> 23) & 0xFFu) - 127u + 7u) << 3) | ((b >> 20) & 7u);
     }
     return sign | mag;
+}
+
+// The E8M0 scale code of a block with this amax, and 2^(127 - s): s =
+// clamp(floor(log2 amax) - 8 + 127, 0, 254); an fp32-subnormal amax is below
+// 2^-126 and clamps to 0. s <= 246 for finite input, so the exponent field of
+// 2^(127 - s) is >= 8.
+__device__ __forceinline__ int mxfp8_scale(float amax, float &inv)
+{
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    const int s = (amax == 0.0f || ex == 0) ? 0 : min(254, max(0, ex - 127 - 8 + 127));
+    inv = __uint_as_float((uint32_t)(254 - s) << 23);
+    return s;
+}
+
+// A DPP move of a float (all rows and banks, no bound control).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
 template <typename InT>
@@ -88,12 +109,8 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const InT *__restri
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(x[j]));
-    const uint32_t u = __float_as_uint(amax);
-    const int ex = (int)((u >> 23) & 0xffu);
-    // floor(log2 amax); an fp32 subnormal amax is below 2^-126 and clamps to 0
-    const int s = (amax == 0.0f || ex == 0) ? 0 : min(254, max(0, ex - 127 - 8 + 127));
-    // 2^(127 - s): s <= 246 for finite input, so the exponent field is >= 8
-    const float inv = __uint_as_float((uint32_t)(254 - s) << 23);
+    float inv;
+    const int s = mxfp8_scale(amax, inv);
     uint8_t *c = codes + n * (int64_t)K + 32 * b;
 #pragma unroll
     for (int h = 0; h < 2; h++) {
@@ -148,6 +165,11 @@ hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t 
 //
 // Pipeline: two LDS stages and two register stages, global loads two K steps
 // ahead (the last steps repeat step nk - 1), one barrier per K step.
+//
+// Output: fp32 or bf16, or (OutT = uint8_t) MXFP8 with the quantiser's
+// arithmetic: a weight tile's 32 columns are one MX block of the output row,
+// held by the 32 lanes of a half-wave, so the block's amax is a 32-lane
+// reduction; codes go to out [rows][ldo], scales to out_scales [rows][ldo/32].
 // ---------------------------------------------------------------------------
 constexpr int M8_BM = 256, M8_BN = 256, M8_BK = 64, M8_THREADS = 512, M8_ALD = 80;
 
@@ -157,9 +179,10 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
     const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
     const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
-    OutT *__restrict__ out, int64_t ldo)
+    OutT *__restrict__ out, uint8_t *__restrict__ out_scales, int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
+    constexpr bool QOUT = std::is_same<OutT, uint8_t>::value;
     constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
     __shared__ __attribute__((aligned(16))) uint8_t Aq[2][M8_BM][M8_ALD];
     __shared__ uint8_t Asc[2][M8_BM][2];
@@ -324,27 +347,46 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
         }
 
         // epilogue: lane holds C[8 (v / 4) + 4 g + v % 4][l32] of each tile
+        auto emit = [&](int rl, int col, float val) {
+            if constexpr (QOUT) {
+                // every lane takes part in the reduction; the 32 columns of a
+                // tile are all inside N or all past it (N % 32 == 0)
+                // max over the half-wave: rotations by 8, 4, 2, 1 inside each
+                // 16-lane row (DPP row_ror), then lane ^ 16 (ds_swizzle, bit
+                // mode: and 0x1f, or 0, xor 0x10)
+                float amax = fabsf(val);
+                amax = fmaxf(amax, dpp_f<0x128>(amax));  // row_ror:8
+                amax = fmaxf(amax, dpp_f<0x124>(amax));  // row_ror:4
+                amax = fmaxf(amax, dpp_f<0x122>(amax));  // row_ror:2
+                amax = fmaxf(amax, dpp_f<0x121>(amax));  // row_ror:1
+                amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_ds_swizzle(
+                                       __float_as_int(amax), 0x401F)));
+                float inv;
+                const int sc = mxfp8_scale(amax, inv);
+                const uint32_t code = amax == 0.0f ? 0u : e4m3_code(val * inv);
+                if (rl < mrows && col < N) {
+                    const int64_t row = r0 + rl;
+                    out[row * ldo + col] = (uint8_t)code;
+                    if (l32 == 0) out_scales[row * (ldo / 32) + col / 32] = (uint8_t)sc;
+                }
+            } else {
+                if (rl < mrows && col < N) store_out<OutT>(out + (int64_t)(r0 + rl) * ldo + col, val);
+            }
+        };
 #pragma unroll
         for (int i = 0; i < NI; i++) {
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int rl = 32 * q + 128 * i + 8 * (v >> 2) + 4 * g + (v & 3);
-                if (rl >= mrows) continue;
-                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                if (!QOUT && rl >= mrows) continue;
                 if constexpr (GLU) {
 #pragma unroll
-                    for (int jj = 0; jj < 2; jj++) {
-                        const int col = n0 + 64 * ch + 32 * jj + l32;
-                        if (col < N)
-                            store_out<OutT>(orow + col,
-                                            act_apply<ACT>(acc[i][jj][v], acc[i][2 + jj][v]));
-                    }
+                    for (int jj = 0; jj < 2; jj++)
+                        emit(rl, n0 + 64 * ch + 32 * jj + l32,
+                             act_apply<ACT>(acc[i][jj][v], acc[i][2 + jj][v]));
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int col = n0 + 128 * ch + 32 * j + l32;
-                        if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
-                    }
+                    for (int j = 0; j < 4; j++) emit(rl, n0 + 128 * ch + 32 * j + l32, acc[i][j][v]);
                 }
             }
         }
@@ -361,7 +403,8 @@ template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
                              const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                              const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa,
-                             int N, int K, OutT *out, int64_t ldo, hipStream_t s)
+                             int N, int K, OutT *out, uint8_t *out_scales, int64_t ldo,
+                             hipStream_t s)
 {
     constexpr int COLS = ACT != ACT_NONE ? M8_BN / 2 : M8_BN;
     const int64_t grid = (int64_t)pa.max_groups * ((N + COLS - 1) / COLS);
@@ -371,7 +414,7 @@ static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
     const int64_t G = (grid + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(M8_THREADS),
                        0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out,
-                       ldo);
+                       out_scales, ldo);
     return hipGetLastError();
 }
 
@@ -379,18 +422,18 @@ template <typename OutT, bool PACKED>
 static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t lda,
                           const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                           const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa, int N,
-                          int K, OutT *out, int64_t ldo, hipStream_t s)
+                          int K, OutT *out, uint8_t *out_scales, int64_t ldo, hipStream_t s)
 {
     switch (act) {
     case ACT_NONE:
         return launch_mx8<ACT_NONE, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N,
-                                                  K, out, ldo, s);
+                                                  K, out, out_scales, ldo, s);
     case ACT_SILU_MUL:
         return launch_mx8<ACT_SILU_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa,
-                                                      N, K, out, ldo, s);
+                                                      N, K, out, out_scales, ldo, s);
     case ACT_GELU_TANH_MUL:
         return launch_mx8<ACT_GELU_TANH_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c,
-                                                           w2s, pa, N, K, out, ldo, s);
+                                                           w2s, pa, N, K, out, out_scales, ldo, s);
     default:
         return hipErrorInvalidValue;
     }
@@ -410,15 +453,21 @@ size_t mx8_gemm_ws_bytes(int num_local, int max_rows)
 hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
                                const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                const uint8_t *w2c, const uint8_t *w2s, int num_local,
-                               int max_rows, int N, int K, int act, void *out, int out_f32,
-                               int64_t ldo, void *plan_ws, int packed, hipStream_t s)
+                               int max_rows, int N, int K, int act, void *out, int out_kind,
+                               uint8_t *out_scales, int64_t ldo, void *plan_ws, int packed,
+                               hipStream_t s)
 {
     const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, plan_ws);
-#define MX8_RUN(OT, PK) \
-    return mx8_act<OT, PK>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, (OT *)out, ldo, s)
-    if (out_f32) {
+#define MX8_RUN(OT, PK)                                                                         \
+    return mx8_act<OT, PK>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, (OT *)out, \
+                           out_scales, ldo, s)
+    if (out_kind == MX8_OUT_F32) {
         if (packed) MX8_RUN(float, true);
         MX8_RUN(float, false);
+    }
+    if (out_kind == MX8_OUT_MXFP8) {
+        if (packed) MX8_RUN(uint8_t, true);
+        MX8_RUN(uint8_t, false);
     }
     if (packed) MX8_RUN(bf16, true);
     MX8_RUN(bf16, false);
@@ -429,12 +478,13 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
                                    const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                    const uint8_t *w2c, const uint8_t *w2s, const int32_t *off,
                                    int num_local, int max_rows, int N, int K, int act, void *out,
-                                   int out_f32, int64_t ldo, void *ws, int packed, hipStream_t s)
+                                   int out_kind, uint8_t *out_scales, int64_t ldo, void *ws,
+                                   int packed, hipStream_t s)
 {
     hipError_t e = launch_gemm_plan_into(off, num_local, mx8_plan_args(num_local, max_rows, ws), s);
     if (e != hipSuccess) return e;
     return launch_gemm_mx8_run(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
-                               K, act, out, out_f32, ldo, ws, packed, s);
+                               K, act, out, out_kind, out_scales, ldo, ws, packed, s);
 }
 
 }  // namespace moe

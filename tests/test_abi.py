@@ -185,7 +185,7 @@ def test_mx8_validation():
     def gemm(**kw):
         a = dict(ac=FAKE, asc=FAKE, lda=256, rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE,
                  off=FAKE, nl=8, maxr=64, N=128, K=256, bs=32, lay=0, act=1, out=FAKE, odt=1,
-                 ldo=128, ws=FAKE, wsb=need)
+                 osc=None, ldo=128, ws=FAKE, wsb=need)
         a.update(kw)
         return L.moe_grouped_gemm_mx8(*a.values(), None)
     assert gemm(bs=64) == 2
@@ -195,12 +195,15 @@ def test_mx8_validation():
     assert gemm(w2c=None, w2s=None) == 1
     assert gemm(wsb=need - 1) == 3
     assert gemm(maxr=0, ac=None, asc=None, out=None, ws=None, wsb=0) == 0
+    assert gemm(odt=2) == 1                   # MXFP8 output without its scales
+    assert gemm(osc=FAKE) == 1                # scales with an fp32 output
+    assert gemm(odt=3, osc=FAKE) == 1
     # the layer's precision field
     p = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8)
     n_mx8 = m.moe_layer_workspace_size(p)
     n_bf16 = m.moe_layer_workspace_size(m.layer_params(8, 3584, 896, 16, 128))
-    # fp32 h plus MXFP8 tokens and h
-    assert n_mx8 >= n_bf16 + 8 * 16 * 128 * 2 + 8 * 3584
+    # fp32 h in place of bf16, plus MXFP8 tokens and h
+    assert n_mx8 >= n_bf16 + 8 * 16 * 128 * 2 + 8 * 3584 + 8 * 16 * 128
     bad = m.layer_params(8, 3584, 896, 16, 128, precision=2)
     assert L.moe_layer_workspace_size(C.byref(bad)) == 0
 

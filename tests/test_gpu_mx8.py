@@ -153,6 +153,36 @@ def test_grouped_gemm_mx8_bf16_out_and_direct_rows(m):
                 + MMA_TOL * _bound(ha[r0:r1], w)).all()
 
 
+@pytest.mark.parametrize("act", [0, 1])
+def test_grouped_gemm_mx8_mxfp8_output_bitexact(m, act):
+    """MXFP8 output (the layer's h): codes and scales equal the oracle's
+    quantiser applied to the fp32 output of the same launch configuration,
+    byte for byte; rows past each group's end and columns past N untouched."""
+    rng = np.random.default_rng(20 + act)
+    nl, N, K, T = 4, 320, 384, 500
+    counts = np.array([150, 0, 257, 40], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    xc, xs = _mx8_rows(rng, T, K)
+    a_rows = torch.from_numpy(rng.integers(0, T, size=A).astype(np.int32)).to(DEV)
+    w1c, w1s = _experts(nl, N, K, 5)
+    w2c, w2s = _experts(nl, N, K, 6) if act else (None, None)
+    dev = lambda t: None if t is None else t.to(DEV)
+    args = (torch.from_numpy(xc).to(DEV), torch.from_numpy(xs).to(DEV), a_rows, dev(w1c),
+            dev(w1s), dev(w2c), dev(w2s), torch.from_numpy(off).to(DEV), A, act)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
+    f32 = torch.empty(A, N, dtype=torch.float32, device=DEV)
+    m.moe_grouped_gemm_mx8(*args, f32, ws)
+    codes = torch.full((A + 2, N), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((A + 2, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
+    m.moe_grouped_gemm_mx8(*args, codes, ws, out_scales=scales)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mxfp8_quantize(np_(f32))
+    assert np.array_equal(np_(scales)[:A], rs)
+    assert np.array_equal(np_(codes)[:A], rc)
+    assert (np_(codes)[A:] == 0xA5).all() and (np_(scales)[A:] == 0x5A).all()
+
+
 # ---------------------------------------------------------------- layer
 SMALL = [
     LayerConfig("x0", T=37, I=128, d=256, E=64, k=8),
