@@ -264,7 +264,9 @@ int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K
  * moe_grouped_gemm_mxfp4, or with out_dtype MOE_DT_MXFP8 the fp32 results
  * converted as moe_mxfp8_quantize does (blocks of 32 along N): codes to out
  * [rows][ldo] (bytes), scales to out_scales [rows][ldo/32] (NULL for the
- * other dtypes). 256-row tiles only; ws holds
+ * other dtypes). mode: MOE_SCHED_TILE128 for 128-row tiles; MOE_SCHED_AUTO,
+ * MOE_SCHED_TILED and MOE_SCHED_TILE256 give 256-row tiles;
+ * MOE_SCHED_STREAM -> INVALID_ARG. ws holds
  * moe_grouped_gemm_mx8_workspace_size(...) bytes.
  * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0 (% 32 for
  * MXFP8 output); 16-byte aligned code and scale arrays. Errors as
@@ -275,8 +277,8 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                          const uint8_t *w1_scales, const uint8_t *w2_codes,
                          const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
                          int max_rows, int N, int K, int block_size, int w_layout, int act,
-                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, void *ws,
-                         size_t ws_bytes, moe_stream_t stream);
+                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, int mode,
+                         void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- weighted unpermute (P3 section 四, combine: results come back
@@ -309,7 +311,8 @@ typedef struct {
     int weight_layout; /* enum moe_weight_layout of all six weight arrays */
     int precision;    /* enum moe_precision: MOE_PREC_BF16 (the pages' bf16
                          activations) or MOE_PREC_MX8 (tokens and h rounded to
-                         MXFP8 before each projection; `mode` is then ignored) */
+                         MXFP8 before each projection; `mode` as in
+                         moe_grouped_gemm_mx8) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

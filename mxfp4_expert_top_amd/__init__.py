@@ -77,7 +77,7 @@ def _load(path=None):
     L.moe_grouped_gemm_mx8_workspace_size.argtypes = [i32, i32]
     L.moe_grouped_gemm_mx8.restype = i32
     L.moe_grouped_gemm_mx8.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
-                                       i32, p, i32, p, i64, p, sz, p]
+                                       i32, p, i32, p, i64, i32, p, sz, p]
     return L
 
 
@@ -328,7 +328,7 @@ def moe_grouped_gemm_mx8_workspace_size(num_local, max_rows):
 
 def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
                          expert_offsets, max_rows, act, out, ws, w_layout=LAYOUT_OCP,
-                         out_scales=None, stream=None):
+                         out_scales=None, mode=MODE_AUTO, stream=None):
     """moe_grouped_gemm_mxfp4 with MXFP8 rows (a_codes uint8 [rows, K] E4M3,
     a_scales uint8 [rows, K/32]) on the block-scaled matrix cores. ``out`` is
     bf16 or fp32, or uint8 (MXFP8 codes) with ``out_scales`` uint8
@@ -366,7 +366,7 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
     st = lib.moe_grouped_gemm_mx8(
         _ptr(a_codes), _ptr(a_scales), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K,
-        MX_BLOCK, w_layout, act, _ptr(out), odt, _ptr(out_scales), N, _ptr(ws), nbytes,
+        MX_BLOCK, w_layout, act, _ptr(out), odt, _ptr(out_scales), N, mode, _ptr(ws), nbytes,
         _stream(stream))
     _check("moe_grouped_gemm_mx8", st)
 

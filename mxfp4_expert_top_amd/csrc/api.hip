@@ -165,6 +165,8 @@ int check_layer_params(const moe_layer_params *p)
     CHECK(p->weight_layout == MOE_LAYOUT_OCP || p->weight_layout == MOE_LAYOUT_PACKED,
           MOE_ERR_INVALID_ARG);
     CHECK(p->precision == MOE_PREC_BF16 || p->precision == MOE_PREC_MX8, MOE_ERR_INVALID_ARG);
+    // the MX8 mode has the two tiled schedules only
+    CHECK(p->precision != MOE_PREC_MX8 || p->mode != MOE_SCHED_STREAM, MOE_ERR_INVALID_ARG);
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
     CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
     CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
@@ -290,10 +292,13 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                          const uint8_t *w1_scales, const uint8_t *w2_codes,
                          const uint8_t *w2_scales, const int32_t *expert_offsets, int num_local,
                          int max_rows, int N, int K, int block_size, int w_layout, int act,
-                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, void *ws,
-                         size_t ws_bytes, moe_stream_t stream)
+                         void *out, int out_dtype, uint8_t *out_scales, int64_t ldo, int mode,
+                         void *ws, size_t ws_bytes, moe_stream_t stream)
 {
     const bool q_out = out_dtype == MOE_DT_MXFP8;
+    CHECK(mode == MOE_SCHED_AUTO || mode == MOE_SCHED_TILED || mode == MOE_SCHED_TILE128 ||
+              mode == MOE_SCHED_TILE256,
+          MOE_ERR_INVALID_ARG);
     int rc = check_gemm(a_codes, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
                         num_local, max_rows, N, K, block_size, w_layout, act, out,
                         q_out ? MOE_DT_BF16 : out_dtype, ldo);
@@ -309,7 +314,7 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                                     K, act, out,
                                     q_out ? MX8_OUT_MXFP8
                                           : out_dtype == MOE_DT_F32 ? MX8_OUT_F32 : MX8_OUT_BF16,
-                                    out_scales, ldo, ws, w_layout == MOE_LAYOUT_PACKED,
+                                    out_scales, ldo, mode, ws, w_layout == MOE_LAYOUT_PACKED,
                                     as_stream(stream)));
     return MOE_OK;
 }
@@ -466,7 +471,7 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);
     if (p->precision == MOE_PREC_MX8) {
-        const GemmPlanArgs pm = mx8_plan_args(p->num_local, A, base + L.gws);
+        const GemmPlanArgs pm = mx8_plan_args(p->num_local, A, p->mode, base + L.gws);
         HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm,
                                inv, base + L.pws, s, &pm));
         uint8_t *xq = (uint8_t *)(base + L.xq), *xs = (uint8_t *)(base + L.xs);
@@ -480,13 +485,15 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
         HIP_TRY(launch_mxfp8_quantize(x, 0, p->d, p->T, p->d, xq, xs, s));
         HIP_TRY(launch_gemm_mx8_run(xq, xs, p->d, perm, gate_codes, gate_scales, up_codes,
                                     up_scales, p->num_local, A, p->I, p->d, p->act, h32,
-                                    MX8_OUT_F32, nullptr, p->I, base + L.gws, packed, s));
+                                    MX8_OUT_F32, nullptr, p->I, p->mode, base + L.gws, packed,
+                                    s));
         if (ev) HIP_TRY(hipEventRecord(ev[3], s));
         // down stage: h to MXFP8, then the projection
         HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s));
         HIP_TRY(launch_gemm_mx8_run(hq, hs, p->I, nullptr, down_codes, down_scales, nullptr,
                                     nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y,
-                                    MX8_OUT_F32, nullptr, p->d, base + L.gws, packed, s));
+                                    MX8_OUT_F32, nullptr, p->d, p->mode, base + L.gws, packed,
+                                    s));
         if (ev) HIP_TRY(hipEventRecord(ev[4], s));
         HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
                                p->out_dtype == MOE_DT_F32, p->d, s));

@@ -108,7 +108,10 @@ hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int
 hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
                                  uint8_t *codes, uint8_t *scales, hipStream_t s);
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows);
-GemmPlanArgs mx8_plan_args(int num_local, int max_rows, void *ws);
+// MOE_SCHED_TILE128 or MOE_SCHED_TILE256 for a requested mode (AUTO / TILED
+// choose as the bf16 tiled schedules do)
+int mx8_resolve_mode(int mode, int num_local, int max_rows);
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws);
 // A: codes [rows][lda] bytes, scales [rows][lda / 32]. Output kinds: bf16,
 // fp32, or MXFP8 (codes in out [rows][ldo], scales in out_scales [rows][ldo/32]).
 enum { MX8_OUT_BF16 = 0, MX8_OUT_F32 = 1, MX8_OUT_MXFP8 = 2 };
@@ -116,14 +119,14 @@ hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda
                                const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                const uint8_t *w2c, const uint8_t *w2s, int num_local,
                                int max_rows, int N, int K, int act, void *out, int out_kind,
-                               uint8_t *out_scales, int64_t ldo, void *plan_ws, int packed,
-                               hipStream_t s);
+                               uint8_t *out_scales, int64_t ldo, int mode, void *plan_ws,
+                               int packed, hipStream_t s);
 hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
                                    const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                    const uint8_t *w2c, const uint8_t *w2s, const int32_t *off,
                                    int num_local, int max_rows, int N, int K, int act, void *out,
-                                   int out_kind, uint8_t *out_scales, int64_t ldo, void *ws,
-                                   int packed, hipStream_t s);
+                                   int out_kind, uint8_t *out_scales, int64_t ldo, int mode,
+                                   void *ws, int packed, hipStream_t s);
 
 // prepack.hip: the streaming weight layout (see prepack.hip) and the fp32 ->
 // MXFP4 quantiser (canonical layout out)

@@ -145,11 +145,13 @@ hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t 
 // ---------------------------------------------------------------------------
 // Grouped projection on the block-scaled matrix cores.
 //
-// Workgroup tile: 256 permuted rows of one expert x 256 weight rows, K step
-// 64 (two MX blocks). 8 waves as 4 row quarters x 2 weight halves; quarter q
-// owns row tiles q and q + 4 of 32 (those holding rows of the group), each
-// against the 4 weight tiles of 32 of its half; one 32 x 32 x 64 MFMA per
-// (row tile, weight tile) per K step. A GLU tile holds 128 W1 rows and the
+// Workgroup tile: BM (256 or 128) permuted rows of one expert x 256 weight
+// rows, K step 64 (two MX blocks). 8 waves as 4 row quarters x 2 weight
+// halves; quarter q owns row tile q of 32, and q + 4 in the 256-row tile
+// (those holding rows of the group), each against the 4 weight tiles of 32 of
+// its half; one 32 x 32 x 64 MFMA per (row tile, weight tile) per K step.
+// The 128-row tile has twice the work items of half the size (one workgroup
+// per CU either way: at 128 VGPRs, for two, the 128-row kernel spills). A GLU tile holds 128 W1 rows and the
 // same 128 W2 rows (weight half ch: rows 64 ch .. 64 ch + 63 of each), so
 // act(gate, up) is applied in registers.
 //
@@ -171,9 +173,9 @@ hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t 
 // held by the 32 lanes of a half-wave, so the block's amax is a 32-lane
 // reduction; codes go to out [rows][ldo], scales to out_scales [rows][ldo/32].
 // ---------------------------------------------------------------------------
-constexpr int M8_BM = 256, M8_BN = 256, M8_BK = 64, M8_THREADS = 512, M8_ALD = 80;
+constexpr int M8_BN = 256, M8_BK = 64, M8_THREADS = 512, M8_ALD = 80;
 
-template <int ACT, typename OutT, bool PACKED>
+template <int ACT, typename OutT, bool PACKED, int BM>
 __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t lda,
     const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
@@ -184,8 +186,9 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr bool QOUT = std::is_same<OutT, uint8_t>::value;
     constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
-    __shared__ __attribute__((aligned(16))) uint8_t Aq[2][M8_BM][M8_ALD];
-    __shared__ uint8_t Asc[2][M8_BM][2];
+    constexpr int AJ = BM / 128;  // 16-byte A chunks per thread per K step
+    __shared__ __attribute__((aligned(16))) uint8_t Aq[2][BM][M8_ALD];
+    __shared__ uint8_t Asc[2][BM][2];
     __shared__ __attribute__((aligned(16))) uint8_t Bq[2][M8_BN][M8_BK / 2];
     __shared__ uint8_t Bsc[2][M8_BN][2];
 
@@ -208,12 +211,14 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     const int ch = wave & 1, q = wave >> 1;
 
     // ---- global -> LDS assignment
-    // A codes: 16-byte chunks c = tid and tid + 512 of the 256 x 64-byte
-    // step, row c / 4, bytes 16 (c % 4); A scales: row tid / 2, block tid % 2
+    // A codes: 16-byte chunks c = tid + 512 j (j < AJ) of the BM x 64-byte
+    // step, row c / 4, bytes 16 (c % 4); A scales: row tid / 2, block tid % 2,
+    // for the first 2 BM threads
     const int64_t lds_ = lda / 32;
-    const uint8_t *ag[2];
+    const bool a_sc = BM == 256 || tid < 2 * BM;
+    const uint8_t *ag[AJ];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < AJ; j++) {
         const int c = tid + 512 * j;
         const int rc = min(r0 + (c >> 2), rend - 1);
         const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     }
     const uint8_t *asg;
     {
-        const int rc = min(r0 + (tid >> 1), rend - 1);
+        const int rc = min(r0 + min(tid >> 1, BM - 1), rend - 1);
         const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
         asg = as + arow * lds_ + (tid & 1);
     }
@@ -251,13 +256,13 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
         sg = wsb + wr64 * (K / 32) + bh;
     }
 
-    u32x4 ra0[2], ra1[2], rb0, rb1;
-    uint8_t rsa0, rsa1, rsb0, rsb1;
+    u32x4 ra0[AJ], ra1[AJ], rb0, rb1;
+    uint8_t rsa0 = 0, rsa1 = 0, rsb0, rsb1;
     auto gload = [&](u32x4 *ra, uint8_t &rsa, u32x4 &rbv, uint8_t &rsb, int kt) {
         const int k0 = kt * M8_BK;
 #pragma unroll
-        for (int j = 0; j < 2; j++) ra[j] = *(const u32x4 *)(ag[j] + k0);
-        rsa = asg[k0 / 32];
+        for (int j = 0; j < AJ; j++) ra[j] = *(const u32x4 *)(ag[j] + k0);
+        if (a_sc) rsa = asg[k0 / 32];
         if constexpr (PACKED) {
             const int c = kt >> 1, gg = 2 * (kt & 1) + bh;
             rbv = *(const u32x4 *)(bg + c * 1024 + gg * 256);
@@ -269,11 +274,11 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     };
     auto lstore = [&](int st, const u32x4 *ra, uint8_t rsa, const u32x4 &rbv, uint8_t rsb) {
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
+        for (int j = 0; j < AJ; j++) {
             const int c = tid + 512 * j;
             *(u32x4 *)(&Aq[st][c >> 2][16 * (c & 3)]) = ra[j];
         }
-        Asc[st][tid >> 1][tid & 1] = rsa;
+        if (a_sc) Asc[st][tid >> 1][tid & 1] = rsa;
         *(u32x4 *)(&Bq[st][br][16 * bh]) = rbv;
         Bsc[st][br][bh] = rsb;
     };
@@ -286,7 +291,8 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
         if (GLU) bt[j] = (j >= 2 ? 128 : 0) + 64 * ch + 32 * (j & 1);  // W1 x2, then W2 x2
         else bt[j] = 128 * ch + 32 * j;
     }
-    const int n_on = (32 * q < mrows ? 1 : 0) + (128 + 32 * q < mrows ? 1 : 0);
+    // row tiles of the wave: q, and q + 4 in the 256-row tile
+    const int n_on = (32 * q < mrows ? 1 : 0) + (BM == 256 && 128 + 32 * q < mrows ? 1 : 0);
     const int nk = K / M8_BK;  // even: K is a multiple of 128
 
     auto run = [&](auto ni_c) {
@@ -393,13 +399,15 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     };
     // every branch runs the same barriers (1 + nk)
     switch (__builtin_amdgcn_readfirstlane(n_on)) {
-    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 2:
+        if constexpr (BM == 256) run(std::integral_constant<int, 2>{});
+        break;
     case 1: run(std::integral_constant<int, 1>{}); break;
     default: run(std::integral_constant<int, 0>{}); break;
     }
 }
 
-template <int ACT, typename OutT, bool PACKED>
+template <int ACT, typename OutT, bool PACKED, int BM>
 static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
                              const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                              const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa,
@@ -412,55 +420,68 @@ static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
     // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(M8_THREADS),
+    hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED, BM>), dim3((unsigned)G), dim3(M8_THREADS),
                        0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out,
                        out_scales, ldo);
     return hipGetLastError();
 }
 
-template <typename OutT, bool PACKED>
+template <typename OutT, bool PACKED, int BM>
 static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t lda,
                           const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                           const uint8_t *w2c, const uint8_t *w2s, const GemmPlanArgs &pa, int N,
                           int K, OutT *out, uint8_t *out_scales, int64_t ldo, hipStream_t s)
 {
+#define MX8_ACT(A)                                                                           \
+    case A:                                                                                  \
+        return launch_mx8<A, OutT, PACKED, BM>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, \
+                                               K, out, out_scales, ldo, s);
     switch (act) {
-    case ACT_NONE:
-        return launch_mx8<ACT_NONE, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N,
-                                                  K, out, out_scales, ldo, s);
-    case ACT_SILU_MUL:
-        return launch_mx8<ACT_SILU_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa,
-                                                      N, K, out, out_scales, ldo, s);
-    case ACT_GELU_TANH_MUL:
-        return launch_mx8<ACT_GELU_TANH_MUL, OutT, PACKED>(ac, as, lda, a_rows, w1c, w1s, w2c,
-                                                           w2s, pa, N, K, out, out_scales, ldo, s);
+        MX8_ACT(ACT_NONE)
+        MX8_ACT(ACT_SILU_MUL)
+        MX8_ACT(ACT_GELU_TANH_MUL)
     default:
         return hipErrorInvalidValue;
     }
+#undef MX8_ACT
 }
 
-GemmPlanArgs mx8_plan_args(int num_local, int max_rows, void *ws)
+// MX8 schedules: the 256-row tile (one tile row per expert of up to 256
+// rows, balanced groups) or the 128-row tile. AUTO and TILED take the 256-row
+// tile: it measured faster on every workload tried (about 146, 360 and 1170
+// mean rows per expert), the 128-row tile running one workgroup per CU too.
+int mx8_resolve_mode(int mode, int num_local, int max_rows)
 {
-    // the 256-row tiles take the 256-row grouping of the bf16 schedule
-    return gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws);
+    (void)num_local;
+    (void)max_rows;
+    return mode == MOE_SCHED_TILE128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256;
+}
+
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws)
+{
+    return gemm_plan_args(num_local, max_rows, mx8_resolve_mode(mode, num_local, max_rows), ws);
 }
 
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows)
 {
-    return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE256);
+    // the 128-row grouping has the most work items
+    return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE128);
 }
 
 hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
                                const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                const uint8_t *w2c, const uint8_t *w2s, int num_local,
                                int max_rows, int N, int K, int act, void *out, int out_kind,
-                               uint8_t *out_scales, int64_t ldo, void *plan_ws, int packed,
-                               hipStream_t s)
+                               uint8_t *out_scales, int64_t ldo, int mode, void *plan_ws,
+                               int packed, hipStream_t s)
 {
-    const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, plan_ws);
-#define MX8_RUN(OT, PK)                                                                         \
-    return mx8_act<OT, PK>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, (OT *)out, \
-                           out_scales, ldo, s)
+    const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, mode, plan_ws);
+    const bool t256 = mx8_resolve_mode(mode, num_local, max_rows) == MOE_SCHED_TILE256;
+#define MX8_RUN(OT, PK)                                                                        \
+    return t256 ? mx8_act<OT, PK, 256>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, \
+                                       (OT *)out, out_scales, ldo, s)                          \
+                : mx8_act<OT, PK, 128>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, \
+                                       (OT *)out, out_scales, ldo, s)
     if (out_kind == MX8_OUT_F32) {
         if (packed) MX8_RUN(float, true);
         MX8_RUN(float, false);
@@ -478,13 +499,14 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
                                    const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                    const uint8_t *w2c, const uint8_t *w2s, const int32_t *off,
                                    int num_local, int max_rows, int N, int K, int act, void *out,
-                                   int out_kind, uint8_t *out_scales, int64_t ldo, void *ws,
-                                   int packed, hipStream_t s)
+                                   int out_kind, uint8_t *out_scales, int64_t ldo, int mode,
+                                   void *ws, int packed, hipStream_t s)
 {
-    hipError_t e = launch_gemm_plan_into(off, num_local, mx8_plan_args(num_local, max_rows, ws), s);
+    hipError_t e = launch_gemm_plan_into(off, num_local,
+                                         mx8_plan_args(num_local, max_rows, mode, ws), s);
     if (e != hipSuccess) return e;
     return launch_gemm_mx8_run(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
-                               K, act, out, out_kind, out_scales, ldo, ws, packed, s);
+                               K, act, out, out_kind, out_scales, ldo, mode, ws, packed, s);
 }
 
 }  // namespace moe

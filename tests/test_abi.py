@@ -185,7 +185,7 @@ def test_mx8_validation():
     def gemm(**kw):
         a = dict(ac=FAKE, asc=FAKE, lda=256, rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE,
                  off=FAKE, nl=8, maxr=64, N=128, K=256, bs=32, lay=0, act=1, out=FAKE, odt=1,
-                 osc=None, ldo=128, ws=FAKE, wsb=need)
+                 osc=None, ldo=128, mode=0, ws=FAKE, wsb=need)
         a.update(kw)
         return L.moe_grouped_gemm_mx8(*a.values(), None)
     assert gemm(bs=64) == 2
@@ -198,6 +198,10 @@ def test_mx8_validation():
     assert gemm(odt=2) == 1                   # MXFP8 output without its scales
     assert gemm(osc=FAKE) == 1                # scales with an fp32 output
     assert gemm(odt=3, osc=FAKE) == 1
+    assert gemm(mode=1) == 1                  # no streaming schedule in this mode
+    assert gemm(mode=5) == 1
+    bad = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8, mode=m.MODE_STREAM)
+    assert L.moe_layer_workspace_size(C.byref(bad)) == 0
     # the layer's precision field
     p = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8)
     n_mx8 = m.moe_layer_workspace_size(p)

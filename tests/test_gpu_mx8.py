@@ -75,13 +75,14 @@ def _bound(a, w):
     return np.abs(a) @ np.abs(w).T
 
 
+@pytest.mark.parametrize("mode", [3, 4])
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("K", [128, 640])
-def test_grouped_gemm_mx8_vs_definition(m, act, packed, K):
+def test_grouped_gemm_mx8_vs_definition(m, act, packed, K, mode):
     """Experts with 0, 1, 37, 150, 257 and 513 rows (empty, one row, ragged,
-    several 256-row groups), a column count that is not a tile multiple,
-    gathered rows, fp32 output."""
+    several 128- and 256-row groups), a column count that is not a tile
+    multiple, gathered rows, fp32 output; both tile heights."""
     rng = np.random.default_rng(K + 3 * act + 7 * packed)
     nl, N, T = 6, 320, 700
     counts = np.array([37, 0, 513, 1, 257, 150], np.int32)
@@ -100,7 +101,7 @@ def test_grouped_gemm_mx8_vs_definition(m, act, packed, K):
     m.moe_grouped_gemm_mx8(torch.from_numpy(xc).to(DEV), torch.from_numpy(xs).to(DEV),
                            torch.from_numpy(a_rows).to(DEV), g1c, g1s, g2c, g2s,
                            torch.from_numpy(off).to(DEV), A, act, out, ws,
-                           w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
+                           w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP, mode=mode)
     torch.cuda.synchronize()
     got = np_(out).astype(np.float64)
     assert (got[A:] == 7.0).all()
@@ -153,8 +154,9 @@ def test_grouped_gemm_mx8_bf16_out_and_direct_rows(m):
                 + MMA_TOL * _bound(ha[r0:r1], w)).all()
 
 
+@pytest.mark.parametrize("mode", [3, 4])
 @pytest.mark.parametrize("act", [0, 1])
-def test_grouped_gemm_mx8_mxfp8_output_bitexact(m, act):
+def test_grouped_gemm_mx8_mxfp8_output_bitexact(m, act, mode):
     """MXFP8 output (the layer's h): codes and scales equal the oracle's
     quantiser applied to the fp32 output of the same launch configuration,
     byte for byte; rows past each group's end and columns past N untouched."""
@@ -172,10 +174,10 @@ def test_grouped_gemm_mx8_mxfp8_output_bitexact(m, act):
             dev(w1s), dev(w2c), dev(w2s), torch.from_numpy(off).to(DEV), A, act)
     ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
     f32 = torch.empty(A, N, dtype=torch.float32, device=DEV)
-    m.moe_grouped_gemm_mx8(*args, f32, ws)
+    m.moe_grouped_gemm_mx8(*args, f32, ws, mode=mode)
     codes = torch.full((A + 2, N), 0xA5, dtype=torch.uint8, device=DEV)
     scales = torch.full((A + 2, N // 32), 0x5A, dtype=torch.uint8, device=DEV)
-    m.moe_grouped_gemm_mx8(*args, codes, ws, out_scales=scales)
+    m.moe_grouped_gemm_mx8(*args, codes, ws, out_scales=scales, mode=mode)
     torch.cuda.synchronize()
     rc, rs = oracle.mxfp8_quantize(np_(f32))
     assert np.array_equal(np_(scales)[:A], rs)
@@ -202,14 +204,15 @@ def _routing(inp, g):
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 @pytest.mark.parametrize("packed", [False, True])
-def test_small_layer_mx8_vs_oracle(m, cfg, packed):
+@pytest.mark.parametrize("mode", [0, 3])
+def test_small_layer_mx8_vs_oracle(m, cfg, packed, mode):
     """The whole MX8 layer against the oracle's MX8 layer on the GPU's scores.
     Both round h to E4M3 from fp32 values that differ by the instruction's
     summation error, so a few h codes may sit one E4M3 step apart; the layer
     bounds (rel-L2 1e-2, max-abs 3e-2 rms) cover that. The routing is the
     bf16 path's, bit for bit."""
     inp = make_inputs(cfg).to(DEV)
-    g = run_gpu_layer(inp, precision=m.PREC_MX8,
+    g = run_gpu_layer(inp, precision=m.PREC_MX8, mode=mode,
                       packed=m.prepack_weights(inp.weights) if packed else None)
     lg, _, _ = _routing(inp, g)
     ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
@@ -233,7 +236,7 @@ def test_mx8_layer_determinism_bitwise(m):
         assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("name", ["prefill", "decode"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "ep_share"])
 def test_full_size_mx8(m, name):
     """The prefill workload (and the decode batch) in the MX8 mode, in the
     benchmark's launch configuration: sampled tokens' rows against the
