@@ -75,6 +75,10 @@ def lib():
         L.oracle_layer_mx8.argtypes = L.oracle_layer.argtypes
         L.oracle_token_rows_mx8.restype = i32
         L.oracle_token_rows_mx8.argtypes = L.oracle_token_rows.argtypes
+        L.oracle_layer_lora.restype = i64
+        L.oracle_layer_lora.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64, i64,
+                                        p, p, p, p, p, p, i32, p, p, p, p, p, p, i64,
+                                        C.c_float, p, p, p, p, p, p, p]
         _lib = L
     return _lib
 
@@ -284,3 +288,42 @@ def token_rows(x, idx, w, tokens, wts, *, I, e0=0, n_local, act=ACT_SILU_MUL, mx
     if rc != 0:
         raise MemoryError("oracle_token_rows failed")
     return out
+
+
+LORA_NAMES = ("gate_a", "gate_b", "up_a", "up_b", "down_a", "down_b")
+
+
+def layer_lora(x, w_router, bias, wts, lora, *, E, k, I, rank, scale, e0=0, n_local=None,
+               act=ACT_SILU_MUL, logits=None):
+    """The whole layer with LoRA adapters on every local expert's gate, up
+    and down projections. ``lora`` maps gate_a/up_a [n_local, rank, d],
+    gate_b/up_b [n_local, I, rank], down_a [n_local, rank, I], down_b
+    [n_local, d, rank] to bf16 tensors or uint16 bit arrays."""
+    xb = bf16_bits(x)
+    T, d = xb.shape
+    n_local = E - e0 if n_local is None else n_local
+    w_router = _arr(w_router, np.float32)
+    if bias is not None:
+        bias = _arr(bias, np.float32)
+    if logits is None:
+        lg, given = np.empty((T, E), np.float32), 0
+    else:
+        lg, given = np.array(_arr(logits, np.float32), copy=True), 1
+    w6 = _weights(wts)
+    ad = [bf16_bits(lora[n]) for n in LORA_NAMES]
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    counts = np.empty(E, np.int32)
+    off = np.empty(n_local + 1, np.int32)
+    perm = np.empty(T * k, np.int32)
+    inv = np.empty((T, k), np.int32)
+    out = np.empty((T, d), np.float32)
+    A = lib().oracle_layer_lora(_ptr(xb), _ptr(w_router), _ptr(bias), _ptr(lg), given,
+                                T, d, E, k, I, e0, n_local, *[_ptr(a) for a in w6], act,
+                                *[_ptr(a) for a in ad], rank, float(scale),
+                                _ptr(idx), _ptr(w), _ptr(counts), _ptr(off), _ptr(perm),
+                                _ptr(inv), _ptr(out))
+    if A < 0:
+        raise MemoryError("oracle_layer_lora failed")
+    return dict(out=out, logits=lg, idx=idx, w=w, counts=counts, off=off,
+                perm=perm[:A], inv=inv, A=int(A))

@@ -42,6 +42,8 @@
  * on tie, clamp, zero and extreme-exponent blocks; the layer against a dense
  * fp64 evaluation with its own quantisation; closed forms of all-ones
  * weights whose h lands on the E4M3 grid, on a tie and on the 448 clamp.
+ * LoRA: zero B factors give the base layer bit for bit; the layer against a
+ * dense fp64 evaluation with W + scale * B A as each expert's weights.
  */
 #include <math.h>
 #include <stdint.h>
@@ -690,4 +692,108 @@ int oracle_token_rows_mx8(const uint16_t *x, int64_t d, int64_t I, int64_t k,
 {
     return token_rows_impl(x, d, I, k, idx, w, tokens, n_tokens, e0, n_local, gc, gs, uc, us,
                            dc, ds, act, 1, out_rows);
+}
+
+/* ------------------------------------------------------------------ */
+/* LoRA on the MXFP4 base (the low-rank increment of P1 §二 第五层)     */
+/* ------------------------------------------------------------------ */
+
+/* A projection with a LoRA delta: the frozen MXFP4 product plus scale times
+ * the low-rank increment, whose rank-r factor t = A v is taken first:
+ *   out[n] = sum_i v[i] W[n][i] + scale * sum_j t[j] B[n][j],
+ *   t[j] = sum_i v[i] A[j][i],
+ * in fp32 with sums in increasing index order. A [r][K] and B [N][r] are
+ * bf16 (widened exactly); W is decoded fp32 [N][K]. */
+static void lora_projection(const float *v, const float *W, const uint16_t *A,
+                            const uint16_t *B, int64_t N, int64_t K, int64_t r, float scale,
+                            float *t, float *out)
+{
+    for (int64_t j = 0; j < r; j++) {
+        float acc = 0.0f;
+        for (int64_t i = 0; i < K; i++) acc += v[i] * bf16_bits_to_float(A[j * K + i]);
+        t[j] = acc;
+    }
+    for (int64_t n = 0; n < N; n++) {
+        float base = 0.0f;
+        for (int64_t i = 0; i < K; i++) base += v[i] * W[n * K + i];
+        float delta = 0.0f;
+        for (int64_t j = 0; j < r; j++) delta += t[j] * bf16_bits_to_float(B[n * r + j]);
+        out[n] = base + scale * delta;
+    }
+}
+
+/* One expert's FFN with LoRA on all three projections (adapters of local
+ * expert le: gate/up A [r][d], B [I][r]; down A [r][I], B [d][r]). */
+static int expert_ffn_lora(const float *xt, const decoded_expert *we, const uint16_t *ga,
+                           const uint16_t *gb, const uint16_t *ua, const uint16_t *ub,
+                           const uint16_t *da, const uint16_t *db, int64_t le, int64_t d,
+                           int64_t I, int64_t r, float scale, int act, float *y)
+{
+    float *g = (float *)malloc((size_t)I * sizeof(float));
+    float *u = (float *)malloc((size_t)I * sizeof(float));
+    float *t = (float *)malloc((size_t)(r > 0 ? r : 1) * sizeof(float));
+    if (!g || !u || !t) {
+        free(g);
+        free(u);
+        free(t);
+        return -1;
+    }
+    lora_projection(xt, we->wg, ga + le * r * d, gb + le * I * r, I, d, r, scale, t, g);
+    lora_projection(xt, we->wu, ua + le * r * d, ub + le * I * r, I, d, r, scale, t, u);
+    for (int64_t n = 0; n < I; n++) g[n] = act_apply(act, g[n], u[n]);  /* g becomes h */
+    lora_projection(g, we->wd, da + le * r * I, db + le * d * r, d, I, r, scale, t, y);
+    free(g);
+    free(u);
+    free(t);
+    return 0;
+}
+
+/* The whole layer with LoRA adapters on every local expert's three
+ * projections (rank r, one scale), otherwise as oracle_layer. Adapters
+ * index local experts: gate_a/up_a [n_local][r][d], gate_b/up_b
+ * [n_local][I][r], down_a [n_local][r][I], down_b [n_local][d][r], bf16. */
+int64_t oracle_layer_lora(const uint16_t *x, const float *w_router, const float *bias,
+                          float *logits, int logits_given,
+                          int64_t T, int64_t d, int64_t E, int64_t k, int64_t I,
+                          int64_t e0, int64_t n_local,
+                          const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                          const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                          const uint16_t *ga, const uint16_t *gb, const uint16_t *ua,
+                          const uint16_t *ub, const uint16_t *da, const uint16_t *db, int64_t r,
+                          float scale, int32_t *idx, float *w, int32_t *counts, int32_t *off,
+                          int32_t *perm_token, int32_t *inv, float *out)
+{
+    if (!logits_given) oracle_router_logits(x, w_router, bias, T, d, E, logits);
+    oracle_topk_softmax(logits, T, E, k, idx, w);
+    oracle_histogram(idx, T, k, E, counts);
+    oracle_offsets(counts, e0, n_local, off);
+    oracle_permute(idx, off, T, k, e0, n_local, perm_token, inv);
+    int64_t A = off[n_local];
+    float *y = (float *)malloc((size_t)(A > 0 ? A : 1) * (size_t)d * sizeof(float));
+    float *xt = (float *)malloc((size_t)d * sizeof(float));
+    if (!y || !xt) {
+        free(y);
+        free(xt);
+        return -1;
+    }
+    int rc = 0;
+    for (int64_t le = 0; le < n_local && rc == 0; le++) {
+        if (off[le + 1] == off[le]) continue;
+        decoded_expert we;
+        if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) {
+            rc = -1;
+            break;
+        }
+        for (int64_t pos = off[le]; pos < off[le + 1] && rc == 0; pos++) {
+            int64_t tk = perm_token[pos];
+            for (int64_t i = 0; i < d; i++) xt[i] = bf16_bits_to_float(x[tk * d + i]);
+            rc = expert_ffn_lora(xt, &we, ga, gb, ua, ub, da, db, le, d, I, r, scale, act,
+                                 y + pos * d);
+        }
+        free_expert(&we);
+    }
+    if (rc == 0) oracle_combine(y, inv, w, T, k, d, out);
+    free(y);
+    free(xt);
+    return rc == 0 ? A : -1;
 }

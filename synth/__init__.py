@@ -14,5 +14,7 @@ from .gen import (  # noqa: F401
     make_router,
     make_tokens,
     make_expert_weights,
+    make_lora,
     quantize_mxfp4,
+    LORA_NAMES,
 )

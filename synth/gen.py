@@ -91,6 +91,7 @@ CONFIG_ORDER = ["tiny", "decode", "prefill", "ep_share", "long_skewed_prefill"]
 # Stream ids: one per tensor kind; experts add their global id.
 _S_TOKENS, _S_ROUTER, _S_BIAS = 1, 2, 3
 _S_GATE, _S_UP, _S_DOWN = 10, 11, 12
+_S_LORA = 20  # + 0..5: gate_a, gate_b, up_a, up_b, down_a, down_b
 
 
 def _gen(device, seed: int, stream: int, sub: int = 0) -> torch.Generator:
@@ -201,6 +202,26 @@ def make_expert_weights(cfg: LayerConfig, device="cpu", experts=None) -> Dict[st
             out[name + "_codes"][i].copy_(c)
             out[name + "_scales"][i].copy_(s)
             del w, c, s
+    return out
+
+
+LORA_NAMES = ("gate_a", "gate_b", "up_a", "up_b", "down_a", "down_b")
+
+
+def make_lora(cfg: LayerConfig, rank: int, device="cpu") -> Dict[str, torch.Tensor]:
+    """bf16 LoRA adapters of the local experts' three projections, rank r:
+    gate_a / up_a [n, r, d] ~ N(0, 1/d), gate_b / up_b [n, I, r] ~ N(0, 1/r),
+    down_a [n, r, I] ~ N(0, 1/I), down_b [n, d, r] ~ N(0, 1/r) (fp32 draws,
+    RNE to bf16). The low-rank increment of the frozen base is B A."""
+    n, I, d = cfg.num_local, cfg.I, cfg.d
+    shapes = {"gate_a": (n, rank, d), "gate_b": (n, I, rank), "up_a": (n, rank, d),
+              "up_b": (n, I, rank), "down_a": (n, rank, I), "down_b": (n, d, rank)}
+    fan = {"gate_a": d, "gate_b": rank, "up_a": d, "up_b": rank, "down_a": I, "down_b": rank}
+    out = {}
+    for i, name in enumerate(LORA_NAMES):
+        g = _gen(device, cfg.seed, _S_LORA + i, rank)
+        w = torch.randn(*shapes[name], generator=g, device=device, dtype=torch.float32)
+        out[name] = (w / math.sqrt(fan[name])).to(torch.bfloat16)
     return out
 
 
