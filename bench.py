@@ -44,6 +44,9 @@ def parse():
                     help="bf16: bf16 tokens and h against MXFP4 weights (the pages' layer); "
                          "mx8: tokens and h rounded to MXFP8 for the block-scaled fp8 x fp4 "
                          "matrix instruction (a separate accuracy contract)")
+    ap.add_argument("--lora-rank", type=int, default=0,
+                    help="> 0: the layer with rank-R LoRA adapters (scale 0.5) on every local "
+                         "expert's three projections (moe_layer_lora; bf16 precision only)")
     ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens the oracle CPU baseline evaluates (0 = skip)")
     ap.add_argument("--weights", default="packed", choices=["packed", "ocp"],
@@ -211,7 +214,19 @@ def main():
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
+    if args.lora_rank > 0:
+        if mx8:
+            print(json.dumps({"error": "LoRA runs in the bf16 precision only"}))
+            sys.exit(2)
+        from synth import make_lora
+        lora = make_lora(cfg, args.lora_rank, dev)
+        ws = m.alloc_workspace(m.moe_layer_lora_workspace_size(p, args.lora_rank), dev)
+
     def step(ev=None):
+        if args.lora_rank > 0:
+            m.moe_layer_lora(p, lora, args.lora_rank, 0.5, inp.x, inp.w_router, inp.bias,
+                             layer_weights, out, ws, topk_idx_out=idx, stage_events=ev)
+            return
         m.moe_layer(p, inp.x, inp.w_router, inp.bias, layer_weights, out, ws, topk_idx_out=idx,
                     stage_events=ev)
 
@@ -260,7 +275,15 @@ def main():
     # bound) for few rows per expert, a tiled bf16 GEMM (MFMA bound) otherwise.
     gu_s = stage_ms["gate_up"] / 1e3
     sched = m.moe_grouped_gemm_schedule(cfg.num_local, cfg.T * cfg.k, args.mode)
-    if mx8:
+    if args.lora_rank > 0:
+        # unfused: two frozen projections, their increments and the activation
+        roof = {"kernel": f"gate/up stage with rank-{args.lora_rank} LoRA (unfused)",
+                "bound": "mfma", "achieved": round(gf / gu_s / 1e12, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": int(gf),
+                "avg_launch_ms": round(stage_ms["gate_up"], 4)}
+    elif mx8:
         # the stage is the token quantiser plus the block-scaled GEMM
         roof = {"kernel": "mxfp8_quantize_kernel + gemm_mx8_kernel<SILU_MUL> (gate/up stage)",
                 "bound": "mfma", "achieved": round(gf / gu_s / 1e12, 1), "peak": FP8_PEAK_TFLOPS,
@@ -298,7 +321,7 @@ def main():
                    "I": cfg.I, "experts_computed": cfg.num_local,
                    "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
                    "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else "bf16",
-                   "routing_bias": cfg.bias},
+                   "lora_rank": args.lora_rank, "routing_bias": cfg.bias},
         "roofline": roof,
         "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),
                   "algorithmic_bytes": int(lb), "algorithmic_flops": int(lf),
@@ -310,7 +333,7 @@ def main():
                   "ms_per_step_with_stage_events": round(ms_step_staged, 4)},
         "cpu_baseline": None,
     }
-    if args.cpu_tokens > 0:
+    if args.cpu_tokens > 0 and args.lora_rank == 0:
         inp.weights = canonical
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens, mx8=mx8)
     print(json.dumps(res), flush=True)

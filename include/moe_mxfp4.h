@@ -332,6 +332,53 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
               void *out, float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
               size_t ws_bytes, void **stage_events, moe_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * LoRA on the MXFP4 base (P1 section 二, 第五层: the large quantised base
+ * stays frozen and a low-rank increment is trained on top of it).
+ * ------------------------------------------------------------------------ */
+#define MOE_MAX_LORA_RANK 64
+
+/* moe_grouped_lora -- the increment of one grouped projection, added to its
+ * fp32 output. For local expert e and each row r in [off[e], off[e+1]):
+ *   t[j]    = scale * sum_k x_row(r)[k] * A_e[j][k]     (j < rank)
+ *   y[r][n] += sum_j t[j] * B_e[n][j]                    (n < N)
+ * x_row(r) = x + (x_rows ? x_rows[r] : r) * ldx (bf16, K elements);
+ * lora_a [num_local][rank][K], lora_b [num_local][N][rank] bf16; y fp32
+ * [rows][ldy]; fp32 accumulation. ws holds
+ * moe_grouped_lora_workspace_size(max_rows, rank) bytes (the rank factors).
+ * Errors: rank outside 1..MOE_MAX_LORA_RANK, K % 8 != 0 or N % 4 != 0 ->
+ * UNSUPPORTED; ldx < K or not a multiple of 8, ldy < N or not a multiple of
+ * 4, NULL or misaligned (16-byte x, lora_a, y) pointers -> INVALID_ARG. */
+size_t moe_grouped_lora_workspace_size(int max_rows, int rank);
+int moe_grouped_lora(const void *x, int64_t ldx, const int32_t *x_rows, const void *lora_a,
+                     const void *lora_b, int rank, float scale, const int32_t *expert_offsets,
+                     int num_local, int max_rows, int N, int K, float *y, int64_t ldy, void *ws,
+                     size_t ws_bytes, moe_stream_t stream);
+
+/* Adapters of every local expert's three projections (bf16, device):
+ *   gate_a, up_a [num_local][rank][d]   gate_b, up_b [num_local][I][rank]
+ *   down_a [num_local][rank][I]         down_b [num_local][d][rank]
+ * Each projection becomes W v + scale * B (A v). */
+typedef struct {
+    int rank;
+    float scale;
+    const void *gate_a, *gate_b, *up_a, *up_b, *down_a, *down_b;
+} moe_lora_adapters;
+
+/* moe_layer_lora -- moe_layer with the adapters applied (bf16 precision
+ * only). The gate and up projections run unfused (fp32 outputs, the
+ * increments, then the activation), since the increment must land before the
+ * activation. Workspace: moe_layer_lora_workspace_size(p, rank) bytes (0 if
+ * invalid). Errors as moe_layer, plus a NULL lora or adapter -> INVALID_ARG,
+ * rank outside 1..MOE_MAX_LORA_RANK or the MX8 precision -> UNSUPPORTED. */
+size_t moe_layer_lora_workspace_size(const moe_layer_params *p, int rank);
+int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, const void *x,
+                   const float *w_router, const float *bias, const uint8_t *gate_codes,
+                   const uint8_t *gate_scales, const uint8_t *up_codes, const uint8_t *up_scales,
+                   const uint8_t *down_codes, const uint8_t *down_scales, void *out,
+                   float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                   size_t ws_bytes, void **stage_events, moe_stream_t stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(int status);
 /* The calling thread's last HIP error message ("" if none). */

@@ -75,6 +75,15 @@ def _load(path=None):
     L.moe_mxfp8_quantize.argtypes = [p, i32, i64, i64, i32, p, p, p]
     L.moe_grouped_gemm_mx8_workspace_size.restype = sz
     L.moe_grouped_gemm_mx8_workspace_size.argtypes = [i32, i32]
+    L.moe_grouped_lora_workspace_size.restype = sz
+    L.moe_grouped_lora_workspace_size.argtypes = [i32, i32]
+    L.moe_grouped_lora.restype = i32
+    L.moe_grouped_lora.argtypes = [p, i64, p, p, p, i32, C.c_float, p, i32, i32, i32, i32, p,
+                                   i64, p, sz, p]
+    L.moe_layer_lora_workspace_size.restype = sz
+    L.moe_layer_lora_workspace_size.argtypes = [p, i32]
+    L.moe_layer_lora.restype = i32
+    L.moe_layer_lora.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, sz, p, p]
     L.moe_grouped_gemm_mx8.restype = i32
     L.moe_grouped_gemm_mx8.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                        i32, p, i32, p, i64, i32, p, sz, p]
@@ -89,7 +98,9 @@ EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4
             "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size",
             "moe_grouped_gemm_schedule", "moe_combine",
             "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error",
-            "moe_mxfp8_quantize", "moe_grouped_gemm_mx8", "moe_grouped_gemm_mx8_workspace_size")
+            "moe_mxfp8_quantize", "moe_grouped_gemm_mx8", "moe_grouped_gemm_mx8_workspace_size",
+            "moe_grouped_lora", "moe_grouped_lora_workspace_size", "moe_layer_lora",
+            "moe_layer_lora_workspace_size")
 
 
 class LayerParams(C.Structure):
@@ -399,11 +410,9 @@ def moe_layer_workspace_size(params: LayerParams) -> int:
     return n
 
 
-def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_out=None,
-              topk_idx_out=None, topk_w_out=None, stage_events=None, stream=None):
-    """The fused layer. ``weights`` holds gate/up/down codes and scales
-    (local experts stacked). ``stage_events``: None or 6 torch.cuda.Event."""
-    p = params
+def _layer_args(p, x, w_router, bias, weights, out, ws, logits_out, topk_idx_out, topk_w_out,
+                stage_events, stream):
+    """Checks of the layer's tensors; returns (byte count of ws, event array)."""
     _dev(x, w_router, bias, out, ws, logits_out, topk_idx_out, topk_w_out,
          *[weights[n] for n in _WNAMES])
     _want(x, torch.bfloat16, (p.T, p.d), "x")
@@ -433,6 +442,16 @@ def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_o
         for e_ in stage_events:
             e_.record(torch.cuda.current_stream() if stream is None else stream)  # materialise
         ev = (C.c_void_p * 6)(*[e_.cuda_event for e_ in stage_events])
+    return nbytes, ev
+
+
+def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_out=None,
+              topk_idx_out=None, topk_w_out=None, stage_events=None, stream=None):
+    """The fused layer. ``weights`` holds gate/up/down codes and scales
+    (local experts stacked). ``stage_events``: None or 6 torch.cuda.Event."""
+    p = params
+    nbytes, ev = _layer_args(p, x, w_router, bias, weights, out, ws, logits_out, topk_idx_out,
+                             topk_w_out, stage_events, stream)
     st = lib.moe_layer(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
                        *[_ptr(weights[n]) for n in _WNAMES], _ptr(out), _ptr(logits_out),
                        _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), nbytes, ev,
@@ -448,3 +467,65 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     ws = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
     assert ws.data_ptr() % 256 == 0
     return ws
+
+
+# ---------------------------------------------------------------- LoRA
+LORA_NAMES = ("gate_a", "gate_b", "up_a", "up_b", "down_a", "down_b")
+
+
+class LoraAdapters(C.Structure):
+    _fields_ = [("rank", C.c_int), ("scale", C.c_float)] + [(n, C.c_void_p) for n in LORA_NAMES]
+
+
+def moe_grouped_lora_workspace_size(max_rows, rank):
+    return int(lib.moe_grouped_lora_workspace_size(max_rows, rank))
+
+
+def moe_grouped_lora(x, x_rows, lora_a, lora_b, scale, expert_offsets, max_rows, y, ws,
+                     stream=None):
+    """y[r] += scale * (x_row(r) @ A_e.T) @ B_e.T for the rows r of each local
+    expert e: x bf16 [rows, K], lora_a [num_local, rank, K], lora_b
+    [num_local, N, rank] bf16, y fp32 [>= max_rows, N]."""
+    num_local, rank, K = lora_a.shape
+    N = lora_b.shape[1]
+    _dev(x, x_rows, lora_a, lora_b, expert_offsets, y, ws)
+    _want(x, torch.bfloat16, (x.shape[0], K), "x")
+    _want(lora_b, torch.bfloat16, (num_local, N, rank), "lora_b")
+    if lora_a.dtype != torch.bfloat16:
+        raise TypeError("lora_a must be bf16")
+    if y.dtype != torch.float32 or y.dim() != 2 or y.shape[1] != N or y.shape[0] < max_rows:
+        raise ValueError("y must be fp32 [>= max_rows, N]")
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("moe_grouped_lora", lib.moe_grouped_lora(
+        _ptr(x), K, _ptr(x_rows), _ptr(lora_a), _ptr(lora_b), rank, float(scale),
+        _ptr(expert_offsets), num_local, max_rows, N, K, _ptr(y), N, _ptr(ws), nbytes,
+        _stream(stream)))
+
+
+def moe_layer_lora_workspace_size(params: LayerParams, rank) -> int:
+    n = int(lib.moe_layer_lora_workspace_size(C.byref(params), rank))
+    if n == 0:
+        raise MoeError("moe_layer_lora_workspace_size", MOE_ERR_INVALID_ARG, "invalid parameters")
+    return n
+
+
+def moe_layer_lora(params: LayerParams, lora, rank, scale, x, w_router, bias, weights, out, ws,
+                   logits_out=None, topk_idx_out=None, topk_w_out=None, stage_events=None,
+                   stream=None):
+    """moe_layer with LoRA adapters (``lora`` maps gate_a .. down_b to bf16
+    tensors of the shapes in the header) on every local expert projection."""
+    p = params
+    nbytes, ev = _layer_args(p, x, w_router, bias, weights, out, ws, logits_out, topk_idx_out,
+                             topk_w_out, stage_events, stream)
+    shapes = {"gate_a": (p.num_local, rank, p.d), "gate_b": (p.num_local, p.I, rank),
+              "up_a": (p.num_local, rank, p.d), "up_b": (p.num_local, p.I, rank),
+              "down_a": (p.num_local, rank, p.I), "down_b": (p.num_local, p.d, rank)}
+    _dev(*[lora[n] for n in LORA_NAMES])
+    for n in LORA_NAMES:
+        _want(lora[n], torch.bfloat16, shapes[n], n)
+    ad = LoraAdapters(rank, float(scale), *[_ptr(lora[n]) for n in LORA_NAMES])
+    st = lib.moe_layer_lora(C.byref(p), C.byref(ad), _ptr(x), _ptr(w_router), _ptr(bias),
+                            *[_ptr(weights[n]) for n in _WNAMES], _ptr(out), _ptr(logits_out),
+                            _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), nbytes, ev,
+                            _stream(stream))
+    _check("moe_layer_lora", st)

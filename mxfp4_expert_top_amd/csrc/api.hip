@@ -152,6 +152,35 @@ LayerWs layer_ws(const moe_layer_params *p)
     return L;
 }
 
+// Router scores, top-k and softmax of the layer. With split-K planes the
+// top-k kernel adds them in a fixed order, then the bias. No expert histogram:
+// the permute kernels count each expert's rows from their dispatch bitmaps (a
+// histogram of skewed routing would serialise atomics on the hot experts).
+hipError_t layer_route(const moe_layer_params *p, const LayerWs &L, char *base, const void *x,
+                       const float *w_router, const float *bias, float *logits, int32_t *idx,
+                       float *w, hipStream_t s)
+{
+    float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
+    const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
+    hipError_t e;
+    if (L.router == ROUTER_TILED) {
+        bf16 *wp = (bf16 *)(base + L.wsplit);
+        e = launch_split_router(w_router, p->E, p->d, wp, s);
+        if (e != hipSuccess) return e;
+        e = launch_router_tile((const bf16 *)x, wp, b_in_gemm, planes, p->T, p->d, p->E,
+                               L.splits, nullptr, s);
+    } else if (L.router == ROUTER_SMALL) {
+        e = launch_router_logits((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d, p->E,
+                                 L.splits, nullptr, s);
+    } else {
+        e = launch_router_skinny((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d, p->E,
+                                 L.splits, nullptr, s);
+    }
+    if (e != hipSuccess) return e;
+    return launch_topk_softmax(planes, L.splits, bias, logits, p->T, p->E, p->k, idx, w, nullptr,
+                               s);
+}
+
 int check_layer_params(const moe_layer_params *p)
 {
     CHECK(p, MOE_ERR_INVALID_ARG);
@@ -446,28 +475,9 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     hipEvent_t *ev = (hipEvent_t *)stage_events;
 
     if (ev) HIP_TRY(hipEventRecord(ev[0], s));
-    // With split-K planes the top-k kernel adds them in a fixed order, then the
-    // bias. No expert histogram here: the permute kernels count each expert's
-    // rows from their dispatch bitmaps (a histogram of skewed routing would
-    // serialise atomics on the hot experts).
-    int32_t *counts = nullptr;
-    float *planes = L.splits > 1 ? (float *)(base + L.planes) : logits;
-    const float *b_in_gemm = L.splits > 1 ? nullptr : bias;
-    if (L.router == ROUTER_TILED) {
-        bf16 *wp = (bf16 *)(base + L.wsplit);
-        HIP_TRY(launch_split_router(w_router, p->E, p->d, wp, s));
-        HIP_TRY(launch_router_tile((const bf16 *)x, wp, b_in_gemm, planes, p->T, p->d, p->E,
-                                   L.splits, counts, s));
-    } else if (L.router == ROUTER_SMALL) {
-        HIP_TRY(launch_router_logits((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
-                                     p->E, L.splits, counts, s));
-    } else {
-        HIP_TRY(launch_router_skinny((const bf16 *)x, w_router, b_in_gemm, planes, p->T, p->d,
-                                     p->E, L.splits, counts, s));
-    }
-    HIP_TRY(launch_topk_softmax(planes, L.splits, bias, logits, p->T, p->E, p->k, idx, w, counts,
-                                s));
+    HIP_TRY(layer_route(p, L, base, x, w_router, bias, logits, idx, w, s));
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    int32_t *counts = nullptr;
     // one work plan serves both projections (same offsets, bound and schedule)
     const GemmPlanArgs plan = gemm_plan_args(p->num_local, A, p->mode, base + L.gws);
     if (p->precision == MOE_PREC_MX8) {
@@ -510,6 +520,147 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
                             p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
                             base + L.gws, packed, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+    HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                           p->out_dtype == MOE_DT_F32, p->d, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[5], s));
+    return MOE_OK;
+}
+
+size_t moe_grouped_lora_workspace_size(int max_rows, int rank)
+{
+    if (max_rows < 0 || rank < 1 || rank > MOE_MAX_LORA_RANK) return 0;
+    return lora_ws_bytes(max_rows, rank);
+}
+
+int moe_grouped_lora(const void *x, int64_t ldx, const int32_t *x_rows, const void *lora_a,
+                     const void *lora_b, int rank, float scale, const int32_t *expert_offsets,
+                     int num_local, int max_rows, int N, int K, float *y, int64_t ldy, void *ws,
+                     size_t ws_bytes, moe_stream_t stream)
+{
+    CHECK(num_local >= 1 && max_rows >= 0 && N >= 1 && K >= 1, MOE_ERR_INVALID_ARG);
+    CHECK(rank >= 1 && rank <= MOE_MAX_LORA_RANK, MOE_ERR_UNSUPPORTED);
+    CHECK(K % 8 == 0 && N % 4 == 0, MOE_ERR_UNSUPPORTED);
+    if (max_rows == 0) return MOE_OK;
+    CHECK(x && lora_a && lora_b && expert_offsets && y, MOE_ERR_INVALID_ARG);
+    CHECK(ldx >= K && ldx % 8 == 0 && ldy >= N && ldy % 4 == 0, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(x, 16) && aligned(lora_a, 16) && aligned(y, 16), MOE_ERR_INVALID_ARG);
+    int rc = check_ws(ws, ws_bytes, lora_ws_bytes(max_rows, rank));
+    if (rc) return rc;
+    HIP_TRY(launch_lora((const bf16 *)x, ldx, x_rows, (const bf16 *)lora_a,
+                        (const bf16 *)lora_b, rank, scale, expert_offsets, num_local, max_rows, N,
+                        K, y, ldy, (float *)ws, as_stream(stream)));
+    return MOE_OK;
+}
+
+namespace {
+// moe_layer's workspace plus fp32 gate and up projections and the rank factor
+struct LoraWs {
+    LayerWs L;
+    size_t g, u, t, total;
+};
+
+LoraWs lora_layer_ws(const moe_layer_params *p, int rank)
+{
+    LoraWs W;
+    W.L = layer_ws(p);
+    const size_t A = (size_t)p->T * p->k;
+    size_t o = W.L.total;
+    W.g = o; o += round_up(A * (size_t)p->I * 4);
+    W.u = o; o += round_up(A * (size_t)p->I * 4);
+    W.t = o; o += lora_ws_bytes((int)A, rank);
+    W.total = o;
+    return W;
+}
+
+int check_lora(const moe_layer_params *p, const moe_lora_adapters *lora)
+{
+    CHECK(lora, MOE_ERR_INVALID_ARG);
+    CHECK(lora->rank >= 1 && lora->rank <= MOE_MAX_LORA_RANK, MOE_ERR_UNSUPPORTED);
+    CHECK(p->precision == MOE_PREC_BF16, MOE_ERR_UNSUPPORTED);
+    return MOE_OK;
+}
+}  // namespace
+
+size_t moe_layer_lora_workspace_size(const moe_layer_params *p, int rank)
+{
+    if (check_layer_params(p) != MOE_OK || p->precision != MOE_PREC_BF16 || rank < 1 ||
+        rank > MOE_MAX_LORA_RANK)
+        return 0;
+    return lora_layer_ws(p, rank).total;
+}
+
+int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, const void *x,
+                   const float *w_router, const float *bias, const uint8_t *gate_codes,
+                   const uint8_t *gate_scales, const uint8_t *up_codes, const uint8_t *up_scales,
+                   const uint8_t *down_codes, const uint8_t *down_scales, void *out,
+                   float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+                   size_t ws_bytes, void **stage_events, moe_stream_t stream)
+{
+    int rc = check_layer_params(p);
+    if (rc) return rc;
+    rc = check_lora(p, lora);
+    if (rc) return rc;
+    if (p->T == 0) return MOE_OK;
+    CHECK(x && w_router && out && gate_codes && gate_scales && up_codes && up_scales &&
+              down_codes && down_scales,
+          MOE_ERR_INVALID_ARG);
+    CHECK(lora->gate_a && lora->gate_b && lora->up_a && lora->up_b && lora->down_a &&
+              lora->down_b,
+          MOE_ERR_INVALID_ARG);
+    CHECK(aligned(x, 16) && aligned(out, 16) && aligned(w_router, 16), MOE_ERR_INVALID_ARG);
+    CHECK(aligned(gate_codes, 16) && aligned(up_codes, 16) && aligned(down_codes, 16) &&
+              aligned(gate_scales, 16) && aligned(up_scales, 16) && aligned(down_scales, 16),
+          MOE_ERR_INVALID_ARG);
+    CHECK(aligned(lora->gate_a, 16) && aligned(lora->up_a, 16) && aligned(lora->down_a, 16),
+          MOE_ERR_INVALID_ARG);
+    const LoraWs W = lora_layer_ws(p, lora->rank);
+    const LayerWs &L = W.L;
+    rc = check_ws(ws, ws_bytes, W.total);
+    if (rc) return rc;
+
+    char *base = (char *)ws;
+    float *logits = logits_out ? logits_out : (float *)(base + L.logits);
+    int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + L.idx);
+    float *w = topk_w_out ? topk_w_out : (float *)(base + L.w);
+    int32_t *off = (int32_t *)(base + L.off);
+    int32_t *perm = (int32_t *)(base + L.perm);
+    int32_t *inv = (int32_t *)(base + L.inv);
+    bf16 *h = (bf16 *)(base + L.h);
+    float *y = (float *)(base + L.y);
+    float *g32 = (float *)(base + W.g), *u32 = (float *)(base + W.u), *t = (float *)(base + W.t);
+    const int A = p->T * p->k, nl = p->num_local, r = lora->rank;
+    const float sc = lora->scale;
+    const int packed = p->weight_layout == MOE_LAYOUT_PACKED;
+    hipStream_t s = as_stream(stream);
+    hipEvent_t *ev = (hipEvent_t *)stage_events;
+
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    HIP_TRY(layer_route(p, L, base, x, w_router, bias, logits, idx, w, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+    const GemmPlanArgs plan = gemm_plan_args(nl, A, p->mode, base + L.gws);
+    HIP_TRY(launch_permute(idx, nullptr, p->T, p->k, p->expert_begin, nl, off, perm, inv,
+                           base + L.pws, s, &plan));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    // gate and up: the frozen projections, each plus its low-rank increment,
+    // then the activation (the increment must land before it)
+    const bf16 *xb = (const bf16 *)x;
+    HIP_TRY(launch_gemm_run(xb, p->d, perm, gate_codes, gate_scales, nullptr, nullptr, nl, A,
+                            p->I, p->d, MOE_ACT_NONE, g32, 1, p->I, p->mode, base + L.gws, packed,
+                            s));
+    HIP_TRY(launch_gemm_run(xb, p->d, perm, up_codes, up_scales, nullptr, nullptr, nl, A, p->I,
+                            p->d, MOE_ACT_NONE, u32, 1, p->I, p->mode, base + L.gws, packed, s));
+    HIP_TRY(launch_lora(xb, p->d, perm, (const bf16 *)lora->gate_a, (const bf16 *)lora->gate_b,
+                        r, sc, off, nl, A, p->I, p->d, g32, p->I, t, s));
+    HIP_TRY(launch_lora(xb, p->d, perm, (const bf16 *)lora->up_a, (const bf16 *)lora->up_b, r,
+                        sc, off, nl, A, p->I, p->d, u32, p->I, t, s));
+    HIP_TRY(launch_glu(g32, u32, off, nl, A, p->I, p->act, h, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr, nl, A,
+                            p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode, base + L.gws, packed,
+                            s));
+    HIP_TRY(launch_lora(h, p->I, nullptr, (const bf16 *)lora->down_a, (const bf16 *)lora->down_b,
+                        r, sc, off, nl, A, p->d, p->I, y, p->d, t, s));
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));
     HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
                            p->out_dtype == MOE_DT_F32, p->d, s));

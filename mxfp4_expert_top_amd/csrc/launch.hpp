@@ -128,6 +128,17 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
                                    int out_kind, uint8_t *out_scales, int64_t ldo, int mode,
                                    void *ws, int packed, hipStream_t s);
 
+// lora.hip: the low-rank increment on a frozen projection (y += t B_e^T with
+// t = scale x A_e^T, rows grouped by expert); t is [max_rows][rank] fp32
+size_t lora_ws_bytes(int max_rows, int rank);
+hipError_t launch_lora(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *la,
+                       const bf16 *lb, int rank, float scale, const int32_t *off, int nl,
+                       int max_rows, int N, int K, float *y, int64_t ldy, float *t,
+                       hipStream_t s);
+// h = act(g, u) over the first off[nl] rows of [*, I] fp32 arrays, bf16 out
+hipError_t launch_glu(const float *g, const float *u, const int32_t *off, int nl, int max_rows,
+                      int I, int act, bf16 *h, hipStream_t s);
+
 // prepack.hip: the streaming weight layout (see prepack.hip) and the fp32 ->
 // MXFP4 quantiser (canonical layout out)
 hipError_t launch_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes,

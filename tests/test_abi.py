@@ -212,6 +212,41 @@ def test_mx8_validation():
     assert L.moe_layer_workspace_size(C.byref(bad)) == 0
 
 
+def test_lora_validation():
+    L = m.lib
+
+    def glora(**kw):
+        a = dict(x=FAKE, ldx=256, rows=None, la=FAKE, lb=FAKE, rank=16, scale=C.c_float(0.5),
+                 off=FAKE, nl=4, maxr=64, N=128, K=256, y=FAKE, ldy=128, ws=FAKE,
+                 wsb=m.moe_grouped_lora_workspace_size(64, 16))
+        a.update(kw)
+        return L.moe_grouped_lora(*a.values(), None)
+    assert glora(rank=0) == 2 and glora(rank=65) == 2
+    assert glora(K=260, ldx=264) == 2          # K % 8
+    assert glora(N=130, ldy=132) == 2          # N % 4
+    assert glora(ldx=200) == 1                 # ldx < K
+    assert glora(ldy=130) == 1                 # ldy % 4
+    assert glora(la=None) == 1
+    assert glora(x=C.c_void_p(0x10004)) == 1   # misaligned
+    assert glora(wsb=16) == 3
+    assert glora(maxr=0, x=None, la=None, lb=None, off=None, y=None, ws=None, wsb=0) == 0
+    assert m.moe_grouped_lora_workspace_size(64, 65) == 0
+    p = m.layer_params(8, 3584, 896, 16, 128)
+    assert m.moe_layer_lora_workspace_size(p, 16) > m.moe_layer_workspace_size(p)
+    assert L.moe_layer_lora_workspace_size(C.byref(p), 0) == 0
+    mx8 = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8)
+    assert L.moe_layer_lora_workspace_size(C.byref(mx8), 16) == 0
+    ad = m.LoraAdapters(16, 0.5, *([None] * 6))
+    # no adapters -> INVALID_ARG (checked before any pointer is used)
+    assert L.moe_layer_lora(C.byref(p), C.byref(ad), *([FAKE] * 10), None, None, None, FAKE,
+                            1 << 30, None, None) == 1
+    assert L.moe_layer_lora(C.byref(p), None, *([FAKE] * 10), None, None, None, FAKE,
+                            1 << 30, None, None) == 1
+    ad2 = m.LoraAdapters(100, 0.5, *([FAKE.value] * 6))
+    assert L.moe_layer_lora(C.byref(p), C.byref(ad2), *([FAKE] * 10), None, None, None, FAKE,
+                            1 << 30, None, None) == 2
+
+
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
