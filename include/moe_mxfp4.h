@@ -366,11 +366,14 @@ typedef struct {
 } moe_lora_adapters;
 
 /* moe_layer_lora -- moe_layer with the adapters applied (bf16 precision
- * only). The gate and up projections run unfused (fp32 outputs, the
- * increments, then the activation), since the increment must land before the
- * activation. Workspace: moe_layer_lora_workspace_size(p, rank) bytes (0 if
- * invalid). Errors as moe_layer, plus a NULL lora or adapter -> INVALID_ARG,
- * rank outside 1..MOE_MAX_LORA_RANK or the MX8 precision -> UNSUPPORTED. */
+ * only). The increment must land before the activation. With a tiled
+ * schedule and a rank that is a multiple of 16 it is added inside the grouped
+ * GEMMs, from rank factors rounded to bf16; otherwise the gate and up
+ * projections run unfused (fp32 outputs, the increments, then the
+ * activation). Workspace: moe_layer_lora_workspace_size(p, rank) bytes (0 if
+ * invalid). Errors as moe_layer, plus a NULL lora or adapter, or an adapter
+ * not 16-byte aligned -> INVALID_ARG, rank outside 1..MOE_MAX_LORA_RANK or
+ * the MX8 precision -> UNSUPPORTED. */
 size_t moe_layer_lora_workspace_size(const moe_layer_params *p, int rank);
 int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, const void *x,
                    const float *w_router, const float *bias, const uint8_t *gate_codes,

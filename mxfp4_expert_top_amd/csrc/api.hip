@@ -560,15 +560,30 @@ struct LoraWs {
     size_t g, u, t, total;
 };
 
+// The increment rides in the tiled GEMMs' epilogue (rank factors in bf16)
+// when the schedule is tiled and the rank a multiple of 16; otherwise the
+// gate and up projections run unfused.
+bool lora_fused(const moe_layer_params *p, int rank)
+{
+    const int md = resolve_mode(p->mode, p->num_local, p->T * p->k);
+    return rank % 16 == 0 && (md == MOE_SCHED_TILE128 || md == MOE_SCHED_TILE256);
+}
+
 LoraWs lora_layer_ws(const moe_layer_params *p, int rank)
 {
     LoraWs W;
     W.L = layer_ws(p);
     const size_t A = (size_t)p->T * p->k;
     size_t o = W.L.total;
-    W.g = o; o += round_up(A * (size_t)p->I * 4);
-    W.u = o; o += round_up(A * (size_t)p->I * 4);
-    W.t = o; o += lora_ws_bytes((int)A, rank);
+    if (lora_fused(p, rank)) {
+        // three bf16 rank-factor arrays (gate, up, down)
+        W.g = W.u = 0;
+        W.t = o; o += 3 * round_up(A * (size_t)rank * 2);
+    } else {
+        W.g = o; o += round_up(A * (size_t)p->I * 4);
+        W.u = o; o += round_up(A * (size_t)p->I * 4);
+        W.t = o; o += lora_ws_bytes((int)A, rank);
+    }
     W.total = o;
     return W;
 }
@@ -612,7 +627,8 @@ int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, con
     CHECK(aligned(gate_codes, 16) && aligned(up_codes, 16) && aligned(down_codes, 16) &&
               aligned(gate_scales, 16) && aligned(up_scales, 16) && aligned(down_scales, 16),
           MOE_ERR_INVALID_ARG);
-    CHECK(aligned(lora->gate_a, 16) && aligned(lora->up_a, 16) && aligned(lora->down_a, 16),
+    CHECK(aligned(lora->gate_a, 16) && aligned(lora->up_a, 16) && aligned(lora->down_a, 16) &&
+              aligned(lora->gate_b, 16) && aligned(lora->up_b, 16) && aligned(lora->down_b, 16),
           MOE_ERR_INVALID_ARG);
     const LoraWs W = lora_layer_ws(p, lora->rank);
     const LayerWs &L = W.L;
@@ -642,9 +658,34 @@ int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, con
     HIP_TRY(launch_permute(idx, nullptr, p->T, p->k, p->expert_begin, nl, off, perm, inv,
                            base + L.pws, s, &plan));
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
-    // gate and up: the frozen projections, each plus its low-rank increment,
-    // then the activation (the increment must land before it)
     const bf16 *xb = (const bf16 *)x;
+    if (lora_fused(p, r)) {
+        // rank factors first (bf16), then the projections with the increment
+        // added to their accumulators before the activation / output
+        const size_t tb = round_up((size_t)A * r * 2);
+        bf16 *tg = (bf16 *)(base + W.t), *tu = (bf16 *)(base + W.t + tb),
+             *td = (bf16 *)(base + W.t + 2 * tb);
+        HIP_TRY(launch_lora_t_plan(xb, p->d, perm, (const bf16 *)lora->gate_a,
+                                   (const bf16 *)lora->up_a, r, p->d, sc, plan, tg, tu, s));
+        const LoraEpi lg{tg, tu, (const bf16 *)lora->gate_b, (const bf16 *)lora->up_b, r};
+        HIP_TRY(launch_gemm_run(xb, p->d, perm, gate_codes, gate_scales, up_codes, up_scales, nl,
+                                A, p->I, p->d, p->act, h, 0, p->I, p->mode, base + L.gws, packed,
+                                s, &lg));
+        if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+        HIP_TRY(launch_lora_t_plan(h, p->I, nullptr, (const bf16 *)lora->down_a, nullptr, r, p->I,
+                                   sc, plan, td, nullptr, s));
+        const LoraEpi ld{td, nullptr, (const bf16 *)lora->down_b, nullptr, r};
+        HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr, nl,
+                                A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode, base + L.gws,
+                                packed, s, &ld));
+        if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+        HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                               p->out_dtype == MOE_DT_F32, p->d, s));
+        if (ev) HIP_TRY(hipEventRecord(ev[5], s));
+        return MOE_OK;
+    }
+    // gate and up unfused: the frozen projections, each plus its low-rank
+    // increment, then the activation (the increment must land before it)
     HIP_TRY(launch_gemm_run(xb, p->d, perm, gate_codes, gate_scales, nullptr, nullptr, nl, A,
                             p->I, p->d, MOE_ACT_NONE, g32, 1, p->I, p->mode, base + L.gws, packed,
                             s));

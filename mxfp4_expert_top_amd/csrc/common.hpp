@@ -10,6 +10,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace moe {
@@ -25,6 +26,15 @@ constexpr int kWave = 64;
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D = A * B + C on one 32x32 fp32 tile with K = 16 bf16 products. Lane L
+// supplies row (L % 32) of A and column (L % 32) of B, 8 consecutive
+// contraction elements of the half L / 32 (same freedom of mapping as above).
+// Result: lane L holds C[8 (v / 4) + 4 (L / 32) + v % 4][L % 32], v = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // E8M0 scale code -> fp32 2^(s-127). Code 0 is the fp32 subnormal 2^-127.

@@ -262,11 +262,19 @@ constexpr int TL_THREADS = 512;
 constexpr int TL_APAD = 8;                   // bf16 pad per A row in LDS
 constexpr int TL_ALD = TL_BK + TL_APAD;      // 72 bf16 = 144 bytes per row
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+// acc += T[trow][0..rank) . B[bcol][0..rank) over a 32 x 32 tile: the MFMA
+// operand of lane L is row (A) or column (B) L % 32 with contraction elements
+// 8 (L / 32) .. + 8 of each 16-wide step, which is how both factors are
+// stored (rank contiguous per row / per weight row).
+__device__ __forceinline__ f32x16 lora_add(f32x16 acc, const bf16 *t, int64_t trow,
+                                           const bf16 *b, int64_t bcol, int rank, int h)
 {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    for (int k0 = 0; k0 < rank; k0 += 16) {
+        const bf16x8 af = *(const bf16x8 *)(t + trow * rank + k0 + 8 * h);
+        const bf16x8 bv = *(const bf16x8 *)(b + bcol * rank + k0 + 8 * h);
+        acc = mfma32x32x16(af, bv, acc);
+    }
+    return acc;
 }
 
 template <int ACT>
@@ -275,13 +283,13 @@ __host__ __device__ constexpr int tile_cols()
     return ACT != ACT_NONE ? TL_BN / 2 : TL_BN;
 }
 
-template <int ACT, typename OutT, bool PACKED>
+template <int ACT, typename OutT, bool PACKED, bool LORA>
 __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
     const int32_t *__restrict__ plan, int N, int K,
-    OutT *__restrict__ out, int64_t ldo)
+    OutT *__restrict__ out, int64_t ldo, LoraEpi lora)
 {
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = tile_cols<ACT>();
@@ -418,6 +426,23 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
         __syncthreads();
     }
 
+    if constexpr (LORA) {
+        // the low-rank increment: rank / 16 more MFMA steps per tile
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            if (!mt_on[i]) continue;
+            const int64_t trow = min(r0 + wm * 64 + 32 * i + l32, rend - 1);
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const bool w2 = GLU && j == 1;
+                const int col = GLU ? n0 + 32 * wn + l32 : n0 + 64 * wn + 32 * j + l32;
+                acc[i][j] = lora_add(acc[i][j], w2 ? lora.t2 : lora.t1, trow,
+                                     (w2 ? lora.b2 : lora.b1) + (int64_t)e * N * lora.rank,
+                                     min(col, N - 1), lora.rank, h);
+            }
+        }
+    }
+
     // ---- epilogue: lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
 #pragma unroll
     for (int i = 0; i < 2; i++) {
@@ -473,13 +498,13 @@ constexpr int TB_ALD = TB_BK + 8;  // 72 bf16 = 144 bytes per A row in LDS
 constexpr size_t TB_LDS = (size_t)2 * TB_BM * TB_ALD * 2 + (size_t)2 * TB_BN * (TB_BK / 2) +
                           (size_t)2 * TB_BN * (TB_BK / 32);
 
-template <int ACT, typename OutT, bool PACKED>
+template <int ACT, typename OutT, bool PACKED, bool LORA>
 __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
     const int32_t *__restrict__ plan, int N, int K,
-    OutT *__restrict__ out, int64_t ldo)
+    OutT *__restrict__ out, int64_t ldo, LoraEpi lora)
 {
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? TB_BN / 2 : TB_BN;
@@ -635,6 +660,23 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
             __syncthreads();
         }
 
+        if constexpr (LORA) {
+            // the low-rank increment: rank / 16 more MFMA steps per tile
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+                const int64_t trow = min(r0 + 32 * q + 128 * i + l32, rend - 1);
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const bool w2 = GLU && j >= 2;
+                    const int col = GLU ? n0 + 64 * ch + 32 * (j & 1) + l32
+                                        : n0 + 128 * ch + 32 * j + l32;
+                    acc[i][j] = lora_add(acc[i][j], w2 ? lora.t2 : lora.t1, trow,
+                                         (w2 ? lora.b2 : lora.b1) + (int64_t)e * N * lora.rank,
+                                         min(col, N - 1), lora.rank, h);
+                }
+            }
+        }
+
         // epilogue: lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
 #pragma unroll
         for (int i = 0; i < NI; i++) {
@@ -776,7 +818,8 @@ template <int ACT, typename OutT, bool PACKED>
 static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
                               const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                               const uint8_t *w2s, const int32_t *plan,
-                              int max_groups, int N, int K, OutT *out, int64_t ldo, hipStream_t s)
+                              int max_groups, int N, int K, OutT *out, int64_t ldo,
+                              const LoraEpi *lora, hipStream_t s)
 {
     constexpr int COLS = tile_cols<ACT>();
     const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
@@ -784,8 +827,15 @@ static hipError_t launch_tile(const bf16 *a, int64_t lda, const int32_t *a_rows,
     // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT, PACKED>), dim3((unsigned)G), dim3(TL_THREADS),
-                       0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, plan, N, K, out, ldo);
+    const LoraEpi le = lora ? *lora : LoraEpi{nullptr, nullptr, nullptr, nullptr, 0};
+    if (lora)
+        hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT, PACKED, true>), dim3((unsigned)G),
+                           dim3(TL_THREADS), 0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, plan, N, K,
+                           out, ldo, le);
+    else
+        hipLaunchKernelGGL((gemm_tile_kernel<ACT, OutT, PACKED, false>), dim3((unsigned)G),
+                           dim3(TL_THREADS), 0, s, a, lda, a_rows, w1c, w1s, w2c, w2s, plan, N, K,
+                           out, ldo, le);
     return hipGetLastError();
 }
 
@@ -794,17 +844,19 @@ static hipError_t launch_tile256(const bf16 *a, int64_t lda, const int32_t *a_ro
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                  const uint8_t *w2s, const int32_t *plan,
                                  int max_groups, int N, int K, OutT *out, int64_t ldo,
-                                 hipStream_t s)
+                                 const LoraEpi *lora, hipStream_t s)
 {
     constexpr int COLS = ACT != ACT_NONE ? TB_BN / 2 : TB_BN;
     const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
     if (grid <= 0) return hipSuccess;
-    auto kern = gemm_tile256_kernel<ACT, OutT, PACKED>;
+    auto kern = lora ? gemm_tile256_kernel<ACT, OutT, PACKED, true>
+                     : gemm_tile256_kernel<ACT, OutT, PACKED, false>;
     hipError_t err = ensure_dynamic_lds((const void *)kern, (int)TB_LDS);
     if (err != hipSuccess) return err;
     const int64_t G = (grid + 7) / 8 * 8;
+    const LoraEpi le = lora ? *lora : LoraEpi{nullptr, nullptr, nullptr, nullptr, 0};
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(TB_THREADS), TB_LDS, s, a, lda, a_rows, w1c,
-                       w1s, w2c, w2s, plan, N, K, out, ldo);
+                       w1s, w2c, w2s, plan, N, K, out, ldo, le);
     return hipGetLastError();
 }
 
@@ -813,14 +865,16 @@ static hipError_t dispatch_act(int act, int md, const bf16 *a, int64_t lda, cons
                                const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                const uint8_t *w2s, const int32_t *plan,
                                int max_groups, int N, int K, OutT *out, int64_t ldo,
-                               hipStream_t s)
+                               const LoraEpi *lora, hipStream_t s)
 {
-#define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, plan, max_groups, N, K, out, ldo, s
-#define MOE_GEMM_CASE(A)                                                     \
-    case A:                                                                  \
-        return md == MOE_SCHED_TILE256   ? launch_tile256<A, OutT, PACKED>(MOE_GEMM_ARGS) \
-               : md == MOE_SCHED_TILE128 ? launch_tile<A, OutT, PACKED>(MOE_GEMM_ARGS)    \
-                                         : launch_stream<A, OutT, PACKED>(MOE_GEMM_ARGS);
+    // the streaming schedule has no LoRA epilogue
+    if (lora && md != MOE_SCHED_TILE256 && md != MOE_SCHED_TILE128) return hipErrorInvalidValue;
+#define MOE_GEMM_ARGS a, lda, a_rows, w1c, w1s, w2c, w2s, plan, max_groups, N, K, out, ldo
+#define MOE_GEMM_CASE(A)                                                                   \
+    case A:                                                                                \
+        return md == MOE_SCHED_TILE256   ? launch_tile256<A, OutT, PACKED>(MOE_GEMM_ARGS, lora, s) \
+               : md == MOE_SCHED_TILE128 ? launch_tile<A, OutT, PACKED>(MOE_GEMM_ARGS, lora, s)    \
+                                         : launch_stream<A, OutT, PACKED>(MOE_GEMM_ARGS, s);
     switch (act) {
         MOE_GEMM_CASE(ACT_NONE)
         MOE_GEMM_CASE(ACT_SILU_MUL)
@@ -858,14 +912,14 @@ hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, co
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
                            int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
-                           int packed, hipStream_t s)
+                           int packed, hipStream_t s, const LoraEpi *lora)
 {
     const int md = resolve_mode(mode, num_local, max_rows);
     const int max_groups = max_groups_for(num_local, max_rows, rows_per_group(md));
     const int32_t *plan = (const int32_t *)plan_ws;
 #define MOE_RUN(OT, PK)                                                                    \
     return dispatch_act<OT, PK>(act, md, a, lda, a_rows, w1c, w1s, w2c, w2s, plan,         \
-                                max_groups, N, K, (OT *)out, ldo, s)
+                                max_groups, N, K, (OT *)out, ldo, lora, s)
     if (out_f32) {
         if (packed) MOE_RUN(float, true);
         MOE_RUN(float, false);

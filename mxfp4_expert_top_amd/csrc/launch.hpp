@@ -76,6 +76,15 @@ hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int 
                           int num_local, int32_t *off, int32_t *perm, int32_t *inv, void *ws,
                           hipStream_t s, const GemmPlanArgs *plan = nullptr);
 
+// LoRA increment of a tiled projection, added to its accumulators before the
+// epilogue: t1 / t2 are the bf16 rank factors [rows][rank] (scale applied) of
+// the W1 / W2 projection, b1 / b2 the B factors [experts][N][rank]; rank is a
+// multiple of 16 (rank / 16 extra 32 x 32 x 16 MFMA steps per tile).
+struct LoraEpi {
+    const bf16 *t1, *t2, *b1, *b2;
+    int rank;
+};
+
 // gemm.hip
 // Work items of the grouped GEMMs: (expert, first row) groups of `rows`
 // consecutive permuted rows, built on the device from the expert offsets.
@@ -93,11 +102,13 @@ hipError_t launch_gemm_plan_into(const int32_t *off, int num_local, const GemmPl
 // run the GEMM from a plan built for the same (offsets, max_rows, mode).
 hipError_t launch_gemm_plan(const int32_t *off, int num_local, int max_rows, int mode, void *ws,
                             hipStream_t s);
+// lora: the low-rank increment added before the epilogue (tiled schedules
+// only: hipErrorInvalidValue for the streaming one)
 hipError_t launch_gemm_run(const bf16 *a, int64_t lda, const int32_t *a_rows, const uint8_t *w1c,
                            const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
                            int num_local, int max_rows, int N, int K, int act,
                            void *out, int out_f32, int64_t ldo, int mode, const void *plan_ws,
-                           int packed, hipStream_t s);
+                           int packed, hipStream_t s, const LoraEpi *lora = nullptr);
 int resolve_mode(int mode, int num_local, int max_rows);
 
 hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K,
@@ -131,6 +142,16 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
 // lora.hip: the low-rank increment on a frozen projection (y += t B_e^T with
 // t = scale x A_e^T, rows grouped by expert); t is [max_rows][rank] fp32
 size_t lora_ws_bytes(int max_rows, int rank);
+// the rank factors alone: t [max_rows][rank], fp32 or (t_bf16) bf16
+hipError_t launch_lora_t(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *la,
+                         int rank, float scale, const int32_t *off, int nl, int max_rows, int K,
+                         void *t, int t_bf16, hipStream_t s);
+// the rank factors (bf16) on the matrix cores, along the tiled GEMM work plan
+// `plan` (already built): t1 = scale x A1_e^T and, if a2, t2 = scale x A2_e^T;
+// rank % 16 == 0, K % 64 == 0, plan rows per group a multiple of 32, <= 256
+hipError_t launch_lora_t_plan(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *a1,
+                              const bf16 *a2, int rank, int K, float scale,
+                              const GemmPlanArgs &plan, bf16 *t1, bf16 *t2, hipStream_t s);
 hipError_t launch_lora(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *la,
                        const bf16 *lb, int rank, float scale, const int32_t *off, int nl,
                        int max_rows, int N, int K, float *y, int64_t ldy, float *t,

@@ -31,13 +31,13 @@ __device__ __forceinline__ int expert_of_row(const int32_t *off, int nl, int r)
 // of chunk c. When the wave's rows belong to one expert (the common case)
 // each A fragment it loads serves all RW rows; otherwise each row reads its
 // expert's.
-template <int RK>
+template <int RK, typename TOut>
 __global__ __launch_bounds__(256) void lora_t_kernel(const bf16 *__restrict__ x, int64_t ldx,
                                                      const int32_t *__restrict__ x_rows,
                                                      const bf16 *__restrict__ la,
                                                      const int32_t *__restrict__ off, int nl,
                                                      int rank, int K, float scale,
-                                                     float *__restrict__ t)
+                                                     TOut *__restrict__ t)
 {
     constexpr int RW = 64 / RK;
     const int A = off[nl];
@@ -101,8 +101,91 @@ __global__ __launch_bounds__(256) void lora_t_kernel(const bf16 *__restrict__ x,
                 float v = acc[i][j];
 #pragma unroll
                 for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-                if (lane == 0 && r0 + i < A) t[(int64_t)(r0 + i) * rank + j] = scale * v;
+                if (lane == 0 && r0 + i < A) store_out<TOut>(t + (int64_t)(r0 + i) * rank + j, scale * v);
             }
+        }
+    }
+}
+
+// Rank factors on the matrix cores, for the layer's tiled schedules. Per
+// expert the factor is a small dense product, t = scale * X_e A_e^T with X_e
+// the expert's rows [rows][K] and A_e [rank][K], so it follows the work plan
+// of the tiled GEMMs: one workgroup per plan item (expert, first row, up to
+// 256 rows), 32 rows per wave. Two adapters that read the same input (gate
+// and up) are evaluated in one pass over it; their 2 rank output columns are
+// covered by NT tiles of 32.
+//
+// Lane L: row (A operand) and adapter column (B operand) L % 32, half
+// h = L / 32. For the 64-wide K chunk at kc, half h holds elements
+// kc + 32 h .. + 32 of its row and of its column (64 contiguous bytes, four
+// 16-byte loads) and MFMA step s (0..3) takes elements kc + 32 h + 8 s .. + 8
+// of both, so every product x[k] A[j][k] enters exactly once. The loads of
+// chunk c + 1 are issued before chunk c is consumed.
+template <int NT>
+__global__ __launch_bounds__(512) void lora_t_mfma_kernel(
+    const bf16 *__restrict__ x, int64_t ldx, const int32_t *__restrict__ x_rows,
+    const bf16 *__restrict__ a1, const bf16 *__restrict__ a2, int rank, int K, float scale,
+    const int32_t *__restrict__ plan, int hdr, bf16 *__restrict__ t1, bf16 *__restrict__ t2)
+{
+    const int grp = blockIdx.x;
+    if (grp >= plan[0]) return;
+    const int2 it = ((const int2 *)(plan + hdr))[grp];
+    const int e = it.x & 0xFFFF, rows = it.x >> 16;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+    if (32 * w >= rows) return;
+    const int r0 = it.y + 32 * w, nr = min(32, rows - 32 * w);
+    const int prow = r0 + min(l32, nr - 1);
+    const bf16 *xp = x + (x_rows ? (int64_t)x_rows[prow] : (int64_t)prow) * ldx + 32 * hf;
+    const int ncol = a2 ? 2 * rank : rank;
+    const bf16 *bp[NT];
+    bool bon[NT];
+#pragma unroll
+    for (int g = 0; g < NT; g++) {
+        const int c = 32 * g + l32;
+        bon[g] = c < ncol;
+        const bool second = bon[g] && c >= rank;
+        bp[g] = (second ? a2 : a1) + ((int64_t)e * rank + (bon[g] ? c - (second ? rank : 0) : 0)) * K +
+                32 * hf;
+    }
+    const bf16x8 zero = {};
+    bf16x8 xa[2][4], bb[2][NT][4];
+    auto load = [&](int buf, int kc) {
+#pragma unroll
+        for (int q = 0; q < 4; q++) xa[buf][q] = *(const bf16x8 *)(xp + kc + 8 * q);
+#pragma unroll
+        for (int g = 0; g < NT; g++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const bf16x8 v = *(const bf16x8 *)(bp[g] + kc + 8 * q);
+                bb[buf][g][q] = bon[g] ? v : zero;
+            }
+    };
+    f32x16 acc[NT];
+#pragma unroll
+    for (int g = 0; g < NT; g++) acc[g] = f32x16{};
+    auto step = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+            for (int g = 0; g < NT; g++) acc[g] = mfma32x32x16(xa[buf][q], bb[buf][g][q], acc[g]);
+    };
+    load(0, 0);
+    for (int kc = 0; kc < K; kc += 128) {
+        if (kc + 64 < K) load(1, kc + 64);
+        step(0);
+        if (kc + 128 < K) load(0, kc + 128);
+        if (kc + 64 < K) step(1);
+    }
+    // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each column tile
+#pragma unroll
+    for (int g = 0; g < NT; g++) {
+        const int c = 32 * g + l32;
+        if (!bon[g]) continue;
+        bf16 *tc = c < rank ? t1 + c : t2 + (c - rank);
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int rr = 8 * (v >> 2) + 4 * hf + (v & 3);
+            if (rr < nr) tc[(int64_t)(r0 + rr) * rank] = to_bf16(scale * acc[g][v]);
         }
     }
 }
@@ -168,29 +251,72 @@ size_t lora_ws_bytes(int max_rows, int rank)
     return (((size_t)max_rows * rank * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+hipError_t launch_lora_t(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *la,
+                         int rank, float scale, const int32_t *off, int nl, int max_rows, int K,
+                         void *t, int t_bf16, hipStream_t s)
+{
+    if (max_rows <= 0) return hipSuccess;
+    // rows per expert on average decide how many rows share an adapter slice:
+    // few (small batches) -> one row per wave, so the grid still covers the chip
+    const int mean = max(1, max_rows / max(1, nl));
+    const int rk = mean < 4 ? 64 : rank <= 16 ? 16 : rank <= 32 ? 32 : 64;
+    const int rw = 64 / rk;
+    const int64_t waves = (max_rows + rw - 1) / rw;
+    const dim3 gt((unsigned)((waves + 3) / 4)), b(256);
+#define LT(R, T)                                                                                \
+    hipLaunchKernelGGL((lora_t_kernel<R, T>), gt, b, 0, s, x, ldx, x_rows, la, off, nl, rank, K, \
+                       scale, (T *)t)
+    if (t_bf16) {
+        if (rk == 16) LT(16, bf16);
+        else if (rk == 32) LT(32, bf16);
+        else LT(64, bf16);
+    } else {
+        if (rk == 16) LT(16, float);
+        else if (rk == 32) LT(32, float);
+        else LT(64, float);
+    }
+#undef LT
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_t_plan(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *a1,
+                              const bf16 *a2, int rank, int K, float scale,
+                              const GemmPlanArgs &plan, bf16 *t1, bf16 *t2, hipStream_t s)
+{
+    if (plan.max_groups <= 0) return hipSuccess;
+    const int R = plan.rows_per_group;
+    if (K % 64 || rank % 16 || rank > MOE_MAX_LORA_RANK || R % 32 || R <= 0 || R > 256)
+        return hipErrorInvalidValue;
+    // more than 96 columns would not fit the registers: one pass per adapter
+    if (a2 && 2 * rank > 96) {
+        const hipError_t e = launch_lora_t_plan(x, ldx, x_rows, a1, nullptr, rank, K, scale, plan,
+                                                t1, nullptr, s);
+        if (e != hipSuccess) return e;
+        return launch_lora_t_plan(x, ldx, x_rows, a2, nullptr, rank, K, scale, plan, t2, nullptr,
+                                  s);
+    }
+    const int nt = ((a2 ? 2 : 1) * rank + 31) / 32;
+    const dim3 grid((unsigned)plan.max_groups), block((unsigned)(R / 32 * 64));
+#define LTP(NT)                                                                                  \
+    hipLaunchKernelGGL(lora_t_mfma_kernel<NT>, grid, block, 0, s, x, ldx, x_rows, a1, a2, rank, K, \
+                       scale, plan.plan, plan.hdr, t1, t2)
+    if (nt == 1) LTP(1);
+    else if (nt == 2) LTP(2);
+    else LTP(3);
+#undef LTP
+    return hipGetLastError();
+}
+
 hipError_t launch_lora(const bf16 *x, int64_t ldx, const int32_t *x_rows, const bf16 *la,
                        const bf16 *lb, int rank, float scale, const int32_t *off, int nl,
                        int max_rows, int N, int K, float *y, int64_t ldy, float *t,
                        hipStream_t s)
 {
     if (max_rows <= 0) return hipSuccess;
-    // rows per expert on average decide how many rows share an adapter slice:
-    // few (small batches) -> one row per wave and small delta blocks, so the
-    // grid still covers the chip
-    const int mean = max(1, max_rows / max(1, nl));
-    const int rk = mean < 4 ? 64 : rank <= 16 ? 16 : rank <= 32 ? 32 : 64;
-    const int rw = 64 / rk;
-    const int64_t waves = (max_rows + rw - 1) / rw;
-    const dim3 gt((unsigned)((waves + 3) / 4)), b(256);
-#define LT(R)                                                                                  \
-    hipLaunchKernelGGL(lora_t_kernel<R>, gt, b, 0, s, x, ldx, x_rows, la, off, nl, rank, K,  \
-                       scale, t)
-    if (rk == 16) LT(16);
-    else if (rk == 32) LT(32);
-    else LT(64);
-#undef LT
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_lora_t(x, ldx, x_rows, la, rank, scale, off, nl, max_rows, K, t, 0, s);
     if (e != hipSuccess) return e;
+    const int mean = max(1, max_rows / max(1, nl));
+    const dim3 b(256);
     const int nchunks = (N + LA_COLS - 1) / LA_COLS;
     int rows = 1;
     while (rows < mean && rows < LA_ROWS) rows *= 2;

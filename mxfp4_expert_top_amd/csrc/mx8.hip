@@ -22,7 +22,6 @@
 namespace moe {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // fp32 -> MXFP8. Per block: s = clamp(floor(log2 amax) - 8 + 127, 0, 254)

@@ -237,12 +237,6 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
     }
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 constexpr size_t RG_LDS = (size_t)2 * RG_BM * RG_LD * 2 + (size_t)2 * 3 * RG_BN * RG_LD * 2;
 

@@ -42,8 +42,18 @@ def bf16_rounding_ok(got, ref, rel_slack=1e-5):
     return bool(np.all(np.abs(a - r) <= (2.0 ** -8 + rel_slack) * np.abs(r) + 1e-5 * rms))
 
 
-def assert_close_layer(got, ref, what=""):
-    r, m = rel_l2(got, ref), max_abs_rms(got, ref)
+def assert_close_layer(got, ref, what="", bf16_out=False):
+    """rel-L2 <= REL_L2 and every |got - ref| <= MAX_ABS_RMS * rms. With
+    ``bf16_out`` each element may also carry the final rounding to bf16, at
+    most the unit roundoff 2^-8 of its own magnitude: that error scales with
+    the value, the rms term covers the roundings inside the layer."""
+    r = rel_l2(got, ref)
+    if bf16_out:
+        a, b = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        rms = float(np.sqrt(np.mean(b ** 2)))
+        m = float(np.max(np.abs(a - b) - 2.0 ** -8 * np.abs(b)) / max(rms, 1e-300))
+    else:
+        m = max_abs_rms(got, ref)
     assert r <= REL_L2 and m <= MAX_ABS_RMS, f"{what}: rel_l2={r:.3e} max_abs/rms={m:.3e}"
     return r, m
 

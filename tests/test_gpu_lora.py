@@ -86,9 +86,11 @@ SMALL = [
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
-@pytest.mark.parametrize("mode", [0, 1, 4])
-@pytest.mark.parametrize("rank", [8, 32])
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+@pytest.mark.parametrize("rank", [8, 16, 32])
 def test_small_lora_layer_vs_oracle(m, cfg, mode, rank):
+    """Ranks 16 and 32 with a tiled schedule add the increment inside the
+    GEMMs; rank 8 or the streaming schedule take the unfused path."""
     inp = make_inputs(cfg).to(DEV)
     lora = {k: v.to(DEV) for k, v in make_lora(cfg, rank).items()}
     g = run_gpu_lora_layer(m, inp, lora, rank, 0.5, mode=mode)
@@ -99,33 +101,43 @@ def test_small_lora_layer_vs_oracle(m, cfg, mode, rank):
                             host_weights(inp.weights), {k: v.cpu() for k, v in lora.items()},
                             E=cfg.E, k=cfg.k, I=cfg.I, rank=rank, scale=0.5,
                             e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg)
-    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], cfg.name)
+    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], cfg.name, bf16_out=True)
+
+
+@pytest.mark.parametrize("cfg", SMALL[1:4:2], ids=lambda c: c.name)
+@pytest.mark.parametrize("mode", [3, 4])
+@pytest.mark.parametrize("rank", [48, 64])
+def test_wide_rank_lora_layer_vs_oracle(m, cfg, mode, rank):
+    """Rank 48 takes three 32-column tiles for gate and up together; rank 64
+    takes one rank-factor pass per adapter."""
+    test_small_lora_layer_vs_oracle(m, cfg, mode, rank)
 
 
 def test_tiny_workload_lora_full_oracle(m):
     """The full-width tiny workload (d = 3584, 896 experts, top-16, I = 128)
-    with rank-16 adapters on all 896 experts."""
+    with rank-16 adapters on all 896 experts, increment inside the GEMMs."""
     cfg = CONFIGS["tiny"]
     inp = make_inputs(cfg).to(DEV)
     lora = {k: v.to(DEV) for k, v in make_lora(cfg, 16).items()}
-    g = run_gpu_lora_layer(m, inp, lora, 16, 0.5)
+    g = run_gpu_lora_layer(m, inp, lora, 16, 0.5, mode=4)
     lg = np_(g["logits"])
     ref = oracle.layer_lora(inp.x, np_(inp.w_router), None, host_weights(inp.weights),
                             {k: v.cpu() for k, v in lora.items()}, E=cfg.E, k=cfg.k, I=cfg.I,
                             rank=16, scale=0.5, logits=lg)
-    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], "tiny lora")
+    assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], "tiny lora", bf16_out=True)
 
 
-@pytest.mark.parametrize("mode", [1, 4])
-def test_zero_increment_is_the_base_layer(m, mode):
-    """Zero B factors: the LoRA layer (unfused projections) gives the fused
-    layer's output to fp32 rounding of the same sums."""
+@pytest.mark.parametrize("mode,rank", [(1, 8), (4, 8), (3, 16), (4, 16)])
+def test_zero_increment_is_the_base_layer(m, mode, rank):
+    """Zero B factors: the LoRA layer, unfused (rank 8, or streaming) or with
+    the increment inside the GEMMs, gives moe_layer's output to fp32 rounding
+    of the same sums."""
     cfg = SMALL[1]
     inp = make_inputs(cfg).to(DEV)
-    lora = {k: v.to(DEV) for k, v in make_lora(cfg, 8).items()}
+    lora = {k: v.to(DEV) for k, v in make_lora(cfg, rank).items()}
     for n in ("gate_b", "up_b", "down_b"):
         lora[n].zero_()
-    a = run_gpu_lora_layer(m, inp, lora, 8, 0.5, mode=mode, out_dtype=torch.float32)
+    a = run_gpu_lora_layer(m, inp, lora, rank, 0.5, mode=mode, out_dtype=torch.float32)
     b = run_gpu_layer(inp, mode=mode, out_dtype=torch.float32)
     assert torch.equal(a["idx"], b["idx"])
     assert rel_l2(np_(a["out"]), np_(b["out"])) <= 1e-6
