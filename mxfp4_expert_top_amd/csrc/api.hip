@@ -560,13 +560,13 @@ struct LoraWs {
     size_t g, u, t, total;
 };
 
-// The increment rides in the tiled GEMMs' epilogue (rank factors in bf16)
-// when the schedule is tiled and the rank a multiple of 16; otherwise the
-// gate and up projections run unfused.
+// The increment rides in the GEMMs (rank factors in bf16, one more MFMA per
+// output tile and 16 or 32 ranks) when the rank is a multiple of 16;
+// otherwise the gate and up projections run unfused.
 bool lora_fused(const moe_layer_params *p, int rank)
 {
-    const int md = resolve_mode(p->mode, p->num_local, p->T * p->k);
-    return rank % 16 == 0 && (md == MOE_SCHED_TILE128 || md == MOE_SCHED_TILE256);
+    (void)p;
+    return rank % 16 == 0;
 }
 
 LoraWs lora_layer_ws(const moe_layer_params *p, int rank)

@@ -107,11 +107,11 @@ __global__ __launch_bounds__(256) void lora_t_kernel(const bf16 *__restrict__ x,
     }
 }
 
-// Rank factors on the matrix cores, for the layer's tiled schedules. Per
+// Rank factors on the matrix cores, for the increment inside the GEMMs. Per
 // expert the factor is a small dense product, t = scale * X_e A_e^T with X_e
-// the expert's rows [rows][K] and A_e [rank][K], so it follows the work plan
-// of the tiled GEMMs: one workgroup per plan item (expert, first row, up to
-// 256 rows), 32 rows per wave. Two adapters that read the same input (gate
+// the expert's rows [rows][K] and A_e [rank][K], so it follows the GEMMs' own
+// work plan: one workgroup per plan item (expert, first row, 16 to 256 rows),
+// 32 rows per wave. Two adapters that read the same input (gate
 // and up) are evaluated in one pass over it; their 2 rank output columns are
 // covered by NT tiles of 32.
 //
@@ -121,7 +121,12 @@ __global__ __launch_bounds__(256) void lora_t_kernel(const bf16 *__restrict__ x,
 // 16-byte loads) and MFMA step s (0..3) takes elements kc + 32 h + 8 s .. + 8
 // of both, so every product x[k] A[j][k] enters exactly once. The loads of
 // chunk c + 1 are issued before chunk c is consumed.
-template <int NT>
+//
+// Items of at most 32 rows (the streaming schedule's groups) leave a single
+// wave per item, which cannot keep enough loads in flight to stream the
+// adapter; there KS = 4 waves take a quarter of K each and add their partial
+// tiles through LDS in wave order.
+template <int NT, int KS>
 __global__ __launch_bounds__(512) void lora_t_mfma_kernel(
     const bf16 *__restrict__ x, int64_t ldx, const int32_t *__restrict__ x_rows,
     const bf16 *__restrict__ a1, const bf16 *__restrict__ a2, int rank, int K, float scale,
@@ -132,8 +137,12 @@ __global__ __launch_bounds__(512) void lora_t_mfma_kernel(
     const int2 it = ((const int2 *)(plan + hdr))[grp];
     const int e = it.x & 0xFFFF, rows = it.x >> 16;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
-    if (32 * w >= rows) return;
-    const int r0 = it.y + 32 * w, nr = min(32, rows - 32 * w);
+    const int rw = KS > 1 ? 0 : w;  // the wave's 32-row slice
+    if (32 * rw >= rows) return;    // (KS > 1: rows <= 32, every wave stays)
+    const int r0 = it.y + 32 * rw, nr = min(32, rows - 32 * rw);
+    // the wave's contraction range, in units of 64
+    const int n64 = K / 64, per = (n64 + KS - 1) / KS;
+    const int kb = KS > 1 ? min(K, 64 * per * w) : 0, ke = KS > 1 ? min(K, 64 * per * (w + 1)) : K;
     const int prow = r0 + min(l32, nr - 1);
     const bf16 *xp = x + (x_rows ? (int64_t)x_rows[prow] : (int64_t)prow) * ldx + 32 * hf;
     const int ncol = a2 ? 2 * rank : rank;
@@ -169,12 +178,27 @@ __global__ __launch_bounds__(512) void lora_t_mfma_kernel(
 #pragma unroll
             for (int g = 0; g < NT; g++) acc[g] = mfma32x32x16(xa[buf][q], bb[buf][g][q], acc[g]);
     };
-    load(0, 0);
-    for (int kc = 0; kc < K; kc += 128) {
-        if (kc + 64 < K) load(1, kc + 64);
-        step(0);
-        if (kc + 128 < K) load(0, kc + 128);
-        if (kc + 64 < K) step(1);
+    if (kb < ke) {
+        load(0, kb);
+        for (int kc = kb; kc < ke; kc += 128) {
+            if (kc + 64 < ke) load(1, kc + 64);
+            step(0);
+            if (kc + 128 < ke) load(0, kc + 128);
+            if (kc + 64 < ke) step(1);
+        }
+    }
+    if constexpr (KS > 1) {
+        // wave 0 adds the other waves' partial tiles, in wave order
+        __shared__ f32x16 part[KS - 1][NT][64];
+        if (w > 0)
+#pragma unroll
+            for (int g = 0; g < NT; g++) part[w - 1][g][lane] = acc[g];
+        __syncthreads();
+        if (w > 0) return;
+#pragma unroll
+        for (int i = 0; i < KS - 1; i++)
+#pragma unroll
+            for (int g = 0; g < NT; g++) acc[g] += part[i][g][lane];
     }
     // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each column tile
 #pragma unroll
@@ -285,7 +309,8 @@ hipError_t launch_lora_t_plan(const bf16 *x, int64_t ldx, const int32_t *x_rows,
 {
     if (plan.max_groups <= 0) return hipSuccess;
     const int R = plan.rows_per_group;
-    if (K % 64 || rank % 16 || rank > MOE_MAX_LORA_RANK || R % 32 || R <= 0 || R > 256)
+    if (K % 64 || rank % 16 || rank > MOE_MAX_LORA_RANK || R % 16 || (R > 32 && R % 32) || R <= 0 ||
+        R > 256)
         return hipErrorInvalidValue;
     // more than 96 columns would not fit the registers: one pass per adapter
     if (a2 && 2 * rank > 96) {
@@ -296,13 +321,22 @@ hipError_t launch_lora_t_plan(const bf16 *x, int64_t ldx, const int32_t *x_rows,
                                   s);
     }
     const int nt = ((a2 ? 2 : 1) * rank + 31) / 32;
-    const dim3 grid((unsigned)plan.max_groups), block((unsigned)(R / 32 * 64));
-#define LTP(NT)                                                                                  \
-    hipLaunchKernelGGL(lora_t_mfma_kernel<NT>, grid, block, 0, s, x, ldx, x_rows, a1, a2, rank, K, \
-                       scale, plan.plan, plan.hdr, t1, t2)
-    if (nt == 1) LTP(1);
-    else if (nt == 2) LTP(2);
-    else LTP(3);
+    // one wave per 32 rows of a work item; items of at most 32 rows (the
+    // streaming plan's 16-row groups) get four waves splitting K
+    const bool ks = R <= 32;
+    const dim3 grid((unsigned)plan.max_groups), block((unsigned)(ks ? 256 : R / 32 * 64));
+#define LTP(NT, KS)                                                                           \
+    hipLaunchKernelGGL((lora_t_mfma_kernel<NT, KS>), grid, block, 0, s, x, ldx, x_rows, a1, a2, \
+                       rank, K, scale, plan.plan, plan.hdr, t1, t2)
+    if (ks) {
+        if (nt == 1) LTP(1, 4);
+        else if (nt == 2) LTP(2, 4);
+        else LTP(3, 4);
+    } else {
+        if (nt == 1) LTP(1, 1);
+        else if (nt == 2) LTP(2, 1);
+        else LTP(3, 1);
+    }
 #undef LTP
     return hipGetLastError();
 }
