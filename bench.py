@@ -276,8 +276,11 @@ def main():
     gu_s = stage_ms["gate_up"] / 1e3
     sched = m.moe_grouped_gemm_schedule(cfg.num_local, cfg.T * cfg.k, args.mode)
     if args.lora_rank > 0:
-        # unfused: two frozen projections, their increments and the activation
-        roof = {"kernel": f"gate/up stage with rank-{args.lora_rank} LoRA (unfused)",
+        # rank a multiple of 16: the rank factors plus the GEMM with the
+        # increment inside; otherwise two frozen projections, their
+        # increments and the activation
+        how = "increment inside the GEMM" if args.lora_rank % 16 == 0 else "unfused"
+        roof = {"kernel": f"gate/up stage with rank-{args.lora_rank} LoRA ({how})",
                 "bound": "mfma", "achieved": round(gf / gu_s / 1e12, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -297,7 +300,9 @@ def main():
                 "algorithmic_bytes_per_launch": int(gb),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
     else:
-        name = "gemm_tile256_kernel" if sched == m.MODE_TILE256 else "gemm_tile_kernel"
+        # the 256-row gate/up kernel loads straight into LDS up to K = 4096
+        name = ("gemm_tile256_dma_kernel" if cfg.d <= 4096 else "gemm_tile256_kernel") \
+            if sched == m.MODE_TILE256 else "gemm_tile_kernel"
         roof = {"kernel": f"{name}<SILU_MUL> (gate/up projection)", "bound": "mfma",
                 "achieved": round(gf / gu_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4),

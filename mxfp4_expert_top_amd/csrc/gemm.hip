@@ -1080,12 +1080,16 @@ static int device_cus()
 }
 
 // Schedule choice from host-known sizes only: the mean rows per local expert
-// (max_rows / num_local). Below TILE_MIN_ROWS the weight-streaming schedule
-// (weights read once per 16 rows) wins. Up to TILE256_MAX_MEAN a typical
-// expert fits one 256-row tile, so the 256-row schedule reads each weight
-// byte once per expert; above it the 128-row schedule (two workgroups per
-// CU) keeps the matrix cores busier.
+// (max_rows / num_local) and the bound on rows itself. Below TILE_MIN_ROWS
+// the weight-streaming schedule (weights read once per 16 rows) wins. Up to
+// TILE256_MAX_MEAN a typical expert fits one 256-row tile, so the 256-row
+// schedule reads each weight byte once per expert. Above it the 128-row
+// schedule (two workgroups per CU) fills the chip with fewer rows, unless
+// the bound is so large (TILE256_MIN_BOUND rows: tens of thousands of tiles)
+// that the last partial wave of workgroups no longer matters and the 256-row
+// tile's weight reuse wins again.
 constexpr int TILE_MIN_ROWS = 48, TILE256_MAX_MEAN = 192;
+constexpr int64_t TILE256_MIN_BOUND = (int64_t)1 << 19;
 
 int resolve_mode(int mode, int num_local, int max_rows)
 {
@@ -1093,8 +1097,10 @@ int resolve_mode(int mode, int num_local, int max_rows)
         return mode;
     if (mode == 0 && (int64_t)max_rows < (int64_t)TILE_MIN_ROWS * num_local)
         return MOE_SCHED_STREAM;
-    return (int64_t)max_rows <= (int64_t)TILE256_MAX_MEAN * num_local ? MOE_SCHED_TILE256
-                                                                        : MOE_SCHED_TILE128;
+    return (int64_t)max_rows <= (int64_t)TILE256_MAX_MEAN * num_local ||
+                   (int64_t)max_rows >= TILE256_MIN_BOUND
+               ? MOE_SCHED_TILE256
+               : MOE_SCHED_TILE128;
 }
 
 static int rows_per_group(int md)

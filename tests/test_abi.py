@@ -37,7 +37,7 @@ def test_schedule_choice():
     assert m.moe_grouped_gemm_schedule(896, 64 * 16) == m.MODE_STREAM
     assert m.moe_grouped_gemm_schedule(896, 8192 * 16) == m.MODE_TILE256
     assert m.moe_grouped_gemm_schedule(112, 16384 * 16) == m.MODE_TILE128
-    assert m.moe_grouped_gemm_schedule(896, 65536 * 16) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(896, 65536 * 16) == m.MODE_TILE256
     # explicit schedules are kept; TILED never streams
     for md in (m.MODE_STREAM, m.MODE_TILE128, m.MODE_TILE256):
         assert m.moe_grouped_gemm_schedule(896, 64, md) == md
@@ -47,6 +47,9 @@ def test_schedule_choice():
     assert m.moe_grouped_gemm_schedule(10, 480) == m.MODE_TILE256
     assert m.moe_grouped_gemm_schedule(10, 1920) == m.MODE_TILE256
     assert m.moe_grouped_gemm_schedule(10, 1921) == m.MODE_TILE128
+    # and a row bound of 2^19 or more: 256-row tiles whatever the mean
+    assert m.moe_grouped_gemm_schedule(112, (1 << 19) - 1) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(112, 1 << 19) == m.MODE_TILE256
     assert m.lib.moe_grouped_gemm_schedule(0, 10, 0) == -1
     assert m.lib.moe_grouped_gemm_schedule(4, 10, 5) == -1
 
