@@ -120,7 +120,7 @@ LayerWs layer_ws(const moe_layer_params *p)
     const size_t A = T * k;
     size_t o = 0;
     L.router = router_kind(p->T, p->d);
-    L.splits = L.router == ROUTER_TILED   ? router_tile_splits(p->T, p->d, p->E, 512)
+    L.splits = L.router == ROUTER_TILED   ? router_tile_splits(p->T, p->d, p->E, 256)
                : L.router == ROUTER_SMALL ? router_splits(p->T, p->d, p->E, 512)
                                           : router_skinny_splits(p->T, p->d, p->E, 256);
     L.logits = o; o += round_up(T * E * 4);

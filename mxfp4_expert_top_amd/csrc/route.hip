@@ -211,14 +211,16 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 // Router scores for larger batches: the fp32 weights are split once into
 // three bf16 planes Wp[p][e][i] (hi, mid, lo; exact sum), then
 //   logits[t][e] = sum_i sum_p x[t][i] * Wp[p][e][i]  (+ bias)
-// on the 32x32x16 matrix cores. Workgroup tile 128 tokens x 128 experts, K
+// on the 32x32x16 matrix cores. Workgroup tile 256 tokens x 256 experts, K
 // step 32 of d covering all three planes: each token fragment read from LDS
-// feeds three MFMAs (one per plane). Both operands double-buffered in LDS
-// (80 KB, two workgroups per CU), 4 waves of 64 x 64. blockIdx.y splits d
-// into ranges whose partial sums go to separate planes when the tile grid
-// alone is too small for the chip.
+// feeds three planes' MFMAs. 8 waves of 128 tokens x 64 experts, so every
+// LDS fragment feeds 6 (token) or 4 (expert) MFMAs: 10 fragment reads per
+// 24 MFMAs, which keeps the LDS read rate well under its bandwidth (64 x 64
+// wave tiles needed 8 per 12). Both operands double-buffered in LDS (160 KB,
+// one workgroup per CU). blockIdx.y splits d into ranges whose partial sums
+// go to separate planes when the tile grid alone is too small for the chip.
 // ---------------------------------------------------------------------------
-constexpr int RG_BM = 128, RG_BN = 128, RG_BK = 32, RG_LD = RG_BK + 8;
+constexpr int RG_BM = 256, RG_BN = 256, RG_BK = 32, RG_LD = RG_BK + 8, RG_THREADS = 512;
 
 __global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ w,
                                                            int64_t n, bf16 *__restrict__ wp)
@@ -237,10 +239,9 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
     }
 }
 
-
 constexpr size_t RG_LDS = (size_t)2 * RG_BM * RG_LD * 2 + (size_t)2 * 3 * RG_BN * RG_LD * 2;
 
-__global__ __launch_bounds__(256, 2) void router_tile_kernel(
+__global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wp, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int ksteps_per_split,
     int32_t *__restrict__ zero_counts)
@@ -255,24 +256,24 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
     const int mb = blockIdx.x / n_nb, nb = blockIdx.x - mb * n_nb;
     const int t0 = mb * RG_BM, e0 = nb * RG_BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;  // 128 tokens x 64 experts per wave
     const int h = lane >> 5, l32 = lane & 31;
     const int kt0 = blockIdx.y * ksteps_per_split, kt1 = kt0 + ksteps_per_split;
     logits += (int64_t)blockIdx.y * T * E;
     if (gridDim.y > 1) bias = nullptr;
 
     // global -> LDS. A: thread -> token row tid / 2, 16 bf16 at 16 (tid % 2).
-    // B: 6 units of 8 bf16 per thread, unit u = tid + 256 i -> plane u / 512,
-    // expert row (u % 512) / 4, column 8 (u % 4).
+    // B: 6 units of 8 bf16 per thread, unit u = tid + 512 i -> plane u / 1024,
+    // expert row (u % 1024) / 4, column 8 (u % 4).
     const int ar = tid >> 1, ac = 16 * (tid & 1);
     const bf16 *xa = x + (int64_t)min(t0 + ar, T - 1) * d + ac;
     const bf16 *wb[6];
     int bp[6], brow[6], bq[6];
 #pragma unroll
     for (int i = 0; i < 6; i++) {
-        const int u = tid + 256 * i;
-        bp[i] = u >> 9;
-        brow[i] = (u & 511) >> 2;
+        const int u = tid + RG_THREADS * i;
+        bp[i] = u >> 10;
+        brow[i] = (u & 1023) >> 2;
         bq[i] = u & 3;
         wb[i] = wp + ((int64_t)bp[i] * E + min(e0 + brow[i], E - 1)) * d + 8 * bq[i];
     }
@@ -290,14 +291,15 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
 #pragma unroll
         for (int i = 0; i < 6; i++) *(u32x4 *)(&Bs[st][bp[i]][brow[i]][8 * bq[i]]) = rb[i];
     };
-    f32x16 acc[2][2];
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
-    const bool mt_on = t0 + wm * 64 < T;  // the wave's 64 tokens hold at least one real row
+    // the wave's 128 tokens hold at least one real row and its 64 experts one real expert
+    const bool on = t0 + wm * 128 < T && e0 + wn * 64 < E;
 
     gload(kt0);
     lstore(0);
@@ -305,13 +307,13 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
     for (int kt = kt0; kt < kt1; kt++) {
         const int st = (kt - kt0) & 1;
         if (kt + 1 < kt1) gload(kt + 1);
-        if (mt_on) {
+        if (on) {
 #pragma unroll
             for (int s = 0; s < 2; s++) {
-                bf16x8 a[2];
+                bf16x8 a[4];
 #pragma unroll
-                for (int i = 0; i < 2; i++)
-                    a[i] = *(const bf16x8 *)(&As[st][wm * 64 + 32 * i + l32][16 * s + 8 * h]);
+                for (int i = 0; i < 4; i++)
+                    a[i] = *(const bf16x8 *)(&As[st][wm * 128 + 32 * i + l32][16 * s + 8 * h]);
 #pragma unroll
                 for (int p = 0; p < 3; p++) {
 #pragma unroll
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
                         const bf16x8 b =
                             *(const bf16x8 *)(&Bs[st][p][wn * 64 + 32 * j + l32][16 * s + 8 * h]);
 #pragma unroll
-                        for (int i = 0; i < 2; i++) acc[i][j] = mfma32x32x16(a[i], b, acc[i][j]);
+                        for (int i = 0; i < 4; i++) acc[i][j] = mfma32x32x16(a[i], b, acc[i][j]);
                     }
                 }
             }
@@ -328,9 +330,9 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
         __syncthreads();
     }
     // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
-    if (!mt_on) return;
+    if (!on) return;
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
+    for (int i = 0; i < 4; i++) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int e = e0 + wn * 64 + 32 * j + l32;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void router_tile_kernel(
             const float bb = bias ? bias[e] : 0.f;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int t = t0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int t = t0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (t < T) logits[(int64_t)t * E + e] = acc[i][j][v] + bb;
             }
         }
@@ -609,8 +611,8 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
     const int steps = d / RG_BK;
     hipError_t err = ensure_dynamic_lds((const void *)router_tile_kernel, (int)RG_LDS);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(256), RG_LDS, s, x, wp, bias,
-                       logits, T, d, E, steps / splits, zero_counts);
+    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(RG_THREADS), RG_LDS, s, x, wp,
+                       bias, logits, T, d, E, steps / splits, zero_counts);
     return hipGetLastError();
 }
 
