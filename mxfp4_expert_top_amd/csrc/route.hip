@@ -253,7 +253,13 @@ __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
     bf16 (*Bs)[3][RG_BN][RG_LD] =
         (bf16 (*)[3][RG_BN][RG_LD])(rg_lds + (size_t)2 * RG_BM * RG_LD * 2);
     const int n_nb = (E + RG_BN - 1) / RG_BN;
-    const int mb = blockIdx.x / n_nb, nb = blockIdx.x - mb * n_nb;
+    // XCD-aware order: XCD b % 8 takes a contiguous range of tiles, token
+    // block major, so the expert blocks of a token block share one L2
+    const int tiles = (T + RG_BM - 1) / RG_BM * n_nb;
+    const int per_xcd = (tiles + 7) / 8;
+    const int wi = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+    if ((int)(blockIdx.x / 8) >= per_xcd || wi >= tiles) return;
+    const int mb = wi / n_nb, nb = wi - mb * n_nb;
     const int t0 = mb * RG_BM, e0 = nb * RG_BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;  // 128 tokens x 64 experts per wave
@@ -611,7 +617,9 @@ hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, 
     const int steps = d / RG_BK;
     hipError_t err = ensure_dynamic_lds((const void *)router_tile_kernel, (int)RG_LDS);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(router_tile_kernel, dim3(tiles, splits), dim3(RG_THREADS), RG_LDS, s, x, wp,
+    // a grid of 8 * ceil(tiles / 8) blocks covers every tile in the XCD-aware order
+    const unsigned G = (unsigned)((tiles + 7) / 8 * 8);
+    hipLaunchKernelGGL(router_tile_kernel, dim3(G, splits), dim3(RG_THREADS), RG_LDS, s, x, wp,
                        bias, logits, T, d, E, steps / splits, zero_counts);
     return hipGetLastError();
 }
