@@ -300,8 +300,8 @@ def main():
                 "algorithmic_bytes_per_launch": int(gb),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
     else:
-        # the 256-row gate/up kernel loads straight into LDS up to K = 4096
-        name = ("gemm_tile256_dma_kernel" if cfg.d <= 4096 else "gemm_tile256_kernel") \
+        # the 256-row schedule loads straight into LDS up to K = 4096
+        name = ("gemm_tile256_w16_kernel" if cfg.d <= 4096 else "gemm_tile256_kernel") \
             if sched == m.MODE_TILE256 else "gemm_tile_kernel"
         roof = {"kernel": f"{name}<SILU_MUL> (gate/up projection)", "bound": "mfma",
                 "achieved": round(gf / gu_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS,

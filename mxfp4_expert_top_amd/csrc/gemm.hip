@@ -756,8 +756,8 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
 // ---------------------------------------------------------------------------
 // 256 x 256 tiles with direct global -> LDS loads (K <= TD_MAX_K).
 //
-// Same tile, waves, plan and epilogue as gemm_tile256_kernel, but the A rows
-// and the 4-bit codes travel from memory straight into a three-stage LDS ring
+// Same tile, plan and epilogue as gemm_tile256_kernel, but the A rows and the
+// 4-bit codes travel from memory straight into a three-stage LDS ring
 // (global_load_lds_dwordx4: each lane's 16 bytes land at the wave's LDS base
 // + 16 * lane), so no register staging and no LDS stores sit in the K loop,
 // and the loads of step k + 2 are in flight during the MFMAs of steps k and
@@ -776,7 +776,6 @@ constexpr int TD_A_BYTES = TB_BM * TB_BK * 2;           // 32 KB
 constexpr int TD_W_BYTES = TB_BN * TB_BK / 2;           // 8 KB
 constexpr int TD_STAGE_BYTES = TD_A_BYTES + TD_W_BYTES;  // 40 KB
 constexpr int TD_MAX_K = 4096;
-constexpr int TD_LOADS = 5;  // DMA instructions per wave per K step (4 A + 1 code)
 constexpr int TD_ASWZ = 1, TD_BSWZ = 1;
 
 // bytes per weight row of the LDS scale table: K / 32, rounded up to an odd
@@ -812,8 +811,18 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base)
 }
 #pragma clang diagnostic pop
 
+// 16 waves (4 per SIMD) share the tile. Wave w takes row block q = w / 4
+// (64 rows: two 32-row tiles) and weight slot c = w % 4: for a GLU tile the
+// gate and up rows of output columns 32 c .. + 32, otherwise weight rows
+// 64 c .. + 64. The four waves that share a SIMD (w % 4 equal) then hold all
+// four row blocks of one slot, so every SIMD gets the same share of the
+// active row tiles whatever the expert's row count, and four waves per SIMD
+// hide each other's LDS and barrier waits. A rows: two DMA instructions per
+// wave (rows 16 w .. + 16); codes: one per wave of the first eight.
+constexpr int TW_THREADS = 1024;
+
 template <int ACT, typename OutT, bool PACKED, bool LORA>
-__global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
+__global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
@@ -828,7 +837,6 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
 
     const int nblk = (N + COLS - 1) / COLS;
     const int total = plan[0] * nblk;
-    // XCD-aware order (as in the other tiled schedules)
     const int per_xcd = (total + 7) / 8;
     const int local = blockIdx.x / 8;
     const int wi = (blockIdx.x % 8) * per_xcd + local;
@@ -841,10 +849,9 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ch = wave & 1, q = wave >> 1;
+    const int slot = wave & 3, q = wave >> 2;
     const int nch = K / 128, nc4 = (nch + 3) / 4;
 
-    // weight row (and its matrix) of LDS weight row `br`
     auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
         int wrow;
         if (GLU) {
@@ -859,19 +866,18 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
         return (int64_t)e * N + wrow;
     };
 
-    // ---- DMA sources. A: instruction j of a wave fills rows 32 wave + 8 j
-    // .. + 7; lane L lands in chunk position L % 8 of row 32 wave + 8 j + L / 8
-    // and so carries logical chunk (L % 8) ^ (((8 j + L / 8) >> TD_ASWZ) % 8).
-    const bf16 *ag[4];
+    // ---- DMA sources. A: instruction j of wave w fills rows 16 w + 8 j .. + 7
+    // (lane L: chunk position L % 8 of row 16 w + 8 j + L / 8).
+    const bf16 *ag[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int rc = min(r0 + 32 * wave + 8 * j + (lane >> 3), rend - 1);
+    for (int j = 0; j < 2; j++) {
+        const int rc = min(r0 + 16 * wave + 8 * j + (lane >> 3), rend - 1);
         const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
         ag[j] = a + arow * lda + 8 * ((lane & 7) ^ (((8 * j + (lane >> 3)) >> TD_ASWZ) & 7));
     }
-    // codes: thread -> LDS weight row tid / 2, half tid % 2, which holds MX
-    // block bh of the K step (16 bytes)
-    const int br = tid >> 1, bh = (tid & 1) ^ (TD_BSWZ & (br >> 3));
+    // codes: threads 0..511 -> LDS weight row tid / 2, half holding MX block bh
+    const bool wload = wave < 8;
+    const int br = (tid & 511) >> 1, bh = (tid & 1) ^ (TD_BSWZ & (br >> 3));
     const uint8_t *bg;
     {
         const uint8_t *wc, *ws;
@@ -885,13 +891,15 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
     auto issue = [&](int kt, int st) {
         const uint32_t sb = lds0 + st * TD_STAGE_BYTES;
 #pragma unroll
-        for (int j = 0; j < 4; j++) dma16(ag[j] + kt * TB_BK, sb + (4 * wave + j) * 1024);
-        const uint8_t *src;
-        if constexpr (PACKED)
-            src = bg + (kt >> 1) * 1024 + (2 * (kt & 1) + bh) * 256;
-        else
-            src = bg + kt * (TB_BK / 2);
-        dma16(src, sb + TD_A_BYTES + wave * 1024);
+        for (int j = 0; j < 2; j++) dma16(ag[j] + kt * TB_BK, sb + (2 * wave + j) * 1024);
+        if (wload) {
+            const uint8_t *src;
+            if constexpr (PACKED)
+                src = bg + (kt >> 1) * 1024 + (2 * (kt & 1) + bh) * 256;
+            else
+                src = bg + kt * (TB_BK / 2);
+            dma16(src, sb + TD_A_BYTES + wave * 1024);
+        }
     };
 
     const int nk = K / TB_BK;  // even: K is a multiple of 128
@@ -900,10 +908,8 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
 
     // ---- the tile's scales -> LDS, in K-block order per weight row
     if constexpr (PACKED) {
-        // dword (row block, chunk group cg, block g, row mm) holds block g of
-        // the 4 chunks 4 cg .. 4 cg + 3: K-blocks 16 cg + 4 i + g
         const int per_row = nc4 * 4;
-        for (int idx = tid; idx < TB_BN * per_row; idx += TB_THREADS) {
+        for (int idx = tid; idx < TB_BN * per_row; idx += TW_THREADS) {
             const int row = idx / per_row, r = idx - row * per_row;
             const int cg = r >> 2, g = r & 3;
             const uint8_t *wc, *ws;
@@ -917,8 +923,8 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
             }
         }
     } else {
-        const int per_row = K / 128;  // dwords of scales per weight row
-        for (int idx = tid; idx < TB_BN * per_row; idx += TB_THREADS) {
+        const int per_row = K / 128;
+        for (int idx = tid; idx < TB_BN * per_row; idx += TW_THREADS) {
             const int row = idx / per_row, r = idx - row * per_row;
             const uint8_t *wc, *ws;
             const int64_t wr64 = wsel(row, wc, ws);
@@ -927,27 +933,23 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
         }
     }
 
-    // ---- wave tiles (as in gemm_tile256_kernel)
+    // ---- wave tiles: weight tiles j = 0, 1 of the slot
     const int h = lane >> 5, l32 = lane & 31;
-    int bt[4];
+    int bt[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        if (GLU) bt[j] = (j >= 2 ? 128 : 0) + 64 * ch + 32 * (j & 1);
-        else bt[j] = 128 * ch + 32 * j;
-    }
-    const int n_on = (32 * q < mrows ? 1 : 0) + (128 + 32 * q < mrows ? 1 : 0);
-    // byte offset of this lane's A row inside a stage, and its chunk key
-    const int arow_off = (32 * q + l32) * 128;
+    for (int j = 0; j < 2; j++) bt[j] = GLU ? 128 * j + 32 * slot : 64 * slot + 32 * j;
+    const int n_on = (64 * q < mrows ? 1 : 0) + (64 * q + 32 < mrows ? 1 : 0);
+    const int arow_off = (64 * q + l32) * 128;
     const int akey = (4 * h) ^ ((l32 >> TD_ASWZ) & 7);
     const int bpos = 16 * (h ^ (TD_BSWZ & (l32 >> 3)));
 
     auto run = [&](auto ni_c) {
         constexpr int NI = decltype(ni_c)::value;
-        f32x16 acc[NI > 0 ? NI : 1][4];
+        f32x16 acc[NI > 0 ? NI : 1][2];
 #pragma unroll
         for (int i = 0; i < NI; i++)
 #pragma unroll
-            for (int j = 0; j < 4; j++)
+            for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
@@ -955,10 +957,10 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
             if constexpr (NI > 0) {
                 const uint8_t *As = td_lds + st * TD_STAGE_BYTES;
                 const uint8_t *Bq = As + TD_A_BYTES;
-                u32x4 qd[4];
-                float f[4];
+                u32x4 qd[2];
+                float f[2];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
+                for (int j = 0; j < 2; j++) {
                     const int row = bt[j] + l32;
                     qd[j] = *(const u32x4 *)(Bq + row * 32 + bpos);
                     f[j] = e8m0_to_f32(Ssc[row * srow + 2 * kt + h]);
@@ -968,10 +970,9 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
                     bf16x8 af[NI];
 #pragma unroll
                     for (int i = 0; i < NI; i++)
-                        af[i] = *(const bf16x8 *)(As + arow_off + 128 * 128 * i +
-                                                  ((akey ^ s) << 4));
+                        af[i] = *(const bf16x8 *)(As + arow_off + 32 * 128 * i + ((akey ^ s) << 4));
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
+                    for (int j = 0; j < 2; j++) {
                         const bf16x8 bv = mx_decode8(qd[j][s], f[j]);
 #pragma unroll
                         for (int i = 0; i < NI; i++) acc[i][j] = mfma32x32x16(af[i], bv, acc[i][j]);
@@ -980,18 +981,18 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
             }
         };
 
-        // scales written, steps 0 and 1 on the way
         for (int kt = 0; kt < nk; kt++) {
-            // this wave's loads of step kt are done (those of kt + 1 may still
-            // be in flight); the barrier makes every wave's visible and ends
-            // every wave's reads of step kt - 1, whose stage step kt + 2 reuses
-            if (kt + 1 < nk)
-                asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
-                             :
-                             : "n"(TD_LOADS)
-                             : "memory");
-            else
+            // this wave's loads of step kt are done (those of kt + 1 -- 3 or 2
+            // instructions -- may still be in flight); the barrier publishes
+            // every wave's and ends the reads of step kt - 1
+            if (kt + 1 < nk) {
+                if (wload)
+                    asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
             const int st = kt % 3;
             if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
             compute(st, kt);
@@ -1000,12 +1001,11 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
         if constexpr (LORA) {
 #pragma unroll
             for (int i = 0; i < NI; i++) {
-                const int64_t trow = min(r0 + 32 * q + 128 * i + l32, rend - 1);
+                const int64_t trow = min(r0 + 64 * q + 32 * i + l32, rend - 1);
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const bool w2 = GLU && j >= 2;
-                    const int col = GLU ? n0 + 64 * ch + 32 * (j & 1) + l32
-                                        : n0 + 128 * ch + 32 * j + l32;
+                for (int j = 0; j < 2; j++) {
+                    const bool w2 = GLU && j == 1;
+                    const int col = GLU ? n0 + 32 * slot + l32 : n0 + 64 * slot + 32 * j + l32;
                     acc[i][j] = lora_add(acc[i][j], w2 ? lora.t2 : lora.t1, trow,
                                          (w2 ? lora.b2 : lora.b1) + (int64_t)e * N * lora.rank,
                                          min(col, N - 1), lora.rank, h);
@@ -1018,21 +1018,17 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_dma_kernel(
         for (int i = 0; i < NI; i++) {
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int rl = 32 * q + 128 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (rl >= mrows) continue;
                 OutT *orow = out + (int64_t)(r0 + rl) * ldo;
                 if constexpr (GLU) {
-#pragma unroll
-                    for (int jj = 0; jj < 2; jj++) {
-                        const int col = n0 + 64 * ch + 32 * jj + l32;
-                        if (col < N)
-                            store_out<OutT>(orow + col,
-                                            act_apply<ACT>(acc[i][jj][v], acc[i][2 + jj][v]));
-                    }
+                    const int col = n0 + 32 * slot + l32;
+                    if (col < N)
+                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int col = n0 + 128 * ch + 32 * j + l32;
+                    for (int j = 0; j < 2; j++) {
+                        const int col = n0 + 64 * slot + 32 * j + l32;
                         if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
                     }
                 }
@@ -1199,28 +1195,27 @@ static hipError_t launch_tile256(const bf16 *a, int64_t lda, const int32_t *a_ro
     constexpr int COLS = ACT != ACT_NONE ? TB_BN / 2 : TB_BN;
     const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
     if (grid <= 0) return hipSuccess;
-    // direct-to-LDS loads for the gate/up projection while the tile's scales
-    // fit beside the three stages. The down projection (K = I, few K steps
-    // per tile) measured 3% slower with them than with register staging.
+    // direct-to-LDS loads while the tile's scales fit beside the three
+    // stages; register staging (8 waves) for longer contractions
     using Kern = void (*)(const bf16 *, int64_t, const int32_t *, const uint8_t *,
                           const uint8_t *, const uint8_t *, const uint8_t *, const int32_t *,
                           int, int, OutT *, int64_t, LoraEpi);
     Kern kern = lora ? gemm_tile256_kernel<ACT, OutT, PACKED, true>
                      : gemm_tile256_kernel<ACT, OutT, PACKED, false>;
     size_t lds = TB_LDS;
-    if constexpr (ACT != ACT_NONE) {
-        if (K <= TD_MAX_K) {
-            kern = lora ? gemm_tile256_dma_kernel<ACT, OutT, PACKED, true>
-                        : gemm_tile256_dma_kernel<ACT, OutT, PACKED, false>;
-            lds = (size_t)td_lds_bytes(K);
-        }
+    unsigned threads = TB_THREADS;
+    if (K <= TD_MAX_K) {
+        kern = lora ? gemm_tile256_w16_kernel<ACT, OutT, PACKED, true>
+                    : gemm_tile256_w16_kernel<ACT, OutT, PACKED, false>;
+        threads = TW_THREADS;
+        lds = (size_t)td_lds_bytes(K);
     }
     hipError_t err = ensure_dynamic_lds((const void *)kern, (int)lds);
     if (err != hipSuccess) return err;
     const int64_t G = (grid + 7) / 8 * 8;
     const LoraEpi le = lora ? *lora : LoraEpi{nullptr, nullptr, nullptr, nullptr, 0};
-    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(TB_THREADS), lds, s, a, lda, a_rows, w1c,
-                       w1s, w2c, w2s, plan, N, K, out, ldo, le);
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(threads), lds, s, a, lda, a_rows, w1c, w1s,
+                       w2c, w2s, plan, N, K, out, ldo, le);
     return hipGetLastError();
 }
 

@@ -315,10 +315,11 @@ def test_grouped_gemm_many_rows(m, mode, act, K):
 @pytest.mark.parametrize("mode", [3, 4])
 @pytest.mark.parametrize("K", [4096, 4224])
 @pytest.mark.parametrize("packed", [False, True])
-def test_grouped_gemm_long_contraction(m, mode, K, packed):
-    """Gate/up at the longest contraction whose scales the 256-row schedule
-    keeps in LDS beside its three load stages (4096), and one chunk past it,
-    where that schedule stages its loads through registers instead."""
+@pytest.mark.parametrize("act", [0, 1])
+def test_grouped_gemm_long_contraction(m, mode, K, packed, act):
+    """The longest contraction whose scales the 256-row schedule keeps in LDS
+    beside its three load stages (4096), and one chunk past it, where that
+    schedule stages its loads through registers instead."""
     rng = np.random.default_rng(K + mode)
     nl, N, T = 3, 128, 200
     counts = np.array([40, 0, 150], np.int32)
@@ -331,10 +332,12 @@ def test_grouped_gemm_long_contraction(m, mode, K, packed):
     dev = [t.to(DEV) for t in (w1c, w1s, w2c, w2s)]
     if packed:
         dev = [*m.moe_mxfp4_prepack(dev[0], dev[1]), *m.moe_mxfp4_prepack(dev[2], dev[3])]
+    if act == 0:
+        dev[2:] = [None, None]
     out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
     ws = m.alloc_workspace(m.moe_grouped_gemm_workspace_size(nl, A, N, mode), DEV)
     m.moe_grouped_gemm_mxfp4(x.to(DEV), torch.from_numpy(a_rows).to(DEV), *dev,
-                             torch.from_numpy(off).to(DEV), A, 1, out, ws, mode=mode,
+                             torch.from_numpy(off).to(DEV), A, act, out, ws, mode=mode,
                              w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
@@ -346,6 +349,9 @@ def test_grouped_gemm_long_contraction(m, mode, K, packed):
         if r0 == r1:
             continue
         g1 = xa[r0:r1] @ oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64).T
+        if act == 0:
+            ref[r0:r1] = g1
+            continue
         u = xa[r0:r1] @ oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64).T
         ref[r0:r1] = ACTS[1](g1, u)
     assert rel_l2(got[:A], ref) <= 1e-5, rel_l2(got[:A], ref)
