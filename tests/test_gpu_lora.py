@@ -62,17 +62,21 @@ def test_grouped_lora_vs_definition(m, rank, gather, K, N):
         assert (np.abs(d_got - delta) <= bound + 1e-30).all(), np.abs(d_got - delta).max()
 
 
-def run_gpu_lora_layer(m, inp, lora, rank, scale, mode=0, out_dtype=torch.bfloat16, act=1):
+def run_gpu_lora_layer(m, inp, lora, rank, scale, mode=0, out_dtype=torch.bfloat16, act=1,
+                       packed=None):
+    """``packed``: the weights converted to the streaming layout (else the
+    canonical ones in ``inp``)."""
     c = inp.cfg
     p = m.layer_params(c.T, c.d, c.E, c.k, c.I, c.expert_begin, c.num_local, act=act,
-                       out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16, mode=mode)
+                       out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16, mode=mode,
+                       weight_layout=m.LAYOUT_OCP if packed is None else m.LAYOUT_PACKED)
     ws = m.alloc_workspace(m.moe_layer_lora_workspace_size(p, rank), DEV)
     out = torch.empty(c.T, c.d, dtype=out_dtype, device=DEV)
     logits = torch.empty(c.T, c.E, dtype=torch.float32, device=DEV)
     idx = torch.empty(c.T, c.k, dtype=torch.int32, device=DEV)
     w = torch.empty(c.T, c.k, dtype=torch.float32, device=DEV)
-    m.moe_layer_lora(p, lora, rank, scale, inp.x, inp.w_router, inp.bias, inp.weights, out, ws,
-                     logits, idx, w)
+    m.moe_layer_lora(p, lora, rank, scale, inp.x, inp.w_router, inp.bias,
+                     inp.weights if packed is None else packed, out, ws, logits, idx, w)
     torch.cuda.synchronize()
     return dict(out=out, logits=logits, idx=idx, w=w)
 
@@ -89,8 +93,8 @@ SMALL = [
 @pytest.mark.parametrize("mode", [0, 1, 3, 4])
 @pytest.mark.parametrize("rank", [8, 16, 32])
 def test_small_lora_layer_vs_oracle(m, cfg, mode, rank):
-    """Ranks 16 and 32 with a tiled schedule add the increment inside the
-    GEMMs; rank 8 or the streaming schedule take the unfused path."""
+    """Ranks 16 and 32 add the increment inside the GEMMs (every schedule);
+    rank 8 takes the unfused path."""
     inp = make_inputs(cfg).to(DEV)
     lora = {k: v.to(DEV) for k, v in make_lora(cfg, rank).items()}
     g = run_gpu_lora_layer(m, inp, lora, rank, 0.5, mode=mode)
@@ -127,11 +131,11 @@ def test_tiny_workload_lora_full_oracle(m):
     assert_close_layer(g["out"].float().cpu().numpy(), ref["out"], "tiny lora", bf16_out=True)
 
 
-@pytest.mark.parametrize("mode,rank", [(1, 8), (4, 8), (3, 16), (4, 16)])
+@pytest.mark.parametrize("mode,rank", [(1, 8), (4, 8), (1, 16), (3, 16), (4, 16)])
 def test_zero_increment_is_the_base_layer(m, mode, rank):
-    """Zero B factors: the LoRA layer, unfused (rank 8, or streaming) or with
-    the increment inside the GEMMs, gives moe_layer's output to fp32 rounding
-    of the same sums."""
+    """Zero B factors: the LoRA layer, unfused (rank 8) or with the increment
+    inside the GEMMs (rank 16, streaming or tiled), gives moe_layer's output
+    to fp32 rounding of the same sums."""
     cfg = SMALL[1]
     inp = make_inputs(cfg).to(DEV)
     lora = {k: v.to(DEV) for k, v in make_lora(cfg, rank).items()}
@@ -141,3 +145,19 @@ def test_zero_increment_is_the_base_layer(m, mode, rank):
     b = run_gpu_layer(inp, mode=mode, out_dtype=torch.float32)
     assert torch.equal(a["idx"], b["idx"])
     assert rel_l2(np_(a["out"]), np_(b["out"])) <= 1e-6
+
+
+@pytest.mark.parametrize("mode", [1, 3, 4])
+@pytest.mark.parametrize("rank", [16, 64])
+def test_lora_layer_packed_equals_canonical(m, mode, rank):
+    """The benchmark's launch configuration: weights in the streaming layout.
+    The layout only permutes bytes, so the LoRA layer's output is bitwise the
+    canonical layout's, on every schedule."""
+    cfg = SMALL[1]
+    inp = make_inputs(cfg).to(DEV)
+    lora = {k: v.to(DEV) for k, v in make_lora(cfg, rank).items()}
+    a = run_gpu_lora_layer(m, inp, lora, rank, 0.5, mode=mode)
+    b = run_gpu_lora_layer(m, inp, lora, rank, 0.5, mode=mode,
+                           packed=m.prepack_weights(inp.weights))
+    assert torch.equal(a["idx"], b["idx"])
+    assert torch.equal(a["out"], b["out"])
