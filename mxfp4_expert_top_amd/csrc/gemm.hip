@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
                                 act_apply<ACT>(acc[2 * jp][i], acc[2 * jp + 1][i]));
         } else {
 #pragma unroll
-            for (int j = 0; j < NS; j++) store_out<OutT>(orow + n0 + 16 * j + m, acc[j][i]);
+            for (int j = 0; j < NS; j++) store_out_once<OutT>(orow + n0 + 16 * j + m, acc[j][i]);
         }
     }
 }
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(TL_THREADS, 2) void gemm_tile_kernel(
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     const int col = n0 + 64 * wn + 32 * j + l32;
-                    if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                    if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
                 }
             }
         }
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
 #pragma unroll
                     for (int j = 0; j < 4; j++) {
                         const int col = n0 + 128 * ch + 32 * j + l32;
-                        if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
                     }
                 }
             }
@@ -1029,7 +1029,7 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
 #pragma unroll
                     for (int j = 0; j < 2; j++) {
                         const int col = n0 + 64 * slot + 32 * j + l32;
-                        if (col < N) store_out<OutT>(orow + col, acc[i][j][v]);
+                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
                     }
                 }
             }
