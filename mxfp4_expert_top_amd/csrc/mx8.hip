@@ -375,7 +375,11 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
                     if (l32 == 0) out_scales[row * (ldo / 32) + col / 32] = (uint8_t)sc;
                 }
             } else {
-                if (rl < mrows && col < N) store_out<OutT>(out + (int64_t)(r0 + rl) * ldo + col, val);
+                if (rl < mrows && col < N) {
+                    // Y (the down projection) is read once, by the combine
+                    if constexpr (GLU) store_out<OutT>(out + (int64_t)(r0 + rl) * ldo + col, val);
+                    else store_out_once<OutT>(out + (int64_t)(r0 + rl) * ldo + col, val);
+                }
             }
         };
 #pragma unroll
