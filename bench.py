@@ -286,6 +286,14 @@ def main():
                 "frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4), "traffic": None,
                 "algorithmic_flops_per_launch": int(gf),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
+    elif mx8 and sched == m.MODE_STREAM:
+        # few rows per expert: the token quantiser plus the weight stream
+        roof = {"kernel": "mxfp8_quantize_kernel + gemm_mx8_stream_kernel<SILU_MUL> "
+                          "(gate/up stage)", "bound": "hbm",
+                "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": int(gb),
+                "avg_launch_ms": round(stage_ms["gate_up"], 4)}
     elif mx8:
         # the stage is the token quantiser plus the block-scaled GEMM
         roof = {"kernel": "mxfp8_quantize_kernel + gemm_mx8_kernel<SILU_MUL> (gate/up stage)",

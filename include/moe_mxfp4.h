@@ -259,14 +259,18 @@ int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K
  *   a_row  = (a_rows ? a_rows[r] : r)
  *   acc1[n] = sum_k A(a_row, k) * W1[e][n][k], A(r, k) = E4M3(a_codes[r *
  *             lda + k]) * 2^(a_scales[r * (lda/32) + k/32] - 127)
- * on v_mfma_scale_f32_32x32x64_f8f6f4 (exact products; each 64-long partial
- * sum is formed inside the instruction, then accumulated in fp32); out as in
- * moe_grouped_gemm_mxfp4, or with out_dtype MOE_DT_MXFP8 the fp32 results
- * converted as moe_mxfp8_quantize does (blocks of 32 along N): codes to out
- * [rows][ldo] (bytes), scales to out_scales [rows][ldo/32] (NULL for the
- * other dtypes). mode: MOE_SCHED_TILE128 for 128-row tiles; MOE_SCHED_AUTO,
- * MOE_SCHED_TILED and MOE_SCHED_TILE256 give 256-row tiles;
- * MOE_SCHED_STREAM -> INVALID_ARG. ws holds
+ * on the block-scaled matrix instruction (v_mfma_scale_f32_32x32x64_f8f6f4
+ * on the tiled schedules, v_mfma_scale_f32_16x16x128_f8f6f4 on the streaming
+ * one; exact products; each 64- or 128-long partial sum is formed inside the
+ * instruction, then accumulated in fp32); out as in moe_grouped_gemm_mxfp4,
+ * or with out_dtype MOE_DT_MXFP8 the fp32 results converted as
+ * moe_mxfp8_quantize does (blocks of 32 along N): codes to out [rows][ldo]
+ * (bytes), scales to out_scales [rows][ldo/32] (NULL for the other dtypes).
+ * mode: MOE_SCHED_STREAM streams the weights once per 16 rows (fp32 or bf16
+ * output; with MOE_DT_MXFP8 -> UNSUPPORTED); MOE_SCHED_TILE128 for 128-row
+ * tiles; MOE_SCHED_TILED and MOE_SCHED_TILE256 give 256-row tiles;
+ * MOE_SCHED_AUTO streams below a mean of 48 rows per local expert (except
+ * for MXFP8 output), else 256-row tiles. ws holds
  * moe_grouped_gemm_mx8_workspace_size(...) bytes.
  * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0 (% 32 for
  * MXFP8 output); 16-byte aligned code and scale arrays. Errors as

@@ -195,7 +195,6 @@ int check_layer_params(const moe_layer_params *p)
           MOE_ERR_INVALID_ARG);
     CHECK(p->precision == MOE_PREC_BF16 || p->precision == MOE_PREC_MX8, MOE_ERR_INVALID_ARG);
     // the MX8 mode has the two tiled schedules only
-    CHECK(p->precision != MOE_PREC_MX8 || p->mode != MOE_SCHED_STREAM, MOE_ERR_INVALID_ARG);
     CHECK(p->block_size == MOE_MX_BLOCK, MOE_ERR_UNSUPPORTED);
     CHECK(p->k <= MOE_MAX_TOPK && p->E <= MOE_MAX_EXPERTS, MOE_ERR_UNSUPPORTED);
     CHECK(p->d % 128 == 0 && p->I % 128 == 0, MOE_ERR_UNSUPPORTED);
@@ -325,9 +324,11 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                          void *ws, size_t ws_bytes, moe_stream_t stream)
 {
     const bool q_out = out_dtype == MOE_DT_MXFP8;
-    CHECK(mode == MOE_SCHED_AUTO || mode == MOE_SCHED_TILED || mode == MOE_SCHED_TILE128 ||
-              mode == MOE_SCHED_TILE256,
+    CHECK(mode == MOE_SCHED_AUTO || mode == MOE_SCHED_STREAM || mode == MOE_SCHED_TILED ||
+              mode == MOE_SCHED_TILE128 || mode == MOE_SCHED_TILE256,
           MOE_ERR_INVALID_ARG);
+    // MXFP8 output is written by the tiled schedules only
+    CHECK(!(q_out && mode == MOE_SCHED_STREAM), MOE_ERR_UNSUPPORTED);
     int rc = check_gemm(a_codes, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
                         num_local, max_rows, N, K, block_size, w_layout, act, out,
                         q_out ? MOE_DT_BF16 : out_dtype, ldo);

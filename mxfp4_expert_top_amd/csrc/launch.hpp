@@ -121,8 +121,8 @@ hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t 
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows);
 // MOE_SCHED_TILE128 or MOE_SCHED_TILE256 for a requested mode (AUTO / TILED
 // choose as the bf16 tiled schedules do)
-int mx8_resolve_mode(int mode, int num_local, int max_rows);
-GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws);
+int mx8_resolve_mode(int mode, int num_local, int max_rows, bool q_out = false);
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws, bool q_out = false);
 // A: codes [rows][lda] bytes, scales [rows][lda / 32]. Output kinds: bf16,
 // fp32, or MXFP8 (codes in out [rows][ldo], scales in out_scales [rows][ldo/32]).
 enum { MX8_OUT_BF16 = 0, MX8_OUT_F32 = 1, MX8_OUT_MXFP8 = 2 };

@@ -429,6 +429,185 @@ static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Streaming schedule of the MX8 mode (few rows per expert: decode), the
+// counterpart of the bf16 streaming GEMM: one workgroup per (16-row group,
+// block of output columns), each wave streaming 4 weight streams of 16 rows
+// (gate and up pairs for GLU) once, in 128-wide K chunks, on
+// v_mfma_scale_f32_16x16x128_f8f6f4. Operands, as the instruction takes them
+// (lane L, m = L % 16, g = L / 16; checked with a one-wave probe against an
+// fp64 evaluation):
+//   B (E2M1, 16 bytes): weight row m, MX block g of the chunk: the 16 stored
+//     code bytes, exactly what a lane of the streaming layout holds;
+//   A (E4M3, 32 bytes): token row m, K 16 g .. + 16 in bytes 0-15 and
+//     64 + 16 g .. + 16 in bytes 16-31;
+//   scales: lane L gives the E8M0 scale of its row for MX block g.
+// Result: lane L holds C[4 g + i][m] (token row 4 g + i, weight row m).
+// Weight loads carry the non-temporal hint (read once per row group).
+// ---------------------------------------------------------------------------
+template <int ACT, typename OutT, int D, bool PACKED>
+__global__ __launch_bounds__(256) void gemm_mx8_stream_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t lda,
+    const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
+    const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
+    const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int NS = 4;
+    constexpr int COLS_W = GLU ? 8 * NS : 16 * NS;  // output columns per wave
+    constexpr int COLS_B = 4 * COLS_W;
+    extern __shared__ uint32_t m8_sscale[];  // canonical layout: the rows' scales
+    const int nblk = (N + COLS_B - 1) / COLS_B;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+
+    const int wi = blockIdx.x;
+    if (wi >= plan[0] * nblk) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int nb0 = nb * COLS_B;
+    const int n0 = nb0 + wave * COLS_W;
+    const bool wave_on = n0 < N;  // N is a multiple of COLS_W
+    const int2 it = ((const int2 *)(plan + hdr))[grp];
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
+    const int rc = min(r0 + m, rend - 1);
+    const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+    const uint8_t *ap = ac + arow * lda + 16 * g;
+    const uint8_t *asp = as + arow * (lda / 32) + g;
+
+    const int nch = K / 128;  // a multiple of D
+    const int nc4 = (nch + 3) / 4;
+    const int sbw = K / 128;  // canonical: scale dwords per weight row
+    if constexpr (!PACKED) {
+        const int rows_v = min(COLS_B, N - nb0);
+        const int per_mat4 = rows_v * sbw / 4;
+        for (int i = threadIdx.x; i < (GLU ? 2 : 1) * per_mat4; i += blockDim.x) {
+            const int mat = i / per_mat4, r = i - mat * per_mat4;
+            const uint8_t *base = (mat ? w2s : w1s) + ((int64_t)e * N + nb0) * (K / 32);
+            *(u32x4 *)(&m8_sscale[mat * COLS_B * sbw + 4 * r]) = *(const u32x4 *)(base + 16 * r);
+        }
+    }
+
+    const uint8_t *cp[NS];
+    const uint8_t *spk[NS];
+    int srow[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        const int wr0 = GLU ? n0 + 16 * (j / 2) : n0 + 16 * j;
+        const bool second = GLU && (j & 1);
+        const int wr = wave_on ? wr0 : 0;
+        if constexpr (PACKED) {
+            const int64_t rb = ((int64_t)e * N + wr) / 16;
+            cp[j] = (second ? w2c : w1c) + rb * nch * 1024 + lane * 16;
+            spk[j] = (second ? w2s : w1s) + rb * nc4 * 256 + lane * 4;
+            srow[j] = 0;
+        } else {
+            const int64_t row = (int64_t)e * N + wr + m;
+            cp[j] = (second ? w2c : w1c) + row * (K / 2) + 16 * g;
+            spk[j] = nullptr;
+            srow[j] = ((second ? 1 : 0) * COLS_B + (wr0 - nb0) + m) * sbw;
+        }
+    }
+
+    u32x4 q[D][NS];
+    uint32_t sq[D][NS];
+    u32x4 alo[D], ahi[D];
+    uint32_t asc[D];
+    f32x4 acc[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int c, u32x4 *qd, uint32_t *sd, u32x4 &lo, u32x4 &hi, uint32_t &sa) {
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            if constexpr (PACKED) {
+                qd[j] = __builtin_nontemporal_load((const u32x4 *)(cp[j] + c * 1024));
+                sd[j] = __builtin_nontemporal_load((const uint32_t *)(spk[j] + (c >> 2) * 256));
+            } else {
+                qd[j] = __builtin_nontemporal_load((const u32x4 *)(cp[j] + c * 64));
+            }
+        }
+        lo = *(const u32x4 *)(ap + c * 128);
+        hi = *(const u32x4 *)(ap + c * 128 + 64);
+        sa = asp[4 * c];
+    };
+    auto consume = [&](int c, const u32x4 *qd, const uint32_t *sd, const u32x4 &lo,
+                       const u32x4 &hi, uint32_t sa) {
+        const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            uint32_t sb;
+            if constexpr (PACKED) sb = (sd[j] >> (8 * (c & 3))) & 0xffu;
+            else sb = (m8_sscale[srow[j] + c] >> (8 * g)) & 0xffu;
+            const i32x8 bv = {(int)qd[j][0], (int)qd[j][1], (int)qd[j][2], (int)qd[j][3],
+                              0, 0, 0, 0};
+            // A format 0: E4M3; B format 4: E2M1; scale byte 0 of each
+            acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[j], 0, 4, 0,
+                                                                      (int)sa, 0, (int)sb);
+        }
+    };
+    if (wave_on) {
+#pragma unroll
+        for (int d = 0; d < D; d++) issue(d, q[d], sq[d], alo[d], ahi[d], asc[d]);
+    }
+    if constexpr (!PACKED) __syncthreads();  // scales in LDS
+    if (!wave_on) return;
+    for (int c0 = 0; c0 < nch - D; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; d++) {
+            consume(c0 + d, q[d], sq[d], alo[d], ahi[d], asc[d]);
+            issue(c0 + d + D, q[d], sq[d], alo[d], ahi[d], asc[d]);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; d++) consume(nch - D + d, q[d], sq[d], alo[d], ahi[d], asc[d]);
+
+    // lane holds C[4 g + i][m] of each stream: token row r0 + 4 g + i
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int row = r0 + 4 * g + i;
+        if (row >= rend) continue;
+        OutT *orow = out + (int64_t)row * ldo;
+        if constexpr (GLU) {
+#pragma unroll
+            for (int jp = 0; jp < NS / 2; jp++)
+                store_out<OutT>(orow + n0 + 16 * jp + m,
+                                act_apply<ACT>(acc[2 * jp][i], acc[2 * jp + 1][i]));
+        } else {
+#pragma unroll
+            for (int j = 0; j < NS; j++) store_out_once<OutT>(orow + n0 + 16 * j + m, acc[j][i]);
+        }
+    }
+}
+
+template <int ACT, typename OutT, bool PACKED>
+static hipError_t launch_mx8_stream(const uint8_t *ac, const uint8_t *as, int64_t lda,
+                                    const int32_t *a_rows, const uint8_t *w1c,
+                                    const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
+                                    const GemmPlanArgs &pa, int N, int K, OutT *out, int64_t ldo,
+                                    hipStream_t s)
+{
+    constexpr int COLS_B = 4 * (ACT != ACT_NONE ? 32 : 64);
+    const int64_t grid = (int64_t)pa.max_groups * ((N + COLS_B - 1) / COLS_B);
+    if (grid <= 0) return hipSuccess;
+    const int nch = K / 128;
+    const int D = (nch % 4 == 0) ? 4 : (nch % 2 == 0 ? 2 : 1);
+    const size_t lds = PACKED ? 0 : (size_t)(ACT != ACT_NONE ? 2 : 1) * COLS_B * (K / 32);
+#define M8S_LAUNCH(DD)                                                                         \
+    hipLaunchKernelGGL((gemm_mx8_stream_kernel<ACT, OutT, DD, PACKED>), dim3((unsigned)grid),  \
+                       dim3(256), lds, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan,    \
+                       pa.hdr, N, K, out, ldo)
+    if (D == 4)
+        M8S_LAUNCH(4);
+    else if (D == 2)
+        M8S_LAUNCH(2);
+    else
+        M8S_LAUNCH(1);
+#undef M8S_LAUNCH
+    return hipGetLastError();
+}
+
 template <typename OutT, bool PACKED, int BM>
 static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t lda,
                           const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
@@ -449,26 +628,31 @@ static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t
 #undef MX8_ACT
 }
 
-// MX8 schedules: the 256-row tile (one tile row per expert of up to 256
-// rows, balanced groups) or the 128-row tile. AUTO and TILED take the 256-row
-// tile: it measured faster on every workload tried (about 146, 360 and 1170
+// MX8 schedules: the streaming one (16-row groups, fp32 or bf16 output) for
+// few rows per expert, as for the bf16 path (AUTO below a mean of 48 rows);
+// otherwise the 256-row tile (one tile row per expert of up to 256 rows,
+// balanced groups) or the 128-row tile. AUTO and TILED take the 256-row tile
+// there: it measured faster on every workload tried (about 146, 360 and 1170
 // mean rows per expert), the 128-row tile running one workgroup per CU too.
-int mx8_resolve_mode(int mode, int num_local, int max_rows)
+// MXFP8 output (q_out) is written by the tiled kernel only.
+int mx8_resolve_mode(int mode, int num_local, int max_rows, bool q_out)
 {
-    (void)num_local;
-    (void)max_rows;
+    if (!q_out && (mode == MOE_SCHED_STREAM ||
+                   (mode == MOE_SCHED_AUTO && (int64_t)max_rows < (int64_t)48 * num_local)))
+        return MOE_SCHED_STREAM;
     return mode == MOE_SCHED_TILE128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256;
 }
 
-GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws)
+GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws, bool q_out)
 {
-    return gemm_plan_args(num_local, max_rows, mx8_resolve_mode(mode, num_local, max_rows), ws);
+    return gemm_plan_args(num_local, max_rows, mx8_resolve_mode(mode, num_local, max_rows, q_out),
+                          ws);
 }
 
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows)
 {
-    // the 128-row grouping has the most work items
-    return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE128);
+    // the streaming schedule's 16-row grouping has the most work items
+    return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_STREAM);
 }
 
 hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
@@ -478,8 +662,33 @@ hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda
                                uint8_t *out_scales, int64_t ldo, int mode, void *plan_ws,
                                int packed, hipStream_t s)
 {
-    const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, mode, plan_ws);
-    const bool t256 = mx8_resolve_mode(mode, num_local, max_rows) == MOE_SCHED_TILE256;
+    const bool q_out = out_kind == MX8_OUT_MXFP8;
+    const GemmPlanArgs pa = mx8_plan_args(num_local, max_rows, mode, plan_ws, q_out);
+    const int md = mx8_resolve_mode(mode, num_local, max_rows, q_out);
+    if (md == MOE_SCHED_STREAM) {
+#define MX8_STREAM(OT, PK)                                                                      \
+    switch (act) {                                                                              \
+    case ACT_NONE:                                                                              \
+        return launch_mx8_stream<ACT_NONE, OT, PK>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, \
+                                                   N, K, (OT *)out, ldo, s);                    \
+    case ACT_SILU_MUL:                                                                          \
+        return launch_mx8_stream<ACT_SILU_MUL, OT, PK>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, \
+                                                       pa, N, K, (OT *)out, ldo, s);            \
+    case ACT_GELU_TANH_MUL:                                                                     \
+        return launch_mx8_stream<ACT_GELU_TANH_MUL, OT, PK>(ac, as, lda, a_rows, w1c, w1s, w2c, \
+                                                            w2s, pa, N, K, (OT *)out, ldo, s);  \
+    default:                                                                                    \
+        return hipErrorInvalidValue;                                                            \
+    }
+        if (out_kind == MX8_OUT_F32) {
+            if (packed) MX8_STREAM(float, true)
+            MX8_STREAM(float, false)
+        }
+        if (packed) MX8_STREAM(bf16, true)
+        MX8_STREAM(bf16, false)
+#undef MX8_STREAM
+    }
+    const bool t256 = md == MOE_SCHED_TILE256;
 #define MX8_RUN(OT, PK)                                                                        \
     return t256 ? mx8_act<OT, PK, 256>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, \
                                        (OT *)out, out_scales, ldo, s)                          \
@@ -505,8 +714,8 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
                                    int out_kind, uint8_t *out_scales, int64_t ldo, int mode,
                                    void *ws, int packed, hipStream_t s)
 {
-    hipError_t e = launch_gemm_plan_into(off, num_local,
-                                         mx8_plan_args(num_local, max_rows, mode, ws), s);
+    hipError_t e = launch_gemm_plan_into(
+        off, num_local, mx8_plan_args(num_local, max_rows, mode, ws, out_kind == MX8_OUT_MXFP8), s);
     if (e != hipSuccess) return e;
     return launch_gemm_mx8_run(ac, as, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
                                K, act, out, out_kind, out_scales, ldo, mode, ws, packed, s);

@@ -201,10 +201,12 @@ def test_mx8_validation():
     assert gemm(odt=2) == 1                   # MXFP8 output without its scales
     assert gemm(osc=FAKE) == 1                # scales with an fp32 output
     assert gemm(odt=3, osc=FAKE) == 1
-    assert gemm(mode=1) == 1                  # no streaming schedule in this mode
+    assert gemm(mode=1, odt=2, osc=FAKE, ldo=128) == 2  # MXFP8 output: tiled schedules only
     assert gemm(mode=5) == 1
-    bad = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8, mode=m.MODE_STREAM)
-    assert L.moe_layer_workspace_size(C.byref(bad)) == 0
+    # the streaming schedule needs the most plan space (16-row groups)
+    assert need >= m.moe_grouped_gemm_workspace_size(8, 64, 128, m.MODE_STREAM)
+    st = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8, mode=m.MODE_STREAM)
+    assert L.moe_layer_workspace_size(C.byref(st)) > 0
     # the layer's precision field
     p = m.layer_params(8, 3584, 896, 16, 128, precision=m.PREC_MX8)
     n_mx8 = m.moe_layer_workspace_size(p)

@@ -75,7 +75,7 @@ def _bound(a, w):
     return np.abs(a) @ np.abs(w).T
 
 
-@pytest.mark.parametrize("mode", [3, 4])
+@pytest.mark.parametrize("mode", [1, 3, 4])
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("K", [128, 640])
@@ -204,7 +204,7 @@ def _routing(inp, g):
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("mode", [0, 3])
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
 def test_small_layer_mx8_vs_oracle(m, cfg, packed, mode):
     """The whole MX8 layer against the oracle's MX8 layer on the GPU's scores.
     Both round h to E4M3 from fp32 values that differ by the instruction's
