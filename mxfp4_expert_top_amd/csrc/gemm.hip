@@ -4,10 +4,12 @@
 // section 二/第一层: 4-bit weights combined with higher-precision activations,
 // dequantise + multiply + accumulate in the kernel).
 //
-// MXFP4 codes go from HBM straight into registers, are decoded there with the
+// MXFP4 codes go from HBM into registers (the streaming schedule) or, still
+// 4-bit, into LDS (the tiled schedules), are decoded in registers with the
 // scaled FP4->bf16 convert (exact: an E2M1 value times a power of two), and
-// feed v_mfma_f32_16x16x32_bf16 with fp32 accumulation. No dequantised copy of
-// a weight ever reaches memory.
+// feed the bf16 matrix instructions (16x16x32 when streaming, 32x32x16 when
+// tiled) with fp32 accumulation. No dequantised copy of a weight ever
+// reaches memory.
 #include <type_traits>
 
 #include "common.hpp"
