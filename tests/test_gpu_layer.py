@@ -101,10 +101,24 @@ def test_packed_layout_layer_bitwise(cfg, mode):
         assert torch.equal(a[key], b[key]), key
 
 
-def test_determinism_bitwise(tiny):
+@pytest.mark.parametrize("mode", [0, 1, 3, 4])
+def test_determinism_bitwise(tiny, mode):
+    """No atomics on any value path: two runs agree bit for bit on every
+    schedule (the 256-row one with its direct-to-LDS loads included)."""
     gi = tiny.to(DEV)
-    a = run_gpu_layer(gi)
-    b = run_gpu_layer(gi)
+    a = run_gpu_layer(gi, mode=mode)
+    b = run_gpu_layer(gi, mode=mode)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("mode", [3, 4])
+def test_determinism_bitwise_many_rows(mode):
+    """The same at a size whose experts hold several 32-row tiles (and,
+    T >= 512, the tiled router's split-K planes)."""
+    gi = make_inputs(SMALL[6]).to(DEV)
+    a = run_gpu_layer(gi, mode=mode)
+    b = run_gpu_layer(gi, mode=mode)
     for key in a:
         assert torch.equal(a[key], b[key]), key
 
