@@ -117,14 +117,16 @@ def _check(fn, status):
         raise MoeError(fn, status, msg)
 
 
-def _dev(*ts):
+def _dev(*ts, strided=()):
+    """All tensors on one GPU and contiguous, except those in ``strided``
+    (whose strides the caller checks and passes on)."""
     dev = None
-    for t in ts:
+    for t in (*ts, *strided):
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError("all tensors must be on the GPU")
-        if not t.is_contiguous():
+        if not t.is_contiguous() and not any(t is u for u in strided):
             raise ValueError("tensors must be contiguous")
         if dev is None:
             dev = t.device
@@ -346,11 +348,21 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
     [>= max_rows, N/32]."""
     num_local = expert_offsets.shape[0] - 1
     N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
-    _dev(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
-         out, ws)
+    _dev(a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets, out, ws,
+         strided=(a_codes, a_scales))
     if a_codes.dtype != torch.uint8 or a_codes.dim() != 2 or a_codes.shape[1] != K:
         raise ValueError("a_codes must be [rows, K] uint8")
-    _want(a_scales, torch.uint8, (a_codes.shape[0], K // 32), "a_scales")
+    # rows may be strided (lda = a_codes.stride(0), a multiple of 32); the
+    # scales then have lda / 32 per row
+    lda = a_codes.stride(0) if a_codes.shape[0] > 1 else K
+    if a_codes.stride(1) != 1 or lda % 32 or lda < K:
+        raise ValueError("a_codes rows must be contiguous with a row stride that is a "
+                         "multiple of 32")
+    if (a_scales.dtype != torch.uint8 or a_scales.dim() != 2
+            or tuple(a_scales.shape) != (a_codes.shape[0], K // 32) or a_scales.stride(1) != 1
+            or (a_scales.shape[0] > 1 and a_scales.stride(0) != lda // 32)):
+        raise ValueError(f"a_scales must be uint8 [{a_codes.shape[0]}, {K // 32}] with row "
+                         f"stride {lda // 32}")
     _want(w1_codes, torch.uint8, (num_local, N, K // 2), "w1_codes")
     _want(w1_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w1_scales")
     if w2_codes is not None:
@@ -375,7 +387,7 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
         odt = _dt(out)
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib.moe_grouped_gemm_mx8(
-        _ptr(a_codes), _ptr(a_scales), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
+        _ptr(a_codes), _ptr(a_scales), lda, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K,
         MX_BLOCK, w_layout, act, _ptr(out), odt, _ptr(out_scales), N, mode, _ptr(ws), nbytes,
         _stream(stream))

@@ -158,6 +158,28 @@ __device__ __forceinline__ void store_out<float>(float *p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void store_out<bf16>(bf16 *p, float v) { *p = to_bf16(v); }
 
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from `src` to LDS at `lds_base` (wave-uniform) + 16 lane
+// (global_load_lds_dwordx4). The load counts in vmcnt like any vector load;
+// callers wait explicitly (the compiler's own wait insertion would otherwise
+// drain every such load before the next LDS read). M0 holds no compiler value
+// in the kernels that use it, so clobbering it needs no save.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // The same for outputs that are read once, much later, by another kernel (the
 // expert outputs Y before the combine): fp32 is stored with the non-temporal
 // hint, which measured 6% faster in the combine that reads it back.

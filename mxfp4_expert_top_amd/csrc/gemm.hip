@@ -788,27 +788,6 @@ __host__ __device__ constexpr int td_lds_bytes(int K)
     return TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K);
 }
 
-__device__ __forceinline__ uint32_t lds_address(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// 16 bytes per lane from `src` to LDS at `lds_base` (wave-uniform) + 16 lane.
-// The load counts in vmcnt like any vector load; the waits are explicit (the
-// compiler's own wait insertion would otherwise drain every such load before
-// the next LDS read). M0 holds no compiler value in these kernels, so
-// clobbering it needs no save.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // 16 waves (4 per SIMD) share the tile. Wave w takes row block q = w / 4
 // (64 rows: two 32-row tiles) and weight slot c = w % 4: for a GLU tile the
 // gate and up rows of output columns 32 c .. + 32, otherwise weight rows

@@ -410,6 +410,264 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The 256-row MX8 tile on 16 waves with direct global -> LDS loads (fp32 or
+// bf16 output, K <= M8D_MAX_K): the bf16 path's gemm_tile256_w16_kernel
+// arrangement on the block-scaled instruction.
+// - MXFP8 rows (64 bytes per K step) and 4-bit codes go into a three-stage
+//   LDS ring by global_load_lds_dwordx4; one barrier per K step publishes
+//   step k and frees the stage that step k + 2 overwrites.
+// - The tile's weight scales and its rows' scales (256 x K / 32 bytes each,
+//   rows padded to an odd number of dwords) are copied to LDS once.
+// - Wave w: row block q = w / 4 (two 32-row tiles) and slot c = w % 4 (gate
+//   and up rows of output columns 32 c .. + 32, or weight rows 64 c .. + 64),
+//   so every SIMD gets the same share of an expert's row tiles.
+// - A rows sit in LDS at 64 bytes with 16-byte chunk c of row r at position
+//   c ^ ((r / 4) % 4), so the 16 rows of a 16-lane read cover all banks;
+//   code rows as in the bf16 kernel.
+// ---------------------------------------------------------------------------
+constexpr int M8D_STAGES = 3;
+constexpr int M8D_A_BYTES = 256 * M8_BK;        // 16 KB of E4M3 rows
+constexpr int M8D_W_BYTES = M8_BN * M8_BK / 2;  // 8 KB of E2M1 codes
+constexpr int M8D_STAGE = M8D_A_BYTES + M8D_W_BYTES;
+constexpr int M8D_THREADS = 1024;
+constexpr int M8D_MAX_K = 4096;
+
+__host__ __device__ constexpr int m8d_scale_row(int K)
+{
+    return (((K / 32 + 3) / 4) | 1) * 4;
+}
+
+__host__ __device__ constexpr int m8d_lds_bytes(int K)
+{
+    return M8D_STAGES * M8D_STAGE + 2 * 256 * m8d_scale_row(K);
+}
+
+template <int ACT, typename OutT, bool PACKED>
+__global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
+    const uint8_t *__restrict__ ac, const uint8_t *__restrict__ as, int64_t lda,
+    const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
+    const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
+    const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
+    extern __shared__ __attribute__((aligned(16))) uint8_t m8d_lds[];
+    const int srow = m8d_scale_row(K);
+    uint8_t *const Wsc = m8d_lds + M8D_STAGES * M8D_STAGE;  // [256][srow] weight scales
+    uint8_t *const Asc = Wsc + 256 * srow;                   // [256][srow] row scales
+
+    const int nblk = (N + COLS - 1) / COLS;
+    const int total = plan[0] * nblk;
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int wi = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || wi >= total) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int2 it = ((const int2 *)(plan + hdr))[grp];
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
+    const int mrows = rend - r0;
+    const int n0 = nb * COLS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = wave & 3, q = wave >> 2;
+    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const int64_t lds_ = lda / 32;
+
+    auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
+        int wrow;
+        if (GLU) {
+            wrow = min(n0 + (br & 127), N - 1);
+            wc = br < 128 ? w1c : w2c;
+            ws = br < 128 ? w1s : w2s;
+        } else {
+            wrow = min(n0 + br, N - 1);
+            wc = w1c;
+            ws = w1s;
+        }
+        return (int64_t)e * N + wrow;
+    };
+    auto arow_of = [&](int row) -> int64_t {
+        const int rc = min(r0 + row, rend - 1);
+        return a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+    };
+
+    // ---- DMA sources. A: wave w fills rows 16 w .. + 15; lane L lands in
+    // chunk position L % 4 of row 16 w + L / 4, carrying logical chunk
+    // (L % 4) ^ ((L / 16) % 4).
+    const uint8_t *ag = ac + arow_of(16 * wave + (lane >> 2)) * lda +
+                        16 * ((lane & 3) ^ ((lane >> 4) & 3));
+    // codes: threads 0..511 -> LDS weight row tid / 2, half holding MX block bh
+    const bool wload = wave < 8;
+    const int br = (tid & 511) >> 1, bh = (tid & 1) ^ ((br >> 3) & 1);
+    const uint8_t *bg;
+    {
+        const uint8_t *wc, *ws;
+        const int64_t wr64 = wsel(br, wc, ws);
+        if constexpr (PACKED)
+            bg = wc + (wr64 / 16) * nch * 1024 + (wr64 % 16) * 16;
+        else
+            bg = wc + wr64 * (K / 2) + 16 * bh;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(m8d_lds));
+    auto issue = [&](int kt, int st) {
+        const uint32_t sb = lds0 + st * M8D_STAGE;
+        dma16(ag + kt * M8_BK, sb + wave * 1024);
+        if (wload) {
+            const uint8_t *src;
+            if constexpr (PACKED)
+                src = bg + (kt >> 1) * 1024 + (2 * (kt & 1) + bh) * 256;
+            else
+                src = bg + kt * (M8_BK / 2);
+            dma16(src, sb + M8D_A_BYTES + wave * 1024);
+        }
+    };
+
+    const int nk = K / M8_BK;  // even: K is a multiple of 128
+    issue(0, 0);
+    issue(1, 1);
+
+    // ---- scales -> LDS, in K-block order per row
+    if constexpr (PACKED) {
+        const int per_row = nc4 * 4;
+        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            const int cg = r >> 2, g = r & 3;
+            const uint8_t *wc, *ws;
+            const int64_t wr64 = wsel(row, wc, ws);
+            const uint32_t v = *(const uint32_t *)(ws + (wr64 / 16) * nc4 * 256 + cg * 256 +
+                                                   g * 64 + (wr64 % 16) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kb = 16 * cg + 4 * i + g;
+                if (kb < K / 32) Wsc[row * srow + kb] = (uint8_t)(v >> (8 * i));
+            }
+        }
+    } else {
+        const int per_row = K / 128;
+        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            const uint8_t *wc, *ws;
+            const int64_t wr64 = wsel(row, wc, ws);
+            *(uint32_t *)(Wsc + row * srow + 4 * r) =
+                *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+        }
+    }
+    if (lds_ % 4 == 0) {
+        const int per_row = K / 128;
+        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            *(uint32_t *)(Asc + row * srow + 4 * r) =
+                *(const uint32_t *)(as + arow_of(row) * lds_ + 4 * r);
+        }
+    } else {
+        const int per_row = K / 32;
+        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            Asc[row * srow + r] = as[arow_of(row) * lds_ + r];
+        }
+    }
+
+    // ---- wave tiles
+    const int h = lane >> 5, l32 = lane & 31;
+    int bt[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) bt[j] = GLU ? 128 * j + 32 * slot : 64 * slot + 32 * j;
+    const int n_on = (64 * q < mrows ? 1 : 0) + (64 * q + 32 < mrows ? 1 : 0);
+    const int arow_off = (64 * q + l32) * M8_BK;
+    const int akey = (l32 >> 2) & 3;
+    const int lo_off = (h ^ akey) << 4, hi_off = ((2 + h) ^ akey) << 4;
+    const int bpos = 16 * (h ^ ((l32 >> 3) & 1));
+
+    auto run = [&](auto ni_c) {
+        constexpr int NI = decltype(ni_c)::value;
+        f32x16 acc[NI > 0 ? NI : 1][2];
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+        auto compute = [&](int st, int kt) {
+            if constexpr (NI > 0) {
+                const uint8_t *A = m8d_lds + st * M8D_STAGE;
+                const uint8_t *Bq = A + M8D_A_BYTES;
+                i32x8 bv[2];
+                int sb[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int row = bt[j] + l32;
+                    const u32x4 w = *(const u32x4 *)(Bq + row * 32 + bpos);
+                    bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+                    sb[j] = Wsc[row * srow + 2 * kt + h];
+                }
+#pragma unroll
+                for (int i = 0; i < NI; i++) {
+                    const uint8_t *ar = A + arow_off + 32 * M8_BK * i;
+                    const u32x4 lo = *(const u32x4 *)(ar + lo_off);
+                    const u32x4 hi = *(const u32x4 *)(ar + hi_off);
+                    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                    const int sa = Asc[(64 * q + 32 * i + l32) * srow + 2 * kt + h];
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        // A format 0: E4M3; B format 4: E2M1; scale byte 0 of each
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            av, bv[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+                }
+            }
+        };
+
+        for (int kt = 0; kt < nk; kt++) {
+            // this wave's loads of step kt are done (those of kt + 1 -- 2 or 1
+            // instructions -- may still be in flight); the barrier publishes
+            // every wave's and ends the reads of step kt - 1
+            if (kt + 1 < nk) {
+                if (wload)
+                    asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(1)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+            const int st = kt % 3;
+            if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
+            compute(st, kt);
+        }
+
+        // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (rl >= mrows) continue;
+                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                if constexpr (GLU) {
+                    const int col = n0 + 32 * slot + l32;
+                    if (col < N)
+                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        const int col = n0 + 64 * slot + 32 * j + l32;
+                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
+                    }
+                }
+            }
+        }
+    };
+    // every branch runs the same barriers (nk) and the same loads
+    switch (__builtin_amdgcn_readfirstlane(n_on)) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+    }
+}
+
 template <int ACT, typename OutT, bool PACKED, int BM>
 static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
                              const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
@@ -423,6 +681,17 @@ static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
     // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
+    // fp32 / bf16 output on the 256-row tile: 16 waves, direct-to-LDS loads
+    if constexpr (BM == 256 && !std::is_same<OutT, uint8_t>::value) {
+        if (K <= M8D_MAX_K) {
+            auto kern = gemm_mx8_w16_kernel<ACT, OutT, PACKED>;
+            const hipError_t err = ensure_dynamic_lds((const void *)kern, m8d_lds_bytes(K));
+            if (err != hipSuccess) return err;
+            hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(M8D_THREADS), m8d_lds_bytes(K), s, ac,
+                               as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out, ldo);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED, BM>), dim3((unsigned)G), dim3(M8_THREADS),
                        0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out,
                        out_scales, ldo);

@@ -126,6 +126,49 @@ def test_grouped_gemm_mx8_vs_definition(m, act, packed, K, mode):
             assert (np.abs(got[r0:r1] - h) <= tol).all(), np.abs(got[r0:r1] - h).max()
 
 
+@pytest.mark.parametrize("mode", [1, 3, 4])
+def test_grouped_gemm_mx8_strided_rows(m, mode):
+    """Rows with a stride past K (lda = K + 32, so lda / 32 scale bytes per
+    row is not a whole number of dwords); the padding holds E4M3 NaN codes
+    and NaN scales, which must never be read."""
+    rng = np.random.default_rng(5 + mode)
+    nl, N, T, K, lda = 4, 320, 400, 128, 160
+    counts = np.array([70, 0, 290, 3], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    xc, xs = _mx8_rows(rng, T, K)
+    xc_full = np.full((T, lda), 0x7F, np.uint8)
+    xs_full = np.full((T, lda // 32), 0xFF, np.uint8)
+    xc_full[:, :K] = xc
+    xs_full[:, :K // 32] = xs
+    a_rows = rng.integers(0, T, size=A).astype(np.int32)
+    w1c, w1s = _experts(nl, N, K, 8)
+    w2c, w2s = _experts(nl, N, K, 9)
+    out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
+    gc = torch.from_numpy(xc_full).to(DEV)
+    gs = torch.from_numpy(xs_full).to(DEV)
+    m.moe_grouped_gemm_mx8(gc[:, :K], gs[:, :K // 32], torch.from_numpy(a_rows).to(DEV),
+                           w1c.to(DEV), w1s.to(DEV), w2c.to(DEV), w2s.to(DEV),
+                           torch.from_numpy(off).to(DEV), A, 1, out, ws, mode=mode)
+    torch.cuda.synchronize()
+    got = np_(out).astype(np.float64)
+    assert np.isfinite(got).all()
+    assert (got[A:] == 7.0).all()
+    xa = oracle.mxfp8_decode(xc, xs).astype(np.float64)[a_rows]
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        if r0 == r1:
+            continue
+        w1 = oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64)
+        w2 = oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64)
+        g, u = xa[r0:r1] @ w1.T, xa[r0:r1] @ w2.T
+        bg, bu = MMA_TOL * _bound(xa[r0:r1], w1), MMA_TOL * _bound(xa[r0:r1], w2)
+        h = g / (1.0 + np.exp(-g)) * u
+        tol = 1.1 * np.abs(u) * bg + (np.abs(g) + 0.28) * bu + 1e-5 * np.abs(h) + 1e-30
+        assert (np.abs(got[r0:r1] - h) <= tol).all(), np.abs(got[r0:r1] - h).max()
+
+
 def test_grouped_gemm_mx8_bf16_out_and_direct_rows(m):
     """No gathered rows (a_rows NULL), bf16 output, the down-projection shape
     (K = 1024, N = 3584 not a tile multiple of 256)."""
