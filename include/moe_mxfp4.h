@@ -87,8 +87,9 @@ enum moe_precision { MOE_PREC_BF16 = 0, MOE_PREC_MX8 = 1 };
  *   TILE256:  256-row x 256-weight-row tiles, an expert's rows cut into
  *             nearly equal groups (an expert of up to 256 rows reads its
  *             weights once)
- *   TILED:    TILE256 when max_rows / num_local <= 192, else TILE128
- *   AUTO:     STREAM when max_rows / num_local < 48, else TILED */
+ *   TILED:    TILE256 when 128 <= max_rows / num_local <= 256 or
+ *             max_rows >= 2^19, else TILE128
+ *   AUTO:     STREAM when max_rows / num_local < 16, else TILED */
 enum moe_sched {
     MOE_SCHED_AUTO = 0,
     MOE_SCHED_STREAM = 1,
@@ -267,10 +268,11 @@ int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K
  * moe_mxfp8_quantize does (blocks of 32 along N): codes to out [rows][ldo]
  * (bytes), scales to out_scales [rows][ldo/32] (NULL for the other dtypes).
  * mode: MOE_SCHED_STREAM streams the weights once per 16 rows (fp32 or bf16
- * output; with MOE_DT_MXFP8 -> UNSUPPORTED); MOE_SCHED_TILE128 for 128-row
- * tiles; MOE_SCHED_TILED and MOE_SCHED_TILE256 give 256-row tiles;
- * MOE_SCHED_AUTO streams below a mean of 48 rows per local expert (except
- * for MXFP8 output), else 256-row tiles. ws holds
+ * output; with MOE_DT_MXFP8 -> UNSUPPORTED); MOE_SCHED_TILE128 and
+ * MOE_SCHED_TILE256 give 128- and 256-row tiles; MOE_SCHED_TILED takes
+ * 128-row tiles below a mean of 128 rows per local expert, else 256-row
+ * tiles; MOE_SCHED_AUTO streams below a mean of 16 (except for MXFP8
+ * output), else as TILED. ws holds
  * moe_grouped_gemm_mx8_workspace_size(...) bytes.
  * Requirements: lda >= K, lda % 32 == 0, ldo >= N, ldo % 8 == 0 (% 32 for
  * MXFP8 output); 16-byte aligned code and scale arrays. Errors as

@@ -1053,27 +1053,30 @@ static int device_cus()
 }
 
 // Schedule choice from host-known sizes only: the mean rows per local expert
-// (max_rows / num_local) and the bound on rows itself. Below TILE_MIN_ROWS
-// the weight-streaming schedule (weights read once per 16 rows) wins. Up to
-// TILE256_MAX_MEAN a typical expert fits one 256-row tile, so the 256-row
-// schedule reads each weight byte once per expert. Above it the 128-row
-// schedule (two workgroups per CU) fills the chip with fewer rows, unless
-// the bound is so large (TILE256_MIN_BOUND rows: tens of thousands of tiles)
-// that the last partial wave of workgroups no longer matters and the 256-row
-// tile's weight reuse wins again.
-constexpr int TILE_MIN_ROWS = 48, TILE256_MAX_MEAN = 192;
+// (max_rows / num_local) and the bound on rows itself. Measured with all 896
+// experts (I = 1024) at mean rows 2 to 585:
+// - below a mean of 16 the weight-streaming schedule wins (it reads an
+//   expert's weights once per 16-row group, so from two groups on the tiled
+//   schedules, which read them once per 128 or 256 rows, pull ahead: 1.32 vs
+//   1.47 ms at a mean of 14, 1.77 vs 1.48 ms at 18);
+// - from 128 to 256 rows a typical expert is one well-filled 256-row tile,
+//   and the 256-row schedule is 4-7% faster than the 128-row one (146, 183,
+//   219 rows), level at 128 and 256;
+// - elsewhere the 128-row schedule (more, smaller tiles) is 2-7% faster,
+//   unless the bound is so large (TILE256_MIN_BOUND rows: tens of thousands
+//   of tiles) that the last partial wave of workgroups no longer matters and
+//   the 256-row tile's weight reuse wins again (long skewed prefill).
+constexpr int TILE_MIN_ROWS = 16, TILE256_MIN_MEAN = 128, TILE256_MAX_MEAN = 256;
 constexpr int64_t TILE256_MIN_BOUND = (int64_t)1 << 19;
 
 int resolve_mode(int mode, int num_local, int max_rows)
 {
     if (mode == MOE_SCHED_STREAM || mode == MOE_SCHED_TILE128 || mode == MOE_SCHED_TILE256)
         return mode;
-    if (mode == 0 && (int64_t)max_rows < (int64_t)TILE_MIN_ROWS * num_local)
-        return MOE_SCHED_STREAM;
-    return (int64_t)max_rows <= (int64_t)TILE256_MAX_MEAN * num_local ||
-                   (int64_t)max_rows >= TILE256_MIN_BOUND
-               ? MOE_SCHED_TILE256
-               : MOE_SCHED_TILE128;
+    const int64_t rows = max_rows, nl = num_local;
+    if (mode == 0 && rows < TILE_MIN_ROWS * nl) return MOE_SCHED_STREAM;
+    const bool window = rows >= TILE256_MIN_MEAN * nl && rows <= TILE256_MAX_MEAN * nl;
+    return window || rows >= TILE256_MIN_BOUND ? MOE_SCHED_TILE256 : MOE_SCHED_TILE128;
 }
 
 static int rows_per_group(int md)

@@ -897,19 +897,19 @@ static hipError_t mx8_act(int act, const uint8_t *ac, const uint8_t *as, int64_t
 #undef MX8_ACT
 }
 
-// MX8 schedules: the streaming one (16-row groups, fp32 or bf16 output) for
-// few rows per expert, as for the bf16 path (AUTO below a mean of 48 rows);
-// otherwise the 256-row tile (one tile row per expert of up to 256 rows,
-// balanced groups) or the 128-row tile. AUTO and TILED take the 256-row tile
-// there: it measured faster on every workload tried (about 146, 360 and 1170
-// mean rows per expert), the 128-row tile running one workgroup per CU too.
-// MXFP8 output (q_out) is written by the tiled kernel only.
+// MX8 schedules, measured with all 896 experts (I = 1024): streaming (16-row
+// groups, fp32 or bf16 output) below a mean of 16 rows per expert (0.91 vs
+// 1.49 ms at a mean of 5, 1.71 vs 1.62 ms at 18); the 128-row tile from 16 to
+// 128 (1.62-2.17 ms against 1.97-2.32 ms for the 256-row tile at means of 18
+// to 73); the 256-row tile from 128 up (faster at the means of 146, 360 and
+// 1170 rows tried). MXFP8 output (q_out) is written by the tiled kernels only.
 int mx8_resolve_mode(int mode, int num_local, int max_rows, bool q_out)
 {
-    if (!q_out && (mode == MOE_SCHED_STREAM ||
-                   (mode == MOE_SCHED_AUTO && (int64_t)max_rows < (int64_t)48 * num_local)))
+    const int64_t rows = max_rows, nl = num_local;
+    if (!q_out && (mode == MOE_SCHED_STREAM || (mode == MOE_SCHED_AUTO && rows < 16 * nl)))
         return MOE_SCHED_STREAM;
-    return mode == MOE_SCHED_TILE128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256;
+    if (mode == MOE_SCHED_TILE128 || mode == MOE_SCHED_TILE256) return mode;
+    return rows < 128 * nl ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256;
 }
 
 GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws, bool q_out)

@@ -41,12 +41,15 @@ def test_schedule_choice():
     # explicit schedules are kept; TILED never streams
     for md in (m.MODE_STREAM, m.MODE_TILE128, m.MODE_TILE256):
         assert m.moe_grouped_gemm_schedule(896, 64, md) == md
-    assert m.moe_grouped_gemm_schedule(896, 64, m.MODE_TILED) == m.MODE_TILE256
-    # the thresholds: mean rows 48 (stream below) and 192 (256-row tiles up to)
-    assert m.moe_grouped_gemm_schedule(10, 479) == m.MODE_STREAM
-    assert m.moe_grouped_gemm_schedule(10, 480) == m.MODE_TILE256
-    assert m.moe_grouped_gemm_schedule(10, 1920) == m.MODE_TILE256
-    assert m.moe_grouped_gemm_schedule(10, 1921) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(896, 64, m.MODE_TILED) == m.MODE_TILE128
+    # the thresholds: mean rows 16 (stream below), 128 and 256 (256-row tiles
+    # between)
+    assert m.moe_grouped_gemm_schedule(10, 159) == m.MODE_STREAM
+    assert m.moe_grouped_gemm_schedule(10, 160) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(10, 1279) == m.MODE_TILE128
+    assert m.moe_grouped_gemm_schedule(10, 1280) == m.MODE_TILE256
+    assert m.moe_grouped_gemm_schedule(10, 2560) == m.MODE_TILE256
+    assert m.moe_grouped_gemm_schedule(10, 2561) == m.MODE_TILE128
     # and a row bound of 2^19 or more: 256-row tiles whatever the mean
     assert m.moe_grouped_gemm_schedule(112, (1 << 19) - 1) == m.MODE_TILE128
     assert m.moe_grouped_gemm_schedule(112, 1 << 19) == m.MODE_TILE256
