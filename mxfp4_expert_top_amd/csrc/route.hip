@@ -215,12 +215,32 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 // step 32 of d covering all three planes: each token fragment read from LDS
 // feeds three planes' MFMAs. 8 waves of 128 tokens x 64 experts, so every
 // LDS fragment feeds 6 (token) or 4 (expert) MFMAs: 10 fragment reads per
-// 24 MFMAs, which keeps the LDS read rate well under its bandwidth (64 x 64
-// wave tiles needed 8 per 12). Both operands double-buffered in LDS (160 KB,
-// one workgroup per CU). blockIdx.y splits d into ranges whose partial sums
-// go to separate planes when the tile grid alone is too small for the chip.
+// 24 MFMAs (64 x 64 wave tiles needed 8 per 12). blockIdx.y splits d into
+// ranges whose partial sums go to separate planes when the tile grid alone
+// is too small for the chip.
+//
+// Operands go from memory straight into a two-stage LDS ring with
+// global_load_lds_dwordx4 (16 bytes per lane at the wave's LDS base + 16
+// lane): step k + 1 is in flight while step k's MFMAs run, and one wait and
+// barrier per step both publish step k + 1 and free step k's stage. A stage
+// holds 256 token rows and 3 x 256 weight rows of 64 bytes (32 bf16), 64 KB;
+// the 16-byte chunk c of row r sits at position c ^ ((r / 4) % 4), which
+// keeps the 32-lane fragment reads free of bank conflicts without padding.
+// 16 waves of 64 x 64 (RG_WAVES = 16) measured level with 8 waves.
 // ---------------------------------------------------------------------------
-constexpr int RG_BM = 256, RG_BN = 256, RG_BK = 32, RG_LD = RG_BK + 8, RG_THREADS = 512;
+constexpr int RG_BM = 256, RG_BN = 256, RG_BK = 32, RG_WAVES = 8, RG_THREADS = 64 * RG_WAVES;
+constexpr int RG_TPW = RG_BM / (RG_WAVES / 4), RG_NI = RG_TPW / 32;  // tokens per wave, 32-row tiles
+constexpr int RG_ROW = RG_BK * 2;                                 // bytes per LDS row
+constexpr int RG_A_BYTES = RG_BM * RG_ROW;                        // 16 KB
+constexpr int RG_STAGE = RG_A_BYTES + 3 * RG_BN * RG_ROW;         // 64 KB
+constexpr size_t RG_LDS = (size_t)2 * RG_STAGE;                   // 128 KB
+// 1 KB DMA blocks (16 rows) per stage: 16 token blocks, 48 weight blocks;
+// each wave moves an equal share of them
+constexpr int RG_A_DMA = RG_BM / 16 / RG_WAVES, RG_B_DMA = 3 * RG_BN / 16 / RG_WAVES;
+static_assert(RG_A_DMA * RG_WAVES * 16 == RG_BM && RG_B_DMA * RG_WAVES * 16 == 3 * RG_BN,
+              "DMA blocks split evenly over the waves");
+
+__device__ __forceinline__ int rg_swz(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(256) void split_router_kernel(const float *__restrict__ w,
                                                            int64_t n, bf16 *__restrict__ wp)
@@ -239,8 +259,6 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
     }
 }
 
-constexpr size_t RG_LDS = (size_t)2 * RG_BM * RG_LD * 2 + (size_t)2 * 3 * RG_BN * RG_LD * 2;
-
 __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
     const bf16 *__restrict__ x, const bf16 *__restrict__ wp, const float *__restrict__ bias,
     float *__restrict__ logits, int T, int d, int E, int ksteps_per_split,
@@ -249,9 +267,6 @@ __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
     if (zero_counts && blockIdx.x == 0 && blockIdx.y == 0)
         for (int i = threadIdx.x; i < E; i += blockDim.x) zero_counts[i] = 0;
     extern __shared__ __attribute__((aligned(16))) uint8_t rg_lds[];
-    bf16 (*As)[RG_BM][RG_LD] = (bf16 (*)[RG_BM][RG_LD])rg_lds;
-    bf16 (*Bs)[3][RG_BN][RG_LD] =
-        (bf16 (*)[3][RG_BN][RG_LD])(rg_lds + (size_t)2 * RG_BM * RG_LD * 2);
     const int n_nb = (E + RG_BN - 1) / RG_BN;
     // XCD-aware order: XCD b % 8 takes a contiguous range of tiles, token
     // block major, so the expert blocks of a token block share one L2
@@ -261,84 +276,89 @@ __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
     if ((int)(blockIdx.x / 8) >= per_xcd || wi >= tiles) return;
     const int mb = wi / n_nb, nb = wi - mb * n_nb;
     const int t0 = mb * RG_BM, e0 = nb * RG_BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;  // 128 tokens x 64 experts per wave
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases in M0
+    const int wm = wave >> 2, wn = wave & 3;  // RG_TPW tokens x 64 experts per wave
     const int h = lane >> 5, l32 = lane & 31;
     const int kt0 = blockIdx.y * ksteps_per_split, kt1 = kt0 + ksteps_per_split;
     logits += (int64_t)blockIdx.y * T * E;
     if (gridDim.y > 1) bias = nullptr;
 
-    // global -> LDS. A: thread -> token row tid / 2, 16 bf16 at 16 (tid % 2).
-    // B: 6 units of 8 bf16 per thread, unit u = tid + 512 i -> plane u / 1024,
-    // expert row (u % 1024) / 4, column 8 (u % 4).
-    const int ar = tid >> 1, ac = 16 * (tid & 1);
-    const bf16 *xa = x + (int64_t)min(t0 + ar, T - 1) * d + ac;
-    const bf16 *wb[6];
-    int bp[6], brow[6], bq[6];
+    // DMA sources. Within a 16-row block lane L fills LDS position L % 4 of
+    // row L / 4, so it loads the chunk that position holds. Rows past T or E
+    // repeat the last real row (their results are never stored).
+    const int dr = lane >> 2, dc = rg_swz(dr, lane & 3);
+    const bf16 *src[RG_A_DMA + RG_B_DMA];
 #pragma unroll
-    for (int i = 0; i < 6; i++) {
-        const int u = tid + RG_THREADS * i;
-        bp[i] = u >> 10;
-        brow[i] = (u & 1023) >> 2;
-        bq[i] = u & 3;
-        wb[i] = wp + ((int64_t)bp[i] * E + min(e0 + brow[i], E - 1)) * d + 8 * bq[i];
+    for (int i = 0; i < RG_A_DMA; i++) {
+        const int r = 16 * (RG_A_DMA * wave + i) + dr;
+        src[i] = x + (int64_t)min(t0 + r, T - 1) * d + 8 * dc;
     }
-    u32x4 ra[2], rb[6];
-    auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < RG_B_DMA; i++) {
+        const int blk = RG_B_DMA * wave + i, p = blk >> 4, r = 16 * (blk & 15) + dr;
+        src[RG_A_DMA + i] = wp + ((int64_t)p * E + min(e0 + r, E - 1)) * d + 8 * dc;
+    }
+    const uint32_t lds0 = lds_address(rg_lds);
+    auto issue = [&](int kt, int st) {
         const int k0 = kt * RG_BK;
-        ra[0] = *(const u32x4 *)(xa + k0);
-        ra[1] = *(const u32x4 *)(xa + k0 + 8);
+        const uint32_t base = lds0 + st * RG_STAGE;
 #pragma unroll
-        for (int i = 0; i < 6; i++) rb[i] = *(const u32x4 *)(wb[i] + k0);
+        for (int i = 0; i < RG_A_DMA; i++)
+            dma16(src[i] + k0, base + 1024 * (RG_A_DMA * wave + i));
+#pragma unroll
+        for (int i = 0; i < RG_B_DMA; i++)
+            dma16(src[RG_A_DMA + i] + k0, base + RG_A_BYTES + 1024 * (RG_B_DMA * wave + i));
     };
-    auto lstore = [&](int st) {
-        *(u32x4 *)(&As[st][ar][ac]) = ra[0];
-        *(u32x4 *)(&As[st][ar][ac + 8]) = ra[1];
+
+    f32x16 acc[RG_NI][2];
 #pragma unroll
-        for (int i = 0; i < 6; i++) *(u32x4 *)(&Bs[st][bp[i]][brow[i]][8 * bq[i]]) = rb[i];
-    };
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < RG_NI; i++)
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
-    // the wave's 128 tokens hold at least one real row and its 64 experts one real expert
-    const bool on = t0 + wm * 128 < T && e0 + wn * 64 < E;
+    // the wave's tokens hold at least one real row and its 64 experts one real expert
+    const bool on = t0 + wm * RG_TPW < T && e0 + wn * 64 < E;
+    // fragment rows: token rows wm RG_TPW + 32 i + l32, expert rows wn 64 + 32 j + l32
+    // (row / 4 % 4 is l32 / 4 % 4 for all of them)
+    const int swz = (l32 >> 2) & 3;
+    const int a_off = (wm * RG_TPW + l32) * RG_ROW, b_off = RG_A_BYTES + (wn * 64 + l32) * RG_ROW;
 
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
+    issue(kt0, 0);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     for (int kt = kt0; kt < kt1; kt++) {
         const int st = (kt - kt0) & 1;
-        if (kt + 1 < kt1) gload(kt + 1);
+        if (kt + 1 < kt1) issue(kt + 1, st ^ 1);
         if (on) {
+            const uint8_t *S = rg_lds + st * RG_STAGE;
 #pragma unroll
             for (int s = 0; s < 2; s++) {
-                bf16x8 a[4];
+                const int cpos = 16 * ((2 * s + h) ^ swz);
+                bf16x8 a[RG_NI];
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    a[i] = *(const bf16x8 *)(&As[st][wm * 128 + 32 * i + l32][16 * s + 8 * h]);
+                for (int i = 0; i < RG_NI; i++)
+                    a[i] = *(const bf16x8 *)(S + a_off + 32 * i * RG_ROW + cpos);
 #pragma unroll
                 for (int p = 0; p < 3; p++) {
 #pragma unroll
                     for (int j = 0; j < 2; j++) {
-                        const bf16x8 b =
-                            *(const bf16x8 *)(&Bs[st][p][wn * 64 + 32 * j + l32][16 * s + 8 * h]);
+                        const bf16x8 b = *(const bf16x8 *)(S + b_off + (p * RG_BN + 32 * j) * RG_ROW +
+                                                           cpos);
 #pragma unroll
-                        for (int i = 0; i < 4; i++) acc[i][j] = mfma32x32x16(a[i], b, acc[i][j]);
+                        for (int i = 0; i < RG_NI; i++) acc[i][j] = mfma32x32x16(a[i], b, acc[i][j]);
                     }
                 }
             }
         }
-        if (kt + 1 < kt1) lstore(st ^ 1);
-        __syncthreads();
+        // this wave's loads of step kt + 1 have landed and every wave is done
+        // with stage st: publish the one, free the other
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each 32 x 32 tile
     if (!on) return;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < RG_NI; i++) {
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int e = e0 + wn * 64 + 32 * j + l32;
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
             const float bb = bias ? bias[e] : 0.f;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int t = t0 + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                const int t = t0 + wm * RG_TPW + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (t < T) logits[(int64_t)t * E + e] = acc[i][j][v] + bb;
             }
         }

@@ -164,7 +164,12 @@ def test_route_t0_zeroes_counts(m):
 @pytest.mark.parametrize("T,d,E,bias", [(77, 3584, 896, False), (130, 256, 40, True),
                                         (1, 3584, 896, True), (16, 3584, 896, False),
                                         (20, 512, 40, True), (64, 3584, 896, True),
-                                        (33, 128, 17, False)])
+                                        (33, 128, 17, False),
+                                        # T >= 512 with d % 64 == 0 takes the tiled router:
+                                        # ragged token and expert blocks, and d split into
+                                        # 28, 8 and 4 partial sums (T=512, 1111, 2600)
+                                        (600, 3584, 896, True), (512, 3584, 896, False),
+                                        (1111, 256, 300, False), (2600, 128, 17, True)])
 def test_router_scores_and_replay(m, T, d, E, bias):
     from synth import make_router, make_tokens
     cfg = LayerConfig("r", T=T, I=128, d=d, E=E, bias="normal" if bias else None)
