@@ -54,7 +54,9 @@ __global__ __launch_bounds__(PERM_TB) void permute_count_kernel(
 // One workgroup: offsets over the local range, then per expert a scan of the
 // block counts (in place: blk[b][e] becomes block b's first row for e).
 // Expert counts come from `counts` (the histogram) or, when it is NULL, from
-// the block counts themselves.
+// the block counts themselves. Loading one block count at a time, each load
+// behind the previous store, took 93 us at 256 blocks; one wave per expert
+// (lanes over blocks) was slower still, 16 waves walking 896 experts.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     const int32_t *__restrict__ counts, int e0, int nl, int nblk, int32_t *__restrict__ off,
     int32_t *__restrict__ blk)
@@ -77,12 +79,20 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     if (lo + 1 < hi) off[lo + 1] = run + c0;
     if (tid == 0) off[nl] = total;
     __syncthreads();
+    // thread per expert (loads coalesce across experts); each chunk of block
+    // counts is loaded before its stores, so 16 loads are in flight per wait
     for (int le = tid; le < nl; le += 1024) {
         int r = off[le];
-        for (int b = 0; b < nblk; b++) {
-            int c = blk[(int64_t)b * nl + le];
-            blk[(int64_t)b * nl + le] = r;
-            r += c;
+        for (int b0 = 0; b0 < nblk; b0 += 16) {
+            int c[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * nl + le] : 0;
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                if (b0 + i < nblk) {
+                    blk[(int64_t)(b0 + i) * nl + le] = r;
+                    r += c[i];
+                }
         }
     }
 }
