@@ -463,7 +463,9 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(
     float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, int32_t *__restrict__ counts)
 {
-    constexpr int PB = NPL <= 16 ? 8 : 2;  // planes loaded per batch
+    // planes loaded per batch: 8 planes of 14 scores took 186 VGPRs (two waves
+    // per SIMD, the top-k of 16 K tokens 40 us); with 2, 76 VGPRs and 25 us
+    constexpr int PB = NPL <= 8 ? 8 : 2;
     __shared__ uint64_t s_key[4][64];
     __shared__ uint64_t s_ord[4][MOE_MAX_TOPK_DEV];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
