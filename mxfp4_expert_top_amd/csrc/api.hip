@@ -499,8 +499,10 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
                                     MX8_OUT_F32, nullptr, p->I, p->mode, base + L.gws, packed,
                                     s));
         if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-        // down stage: h to MXFP8, then the projection
-        HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s));
+        // down stage: h to MXFP8 (only the off[num_local] rows it holds: A is
+        // the host bound, T k, eight times the local rows on an EP share), then
+        // the projection
+        HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s, off + p->num_local));
         HIP_TRY(launch_gemm_mx8_run(hq, hs, p->I, nullptr, down_codes, down_scales, nullptr,
                                     nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y,
                                     MX8_OUT_F32, nullptr, p->d, p->mode, base + L.gws, packed,

@@ -117,7 +117,8 @@ hipError_t launch_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int
 // mx8.hip: the block-scaled precision mode (MXFP8 activations x MXFP4
 // weights on v_mfma_scale_f32_32x32x64_f8f6f4)
 hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
-                                 uint8_t *codes, uint8_t *scales, hipStream_t s);
+                                 uint8_t *codes, uint8_t *scales, hipStream_t s,
+                                 const int32_t *n_dev = nullptr);
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows);
 // MOE_SCHED_TILE128 or MOE_SCHED_TILE256 for a requested mode (AUTO / TILED
 // choose as the bf16 tiled schedules do)

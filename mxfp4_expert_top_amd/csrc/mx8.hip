@@ -92,52 +92,61 @@ __device__ __forceinline__ void load32<bf16>(const bf16 *p, float v[32])
     }
 }
 
+// Rows n < min(N, *n_dev) (all N rows when n_dev is null: a device-side row
+// count, so a buffer sized for the host bound is converted only as far as it
+// holds rows); one thread per 32-element block, grid-stride.
 template <typename InT>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const InT *__restrict__ v,
                                                              int64_t ldv, int64_t N, int K,
+                                                             const int32_t *__restrict__ n_dev,
                                                              uint8_t *__restrict__ codes,
                                                              uint8_t *__restrict__ scales)
 {
     const int nb = K / 32;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= N * nb) return;
-    const int64_t n = i / nb;
-    const int b = (int)(i - n * nb);
-    float x[32];
-    load32<InT>(v + n * ldv + 32 * b, x);
-    float amax = 0.0f;
+    const int64_t rows = n_dev ? min(N, (int64_t)max(*n_dev, 0)) : N;
+    const int64_t total = rows * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = i / nb;
+        const int b = (int)(i - n * nb);
+        float x[32];
+        load32<InT>(v + n * ldv + 32 * b, x);
+        float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(x[j]));
-    float inv;
-    const int s = mxfp8_scale(amax, inv);
-    uint8_t *c = codes + n * (int64_t)K + 32 * b;
+        for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(x[j]));
+        float inv;
+        const int s = mxfp8_scale(amax, inv);
+        uint8_t *c = codes + n * (int64_t)K + 32 * b;
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        u32x4 w;
+        for (int h = 0; h < 2; h++) {
+            u32x4 w;
 #pragma unroll
-        for (int d = 0; d < 4; d++) {
-            uint32_t word = 0;
+            for (int d = 0; d < 4; d++) {
+                uint32_t word = 0;
 #pragma unroll
-            for (int j = 0; j < 4; j++) word |= e4m3_code(x[16 * h + 4 * d + j] * inv) << (8 * j);
-            w[d] = amax == 0.0f ? 0u : word;
+                for (int j = 0; j < 4; j++) word |= e4m3_code(x[16 * h + 4 * d + j] * inv) << (8 * j);
+                w[d] = amax == 0.0f ? 0u : word;
+            }
+            *(u32x4 *)(c + 16 * h) = w;
         }
-        *(u32x4 *)(c + 16 * h) = w;
+        scales[n * nb + b] = (uint8_t)s;
     }
-    scales[n * nb + b] = (uint8_t)s;
 }
 
 hipError_t launch_mxfp8_quantize(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
-                                 uint8_t *codes, uint8_t *scales, hipStream_t s)
+                                 uint8_t *codes, uint8_t *scales, hipStream_t s,
+                                 const int32_t *n_dev)
 {
     const int64_t nb = N * (K / 32);
     if (nb <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+    // at most 16 K workgroups (64 per CU); larger inputs loop
+    const dim3 grid((unsigned)std::min<int64_t>((nb + 255) / 256, 16384)), block(256);
     if (v_f32)
         hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, block, 0, s, (const float *)v, ldv,
-                           N, K, codes, scales);
+                           N, K, n_dev, codes, scales);
     else
         hipLaunchKernelGGL(mxfp8_quantize_kernel<bf16>, grid, block, 0, s, (const bf16 *)v, ldv,
-                           N, K, codes, scales);
+                           N, K, n_dev, codes, scales);
     return hipGetLastError();
 }
 

@@ -58,6 +58,21 @@ def test_mxfp8_quantize_bf16_rows_with_stride(m):
     assert np.array_equal(np_(s), rs) and np.array_equal(np_(c), rc)
 
 
+def test_mxfp8_quantize_grid_stride(m):
+    """More 32-element blocks (140000 x 32) than the launch's threads (16384 x 256): the
+    threads past the first pass's end and rows on both sides of the wrap, against the oracle."""
+    N, K = 140000, 1024
+    g = torch.Generator(device=DEV).manual_seed(7)
+    v = torch.randn(N, K, generator=g, device=DEV) * 2.0
+    c, s = m.moe_mxfp8_quantize(v)
+    torch.cuda.synchronize()
+    wrap = 16384 * 256 // (K // 32)  # first row of the second pass
+    rows = np.r_[0:4, wrap - 4:wrap + 4, N - 4:N]
+    rc, rs = oracle.mxfp8_quantize(v[torch.from_numpy(rows).to(DEV)].cpu().numpy())
+    assert np.array_equal(np_(s)[rows], rs)
+    assert np.array_equal(np_(c)[rows], rc)
+
+
 # ---------------------------------------------------------------- projection
 def _experts(num_local, N, K, seed):
     g = torch.Generator().manual_seed(seed)
