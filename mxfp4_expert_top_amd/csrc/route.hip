@@ -249,14 +249,19 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
     if (i >= n) return;
     const float4 v = *(const float4 *)(w + i);
     const float vv[4] = {v.x, v.y, v.z, v.w};
+    // one 8-byte store per plane
+    bf16x4 h, md, lo;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        bf16 h, md, lo;
-        split3_bf16(vv[c], h, md, lo);
-        wp[i + c] = h;
-        wp[n + i + c] = md;
-        wp[2 * n + i + c] = lo;
+        bf16 a, b, e;
+        split3_bf16(vv[c], a, b, e);
+        h[c] = a;
+        md[c] = b;
+        lo[c] = e;
     }
+    *(bf16x4 *)(wp + i) = h;
+    *(bf16x4 *)(wp + n + i) = md;
+    *(bf16x4 *)(wp + 2 * n + i) = lo;
 }
 
 __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
