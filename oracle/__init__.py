@@ -79,6 +79,10 @@ def lib():
         L.oracle_layer_lora.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i64, i64, i64,
                                         p, p, p, p, p, p, i32, p, p, p, p, p, p, i64,
                                         C.c_float, p, p, p, p, p, p, p]
+        L.oracle_token_rows_lora.restype = i32
+        L.oracle_token_rows_lora.argtypes = [p, i64, i64, i64, p, p, p, i64, i64, i64,
+                                             p, p, p, p, p, p, i32, p, p, p, p, p, p, i64,
+                                             C.c_float, p]
         _lib = L
     return _lib
 
@@ -327,3 +331,23 @@ def layer_lora(x, w_router, bias, wts, lora, *, E, k, I, rank, scale, e0=0, n_lo
         raise MemoryError("oracle_layer_lora failed")
     return dict(out=out, logits=lg, idx=idx, w=w, counts=counts, off=off,
                 perm=perm[:A], inv=inv, A=int(A))
+
+
+def token_rows_lora(x, idx, w, tokens, wts, lora, *, I, rank, scale, e0=0, n_local,
+                    act=ACT_SILU_MUL):
+    """The LoRA layer's output rows for the listed tokens only, from their
+    routing. ``lora`` as in layer_lora, indexed by local expert."""
+    xb = bf16_bits(x)
+    T, d = xb.shape
+    idx, w = _arr(idx, np.int32), _arr(w, np.float32)
+    k = idx.shape[1]
+    tokens = _arr(np.asarray(tokens, np.int64), np.int64)
+    w6 = _weights(wts)
+    ad = [bf16_bits(lora[n]) for n in LORA_NAMES]
+    out = np.empty((tokens.shape[0], d), np.float32)
+    rc = lib().oracle_token_rows_lora(_ptr(xb), d, I, k, _ptr(idx), _ptr(w), _ptr(tokens),
+                                      tokens.shape[0], e0, n_local, *[_ptr(a) for a in w6], act,
+                                      *[_ptr(a) for a in ad], rank, float(scale), _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle_token_rows_lora failed")
+    return out

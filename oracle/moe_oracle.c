@@ -797,3 +797,45 @@ int64_t oracle_layer_lora(const uint16_t *x, const float *w_router, const float 
     free(xt);
     return rc == 0 ? A : -1;
 }
+
+/* The LoRA layer's output for chosen tokens only, given their routing: as
+ * oracle_token_rows, with each selected local expert's FFN carrying its
+ * adapters (expert_ffn_lora). Used where the whole LoRA layer is too slow. */
+int oracle_token_rows_lora(const uint16_t *x, int64_t d, int64_t I, int64_t k,
+                           const int32_t *idx, const float *w, const int64_t *tokens,
+                           int64_t n_tokens, int64_t e0, int64_t n_local,
+                           const uint8_t *gc, const uint8_t *gs, const uint8_t *uc,
+                           const uint8_t *us, const uint8_t *dc, const uint8_t *ds, int act,
+                           const uint16_t *ga, const uint16_t *gb, const uint16_t *ua,
+                           const uint16_t *ub, const uint16_t *da, const uint16_t *db, int64_t r,
+                           float scale, float *out_rows)
+{
+    ffn_scratch sc;
+    if (scratch_alloc(&sc, d, I)) {
+        scratch_free(&sc);
+        return -1;
+    }
+    int rc = 0;
+    for (int64_t q = 0; q < n_tokens && rc == 0; q++) {
+        int64_t t = tokens[q];
+        float *o = out_rows + q * d;
+        for (int64_t m = 0; m < d; m++) o[m] = 0.0f;
+        token_input(x, t, d, 0, sc.xc, sc.xs, sc.xt);
+        for (int64_t j = 0; j < k && rc == 0; j++) {
+            int64_t le = (int64_t)idx[t * k + j] - e0;
+            if (le < 0 || le >= n_local) continue;
+            decoded_expert we;
+            if (decode_expert(gc, gs, uc, us, dc, ds, le, d, I, &we)) {
+                rc = -1;
+                break;
+            }
+            rc = expert_ffn_lora(sc.xt, &we, ga, gb, ua, ub, da, db, le, d, I, r, scale, act,
+                                 sc.y);
+            free_expert(&we);
+            if (rc == 0)
+                for (int64_t m = 0; m < d; m++) o[m] += w[t * k + j] * sc.y[m];
+        }
+    }
+    scratch_free(&sc);
+    return rc;
+}

@@ -76,3 +76,23 @@ def test_lora_layer_vs_dense(cfg, rank):
     base = dense_lora_layer(inp.x.float().numpy(), r["idx"], r["w"], _np(inp.weights), lora,
                             E=cfg.E, e0=cfg.expert_begin, n_local=cfg.num_local, scale=0.0)
     assert rel_l2(r["out"], base) > 1e-2
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
+def test_token_rows_lora_vs_dense(cfg):
+    """The per-token form (used at workload sizes, where the whole LoRA
+    layer is too slow) against the same dense fp64 evaluation, and equal to
+    the whole layer's rows: the same sums per token, in the same order."""
+    rank, scale = 8, 0.5
+    inp = make_inputs(cfg)
+    lora = make_lora(cfg, rank)
+    r = _run(inp, lora, rank, scale)
+    toks = sorted({0, cfg.T // 2, cfg.T - 1})
+    rows = oracle.token_rows_lora(inp.x, r["idx"], r["w"], toks, _np(inp.weights), lora, I=cfg.I,
+                                  rank=rank, scale=scale, e0=cfg.expert_begin,
+                                  n_local=cfg.num_local)
+    ref = dense_lora_layer(inp.x.float().numpy(), r["idx"], r["w"], _np(inp.weights), lora,
+                           E=cfg.E, e0=cfg.expert_begin, n_local=cfg.num_local, scale=scale)
+    assert rel_l2(rows, ref[toks]) <= 1e-5
+    assert max_abs_over_rms(rows, ref[toks]) <= 1e-4
+    assert np.array_equal(rows, r["out"][toks])
