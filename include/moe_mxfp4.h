@@ -374,8 +374,10 @@ typedef struct {
 /* moe_layer_lora -- moe_layer with the adapters applied (bf16 precision
  * only). The increment must land before the activation. With a rank that
  * is a multiple of 16 it is added inside the grouped GEMMs (every schedule),
- * from rank factors rounded to bf16; otherwise the gate and up projections
- * run unfused (fp32 outputs, the increments, then the activation). Workspace: moe_layer_lora_workspace_size(p, rank) bytes (0 if
+ * from fp32 rank factors carried as an exact hi + lo pair of bf16 parts;
+ * otherwise the gate and up projections run unfused (fp32 outputs, the
+ * increments, then the activation). Workspace:
+ * moe_layer_lora_workspace_size(p, rank) bytes (0 if
  * invalid). Errors as moe_layer, plus a NULL lora or adapter, or an adapter
  * not 16-byte aligned -> INVALID_ARG, rank outside 1..MOE_MAX_LORA_RANK or
  * the MX8 precision -> UNSUPPORTED. */

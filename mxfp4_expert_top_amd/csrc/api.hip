@@ -563,9 +563,9 @@ struct LoraWs {
     size_t g, u, t, total;
 };
 
-// The increment rides in the GEMMs (rank factors in bf16, one more MFMA per
-// output tile and 16 or 32 ranks) when the rank is a multiple of 16;
-// otherwise the gate and up projections run unfused.
+// The increment rides in the GEMMs (rank factors as hi + lo bf16 parts, two
+// more MFMAs per output tile and 16 or 32 ranks) when the rank is a multiple
+// of 16; otherwise the gate and up projections run unfused.
 bool lora_fused(const moe_layer_params *p, int rank)
 {
     (void)p;
@@ -579,9 +579,9 @@ LoraWs lora_layer_ws(const moe_layer_params *p, int rank)
     const size_t A = (size_t)p->T * p->k;
     size_t o = W.L.total;
     if (lora_fused(p, rank)) {
-        // three bf16 rank-factor arrays (gate, up, down)
+        // three rank-factor arrays (gate, up, down), hi and lo bf16 parts
         W.g = W.u = 0;
-        W.t = o; o += 3 * round_up(A * (size_t)rank * 2);
+        W.t = o; o += 3 * round_up(A * (size_t)rank * 4);
     } else {
         W.g = o; o += round_up(A * (size_t)p->I * 4);
         W.u = o; o += round_up(A * (size_t)p->I * 4);
@@ -663,9 +663,9 @@ int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, con
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     const bf16 *xb = (const bf16 *)x;
     if (lora_fused(p, r)) {
-        // rank factors first (bf16), then the projections with the increment
-        // added to their accumulators before the activation / output
-        const size_t tb = round_up((size_t)A * r * 2);
+        // rank factors first (hi + lo bf16), then the projections with the
+        // increment added to their accumulators before the activation / output
+        const size_t tb = round_up((size_t)A * r * 4);
         bf16 *tg = (bf16 *)(base + W.t), *tu = (bf16 *)(base + W.t + tb),
              *td = (bf16 *)(base + W.t + 2 * tb);
         HIP_TRY(launch_lora_t_plan(xb, p->d, perm, (const bf16 *)lora->gate_a,

@@ -111,11 +111,12 @@ __host__ __device__ constexpr int stream_cols_per_wave()
 
 // LoRA increment of the streaming schedule (rank a multiple of 8, at most
 // 64): each stream's 16 x 16 accumulator tile gains sum_k t[row][k] B[col][k]
-// (t = the scaled rank factors, bf16 [rows][rank]; B = the expert's adapter
-// rows, bf16 [N][rank]) as one more 16x16x32 MFMA per 32-wide slice of the
-// rank. Lane group g supplies elements 8 g .. + 8 of the slice for its token
-// row (A operand) and its weight row (B operand); groups past the rank
-// supply zeros.
+// (t = the scaled rank factors, stored per row as bf16 hi [0, rank) and lo
+// [rank, 2 rank) parts whose sum is the fp32 factor to 16 significant bits;
+// B = the expert's adapter rows, bf16 [N][rank]) as two more 16x16x32 MFMAs
+// (hi, then lo, on the same B fragment) per 32-wide slice of the rank. Lane
+// group g supplies elements 8 g .. + 8 of the slice for its token row (A
+// operand) and its weight row (B operand); groups past the rank supply zeros.
 template <int ACT, typename OutT, int D, bool PACKED, bool LORA>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(
     const bf16 *__restrict__ a, int64_t lda, const int32_t *__restrict__ a_rows,
@@ -226,7 +227,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     if constexpr (!PACKED) __syncthreads();  // scales in LDS
     if (!wave_on) return;
     // LoRA operands, in flight behind the first chunks
-    bf16x8 lt[2][2], lbf[2][NS];
+    // rank factors as hi and lo bf16 parts (row: hi [0, rank), lo [rank, 2 rank))
+    bf16x8 lt[2][2][2], lbf[2][NS];
     if constexpr (LORA) {
         const bf16x8 z = {};
 #pragma unroll
@@ -236,9 +238,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
             const int kk = on ? k0 : 0;  // a valid address either way
 #pragma unroll
             for (int t = 0; t < (GLU ? 2 : 1); t++) {
-                const bf16x8 v = *(const bf16x8 *)((t ? lora.t2 : lora.t1) +
-                                                   (int64_t)rc * lora.rank + kk);
-                lt[c][t] = on ? v : z;
+                const bf16 *tr = (t ? lora.t2 : lora.t1) + (int64_t)rc * 2 * lora.rank + kk;
+                const bf16x8 vh = *(const bf16x8 *)tr;
+                const bf16x8 vl = *(const bf16x8 *)(tr + lora.rank);
+                lt[c][t][0] = on ? vh : z;
+                lt[c][t][1] = on ? vl : z;
             }
 #pragma unroll
             for (int j = 0; j < NS; j++) {
@@ -267,8 +271,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
         for (int c = 0; c < 2; c++) {
             if (32 * c >= lora.rank) break;
 #pragma unroll
-            for (int j = 0; j < NS; j++)
-                acc[j] = mfma16x16x32(lt[c][GLU && (j & 1)], lbf[c][j], acc[j]);
+            for (int j = 0; j < NS; j++) {
+                acc[j] = mfma16x16x32(lt[c][GLU && (j & 1)][0], lbf[c][j], acc[j]);
+                acc[j] = mfma16x16x32(lt[c][GLU && (j & 1)][1], lbf[c][j], acc[j]);
+            }
         }
     }
 
@@ -323,14 +329,21 @@ constexpr int TL_ALD = TL_BK + TL_APAD;      // 72 bf16 = 144 bytes per row
 // acc += T[trow][0..rank) . B[bcol][0..rank) over a 32 x 32 tile: the MFMA
 // operand of lane L is row (A) or column (B) L % 32 with contraction elements
 // 8 (L / 32) .. + 8 of each 16-wide step, which is how both factors are
-// stored (rank contiguous per row / per weight row).
+// stored (rank contiguous per row / per weight row). A row of T holds the
+// rank factors as two bf16 parts, hi [0, rank) and lo [rank, 2 rank) with
+// hi + lo the fp32 factor to 16 significant bits; both meet the same B
+// fragment, so the increment carries the factor's fp32 precision rather than
+// one bf16 rounding of it.
 __device__ __forceinline__ f32x16 lora_add(f32x16 acc, const bf16 *t, int64_t trow,
                                            const bf16 *b, int64_t bcol, int rank, int h)
 {
+    const bf16 *tr = t + trow * 2 * rank + 8 * h;
     for (int k0 = 0; k0 < rank; k0 += 16) {
-        const bf16x8 af = *(const bf16x8 *)(t + trow * rank + k0 + 8 * h);
+        const bf16x8 ahi = *(const bf16x8 *)(tr + k0);
+        const bf16x8 alo = *(const bf16x8 *)(tr + rank + k0);
         const bf16x8 bv = *(const bf16x8 *)(b + bcol * rank + k0 + 8 * h);
-        acc = mfma32x32x16(af, bv, acc);
+        acc = mfma32x32x16(ahi, bv, acc);
+        acc = mfma32x32x16(alo, bv, acc);
     }
     return acc;
 }

@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void lora_t_kernel(const bf16 *__restrict__ x,
 // kc + 32 h .. + 32 of its row and of its column (64 contiguous bytes, four
 // 16-byte loads) and MFMA step s (0..3) takes elements kc + 32 h + 8 s .. + 8
 // of both, so every product x[k] A[j][k] enters exactly once. The loads of
-// chunk c + 1 are issued before chunk c is consumed.
+// chunk c + 1 are issued before chunk c is consumed. Output rows hold the
+// hi and lo bf16 parts of each factor (2 rank bf16 per row).
 //
 // Items of at most 32 rows (the streaming schedule's groups) leave a single
 // wave per item, which cannot keep enough loads in flight to stream the
@@ -200,7 +201,11 @@ __global__ __launch_bounds__(512) void lora_t_mfma_kernel(
 #pragma unroll
             for (int g = 0; g < NT; g++) acc[g] += part[i][g][lane];
     }
-    // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each column tile
+    // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each column tile. Each
+    // factor is stored as two bf16 parts, hi = bf16(v) at column c and
+    // lo = bf16(v - hi) at column rank + c of a row of 2 rank: v - hi is exact
+    // in fp32, and hi + lo matches v to 16 significant bits, so the
+    // increment's MFMAs see the fp32 factor rather than one bf16 rounding.
 #pragma unroll
     for (int g = 0; g < NT; g++) {
         const int c = 32 * g + l32;
@@ -209,7 +214,13 @@ __global__ __launch_bounds__(512) void lora_t_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int rr = 8 * (v >> 2) + 4 * hf + (v & 3);
-            if (rr < nr) tc[(int64_t)(r0 + rr) * rank] = to_bf16(scale * acc[g][v]);
+            if (rr < nr) {
+                const float f = scale * acc[g][v];
+                const bf16 hi = to_bf16(f);
+                bf16 *dst = tc + (int64_t)(r0 + rr) * 2 * rank;
+                dst[0] = hi;
+                dst[rank] = to_bf16(f - (float)hi);
+            }
         }
     }
 }
