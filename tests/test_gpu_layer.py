@@ -14,7 +14,7 @@ import torch
 import oracle
 from synth import CONFIGS, LayerConfig, make_inputs
 from tests.parity_util import (LOGIT_TOL, W_TOL, assert_close_layer, host_weights, np_,
-                               oracle_rows, run_gpu_layer)
+                               oracle_rows, run_gpu_layer, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -124,41 +124,63 @@ def test_determinism_bitwise_many_rows(mode):
 
 
 # ---------------------------------------------------------------- full sizes
-def _sample_tokens(cfg, idx, n_random, seed=0):
-    """Random tokens, first/last tokens, the first and last token of the
-    hottest local expert's segment, and a token with no local expert."""
-    rng = np.random.default_rng(seed)
-    toks = set(rng.choice(cfg.T, size=min(n_random, cfg.T), replace=False).tolist())
-    toks |= {0, cfg.T - 1}
-    loc = idx - cfg.expert_begin
-    is_loc = (loc >= 0) & (loc < cfg.num_local)
-    counts = np.bincount(loc[is_loc], minlength=cfg.num_local)
-    hot = int(counts.argmax())
-    users = np.nonzero((loc == hot).any(1))[0]
-    toks |= {int(users[0]), int(users[-1])}
-    none = np.nonzero(~is_loc.any(1))[0]
-    if len(none):
-        toks.add(int(none[0]))
-    return sorted(toks)
+def _check_dispatch(inp, lg, r_idx):
+    """The dispatch arrays on every token at full size: moe_route on the
+    layer's own fp32 scores (given, not recomputed) and moe_permute -- the
+    layer's bitmap counting path, and the path fed the top-k kernel's
+    histogram -- against the oracle's histogram, offsets and permutation of
+    the replayed routing, bit for bit."""
+    import mxfp4_expert_top_amd as m
+    c = inp.cfg
+    T, k, E = c.T, c.k, c.E
+    logits = torch.from_numpy(lg).to(DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    m.moe_route(None, None, None, logits, 1, idx, w, counts)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(idx), r_idx)
+    r_cnt = oracle.histogram(r_idx, E)
+    assert np.array_equal(np_(counts), r_cnt)
+    r_off = oracle.offsets(r_cnt, c.expert_begin, c.num_local)
+    r_perm, r_inv = oracle.permute(r_idx, r_off, c.expert_begin, c.num_local)
+    A = int(r_off[-1])
+    ws = m.alloc_workspace(m.moe_permute_workspace_size(T, c.num_local), DEV)
+    for cnt in (None, counts):
+        off = torch.full((c.num_local + 1,), -7, dtype=torch.int32, device=DEV)
+        perm = torch.full((T * k,), -7, dtype=torch.int32, device=DEV)
+        inv = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+        m.moe_permute(idx, cnt, c.expert_begin, c.num_local, off, perm, inv, ws, E=E)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(off), r_off)
+        assert np.array_equal(np_(perm)[:A], r_perm[:A])
+        assert np.array_equal(np_(inv), r_inv)
+    return r_cnt, A
 
 
-@pytest.mark.parametrize("name,n_random", [("decode", 10), ("prefill", 6), ("ep_share", 6),
-                                           ("long_skewed_prefill", 3)])
-def test_full_size_workload(name, n_random):
+@pytest.mark.parametrize("name", ["decode", "prefill", "ep_share", "long_skewed_prefill"])
+def test_full_size_workload(name):
     """The benchmark's launch configuration: weights converted to the streaming
-    layout at load, schedule chosen automatically, bf16 output."""
+    layout at load, schedule chosen automatically, fp32 output. Routing and
+    dispatch arrays on every token; the output on 64 sampled tokens (segment
+    edges, the hottest expert, a token with no local expert, seeded random)
+    evaluated one by one by the oracle. The bf16 output is then checked, on
+    every token, to be exactly the fp32 output rounded to nearest-even: the
+    only difference between the two is that final rounding, which on its own
+    reaches about 0.024 rms on heavy-tailed rows, most of the 3e-2 rms
+    max-abs budget."""
     import mxfp4_expert_top_amd as m
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, DEV)
-    g = run_gpu_layer(inp, packed=m.prepack_weights(inp.weights))
+    packed = m.prepack_weights(inp.weights)
+    g = run_gpu_layer(inp, packed=packed, out_dtype=torch.float32)
     lg, r_idx, _ = _check_routing(inp, g)
     # scores of a few tokens against the oracle's own router product
     _check_scores(inp, lg, rows=[0, cfg.T // 2, cfg.T - 1])
-    # dispatch arrays: the oracle's permutation of the replayed routing
-    cnt = oracle.histogram(r_idx, cfg.E)
-    off = oracle.offsets(cnt, cfg.expert_begin, cfg.num_local)
-    assert off[-1] > 0
-    toks = _sample_tokens(cfg, r_idx, n_random)
+    _, A = _check_dispatch(inp, lg, r_idx)
+    assert A > 0
+    toks = sample_tokens(cfg, r_idx, 64)
+    assert len(toks) == min(64, cfg.T)
     ref = oracle_rows(inp, r_idx, np_(g["w"]), toks)
     got = g["out"].float().cpu().numpy()[toks]
     assert_close_layer(got, ref, name)
@@ -167,5 +189,8 @@ def test_full_size_workload(name, n_random):
     none = ~((loc >= 0) & (loc < cfg.num_local)).any(1)
     if none.any():
         assert (g["out"][torch.as_tensor(np.nonzero(none)[0], device=DEV)] == 0).all()
-    del inp, g
+    b = run_gpu_layer(inp, packed=packed, out_dtype=torch.bfloat16)
+    assert torch.equal(b["idx"], g["idx"])
+    assert torch.equal(b["out"], g["out"].to(torch.bfloat16))
+    del inp, g, b, packed
     torch.cuda.empty_cache()

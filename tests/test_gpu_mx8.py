@@ -18,7 +18,7 @@ import torch
 import oracle
 from synth import CONFIGS, LayerConfig, make_inputs, quantize_mxfp4
 from tests.parity_util import (assert_close_layer, host_weights, np_, oracle_rows, rel_l2,
-                               run_gpu_layer)
+                               run_gpu_layer, sample_tokens)
 from tests.test_oracle_mx8 import _blocks
 
 pytestmark = pytest.mark.gpu
@@ -294,18 +294,18 @@ def test_mx8_layer_determinism_bitwise(m):
         assert torch.equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("name", ["prefill", "decode", "ep_share"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "ep_share", "long_skewed_prefill"])
 def test_full_size_mx8(m, name):
-    """The prefill workload (and the decode batch) in the MX8 mode, in the
-    benchmark's launch configuration: sampled tokens' rows against the
-    oracle's MX8 rows on the GPU's routing."""
+    """The workloads in the MX8 mode, in the benchmark's launch configuration
+    (fp32 output): 64 sampled tokens' rows (segment edges, the hottest
+    expert, seeded random) against the oracle's MX8 rows on the GPU's
+    routing."""
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, DEV)
-    g = run_gpu_layer(inp, precision=m.PREC_MX8, packed=m.prepack_weights(inp.weights))
+    g = run_gpu_layer(inp, precision=m.PREC_MX8, packed=m.prepack_weights(inp.weights),
+                      out_dtype=torch.float32)
     _, r_idx, _ = _routing(inp, g)
-    rng = np.random.default_rng(1)
-    toks = sorted(set(rng.choice(cfg.T, size=min(5, cfg.T), replace=False).tolist())
-                  | {0, cfg.T - 1})
+    toks = sample_tokens(cfg, r_idx, 64, seed=1)
     ref = oracle_rows(inp, r_idx, np_(g["w"]), toks, mx8=True)
     assert_close_layer(g["out"].float().cpu().numpy()[toks], ref, name)
     del inp, g
