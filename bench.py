@@ -6,7 +6,10 @@ in HBM. Prints one JSON line: whole-layer tokens/s, the dominant kernel's
 roofline fraction (from HIP events recorded on the launch stream inside the
 timed steps), and the oracle's CPU rate on a bounded token sample.
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill|...]
+    python bench.py [--steps K] [--warmup W] [--workload long_skewed_prefill|decode|...]
+
+The default workload is the largest one that fits one GPU: a long skewed
+prefill chunk of 65,536 tokens (I = 2048, Zipf(1.1) expert popularity).
 """
 
 from __future__ import annotations
@@ -36,7 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--workload", default="long_skewed_prefill",
+                    choices=["tiny", "decode", "prefill", "ep_share", "long_skewed_prefill"])
     ap.add_argument("--mode", type=int, default=0,
                     help="GEMM schedule (enum moe_sched): 0 auto, 1 stream, 2 tiled, "
                          "3 128-row tiles, 4 256-row tiles")
@@ -47,8 +51,9 @@ def parse():
     ap.add_argument("--lora-rank", type=int, default=0,
                     help="> 0: the layer with rank-R LoRA adapters (scale 0.5) on every local "
                          "expert's three projections (moe_layer_lora; bf16 precision only)")
-    ap.add_argument("--cpu-tokens", type=int, default=24,
-                    help="tokens the oracle CPU baseline evaluates (0 = skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=-1,
+                    help="tokens the oracle CPU baseline evaluates: -1 = every token of "
+                         "batches up to 64 tokens, else a 16-token sample; 0 = skip")
     ap.add_argument("--weights", default="packed", choices=["packed", "ocp"],
                     help="expert weight layout: converted at load (packed) or canonical")
     ap.add_argument("--quantize-probe-mib", type=int, default=0,
@@ -74,16 +79,66 @@ def algorithmic(cfg, A, U, out_bytes=2):
     return layer_bytes, layer_flops, gu_bytes, gu_flops
 
 
-def cpu_baseline(inp, n_tokens, mx8=False):
-    """The oracle, as it stands, on `n_tokens` seeded tokens of the same
-    workload: router scores, top-k, softmax and every selected expert's FFN
-    and the weighted combine of each token. Single-threaded."""
+def host_weights(weights, local_ids):
+    """numpy copies of the listed local experts' weight arrays."""
+    ids = None
+    out = {}
+    for n, t in weights.items():
+        if ids is None:
+            ids = torch.as_tensor(local_ids, device=t.device)
+        out[n] = t[ids].cpu().numpy()
+    return out
+
+
+def cpu_sample(cfg, idx, n_tokens, seed=1):
+    """The oracle leg's tokens, from the GPU's routing of the batch: the first
+    and last token of the largest and of the smallest non-empty local expert
+    segment, up to four more tokens of the hottest expert, and seeded random
+    tokens for the rest. Every token when the batch is no larger than
+    ``n_tokens``."""
+    if cfg.T <= n_tokens:
+        return np.arange(cfg.T), f"all {cfg.T} tokens"
+    loc = idx - cfg.expert_begin
+    is_loc = (loc >= 0) & (loc < cfg.num_local)
+    counts = np.bincount(loc[is_loc], minlength=cfg.num_local)
+    nz = np.nonzero(counts)[0]
+    big, small = int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])
+    users = {e: np.nonzero((loc == e).any(1))[0] for e in (big, small)}
+    picks = [users[big][0], users[big][-1], users[small][0], users[small][-1]]
+    hot = users[big]
+    picks += list(hot[np.linspace(0, len(hot) - 1, 6).astype(int)[1:-1]])
+    toks = list(dict.fromkeys(int(t) for t in picks))
+    n_edges = len(toks)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(cfg.T), toks)
+    toks += rng.choice(rest, size=max(0, n_tokens - len(toks)), replace=False).tolist()
+    how = (f"{len(toks)} of {cfg.T} tokens: {n_edges} at the first and last rows of the largest "
+           f"({int(counts[big])} rows) and smallest ({int(counts[small])} rows) local expert "
+           f"segments and inside the hottest one, {len(toks) - n_edges} seeded random")
+    return np.sort(np.array(toks)), how
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline(inp, idx_gpu, n_tokens, mx8=False):
+    """The oracle, as it stands, on a sample of the same workload: router
+    scores, top-k, softmax and every selected expert's FFN and the weighted
+    combine of each sampled token. Single-threaded, the process pinned to one
+    core for the timed part (its affinity restored afterwards)."""
     import oracle
-    from tests.parity_util import host_weights
 
     cfg = inp.cfg
-    rng = np.random.default_rng(1)
-    toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    toks, how = cpu_sample(cfg, idx_gpu, n_tokens)
     xs = inp.x[torch.as_tensor(toks, device=inp.x.device)].cpu()
     w_r = inp.w_router.cpu().numpy()
     bias = None if inp.bias is None else inp.bias.cpu().numpy()
@@ -96,36 +151,45 @@ def cpu_baseline(inp, n_tokens, mx8=False):
     remap = np.full(cfg.num_local, -1, np.int64)
     remap[used] = np.arange(len(used))
 
-    t0 = time.perf_counter()
-    lg = oracle.router_logits(xs, w_r, bias)
-    idx, w = oracle.topk_softmax(lg, cfg.k)
-    loc = idx - cfg.expert_begin
-    cidx = np.full(idx.shape, -1, np.int32)
-    ok = (loc >= 0) & (loc < cfg.num_local)
-    cidx[ok] = remap[loc[ok]]
-    oracle.token_rows(xs, cidx, w, np.arange(len(toks)), wts, I=cfg.I, e0=0,
-                      n_local=max(len(used), 1), mx8=mx8)
-    dt = time.perf_counter() - t0
+    model, nproc = cpu_info()
+    aff = os.sched_getaffinity(0)
+    core = max(aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(xs, w_r, bias)
+        idx, w = oracle.topk_softmax(lg, cfg.k)
+        loc = idx - cfg.expert_begin
+        cidx = np.full(idx.shape, -1, np.int32)
+        ok = (loc >= 0) & (loc < cfg.num_local)
+        cidx[ok] = remap[loc[ok]]
+        oracle.token_rows(xs, cidx, w, np.arange(len(toks)), wts, I=cfg.I, e0=0,
+                          n_local=max(len(used), 1), mx8=mx8)
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, aff)
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(toks)} of {cfg.T} tokens of the same workload, whole layer per "
-                      f"token (router scores over {cfg.E} experts, top-{cfg.k}, softmax, "
-                      f"{cfg.k} MXFP4 expert FFNs with I={cfg.I}"
+            "nproc": nproc, "cpu_model": model, "pinned_core": core,
+            "sample": f"{how}; whole layer per token (router scores over {cfg.E} experts, "
+                      f"top-{cfg.k}, softmax, {cfg.k} MXFP4 expert FFNs with I={cfg.I}"
                       f"{' on MXFP8 tokens and h' if mx8 else ''}, weighted combine), "
-                      f"single-threaded fp32 C; {dt:.1f} s"}
+                      f"single-threaded fp32 C on one pinned core; {dt:.1f} s"}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_stream_gate_up_decode_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SRC = os.path.join(ROOT, "mxfp4_expert_top_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the gate/up kernel from the committed counter
-    summary, or None if the kernel source changed since it was taken."""
+def measured_traffic(summary):
+    """HBM bytes per launch of the roofline kernel from its committed counter
+    summary ``profiles/<summary>``, or None if there is none or the kernel
+    source changed since the counters were taken."""
     import hashlib
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -206,11 +270,14 @@ def main():
     else:
         layer_weights = inp.weights
     p = m.layer_params(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.expert_begin, cfg.num_local,
-                       mode=args.mode,
+                       mode=args.mode, out_dtype=m.DT_F32,
                        weight_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP,
                        precision=m.PREC_MX8 if mx8 else m.PREC_BF16)
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
-    out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
+    # fp32 layer output: the form the parity tests hold to the stated bounds
+    # (a bf16 output is that result rounded to nearest-even, whose rounding
+    # alone takes most of the max-abs budget on heavy-tailed rows)
+    out = torch.empty(cfg.T, cfg.d, dtype=torch.float32, device=dev)
     idx = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -269,7 +336,7 @@ def main():
     A = int(local.sum())
     counts = np.bincount(ii[local], minlength=cfg.num_local)
     U = int((counts > 0).sum())
-    lb, lf, gb, gf = algorithmic(cfg, A, U)
+    lb, lf, gb, gf = algorithmic(cfg, A, U, out_bytes=4)
 
     # The dominant kernel is the gate/up projection: weight streaming (HBM
     # bound) for few rows per expert, a tiled bf16 GEMM (MFMA bound) otherwise.
@@ -304,7 +371,8 @@ def main():
     elif sched == m.MODE_STREAM:
         roof = {"kernel": "gemm_stream_kernel<SILU_MUL> (gate/up projection)", "bound": "hbm",
                 "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                "frac": round(gb / gu_s / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(f"gemm_stream_gate_up_{cfg.name}_traffic.txt"),
                 "algorithmic_bytes_per_launch": int(gb),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
     else:
@@ -314,7 +382,9 @@ def main():
         roof = {"kernel": f"{name}<SILU_MUL> (gate/up projection)", "bound": "mfma",
                 "achieved": round(gf / gu_s / 1e12, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "algorithmic_flops_per_launch": int(gf),
+                "traffic": measured_traffic(f"{name}_gate_up_{cfg.name}_traffic.txt"),
+                "algorithmic_flops_per_launch": int(gf),
+                "algorithmic_bytes_per_launch": int(gb),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
 
     res = {
@@ -333,7 +403,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "experts_computed": cfg.num_local,
                    "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
-                   "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else "bf16",
+                   "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else "bf16", "output": "fp32",
                    "lora_rank": args.lora_rank, "routing_bias": cfg.bias},
         "roofline": roof,
         "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),
@@ -346,9 +416,10 @@ def main():
                   "ms_per_step_with_stage_events": round(ms_step_staged, 4)},
         "cpu_baseline": None,
     }
-    if args.cpu_tokens > 0 and args.lora_rank == 0:
+    if args.cpu_tokens != 0 and args.lora_rank == 0:
         inp.weights = canonical
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens, mx8=mx8)
+        n_cpu = args.cpu_tokens if args.cpu_tokens > 0 else (64 if cfg.T <= 64 else 16)
+        res["cpu_baseline"] = cpu_baseline(inp, idx.cpu().numpy(), n_cpu, mx8=mx8)
     print(json.dumps(res), flush=True)
 
 

@@ -67,7 +67,8 @@ class LayerConfig:
         return replace(self, **kw)
 
 
-# The five workloads of the benchmark suite. Index 1 is the headline workload.
+# The five workloads of the benchmark suite. The last, the largest that fits
+# one GPU, is the headline workload.
 CONFIGS: Dict[str, LayerConfig] = {
     "tiny": LayerConfig(
         "tiny", T=8, I=128,
