@@ -339,6 +339,36 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
               size_t ws_bytes, void **stage_events, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_layer_noalloc -- moe_layer for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It takes no workspace: its scratch is a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends (its address is looked up once per device,
+ * on the first call with that device current). It calls no hipMalloc,
+ * hipFree or allocating routine; the caller still owns x, the weights, out
+ * and the optional routing copies, as for moe_layer.
+ *
+ * Arguments, layouts and results are moe_layer's (no workspace, no stage
+ * events); the kernels and their results are the same. The scratch used is
+ * the current device's (hipGetDevice): `stream` must belong to that device.
+ * Every call on one GPU shares its scratch, so calls that overlap on one GPU
+ * (two streams, two threads) race: serialise them. Nothing is carried from
+ * one call to the next: each call writes every scratch word it reads.
+ *
+ * Errors: as moe_layer; parameters whose moe_layer_workspace_size exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES -> MOE_ERR_WORKSPACE before any HIP call, with
+ * the sizes in moe_last_error() (64 MiB holds, for example, the 64-token
+ * decode batch at d = 3584, 896 experts, top-16, I = 1024: 18 MB).
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_noalloc(const moe_layer_params *p, const void *x, const float *w_router,
+                      const float *bias, const uint8_t *gate_codes, const uint8_t *gate_scales,
+                      const uint8_t *up_codes, const uint8_t *up_scales,
+                      const uint8_t *down_codes, const uint8_t *down_scales, void *out,
+                      float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
+                      moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * LoRA on the MXFP4 base (P1 section 二, 第五层: the large quantised base
  * stays frozen and a low-rank increment is trained on top of it).
  * ------------------------------------------------------------------------ */
@@ -391,7 +421,8 @@ int moe_layer_lora(const moe_layer_params *p, const moe_lora_adapters *lora, con
 
 /* Static text for a status code. */
 const char *moe_status_string(int status);
-/* The calling thread's last HIP error message ("" if none). */
+/* The calling thread's last error message: the last HIP error, or the size
+ * message of moe_layer_noalloc ("" if none). */
 const char *moe_last_error(void);
 
 #ifdef __cplusplus

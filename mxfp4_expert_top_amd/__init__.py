@@ -71,6 +71,8 @@ def _load(path=None):
     L.moe_layer_workspace_size.argtypes = [p]
     L.moe_layer.restype = i32
     L.moe_layer.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, p, p, sz, p, p]
+    L.moe_layer_noalloc.restype = i32
+    L.moe_layer_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, p, p, p, p, p, p]
     L.moe_mxfp8_quantize.restype = i32
     L.moe_mxfp8_quantize.argtypes = [p, i32, i64, i64, i32, p, p, p]
     L.moe_grouped_gemm_mx8_workspace_size.restype = sz
@@ -97,7 +99,8 @@ EXPORTED = ("moe_route", "moe_permute", "moe_permute_workspace_size", "moe_mxfp4
             "moe_mxfp4_prepack", "moe_mxfp4_packed_scale_bytes",
             "moe_grouped_gemm_mxfp4", "moe_grouped_gemm_workspace_size",
             "moe_grouped_gemm_schedule", "moe_combine",
-            "moe_layer", "moe_layer_workspace_size", "moe_status_string", "moe_last_error",
+            "moe_layer", "moe_layer_workspace_size", "moe_layer_noalloc", "moe_status_string",
+            "moe_last_error",
             "moe_mxfp8_quantize", "moe_grouped_gemm_mx8", "moe_grouped_gemm_mx8_workspace_size",
             "moe_grouped_lora", "moe_grouped_lora_workspace_size", "moe_layer_lora",
             "moe_layer_lora_workspace_size")
@@ -446,7 +449,7 @@ def _layer_args(p, x, w_router, bias, weights, out, ws, logits_out, topk_idx_out
         _want(topk_idx_out, torch.int32, (p.T, p.k), "topk_idx_out")
     if topk_w_out is not None:
         _want(topk_w_out, torch.float32, (p.T, p.k), "topk_w_out")
-    nbytes = ws.numel() * ws.element_size()
+    nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     ev = None
     if stage_events is not None:
         if len(stage_events) != 6:
@@ -472,6 +475,27 @@ def moe_layer(params: LayerParams, x, w_router, bias, weights, out, ws, logits_o
 
 
 _WNAMES = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+
+# Bytes of the static device scratch of moe_layer_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_noalloc(params: LayerParams, x, w_router, bias, weights, out, logits_out=None,
+                      topk_idx_out=None, topk_w_out=None, stream=None):
+    """moe_layer without a workspace: the library's static per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) instead. The tensors' GPU is made current for the
+    call, as the scratch is looked up on the current device."""
+    p = params
+    _layer_args(p, x, w_router, bias, weights, out, None, logits_out, topk_idx_out, topk_w_out,
+                None, stream)
+    with torch.cuda.device(x.device):
+        st = lib.moe_layer_noalloc(C.byref(p), _ptr(x), _ptr(w_router), _ptr(bias),
+                                   *[_ptr(weights[n]) for n in _WNAMES], _ptr(out),
+                                   _ptr(logits_out), _ptr(topk_idx_out), _ptr(topk_w_out),
+                                   _stream(stream))
+    if st == MOE_ERR_WORKSPACE:  # the sizes are in the thread's last error message
+        raise MoeError("moe_layer_noalloc", st, lib.moe_last_error().decode())
+    _check("moe_layer_noalloc", st)
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:

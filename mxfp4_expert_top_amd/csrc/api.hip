@@ -12,6 +12,11 @@
 
 using namespace moe;
 
+// Scratch of moe_layer_noalloc, for callers that cannot allocate: a device
+// array of MOE_NOALLOC_SCRATCH_BYTES, one copy per GPU the library runs on,
+// held until the process ends. Calls on one GPU share it.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -441,15 +446,14 @@ size_t moe_layer_workspace_size(const moe_layer_params *p)
     return layer_ws(p).total;
 }
 
-int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, const float *bias,
-              const uint8_t *gate_codes, const uint8_t *gate_scales, const uint8_t *up_codes,
-              const uint8_t *up_scales, const uint8_t *down_codes, const uint8_t *down_scales,
-              void *out, float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
-              size_t ws_bytes, void **stage_events, moe_stream_t stream)
+namespace {
+// Pointer checks shared by moe_layer and moe_layer_noalloc (the parameters
+// already checked).
+int check_layer_ptrs(const void *x, const float *w_router, const uint8_t *gate_codes,
+                     const uint8_t *gate_scales, const uint8_t *up_codes,
+                     const uint8_t *up_scales, const uint8_t *down_codes,
+                     const uint8_t *down_scales, const void *out)
 {
-    int rc = check_layer_params(p);
-    if (rc) return rc;
-    if (p->T == 0) return MOE_OK;
     CHECK(x && w_router && out && gate_codes && gate_scales && up_codes && up_scales &&
               down_codes && down_scales,
           MOE_ERR_INVALID_ARG);
@@ -457,11 +461,19 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
     CHECK(aligned(gate_codes, 16) && aligned(up_codes, 16) && aligned(down_codes, 16) &&
               aligned(gate_scales, 16) && aligned(up_scales, 16) && aligned(down_scales, 16),
           MOE_ERR_INVALID_ARG);
-    const LayerWs L = layer_ws(p);
-    rc = check_ws(ws, ws_bytes, L.total);
-    if (rc) return rc;
+    return MOE_OK;
+}
 
-    char *base = (char *)ws;
+// The layer's launch sequence over the scratch at `base` (L.total bytes,
+// 256-byte aligned). Every scratch word a kernel reads was written earlier in
+// the same call, so the scratch need not start cleared.
+int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const void *x,
+              const float *w_router, const float *bias, const uint8_t *gate_codes,
+              const uint8_t *gate_scales, const uint8_t *up_codes, const uint8_t *up_scales,
+              const uint8_t *down_codes, const uint8_t *down_scales, void *out,
+              float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void **stage_events,
+              moe_stream_t stream)
+{
     float *logits = logits_out ? logits_out : (float *)(base + L.logits);
     int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(base + L.idx);
     float *w = topk_w_out ? topk_w_out : (float *)(base + L.w);
@@ -528,6 +540,86 @@ int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, c
                            p->out_dtype == MOE_DT_F32, p->d, s));
     if (ev) HIP_TRY(hipEventRecord(ev[5], s));
     return MOE_OK;
+}
+
+// The scratch of moe_layer_noalloc is `scratch` (file scope, above). In host
+// code that name is a host-side stand-in, never the device memory: kernels
+// get the address hipGetSymbolAddress returns for the current device, looked
+// up once per device on its first call and kept in g_scratch_ptr.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+int noalloc_scratch(char **base)
+{
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        g_last_error = "moe_layer_noalloc: device ordinal outside the scratch table";
+        return MOE_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr || !aligned(ptr, 256)) {
+            g_last_error = "moe_layer_noalloc: scratch symbol address missing or misaligned";
+            return MOE_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *base = (char *)g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+int moe_layer(const moe_layer_params *p, const void *x, const float *w_router, const float *bias,
+              const uint8_t *gate_codes, const uint8_t *gate_scales, const uint8_t *up_codes,
+              const uint8_t *up_scales, const uint8_t *down_codes, const uint8_t *down_scales,
+              void *out, float *logits_out, int32_t *topk_idx_out, float *topk_w_out, void *ws,
+              size_t ws_bytes, void **stage_events, moe_stream_t stream)
+{
+    int rc = check_layer_params(p);
+    if (rc) return rc;
+    if (p->T == 0) return MOE_OK;
+    rc = check_layer_ptrs(x, w_router, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                          down_scales, out);
+    if (rc) return rc;
+    const LayerWs L = layer_ws(p);
+    rc = check_ws(ws, ws_bytes, L.total);
+    if (rc) return rc;
+    return layer_run(p, L, (char *)ws, x, w_router, bias, gate_codes, gate_scales, up_codes,
+                     up_scales, down_codes, down_scales, out, logits_out, topk_idx_out,
+                     topk_w_out, stage_events, stream);
+}
+
+int moe_layer_noalloc(const moe_layer_params *p, const void *x, const float *w_router,
+                      const float *bias, const uint8_t *gate_codes, const uint8_t *gate_scales,
+                      const uint8_t *up_codes, const uint8_t *up_scales,
+                      const uint8_t *down_codes, const uint8_t *down_scales, void *out,
+                      float *logits_out, int32_t *topk_idx_out, float *topk_w_out,
+                      moe_stream_t stream)
+{
+    int rc = check_layer_params(p);
+    if (rc) return rc;
+    if (p->T == 0) return MOE_OK;
+    rc = check_layer_ptrs(x, w_router, gate_codes, gate_scales, up_codes, up_scales, down_codes,
+                          down_scales, out);
+    if (rc) return rc;
+    const LayerWs L = layer_ws(p);
+    if (L.total > MOE_NOALLOC_SCRATCH_BYTES) {
+        g_last_error = "moe_layer_noalloc: these parameters need " + std::to_string(L.total) +
+                       " bytes of scratch, more than the " +
+                       std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES) +
+                       "-byte static scratch; use moe_layer with a workspace";
+        return MOE_ERR_WORKSPACE;
+    }
+    char *base = nullptr;
+    rc = noalloc_scratch(&base);
+    if (rc) return rc;
+    return layer_run(p, L, base, x, w_router, bias, gate_codes, gate_scales, up_codes,
+                     up_scales, down_codes, down_scales, out, logits_out, topk_idx_out,
+                     topk_w_out, nullptr, stream);
 }
 
 size_t moe_grouped_lora_workspace_size(int max_rows, int rank)

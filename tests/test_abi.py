@@ -260,3 +260,25 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         m.moe_combine(x, torch.zeros(4, 2, dtype=torch.int32), torch.zeros(4, 2), x)
+
+
+def test_layer_noalloc_rejects_sizes_beyond_its_scratch():
+    """moe_layer_noalloc checks the scratch its parameters need against its
+    static maximum before any HIP call, and says why in moe_last_error()."""
+    L = m.lib
+    big = m.layer_params(4096, 3584, 896, 16, 1024)  # about 1 GB of scratch
+    assert m.moe_layer_workspace_size(big) > m.NOALLOC_SCRATCH_BYTES
+    # x, w_router, bias, the six weight arrays, out; no routing copies; stream
+    args = [FAKE, FAKE, None] + [FAKE] * 6 + [FAKE] + [None] * 4
+    assert L.moe_layer_noalloc(C.byref(big), *args) == m.MOE_ERR_WORKSPACE
+    msg = L.moe_last_error().decode()
+    assert "moe_layer_noalloc" in msg and str(m.NOALLOC_SCRATCH_BYTES) in msg
+    # the decode batch fits (the size check passes; no call is made here)
+    dec = m.layer_params(64, 3584, 896, 16, 1024)
+    assert m.moe_layer_workspace_size(dec) <= m.NOALLOC_SCRATCH_BYTES
+    # T == 0: a no-op before any pointer is looked at
+    p0 = m.layer_params(0, 3584, 896, 16, 128)
+    assert L.moe_layer_noalloc(C.byref(p0), *([None] * 14)) == 0
+    # parameters are checked as for moe_layer
+    bad = m.layer_params(8, 3584, 896, 16, 96)
+    assert L.moe_layer_noalloc(C.byref(bad), *args) == m.MOE_ERR_UNSUPPORTED
