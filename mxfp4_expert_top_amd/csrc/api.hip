@@ -130,7 +130,7 @@ LayerWs layer_ws(const moe_layer_params *p)
                                           : router_skinny_splits(p->T, p->d, p->E, 256);
     L.logits = o; o += round_up(T * E * 4);
     L.planes = o; o += L.splits > 1 ? round_up((size_t)L.splits * T * E * 4) : 0;
-    L.wsplit = o; o += L.router == ROUTER_TILED ? round_up(3 * E * (size_t)p->d * 2) : 0;
+    L.wsplit = o; o += L.router == ROUTER_TILED ? round_up(2 * E * (size_t)p->d * 2) : 0;
     L.idx = o;    o += round_up(A * 4);
     L.w = o;      o += round_up(A * 4);
     L.off = o;    o += round_up(((size_t)p->num_local + 1) * 4);

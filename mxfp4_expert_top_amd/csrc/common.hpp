@@ -85,6 +85,15 @@ __device__ __forceinline__ void split3_bf16(float v, bf16 &hi, bf16 &mid, bf16 &
     lo = (bf16)r2;
 }
 
+// v ~ hi + mid, both rounded to nearest bf16: hi = bf16(v), mid = bf16(v - hi)
+// (v - hi is exact in fp32), so |v - hi - mid| <= 2^-17 |v| (16 significant
+// bits against fp32's 24).
+__device__ __forceinline__ void split2_bf16(float v, bf16 &hi, bf16 &mid)
+{
+    hi = to_bf16(v);
+    mid = to_bf16(v - (float)hi);
+}
+
 // Activation stages (the elementwise step between the two projections).
 enum { ACT_NONE = 0, ACT_SILU_MUL = 1, ACT_GELU_TANH_MUL = 2 };
 

@@ -36,8 +36,9 @@ int router_skinny_splits(int T, int d, int E, int target_blocks);
 hipError_t launch_router_skinny(const bf16 *x, const float *w, const float *bias, float *out,
                                 int T, int d, int E, int splits, int32_t *zero_counts,
                                 hipStream_t s);
-// Larger batches: fp32 router weights -> three exact bf16 planes [3][E][d],
-// then a tiled bf16 GEMM over K' = 3 d into `splits` planes of [T][E].
+// Larger batches: fp32 router weights -> two bf16 planes [2][E][d] (hi and
+// mid, 16 significant bits), then a tiled bf16 GEMM over K' = 2 d into
+// `splits` planes of [T][E].
 hipError_t launch_split_router(const float *w, int E, int d, bf16 *wp, hipStream_t s);
 int router_tile_splits(int T, int d, int E, int target_blocks);
 hipError_t launch_router_tile(const bf16 *x, const bf16 *wp, const float *bias, float *logits,

@@ -1,5 +1,6 @@
 // Routing kernels: router scores (a dense GEMM on the bf16 matrix cores with
-// the fp32 router weights split into three exact bf16 parts), and a
+// the fp32 router weights split into bf16 parts: three exact ones for the
+// bandwidth-bound small batches, two for the MFMA-bound tiled router), and a
 // wavefront-per-token top-k select with softmax weights and the expert
 // histogram.
 //
@@ -208,36 +209,41 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Router scores for larger batches: the fp32 weights are split once into
-// three bf16 planes Wp[p][e][i] (hi, mid, lo; exact sum), then
+// Router scores for larger batches (the MFMA-bound case): the fp32 weights
+// are split once into RG_P = 2 bf16 planes Wp[p][e][i] (hi, mid, each rounded
+// to nearest; hi + mid holds 16 of fp32's 24 significant bits, within
+// 2^-17 |w| of the weight), then
 //   logits[t][e] = sum_i sum_p x[t][i] * Wp[p][e][i]  (+ bias)
-// on the 32x32x16 matrix cores. Workgroup tile 256 tokens x 256 experts, K
-// step 32 of d covering all three planes: each token fragment read from LDS
-// feeds three planes' MFMAs. 8 waves of 128 tokens x 64 experts, so every
-// LDS fragment feeds 6 (token) or 4 (expert) MFMAs: 10 fragment reads per
-// 24 MFMAs (64 x 64 wave tiles needed 8 per 12). blockIdx.y splits d into
-// ranges whose partial sums go to separate planes when the tile grid alone
-// is too small for the chip.
+// on the 32x32x16 matrix cores. A third plane would make every product exact
+// for one more MFMA per fragment; the scores' own contract is
+// |l - l_exact| <= 1e-4 max(1, |l|), and two planes leave an error of about
+// 2^-17 / sqrt(3) of the rms of x w per term summed over d (~4e-6 on the
+// workloads' scores), so the third plane is spent on nothing. Workgroup tile
+// 256 tokens x 256 experts, K step 32 of d covering both planes: each token
+// fragment read from LDS feeds both planes' MFMAs. 8 waves of 128 tokens x 64
+// experts. blockIdx.y splits d into ranges whose partial sums go to separate
+// planes when the tile grid alone is too small for the chip.
 //
 // Operands go from memory straight into a two-stage LDS ring with
 // global_load_lds_dwordx4 (16 bytes per lane at the wave's LDS base + 16
 // lane): step k + 1 is in flight while step k's MFMAs run, and one wait and
 // barrier per step both publish step k + 1 and free step k's stage. A stage
-// holds 256 token rows and 3 x 256 weight rows of 64 bytes (32 bf16), 64 KB;
+// holds 256 token rows and 2 x 256 weight rows of 64 bytes (32 bf16), 48 KB;
 // the 16-byte chunk c of row r sits at position c ^ ((r / 4) % 4), which
 // keeps the 32-lane fragment reads free of bank conflicts without padding.
 // 16 waves of 64 x 64 (RG_WAVES = 16) measured level with 8 waves.
 // ---------------------------------------------------------------------------
 constexpr int RG_BM = 256, RG_BN = 256, RG_BK = 32, RG_WAVES = 8, RG_THREADS = 64 * RG_WAVES;
+constexpr int RG_P = 2;  // bf16 planes of the weights
 constexpr int RG_TPW = RG_BM / (RG_WAVES / 4), RG_NI = RG_TPW / 32;  // tokens per wave, 32-row tiles
 constexpr int RG_ROW = RG_BK * 2;                                 // bytes per LDS row
 constexpr int RG_A_BYTES = RG_BM * RG_ROW;                        // 16 KB
-constexpr int RG_STAGE = RG_A_BYTES + 3 * RG_BN * RG_ROW;         // 64 KB
-constexpr size_t RG_LDS = (size_t)2 * RG_STAGE;                   // 128 KB
-// 1 KB DMA blocks (16 rows) per stage: 16 token blocks, 48 weight blocks;
+constexpr int RG_STAGE = RG_A_BYTES + RG_P * RG_BN * RG_ROW;      // 48 KB
+constexpr size_t RG_LDS = (size_t)2 * RG_STAGE;                   // 96 KB
+// 1 KB DMA blocks (16 rows) per stage: 16 token blocks, 16 per weight plane;
 // each wave moves an equal share of them
-constexpr int RG_A_DMA = RG_BM / 16 / RG_WAVES, RG_B_DMA = 3 * RG_BN / 16 / RG_WAVES;
-static_assert(RG_A_DMA * RG_WAVES * 16 == RG_BM && RG_B_DMA * RG_WAVES * 16 == 3 * RG_BN,
+constexpr int RG_A_DMA = RG_BM / 16 / RG_WAVES, RG_B_DMA = RG_P * RG_BN / 16 / RG_WAVES;
+static_assert(RG_A_DMA * RG_WAVES * 16 == RG_BM && RG_B_DMA * RG_WAVES * 16 == RG_P * RG_BN,
               "DMA blocks split evenly over the waves");
 
 __device__ __forceinline__ int rg_swz(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -250,18 +256,16 @@ __global__ __launch_bounds__(256) void split_router_kernel(const float *__restri
     const float4 v = *(const float4 *)(w + i);
     const float vv[4] = {v.x, v.y, v.z, v.w};
     // one 8-byte store per plane
-    bf16x4 h, md, lo;
+    bf16x4 h, md;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-        bf16 a, b, e;
-        split3_bf16(vv[c], a, b, e);
+        bf16 a, b;
+        split2_bf16(vv[c], a, b);
         h[c] = a;
         md[c] = b;
-        lo[c] = e;
     }
     *(bf16x4 *)(wp + i) = h;
     *(bf16x4 *)(wp + n + i) = md;
-    *(bf16x4 *)(wp + 2 * n + i) = lo;
 }
 
 __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
@@ -345,7 +349,7 @@ __global__ __launch_bounds__(RG_THREADS, 1) void router_tile_kernel(
                 for (int i = 0; i < RG_NI; i++)
                     a[i] = *(const bf16x8 *)(S + a_off + 32 * i * RG_ROW + cpos);
 #pragma unroll
-                for (int p = 0; p < 3; p++) {
+                for (int p = 0; p < RG_P; p++) {
 #pragma unroll
                     for (int j = 0; j < 2; j++) {
                         const bf16x8 b = *(const bf16x8 *)(S + b_off + (p * RG_BN + 32 * j) * RG_ROW +

@@ -147,6 +147,22 @@ def oracle_rows(inp, idx, w, tokens, act=1, mx8=False, lora=None, rank=0, scale=
         return np.concatenate(list(ex.map(part, range(nw))), axis=0)
 
 
+def oracle_scores(x, w_router, bias):
+    """The oracle's router scores of every token of x (a torch bf16 tensor,
+    any device) against w_router / bias (numpy), over chunks of tokens in
+    parallel threads."""
+    T = x.shape[0]
+    nw = max(1, min(oracle_workers(), T))
+    bounds = np.linspace(0, T, nw + 1).astype(int)
+    xs = x.cpu()
+
+    def part(i):
+        return oracle.router_logits(xs[bounds[i]:bounds[i + 1]], w_router, bias)
+
+    with ThreadPoolExecutor(max_workers=nw) as ex:
+        return np.concatenate(list(ex.map(part, range(nw))), axis=0)
+
+
 def sample_tokens(cfg, idx, n_total=64, seed=0):
     """Tokens whose layer rows the full-size tests compare: the first and last
     token of the batch; the first and last token of the largest and of the

@@ -14,7 +14,7 @@ import torch
 import oracle
 from synth import CONFIGS, LayerConfig, make_inputs
 from tests.parity_util import (LOGIT_TOL, W_TOL, assert_close_layer, host_weights, np_,
-                               oracle_rows, run_gpu_layer, sample_tokens)
+                               oracle_rows, oracle_scores, run_gpu_layer, sample_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -175,8 +175,11 @@ def test_full_size_workload(name):
     packed = m.prepack_weights(inp.weights)
     g = run_gpu_layer(inp, packed=packed, out_dtype=torch.float32)
     lg, r_idx, _ = _check_routing(inp, g)
-    # scores of a few tokens against the oracle's own router product
-    _check_scores(inp, lg, rows=[0, cfg.T // 2, cfg.T - 1])
+    # the scores of every token against the oracle's own router product
+    ref = oracle_scores(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias))
+    err = np.abs(lg - ref) / np.maximum(1, np.abs(ref))
+    assert err.max() <= LOGIT_TOL, (name, float(err.max()))
+    print(f"{name}: router scores of all {cfg.T} tokens within {err.max():.2e} max(1, |l|)")
     _, A = _check_dispatch(inp, lg, r_idx)
     assert A > 0
     toks = sample_tokens(cfg, r_idx, 64)
