@@ -38,11 +38,12 @@
  *
  * MXFP4 weight layout (one matrix [N, K], K the contraction dim): codes
  * [N][K/2] bytes, element 2i in bits 0-3 and element 2i+1 in bits 4-7 of
- * byte i; scales [N][K/32] bytes (E8M0: value 2^(s-127); the contract is
- * 2 <= s <= 252, the codes of every finite fp32 block whose largest
- * magnitude is at least 2^-123: s = 255 is NaN, s >= 253 can overflow,
- * s <= 1 reaches subnormals). Element value =
- * E2M1(code) * 2^(s-127). Experts are stacked: [num_local][N][...]; code and
+ * byte i; scales [N][K/32] bytes (E8M0: value 2^(s-127) for 0 <= s <= 254;
+ * s = 255 is NaN and is a precondition violation). Element value =
+ * E2M1(code) * 2^(s-127), decoded exactly for every finite scale code: s <= 1
+ * gives bf16 subnormals, which decode and multiply exactly; s = 253 and 254
+ * overflow to +-inf for the codes whose value exceeds the bf16 range, as the
+ * same value does in fp32 (the quantiser never emits s > 252). Experts are stacked: [num_local][N][...]; code and
  * scale arrays start 16-byte aligned.
  */
 #ifndef MOE_MXFP4_H
@@ -169,8 +170,9 @@ int moe_mxfp4_quantize(const float *w, int64_t N, int K, uint8_t *codes, uint8_t
 
 /* ------------------------------------------------------------------------
  * moe_mxfp4_dequant -- decode an MXFP4 matrix to bf16 (OCP-MX element value
- * E2M1(code) * 2^(s-127), exact in bf16 for scale codes 2..252; codes 0 and 1
- * reach bf16 subnormals, which the hardware may flush to zero).
+ * E2M1(code) * 2^(s-127), exact in bf16 for every scale code 0..254:
+ * subnormal results for codes 0 and 1 included, +-inf where the value
+ * overflows for codes 253 and 254).
  *   codes [N][K/2], scales [N][K/32] -> out [N][K] bf16
  * ------------------------------------------------------------------------ */
 int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t N, int K, void *out,

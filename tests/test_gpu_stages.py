@@ -23,8 +23,10 @@ def m():
 
 # ---------------------------------------------------------------- decode
 def test_dequant_every_code_and_scale_bitexact(m):
-    # row s-2 uses scale code s (2..252); its 32-element blocks cycle all codes
-    S = np.arange(2, 253)
+    """Every E2M1 code under every finite E8M0 scale code (row s uses scale
+    code s, 0..254): subnormal results of codes 0 and 1 and the overflow to
+    +-inf of codes 253 and 254 included, bit for bit with the oracle."""
+    S = np.arange(0, 255)
     N, K = len(S), 128
     nib = np.tile(np.arange(16), (N, K // 16))
     codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
@@ -36,6 +38,30 @@ def test_dequant_every_code_and_scale_bitexact(m):
     want = oracle.mxfp4_decode(codes, scales)
     assert np.array_equal(got, want)
     assert np.array_equal(np.signbit(got), np.signbit(want))  # -0 stays -0
+    assert (want[:2] != 0).any() and np.isinf(want[253:]).any()  # both edges reached
+
+
+@pytest.mark.parametrize("sc", [0, 1])
+@pytest.mark.parametrize("mode", [1, 3, 4])
+def test_grouped_gemm_subnormal_weight_scales(m, sc, mode):
+    """Weights whose scale code is 0 or 1 decode to bf16 subnormals; against
+    activations of 2^100 their products are ordinary numbers, and the
+    grouped GEMM gives them exactly (every product and sum exact in fp32)."""
+    rng = np.random.default_rng(sc)
+    R, K, N = 32, 128, 64
+    wc = rng.integers(0, 256, (1, N, K // 2), dtype=np.uint8)
+    ws = np.full((1, N, K // 32), sc, np.uint8)
+    a = torch.full((R, K), 2.0 ** 100, dtype=torch.bfloat16)
+    off = torch.tensor([0, R], dtype=torch.int32, device=DEV)
+    out = torch.empty(R, N, dtype=torch.float32, device=DEV)
+    wsb = m.alloc_workspace(m.moe_grouped_gemm_workspace_size(1, R, N), DEV)
+    m.moe_grouped_gemm_mxfp4(a.to(DEV), None, torch.from_numpy(wc).to(DEV),
+                             torch.from_numpy(ws).to(DEV), None, None, off, R, 0, out, wsb,
+                             mode=mode)
+    torch.cuda.synchronize()
+    ref = a.double().numpy() @ oracle.mxfp4_decode(wc[0], ws[0]).astype(np.float64).T
+    assert np.abs(ref).max() > 1e-7
+    assert np.array_equal(np_(out).astype(np.float64), ref)
 
 
 def _quantize_cases():
