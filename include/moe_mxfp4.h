@@ -219,7 +219,7 @@ int moe_mxfp4_prepack(const uint8_t *codes, const uint8_t *scales, int n_mats, i
  *   ws / ws_bytes: scratch of moe_grouped_gemm_workspace_size(...) bytes (the
  *         device-built work list)
  * Requirements: lda >= K and ldo >= N, both multiples of 8; a_rows entries
- * index valid rows of `a`; code and scale arrays 16-byte aligned.
+ * index valid rows of `a`; a, out, code and scale arrays 16-byte aligned.
  * Errors: block_size != 32, K % 128 != 0, N % 64 != 0 or K > MOE_MAX_K ->
  * UNSUPPORTED;
  * a GLU act without w2, or w2 with MOE_ACT_NONE -> INVALID_ARG.

@@ -91,7 +91,8 @@ int check_gemm(const void *a, int64_t lda, const uint8_t *w1c, const uint8_t *w1
     if (max_rows == 0) return MOE_OK;
     CHECK(a && w1c && w1s && off && out, MOE_ERR_INVALID_ARG);
     CHECK(lda >= K && lda % 8 == 0 && ldo >= N && ldo % 8 == 0, MOE_ERR_INVALID_ARG);
-    CHECK(aligned(a, 16) && aligned(w1c, 16) && aligned(w1s, 16), MOE_ERR_INVALID_ARG);
+    CHECK(aligned(a, 16) && aligned(w1c, 16) && aligned(w1s, 16) && aligned(out, 16),
+          MOE_ERR_INVALID_ARG);
     if (w2c) CHECK(aligned(w2c, 16) && aligned(w2s, 16), MOE_ERR_INVALID_ARG);
     return MOE_OK;
 }

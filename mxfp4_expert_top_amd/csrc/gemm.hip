@@ -814,9 +814,14 @@ __host__ __device__ constexpr int td_scale_row(int K)
     return (((K / 32 + 3) / 4) | 1) * 4;
 }
 
+// the epilogue stages up to 32 rows x (256 + 16) bytes per wave in the same LDS
+constexpr int TD_EPI_BYTES = 16 * 32 * (256 + 16);
+
 __host__ __device__ constexpr int td_lds_bytes(int K)
 {
-    return TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K);
+    return TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K) > TD_EPI_BYTES
+               ? TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K)
+               : TD_EPI_BYTES;
 }
 
 // 16 waves (4 per SIMD) share the tile. Wave w takes row block q = w / 4
@@ -1021,24 +1026,44 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
             }
         }
 
-        // epilogue: lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+        // epilogue through LDS: the ring is idle once every wave is past its
+        // last step, so each wave stages one 32-row tile of its output at a
+        // time in a private area (rows of its COLS_W columns, padded by 16
+        // bytes) and stores whole 16-byte row segments from there: 2 to 8
+        // stores per row tile instead of one narrow store per row pair and
+        // accumulator tile. Lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each
+        // 32 x 32 accumulator tile.
+        __syncthreads();
+        constexpr int COLS_W = GLU ? 32 : 64;                 // output columns of the wave
+        constexpr int ROW_B = COLS_W * (int)sizeof(OutT);     // 64, 128 or 256 bytes
+        constexpr int PITCH = ROW_B + 16;
+        constexpr int LPR = ROW_B / 16, RPI = 64 / LPR;       // lanes per row, rows per store
+        static_assert(16 * 32 * PITCH <= TD_EPI_BYTES, "staging fits the LDS allocation");
+        uint8_t *const stg = td_lds + wave * (32 * PITCH);
+        const int c0 = n0 + COLS_W * slot;                    // first output column of the wave
+        const bool col_on = c0 < N;                           // N is a multiple of COLS_W
 #pragma unroll
         for (int i = 0; i < NI; i++) {
 #pragma unroll
             for (int v = 0; v < 16; v++) {
-                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (rl >= mrows) continue;
-                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+                OutT *row = (OutT *)(stg + r * PITCH);
                 if constexpr (GLU) {
-                    const int col = n0 + 32 * slot + l32;
-                    if (col < N)
-                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                    store_out<OutT>(row + l32, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
                 } else {
 #pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const int col = n0 + 64 * slot + 32 * j + l32;
-                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
-                    }
+                    for (int j = 0; j < 2; j++) store_out<OutT>(row + 32 * j + l32, acc[i][j][v]);
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < 32 / RPI; it++) {
+                const int r = RPI * it + lane / LPR, seg = lane % LPR;
+                const u32x4 val = *(const u32x4 *)(stg + r * PITCH + 16 * seg);
+                const int rl = 64 * q + 32 * i + r;
+                if (col_on && rl < mrows) {
+                    u32x4 *dst = (u32x4 *)((uint8_t *)(out + (int64_t)(r0 + rl) * ldo + c0) + 16 * seg);
+                    if constexpr (!GLU && sizeof(OutT) == 4) __builtin_nontemporal_store(val, dst);
+                    else *dst = val;
                 }
             }
         }
