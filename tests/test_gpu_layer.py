@@ -46,6 +46,10 @@ SMALL = [
     # T >= 512: the tiled router (split-K planes, bias, E not a tile multiple)
     LayerConfig("g5", T=700, I=128, d=256, E=100, k=6, bias="normal"),
     LayerConfig("g6", T=1030, I=256, d=384, E=40, k=4, expert_begin=4, num_local=30),
+    # the largest expert count and top-k the ABI takes (E = 2048, k = 32), with
+    # a local range, and at T >= 512 on the tiled router
+    LayerConfig("g7", T=40, I=128, d=256, E=2048, k=32, expert_begin=1000, num_local=700),
+    LayerConfig("g8", T=520, I=128, d=256, E=2048, k=32, bias="normal"),
 ]
 
 
