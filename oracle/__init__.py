@@ -19,7 +19,10 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "moe_oracle.c"
-_LIB = _HERE / "liboracle.so"
+# MOE_ORACLE_LIB names another build of moe_oracle.c to load instead (the
+# mutation test points the pins at deliberately broken builds this way)
+_LIB = Path(os.environ["MOE_ORACLE_LIB"]) if os.environ.get("MOE_ORACLE_LIB") else \
+    _HERE / "liboracle.so"
 
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
 
