@@ -72,6 +72,12 @@ def lib():
         L.oracle_e4m3_value.argtypes = [i32]
         L.oracle_mxfp8_quantize.argtypes = [p, i64, i64, p, p]
         L.oracle_mxfp8_decode.argtypes = [p, p, i64, i64, p]
+        L.oracle_e2m3_value.argtypes = [i32]
+        L.oracle_e2m3_value.restype = C.c_float
+        L.oracle_mxfp6_quantize.argtypes = [p, i64, i64, p, p]
+        L.oracle_mxfp6_decode.argtypes = [p, p, i64, i64, p]
+        L.oracle_fp6x2_split.argtypes = [p, i64, i64, p, p]
+        L.oracle_fp6x2_split.restype = i32
         L.oracle_expert_compute_mx8.restype = i32
         L.oracle_expert_compute_mx8.argtypes = L.oracle_expert_compute.argtypes
         L.oracle_layer_mx8.restype = i64
@@ -159,6 +165,52 @@ def mxfp8_decode(codes, scales) -> np.ndarray:
     out = np.empty((N, K), np.float32)
     lib().oracle_mxfp8_decode(_ptr(codes), _ptr(scales), N, K, _ptr(out))
     return out
+
+
+def e2m3_value(code: int) -> float:
+    """OCP-MX E2M3 element value of a code."""
+    return float(lib().oracle_e2m3_value(int(code)))
+
+
+def mxfp6_quantize(v):
+    """[N, K] fp32 -> MXFP6: codes [N, K] u8 (E2M3, one per byte), scales
+    [N, K/32] u8 (E8M0)."""
+    v = _arr(v, np.float32)
+    N, K = v.shape
+    assert K % 32 == 0
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((N, K // 32), np.uint8)
+    lib().oracle_mxfp6_quantize(_ptr(v), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mxfp6_decode(codes, scales) -> np.ndarray:
+    codes, scales = _arr(codes, np.uint8), _arr(scales, np.uint8)
+    N, K = codes.shape
+    assert scales.shape == (N, K // 32)
+    out = np.empty((N, K), np.float32)
+    lib().oracle_mxfp6_decode(_ptr(codes), _ptr(scales), N, K, _ptr(out))
+    return out
+
+
+def fp6x2_split(v):
+    """[N, K] fp32 -> the two MXFP6 planes: codes [2, N, K] u8, scales
+    [2, N, K/32] u8 (plane 2 carries v - decode(plane 1))."""
+    v = _arr(v, np.float32)
+    N, K = v.shape
+    assert K % 32 == 0
+    codes = np.empty((2, N, K), np.uint8)
+    scales = np.empty((2, N, K // 32), np.uint8)
+    if lib().oracle_fp6x2_split(_ptr(v), N, K, _ptr(codes), _ptr(scales)) != 0:
+        raise MemoryError("oracle_fp6x2_split")
+    return codes, scales
+
+
+def fp6x2_value(codes, scales) -> np.ndarray:
+    """The value the two planes carry: decode(plane 1) + decode(plane 2), in
+    fp64 (exact)."""
+    return (mxfp6_decode(codes[0], scales[0]).astype(np.float64) +
+            mxfp6_decode(codes[1], scales[1]).astype(np.float64))
 
 
 def router_logits(x, w_router, bias=None) -> np.ndarray:

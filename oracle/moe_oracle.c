@@ -27,7 +27,9 @@
  * (functions ending in _mx8) quantises the tokens and h to MXFP8 (E4M3) before
  * each projection, the input contract of block-scaled 8-bit x 4-bit matrix
  * instructions; it is a separate accuracy contract, not an approximation of
- * the default mode.
+ * the default mode. The FP6X2 functions state the two-plane MXFP6 (E2M3)
+ * carriage of activations that the block-scaled 6-bit x 4-bit instructions
+ * take; layers that use it are held to the default mode's contract.
  *
  * Pins (tests/test_oracle_*.py): the E2M1 table against its bit-field
  * definition; every E8M0 scale; every (code, scale) decode; hand-built
@@ -44,6 +46,11 @@
  * weights whose h lands on the E4M3 grid, on a tie and on the 448 clamp.
  * LoRA: zero B factors give the base layer bit for bit; the layer against a
  * dense fp64 evaluation with W + scale * B A as each expert's weights.
+ * FP6X2: every E2M3 code against its bit fields and the spec's landmark
+ * values; the MXFP6 quantiser against an arithmetic round-half-even on each
+ * binade's step with a bit-field encoder, on tie, clamp, zero and
+ * extreme-exponent blocks; a split worked by hand; the per-element bound
+ * 2^(E-7) that two planes imply.
  */
 #include <math.h>
 #include <stdint.h>
@@ -230,6 +237,114 @@ void oracle_mxfp8_decode(const uint8_t *codes, const uint8_t *scales,
         for (int64_t i = 0; i < K; i++)
             out[n * K + i] = ldexpf(oracle_e4m3_value(codes[n * K + i]),
                                     (int)scales[n * (K / 32) + i / 32] - 127);
+}
+
+/* ------------------------------------------------------------------ */
+/* Two-plane MXFP6 carriage of the activations (the FP6X2 mode)        */
+/* ------------------------------------------------------------------ */
+
+/* OCP-MX E2M3 (FP6): sign bit 5, exponent bits 4-3 (bias 1), mantissa bits
+ * 2-0; exponent 0 is subnormal (m/8); the largest magnitude is 0.11.111 =
+ * 7.5. No infinities or NaN. */
+float oracle_e2m3_value(int code)
+{
+    code &= 0x3f;
+    int sign = code >> 5, e = (code >> 3) & 3, m = code & 7;
+    float v = (e == 0) ? (float)m / 8.0f : ldexpf(1.0f + (float)m / 8.0f, e - 1);
+    return sign ? -v : v;
+}
+
+/* Round a magnitude in [0, 7.5] to the nearest E2M3 magnitude (codes
+ * 0..31); on a tie take the even code. An argmin over the grid. */
+static int e2m3_round_magnitude(float a)
+{
+    int best = 0;
+    float best_dist = fabsf(a - oracle_e2m3_value(0));
+    for (int c = 1; c < 32; c++) {
+        float dist = fabsf(a - oracle_e2m3_value(c));
+        if (dist < best_dist || (dist == best_dist && (c % 2) == 0 && (best % 2) != 0)) {
+            best = c;
+            best_dist = dist;
+        }
+    }
+    return best;
+}
+
+/* OCP-MX conversion of [N, K] fp32 to MXFP6 (E2M3 elements, E8M0 scale per
+ * 32-element block along K): shared exponent floor(log2 amax) - emax(E2M3)=2,
+ * taken exactly from frexp and clamped to the E8M0 range; elements divided by
+ * the scale (a power of two, so exactly) and rounded to nearest-even, with
+ * magnitudes beyond 7.5 clamped to 7.5. All-zero block: scale 0, codes 0. A
+ * negative element that rounds to zero keeps its sign (code 0x20).
+ * codes [N, K] (one code per byte), scales [N, K/32]. */
+void oracle_mxfp6_quantize(const float *v, int64_t N, int64_t K,
+                           uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t b = 0; b < K / 32; b++) {
+            const float *blk = v + n * K + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; i++)
+                if (fabsf(blk[i]) > amax) amax = fabsf(blk[i]);
+            const int emax_e2m3 = 2;
+            int s = 0;
+            if (amax != 0.0f) {
+                int e2;
+                frexpf(amax, &e2); /* amax = m * 2^e2, m in [0.5, 1) */
+                s = (e2 - 1) - emax_e2m3 + 127;
+                if (s < 0) s = 0;
+                if (s > 254) s = 254;
+            }
+            scales[n * (K / 32) + b] = (uint8_t)s;
+            for (int i = 0; i < 32; i++) {
+                int c = 0;
+                if (amax != 0.0f) {
+                    float q = blk[i] / ldexpf(1.0f, s - 127);
+                    float a = fabsf(q);
+                    int mag = (a >= 7.5f) ? 31 : e2m3_round_magnitude(a);
+                    c = mag | (signbit(q) ? 0x20 : 0);
+                }
+                codes[n * K + b * 32 + i] = (uint8_t)c;
+            }
+        }
+    }
+}
+
+/* Decode [N, K] MXFP6: element value times its block's scale (exact). */
+void oracle_mxfp6_decode(const uint8_t *codes, const uint8_t *scales,
+                         int64_t N, int64_t K, float *out)
+{
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t i = 0; i < K; i++)
+            out[n * K + i] = ldexpf(oracle_e2m3_value(codes[n * K + i]),
+                                    (int)scales[n * (K / 32) + i / 32] - 127);
+}
+
+/* The FP6X2 carriage of [N, K] activations as two MXFP6 planes, for the
+ * block-scaled 6-bit x 4-bit matrix instructions (the pages keep activations
+ * at higher precision than the 4-bit weights, P1 §二 第一层; two 6-bit planes
+ * carry each value to within 2^(E-7), E = floor(log2 amax) of its block):
+ *   plane 1 = MXFP6(v),
+ *   plane 2 = MXFP6(v - decode(plane 1)), the difference taken in fp32.
+ * The value carried is decode(plane 1) + decode(plane 2).
+ * codes [2][N][K] (one code per byte), scales [2][N][K/32]. */
+int oracle_fp6x2_split(const float *v, int64_t N, int64_t K, uint8_t *codes,
+                       uint8_t *scales)
+{
+    float *d1 = (float *)malloc(sizeof(float) * (size_t)(N * K));
+    float *r = (float *)malloc(sizeof(float) * (size_t)(N * K));
+    if (!d1 || !r) {
+        free(d1);
+        free(r);
+        return -1;
+    }
+    oracle_mxfp6_quantize(v, N, K, codes, scales);
+    oracle_mxfp6_decode(codes, scales, N, K, d1);
+    for (int64_t i = 0; i < N * K; i++) r[i] = v[i] - d1[i];
+    oracle_mxfp6_quantize(r, N, K, codes + N * K, scales + N * (K / 32));
+    free(d1);
+    free(r);
+    return 0;
 }
 
 /* ------------------------------------------------------------------ */

@@ -23,6 +23,7 @@ ROUTE = "tests/test_oracle_routing.py"
 LAYER = "tests/test_oracle_layer.py"
 LORA = "tests/test_oracle_lora.py"
 MX8 = "tests/test_oracle_mx8.py"
+FP6 = "tests/test_oracle_fp6x2.py"
 
 # name: (text in moe_oracle.c, replacement, pin files expected to catch it)
 MUTANTS = {
@@ -66,6 +67,16 @@ MUTANTS = {
                                "delta += t[j] * bf16_bits_to_float(B[(j * N + n) % (N * r)]);",
                                [LORA]),
     "e4m3_emax_7": ("s = (e2 - 1) - 8 + 127;", "s = (e2 - 1) - 7 + 127;", [MX8]),
+    "e2m3_emax_3": ("s = (e2 - 1) - emax_e2m3 + 127;", "s = (e2 - 1) - 3 + 127;", [FP6]),
+    "e2m3_subnormal_step": ("(float)m / 8.0f : ldexpf(1.0f + (float)m / 8.0f, e - 1);",
+                            "(float)m / 4.0f : ldexpf(1.0f + (float)m / 8.0f, e - 1);", [FP6]),
+    "e2m3_ties_to_odd": ("(dist == best_dist && (c % 2) == 0 && (best % 2) != 0)) {\n            best = c;\n            best_dist = dist;\n        }\n    }\n    return best;\n}\n\n/* OCP-MX conversion of [N, K] fp32 to MXFP6",
+                         "(dist == best_dist && (c % 2) != 0 && (best % 2) == 0)) {\n            best = c;\n            best_dist = dist;\n        }\n    }\n    return best;\n}\n\n/* OCP-MX conversion of [N, K] fp32 to MXFP6", [FP6]),
+    "e2m3_clamp_at_7": ("int mag = (a >= 7.5f) ? 31 : e2m3_round_magnitude(a);",
+                        "int mag = (a >= 7.0f) ? 31 : e2m3_round_magnitude(a);", [FP6]),
+    "fp6x2_plane2_of_value": ("for (int64_t i = 0; i < N * K; i++) r[i] = v[i] - d1[i];",
+                              "for (int64_t i = 0; i < N * K; i++) r[i] = v[i] + 0.0f * d1[i];",
+                              [FP6]),
 }
 
 
@@ -100,6 +111,6 @@ def test_unmodified_build_passes_the_same_pins(tmp_path):
     _build(SRC.read_text(), lib)
     env = dict(os.environ, MOE_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "-m", "not gpu", MX, ROUTE, LORA, MX8], cwd=ROOT, env=env,
+                        "-m", "not gpu", MX, ROUTE, LORA, MX8, FP6], cwd=ROOT, env=env,
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
