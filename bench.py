@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense fp4 matrix
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 matrix (the fp8 x fp4 block-scaled rate)
+FP6_PEAK_TFLOPS = 10100.0      # MI355X dense fp6 matrix (the fp6 x fp4 block-scaled rate)
 STAGES = ("route", "permute", "gate_up", "down", "combine")
 
 
@@ -44,10 +45,13 @@ def parse():
     ap.add_argument("--mode", type=int, default=0,
                     help="GEMM schedule (enum moe_sched): 0 auto, 1 stream, 2 tiled, "
                          "3 128-row tiles, 4 256-row tiles")
-    ap.add_argument("--precision", default="bf16", choices=["bf16", "mx8"],
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "mx8", "fp6x2"],
                     help="bf16: bf16 tokens and h against MXFP4 weights (the pages' layer); "
                          "mx8: tokens and h rounded to MXFP8 for the block-scaled fp8 x fp4 "
-                         "matrix instruction (a separate accuracy contract)")
+                         "matrix instruction (a separate accuracy contract); fp6x2: on "
+                         "256-row tiles the gate/up projection takes the tokens as two MXFP6 "
+                         "planes on the block-scaled fp6 x fp4 instruction (the bf16 "
+                         "contract)")
     ap.add_argument("--lora-rank", type=int, default=0,
                     help="> 0: the layer with rank-R LoRA adapters (scale 0.5) on every local "
                          "expert's three projections (moe_layer_lora; bf16 precision only)")
@@ -263,6 +267,7 @@ def main():
     inp = make_inputs(cfg, dev)
     packed = args.weights == "packed"
     mx8 = args.precision == "mx8"
+    f6 = args.precision == "fp6x2"
     canonical = inp.weights  # the oracle reads the canonical layout
     if packed:  # the load-time conversion, outside the timed region
         layer_weights = m.prepack_weights(inp.weights)
@@ -272,7 +277,7 @@ def main():
     p = m.layer_params(cfg.T, cfg.d, cfg.E, cfg.k, cfg.I, cfg.expert_begin, cfg.num_local,
                        mode=args.mode, out_dtype=m.DT_F32,
                        weight_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP,
-                       precision=m.PREC_MX8 if mx8 else m.PREC_BF16)
+                       precision=m.PREC_MX8 if mx8 else m.PREC_FP6X2 if f6 else m.PREC_BF16)
     ws = m.alloc_workspace(m.moe_layer_workspace_size(p), dev)
     # fp32 layer output: the form the parity tests hold to the stated bounds
     # (a bf16 output is that result rounded to nearest-even, whose rounding
@@ -282,7 +287,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.lora_rank > 0:
-        if mx8:
+        if mx8 or f6:
             print(json.dumps({"error": "LoRA runs in the bf16 precision only"}))
             sys.exit(2)
         from synth import make_lora
@@ -368,6 +373,18 @@ def main():
                 "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / FP8_PEAK_TFLOPS, 4),
                 "traffic": None, "algorithmic_flops_per_launch": int(gf),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
+    elif f6 and sched == m.MODE_TILE256 and cfg.d <= 4096:
+        # the stage is the token split plus the block-scaled GEMM, which
+        # issues two 6-bit x 4-bit products (one per plane) per bf16-equivalent
+        # product: priced at the fp6 peak on the algorithmic flops
+        roof = {"kernel": "fp6x2_split_kernel + gemm_fp6x2_w16_kernel<SILU_MUL> "
+                          "(gate/up stage)", "bound": "mfma",
+                "achieved": round(gf / gu_s / 1e12, 1), "peak": FP6_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / FP6_PEAK_TFLOPS, 4),
+                "traffic": None, "algorithmic_flops_per_launch": int(gf),
+                "instruction_flops_per_launch": int(2 * gf),
+                "bf16_peak_frac": round(gf / gu_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "avg_launch_ms": round(stage_ms["gate_up"], 4)}
     elif sched == m.MODE_STREAM:
         roof = {"kernel": "gemm_stream_kernel<SILU_MUL> (gate/up projection)", "bound": "hbm",
                 "achieved": round(gb / gu_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -398,12 +415,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if mx8 else "bf16",
+        "dtype": "mxfp8" if mx8 else "fp6x2+bf16" if f6 else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "experts_computed": cfg.num_local,
                    "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
-                   "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else "bf16", "output": "fp32",
+                   "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else
+                   "bf16 (gate/up: two mxfp6-e2m3-e8m0-b32 planes)" if f6 else "bf16",
+                   "output": "fp32",
                    "lora_rank": args.lora_rank, "routing_bias": cfg.bias},
         "roofline": roof,
         "layer": {"assignments": A, "experts_touched": U, "max_rows_per_expert": int(counts.max()),

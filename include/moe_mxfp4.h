@@ -78,7 +78,7 @@ enum moe_act { MOE_ACT_NONE = 0, MOE_ACT_SILU_MUL = 1, MOE_ACT_GELU_TANH_MUL = 2
  * layout described above. PACKED: the streaming layout moe_mxfp4_prepack
  * produces (same codes and scales, permuted for the kernels). */
 enum moe_weight_layout { MOE_LAYOUT_OCP = 0, MOE_LAYOUT_PACKED = 1 };
-enum moe_precision { MOE_PREC_BF16 = 0, MOE_PREC_MX8 = 1 };
+enum moe_precision { MOE_PREC_BF16 = 0, MOE_PREC_MX8 = 1, MOE_PREC_FP6X2 = 2 };
 
 /* Schedules of the grouped expert GEMMs (the `mode` argument). All give the
  * same results up to fp32 summation order; they differ in how work is cut:
@@ -289,6 +289,58 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
                          void *ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The FP6X2 carriage of activations. The pages' layer pairs 4-bit weights
+ * with higher-precision activations (P1 section 二, 第一层). gfx950's
+ * block-scaled matrix instruction takes 6-bit x 4-bit operands at twice its
+ * 8-bit rate, so activations go to it as two MXFP6 planes (OCP-MX v1.0 E2M3
+ * elements: bias 1, largest magnitude 7.5; one E8M0 scale per 32 elements
+ * along the contraction): plane 1 is the MXFP6 conversion of the value,
+ * plane 2 that of the fp32 residual. The planes carry each value to within
+ * 2^(E-7), E = floor(log2 amax) of its block; layers that use them keep the
+ * default accuracy contract.
+ * ------------------------------------------------------------------------ */
+
+/* moe_fp6x2_split -- rows of v (bf16 or fp32, row stride ldv elements) as two
+ * MXFP6 planes. Per 32-element block b of row n and plane p (plane 1 from v,
+ * plane 2 from r = v - decode(plane 1) in fp32): amax = max|.|; all zero ->
+ * scale code 0, codes 0; else s = clamp(floor(log2 amax) - 2 + 127, 0, 254),
+ * and each element is ./2^(s-127) rounded to the nearest E2M3 value (ties to
+ * the even code), magnitudes from 7.5 up clamped to 7.5, sign bit from the
+ * element (-0 keeps it, code 0x20).
+ *   data   [N][K/32][48] bytes: block b's plane-1 codes, then its plane-2
+ *          codes, 24 bytes each; code i of a plane at bits 6i..6i+5 of its
+ *          24 little-endian bytes
+ *   scales [N][K/32][2]: plane-1 and plane-2 scale codes of block b
+ * Preconditions: finite v. Errors: K % 32 != 0 -> UNSUPPORTED; v_dtype not
+ * bf16 or fp32, ldv < K, ldv % 8 != 0, NULL or misaligned (16-byte v and
+ * data, 2-byte scales) pointers -> INVALID_ARG. N == 0 is a no-op. */
+int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, uint8_t *data,
+                    uint8_t *scales, moe_stream_t stream);
+
+/* moe_grouped_gemm_fp6x2 -- moe_grouped_gemm_mxfp4 with rows carried as two
+ * MXFP6 planes:
+ *   a_row  = (a_rows ? a_rows[r] : r)
+ *   acc1[n] = sum_k A(a_row, k) * W1[e][n][k], A(r, k) = the plane-1 value
+ *             plus the plane-2 value of element k of split row r
+ * with split rows as moe_fp6x2_split writes them (row r: data at a_data +
+ * r * ldb * 48, scales at a_scales + r * ldb * 2; ldb = row stride in
+ * 32-element blocks), on v_mfma_scale_f32_32x32x64_f8f6f4 (exact products;
+ * each 64-long partial sum formed inside the instruction, one per plane, then
+ * accumulated in fp32); out as in moe_grouped_gemm_mxfp4. Schedule: 256-row
+ * tiles (no mode argument). ws holds moe_grouped_gemm_fp6x2_workspace_size(...)
+ * bytes. Requirements: ldb >= K/32, ldb % 4 == 0, ldo >= N, ldo % 8 == 0;
+ * 16-byte aligned arrays. Errors as moe_grouped_gemm_mxfp4, and K > 4096 ->
+ * UNSUPPORTED. */
+size_t moe_grouped_gemm_fp6x2_workspace_size(int num_local, int max_rows);
+int moe_grouped_gemm_fp6x2(const uint8_t *a_data, const uint8_t *a_scales, int64_t ldb,
+                           const int32_t *a_rows, const uint8_t *w1_codes,
+                           const uint8_t *w1_scales, const uint8_t *w2_codes,
+                           const uint8_t *w2_scales, const int32_t *expert_offsets,
+                           int num_local, int max_rows, int N, int K, int block_size,
+                           int w_layout, int act, void *out, int out_dtype, int64_t ldo,
+                           void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_combine -- weighted unpermute (P3 section 四, combine: results come back
  * weighted; P2 "MoE 稀疏激活": weighted sum of the selected experts):
  *   out[t][m] = sum_{j=0..k-1, inv[t][j] >= 0} topk_w[t][j] * y[inv[t][j]][m]
@@ -322,9 +374,12 @@ typedef struct {
     int mode;         /* GEMM schedule, as moe_grouped_gemm_mxfp4 */
     int weight_layout; /* enum moe_weight_layout of all six weight arrays */
     int precision;    /* enum moe_precision: MOE_PREC_BF16 (the pages' bf16
-                         activations) or MOE_PREC_MX8 (tokens and h rounded to
+                         activations), MOE_PREC_MX8 (tokens and h rounded to
                          MXFP8 before each projection; `mode` as in
-                         moe_grouped_gemm_mx8) */
+                         moe_grouped_gemm_mx8) or MOE_PREC_FP6X2 (where the
+                         schedule resolves to 256-row tiles and d <= 4096, the
+                         gate/up projection takes the tokens as two MXFP6
+                         planes, moe_grouped_gemm_fp6x2; otherwise as bf16) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

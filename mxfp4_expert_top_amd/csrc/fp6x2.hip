@@ -1,0 +1,540 @@
+// The FP6X2 carriage of activations: bf16 (or fp32) rows as two MXFP6 planes
+// (OCP MX v1.0 E2M3 elements, one E8M0 scale per 32), the second plane
+// holding the fp32 residual of the first, against MXFP4 weights on the
+// gfx950 block-scaled instruction v_mfma_scale_f32_32x32x64_f8f6f4 with
+// 6-bit A and 4-bit B operands. With both operands at most 6 bits wide the
+// instruction issues a 32 x 32 x 64 product in about the time of one bf16
+// 32 x 32 x 16 one, so the two planes take half the matrix-core time of the
+// bf16 path and no decode instructions.
+//
+// The pages' layer keeps activations at higher precision than the 4-bit
+// weights (P1 section 二, 第一层); the two planes carry each value to within
+// 2^(E-7), E = floor(log2 amax) of its 32-block (about 3.4e-4 rms on
+// N(0, 1) tokens, a third of bf16's own rounding), and layers that use them
+// are held to the default accuracy contract.
+//
+//   fp6x2_split_kernel       rows -> two planes; one thread per 32-element
+//                            block
+//   gemm_fp6x2_w16_kernel    grouped projection on 256 x 256 tiles, the two
+//                            planes x MXFP4 weights, fp32 accumulation
+//
+// Storage of a split row (K elements, nb = K / 32 blocks):
+//   data   [nb][48] bytes: block b's plane-1 codes (24 bytes), then its
+//          plane-2 codes (24 bytes); code i of a plane at bits 6 i .. 6 i + 5
+//          of the 24 little-endian bytes (the instruction's operand order)
+//   scales [nb][2]: block b's plane-1 and plane-2 E8M0 codes
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// fp32 -> MXFP6 (E2M3). Per block: s = clamp(floor(log2 amax) - 2 + 127, 0,
+// 254) (2 = emax of E2M3), q = v * 2^(127 - s) (exact), E2M3 code of q
+// rounded to nearest-even with magnitudes from 7.5 up clamped to 7.5 (code
+// 31); an all-zero block gets scale 0 and codes 0; the sign bit comes from
+// q, so -0 and negatives rounding to zero give 0x20.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m3_code(float q)
+{
+    const uint32_t sign = (__float_as_uint(q) >> 26) & 0x20u;
+    const float a = fabsf(q);
+    uint32_t mag;
+    if (a >= 7.5f) {
+        mag = 31u;
+    } else if (a < 1.0f) {
+        // below 1 the grid is k / 8, k = 0..8 (k = 8 is the smallest normal,
+        // whose code is also 8); the scaling is exact
+        mag = (uint32_t)__builtin_rintf(a * 8.0f);
+    } else {
+        // round the 23-bit fp32 mantissa to 3 bits, nearest-even; a carry
+        // moves into the exponent field (biased 127 for [1, 2) -> E2M3 field 1)
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        mag = ((((b >> 23) & 0xFFu) - 126u) << 3) | ((b >> 20) & 7u);
+    }
+    return sign | mag;
+}
+
+// The E2M3 value of a code: m / 8 for exponent field 0, else
+// (8 + m) * 2^(e - 4).
+__device__ __forceinline__ float e2m3_value(uint32_t c)
+{
+    const uint32_t e = (c >> 3) & 3u, m = c & 7u;
+    const float mag = (float)(e ? 8u + m : m) * __uint_as_float((e ? 123u + e : 124u) << 23);
+    return (c & 0x20u) ? -mag : mag;
+}
+
+// The E8M0 scale code of a block with this amax, and 2^(127 - s): s =
+// clamp(floor(log2 amax) - 2 + 127, 0, 254); an fp32-subnormal amax clamps to
+// 0. s <= 252 for finite input, so the exponent field of 2^(127 - s) is >= 2.
+__device__ __forceinline__ int mxfp6_scale(float amax, float &inv)
+{
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    const int s = (amax == 0.0f || ex == 0) ? 0 : min(254, max(0, ex - 2));
+    inv = __uint_as_float((uint32_t)(254 - s) << 23);
+    return s;
+}
+
+// One plane of one block: the codes of v (32 values), packed 6 bits each into
+// w[0..5], and v replaced by its residual v - decode (exact in fp32).
+__device__ __forceinline__ uint32_t mxfp6_plane(float v[32], uint32_t w[6])
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
+    float inv;
+    const int s = mxfp6_scale(amax, inv);
+    // 2^(s - 127), an fp32 subnormal for s = 0
+    const float X = s ? __uint_as_float((uint32_t)s << 23) : __uint_as_float(0x00400000u);
+#pragma unroll
+    for (int j = 0; j < 6; j++) w[j] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        const uint32_t c = amax == 0.0f ? 0u : e2m3_code(v[j] * inv);
+        v[j] -= e2m3_value(c) * X;
+        const int bit = 6 * j, wd = bit >> 5, off = bit & 31;
+        w[wd] |= c << off;
+        if (off > 26) w[wd + 1] |= c >> (32 - off);
+    }
+    return (uint32_t)s;
+}
+
+template <typename InT>
+__device__ __forceinline__ void f6_load32(const InT *p, float v[32]);
+template <>
+__device__ __forceinline__ void f6_load32<float>(const float *p, float v[32])
+{
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const float4 t = ((const float4 *)p)[j];
+        v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+}
+template <>
+__device__ __forceinline__ void f6_load32<bf16>(const bf16 *p, float v[32])
+{
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const bf16x8 t = ((const bf16x8 *)p)[j];
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[8 * j + i] = (float)t[i];
+    }
+}
+
+// Rows n < min(N, *n_dev) (all N rows when n_dev is null); one thread per
+// 32-element block, grid-stride. data [N][K/32][48], scales [N][K/32][2].
+template <typename InT>
+__global__ __launch_bounds__(256) void fp6x2_split_kernel(const InT *__restrict__ v, int64_t ldv,
+                                                          int64_t N, int K,
+                                                          const int32_t *__restrict__ n_dev,
+                                                          uint8_t *__restrict__ data,
+                                                          uint8_t *__restrict__ scales)
+{
+    const int nb = K / 32;
+    const int64_t rows = n_dev ? min(N, (int64_t)max(*n_dev, 0)) : N;
+    const int64_t total = rows * nb;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = i / nb;
+        const int b = (int)(i - n * nb);
+        float x[32];
+        f6_load32<InT>(v + n * ldv + 32 * b, x);
+        uint32_t w[12];
+        const uint32_t s1 = mxfp6_plane(x, w);
+        const uint32_t s2 = mxfp6_plane(x, w + 6);
+        u32x4 *dst = (u32x4 *)(data + i * 48);
+        dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+        dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+        dst[2] = u32x4{w[8], w[9], w[10], w[11]};
+        *(uint16_t *)(scales + i * 2) = (uint16_t)(s1 | (s2 << 8));
+    }
+}
+
+hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
+                              uint8_t *data, uint8_t *scales, hipStream_t s, const int32_t *n_dev)
+{
+    const int64_t nb = N * (K / 32);
+    if (nb <= 0) return hipSuccess;
+    const dim3 grid((unsigned)std::min<int64_t>((nb + 255) / 256, 16384)), block(256);
+    if (v_f32)
+        hipLaunchKernelGGL(fp6x2_split_kernel<float>, grid, block, 0, s, (const float *)v, ldv, N,
+                           K, n_dev, data, scales);
+    else
+        hipLaunchKernelGGL(fp6x2_split_kernel<bf16>, grid, block, 0, s, (const bf16 *)v, ldv, N,
+                           K, n_dev, data, scales);
+    return hipGetLastError();
+}
+
+// 4 bytes per lane from `src` to LDS at `lds_base` (wave-uniform) + 4 lane
+// (global_load_lds_dword); waited for explicitly like dma16.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// ---------------------------------------------------------------------------
+// Grouped projection on the block-scaled matrix cores, 256-row tiles.
+//
+// Workgroup tile: up to 256 permuted rows of one expert (a work item of the
+// 256-row plan) x 256 weight rows, K step 64 (two MX blocks), 16 waves (4
+// per SIMD). Wave w: row block q = w / 4 (row tiles 2 q, 2 q + 1 of 32) and
+// slot c = w % 4 (gate and up rows of output columns 32 c .. + 32, or
+// weight rows 64 c .. + 64); per K step and (row tile, weight tile) two
+// 32 x 32 x 64 MFMAs, one per plane, into the same fp32 accumulator.
+//
+// Operands, as the instruction takes them (lane L, l = L % 32, g = L / 32;
+// checked with a one-wave probe against an fp64 evaluation):
+//   A (E2M3, 24 bytes): row l, MX block g of the step, the 24 stored bytes;
+//   B (E2M1, 16 bytes): weight row l, MX block g, the 16 stored code bytes;
+//   scales: lane L gives its row's (A) or weight row's (B) E8M0 code for
+//     MX block g.
+//
+// LDS: a three-stage ring filled by global_load_lds_dwordx4 / _dword (each
+// stage: 256 rows x 96 bytes of planes, 256 weight rows x 32 code bytes,
+// 256 rows x 4 scale bytes), one barrier per K step publishing step k and
+// freeing the stage that step k + 2 overwrites; the tile's weight scales
+// (256 x K / 32 bytes, rows padded to an odd number of dwords) copied once.
+// A row's 96 bytes are six 16-byte chunks (logical chunk c = bytes 16 c ..
+// of the step's blocks [b0 plane 1 | b0 plane 2 | b1 plane 1 | b1 plane 2]);
+// chunk c of row r sits at position c ^ ((r / 8) % 2), so the 16 rows of a
+// 16-lane read (96-byte stride: 8 distinct 8-bank offsets) cover all banks.
+// ---------------------------------------------------------------------------
+constexpr int F6_BN = 256, F6_BK = 64, F6_ROW = 96;
+constexpr int F6_STAGES = 3;
+constexpr int F6_A_BYTES = 256 * F6_ROW;         // 24 KB of planes
+constexpr int F6_W_BYTES = F6_BN * F6_BK / 2;    // 8 KB of E2M1 codes
+constexpr int F6_S_BYTES = 256 * 4;              // 1 KB of row scales
+constexpr int F6_STAGE = F6_A_BYTES + F6_W_BYTES + F6_S_BYTES;
+constexpr int F6_THREADS = 1024;
+constexpr int F6_MAX_K = 4096;
+
+__host__ __device__ constexpr int f6_scale_row(int K)
+{
+    return (((K / 32 + 3) / 4) | 1) * 4;
+}
+
+__host__ __device__ constexpr int f6_lds_bytes(int K)
+{
+    return F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K);
+}
+static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
+
+template <int ACT, typename OutT, bool PACKED>
+__global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
+    const uint8_t *__restrict__ ad, const uint8_t *__restrict__ as, int64_t ldb,
+    const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
+    const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
+    const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
+    OutT *__restrict__ out, int64_t ldo)
+{
+    constexpr bool GLU = ACT != ACT_NONE;
+    constexpr int COLS = GLU ? F6_BN / 2 : F6_BN;
+    extern __shared__ __attribute__((aligned(16))) uint8_t f6_lds[];
+    const int srow = f6_scale_row(K);
+    uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [256][srow] weight scales
+
+    const int nblk = (N + COLS - 1) / COLS;
+    const int total = plan[0] * nblk;
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    const int wi = (blockIdx.x % 8) * per_xcd + local;
+    if (local >= per_xcd || wi >= total) return;
+    const int grp = wi / nblk, nb = wi - grp * nblk;
+    const int2 it = ((const int2 *)(plan + hdr))[grp];
+    const int e = it.x & 0xffff, r0 = it.y, rend = r0 + (it.x >> 16);
+    const int mrows = rend - r0;
+    const int n0 = nb * COLS;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = wave & 3, q = wave >> 2;
+    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const int64_t row_d = ldb * 48, row_s = ldb * 2;  // bytes per split row
+
+    auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
+        int wrow;
+        if (GLU) {
+            wrow = min(n0 + (br & 127), N - 1);
+            wc = br < 128 ? w1c : w2c;
+            ws = br < 128 ? w1s : w2s;
+        } else {
+            wrow = min(n0 + br, N - 1);
+            wc = w1c;
+            ws = w1s;
+        }
+        return (int64_t)e * N + wrow;
+    };
+    auto arow_of = [&](int row) -> int64_t {
+        const int rc = min(r0 + row, rend - 1);
+        return a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+    };
+    // the DMA source of byte offset o of a stage's plane region
+    auto asrc = [&](int o) -> const uint8_t * {
+        const int r = o / F6_ROW, p = (o - r * F6_ROW) >> 4;
+        return ad + arow_of(r) * row_d + 16 * (p ^ ((r >> 3) & 1));
+    };
+
+    // ---- DMA sources. Every wave: plane bytes 1024 w + 16 L; waves 0-7 also
+    // plane bytes 16384 + 1024 w + 16 L, waves 8-15 the codes (threads
+    // 512..1023 -> LDS weight row (tid - 512) / 2, half holding MX block bh),
+    // waves 0-3 the scales of rows 64 w + L (4 bytes each).
+    const uint8_t *ag0 = asrc(1024 * wave + 16 * lane);
+    const bool aload2 = wave < 8;
+    const uint8_t *ag1 = asrc(aload2 ? 16384 + 1024 * wave + 16 * lane : 0);
+    const bool sload = wave < 4;
+    const uint8_t *sg = as + arow_of(sload ? 64 * wave + lane : 0) * row_s;
+    const int br = (tid & 511) >> 1, bh = (tid & 1) ^ ((br >> 3) & 1);
+    const uint8_t *bg;
+    {
+        const uint8_t *wc, *ws;
+        const int64_t wr64 = wsel(br, wc, ws);
+        if constexpr (PACKED)
+            bg = wc + (wr64 / 16) * nch * 1024 + (wr64 % 16) * 16;
+        else
+            bg = wc + wr64 * (K / 2) + 16 * bh;
+    }
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(f6_lds));
+    auto issue = [&](int kt, int st) {
+        const uint32_t sb = lds0 + st * F6_STAGE;
+        dma16(ag0 + kt * F6_ROW, sb + wave * 1024);
+        if (aload2) {
+            dma16(ag1 + kt * F6_ROW, sb + 16384 + wave * 1024);
+        } else {
+            const uint8_t *src;
+            if constexpr (PACKED)
+                src = bg + (kt >> 1) * 1024 + (2 * (kt & 1) + bh) * 256;
+            else
+                src = bg + kt * (F6_BK / 2);
+            dma16(src, sb + F6_A_BYTES + (wave - 8) * 1024);
+        }
+        if (sload) dma4(sg + kt * 4, sb + F6_A_BYTES + F6_W_BYTES + wave * 256);
+    };
+
+    const int nk = K / F6_BK;
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+
+    // ---- weight scales -> LDS, in K-block order per weight row
+    if constexpr (PACKED) {
+        const int per_row = nc4 * 4;
+        for (int idx = tid; idx < 256 * per_row; idx += F6_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            const int cg = r >> 2, g = r & 3;
+            const uint8_t *wc, *ws;
+            const int64_t wr64 = wsel(row, wc, ws);
+            const uint32_t v = *(const uint32_t *)(ws + (wr64 / 16) * nc4 * 256 + cg * 256 +
+                                                   g * 64 + (wr64 % 16) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kb = 16 * cg + 4 * i + g;
+                if (kb < K / 32) Wsc[row * srow + kb] = (uint8_t)(v >> (8 * i));
+            }
+        }
+    } else {
+        const int per_row = K / 128;
+        for (int idx = tid; idx < 256 * per_row; idx += F6_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            const uint8_t *wc, *ws;
+            const int64_t wr64 = wsel(row, wc, ws);
+            *(uint32_t *)(Wsc + row * srow + 4 * r) =
+                *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+        }
+    }
+
+    // ---- wave tiles
+    const int h = lane >> 5, l32 = lane & 31;
+    int bt[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) bt[j] = GLU ? 128 * j + 32 * slot : 64 * slot + 32 * j;
+    const int n_on = (64 * q < mrows ? 1 : 0) + (64 * q + 32 < mrows ? 1 : 0);
+    const int bpos = 16 * (h ^ ((l32 >> 3) & 1));
+    // rows 64 q + 32 i + l32 share (row / 8) % 2 = (l32 / 8) % 2
+    const int sw = (l32 >> 3) & 1;
+    const int apos0 = ((3 * h) ^ sw) << 4, apos1 = ((3 * h + 1) ^ sw) << 4,
+              apos2 = ((3 * h + 2) ^ sw) << 4;
+
+    auto run = [&](auto ni_c) {
+        constexpr int NI = decltype(ni_c)::value;
+        f32x16 acc[NI > 0 ? NI : 1][2];
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
+
+        auto compute = [&](int st, int kt) {
+            if constexpr (NI > 0) {
+                const uint8_t *Ap = f6_lds + st * F6_STAGE;
+                const uint8_t *Bq = Ap + F6_A_BYTES;
+                const uint8_t *Ss = Bq + F6_W_BYTES;
+                i32x8 bv[2];
+                int sb[2];
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int row = bt[j] + l32;
+                    const u32x4 w = *(const u32x4 *)(Bq + row * 32 + bpos);
+                    bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
+                    sb[j] = Wsc[row * srow + 2 * kt + h];
+                }
+                i32x8 a1[NI > 0 ? NI : 1], a2[NI > 0 ? NI : 1];
+                int sa1[NI > 0 ? NI : 1], sa2[NI > 0 ? NI : 1];
+#pragma unroll
+                for (int i = 0; i < NI; i++) {
+                    const int row = 64 * q + 32 * i + l32;
+                    const uint8_t *ar = Ap + row * F6_ROW;
+                    const u32x4 c0 = *(const u32x4 *)(ar + apos0);
+                    const u32x4 c1 = *(const u32x4 *)(ar + apos1);
+                    const u32x4 c2 = *(const u32x4 *)(ar + apos2);
+                    a1[i] = i32x8{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3],
+                                  (int)c1[0], (int)c1[1], 0, 0};
+                    a2[i] = i32x8{(int)c1[2], (int)c1[3], (int)c2[0], (int)c2[1],
+                                  (int)c2[2], (int)c2[3], 0, 0};
+                    const uint32_t s2 = *(const uint16_t *)(Ss + row * 4 + 2 * h);
+                    sa1[i] = (int)(s2 & 0xffu);
+                    sa2[i] = (int)(s2 >> 8);
+                }
+                // A format 2: E2M3; B format 4: E2M1; scale byte 0 of each
+#pragma unroll
+                for (int i = 0; i < NI; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a1[i], bv[j], acc[i][j], 2, 4, 0, sa1[i], 0, sb[j]);
+#pragma unroll
+                for (int i = 0; i < NI; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a2[i], bv[j], acc[i][j], 2, 4, 0, sa2[i], 0, sb[j]);
+            }
+        };
+
+        // loads of one step issued by this wave: the plane chunk(s), the
+        // codes or a second plane chunk, and (waves 0-3) the scales
+        for (int kt = 0; kt < nk; kt++) {
+            // this wave's loads of step kt are done (those of kt + 1 may
+            // still be in flight); the barrier publishes every wave's and ends
+            // the reads of step kt - 1
+            if (kt + 1 < nk) {
+                if (sload)
+                    asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+            const int st = kt % 3;
+            if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
+            compute(st, kt);
+        }
+
+        // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (rl >= mrows) continue;
+                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                if constexpr (GLU) {
+                    const int col = n0 + 32 * slot + l32;
+                    if (col < N)
+                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        const int col = n0 + 64 * slot + 32 * j + l32;
+                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
+                    }
+                }
+            }
+        }
+    };
+    // every branch runs the same barriers (nk) and the same loads
+    switch (__builtin_amdgcn_readfirstlane(n_on)) {
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    default: run(std::integral_constant<int, 0>{}); break;
+    }
+}
+
+template <int ACT, typename OutT, bool PACKED>
+static hipError_t launch_f6(const uint8_t *ad, const uint8_t *as, int64_t ldb,
+                            const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                            const uint8_t *w2c, const uint8_t *w2s, const int32_t *plan,
+                            int max_groups, int hdr, int N, int K, OutT *out, int64_t ldo,
+                            hipStream_t s)
+{
+    constexpr int COLS = ACT != ACT_NONE ? F6_BN / 2 : F6_BN;
+    const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
+    if (grid <= 0) return hipSuccess;
+    // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
+    // a grid of 8 * ceil(bound / 8) blocks covers every work item
+    const int64_t G = (grid + 7) / 8 * 8;
+    auto kern = gemm_fp6x2_w16_kernel<ACT, OutT, PACKED>;
+    const hipError_t err = ensure_dynamic_lds((const void *)kern, f6_lds_bytes(K));
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(F6_THREADS), f6_lds_bytes(K), s, ad, as, ldb,
+                       a_rows, w1c, w1s, w2c, w2s, plan, hdr, N, K, out, ldo);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, const uint8_t *as, int64_t ldb,
+                                 const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
+                                 const uint8_t *w2c, const uint8_t *w2s, int num_local,
+                                 int max_rows, int N, int K, int act, void *out, int out_f32,
+                                 int64_t ldo, const void *plan_ws, int packed, hipStream_t s)
+{
+    if (K % 128 != 0 || K > F6_MAX_K) return hipErrorInvalidValue;
+    const GemmPlanArgs pa = gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, nullptr);
+    const int32_t *plan = (const int32_t *)plan_ws;
+#define F6_ACT(OT, PK)                                                                            \
+    switch (act) {                                                                                \
+    case ACT_NONE:                                                                                \
+        return launch_f6<ACT_NONE, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, plan,         \
+                                           pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);               \
+    case ACT_SILU_MUL:                                                                            \
+        return launch_f6<ACT_SILU_MUL, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, plan,     \
+                                               pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);           \
+    case ACT_GELU_TANH_MUL:                                                                       \
+        return launch_f6<ACT_GELU_TANH_MUL, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s,      \
+                                                    plan, pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s); \
+    default:                                                                                      \
+        return hipErrorInvalidValue;                                                              \
+    }
+    if (out_f32) {
+        if (packed) F6_ACT(float, true)
+        F6_ACT(float, false)
+    }
+    if (packed) F6_ACT(bf16, true)
+    F6_ACT(bf16, false)
+#undef F6_ACT
+}
+
+hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, const uint8_t *as, int64_t ldb,
+                                     const int32_t *a_rows, const uint8_t *w1c,
+                                     const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
+                                     const int32_t *off, int num_local, int max_rows, int N,
+                                     int K, int act, void *out, int out_f32, int64_t ldo,
+                                     void *ws, int packed, hipStream_t s)
+{
+    hipError_t e = launch_gemm_plan_into(
+        off, num_local, gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws), s);
+    if (e != hipSuccess) return e;
+    return launch_gemm_fp6x2_run(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
+                                 K, act, out, out_f32, ldo, ws, packed, s);
+}
+
+}  // namespace moe

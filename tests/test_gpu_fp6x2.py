@@ -1,0 +1,265 @@
+"""GPU parity of the FP6X2 carriage (activations as two MXFP6 planes, MXFP4
+weights, v_mfma_scale_f32_32x32x64_f8f6f4 at the 6-bit x 4-bit rate).
+
+Stage by stage: the split byte for byte against the oracle's; the grouped
+projection elementwise against the exact sum of the planes' values times the
+exactly decoded weights; the layer against the oracle's default (bf16
+activation) layer on the GPU's routing, within the default contract. The
+projection's bound: the products are exact, a one-wave probe of the 6-bit x
+4-bit instruction found its 64-long sums exact to fp32 rounding, and the fp32
+accumulation of two partial sums per 64-long step adds at most
+2 (K/64) 2^-24 of sum|products|; the tests allow 1e-5 sum|a w|."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, LayerConfig, make_inputs, quantize_mxfp4
+from tests.parity_util import (assert_close_layer, host_weights, np_, oracle_rows, rel_l2,
+                               run_gpu_layer, sample_tokens)
+from tests.test_oracle_fp6x2 import _blocks
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MMA_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def m():
+    import mxfp4_expert_top_amd as mod
+    return mod
+
+
+def unpack_planes(data):
+    """[N, nb, 48] bytes as written by moe_fp6x2_split -> codes [2, N, nb * 32]:
+    per block, plane p's 24 bytes hold code i at bits 6 i .. 6 i + 5
+    (little-endian)."""
+    N, nb, _ = data.shape
+    planes = data.reshape(N, nb, 2, 24).transpose(2, 0, 1, 3)
+    bits = np.unpackbits(planes, axis=-1, bitorder="little").reshape(2, N, nb, 32, 6)
+    codes = (bits * (1 << np.arange(6))).sum(-1).astype(np.uint8)
+    return codes.reshape(2, N, nb * 32)
+
+
+def split_scales(scales):
+    """[N, nb, 2] -> [2, N, nb]."""
+    return np.ascontiguousarray(scales.transpose(2, 0, 1))
+
+
+def _check_split(m, v_dev, v_host):
+    data, scales = m.moe_fp6x2_split(v_dev)
+    torch.cuda.synchronize()
+    rc, rs = oracle.fp6x2_split(v_host)
+    assert np.array_equal(split_scales(np_(scales)), rs)
+    got = unpack_planes(np_(data))
+    assert np.array_equal(got, rc), np.argwhere(got != rc)[:5]
+
+
+# ---------------------------------------------------------------- the split
+@pytest.mark.parametrize("K", [32, 128, 3584])
+def test_fp6x2_split_fp32_bitexact(m, K):
+    """Ties of the E2M3 grid and either side of them, the 7.5 clamp, zero
+    blocks, a negative value rounding to zero, fp32 subnormals and the fp32
+    maximum; random rows of three magnitudes."""
+    v = _blocks().reshape(-1)
+    v = np.resize(v, ((v.size + K - 1) // K) * K).reshape(-1, K).astype(np.float32)
+    rnd = np.random.default_rng(K).standard_normal((7, K)).astype(np.float32)
+    v = np.ascontiguousarray(np.concatenate([v, rnd * 3.0, rnd * 1e-30, rnd * 1e30]))
+    _check_split(m, torch.from_numpy(v).to(DEV), v)
+
+
+def test_fp6x2_split_bf16_rows_with_stride(m):
+    rng = np.random.default_rng(5)
+    x = torch.from_numpy(rng.standard_normal((33, 3584 + 64)).astype(np.float32)).to(torch.bfloat16)
+    x[3, :64] = 0
+    x[4] *= 1e-20
+    x[5, :32] = torch.tensor(np.float32(2.0) ** -133)  # bf16 subnormals
+    _check_split(m, x.to(DEV)[:, :3584], x[:, :3584].float().numpy())
+
+
+def test_fp6x2_split_grid_stride(m):
+    """More blocks (140000 x 32) than the launch's threads (16384 x 256): rows
+    on both sides of the first pass's end, against the oracle."""
+    N, K = 140000, 1024
+    g = torch.Generator(device=DEV).manual_seed(7)
+    v = (torch.randn(N, K, generator=g, device=DEV) * 2.0).to(torch.bfloat16)
+    data, scales = m.moe_fp6x2_split(v)
+    torch.cuda.synchronize()
+    wrap = 16384 * 256 // (K // 32)
+    rows = np.r_[0:4, wrap - 4:wrap + 4, N - 4:N]
+    rc, rs = oracle.fp6x2_split(v[torch.from_numpy(rows).to(DEV)].float().cpu().numpy())
+    assert np.array_equal(split_scales(np_(scales)[rows]), rs)
+    assert np.array_equal(unpack_planes(np_(data)[rows]), rc)
+
+
+# ---------------------------------------------------------------- projection
+def _experts(num_local, N, K, seed):
+    g = torch.Generator().manual_seed(seed)
+    cs = [quantize_mxfp4(torch.randn(N, K, generator=g) / np.sqrt(K)) for _ in range(num_local)]
+    return torch.stack([c for c, _ in cs]), torch.stack([s for _, s in cs])
+
+
+def _bound(a, w):
+    return np.abs(a) @ np.abs(w).T
+
+
+def _split_rows(m, rng, R, K):
+    """Random bf16 rows of mixed magnitudes, split on the GPU; the value the
+    oracle's split of the same rows carries (fp64)."""
+    v = (rng.standard_normal((R, K)) * np.exp2(rng.integers(-3, 4, (R, 1)))).astype(np.float32)
+    vb = torch.from_numpy(v).to(torch.bfloat16)
+    data, scales = m.moe_fp6x2_split(vb.to(DEV))
+    rc, rs = oracle.fp6x2_split(vb.float().numpy())
+    return data, scales, oracle.fp6x2_value(rc, rs), vb.float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("K", [128, 640, 3584])
+def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
+    """Experts with 37, 0, 513, 1, 257 and 150 rows (empty, one row, ragged,
+    several 256-row groups), a column count that is not a tile multiple,
+    gathered rows, fp32 output; rows past the last expert's end untouched."""
+    rng = np.random.default_rng(K + 3 * act + 7 * packed)
+    nl, N, T = 6, 320, 700
+    counts = np.array([37, 0, 513, 1, 257, 150], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    xd, xs, xval, xb = _split_rows(m, rng, T, K)
+    a_rows = rng.integers(0, T, size=A).astype(np.int32)
+    w1c, w1s = _experts(nl, N, K, 3)
+    w2c, w2s = _experts(nl, N, K, 4) if act else (None, None)
+    dev = lambda t: None if t is None else t.to(DEV)
+    pk = lambda c, s: m.moe_mxfp4_prepack(dev(c), dev(s)) if packed else (dev(c), dev(s))
+    g1c, g1s = pk(w1c, w1s)
+    g2c, g2s = pk(w2c, w2s) if act else (None, None)
+    out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
+    m.moe_grouped_gemm_fp6x2(xd, xs, torch.from_numpy(a_rows).to(DEV), g1c, g1s, g2c, g2s,
+                             torch.from_numpy(off).to(DEV), A, act, out, ws,
+                             w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
+    torch.cuda.synchronize()
+    got = np_(out).astype(np.float64)
+    assert (got[A:] == 7.0).all()
+    xa, xba = xval[a_rows], xb[a_rows]
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        if r0 == r1:
+            continue
+        w1 = oracle.mxfp4_decode(w1c[e].numpy(), w1s[e].numpy()).astype(np.float64)
+        g = xa[r0:r1] @ w1.T
+        bg = MMA_TOL * _bound(xa[r0:r1], w1)
+        if act == 0:
+            assert (np.abs(got[r0:r1] - g) <= bg).all(), np.abs(got[r0:r1] - g).max()
+            # and the exact bf16 rows' product within what the planes leave
+            # out (at most 2^(E-7) per element)
+            gb = xba[r0:r1] @ w1.T
+            assert rel_l2(got[r0:r1], gb) < 2e-3
+        else:
+            w2 = oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64)
+            u = xa[r0:r1] @ w2.T
+            bu = MMA_TOL * _bound(xa[r0:r1], w2)
+            h = g / (1.0 + np.exp(-g)) * u
+            # first-order propagation: |d silu/dg| <= 1.1, |silu(g)| <= |g| + 0.28
+            tol = 1.1 * np.abs(u) * bg + (np.abs(g) + 0.28) * bu + 1e-5 * np.abs(h) + 1e-30
+            assert (np.abs(got[r0:r1] - h) <= tol).all(), np.abs(got[r0:r1] - h).max()
+
+
+def test_grouped_gemm_fp6x2_bf16_out_and_direct_rows(m):
+    """No gathered rows, bf16 output, the down-projection shape (K = 1024,
+    N = 3584 not a multiple of 256)."""
+    rng = np.random.default_rng(9)
+    nl, N, K = 3, 3584, 1024
+    counts = np.array([200, 3, 70], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    hd, hs, hval, _ = _split_rows(m, rng, A, K)
+    wc, wsc = _experts(nl, N, K, 8)
+    out = torch.empty(A, N, dtype=torch.bfloat16, device=DEV)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
+    m.moe_grouped_gemm_fp6x2(hd, hs, None, wc.to(DEV), wsc.to(DEV), None, None,
+                             torch.from_numpy(off).to(DEV), A, 0, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    for e in range(nl):
+        r0, r1 = off[e], off[e + 1]
+        w = oracle.mxfp4_decode(wc[e].numpy(), wsc[e].numpy()).astype(np.float64)
+        ref = hval[r0:r1] @ w.T
+        b = MMA_TOL * _bound(hval[r0:r1], w)
+        assert (np.abs(got[r0:r1] - ref) <= 2.0 ** -8 * (np.abs(ref) + b) + b).all()
+
+
+# ---------------------------------------------------------------- layer
+SMALL = [
+    LayerConfig("f0", T=37, I=128, d=256, E=64, k=8),
+    LayerConfig("f1", T=300, I=256, d=384, E=16, k=4),
+    LayerConfig("f2", T=50, I=128, d=256, E=40, k=6, expert_begin=8, num_local=20, bias="normal"),
+    LayerConfig("f3", T=700, I=128, d=256, E=100, k=6, bias="normal"),
+    LayerConfig("f4", T=2600, I=256, d=512, E=32, k=8, bias="normal"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+@pytest.mark.parametrize("packed", [False, True])
+def test_small_layer_fp6x2_vs_oracle(m, cfg, packed):
+    """The FP6X2 layer on 256-row tiles against the oracle's bf16-activation
+    layer on the GPU's scores, within the default contract; and against the
+    GPU's own bf16 layer (fp32 outputs), which it matches to the planes'
+    representation error."""
+    inp = make_inputs(cfg).to(DEV)
+    pw = m.prepack_weights(inp.weights) if packed else None
+    g = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, packed=pw,
+                      out_dtype=torch.float32)
+    lg = np_(g["logits"])
+    r_idx, _ = oracle.topk_softmax(lg, cfg.k)
+    assert np.array_equal(np_(g["idx"]), r_idx)
+    ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                       host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                       e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg)
+    got = np_(g["out"])
+    assert_close_layer(got, ref["out"], cfg.name)
+    b = run_gpu_layer(inp, mode=m.MODE_TILE256, packed=pw, out_dtype=torch.float32)
+    assert torch.equal(b["idx"], g["idx"])
+    assert rel_l2(got, np_(b["out"])) < 2e-3
+    assert not torch.equal(b["out"], g["out"])  # the FP6X2 projection ran
+
+
+def test_fp6x2_layer_determinism_bitwise(m):
+    inp = make_inputs(SMALL[4]).to(DEV)
+    a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
+    b = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_fp6x2_streaming_shapes_are_the_bf16_layer(m):
+    """Where the schedule streams the weights (few rows per expert) the FP6X2
+    precision runs the bf16 kernels: bitwise the bf16 layer."""
+    inp = make_inputs(SMALL[0]).to(DEV)
+    a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_STREAM)
+    b = run_gpu_layer(inp, mode=m.MODE_STREAM)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("name", ["prefill", "ep_share", "long_skewed_prefill"])
+def test_full_size_fp6x2(m, name):
+    """The prefill-sized workloads with the FP6X2 gate/up projection, in the
+    benchmark's launch configuration (streaming-layout weights, schedule
+    chosen automatically, fp32 output): routing on every token, 64 sampled
+    tokens' rows (segment edges, the hottest expert, seeded random) against
+    the oracle's bf16-activation layer, within the default contract."""
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, DEV)
+    g = run_gpu_layer(inp, precision=m.PREC_FP6X2, packed=m.prepack_weights(inp.weights),
+                      out_dtype=torch.float32)
+    r_idx, _ = oracle.topk_softmax(np_(g["logits"]), cfg.k)
+    assert np.array_equal(np_(g["idx"]), r_idx)
+    toks = sample_tokens(cfg, r_idx, 64, seed=3)
+    ref = oracle_rows(inp, r_idx, np_(g["w"]), toks)
+    got = g["out"].float().cpu().numpy()[toks]
+    print(f"{name}: rel-L2 {rel_l2(got, ref):.3e}")
+    assert_close_layer(got, ref, name)
+    del inp, g
+    torch.cuda.empty_cache()
