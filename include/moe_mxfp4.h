@@ -307,38 +307,44 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
  * and each element is ./2^(s-127) rounded to the nearest E2M3 value (ties to
  * the even code), magnitudes from 7.5 up clamped to 7.5, sign bit from the
  * element (-0 keeps it, code 0x20).
- *   data   [N][K/32][48] bytes: block b's plane-1 codes, then its plane-2
- *          codes, 24 bytes each; code i of a plane at bits 6i..6i+5 of its
- *          24 little-endian bytes
- *   scales [N][K/32][2]: plane-1 and plane-2 scale codes of block b
- * Preconditions: finite v. Errors: K % 32 != 0 -> UNSUPPORTED; v_dtype not
- * bf16 or fp32, ldv < K, ldv % 8 != 0, NULL or misaligned (16-byte v and
- * data, 2-byte scales) pointers -> INVALID_ARG. N == 0 is a no-op. */
-int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, uint8_t *data,
-                    uint8_t *scales, moe_stream_t stream);
+ * Output row n at out + 2 n ldo bytes (ldo in elements: a split row of K
+ * elements takes the 2 K bytes of a bf16 row), one 128-byte record per 64
+ * elements (blocks 2s and 2s+1):
+ *   bytes   0..47  block 2s: plane-1 codes (24 bytes), plane-2 codes (24)
+ *   bytes  48..95  block 2s+1: the same
+ *   bytes  96..99  scale codes (2s, plane 1), (2s, plane 2), (2s+1, plane 1),
+ *                  (2s+1, plane 2)
+ *   bytes 100..127 zero
+ * with code i of a plane at bits 6i..6i+5 of its 24 little-endian bytes.
+ * Preconditions: finite v. Errors: K % 64 != 0 -> UNSUPPORTED; v_dtype not
+ * bf16 or fp32, ldv < K, ldv % 8 != 0, ldo < K, ldo % 64 != 0, NULL or
+ * misaligned (16-byte v, 128-byte out) pointers -> INVALID_ARG. N == 0 is a
+ * no-op. */
+int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, uint8_t *out,
+                    int64_t ldo, moe_stream_t stream);
 
 /* moe_grouped_gemm_fp6x2 -- moe_grouped_gemm_mxfp4 with rows carried as two
  * MXFP6 planes:
  *   a_row  = (a_rows ? a_rows[r] : r)
  *   acc1[n] = sum_k A(a_row, k) * W1[e][n][k], A(r, k) = the plane-1 value
  *             plus the plane-2 value of element k of split row r
- * with split rows as moe_fp6x2_split writes them (row r: data at a_data +
- * r * ldb * 48, scales at a_scales + r * ldb * 2; ldb = row stride in
- * 32-element blocks), on v_mfma_scale_f32_32x32x64_f8f6f4 (exact products;
- * each 64-long partial sum formed inside the instruction, one per plane, then
- * accumulated in fp32); out as in moe_grouped_gemm_mxfp4. Schedule: 256-row
- * tiles (no mode argument). ws holds moe_grouped_gemm_fp6x2_workspace_size(...)
- * bytes. Requirements: ldb >= K/32, ldb % 4 == 0, ldo >= N, ldo % 8 == 0;
- * 16-byte aligned arrays. Errors as moe_grouped_gemm_mxfp4, and K > 4096 ->
+ * with split rows as moe_fp6x2_split writes them (row r at a + 2 r lda
+ * bytes; lda in elements), on v_mfma_scale_f32_32x32x64_f8f6f4 (exact
+ * products; each 64-long partial sum formed inside the instruction, one per
+ * plane, then accumulated in fp32); out as in moe_grouped_gemm_mxfp4.
+ * Schedule: 256-row tiles (no mode argument). ws holds
+ * moe_grouped_gemm_fp6x2_workspace_size(...) bytes. Requirements: lda >= K,
+ * lda % 64 == 0, 128-byte aligned a, ldo >= N, ldo % 8 == 0, 16-byte aligned
+ * weight and output arrays. Errors as moe_grouped_gemm_mxfp4, and K > 4096 ->
  * UNSUPPORTED. */
 size_t moe_grouped_gemm_fp6x2_workspace_size(int num_local, int max_rows);
-int moe_grouped_gemm_fp6x2(const uint8_t *a_data, const uint8_t *a_scales, int64_t ldb,
-                           const int32_t *a_rows, const uint8_t *w1_codes,
-                           const uint8_t *w1_scales, const uint8_t *w2_codes,
-                           const uint8_t *w2_scales, const int32_t *expert_offsets,
-                           int num_local, int max_rows, int N, int K, int block_size,
-                           int w_layout, int act, void *out, int out_dtype, int64_t ldo,
-                           void *ws, size_t ws_bytes, moe_stream_t stream);
+int moe_grouped_gemm_fp6x2(const uint8_t *a, int64_t lda, const int32_t *a_rows,
+                           const uint8_t *w1_codes, const uint8_t *w1_scales,
+                           const uint8_t *w2_codes, const uint8_t *w2_scales,
+                           const int32_t *expert_offsets, int num_local, int max_rows, int N,
+                           int K, int block_size, int w_layout, int act, void *out,
+                           int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
+                           moe_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- weighted unpermute (P3 section 四, combine: results come back

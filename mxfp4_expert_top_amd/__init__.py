@@ -90,12 +90,12 @@ def _load(path=None):
     L.moe_grouped_gemm_mx8.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                        i32, p, i32, p, i64, i32, p, sz, p]
     L.moe_fp6x2_split.restype = i32
-    L.moe_fp6x2_split.argtypes = [p, i32, i64, i64, i32, p, p, p]
+    L.moe_fp6x2_split.argtypes = [p, i32, i64, i64, i32, p, i64, p]
     L.moe_grouped_gemm_fp6x2_workspace_size.restype = sz
     L.moe_grouped_gemm_fp6x2_workspace_size.argtypes = [i32, i32]
     L.moe_grouped_gemm_fp6x2.restype = i32
-    L.moe_grouped_gemm_fp6x2.argtypes = [p, p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32,
-                                         i32, i32, p, i32, i64, p, sz, p]
+    L.moe_grouped_gemm_fp6x2.argtypes = [p, i64, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                         i32, p, i32, i64, p, sz, p]
     return L
 
 
@@ -405,46 +405,42 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
     _check("moe_grouped_gemm_mx8", st)
 
 
-def moe_fp6x2_split(v, data=None, scales=None, stream=None):
-    """bf16 or fp32 [N, K] on the GPU -> two MXFP6 planes: data uint8
-    [N, K/32, 48] (per block: plane-1 codes, plane-2 codes, 24 bytes each,
-    code i at bits 6i..6i+5), scales uint8 [N, K/32, 2]."""
+def moe_fp6x2_split(v, out=None, stream=None):
+    """bf16 or fp32 [N, K] on the GPU -> the two MXFP6 planes as uint8
+    [N, 2 K]: one 128-byte record per 64 elements (per block: plane-1 codes,
+    plane-2 codes, 24 bytes each, code i at bits 6i..6i+5; then the four
+    scale codes at bytes 96..99 and zeros)."""
     if v.dtype not in (torch.bfloat16, torch.float32) or v.dim() != 2:
         raise TypeError("v must be a 2-D bf16 or fp32 tensor")
     N, K = v.shape
     if v.stride(1) != 1:
         raise ValueError("v rows must be contiguous")
-    if data is None:
-        data = torch.empty(N, K // 32, 48, dtype=torch.uint8, device=v.device)
-    if scales is None:
-        scales = torch.empty(N, K // 32, 2, dtype=torch.uint8, device=v.device)
-    _dev(data, scales)
-    if not v.is_cuda or v.device != data.device:
-        raise ValueError("v must be on the GPU of data and scales")
-    _want(data, torch.uint8, (N, K // 32, 48), "data")
-    _want(scales, torch.uint8, (N, K // 32, 2), "scales")
-    _check("moe_fp6x2_split", lib.moe_fp6x2_split(_ptr(v), _dt(v), v.stride(0), N, K,
-                                                  _ptr(data), _ptr(scales), _stream(stream)))
-    return data, scales
+    if out is None:
+        out = torch.empty(N, 2 * K, dtype=torch.uint8, device=v.device)
+    _dev(out)
+    if not v.is_cuda or v.device != out.device:
+        raise ValueError("v must be on the GPU of out")
+    _want(out, torch.uint8, (N, 2 * K), "out")
+    _check("moe_fp6x2_split", lib.moe_fp6x2_split(_ptr(v), _dt(v), v.stride(0), N, K, _ptr(out),
+                                                  K, _stream(stream)))
+    return out
 
 
 def moe_grouped_gemm_fp6x2_workspace_size(num_local, max_rows):
     return int(lib.moe_grouped_gemm_fp6x2_workspace_size(num_local, max_rows))
 
 
-def moe_grouped_gemm_fp6x2(a_data, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
+def moe_grouped_gemm_fp6x2(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
                            expert_offsets, max_rows, act, out, ws, w_layout=LAYOUT_OCP,
                            stream=None):
-    """moe_grouped_gemm_mxfp4 with rows as two MXFP6 planes (a_data uint8
-    [rows, K/32, 48], a_scales uint8 [rows, K/32, 2], as moe_fp6x2_split
-    writes them) on the block-scaled matrix cores, 256-row tiles."""
+    """moe_grouped_gemm_mxfp4 with rows as two MXFP6 planes (``a`` uint8
+    [rows, 2 K] as moe_fp6x2_split writes it) on the block-scaled matrix
+    cores, 256-row tiles."""
     num_local = expert_offsets.shape[0] - 1
     N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
-    _dev(a_data, a_scales, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
-         out, ws)
-    rows = a_data.shape[0]
-    _want(a_data, torch.uint8, (rows, K // 32, 48), "a_data")
-    _want(a_scales, torch.uint8, (rows, K // 32, 2), "a_scales")
+    _dev(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets, out, ws)
+    rows = a.shape[0]
+    _want(a, torch.uint8, (rows, 2 * K), "a")
     _want(w1_codes, torch.uint8, (num_local, N, K // 2), "w1_codes")
     _want(w1_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w1_scales")
     if w2_codes is not None:
@@ -456,12 +452,12 @@ def moe_grouped_gemm_fp6x2(a_data, a_scales, a_rows, w1_codes, w1_scales, w2_cod
         if a_rows.dtype != torch.int32 or a_rows.numel() < max_rows:
             raise ValueError("a_rows must be int32 with >= max_rows entries")
     elif rows < max_rows:
-        raise ValueError("a_data must hold >= max_rows rows")
+        raise ValueError("a must hold >= max_rows rows")
     nbytes = ws.numel() * ws.element_size() if ws is not None else 0
     st = lib.moe_grouped_gemm_fp6x2(
-        _ptr(a_data), _ptr(a_scales), K // 32, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales),
-        _ptr(w2_codes), _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K,
-        MX_BLOCK, w_layout, act, _ptr(out), _dt(out), N, _ptr(ws), nbytes, _stream(stream))
+        _ptr(a), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K, MX_BLOCK, w_layout, act,
+        _ptr(out), _dt(out), N, _ptr(ws), nbytes, _stream(stream))
     _check("moe_grouped_gemm_fp6x2", st)
 
 

@@ -108,7 +108,7 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 struct LayerWs {
     size_t logits, planes, wsplit, idx, w, off, perm, inv, pws, gws, h, y, total;
     size_t xq, xs, hq, hs;  // MX8 mode: MXFP8 tokens and h (codes, scales)
-    size_t xf, xfs;         // FP6X2 gate/up: the tokens' two MXFP6 planes
+    size_t xf;              // FP6X2 gate/up: the tokens' two MXFP6 planes
     bool f6;                // the FP6X2 gate/up projection runs
     int splits;
     int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
@@ -157,8 +157,7 @@ LayerWs layer_ws(const moe_layer_params *p)
     L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
     L.f6 = fp6x2_gate_up(p);
     if (L.f6) {
-        L.xf = o;  o += round_up(T * (size_t)(p->d / 32) * 48);
-        L.xfs = o; o += round_up(T * (size_t)(p->d / 32) * 2);
+        L.xf = o;  o += round_up(T * (size_t)p->d * 2);
     }
     if (mx8) {
         L.xq = o; o += round_up(T * (size_t)p->d);
@@ -332,17 +331,17 @@ int moe_mxfp8_quantize(const void *v, int v_dtype, int64_t ldv, int64_t N, int K
     return MOE_OK;
 }
 
-int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, uint8_t *data,
-                    uint8_t *scales, moe_stream_t stream)
+int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, uint8_t *out,
+                    int64_t ldo, moe_stream_t stream)
 {
     CHECK(N >= 0 && K >= 0, MOE_ERR_INVALID_ARG);
     CHECK(v_dtype == MOE_DT_BF16 || v_dtype == MOE_DT_F32, MOE_ERR_INVALID_ARG);
-    CHECK(K % 32 == 0, MOE_ERR_UNSUPPORTED);
+    CHECK(K % 64 == 0, MOE_ERR_UNSUPPORTED);
     if (N == 0 || K == 0) return MOE_OK;
-    CHECK(v && data && scales, MOE_ERR_INVALID_ARG);
-    CHECK(ldv >= K && ldv % 8 == 0, MOE_ERR_INVALID_ARG);
-    CHECK(aligned(v, 16) && aligned(data, 16) && aligned(scales, 2), MOE_ERR_INVALID_ARG);
-    HIP_TRY(launch_fp6x2_split(v, v_dtype == MOE_DT_F32, ldv, N, K, data, scales,
+    CHECK(v && out, MOE_ERR_INVALID_ARG);
+    CHECK(ldv >= K && ldv % 8 == 0 && ldo >= K && ldo % 64 == 0, MOE_ERR_INVALID_ARG);
+    CHECK(aligned(v, 16) && aligned(out, 128), MOE_ERR_INVALID_ARG);
+    HIP_TRY(launch_fp6x2_split(v, v_dtype == MOE_DT_F32, ldv, N, K, out, 2 * ldo,
                                as_stream(stream)));
     return MOE_OK;
 }
@@ -353,27 +352,26 @@ size_t moe_grouped_gemm_fp6x2_workspace_size(int num_local, int max_rows)
     return grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE256);
 }
 
-int moe_grouped_gemm_fp6x2(const uint8_t *a_data, const uint8_t *a_scales, int64_t ldb,
-                           const int32_t *a_rows, const uint8_t *w1_codes,
-                           const uint8_t *w1_scales, const uint8_t *w2_codes,
-                           const uint8_t *w2_scales, const int32_t *expert_offsets,
-                           int num_local, int max_rows, int N, int K, int block_size,
-                           int w_layout, int act, void *out, int out_dtype, int64_t ldo,
-                           void *ws, size_t ws_bytes, moe_stream_t stream)
+int moe_grouped_gemm_fp6x2(const uint8_t *a, int64_t lda, const int32_t *a_rows,
+                           const uint8_t *w1_codes, const uint8_t *w1_scales,
+                           const uint8_t *w2_codes, const uint8_t *w2_scales,
+                           const int32_t *expert_offsets, int num_local, int max_rows, int N,
+                           int K, int block_size, int w_layout, int act, void *out,
+                           int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
+                           moe_stream_t stream)
 {
-    // check_gemm takes the row stride in elements: 32 per block
-    int rc = check_gemm(a_data, ldb * 32, w1_codes, w1_scales, w2_codes, w2_scales,
-                        expert_offsets, num_local, max_rows, N, K, block_size, w_layout, act,
-                        out, out_dtype, ldo);
+    int rc = check_gemm(a, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
+                        num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
+                        ldo);
     if (rc) return rc;
     CHECK(K <= 4096, MOE_ERR_UNSUPPORTED);
     if (max_rows == 0) return MOE_OK;
-    CHECK(a_scales && ldb % 4 == 0 && aligned(a_scales, 16), MOE_ERR_INVALID_ARG);
+    CHECK(lda % 64 == 0 && aligned(a, 128), MOE_ERR_INVALID_ARG);
     rc = check_ws(ws, ws_bytes, grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE256));
     if (rc) return rc;
-    HIP_TRY(launch_grouped_gemm_fp6x2(a_data, a_scales, ldb, a_rows, w1_codes, w1_scales,
-                                      w2_codes, w2_scales, expert_offsets, num_local, max_rows,
-                                      N, K, act, out, out_dtype == MOE_DT_F32, ldo, ws,
+    HIP_TRY(launch_grouped_gemm_fp6x2(a, lda, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
+                                      expert_offsets, num_local, max_rows, N, K, act, out,
+                                      out_dtype == MOE_DT_F32, ldo, ws,
                                       w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
     return MOE_OK;
 }
@@ -594,11 +592,11 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
     if (ev) HIP_TRY(hipEventRecord(ev[2], s));
     if (L.f6) {
         // the tokens as two MXFP6 planes, then the block-scaled projection
-        uint8_t *xf = (uint8_t *)(base + L.xf), *xfs = (uint8_t *)(base + L.xfs);
-        HIP_TRY(launch_fp6x2_split(x, 0, p->d, p->T, p->d, xf, xfs, s));
-        HIP_TRY(launch_gemm_fp6x2_run(xf, xfs, p->d / 32, perm, gate_codes, gate_scales,
-                                      up_codes, up_scales, p->num_local, A, p->I, p->d, p->act,
-                                      h, 0, p->I, base + L.gws, packed, s));
+        uint8_t *xf = (uint8_t *)(base + L.xf);
+        HIP_TRY(launch_fp6x2_split(x, 0, p->d, p->T, p->d, xf, 2 * (int64_t)p->d, s));
+        HIP_TRY(launch_gemm_fp6x2_run(xf, p->d, perm, gate_codes, gate_scales, up_codes,
+                                      up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
+                                      base + L.gws, packed, s));
     } else {
         HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
                                 up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,

@@ -18,11 +18,16 @@
 //   gemm_fp6x2_w16_kernel    grouped projection on 256 x 256 tiles, the two
 //                            planes x MXFP4 weights, fp32 accumulation
 //
-// Storage of a split row (K elements, nb = K / 32 blocks):
-//   data   [nb][48] bytes: block b's plane-1 codes (24 bytes), then its
-//          plane-2 codes (24 bytes); code i of a plane at bits 6 i .. 6 i + 5
-//          of the 24 little-endian bytes (the instruction's operand order)
-//   scales [nb][2]: block b's plane-1 and plane-2 E8M0 codes
+// Storage of a split row of K elements: 2 K bytes (the size of the bf16 row),
+// one 128-byte record per 64 elements (blocks 2 s and 2 s + 1):
+//   bytes  0..23  block 2 s, plane-1 codes    bytes 48..71  block 2 s + 1, plane 1
+//   bytes 24..47  block 2 s, plane-2 codes    bytes 72..95  block 2 s + 1, plane 2
+//   bytes 96..99  E8M0 scales: (2 s, plane 1), (2 s, plane 2), (2 s + 1,
+//                 plane 1), (2 s + 1, plane 2)
+//   bytes 100..127 zero
+// with code i of a plane at bits 6 i .. 6 i + 5 of its 24 little-endian bytes
+// (the instruction's operand order). Each K step of the projection then
+// reads one aligned 128-byte line per row, scales included.
 #include <type_traits>
 
 #include "common.hpp"
@@ -30,7 +35,9 @@
 
 namespace moe {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // fp32 -> MXFP6 (E2M3). Per block: s = clamp(floor(log2 amax) - 2 + 127, 0,
@@ -127,13 +134,12 @@ __device__ __forceinline__ void f6_load32<bf16>(const bf16 *p, float v[32])
 }
 
 // Rows n < min(N, *n_dev) (all N rows when n_dev is null); one thread per
-// 32-element block, grid-stride. data [N][K/32][48], scales [N][K/32][2].
+// 32-element block, grid-stride. Row n of the output at out + n * ldo bytes.
 template <typename InT>
 __global__ __launch_bounds__(256) void fp6x2_split_kernel(const InT *__restrict__ v, int64_t ldv,
                                                           int64_t N, int K,
                                                           const int32_t *__restrict__ n_dev,
-                                                          uint8_t *__restrict__ data,
-                                                          uint8_t *__restrict__ scales)
+                                                          uint8_t *__restrict__ out, int64_t ldo)
 {
     const int nb = K / 32;
     const int64_t rows = n_dev ? min(N, (int64_t)max(*n_dev, 0)) : N;
@@ -147,51 +153,45 @@ __global__ __launch_bounds__(256) void fp6x2_split_kernel(const InT *__restrict_
         uint32_t w[12];
         const uint32_t s1 = mxfp6_plane(x, w);
         const uint32_t s2 = mxfp6_plane(x, w + 6);
-        u32x4 *dst = (u32x4 *)(data + i * 48);
+        uint8_t *rec = out + n * ldo + (b >> 1) * 128;
+        u32x4 *dst = (u32x4 *)(rec + (b & 1) * 48);
         dst[0] = u32x4{w[0], w[1], w[2], w[3]};
         dst[1] = u32x4{w[4], w[5], w[6], w[7]};
         dst[2] = u32x4{w[8], w[9], w[10], w[11]};
-        *(uint16_t *)(scales + i * 2) = (uint16_t)(s1 | (s2 << 8));
+        *(uint16_t *)(rec + 96 + 2 * (b & 1)) = (uint16_t)(s1 | (s2 << 8));
+        if (b & 1) {
+            *(uint32_t *)(rec + 100) = 0u;
+            *(uint2 *)(rec + 104) = make_uint2(0u, 0u);
+            *(u32x4 *)(rec + 112) = u32x4{0u, 0u, 0u, 0u};
+        }
     }
 }
 
 hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
-                              uint8_t *data, uint8_t *scales, hipStream_t s, const int32_t *n_dev)
+                              uint8_t *out, int64_t ldo, hipStream_t s, const int32_t *n_dev)
 {
     const int64_t nb = N * (K / 32);
     if (nb <= 0) return hipSuccess;
     const dim3 grid((unsigned)std::min<int64_t>((nb + 255) / 256, 16384)), block(256);
     if (v_f32)
         hipLaunchKernelGGL(fp6x2_split_kernel<float>, grid, block, 0, s, (const float *)v, ldv, N,
-                           K, n_dev, data, scales);
+                           K, n_dev, out, ldo);
     else
         hipLaunchKernelGGL(fp6x2_split_kernel<bf16>, grid, block, 0, s, (const bf16 *)v, ldv, N,
-                           K, n_dev, data, scales);
+                           K, n_dev, out, ldo);
     return hipGetLastError();
 }
-
-// 4 bytes per lane from `src` to LDS at `lds_base` (wave-uniform) + 4 lane
-// (global_load_lds_dword); waited for explicitly like dma16.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-                 :
-                 : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // ---------------------------------------------------------------------------
 // Grouped projection on the block-scaled matrix cores, 256-row tiles.
 //
 // Workgroup tile: up to 256 permuted rows of one expert (a work item of the
-// 256-row plan) x 256 weight rows, K step 64 (two MX blocks), 16 waves (4
-// per SIMD). Wave w: row block q = w / 4 (row tiles 2 q, 2 q + 1 of 32) and
-// slot c = w % 4 (gate and up rows of output columns 32 c .. + 32, or
-// weight rows 64 c .. + 64); per K step and (row tile, weight tile) two
-// 32 x 32 x 64 MFMAs, one per plane, into the same fp32 accumulator.
+// 256-row plan) x 256 weight rows, K step 64 (two MX blocks, one 128-byte
+// record of a split row), 16 waves (4 per SIMD). Wave w: row block q = w / 4
+// (row tiles 2 q, 2 q + 1 of 32) and slot c = w % 4 (gate and up rows of
+// output columns 32 c .. + 32, or weight rows 64 c .. + 64); per K step and
+// (row tile, weight tile) two 32 x 32 x 64 MFMAs, one per plane, into the
+// same fp32 accumulator.
 //
 // Operands, as the instruction takes them (lane L, l = L % 32, g = L / 32;
 // checked with a one-wave probe against an fp64 evaluation):
@@ -200,22 +200,19 @@ __device__ __forceinline__ void dma4(const void *src, uint32_t lds_base)
 //   scales: lane L gives its row's (A) or weight row's (B) E8M0 code for
 //     MX block g.
 //
-// LDS: a three-stage ring filled by global_load_lds_dwordx4 / _dword (each
-// stage: 256 rows x 96 bytes of planes, 256 weight rows x 32 code bytes,
-// 256 rows x 4 scale bytes), one barrier per K step publishing step k and
-// freeing the stage that step k + 2 overwrites; the tile's weight scales
-// (256 x K / 32 bytes, rows padded to an odd number of dwords) copied once.
-// A row's 96 bytes are six 16-byte chunks (logical chunk c = bytes 16 c ..
-// of the step's blocks [b0 plane 1 | b0 plane 2 | b1 plane 1 | b1 plane 2]);
-// chunk c of row r sits at position c ^ ((r / 8) % 2), so the 16 rows of a
-// 16-lane read (96-byte stride: 8 distinct 8-bank offsets) cover all banks.
+// LDS: a three-stage ring filled by global_load_lds_dwordx4 (each stage:
+// 256 rows x 128 bytes of records, 256 weight rows x 32 code bytes), one
+// barrier per K step publishing step k and freeing the stage that step k + 2
+// overwrites; the tile's weight scales (256 x K / 32 bytes, rows padded to an
+// odd number of dwords) copied once. Chunk c (16 bytes) of a row's record
+// sits at position c ^ ((r / 2) % 8), so the 16 rows of a 16-lane read
+// cover all banks (the bf16 kernel's A arrangement).
 // ---------------------------------------------------------------------------
-constexpr int F6_BN = 256, F6_BK = 64, F6_ROW = 96;
+constexpr int F6_BN = 256, F6_BK = 64, F6_ROW = 128;
 constexpr int F6_STAGES = 3;
-constexpr int F6_A_BYTES = 256 * F6_ROW;         // 24 KB of planes
+constexpr int F6_A_BYTES = 256 * F6_ROW;         // 32 KB of records
 constexpr int F6_W_BYTES = F6_BN * F6_BK / 2;    // 8 KB of E2M1 codes
-constexpr int F6_S_BYTES = 256 * 4;              // 1 KB of row scales
-constexpr int F6_STAGE = F6_A_BYTES + F6_W_BYTES + F6_S_BYTES;
+constexpr int F6_STAGE = F6_A_BYTES + F6_W_BYTES;
 constexpr int F6_THREADS = 1024;
 constexpr int F6_MAX_K = 4096;
 
@@ -232,11 +229,11 @@ static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
 
 template <int ACT, typename OutT, bool PACKED>
 __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
-    const uint8_t *__restrict__ ad, const uint8_t *__restrict__ as, int64_t ldb,
-    const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
-    const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
-    const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
-    OutT *__restrict__ out, int64_t ldo)
+    const uint8_t *__restrict__ ad, int64_t lda, const int32_t *__restrict__ a_rows,
+    const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
+    const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
+    const int32_t *__restrict__ plan, int hdr, int N, int K, OutT *__restrict__ out,
+    int64_t ldo)
 {
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? F6_BN / 2 : F6_BN;
@@ -260,7 +257,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = wave & 3, q = wave >> 2;
     const int nch = K / 128, nc4 = (nch + 3) / 4;
-    const int64_t row_d = ldb * 48, row_s = ldb * 2;  // bytes per split row
+    const int64_t row_b = 2 * lda;  // bytes per split row
 
     auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
         int wrow;
@@ -275,25 +272,19 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
         }
         return (int64_t)e * N + wrow;
     };
-    auto arow_of = [&](int row) -> int64_t {
-        const int rc = min(r0 + row, rend - 1);
-        return a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
-    };
-    // the DMA source of byte offset o of a stage's plane region
-    auto asrc = [&](int o) -> const uint8_t * {
-        const int r = o / F6_ROW, p = (o - r * F6_ROW) >> 4;
-        return ad + arow_of(r) * row_d + 16 * (p ^ ((r >> 3) & 1));
-    };
 
-    // ---- DMA sources. Every wave: plane bytes 1024 w + 16 L; waves 0-7 also
-    // plane bytes 16384 + 1024 w + 16 L, waves 8-15 the codes (threads
-    // 512..1023 -> LDS weight row (tid - 512) / 2, half holding MX block bh),
-    // waves 0-3 the scales of rows 64 w + L (4 bytes each).
-    const uint8_t *ag0 = asrc(1024 * wave + 16 * lane);
-    const bool aload2 = wave < 8;
-    const uint8_t *ag1 = asrc(aload2 ? 16384 + 1024 * wave + 16 * lane : 0);
-    const bool sload = wave < 4;
-    const uint8_t *sg = as + arow_of(sload ? 64 * wave + lane : 0) * row_s;
+    // ---- DMA sources. Records: instruction j of wave w fills rows 16 w + 8 j
+    // .. + 7 (lane L: chunk position L % 8 of row 16 w + 8 j + L / 8).
+    const uint8_t *ag[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int rt = 16 * wave + 8 * j + (lane >> 3);
+        const int rc = min(r0 + rt, rend - 1);
+        const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
+        ag[j] = ad + arow * row_b + 16 * ((lane & 7) ^ ((rt >> 1) & 7));
+    }
+    // codes: threads 0..511 -> LDS weight row tid / 2, half holding MX block bh
+    const bool wload = wave < 8;
     const int br = (tid & 511) >> 1, bh = (tid & 1) ^ ((br >> 3) & 1);
     const uint8_t *bg;
     {
@@ -307,23 +298,21 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_address(f6_lds));
     auto issue = [&](int kt, int st) {
         const uint32_t sb = lds0 + st * F6_STAGE;
-        dma16(ag0 + kt * F6_ROW, sb + wave * 1024);
-        if (aload2) {
-            dma16(ag1 + kt * F6_ROW, sb + 16384 + wave * 1024);
-        } else {
+#pragma unroll
+        for (int j = 0; j < 2; j++) dma16(ag[j] + kt * F6_ROW, sb + (2 * wave + j) * 1024);
+        if (wload) {
             const uint8_t *src;
             if constexpr (PACKED)
                 src = bg + (kt >> 1) * 1024 + (2 * (kt & 1) + bh) * 256;
             else
                 src = bg + kt * (F6_BK / 2);
-            dma16(src, sb + F6_A_BYTES + (wave - 8) * 1024);
+            dma16(src, sb + F6_A_BYTES + wave * 1024);
         }
-        if (sload) dma4(sg + kt * 4, sb + F6_A_BYTES + F6_W_BYTES + wave * 256);
     };
 
-    const int nk = K / F6_BK;
+    const int nk = K / F6_BK;  // even: K is a multiple of 128
     issue(0, 0);
-    if (nk > 1) issue(1, 1);
+    issue(1, 1);
 
     // ---- weight scales -> LDS, in K-block order per weight row
     if constexpr (PACKED) {
@@ -359,10 +348,10 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     for (int j = 0; j < 2; j++) bt[j] = GLU ? 128 * j + 32 * slot : 64 * slot + 32 * j;
     const int n_on = (64 * q < mrows ? 1 : 0) + (64 * q + 32 < mrows ? 1 : 0);
     const int bpos = 16 * (h ^ ((l32 >> 3) & 1));
-    // rows 64 q + 32 i + l32 share (row / 8) % 2 = (l32 / 8) % 2
-    const int sw = (l32 >> 3) & 1;
-    const int apos0 = ((3 * h) ^ sw) << 4, apos1 = ((3 * h + 1) ^ sw) << 4,
-              apos2 = ((3 * h + 2) ^ sw) << 4;
+    // rows 64 q + 32 i + l32 share (row / 2) % 8 = (l32 / 2) % 8
+    const int key = (l32 >> 1) & 7;
+    const int apos0 = ((3 * h) ^ key) << 4, apos1 = ((3 * h + 1) ^ key) << 4,
+              apos2 = ((3 * h + 2) ^ key) << 4, spos = ((6 ^ key) << 4) + 2 * h;
 
     auto run = [&](auto ni_c) {
         constexpr int NI = decltype(ni_c)::value;
@@ -378,7 +367,6 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
             if constexpr (NI > 0) {
                 const uint8_t *Ap = f6_lds + st * F6_STAGE;
                 const uint8_t *Bq = Ap + F6_A_BYTES;
-                const uint8_t *Ss = Bq + F6_W_BYTES;
                 i32x8 bv[2];
                 int sb[2];
 #pragma unroll
@@ -392,8 +380,10 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                 int sa1[NI > 0 ? NI : 1], sa2[NI > 0 ? NI : 1];
 #pragma unroll
                 for (int i = 0; i < NI; i++) {
-                    const int row = 64 * q + 32 * i + l32;
-                    const uint8_t *ar = Ap + row * F6_ROW;
+                    const uint8_t *ar = Ap + (64 * q + 32 * i + l32) * F6_ROW;
+                    // plane 1 is dwords 0-5 of the lane's 48 bytes, plane 2
+                    // dwords 6-11 (the instruction reads 6 registers of a
+                    // 6-bit operand; lanes 6-7 are ignored)
                     const u32x4 c0 = *(const u32x4 *)(ar + apos0);
                     const u32x4 c1 = *(const u32x4 *)(ar + apos1);
                     const u32x4 c2 = *(const u32x4 *)(ar + apos2);
@@ -401,7 +391,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                                   (int)c1[0], (int)c1[1], 0, 0};
                     a2[i] = i32x8{(int)c1[2], (int)c1[3], (int)c2[0], (int)c2[1],
                                   (int)c2[2], (int)c2[3], 0, 0};
-                    const uint32_t s2 = *(const uint16_t *)(Ss + row * 4 + 2 * h);
+                    const uint32_t s2 = *(const uint16_t *)(ar + spos);
                     sa1[i] = (int)(s2 & 0xffu);
                     sa2[i] = (int)(s2 >> 8);
                 }
@@ -421,14 +411,12 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
             }
         };
 
-        // loads of one step issued by this wave: the plane chunk(s), the
-        // codes or a second plane chunk, and (waves 0-3) the scales
         for (int kt = 0; kt < nk; kt++) {
-            // this wave's loads of step kt are done (those of kt + 1 may
-            // still be in flight); the barrier publishes every wave's and ends
-            // the reads of step kt - 1
+            // this wave's loads of step kt are done (those of kt + 1 -- 3 or 2
+            // instructions -- may still be in flight); the barrier publishes
+            // every wave's and ends the reads of step kt - 1
             if (kt + 1 < nk) {
-                if (sload)
+                if (wload)
                     asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -471,9 +459,9 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
 }
 
 template <int ACT, typename OutT, bool PACKED>
-static hipError_t launch_f6(const uint8_t *ad, const uint8_t *as, int64_t ldb,
-                            const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
-                            const uint8_t *w2c, const uint8_t *w2s, const int32_t *plan,
+static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+                            const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                            const uint8_t *w2s, const int32_t *plan,
                             int max_groups, int hdr, int N, int K, OutT *out, int64_t ldo,
                             hipStream_t s)
 {
@@ -486,33 +474,35 @@ static hipError_t launch_f6(const uint8_t *ad, const uint8_t *as, int64_t ldb,
     auto kern = gemm_fp6x2_w16_kernel<ACT, OutT, PACKED>;
     const hipError_t err = ensure_dynamic_lds((const void *)kern, f6_lds_bytes(K));
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(F6_THREADS), f6_lds_bytes(K), s, ad, as, ldb,
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(F6_THREADS), f6_lds_bytes(K), s, ad, lda,
                        a_rows, w1c, w1s, w2c, w2s, plan, hdr, N, K, out, ldo);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, const uint8_t *as, int64_t ldb,
-                                 const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
-                                 const uint8_t *w2c, const uint8_t *w2s, int num_local,
+hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+                                 const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                                 const uint8_t *w2s, int num_local,
                                  int max_rows, int N, int K, int act, void *out, int out_f32,
                                  int64_t ldo, const void *plan_ws, int packed, hipStream_t s)
 {
     if (K % 128 != 0 || K > F6_MAX_K) return hipErrorInvalidValue;
     const GemmPlanArgs pa = gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, nullptr);
     const int32_t *plan = (const int32_t *)plan_ws;
-#define F6_ACT(OT, PK)                                                                            \
-    switch (act) {                                                                                \
-    case ACT_NONE:                                                                                \
-        return launch_f6<ACT_NONE, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, plan,         \
-                                           pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);               \
-    case ACT_SILU_MUL:                                                                            \
-        return launch_f6<ACT_SILU_MUL, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, plan,     \
-                                               pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);           \
-    case ACT_GELU_TANH_MUL:                                                                       \
-        return launch_f6<ACT_GELU_TANH_MUL, OT, PK>(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s,      \
-                                                    plan, pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s); \
-    default:                                                                                      \
-        return hipErrorInvalidValue;                                                              \
+#define F6_ACT(OT, PK)                                                                         \
+    switch (act) {                                                                             \
+    case ACT_NONE:                                                                             \
+        return launch_f6<ACT_NONE, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan,         \
+                                           pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);    \
+    case ACT_SILU_MUL:                                                                         \
+        return launch_f6<ACT_SILU_MUL, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan,     \
+                                               pa.max_groups, pa.hdr, N, K, (OT *)out, ldo,    \
+                                               s);                                             \
+    case ACT_GELU_TANH_MUL:                                                                    \
+        return launch_f6<ACT_GELU_TANH_MUL, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, \
+                                                    pa.max_groups, pa.hdr, N, K, (OT *)out,    \
+                                                    ldo, s);                                   \
+    default:                                                                                   \
+        return hipErrorInvalidValue;                                                           \
     }
     if (out_f32) {
         if (packed) F6_ACT(float, true)
@@ -523,9 +513,9 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, const uint8_t *as, int64_t l
 #undef F6_ACT
 }
 
-hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, const uint8_t *as, int64_t ldb,
-                                     const int32_t *a_rows, const uint8_t *w1c,
-                                     const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
+hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+                                     const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                                     const uint8_t *w2s,
                                      const int32_t *off, int num_local, int max_rows, int N,
                                      int K, int act, void *out, int out_f32, int64_t ldo,
                                      void *ws, int packed, hipStream_t s)
@@ -533,7 +523,7 @@ hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, const uint8_t *as, int64
     hipError_t e = launch_gemm_plan_into(
         off, num_local, gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws), s);
     if (e != hipSuccess) return e;
-    return launch_gemm_fp6x2_run(ad, as, ldb, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
+    return launch_gemm_fp6x2_run(ad, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
                                  K, act, out, out_f32, ldo, ws, packed, s);
 }
 

@@ -143,24 +143,23 @@ hipError_t launch_grouped_gemm_mx8(const uint8_t *ac, const uint8_t *as, int64_t
 
 // fp6x2.hip: activations as two MXFP6 (E2M3) planes against MXFP4 weights on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (6-bit x 4-bit rate). A split row of K
-// elements: data [K/32][48] bytes (plane 1, plane 2 codes of each block),
-// scales [K/32][2]; ldb = row stride in 32-element blocks.
+// elements is 2 K bytes: one 128-byte record (both blocks' planes and scales)
+// per 64 elements; lda = the row stride in elements (2 lda bytes).
 hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, int K,
-                              uint8_t *data, uint8_t *scales, hipStream_t s,
+                              uint8_t *out, int64_t ldo, hipStream_t s,
                               const int32_t *n_dev = nullptr);
 // The 256-row tile from a 256-row work plan (MOE_SCHED_TILE256) already built
 // in plan_ws; K % 128 == 0, K <= 4096 (hipErrorInvalidValue otherwise)
-hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, const uint8_t *as, int64_t ldb,
-                                 const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
-                                 const uint8_t *w2c, const uint8_t *w2s, int num_local,
-                                 int max_rows, int N, int K, int act, void *out, int out_f32,
-                                 int64_t ldo, const void *plan_ws, int packed, hipStream_t s);
-hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, const uint8_t *as, int64_t ldb,
-                                     const int32_t *a_rows, const uint8_t *w1c,
-                                     const uint8_t *w1s, const uint8_t *w2c, const uint8_t *w2s,
-                                     const int32_t *off, int num_local, int max_rows, int N,
-                                     int K, int act, void *out, int out_f32, int64_t ldo,
-                                     void *ws, int packed, hipStream_t s);
+hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+                                 const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                                 const uint8_t *w2s, int num_local, int max_rows, int N, int K,
+                                 int act, void *out, int out_f32, int64_t ldo,
+                                 const void *plan_ws, int packed, hipStream_t s);
+hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+                                     const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
+                                     const uint8_t *w2s, const int32_t *off, int num_local,
+                                     int max_rows, int N, int K, int act, void *out, int out_f32,
+                                     int64_t ldo, void *ws, int packed, hipStream_t s);
 
 // lora.hip: the low-rank increment on a frozen projection (y += t B_e^T with
 // t = scale x A_e^T, rows grouped by expert); t is [max_rows][rank] fp32

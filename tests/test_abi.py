@@ -223,36 +223,38 @@ def test_mx8_validation():
 def test_fp6x2_validation():
     L = m.lib
     sp = L.moe_fp6x2_split
-    assert sp(FAKE, m.DT_BF16, 256, 0, 256, FAKE, FAKE, None) == 0  # no rows: a no-op
-    assert sp(FAKE, 2, 256, 4, 256, FAKE, FAKE, None) == 1          # not bf16 / fp32
-    assert sp(FAKE, m.DT_BF16, 256, 4, 250, FAKE, FAKE, None) == 2  # K % 32
-    assert sp(FAKE, m.DT_BF16, 128, 4, 256, FAKE, FAKE, None) == 1  # ldv < K
-    assert sp(FAKE, m.DT_BF16, 256, 4, 256, None, FAKE, None) == 1
-    assert sp(C.c_void_p(0x10001), m.DT_BF16, 256, 4, 256, FAKE, FAKE, None) == 1  # misaligned
+    A128 = C.c_void_p(0x10000)
+    assert sp(FAKE, m.DT_BF16, 256, 0, 256, A128, 256, None) == 0  # no rows: a no-op
+    assert sp(FAKE, 2, 256, 4, 256, A128, 256, None) == 1          # not bf16 / fp32
+    assert sp(FAKE, m.DT_BF16, 256, 4, 224, A128, 256, None) == 2  # K % 64
+    assert sp(FAKE, m.DT_BF16, 128, 4, 256, A128, 256, None) == 1  # ldv < K
+    assert sp(FAKE, m.DT_BF16, 256, 4, 256, A128, 288, None) == 1  # ldo % 64
+    assert sp(FAKE, m.DT_BF16, 256, 4, 256, None, 256, None) == 1
+    assert sp(FAKE, m.DT_BF16, 256, 4, 256, C.c_void_p(0x10040), 256, None) == 1  # 64-byte out
     need = m.moe_grouped_gemm_fp6x2_workspace_size(8, 64)
     assert need > 0 and m.moe_grouped_gemm_fp6x2_workspace_size(0, 64) == 0
 
     def gemm(**kw):
-        a = dict(ad=FAKE, asc=FAKE, ldb=8, rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE,
+        a = dict(a=A128, lda=256, rows=None, w1c=FAKE, w1s=FAKE, w2c=FAKE, w2s=FAKE,
                  off=FAKE, nl=8, maxr=64, N=128, K=256, bs=32, lay=0, act=1, out=FAKE, odt=0,
                  ldo=128, ws=FAKE, wsb=need)
         a.update(kw)
         return L.moe_grouped_gemm_fp6x2(*a.values(), None)
-    assert gemm(ad=None) == 1
-    assert gemm(ldb=6) == 1                   # row stride below K / 32
-    assert gemm(ldb=10) == 1                  # row stride not a multiple of 4 blocks
-    assert gemm(asc=None) == 1
-    assert gemm(K=8192, ldb=256) == 2         # beyond the tile's 4096
-    assert gemm(K=320, ldb=12) == 2           # K % 128
+    assert gemm(a=None) == 1
+    assert gemm(lda=192) == 1                 # row stride below K
+    assert gemm(lda=288) == 1                 # row stride not a multiple of 64
+    assert gemm(a=C.c_void_p(0x10040)) == 1   # records 128-byte aligned
+    assert gemm(K=8192, lda=8192) == 2        # beyond the tile's 4096
+    assert gemm(K=320, lda=320) == 2          # K % 128
     assert gemm(wsb=need - 1) == 3
     assert gemm(act=0) == 1                   # ACT_NONE takes no second weight
     assert gemm(maxr=0) == 0
-    # the layer: FP6X2 adds the tokens' planes (T * d / 32 * 50 bytes) where
-    # its schedule resolves to 256-row tiles, nothing where it streams
+    # the layer: FP6X2 adds the tokens' planes (T * d * 2 bytes) where its
+    # schedule resolves to 256-row tiles, nothing where it streams
     big = dict(T=8192, d=3584, E=896, k=16, I=1024)
     n6 = m.moe_layer_workspace_size(m.layer_params(**big, precision=m.PREC_FP6X2))
     nb = m.moe_layer_workspace_size(m.layer_params(**big))
-    assert n6 >= nb + 8192 * 112 * 50
+    assert n6 >= nb + 8192 * 3584 * 2
     small = dict(T=64, d=3584, E=896, k=16, I=1024)
     assert (m.moe_layer_workspace_size(m.layer_params(**small, precision=m.PREC_FP6X2)) ==
             m.moe_layer_workspace_size(m.layer_params(**small)))

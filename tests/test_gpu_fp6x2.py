@@ -31,33 +31,34 @@ def m():
     return mod
 
 
-def unpack_planes(data):
-    """[N, nb, 48] bytes as written by moe_fp6x2_split -> codes [2, N, nb * 32]:
-    per block, plane p's 24 bytes hold code i at bits 6 i .. 6 i + 5
-    (little-endian)."""
-    N, nb, _ = data.shape
-    planes = data.reshape(N, nb, 2, 24).transpose(2, 0, 1, 3)
-    bits = np.unpackbits(planes, axis=-1, bitorder="little").reshape(2, N, nb, 32, 6)
-    codes = (bits * (1 << np.arange(6))).sum(-1).astype(np.uint8)
-    return codes.reshape(2, N, nb * 32)
-
-
-def split_scales(scales):
-    """[N, nb, 2] -> [2, N, nb]."""
-    return np.ascontiguousarray(scales.transpose(2, 0, 1))
+def unpack_split(rec):
+    """[N, 2 K] bytes as written by moe_fp6x2_split -> codes [2, N, K] and
+    scales [2, N, K/32]. Per 128-byte record s: blocks 2s and 2s+1 at bytes
+    0 and 48 (plane 1, then plane 2, 24 bytes each, code i at bits
+    6i..6i+5, little-endian), the four scale codes at bytes 96..99 ((2s, 1),
+    (2s, 2), (2s+1, 1), (2s+1, 2)), zeros after."""
+    N, K2 = rec.shape
+    r = rec.reshape(N, K2 // 128, 128)
+    assert not r[:, :, 100:].any()
+    blocks = r[:, :, :96].reshape(N, -1, 2, 2, 24)        # [N, s, block, plane, 24]
+    bits = np.unpackbits(blocks, axis=-1, bitorder="little").reshape(N, -1, 2, 2, 32, 6)
+    codes = (bits * (1 << np.arange(6))).sum(-1).astype(np.uint8)  # [N, s, block, plane, 32]
+    codes = codes.transpose(3, 0, 1, 2, 4).reshape(2, N, -1)
+    sc = r[:, :, 96:100].reshape(N, -1, 2, 2).transpose(3, 0, 1, 2).reshape(2, N, -1)
+    return codes, np.ascontiguousarray(sc)
 
 
 def _check_split(m, v_dev, v_host):
-    data, scales = m.moe_fp6x2_split(v_dev)
+    rec = m.moe_fp6x2_split(v_dev)
     torch.cuda.synchronize()
     rc, rs = oracle.fp6x2_split(v_host)
-    assert np.array_equal(split_scales(np_(scales)), rs)
-    got = unpack_planes(np_(data))
-    assert np.array_equal(got, rc), np.argwhere(got != rc)[:5]
+    codes, scales = unpack_split(np_(rec))
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc), np.argwhere(codes != rc)[:5]
 
 
 # ---------------------------------------------------------------- the split
-@pytest.mark.parametrize("K", [32, 128, 3584])
+@pytest.mark.parametrize("K", [64, 128, 3584])
 def test_fp6x2_split_fp32_bitexact(m, K):
     """Ties of the E2M3 grid and either side of them, the 7.5 clamp, zero
     blocks, a negative value rounding to zero, fp32 subnormals and the fp32
@@ -84,13 +85,13 @@ def test_fp6x2_split_grid_stride(m):
     N, K = 140000, 1024
     g = torch.Generator(device=DEV).manual_seed(7)
     v = (torch.randn(N, K, generator=g, device=DEV) * 2.0).to(torch.bfloat16)
-    data, scales = m.moe_fp6x2_split(v)
+    rec = m.moe_fp6x2_split(v)
     torch.cuda.synchronize()
     wrap = 16384 * 256 // (K // 32)
     rows = np.r_[0:4, wrap - 4:wrap + 4, N - 4:N]
     rc, rs = oracle.fp6x2_split(v[torch.from_numpy(rows).to(DEV)].float().cpu().numpy())
-    assert np.array_equal(split_scales(np_(scales)[rows]), rs)
-    assert np.array_equal(unpack_planes(np_(data)[rows]), rc)
+    codes, scales = unpack_split(np_(rec)[rows])
+    assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
 
 
 # ---------------------------------------------------------------- projection
@@ -109,9 +110,9 @@ def _split_rows(m, rng, R, K):
     oracle's split of the same rows carries (fp64)."""
     v = (rng.standard_normal((R, K)) * np.exp2(rng.integers(-3, 4, (R, 1)))).astype(np.float32)
     vb = torch.from_numpy(v).to(torch.bfloat16)
-    data, scales = m.moe_fp6x2_split(vb.to(DEV))
+    rec = m.moe_fp6x2_split(vb.to(DEV))
     rc, rs = oracle.fp6x2_split(vb.float().numpy())
-    return data, scales, oracle.fp6x2_value(rc, rs), vb.float().numpy().astype(np.float64)
+    return rec, oracle.fp6x2_value(rc, rs), vb.float().numpy().astype(np.float64)
 
 
 @pytest.mark.parametrize("act", [0, 1])
@@ -126,7 +127,7 @@ def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
     counts = np.array([37, 0, 513, 1, 257, 150], np.int32)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     A = int(off[-1])
-    xd, xs, xval, xb = _split_rows(m, rng, T, K)
+    xd, xval, xb = _split_rows(m, rng, T, K)
     a_rows = rng.integers(0, T, size=A).astype(np.int32)
     w1c, w1s = _experts(nl, N, K, 3)
     w2c, w2s = _experts(nl, N, K, 4) if act else (None, None)
@@ -136,7 +137,7 @@ def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
     g2c, g2s = pk(w2c, w2s) if act else (None, None)
     out = torch.full((A + 3, N), 7.0, dtype=torch.float32, device=DEV)
     ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
-    m.moe_grouped_gemm_fp6x2(xd, xs, torch.from_numpy(a_rows).to(DEV), g1c, g1s, g2c, g2s,
+    m.moe_grouped_gemm_fp6x2(xd, torch.from_numpy(a_rows).to(DEV), g1c, g1s, g2c, g2s,
                              torch.from_numpy(off).to(DEV), A, act, out, ws,
                              w_layout=m.LAYOUT_PACKED if packed else m.LAYOUT_OCP)
     torch.cuda.synchronize()
@@ -174,11 +175,11 @@ def test_grouped_gemm_fp6x2_bf16_out_and_direct_rows(m):
     counts = np.array([200, 3, 70], np.int32)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     A = int(off[-1])
-    hd, hs, hval, _ = _split_rows(m, rng, A, K)
+    hd, hval, _ = _split_rows(m, rng, A, K)
     wc, wsc = _experts(nl, N, K, 8)
     out = torch.empty(A, N, dtype=torch.bfloat16, device=DEV)
     ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
-    m.moe_grouped_gemm_fp6x2(hd, hs, None, wc.to(DEV), wsc.to(DEV), None, None,
+    m.moe_grouped_gemm_fp6x2(hd, None, wc.to(DEV), wsc.to(DEV), None, None,
                              torch.from_numpy(off).to(DEV), A, 0, out, ws)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
