@@ -383,9 +383,11 @@ typedef struct {
                          activations), MOE_PREC_MX8 (tokens and h rounded to
                          MXFP8 before each projection; `mode` as in
                          moe_grouped_gemm_mx8) or MOE_PREC_FP6X2 (where the
-                         schedule resolves to 256-row tiles and d <= 4096, the
-                         gate/up projection takes the tokens as two MXFP6
-                         planes, moe_grouped_gemm_fp6x2; otherwise as bf16) */
+                         schedule resolves to 256-row tiles and d, I <= 4096,
+                         both projections take their activations -- the
+                         tokens, and h as the bf16 path rounds it -- as two
+                         MXFP6 planes, moe_grouped_gemm_fp6x2; otherwise the
+                         bf16 path) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

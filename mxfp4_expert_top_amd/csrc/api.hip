@@ -108,7 +108,7 @@ int check_ws(const void *ws, size_t ws_bytes, size_t need)
 struct LayerWs {
     size_t logits, planes, wsplit, idx, w, off, perm, inv, pws, gws, h, y, total;
     size_t xq, xs, hq, hs;  // MX8 mode: MXFP8 tokens and h (codes, scales)
-    size_t xf;              // FP6X2 gate/up: the tokens' two MXFP6 planes
+    size_t xf, hf;          // FP6X2: the tokens' and h's two MXFP6 planes
     bool f6;                // the FP6X2 gate/up projection runs
     int splits;
     int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
@@ -123,9 +123,9 @@ static int router_kind(int T, int d)
 
 // The FP6X2 precision takes the 256-row tiles only (below their mean of rows
 // per expert the bf16 schedules keep the weight stream, which bounds them).
-static bool fp6x2_gate_up(const moe_layer_params *p)
+static bool fp6x2_layer(const moe_layer_params *p)
 {
-    return p->precision == MOE_PREC_FP6X2 && p->d <= 4096 &&
+    return p->precision == MOE_PREC_FP6X2 && p->d <= 4096 && p->I <= 4096 &&
            resolve_mode(p->mode, p->num_local, p->T * p->k) == MOE_SCHED_TILE256;
 }
 
@@ -155,9 +155,10 @@ LayerWs layer_ws(const moe_layer_params *p)
     // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
     // from there to MXFP8 (hq, hs)
     L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
-    L.f6 = fp6x2_gate_up(p);
+    L.f6 = fp6x2_layer(p);
     if (L.f6) {
         L.xf = o;  o += round_up(T * (size_t)p->d * 2);
+        L.hf = o;  o += round_up(A * (size_t)p->I * 2);
     }
     if (mx8) {
         L.xq = o; o += round_up(T * (size_t)p->d);
@@ -603,9 +604,20 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
                                 p->mode, base + L.gws, packed, s));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
-    HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
-                            p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
-                            base + L.gws, packed, s));
+    if (L.f6) {
+        // h as two MXFP6 planes (only the off[num_local] rows it holds), then
+        // the block-scaled down projection
+        uint8_t *hf = (uint8_t *)(base + L.hf);
+        HIP_TRY(launch_fp6x2_split(h, 0, p->I, A, p->I, hf, 2 * (int64_t)p->I, s,
+                                   off + p->num_local));
+        HIP_TRY(launch_gemm_fp6x2_run(hf, p->I, nullptr, down_codes, down_scales, nullptr,
+                                      nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1,
+                                      p->d, base + L.gws, packed, s));
+    } else {
+        HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
+                                p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
+                                base + L.gws, packed, s));
+    }
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));
     HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
                            p->out_dtype == MOE_DT_F32, p->d, s));

@@ -87,8 +87,20 @@ __device__ __forceinline__ int mxfp6_scale(float amax, float &inv)
     return s;
 }
 
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+typedef int i32x6 __attribute__((ext_vector_type(6)));
+
 // One plane of one block: the codes of v (32 values), packed 6 bits each into
 // w[0..5], and v replaced by its residual v - decode (exact in fp32).
+//
+// Blocks with a normal scale (s > 0) use the gfx950 scaled conversions:
+// v_cvt_scalef32_2xpk16_fp6_f32 rounds x / X to nearest-even E2M3 with
+// magnitudes beyond 7.5 saturating to 7.5 and the sign kept on zeros (output
+// element 2 i from its first operand's element i, 2 i + 1 from the second's),
+// and v_cvt_scalef32_pk32_f32_fp6 decodes code * X; a one-wave probe matched
+// both to the rounding above on grid values, ties, near-ties, the clamp
+// region and signed zeros. Blocks whose scale is the fp32 subnormal 2^-127
+// (amax below 2^-125) and all-zero blocks take the element-wise path.
 __device__ __forceinline__ uint32_t mxfp6_plane(float v[32], uint32_t w[6])
 {
     float amax = 0.0f;
@@ -96,6 +108,22 @@ __device__ __forceinline__ uint32_t mxfp6_plane(float v[32], uint32_t w[6])
     for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(v[j]));
     float inv;
     const int s = mxfp6_scale(amax, inv);
+    if (s > 0 && amax != 0.0f) {
+        const float X = __uint_as_float((uint32_t)s << 23);
+        f32x16 ev, od;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            ev[i] = v[2 * i];
+            od[i] = v[2 * i + 1];
+        }
+        const i32x6 c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, X);
+        const f32x32 d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, X);
+#pragma unroll
+        for (int j = 0; j < 6; j++) w[j] = (uint32_t)c[j];
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] -= d[j];
+        return (uint32_t)s;
+    }
     // 2^(s - 127), an fp32 subnormal for s = 0
     const float X = s ? __uint_as_float((uint32_t)s << 23) : __uint_as_float(0x00400000u);
 #pragma unroll

@@ -249,12 +249,13 @@ def test_fp6x2_validation():
     assert gemm(wsb=need - 1) == 3
     assert gemm(act=0) == 1                   # ACT_NONE takes no second weight
     assert gemm(maxr=0) == 0
-    # the layer: FP6X2 adds the tokens' planes (T * d * 2 bytes) where its
-    # schedule resolves to 256-row tiles, nothing where it streams
+    # the layer: FP6X2 adds the tokens' and h's planes (2 T d + 2 T k I
+    # bytes) where its schedule resolves to 256-row tiles, nothing where it
+    # streams
     big = dict(T=8192, d=3584, E=896, k=16, I=1024)
     n6 = m.moe_layer_workspace_size(m.layer_params(**big, precision=m.PREC_FP6X2))
     nb = m.moe_layer_workspace_size(m.layer_params(**big))
-    assert n6 >= nb + 8192 * 3584 * 2
+    assert n6 >= nb + 8192 * 3584 * 2 + 8192 * 16 * 1024 * 2
     small = dict(T=64, d=3584, E=896, k=16, I=1024)
     assert (m.moe_layer_workspace_size(m.layer_params(**small, precision=m.PREC_FP6X2)) ==
             m.moe_layer_workspace_size(m.layer_params(**small)))
