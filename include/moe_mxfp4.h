@@ -66,7 +66,12 @@ enum moe_status {
     MOE_ERR_HIP = 4          /* a HIP runtime call or launch failed              */
 };
 
-enum moe_dtype { MOE_DT_BF16 = 0, MOE_DT_F32 = 1, MOE_DT_MXFP8 = 2 /* moe_grouped_gemm_mx8 output only */ };
+enum moe_dtype {
+    MOE_DT_BF16 = 0,
+    MOE_DT_F32 = 1,
+    MOE_DT_MXFP8 = 2, /* moe_grouped_gemm_mx8 output only */
+    MOE_DT_FP6X2 = 3  /* moe_grouped_gemm_fp6x2 output only: split records */
+};
 
 /* Elementwise stage between the two expert projections. P1 (section 一)
  * names a K3-specific activation path without defining it, so the stage is
@@ -331,7 +336,10 @@ int moe_fp6x2_split(const void *v, int v_dtype, int64_t ldv, int64_t N, int K, u
  * with split rows as moe_fp6x2_split writes them (row r at a + 2 r lda
  * bytes; lda in elements), on v_mfma_scale_f32_32x32x64_f8f6f4 (exact
  * products; each 64-long partial sum formed inside the instruction, one per
- * plane, then accumulated in fp32); out as in moe_grouped_gemm_mxfp4.
+ * plane, then accumulated in fp32); out as in moe_grouped_gemm_mxfp4, or with
+ * out_dtype MOE_DT_FP6X2 (act != NONE) the fp32 results written as
+ * moe_fp6x2_split writes a row of N elements (row r at out + 2 r ldo bytes;
+ * ldo % 64 == 0, 128-byte aligned out): the next projection's input.
  * Schedule: 256-row tiles (no mode argument). ws holds
  * moe_grouped_gemm_fp6x2_workspace_size(...) bytes. Requirements: lda >= K,
  * lda % 64 == 0, 128-byte aligned a, ldo >= N, ldo % 8 == 0, 16-byte aligned
@@ -385,9 +393,9 @@ typedef struct {
                          moe_grouped_gemm_mx8) or MOE_PREC_FP6X2 (where the
                          schedule resolves to 256-row tiles and d, I <= 4096,
                          both projections take their activations -- the
-                         tokens, and h as the bf16 path rounds it -- as two
-                         MXFP6 planes, moe_grouped_gemm_fp6x2; otherwise the
-                         bf16 path) */
+                         tokens, and h from its fp32 value -- as two MXFP6
+                         planes, moe_grouped_gemm_fp6x2; otherwise the bf16
+                         path) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

@@ -18,7 +18,7 @@ import torch
 _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mxfp4.so"
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-DT_BF16, DT_F32, DT_MXFP8 = 0, 1, 2
+DT_BF16, DT_F32, DT_MXFP8, DT_FP6X2 = 0, 1, 2, 3
 ACT_NONE, ACT_SILU_MUL, ACT_GELU_TANH_MUL = 0, 1, 2
 MODE_AUTO, MODE_STREAM, MODE_TILED, MODE_TILE128, MODE_TILE256 = 0, 1, 2, 3, 4
 LAYOUT_OCP, LAYOUT_PACKED = 0, 1
@@ -435,7 +435,8 @@ def moe_grouped_gemm_fp6x2(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
                            stream=None):
     """moe_grouped_gemm_mxfp4 with rows as two MXFP6 planes (``a`` uint8
     [rows, 2 K] as moe_fp6x2_split writes it) on the block-scaled matrix
-    cores, 256-row tiles."""
+    cores, 256-row tiles. ``out`` is bf16 or fp32 [>= max_rows, N], or uint8
+    [>= max_rows, 2 N]: the results as split records (GLU acts only)."""
     num_local = expert_offsets.shape[0] - 1
     N, K = w1_codes.shape[1], w1_codes.shape[2] * 2
     _dev(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets, out, ws)
@@ -446,8 +447,9 @@ def moe_grouped_gemm_fp6x2(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
     if w2_codes is not None:
         _want(w2_codes, torch.uint8, (num_local, N, K // 2), "w2_codes")
         _want(w2_scales, torch.uint8, scale_shape(num_local, N, K, w_layout), "w2_scales")
-    if out.dim() != 2 or out.shape[1] != N or out.shape[0] < max_rows:
-        raise ValueError("out must be [>= max_rows, N]")
+    rec = out.dtype == torch.uint8
+    if out.dim() != 2 or out.shape[1] != (2 * N if rec else N) or out.shape[0] < max_rows:
+        raise ValueError("out must be [>= max_rows, N] (uint8: [>= max_rows, 2 N])")
     if a_rows is not None:
         if a_rows.dtype != torch.int32 or a_rows.numel() < max_rows:
             raise ValueError("a_rows must be int32 with >= max_rows entries")
@@ -457,7 +459,7 @@ def moe_grouped_gemm_fp6x2(a, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
     st = lib.moe_grouped_gemm_fp6x2(
         _ptr(a), K, _ptr(a_rows), _ptr(w1_codes), _ptr(w1_scales), _ptr(w2_codes),
         _ptr(w2_scales), _ptr(expert_offsets), num_local, max_rows, N, K, MX_BLOCK, w_layout, act,
-        _ptr(out), _dt(out), N, _ptr(ws), nbytes, _stream(stream))
+        _ptr(out), DT_FP6X2 if rec else _dt(out), N, _ptr(ws), nbytes, _stream(stream))
     _check("moe_grouped_gemm_fp6x2", st)
 
 

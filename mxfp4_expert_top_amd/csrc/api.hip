@@ -361,19 +361,22 @@ int moe_grouped_gemm_fp6x2(const uint8_t *a, int64_t lda, const int32_t *a_rows,
                            int out_dtype, int64_t ldo, void *ws, size_t ws_bytes,
                            moe_stream_t stream)
 {
+    const bool rec = out_dtype == MOE_DT_FP6X2;
     int rc = check_gemm(a, lda, w1_codes, w1_scales, w2_codes, w2_scales, expert_offsets,
-                        num_local, max_rows, N, K, block_size, w_layout, act, out, out_dtype,
-                        ldo);
+                        num_local, max_rows, N, K, block_size, w_layout, act, out,
+                        rec ? MOE_DT_BF16 : out_dtype, ldo);
     if (rc) return rc;
     CHECK(K <= 4096, MOE_ERR_UNSUPPORTED);
+    CHECK(!(rec && act == MOE_ACT_NONE), MOE_ERR_UNSUPPORTED);
     if (max_rows == 0) return MOE_OK;
     CHECK(lda % 64 == 0 && aligned(a, 128), MOE_ERR_INVALID_ARG);
+    if (rec) CHECK(ldo % 64 == 0 && aligned(out, 128), MOE_ERR_INVALID_ARG);
     rc = check_ws(ws, ws_bytes, grouped_gemm_ws_bytes(num_local, max_rows, 0, MOE_SCHED_TILE256));
     if (rc) return rc;
+    const int kind = rec ? F6_OUT_RECORDS : out_dtype == MOE_DT_F32 ? F6_OUT_F32 : F6_OUT_BF16;
     HIP_TRY(launch_grouped_gemm_fp6x2(a, lda, a_rows, w1_codes, w1_scales, w2_codes, w2_scales,
-                                      expert_offsets, num_local, max_rows, N, K, act, out,
-                                      out_dtype == MOE_DT_F32, ldo, ws,
-                                      w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
+                                      expert_offsets, num_local, max_rows, N, K, act, out, kind,
+                                      ldo, ws, w_layout == MOE_LAYOUT_PACKED, as_stream(stream)));
     return MOE_OK;
 }
 
@@ -595,9 +598,11 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
         // the tokens as two MXFP6 planes, then the block-scaled projection
         uint8_t *xf = (uint8_t *)(base + L.xf);
         HIP_TRY(launch_fp6x2_split(x, 0, p->d, p->T, p->d, xf, 2 * (int64_t)p->d, s));
+        // h leaves the epilogue as split records (from fp32, no bf16 h)
         HIP_TRY(launch_gemm_fp6x2_run(xf, p->d, perm, gate_codes, gate_scales, up_codes,
-                                      up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
-                                      base + L.gws, packed, s));
+                                      up_scales, p->num_local, A, p->I, p->d, p->act,
+                                      base + L.hf, F6_OUT_RECORDS, p->I, base + L.gws, packed,
+                                      s));
     } else {
         HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
                                 up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
@@ -605,14 +610,10 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
     }
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
     if (L.f6) {
-        // h as two MXFP6 planes (only the off[num_local] rows it holds), then
-        // the block-scaled down projection
-        uint8_t *hf = (uint8_t *)(base + L.hf);
-        HIP_TRY(launch_fp6x2_split(h, 0, p->I, A, p->I, hf, 2 * (int64_t)p->I, s,
-                                   off + p->num_local));
-        HIP_TRY(launch_gemm_fp6x2_run(hf, p->I, nullptr, down_codes, down_scales, nullptr,
-                                      nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1,
-                                      p->d, base + L.gws, packed, s));
+        HIP_TRY(launch_gemm_fp6x2_run((const uint8_t *)(base + L.hf), p->I, nullptr,
+                                      down_codes, down_scales, nullptr, nullptr, p->num_local, A,
+                                      p->d, p->I, MOE_ACT_NONE, y, F6_OUT_F32, p->d,
+                                      base + L.gws, packed, s));
     } else {
         HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
                                 p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,

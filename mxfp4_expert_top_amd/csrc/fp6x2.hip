@@ -90,11 +90,34 @@ __device__ __forceinline__ int mxfp6_scale(float amax, float &inv)
 typedef float f32x32 __attribute__((ext_vector_type(32)));
 typedef int i32x6 __attribute__((ext_vector_type(6)));
 
+// The two scaled conversions, with their results in registers apart from
+// their operands (early clobber). The compiler's builtins may give the
+// 6-register result of v_cvt_scalef32_2xpk16_fp6_f32 registers that overlap
+// the tail of an operand; the instruction writes its first result dwords
+// before it reads the last operand registers, which then turned the last
+// elements' codes wrong (elements 29 and 31 when the result overlapped the
+// second operand's registers 14-15).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ i32x6 cvt_fp6_of(f32x16 ev, f32x16 od, float X)
+{
+    i32x6 r;
+    asm("v_cvt_scalef32_2xpk16_fp6_f32 %0, %1, %2, %3" : "=&v"(r) : "v"(ev), "v"(od), "v"(X));
+    return r;
+}
+__device__ __forceinline__ f32x32 cvt_f32_of(i32x6 c, float X)
+{
+    f32x32 d;
+    asm("v_cvt_scalef32_pk32_f32_fp6 %0, %1, %2" : "=&v"(d) : "v"(c), "v"(X));
+    return d;
+}
+#pragma clang diagnostic pop
+
 // One plane of one block: the codes of v (32 values), packed 6 bits each into
 // w[0..5], and v replaced by its residual v - decode (exact in fp32).
 //
-// Blocks with a normal scale (s > 0) use the gfx950 scaled conversions:
-// v_cvt_scalef32_2xpk16_fp6_f32 rounds x / X to nearest-even E2M3 with
+// Blocks with a normal scale (s > 0) use the gfx950 scaled conversions
+// (above): v_cvt_scalef32_2xpk16_fp6_f32 rounds x / X to nearest-even E2M3 with
 // magnitudes beyond 7.5 saturating to 7.5 and the sign kept on zeros (output
 // element 2 i from its first operand's element i, 2 i + 1 from the second's),
 // and v_cvt_scalef32_pk32_f32_fp6 decodes code * X; a one-wave probe matched
@@ -116,8 +139,8 @@ __device__ __forceinline__ uint32_t mxfp6_plane(float v[32], uint32_t w[6])
             ev[i] = v[2 * i];
             od[i] = v[2 * i + 1];
         }
-        const i32x6 c = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, X);
-        const f32x32 d = __builtin_amdgcn_cvt_scalef32_pk32_f32_fp6(c, X);
+        const i32x6 c = cvt_fp6_of(ev, od, X);
+        const f32x32 d = cvt_f32_of(c, X);
 #pragma unroll
         for (int j = 0; j < 6; j++) w[j] = (uint32_t)c[j];
 #pragma unroll
@@ -249,11 +272,22 @@ __host__ __device__ constexpr int f6_scale_row(int K)
     return (((K / 32 + 3) / 4) | 1) * 4;
 }
 
+// the epilogue's staging: per wave 64 rows of up to 256 bytes, padded by 16
+constexpr int F6_EPI_PITCH = 144, F6_EPI_BYTES = 16 * 64 * F6_EPI_PITCH;
+
 __host__ __device__ constexpr int f6_lds_bytes(int K)
 {
-    return F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K);
+    return F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K) > F6_EPI_BYTES
+               ? F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K)
+               : F6_EPI_BYTES;
 }
 static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
+
+// Output kinds of the projection: OutT = float or bf16 rows, or uint8_t for
+// split records (the next projection's input, written as moe_fp6x2_split
+// would write the fp32 results).
+template <typename OutT>
+constexpr bool f6_records = std::is_same<OutT, uint8_t>::value;
 
 template <int ACT, typename OutT, bool PACKED>
 __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
@@ -456,23 +490,85 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
             compute(st, kt);
         }
 
-        // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+        // Epilogue through LDS (the ring is idle once every wave is past its
+        // last step). Lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each
+        // 32 x 32 accumulator tile; a wave's output is rows 64 q .. + 63 of
+        // columns c0 .. c0 + COLS_W - 1.
+        __syncthreads();
+        constexpr int COLS_W = GLU ? 32 : 64;
+        const int c0 = n0 + COLS_W * slot;
+        const bool col_on = c0 < N;  // N is a multiple of 64
+        uint8_t *const stg = f6_lds + wave * (64 * F6_EPI_PITCH);
+        if constexpr (f6_records<OutT>) {
+            // (GLU only: a wave's 32 output columns are one MX block.) The
+            // fp32 results of the wave's 64 rows staged, 128 bytes per row;
+            // then lane r converts row r's block as the split does and
+            // writes it into the row's record
+            static_assert(GLU, "records are written by the GLU projection");
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
+            for (int i = 0; i < NI; i++)
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (rl >= mrows) continue;
-                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
-                if constexpr (GLU) {
-                    const int col = n0 + 32 * slot + l32;
-                    if (col < N)
-                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
-                } else {
+                for (int v = 0; v < 16; v++) {
+                    const int r = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                    ((float *)(stg + r * F6_EPI_PITCH))[l32] =
+                        act_apply<ACT>(acc[i][0][v], acc[i][1][v]);
+                }
+            {
+                const int r = lane, rl = 64 * q + r;
+                if (r < 32 * NI && rl < mrows && col_on) {
+                    float x[32];
 #pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const int col = n0 + 64 * slot + 32 * j + l32;
-                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
+                    for (int j = 0; j < 8; j++) {
+                        const f32x4 t = *(const f32x4 *)(stg + r * F6_EPI_PITCH + 16 * j);
+                        x[4 * j] = t[0]; x[4 * j + 1] = t[1]; x[4 * j + 2] = t[2]; x[4 * j + 3] = t[3];
+                    }
+                    uint32_t w[12];
+                    const uint32_t s1 = mxfp6_plane(x, w);
+                    const uint32_t s2 = mxfp6_plane(x, w + 6);
+                    const int b = c0 >> 5;
+                    uint8_t *rec = (uint8_t *)out + (int64_t)(r0 + rl) * 2 * ldo + (b >> 1) * 128;
+                    u32x4 *dst = (u32x4 *)(rec + (b & 1) * 48);
+                    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+                    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+                    dst[2] = u32x4{w[8], w[9], w[10], w[11]};
+                    *(uint16_t *)(rec + 96 + 2 * (b & 1)) = (uint16_t)(s1 | (s2 << 8));
+                    if (b & 1) {
+                        *(uint32_t *)(rec + 100) = 0u;
+                        *(uint2 *)(rec + 104) = make_uint2(0u, 0u);
+                        *(u32x4 *)(rec + 112) = u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+        } else {
+            // one 32-row tile at a time, stored as whole 16-byte row segments
+            constexpr int ROW_B = COLS_W * (int)sizeof(OutT);  // 64, 128 or 256 bytes
+            constexpr int PITCH = ROW_B + 16;
+            constexpr int LPR = ROW_B / 16, RPI = 64 / LPR;    // lanes per row, rows per store
+            static_assert(32 * PITCH <= 64 * F6_EPI_PITCH, "staging fits the wave's area");
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+                    OutT *row = (OutT *)(stg + r * PITCH);
+                    if constexpr (GLU) {
+                        store_out<OutT>(row + l32, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            store_out<OutT>(row + 32 * j + l32, acc[i][j][v]);
+                    }
+                }
+#pragma unroll
+                for (int it = 0; it < 32 / RPI; it++) {
+                    const int r = RPI * it + lane / LPR, seg = lane % LPR;
+                    const u32x4 val = *(const u32x4 *)(stg + r * PITCH + 16 * seg);
+                    const int rl = 64 * q + 32 * i + r;
+                    if (col_on && rl < mrows) {
+                        u32x4 *dst = (u32x4 *)((uint8_t *)(out + (int64_t)(r0 + rl) * ldo + c0) +
+                                               16 * seg);
+                        if constexpr (!GLU && sizeof(OutT) == 4) __builtin_nontemporal_store(val, dst);
+                        else *dst = val;
                     }
                 }
             }
@@ -509,50 +605,55 @@ static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_row
 
 hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                                 const uint8_t *w2s, int num_local,
-                                 int max_rows, int N, int K, int act, void *out, int out_f32,
-                                 int64_t ldo, const void *plan_ws, int packed, hipStream_t s)
+                                 const uint8_t *w2s, int num_local, int max_rows, int N, int K,
+                                 int act, void *out, int out_kind, int64_t ldo,
+                                 const void *plan_ws, int packed, hipStream_t s)
 {
     if (K % 128 != 0 || K > F6_MAX_K) return hipErrorInvalidValue;
+    if (out_kind == F6_OUT_RECORDS && act == ACT_NONE) return hipErrorInvalidValue;
     const GemmPlanArgs pa = gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, nullptr);
     const int32_t *plan = (const int32_t *)plan_ws;
-#define F6_ACT(OT, PK)                                                                         \
+#define F6_LAUNCH(A, OT, PK)                                                                   \
+    return launch_f6<A, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,      \
+                                pa.hdr, N, K, (OT *)out, ldo, s)
+#define F6_GLU(OT, PK)                                                                         \
     switch (act) {                                                                             \
-    case ACT_NONE:                                                                             \
-        return launch_f6<ACT_NONE, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan,         \
-                                           pa.max_groups, pa.hdr, N, K, (OT *)out, ldo, s);    \
-    case ACT_SILU_MUL:                                                                         \
-        return launch_f6<ACT_SILU_MUL, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan,     \
-                                               pa.max_groups, pa.hdr, N, K, (OT *)out, ldo,    \
-                                               s);                                             \
-    case ACT_GELU_TANH_MUL:                                                                    \
-        return launch_f6<ACT_GELU_TANH_MUL, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, \
-                                                    pa.max_groups, pa.hdr, N, K, (OT *)out,    \
-                                                    ldo, s);                                   \
-    default:                                                                                   \
-        return hipErrorInvalidValue;                                                           \
+    case ACT_SILU_MUL: F6_LAUNCH(ACT_SILU_MUL, OT, PK);                                       \
+    case ACT_GELU_TANH_MUL: F6_LAUNCH(ACT_GELU_TANH_MUL, OT, PK);                             \
+    default: return hipErrorInvalidValue;                                                      \
     }
-    if (out_f32) {
-        if (packed) F6_ACT(float, true)
-        F6_ACT(float, false)
+#define F6_ANY(OT, PK)                                                                         \
+    {                                                                                          \
+        if (act == ACT_NONE) F6_LAUNCH(ACT_NONE, OT, PK);                                      \
+        F6_GLU(OT, PK)                                                                         \
     }
-    if (packed) F6_ACT(bf16, true)
-    F6_ACT(bf16, false)
-#undef F6_ACT
+    if (out_kind == F6_OUT_RECORDS) {
+        if (packed) F6_GLU(uint8_t, true)
+        F6_GLU(uint8_t, false)
+    }
+    if (out_kind == F6_OUT_F32) {
+        if (packed) F6_ANY(float, true)
+        F6_ANY(float, false)
+    }
+    if (packed) F6_ANY(bf16, true)
+    F6_ANY(bf16, false)
+#undef F6_ANY
+#undef F6_GLU
+#undef F6_LAUNCH
 }
 
 hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                      const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
-                                     const uint8_t *w2s,
-                                     const int32_t *off, int num_local, int max_rows, int N,
-                                     int K, int act, void *out, int out_f32, int64_t ldo,
-                                     void *ws, int packed, hipStream_t s)
+                                     const uint8_t *w2s, const int32_t *off, int num_local,
+                                     int max_rows, int N, int K, int act, void *out,
+                                     int out_kind, int64_t ldo, void *ws, int packed,
+                                     hipStream_t s)
 {
     hipError_t e = launch_gemm_plan_into(
         off, num_local, gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws), s);
     if (e != hipSuccess) return e;
     return launch_gemm_fp6x2_run(ad, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
-                                 K, act, out, out_f32, ldo, ws, packed, s);
+                                 K, act, out, out_kind, ldo, ws, packed, s);
 }
 
 }  // namespace moe

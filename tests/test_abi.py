@@ -249,6 +249,10 @@ def test_fp6x2_validation():
     assert gemm(wsb=need - 1) == 3
     assert gemm(act=0) == 1                   # ACT_NONE takes no second weight
     assert gemm(maxr=0) == 0
+    assert gemm(odt=3, act=0, w2c=None, w2s=None) == 2  # records need a GLU act
+    assert gemm(odt=3, ldo=160) == 1          # record rows: ldo % 64
+    assert gemm(odt=3, out=C.c_void_p(0x10040)) == 1  # records 128-byte aligned
+    assert gemm(odt=4) == 1
     # the layer: FP6X2 adds the tokens' and h's planes (2 T d + 2 T k I
     # bytes) where its schedule resolves to 256-row tiles, nothing where it
     # streams

@@ -191,6 +191,40 @@ def test_grouped_gemm_fp6x2_bf16_out_and_direct_rows(m):
         assert (np.abs(got[r0:r1] - ref) <= 2.0 ** -8 * (np.abs(ref) + b) + b).all()
 
 
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("act", [1, 2])
+def test_grouped_gemm_fp6x2_record_output_bitexact(m, act, packed):
+    """Split-record output (the layer's h): byte for byte the oracle's split
+    of the fp32 output of the same launch configuration; rows past each
+    group's end untouched."""
+    rng = np.random.default_rng(30 + act + 2 * packed)
+    nl, N, K, T = 4, 320, 384, 500
+    counts = np.array([150, 0, 257, 40], np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    xd, _, _ = _split_rows(m, rng, T, K)
+    a_rows = torch.from_numpy(rng.integers(0, T, size=A).astype(np.int32)).to(DEV)
+    w1c, w1s = _experts(nl, N, K, 5)
+    w2c, w2s = _experts(nl, N, K, 6)
+    dev = lambda t: t.to(DEV)
+    pk = lambda c, s: m.moe_mxfp4_prepack(dev(c), dev(s)) if packed else (dev(c), dev(s))
+    g1c, g1s = pk(w1c, w1s)
+    g2c, g2s = pk(w2c, w2s)
+    lay = m.LAYOUT_PACKED if packed else m.LAYOUT_OCP
+    args = (xd, a_rows, g1c, g1s, g2c, g2s, torch.from_numpy(off).to(DEV), A, act)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
+    f32 = torch.empty(A, N, dtype=torch.float32, device=DEV)
+    m.moe_grouped_gemm_fp6x2(*args, f32, ws, w_layout=lay)
+    rec = torch.full((A + 2, 2 * N), 0xA5, dtype=torch.uint8, device=DEV)
+    m.moe_grouped_gemm_fp6x2(*args, rec, ws, w_layout=lay)
+    torch.cuda.synchronize()
+    rc, rs = oracle.fp6x2_split(np_(f32))
+    codes, scales = unpack_split(np_(rec)[:A])
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc), np.argwhere(codes != rc)[:5]
+    assert (np_(rec)[A:] == 0xA5).all()
+
+
 # ---------------------------------------------------------------- layer
 SMALL = [
     LayerConfig("f0", T=37, I=128, d=256, E=64, k=8),
@@ -204,10 +238,11 @@ SMALL = [
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 @pytest.mark.parametrize("packed", [False, True])
 def test_small_layer_fp6x2_vs_oracle(m, cfg, packed):
-    """The FP6X2 layer on 256-row tiles against the oracle's bf16-activation
-    layer on the GPU's scores, within the default contract; and against the
-    GPU's own bf16 layer (fp32 outputs), which it matches to the planes'
-    representation error."""
+    """The FP6X2 layer on 256-row tiles (tokens and h as two MXFP6 planes)
+    against the oracle's bf16-activation layer on the GPU's scores, within the
+    default contract; and no further from it than the GPU's bf16 layer (fp32
+    outputs), which rounds h to bf16 where the FP6X2 layer carries h from its
+    fp32 value."""
     inp = make_inputs(cfg).to(DEV)
     pw = m.prepack_weights(inp.weights) if packed else None
     g = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, packed=pw,
@@ -222,8 +257,10 @@ def test_small_layer_fp6x2_vs_oracle(m, cfg, packed):
     assert_close_layer(got, ref["out"], cfg.name)
     b = run_gpu_layer(inp, mode=m.MODE_TILE256, packed=pw, out_dtype=torch.float32)
     assert torch.equal(b["idx"], g["idx"])
-    assert rel_l2(got, np_(b["out"])) < 2e-3
-    assert not torch.equal(b["out"], g["out"])  # the FP6X2 projection ran
+    e6, e16 = rel_l2(got, ref["out"]), rel_l2(np_(b["out"]), ref["out"])
+    print(f"{cfg.name}: rel-L2 FP6X2 {e6:.3e}, bf16 {e16:.3e}")
+    assert e6 <= max(1.5 * e16, 1e-3)
+    assert not torch.equal(b["out"], g["out"])  # the FP6X2 projections ran
 
 
 def test_fp6x2_layer_determinism_bitwise(m):
