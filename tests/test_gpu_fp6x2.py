@@ -263,6 +263,25 @@ def test_small_layer_fp6x2_vs_oracle(m, cfg, packed):
     assert not torch.equal(b["out"], g["out"])  # the FP6X2 projections ran
 
 
+@pytest.mark.parametrize("cfg", [SMALL[4], LayerConfig("f5", T=3000, I=256, d=512, E=64, k=8,
+                                                       expert_begin=16, num_local=24,
+                                                       bias="normal")], ids=lambda c: c.name)
+def test_auto_schedule_takes_fp6x2(m, cfg):
+    """With the schedule left to the library and a mean of 128 or more rows
+    per local expert over the row bound, the FP6X2 layer takes its 256-row
+    tiles (bitwise the explicit choice), here also on a local expert range."""
+    inp = make_inputs(cfg).to(DEV)
+    a = run_gpu_layer(inp, precision=m.PREC_FP6X2, out_dtype=torch.float32)
+    b = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, out_dtype=torch.float32)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    lg = np_(a["logits"])
+    ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                       host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                       e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg)
+    assert_close_layer(np_(a["out"]), ref["out"], cfg.name)
+
+
 def test_fp6x2_layer_determinism_bitwise(m):
     inp = make_inputs(SMALL[4]).to(DEV)
     a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
