@@ -316,10 +316,10 @@ int moe_grouped_gemm_mx8(const uint8_t *a_codes, const uint8_t *a_scales, int64_
  * elements takes the 2 K bytes of a bf16 row), one 128-byte record per 64
  * elements (blocks 2s and 2s+1):
  *   bytes   0..47  block 2s: plane-1 codes (24 bytes), plane-2 codes (24)
- *   bytes  48..95  block 2s+1: the same
- *   bytes  96..99  scale codes (2s, plane 1), (2s, plane 2), (2s+1, plane 1),
- *                  (2s+1, plane 2)
- *   bytes 100..127 zero
+ *   bytes  48..51  scale codes (2s, plane 1), (2s, plane 2), (2s+1, plane 1),
+ *                  (2s+1, plane 2); bytes 52..63 three more copies of them
+ *   bytes  64..111 block 2s+1: plane-1 codes, plane-2 codes
+ *   bytes 112..127 zero
  * with code i of a plane at bits 6i..6i+5 of its 24 little-endian bytes.
  * Preconditions: finite v. Errors: K % 64 != 0 -> UNSUPPORTED; v_dtype not
  * bf16 or fp32, ldv < K, ldv % 8 != 0, ldo < K, ldo % 64 != 0, NULL or

@@ -407,9 +407,10 @@ def moe_grouped_gemm_mx8(a_codes, a_scales, a_rows, w1_codes, w1_scales, w2_code
 
 def moe_fp6x2_split(v, out=None, stream=None):
     """bf16 or fp32 [N, K] on the GPU -> the two MXFP6 planes as uint8
-    [N, 2 K]: one 128-byte record per 64 elements (per block: plane-1 codes,
-    plane-2 codes, 24 bytes each, code i at bits 6i..6i+5; then the four
-    scale codes at bytes 96..99 and zeros)."""
+    [N, 2 K]: one 128-byte record per 64 elements (the two blocks at bytes 0
+    and 64, each plane-1 codes then plane-2 codes, 24 bytes each, code i at
+    bits 6i..6i+5; the four scale codes at bytes 48..51, repeated at 52..63;
+    zeros at 112..127)."""
     if v.dtype not in (torch.bfloat16, torch.float32) or v.dim() != 2:
         raise TypeError("v must be a 2-D bf16 or fp32 tensor")
     N, K = v.shape

@@ -34,17 +34,20 @@ def m():
 def unpack_split(rec):
     """[N, 2 K] bytes as written by moe_fp6x2_split -> codes [2, N, K] and
     scales [2, N, K/32]. Per 128-byte record s: blocks 2s and 2s+1 at bytes
-    0 and 48 (plane 1, then plane 2, 24 bytes each, code i at bits
-    6i..6i+5, little-endian), the four scale codes at bytes 96..99 ((2s, 1),
-    (2s, 2), (2s+1, 1), (2s+1, 2)), zeros after."""
+    0 and 64 (plane 1, then plane 2, 24 bytes each, code i at bits
+    6i..6i+5, little-endian), the four scale codes at bytes 48..51 ((2s, 1),
+    (2s, 2), (2s+1, 1), (2s+1, 2)) and again at 52..55, 56..59, 60..63,
+    zeros at 112..127."""
     N, K2 = rec.shape
     r = rec.reshape(N, K2 // 128, 128)
-    assert not r[:, :, 100:].any()
-    blocks = r[:, :, :96].reshape(N, -1, 2, 2, 24)        # [N, s, block, plane, 24]
+    assert not r[:, :, 112:].any()
+    for c in (52, 56, 60):
+        assert np.array_equal(r[:, :, c:c + 4], r[:, :, 48:52])
+    blocks = np.stack([r[:, :, 0:48], r[:, :, 64:112]], axis=2).reshape(N, -1, 2, 2, 24)
     bits = np.unpackbits(blocks, axis=-1, bitorder="little").reshape(N, -1, 2, 2, 32, 6)
     codes = (bits * (1 << np.arange(6))).sum(-1).astype(np.uint8)  # [N, s, block, plane, 32]
     codes = codes.transpose(3, 0, 1, 2, 4).reshape(2, N, -1)
-    sc = r[:, :, 96:100].reshape(N, -1, 2, 2).transpose(3, 0, 1, 2).reshape(2, N, -1)
+    sc = r[:, :, 48:52].reshape(N, -1, 2, 2).transpose(3, 0, 1, 2).reshape(2, N, -1)
     return codes, np.ascontiguousarray(sc)
 
 
