@@ -350,8 +350,13 @@ def main():
     U = int((counts > 0).sum())
     lb, lf, gb, gf = algorithmic(cfg, A, U, out_bytes=4)
 
+    # The layer's FP6X2 rule: 256-row tiles when asked to, or from a mean of
+    # 128 rows per local expert over the row bound T k (else the bf16 path).
+    f6_layer = f6 and cfg.d <= 4096 and cfg.I <= 4096 and (
+        args.mode == m.MODE_TILE256 or (args.mode in (m.MODE_AUTO, m.MODE_TILED) and
+                                        cfg.T * cfg.k >= 128 * cfg.num_local))
     # The dominant kernel is the gate/up projection: weight streaming (HBM
-    # bound) for few rows per expert, a tiled bf16 GEMM (MFMA bound) otherwise.
+    # bound) for few rows per expert, a tiled GEMM (MFMA bound) otherwise.
     gu_s = stage_ms["gate_up"] / 1e3
     sched = m.moe_grouped_gemm_schedule(cfg.num_local, cfg.T * cfg.k, args.mode)
     if args.lora_rank > 0:
@@ -380,11 +385,7 @@ def main():
                 "unit": "TFLOP/s", "frac": round(gf / gu_s / 1e12 / FP8_PEAK_TFLOPS, 4),
                 "traffic": None, "algorithmic_flops_per_launch": int(gf),
                 "avg_launch_ms": round(stage_ms["gate_up"], 4)}
-    elif f6 and cfg.d <= 4096 and cfg.I <= 4096 and (
-            args.mode == m.MODE_TILE256 or (args.mode in (m.MODE_AUTO, m.MODE_TILED) and
-                                            cfg.T * cfg.k >= 128 * cfg.num_local)):
-        # (the layer's FP6X2 rule: 256-row tiles when asked to, or from a mean
-        # of 128 rows per local expert over the row bound T k)
+    elif f6_layer:
         # the block-scaled GEMM issues two 6-bit x 4-bit products (one per
         # plane) per product of the layer: the algorithmic flops priced at the
         # fp6 x fp4 peak (and, for reference, at the bf16 one)
@@ -430,13 +431,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8" if mx8 else "fp6x2+bf16" if f6 else "bf16",
+        "dtype": "mxfp8" if mx8 else "fp6x2" if f6_layer else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "experts_computed": cfg.num_local,
                    "weights": "mxfp4-e2m1-e8m0-b32" + ("-packed" if packed else ""),
                    "activations": "mxfp8-e4m3-e8m0-b32" if mx8 else
-                   "bf16 (gate/up: two mxfp6-e2m3-e8m0-b32 planes)" if f6 else "bf16",
+                   "bf16 tokens; both projections take tokens and h as two "
+                   "mxfp6-e2m3-e8m0-b32 planes" if f6_layer else "bf16",
                    "output": "fp32",
                    "lora_rank": args.lora_rank, "routing_bias": cfg.bias},
         "roofline": roof,
