@@ -264,8 +264,9 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // LDS: a three-stage ring filled by global_load_lds_dwordx4 (each stage:
 // 256 rows x 128 bytes of records, 256 weight rows x 32 code bytes), one
 // barrier per K step publishing step k and freeing the stage that step k + 2
-// overwrites; the tile's weight scales (256 x K / 32 bytes, rows padded to an
-// odd number of dwords) copied once. Chunk c (16 bytes) of a row's record
+// overwrites; the tile's weight scales (256 x K / 32 bytes) loaded once, in
+// the streaming layout's order (16 groups of 16 weight rows, each group as
+// the layout stores it), by the same DMA ahead of the first two stages. Chunk c (16 bytes) of a row's record
 // sits at position c ^ ((r / 2) % 8), so the 16 rows of a 16-lane read
 // cover all banks (the bf16 kernel's A arrangement); lanes 32-63 read the
 // other half of each record (block 1), whose positions differ from block 0's
@@ -280,9 +281,11 @@ constexpr int F6_STAGE = F6_A_BYTES + F6_W_BYTES;
 constexpr int F6_THREADS = 1024;
 constexpr int F6_MAX_K = 4096;
 
-__host__ __device__ constexpr int f6_scale_row(int K)
+// Weight scales of 16 weight rows in the streaming layout: K / 512 groups
+// (rounded up) of 256 bytes; the LDS copy of a tile holds 16 of them.
+__host__ __device__ constexpr int f6_scale_chunk(int K)
 {
-    return (((K / 32 + 3) / 4) | 1) * 4;
+    return 256 * ((K / 128 + 3) / 4);
 }
 
 // the epilogue's staging: per wave 64 rows of up to 256 bytes, padded by 16
@@ -290,8 +293,8 @@ constexpr int F6_EPI_PITCH = 144, F6_EPI_BYTES = 16 * 64 * F6_EPI_PITCH;
 
 __host__ __device__ constexpr int f6_lds_bytes(int K)
 {
-    return F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K) > F6_EPI_BYTES
-               ? F6_STAGES * F6_STAGE + F6_BN * f6_scale_row(K)
+    return F6_STAGES * F6_STAGE + 16 * f6_scale_chunk(K) > F6_EPI_BYTES
+               ? F6_STAGES * F6_STAGE + 16 * f6_scale_chunk(K)
                : F6_EPI_BYTES;
 }
 static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
@@ -313,8 +316,8 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? F6_BN / 2 : F6_BN;
     extern __shared__ __attribute__((aligned(16))) uint8_t f6_lds[];
-    const int srow = f6_scale_row(K);
-    uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [256][srow] weight scales
+    const int chunk_b = f6_scale_chunk(K);
+    uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [16][chunk_b] weight scales
 
     const int nblk = (N + COLS - 1) / COLS;
     const int total = plan[0] * nblk;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = wave & 3, q = wave >> 2;
-    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const int nch = K / 128;
     const int64_t row_b = 2 * lda;  // bytes per split row
 
     auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
@@ -386,35 +389,38 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     };
 
     const int nk = K / F6_BK;  // even: K is a multiple of 128
-    issue(0, 0);
-    issue(1, 1);
 
-    // ---- weight scales -> LDS, in K-block order per weight row
+    // ---- weight scales -> LDS. Group c of 16 LDS weight rows (16 c .. +15)
+    // in the streaming layout's order: the scale of k-block kb of its row r
+    // is byte (kb % 16) / 4 of the word at (kb / 16) * 256 + (kb % 4) * 64 +
+    // (r % 16) * 4. Streaming weights: each group is contiguous in HBM (N is
+    // a multiple of 16), so 16 DMA copies, issued before the first stages so
+    // that the first barrier's wait covers them; groups past N take the last
+    // group's scales (their rows are clamped and their outputs dropped).
     if constexpr (PACKED) {
-        const int per_row = nc4 * 4;
-        for (int idx = tid; idx < 256 * per_row; idx += F6_THREADS) {
-            const int row = idx / per_row, r = idx - row * per_row;
-            const int cg = r >> 2, g = r & 3;
-            const uint8_t *wc, *ws;
-            const int64_t wr64 = wsel(row, wc, ws);
-            const uint32_t v = *(const uint32_t *)(ws + (wr64 / 16) * nc4 * 256 + cg * 256 +
-                                                   g * 64 + (wr64 % 16) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int kb = 16 * cg + 4 * i + g;
-                if (kb < K / 32) Wsc[row * srow + kb] = (uint8_t)(v >> (8 * i));
-            }
+        for (int m = wave; m < 16 * chunk_b / 1024; m += F6_THREADS / 64) {
+            const int b = 1024 * m + 16 * lane;
+            const int c = b / chunk_b, off = b - c * chunk_b;
+            const int wr0 = min(GLU ? n0 + ((16 * c) & 127) : n0 + 16 * c, N - 16);
+            const uint8_t *ws = (GLU && c >= 8) ? w2s : w1s;
+            dma16(ws + (((int64_t)e * N + wr0) / 16) * chunk_b + off,
+                  lds0 + F6_STAGES * F6_STAGE + 1024 * m);
         }
     } else {
+        // row-major scales: a word holds k-blocks 4 r .. 4 r + 3 of a row
         const int per_row = K / 128;
         for (int idx = tid; idx < 256 * per_row; idx += F6_THREADS) {
             const int row = idx / per_row, r = idx - row * per_row;
             const uint8_t *wc, *ws;
             const int64_t wr64 = wsel(row, wc, ws);
-            *(uint32_t *)(Wsc + row * srow + 4 * r) =
-                *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+            const uint32_t v = *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+            uint8_t *dst = Wsc + (row / 16) * chunk_b + (r / 4) * 256 + (row % 16) * 4 + (r % 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) dst[64 * i] = (uint8_t)(v >> (8 * i));
         }
     }
+    issue(0, 0);
+    issue(1, 1);
 
     // ---- wave tiles
     const int h = lane >> 5, l32 = lane & 31;
@@ -427,6 +433,14 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     // logical chunks 4 h .. 4 h + 2, the scales chunk 3 (the copy that rows
     // with the same key and parity read apart)
     const int key = (l32 >> 1) & 7;
+    // weight scales: this lane's rows and MX block h; the step adds
+    // (k / 8) * 256 + (k % 2) * 128 + (k % 8) / 2 (k-block 2 k + h)
+    int wso[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int row = bt[j] + l32;
+        wso[j] = (row / 16) * chunk_b + (row % 16) * 4 + 64 * h;
+    }
     const int apos0 = ((4 * h) ^ key) << 4, apos1 = ((4 * h + 1) ^ key) << 4,
               apos2 = ((4 * h + 2) ^ key) << 4,
               spos = ((3 ^ key) << 4) + 4 * (2 * ((l32 >> 4) & 1) + (l32 & 1)) + 2 * h;
@@ -452,7 +466,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                     const int row = bt[j] + l32;
                     const u32x4 w = *(const u32x4 *)(Bq + row * 32 + bpos);
                     bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-                    sb[j] = Wsc[row * srow + 2 * kt + h];
+                    sb[j] = Wsc[wso[j] + (kt >> 3) * 256 + (kt & 1) * 128 + ((kt & 7) >> 1)];
                 }
                 i32x8 a1[NI > 0 ? NI : 1], a2[NI > 0 ? NI : 1];
                 int sa1[NI > 0 ? NI : 1], sa2[NI > 0 ? NI : 1];
