@@ -469,7 +469,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                     sb[j] = Wsc[wso[j] + (kt >> 3) * 256 + (kt & 1) * 128 + ((kt & 7) >> 1)];
                 }
                 i32x8 a1[NI > 0 ? NI : 1], a2[NI > 0 ? NI : 1];
-                int sa1[NI > 0 ? NI : 1], sa2[NI > 0 ? NI : 1];
+                int sa[NI > 0 ? NI : 1];
 #pragma unroll
                 for (int i = 0; i < NI; i++) {
                     const uint8_t *ar = Ap + (64 * q + 32 * i + l32) * F6_ROW;
@@ -483,35 +483,35 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                                   (int)c1[0], (int)c1[1], 0, 0};
                     a2[i] = i32x8{(int)c1[2], (int)c1[3], (int)c2[0], (int)c2[1],
                                   (int)c2[2], (int)c2[3], 0, 0};
-                    const uint32_t s2 = *(const uint16_t *)(ar + spos);
-                    sa1[i] = (int)(s2 & 0xffu);
-                    sa2[i] = (int)(s2 >> 8);
+                    // both planes' scales: bytes 0 and 1, selected by the
+                    // instruction's scale byte select
+                    sa[i] = (int)*(const uint16_t *)(ar + spos);
                 }
-                // A format 2: E2M3; B format 4: E2M1; scale byte 0 of each
+                // A format 2: E2M3; B format 4: E2M1; the A scale is byte 0
+                // (plane 1) or byte 1 (plane 2) of sa, the B scale byte 0
 #pragma unroll
                 for (int i = 0; i < NI; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a1[i], bv[j], acc[i][j], 2, 4, 0, sa1[i], 0, sb[j]);
+                            a1[i], bv[j], acc[i][j], 2, 4, 0, sa[i], 0, sb[j]);
 #pragma unroll
                 for (int i = 0; i < NI; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            a2[i], bv[j], acc[i][j], 2, 4, 0, sa2[i], 0, sb[j]);
+                            a2[i], bv[j], acc[i][j], 2, 4, 1, sa[i], 0, sb[j]);
             }
         };
 
         for (int kt = 0; kt < nk; kt++) {
-            // this wave's loads of step kt are done (those of kt + 1 -- 3 or 2
-            // instructions -- may still be in flight); the barrier publishes
+            // this wave's loads of step kt are done: at most two of its loads
+            // are left in flight, all of step kt + 1 (a wave that also loads
+            // codes issues three per step and so waits for one of kt + 1's
+            // too: one wait for every wave, no branch); the barrier publishes
             // every wave's and ends the reads of step kt - 1
             if (kt + 1 < nk) {
-                if (wload)
-                    asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
