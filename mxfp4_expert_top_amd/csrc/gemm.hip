@@ -792,7 +792,8 @@ __global__ __launch_bounds__(TB_THREADS, 1) void gemm_tile256_kernel(
 // and the loads of step k + 2 are in flight during the MFMAs of steps k and
 // k + 1. One barrier per K step: it publishes step k and frees the stage that
 // step k + 2 overwrites (read during step k - 1). The scales of the whole
-// tile (256 weight rows x K / 32) are copied to LDS once, before the loop.
+// tile (256 weight rows x K / 32) go to LDS once, before the loop, in the
+// streaming layout's order (16 groups of 16 weight rows).
 //
 // A rows in LDS: 128 bytes per row, 16-byte chunk c of row r stored at
 // chunk position c ^ ((r >> TD_ASWZ) % 8). With TD_ASWZ = 1 the 16 rows that
@@ -807,11 +808,11 @@ constexpr int TD_STAGE_BYTES = TD_A_BYTES + TD_W_BYTES;  // 40 KB
 constexpr int TD_MAX_K = 4096;
 constexpr int TD_ASWZ = 1, TD_BSWZ = 1;
 
-// bytes per weight row of the LDS scale table: K / 32, rounded up to an odd
-// number of dwords so that 32 consecutive rows hit distinct banks
-__host__ __device__ constexpr int td_scale_row(int K)
+// Scales of 16 weight rows in the streaming layout: K / 512 groups (rounded
+// up) of 256 bytes; the tile's LDS table holds 16 of them.
+__host__ __device__ constexpr int td_scale_chunk(int K)
 {
-    return (((K / 32 + 3) / 4) | 1) * 4;
+    return 256 * ((K / 128 + 3) / 4);
 }
 
 // the epilogue stages up to 32 rows x (256 + 16) bytes per wave in the same LDS
@@ -819,8 +820,8 @@ constexpr int TD_EPI_BYTES = 16 * 32 * (256 + 16);
 
 __host__ __device__ constexpr int td_lds_bytes(int K)
 {
-    return TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K) > TD_EPI_BYTES
-               ? TD_STAGES * TD_STAGE_BYTES + TB_BN * td_scale_row(K)
+    return TD_STAGES * TD_STAGE_BYTES + 16 * td_scale_chunk(K) > TD_EPI_BYTES
+               ? TD_STAGES * TD_STAGE_BYTES + 16 * td_scale_chunk(K)
                : TD_EPI_BYTES;
 }
 
@@ -845,8 +846,8 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? TB_BN / 2 : TB_BN;
     extern __shared__ __attribute__((aligned(16))) uint8_t td_lds[];
-    uint8_t *const Ssc = td_lds + TD_STAGES * TD_STAGE_BYTES;  // [256][srow] scales
-    const int srow = td_scale_row(K);
+    uint8_t *const Ssc = td_lds + TD_STAGES * TD_STAGE_BYTES;  // [16][chunk_b] scales
+    const int chunk_b = td_scale_chunk(K);
 
     const int nblk = (N + COLS - 1) / COLS;
     const int total = plan[0] * nblk;
@@ -863,7 +864,7 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = wave & 3, q = wave >> 2;
-    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const int nch = K / 128;
 
     auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
         int wrow;
@@ -916,35 +917,38 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
     };
 
     const int nk = K / TB_BK;  // even: K is a multiple of 128
-    issue(0, 0);
-    issue(1, 1);
 
-    // ---- the tile's scales -> LDS, in K-block order per weight row
+    // ---- the tile's scales -> LDS. Group c of 16 LDS weight rows in the
+    // streaming layout's order: the scale of k-block kb of its row r is byte
+    // (kb % 16) / 4 of the word at (kb / 16) * 256 + (kb % 4) * 64 + (r % 16) * 4.
+    // Streaming weights: each group is contiguous in HBM (N is a multiple of
+    // 16), so DMA copies, issued before the first stages so that the first
+    // barrier's wait covers them; groups past N take the last group's scales
+    // (their rows are clamped and their outputs dropped).
     if constexpr (PACKED) {
-        const int per_row = nc4 * 4;
-        for (int idx = tid; idx < TB_BN * per_row; idx += TW_THREADS) {
-            const int row = idx / per_row, r = idx - row * per_row;
-            const int cg = r >> 2, g = r & 3;
-            const uint8_t *wc, *ws;
-            const int64_t wr64 = wsel(row, wc, ws);
-            const uint32_t v =
-                *(const uint32_t *)(ws + (wr64 / 16) * nc4 * 256 + cg * 256 + g * 64 + (wr64 % 16) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int kb = 16 * cg + 4 * i + g;
-                if (kb < K / 32) Ssc[row * srow + kb] = (uint8_t)(v >> (8 * i));
-            }
+        for (int m = wave; m < 16 * chunk_b / 1024; m += TW_THREADS / 64) {
+            const int b = 1024 * m + 16 * lane;
+            const int c = b / chunk_b, off = b - c * chunk_b;
+            const int wr0 = min(GLU ? n0 + ((16 * c) & 127) : n0 + 16 * c, N - 16);
+            const uint8_t *ws = (GLU && c >= 8) ? w2s : w1s;
+            dma16(ws + (((int64_t)e * N + wr0) / 16) * chunk_b + off,
+                  lds0 + TD_STAGES * TD_STAGE_BYTES + 1024 * m);
         }
     } else {
+        // row-major scales: a word holds k-blocks 4 r .. 4 r + 3 of a row
         const int per_row = K / 128;
         for (int idx = tid; idx < TB_BN * per_row; idx += TW_THREADS) {
             const int row = idx / per_row, r = idx - row * per_row;
             const uint8_t *wc, *ws;
             const int64_t wr64 = wsel(row, wc, ws);
-            *(uint32_t *)(Ssc + row * srow + 4 * r) =
-                *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+            const uint32_t v = *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+            uint8_t *dst = Ssc + (row / 16) * chunk_b + (r / 4) * 256 + (row % 16) * 4 + (r % 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) dst[64 * i] = (uint8_t)(v >> (8 * i));
         }
     }
+    issue(0, 0);
+    issue(1, 1);
 
     // ---- wave tiles: weight tiles j = 0, 1 of the slot
     const int h = lane >> 5, l32 = lane & 31;
@@ -955,6 +959,14 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
     const int arow_off = (64 * q + l32) * 128;
     const int akey = (4 * h) ^ ((l32 >> TD_ASWZ) & 7);
     const int bpos = 16 * (h ^ (TD_BSWZ & (l32 >> 3)));
+    // weight scales of this lane's rows and MX block h; the step adds
+    // (k / 8) * 256 + (k % 2) * 128 + (k % 8) / 2 (k-block 2 k + h)
+    int wso[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int row = bt[j] + l32;
+        wso[j] = (row / 16) * chunk_b + (row % 16) * 4 + 64 * h;
+    }
 
     auto run = [&](auto ni_c) {
         constexpr int NI = decltype(ni_c)::value;
@@ -976,7 +988,7 @@ __global__ __launch_bounds__(TW_THREADS, 1) void gemm_tile256_w16_kernel(
                 for (int j = 0; j < 2; j++) {
                     const int row = bt[j] + l32;
                     qd[j] = *(const u32x4 *)(Bq + row * 32 + bpos);
-                    f[j] = e8m0_to_f32(Ssc[row * srow + 2 * kt + h]);
+                    f[j] = e8m0_to_f32(Ssc[wso[j] + (kt >> 3) * 256 + (kt & 1) * 128 + ((kt & 7) >> 1)]);
                 }
 #pragma unroll
                 for (int s = 0; s < 4; s++) {
