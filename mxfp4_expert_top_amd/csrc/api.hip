@@ -174,7 +174,9 @@ LayerWs layer_ws(const moe_layer_params *p)
         L.hs = o; o += round_up(A * (size_t)(p->I / 32));
     }
     // fp32 expert outputs: bf16 here would spend most of the max-abs error
-    // budget of the layer (measured 3.05e-2 rms against the 3e-2 bound)
+    // budget of the layer (measured 3.05e-2 rms against the 3e-2 bound). The
+    // FP6X2 layer keeps them as block-int16 rows in the same space (A d
+    // int16, then A d / 32 scale codes)
     L.y = o;      o += round_up(A * (size_t)p->d * 4);
     L.total = o;
     return L;
@@ -621,19 +623,28 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
                                 p->mode, base + L.gws, packed, s));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+    // FP6X2: the expert outputs as block-int16 rows (each value within 2^-15
+    // of its 32-column block's largest magnitude), half the bytes of fp32
+    // for the down projection to write and the combine to read
+    int16_t *yq = (int16_t *)y;
+    uint8_t *ys = (uint8_t *)(base + L.y) + (size_t)A * p->d * 2;
     if (L.f6) {
         HIP_TRY(launch_gemm_fp6x2_run((const uint8_t *)(base + L.hf), p->I, nullptr,
                                       down_codes, down_scales, nullptr, nullptr, p->num_local, A,
-                                      p->d, p->I, MOE_ACT_NONE, y, F6_OUT_F32, p->d,
-                                      base + L.gws, packed, s));
+                                      p->d, p->I, MOE_ACT_NONE, yq, F6_OUT_Q16, p->d,
+                                      base + L.gws, packed, s, ys));
     } else {
         HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
                                 p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,
                                 base + L.gws, packed, s));
     }
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));
-    HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
-                           p->out_dtype == MOE_DT_F32, p->d, s));
+    if (L.f6)
+        HIP_TRY(launch_combine_q16(yq, ys, p->d, inv, w, p->T, p->d, p->k, out,
+                                   p->out_dtype == MOE_DT_F32, p->d, s));
+    else
+        HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                               p->out_dtype == MOE_DT_F32, p->d, s));
     if (ev) HIP_TRY(hipEventRecord(ev[5], s));
     return MOE_OK;
 }

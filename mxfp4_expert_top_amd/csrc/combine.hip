@@ -86,6 +86,70 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT *__restrict__ y, 
     store8<OT>(out + (int64_t)t * ldo + c, acc);
 }
 
+// The same gather over block-int16 expert outputs (the FP6X2 down
+// projection's F6_OUT_Q16 rows: half the bytes of fp32). A thread's 8 columns
+// lie in one 32-column block; value = q 2^(e - 126) / 32767, taken as
+// q (w / 32767) 2^(e - 126) with the weight's factor formed once per row.
+template <typename OT>
+__global__ __launch_bounds__(256) void combine_q16_kernel(const int16_t *__restrict__ yq,
+                                                          const uint8_t *__restrict__ ys,
+                                                          int64_t ldy,
+                                                          const int32_t *__restrict__ inv,
+                                                          const float *__restrict__ w, int d,
+                                                          int k, OT *__restrict__ out,
+                                                          int64_t ldo)
+{
+    const int t = blockIdx.x;
+    __shared__ int32_t rows[MOE_MAX_TOPK_DEV];
+    __shared__ float wts[MOE_MAX_TOPK_DEV];
+    __shared__ int n_rows;
+    if (threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        const int r = j < k ? inv[(int64_t)t * k + j] : -1;
+        const uint64_t valid = __ballot(r >= 0);
+        const int slot = __popcll(valid & ((1ull << j) - 1ull));
+        if (r >= 0) {
+            rows[slot] = r;
+            wts[slot] = w[(int64_t)t * k + j];
+        }
+        if (j == 0) n_rows = __popcll(valid);
+    }
+    __syncthreads();
+    const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (c >= d) return;
+    const int n = n_rows;
+    const int64_t lds = ldy / 32;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int j = 0; j < n; j++) {
+        const int64_t r = rows[j];
+        const u32x4 q = *(const u32x4 *)(yq + r * ldy + c);
+        const float wx = ldexpf(wts[j] * (1.0f / 32767.0f), (int)ys[r * lds + c / 32] - 126);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            acc[2 * i] += wx * (float)(int16_t)(q[i] & 0xffffu);
+            acc[2 * i + 1] += wx * (float)(int16_t)(q[i] >> 16);
+        }
+    }
+    store8<OT>(out + (int64_t)t * ldo + c, acc);
+}
+
+hipError_t launch_combine_q16(const int16_t *yq, const uint8_t *ys, int64_t ldy,
+                              const int32_t *inv, const float *w, int T, int d, int k,
+                              void *out, int out_f32, int64_t ldo, hipStream_t s)
+{
+    if (T <= 0) return hipSuccess;
+    if (d % 32 != 0 || ldy % 32 != 0) return hipErrorInvalidValue;
+    dim3 grid(T, (d + 8 * 256 - 1) / (8 * 256)), block(256);
+    if (out_f32)
+        hipLaunchKernelGGL((combine_q16_kernel<float>), grid, block, 0, s, yq, ys, ldy, inv, w, d,
+                           k, (float *)out, ldo);
+    else
+        hipLaunchKernelGGL((combine_q16_kernel<bf16>), grid, block, 0, s, yq, ys, ldy, inv, w, d,
+                           k, (bf16 *)out, ldo);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,
                           const float *w, int T, int d, int k, void *out, int out_f32,
                           int64_t ldo, hipStream_t s)

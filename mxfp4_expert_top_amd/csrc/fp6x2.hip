@@ -41,6 +41,7 @@
 namespace moe {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
@@ -299,11 +300,18 @@ __host__ __device__ constexpr int f6_lds_bytes(int K)
 }
 static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
 
-// Output kinds of the projection: OutT = float or bf16 rows, or uint8_t for
+// Output kinds of the projection: OutT = float or bf16 rows, uint8_t for
 // split records (the next projection's input, written as moe_fp6x2_split
-// would write the fp32 results).
+// would write the fp32 results), or int16_t for block-int16 rows (the expert
+// outputs inside the layer, read once by the combine): per 32 columns one
+// code e in osc, the biased exponent of the block's largest magnitude m
+// (at most 252), and each value v as the integer q nearest 32767 v 2^(126 - e)
+// (|v| 2^(126 - e) < 1), standing for q 2^(e - 126) / 32767: within
+// 2^(e - 126) / 65534 <= 2^-15 m of v.
 template <typename OutT>
 constexpr bool f6_records = std::is_same<OutT, uint8_t>::value;
+template <typename OutT>
+constexpr bool f6_q16 = std::is_same<OutT, int16_t>::value;
 
 template <int ACT, typename OutT, bool PACKED>
 __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
@@ -311,10 +319,11 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
     const int32_t *__restrict__ plan, int hdr, int N, int K, OutT *__restrict__ out,
-    int64_t ldo)
+    int64_t ldo, uint8_t *__restrict__ osc)
 {
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? F6_BN / 2 : F6_BN;
+    static_assert(!(GLU && f6_q16<OutT>), "block-int16 rows come from the down projection");
     extern __shared__ __attribute__((aligned(16))) uint8_t f6_lds[];
     const int chunk_b = f6_scale_chunk(K);
     uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [16][chunk_b] weight scales
@@ -561,8 +570,10 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                 }
             }
         } else {
-            // one 32-row tile at a time, stored as whole 16-byte row segments
-            constexpr int ROW_B = COLS_W * (int)sizeof(OutT);  // 64, 128 or 256 bytes
+            // one 32-row tile at a time, staged (fp32 for block-int16 rows)
+            // and stored as whole row segments
+            using StT = typename std::conditional<f6_q16<OutT>, float, OutT>::type;
+            constexpr int ROW_B = COLS_W * (int)sizeof(StT);  // 64, 128 or 256 bytes
             constexpr int PITCH = ROW_B + 16;
             constexpr int LPR = ROW_B / 16, RPI = 64 / LPR;    // lanes per row, rows per store
             static_assert(32 * PITCH <= 64 * F6_EPI_PITCH, "staging fits the wave's area");
@@ -571,21 +582,61 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-                    OutT *row = (OutT *)(stg + r * PITCH);
+                    StT *row = (StT *)(stg + r * PITCH);
                     if constexpr (GLU) {
-                        store_out<OutT>(row + l32, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                        store_out<StT>(row + l32, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
                     } else {
 #pragma unroll
                         for (int j = 0; j < 2; j++)
-                            store_out<OutT>(row + 32 * j + l32, acc[i][j][v]);
+                            store_out<StT>(row + 32 * j + l32, acc[i][j][v]);
                     }
+                }
+                // block-int16 rows: this lane's row of iteration 0
+                OutT *yrow = nullptr;
+                uint8_t *srow = nullptr;
+                if constexpr (f6_q16<OutT>) {
+                    const int64_t r = (int64_t)r0 + 64 * q + 32 * i + lane / LPR;
+                    yrow = out + r * ldo + c0 + 4 * (lane % LPR);
+                    srow = osc + r * (ldo / 32) + (c0 + 4 * (lane % LPR)) / 32;
                 }
 #pragma unroll
                 for (int it = 0; it < 32 / RPI; it++) {
                     const int r = RPI * it + lane / LPR, seg = lane % LPR;
                     const u32x4 val = *(const u32x4 *)(stg + r * PITCH + 16 * seg);
                     const int rl = 64 * q + 32 * i + r;
-                    if (col_on && rl < mrows) {
+                    if constexpr (f6_q16<OutT>) {
+                        // columns c0 + 4 seg .. + 3; the 8 lanes with equal
+                        // lane / 8 hold one 32-column block. Magnitudes are
+                        // compared as bit patterns (non-negative floats
+                        // order as their bits)
+                        uint32_t mb = 0;
+#pragma unroll
+                        for (int c = 0; c < 4; c++) mb = max(mb, val[c] & 0x7fffffffu);
+                        // max over the 8 lanes: swap neighbours, then pairs
+                        // (quad_perm 1,0,3,2 and 2,3,0,1), then mirror the
+                        // 8-lane half row (lane i and 7 - i): DPP moves on
+                        // the vector unit, no LDS round trip
+                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false));
+                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, false));
+                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x141, 0xF, 0xF, false));
+                        // e: the block's largest biased exponent (at most
+                        // 252: larger blocks saturate); x 2^(126 - e) lies
+                        // in (-1, 1), and v_cvt_pknorm_i16_f32 rounds its
+                        // 32767 multiple to an integer, two values a step
+                        const int code = min((int)(mb >> 23), 252);
+                        const float inv = __uint_as_float((uint32_t)(253 - code) << 23);
+                        if (col_on && rl < mrows) {
+                            float x[4];
+#pragma unroll
+                            for (int c = 0; c < 4; c++) x[c] = __uint_as_float(val[c]) * inv;
+                            const u32x2 pk = {
+                                (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[0], x[1])),
+                                (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[2], x[3]))};
+                            __builtin_nontemporal_store(pk, (u32x2 *)(yrow + (int64_t)it * RPI * ldo));
+                            if ((seg & 7) == 0)
+                                srow[(int64_t)it * RPI * (ldo / 32)] = (uint8_t)code;
+                        }
+                    } else if (col_on && rl < mrows) {
                         u32x4 *dst = (u32x4 *)((uint8_t *)(out + (int64_t)(r0 + rl) * ldo + c0) +
                                                16 * seg);
                         if constexpr (!GLU && sizeof(OutT) == 4) __builtin_nontemporal_store(val, dst);
@@ -608,7 +659,7 @@ static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_row
                             const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                             const uint8_t *w2s, const int32_t *plan,
                             int max_groups, int hdr, int N, int K, OutT *out, int64_t ldo,
-                            hipStream_t s)
+                            uint8_t *osc, hipStream_t s)
 {
     constexpr int COLS = ACT != ACT_NONE ? F6_BN / 2 : F6_BN;
     const int64_t grid = (int64_t)max_groups * ((N + COLS - 1) / COLS);
@@ -620,7 +671,7 @@ static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_row
     const hipError_t err = ensure_dynamic_lds((const void *)kern, f6_lds_bytes(K));
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(F6_THREADS), f6_lds_bytes(K), s, ad, lda,
-                       a_rows, w1c, w1s, w2c, w2s, plan, hdr, N, K, out, ldo);
+                       a_rows, w1c, w1s, w2c, w2s, plan, hdr, N, K, out, ldo, osc);
     return hipGetLastError();
 }
 
@@ -628,15 +679,18 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                  const uint8_t *w2s, int num_local, int max_rows, int N, int K,
                                  int act, void *out, int out_kind, int64_t ldo,
-                                 const void *plan_ws, int packed, hipStream_t s)
+                                 const void *plan_ws, int packed, hipStream_t s,
+                                 uint8_t *out_scales)
 {
     if (K % 128 != 0 || K > F6_MAX_K) return hipErrorInvalidValue;
     if (out_kind == F6_OUT_RECORDS && act == ACT_NONE) return hipErrorInvalidValue;
+    if (out_kind == F6_OUT_Q16 && (act != ACT_NONE || out_scales == nullptr || ldo % 32 != 0))
+        return hipErrorInvalidValue;
     const GemmPlanArgs pa = gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, nullptr);
     const int32_t *plan = (const int32_t *)plan_ws;
 #define F6_LAUNCH(A, OT, PK)                                                                   \
     return launch_f6<A, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,      \
-                                pa.hdr, N, K, (OT *)out, ldo, s)
+                                pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
 #define F6_GLU(OT, PK)                                                                         \
     switch (act) {                                                                             \
     case ACT_SILU_MUL: F6_LAUNCH(ACT_SILU_MUL, OT, PK);                                       \
@@ -655,6 +709,10 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
     if (out_kind == F6_OUT_F32) {
         if (packed) F6_ANY(float, true)
         F6_ANY(float, false)
+    }
+    if (out_kind == F6_OUT_Q16) {
+        if (packed) F6_LAUNCH(ACT_NONE, int16_t, true);
+        F6_LAUNCH(ACT_NONE, int16_t, false);
     }
     if (packed) F6_ANY(bf16, true)
     F6_ANY(bf16, false)

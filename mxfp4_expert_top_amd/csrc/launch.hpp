@@ -150,15 +150,18 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
                               const int32_t *n_dev = nullptr);
 // The 256-row tile from a 256-row work plan (MOE_SCHED_TILE256) already built
 // in plan_ws; K % 128 == 0, K <= 4096 (hipErrorInvalidValue otherwise).
-// Output kinds: bf16 or fp32 rows [rows][ldo], or (GLU only) split records of
+// Output kinds: bf16 or fp32 rows [rows][ldo]; (GLU only) split records of
 // the fp32 results, row r at out + 2 r ldo bytes, as launch_fp6x2_split
-// writes them.
-enum { F6_OUT_BF16 = 0, F6_OUT_F32 = 1, F6_OUT_RECORDS = 2 };
+// writes them; (no activation only) block-int16 rows: int16 [rows][ldo] and
+// one exponent code per 32 columns in out_scales [rows][ldo / 32], the value
+// of q under code e being q 2^(e - 126) / 32767 (ldo % 32 == 0).
+enum { F6_OUT_BF16 = 0, F6_OUT_F32 = 1, F6_OUT_RECORDS = 2, F6_OUT_Q16 = 3 };
 hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                  const uint8_t *w2s, int num_local, int max_rows, int N, int K,
                                  int act, void *out, int out_kind, int64_t ldo,
-                                 const void *plan_ws, int packed, hipStream_t s);
+                                 const void *plan_ws, int packed, hipStream_t s,
+                                 uint8_t *out_scales = nullptr);
 hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                      const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                      const uint8_t *w2s, const int32_t *off, int num_local,
@@ -196,6 +199,11 @@ hipError_t launch_prepack(const uint8_t *codes, const uint8_t *scales, int64_t n
                           uint8_t *pcodes, uint8_t *pscales, hipStream_t s);
 
 // combine.hip
+// The combine over block-int16 expert outputs (F6_OUT_Q16: yq [rows][ldy],
+// ys [rows][ldy / 32]); same sum, order and output as launch_combine.
+hipError_t launch_combine_q16(const int16_t *yq, const uint8_t *ys, int64_t ldy,
+                              const int32_t *inv, const float *w, int T, int d, int k,
+                              void *out, int out_f32, int64_t ldo, hipStream_t s);
 hipError_t launch_combine(const void *y, int y_f32, int64_t ldy, const int32_t *inv,
                           const float *w, int T, int d, int k, void *out, int out_f32,
                           int64_t ldo, hipStream_t s);

@@ -285,6 +285,67 @@ def test_auto_schedule_takes_fp6x2(m, cfg):
     assert_close_layer(np_(a["out"]), ref["out"], cfg.name)
 
 
+def _block_int16_step(y):
+    """The spacing of the block-int16 codes of fp32 rows y [R, d]: per 32
+    columns, with e the biased exponent of the block's largest magnitude
+    (at most 252), 2^(e - 126) / 32767."""
+    R, d = y.shape
+    mb = (np.abs(y).reshape(R, d // 32, 32).view(np.uint32).max(-1) >> 23).astype(np.int64)
+    e = np.minimum(mb, 252)
+    return np.repeat(np.exp2(e - 126.0) / 32767.0, 32, axis=1)
+
+
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[4]], ids=lambda c: c.name)
+def test_fp6x2_layer_block_int16_expert_outputs(m, cfg):
+    """Inside the FP6X2 layer the expert outputs Y travel as block-int16 rows
+    (per 32 columns the biased exponent e of the largest magnitude; each value
+    as the integer nearest 32767 v 2^(126 - e)). Against the same layer built
+    from the standalone entry points -- the permutation, the split, the
+    gate/up projection's records and the down projection's fp32 rows -- and
+    an fp32 combine of those unrounded rows in slot order: every output
+    element within sum_j w_j (0.5 + 2^-9) step_j plus fp32 rounding, step_j
+    the code spacing of row j's block. A rounding toward zero (errors up to a
+    whole step), a wrong exponent or a wrong block would exceed that on many
+    of the elements."""
+    inp = make_inputs(cfg).to(DEV)
+    T, k, d, I, nl = cfg.T, cfg.k, cfg.d, cfg.I, cfg.num_local
+    g = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, out_dtype=torch.float32)
+    A = T * k
+    off = torch.empty(nl + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(A, dtype=torch.int32, device=DEV)
+    inv = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    pws = m.alloc_workspace(m.moe_permute_workspace_size(T, nl), DEV)
+    m.moe_permute(g["idx"], None, cfg.expert_begin, nl, off, perm, inv, pws, E=cfg.E)
+    W = inp.weights
+    xd = m.moe_fp6x2_split(inp.x)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_fp6x2_workspace_size(nl, A), DEV)
+    hrec = torch.empty(A, 2 * I, dtype=torch.uint8, device=DEV)
+    m.moe_grouped_gemm_fp6x2(xd, perm, W["gate_codes"], W["gate_scales"], W["up_codes"],
+                             W["up_scales"], off, A, 1, hrec, ws)
+    y = torch.zeros(A, d, dtype=torch.float32, device=DEV)
+    m.moe_grouped_gemm_fp6x2(hrec, None, W["down_codes"], W["down_scales"], None, None, off, A, 0,
+                             y, ws)
+    torch.cuda.synchronize()
+    yv, iv, wv = np_(y), np_(inv), np_(g["w"])
+    step = _block_int16_step(yv)
+    ref = np.zeros((T, d), np.float32)
+    bound = np.zeros((T, d), np.float64)
+    mag = np.zeros((T, d), np.float64)
+    for j in range(k):
+        r = iv[:, j]
+        on = r >= 0
+        wj = np.where(on, wv[:, j], 0.0).astype(np.float32)[:, None]
+        rows = np.where(on, r, 0)
+        ref = ref + wj * yv[rows]
+        bound += wj.astype(np.float64) * step[rows]
+        mag += np.abs(wj.astype(np.float64) * yv[rows])
+    got = np_(g["out"]).astype(np.float64)
+    diff = np.abs(got - ref.astype(np.float64))
+    lim = (0.5 + 2.0 ** -9) * bound + 4 * k * 2.0 ** -24 * mag
+    print(f"{cfg.name}: max |out - fp32-Y out| / sum w step = {(diff / bound).max():.3f}")
+    assert (diff <= lim).all(), (diff - lim).max()
+
+
 def test_fp6x2_layer_determinism_bitwise(m):
     inp = make_inputs(SMALL[4]).to(DEV)
     a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
