@@ -426,8 +426,10 @@ __global__ __launch_bounds__(M8_THREADS, 1) void gemm_mx8_kernel(
 // - MXFP8 rows (64 bytes per K step) and 4-bit codes go into a three-stage
 //   LDS ring by global_load_lds_dwordx4; one barrier per K step publishes
 //   step k and frees the stage that step k + 2 overwrites.
-// - The tile's weight scales and its rows' scales (256 x K / 32 bytes each,
-//   rows padded to an odd number of dwords) are copied to LDS once.
+// - The tile's weight scales go to LDS once, by the same DMA, in the
+//   streaming layout's order (16 groups of 16 weight rows); its rows' scales
+//   (256 x K / 32 bytes, rows padded to an odd number of dwords) are copied
+//   once, every load of a thread issued before its first store.
 // - Wave w: row block q = w / 4 (two 32-row tiles) and slot c = w % 4 (gate
 //   and up rows of output columns 32 c .. + 32, or weight rows 64 c .. + 64),
 //   so every SIMD gets the same share of an expert's row tiles.
@@ -447,9 +449,16 @@ __host__ __device__ constexpr int m8d_scale_row(int K)
     return (((K / 32 + 3) / 4) | 1) * 4;
 }
 
+// Weight scales of 16 weight rows in the streaming layout: K / 512 groups
+// (rounded up) of 256 bytes; the tile's LDS table holds 16 of them.
+__host__ __device__ constexpr int m8d_scale_chunk(int K)
+{
+    return 256 * ((K / 128 + 3) / 4);
+}
+
 __host__ __device__ constexpr int m8d_lds_bytes(int K)
 {
-    return M8D_STAGES * M8D_STAGE + 2 * 256 * m8d_scale_row(K);
+    return M8D_STAGES * M8D_STAGE + 16 * m8d_scale_chunk(K) + 256 * m8d_scale_row(K);
 }
 
 template <int ACT, typename OutT, bool PACKED>
@@ -463,9 +472,9 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
     extern __shared__ __attribute__((aligned(16))) uint8_t m8d_lds[];
-    const int srow = m8d_scale_row(K);
-    uint8_t *const Wsc = m8d_lds + M8D_STAGES * M8D_STAGE;  // [256][srow] weight scales
-    uint8_t *const Asc = Wsc + 256 * srow;                   // [256][srow] row scales
+    const int srow = m8d_scale_row(K), chunk_b = m8d_scale_chunk(K);
+    uint8_t *const Wsc = m8d_lds + M8D_STAGES * M8D_STAGE;  // [16][chunk_b] weight scales
+    uint8_t *const Asc = Wsc + 16 * chunk_b;                 // [256][srow] row scales
 
     const int nblk = (N + COLS - 1) / COLS;
     const int total = plan[0] * nblk;
@@ -482,7 +491,7 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slot = wave & 3, q = wave >> 2;
-    const int nch = K / 128, nc4 = (nch + 3) / 4;
+    const int nch = K / 128;
     const int64_t lds_ = lda / 32;
 
     auto wsel = [&](int br, const uint8_t *&wc, const uint8_t *&ws) -> int64_t {
@@ -535,42 +544,59 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
     };
 
     const int nk = K / M8_BK;  // even: K is a multiple of 128
+
+    // ---- weight scales -> LDS. Group c of 16 LDS weight rows in the
+    // streaming layout's order: the scale of k-block kb of its row r is byte
+    // (kb % 16) / 4 of the word at (kb / 16) * 256 + (kb % 4) * 64 + (r % 16) * 4.
+    // Streaming weights: each group is contiguous in HBM (N is a multiple of
+    // 16), so DMA copies ahead of the first stages (the first barrier's wait
+    // covers them); groups past N take the last group's scales (their rows
+    // are clamped and their outputs dropped).
+    if constexpr (PACKED) {
+        for (int m = wave; m < 16 * chunk_b / 1024; m += M8D_THREADS / 64) {
+            const int b = 1024 * m + 16 * lane;
+            const int c = b / chunk_b, off = b - c * chunk_b;
+            const int wr0 = min(GLU ? n0 + ((16 * c) & 127) : n0 + 16 * c, N - 16);
+            const uint8_t *ws = (GLU && c >= 8) ? w2s : w1s;
+            dma16(ws + (((int64_t)e * N + wr0) / 16) * chunk_b + off,
+                  lds0 + M8D_STAGES * M8D_STAGE + 1024 * m);
+        }
+    } else {
+        // row-major scales: a word holds k-blocks 4 r .. 4 r + 3 of a row
+        const int per_row = K / 128;
+        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
+            const int row = idx / per_row, r = idx - row * per_row;
+            const uint8_t *wc, *ws;
+            const int64_t wr64 = wsel(row, wc, ws);
+            const uint32_t v = *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
+            uint8_t *dst = Wsc + (row / 16) * chunk_b + (r / 4) * 256 + (row % 16) * 4 + (r % 4);
+#pragma unroll
+            for (int i = 0; i < 4; i++) dst[64 * i] = (uint8_t)(v >> (8 * i));
+        }
+    }
     issue(0, 0);
     issue(1, 1);
 
-    // ---- scales -> LDS, in K-block order per row
-    if constexpr (PACKED) {
-        const int per_row = nc4 * 4;
-        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
-            const int row = idx / per_row, r = idx - row * per_row;
-            const int cg = r >> 2, g = r & 3;
-            const uint8_t *wc, *ws;
-            const int64_t wr64 = wsel(row, wc, ws);
-            const uint32_t v = *(const uint32_t *)(ws + (wr64 / 16) * nc4 * 256 + cg * 256 +
-                                                   g * 64 + (wr64 % 16) * 4);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int kb = 16 * cg + 4 * i + g;
-                if (kb < K / 32) Wsc[row * srow + kb] = (uint8_t)(v >> (8 * i));
-            }
-        }
-    } else {
-        const int per_row = K / 128;
-        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
-            const int row = idx / per_row, r = idx - row * per_row;
-            const uint8_t *wc, *ws;
-            const int64_t wr64 = wsel(row, wc, ws);
-            *(uint32_t *)(Wsc + row * srow + 4 * r) =
-                *(const uint32_t *)(ws + wr64 * (K / 32) + 4 * r);
-        }
-    }
+    // ---- the rows' scales -> LDS: every load of a thread before its first
+    // store (K <= 4096: at most 8 words per thread)
     if (lds_ % 4 == 0) {
         const int per_row = K / 128;
-        for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
-            const int row = idx / per_row, r = idx - row * per_row;
-            *(uint32_t *)(Asc + row * srow + 4 * r) =
-                *(const uint32_t *)(as + arow_of(row) * lds_ + 4 * r);
+        constexpr int MAXW = 256 * (M8D_MAX_K / 128) / M8D_THREADS;
+        uint32_t v[MAXW];
+        int dsto[MAXW];
+#pragma unroll
+        for (int u = 0; u < MAXW; u++) {
+            const int idx = tid + u * M8D_THREADS;
+            dsto[u] = -1;
+            if (idx < 256 * per_row) {
+                const int row = idx / per_row, r = idx - row * per_row;
+                v[u] = *(const uint32_t *)(as + arow_of(row) * lds_ + 4 * r);
+                dsto[u] = row * srow + 4 * r;
+            }
         }
+#pragma unroll
+        for (int u = 0; u < MAXW; u++)
+            if (dsto[u] >= 0) *(uint32_t *)(Asc + dsto[u]) = v[u];
     } else {
         const int per_row = K / 32;
         for (int idx = tid; idx < 256 * per_row; idx += M8D_THREADS) {
@@ -589,6 +615,14 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
     const int akey = (l32 >> 2) & 3;
     const int lo_off = (h ^ akey) << 4, hi_off = ((2 + h) ^ akey) << 4;
     const int bpos = 16 * (h ^ ((l32 >> 3) & 1));
+    // weight scales of this lane's rows and MX block h; the step adds
+    // (k / 8) * 256 + (k % 2) * 128 + (k % 8) / 2 (k-block 2 k + h)
+    int wso[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int row = bt[j] + l32;
+        wso[j] = (row / 16) * chunk_b + (row % 16) * 4 + 64 * h;
+    }
 
     auto run = [&](auto ni_c) {
         constexpr int NI = decltype(ni_c)::value;
@@ -611,7 +645,7 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
                     const int row = bt[j] + l32;
                     const u32x4 w = *(const u32x4 *)(Bq + row * 32 + bpos);
                     bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-                    sb[j] = Wsc[row * srow + 2 * kt + h];
+                    sb[j] = Wsc[wso[j] + (kt >> 3) * 256 + (kt & 1) * 128 + ((kt & 7) >> 1)];
                 }
 #pragma unroll
                 for (int i = 0; i < NI; i++) {
