@@ -183,6 +183,24 @@ __device__ __forceinline__ void f6_store_block(uint8_t *rec, int half, const uin
     if (half) *(u32x4 *)(rec + 112) = u32x4{0u, 0u, 0u, 0u};
 }
 
+// The same record written by a lane pair: the lanes 2 m and 2 m + 1 of a
+// wave hold blocks 2 s and 2 s + 1 of one record. The scale pairs meet in
+// both lanes (a DPP swap of neighbours); the even lane stores the 16-byte
+// scale chunk (four copies), the odd one the 16 zero bytes: four 16-byte
+// stores per lane, none of 2 bytes. Both lanes of a pair must be active.
+__device__ __forceinline__ void f6_store_pair(uint8_t *rec, int half, const uint32_t w[12],
+                                              uint32_t s1, uint32_t s2)
+{
+    u32x4 *dst = (u32x4 *)(rec + 64 * half);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    dst[2] = u32x4{w[8], w[9], w[10], w[11]};
+    const uint32_t sc = s1 | (s2 << 8);
+    const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0xB1, 0xF, 0xF, false);
+    const uint32_t sw = half ? 0u : (sc | (other << 16));
+    dst[3] = u32x4{sw, sw, sw, sw};
+}
+
 template <typename InT>
 __device__ __forceinline__ void f6_load32(const InT *p, float v[32]);
 template <>
@@ -207,6 +225,8 @@ __device__ __forceinline__ void f6_load32<bf16>(const bf16 *p, float v[32])
 
 // Rows n < min(N, *n_dev) (all N rows when n_dev is null); one thread per
 // 32-element block, grid-stride. Row n of the output at out + n * ldo bytes.
+// K % 64 == 0, so the two blocks of a record sit in lanes 2 m and 2 m + 1 and
+// enter and leave the loop together (f6_store_pair).
 template <typename InT>
 __global__ __launch_bounds__(256) void fp6x2_split_kernel(const InT *__restrict__ v, int64_t ldv,
                                                           int64_t N, int K,
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(256) void fp6x2_split_kernel(const InT *__restrict_
         uint32_t w[12];
         const uint32_t s1 = mxfp6_plane(x, w);
         const uint32_t s2 = mxfp6_plane(x, w + 6);
-        f6_store_block(out + n * ldo + (b >> 1) * 128, b & 1, w, s1, s2);
+        f6_store_pair(out + n * ldo + (b >> 1) * 128, b & 1, w, s1, s2);
     }
 }
 
@@ -233,6 +253,7 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
                               uint8_t *out, int64_t ldo, hipStream_t s, const int32_t *n_dev)
 {
     const int64_t nb = N * (K / 32);
+    if (K % 64 != 0) return hipErrorInvalidValue;  // records pair the blocks of 64
     if (nb <= 0) return hipSuccess;
     const dim3 grid((unsigned)std::min<int64_t>((nb + 255) / 256, 16384)), block(256);
     if (v_f32)
