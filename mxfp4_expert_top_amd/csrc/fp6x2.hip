@@ -168,23 +168,9 @@ __device__ __forceinline__ uint32_t mxfp6_plane(float v[32], uint32_t w[6])
     return (uint32_t)s;
 }
 
-// Block `half` (0 or 1) of a 128-byte record: its 48 code bytes, its two
-// scale bytes and the zeros of its half.
-__device__ __forceinline__ void f6_store_block(uint8_t *rec, int half, const uint32_t w[12],
-                                               uint32_t s1, uint32_t s2)
-{
-    u32x4 *dst = (u32x4 *)(rec + 64 * half);
-    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
-    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
-    dst[2] = u32x4{w[8], w[9], w[10], w[11]};
-    const uint16_t sc = (uint16_t)(s1 | (s2 << 8));
-#pragma unroll
-    for (int c = 0; c < 4; c++) *(uint16_t *)(rec + 48 + 4 * c + 2 * half) = sc;
-    if (half) *(u32x4 *)(rec + 112) = u32x4{0u, 0u, 0u, 0u};
-}
-
-// The same record written by a lane pair: the lanes 2 m and 2 m + 1 of a
-// wave hold blocks 2 s and 2 s + 1 of one record. The scale pairs meet in
+// One 128-byte record written by a lane pair: the lanes 2 m and 2 m + 1 of a
+// wave hold blocks 2 s and 2 s + 1 of the record, with their 48 code bytes
+// each and their two scale bytes each. The scale pairs meet in
 // both lanes (a DPP swap of neighbours); the even lane stores the 16-byte
 // scale chunk (four copies), the odd one the 16 zero bytes: four 16-byte
 // stores per lane, none of 2 bytes. Both lanes of a pair must be active.
@@ -561,9 +547,12 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
         uint8_t *const stg = f6_lds + wave * (64 * F6_EPI_PITCH);
         if constexpr (f6_records<OutT>) {
             // (GLU only: a wave's 32 output columns are one MX block.) The
-            // fp32 results of the wave's 64 rows staged, 128 bytes per row;
-            // then lane r converts row r's block as the split does and
-            // writes it into the row's record
+            // fp32 results of the wave's 64 rows staged, 128 bytes per row.
+            // Then thread t takes row t / 4 of the tile and block t % 4 (the
+            // columns of slot t % 4), from the staging of the wave that holds
+            // them, converts it as the split does, and lanes 4 r, 4 r + 1 and
+            // 4 r + 2, 4 r + 3 write the row's two records as pairs (a pair
+            // is active together: it shares the row, and N % 64 == 0)
             static_assert(GLU, "records are written by the GLU projection");
 #pragma unroll
             for (int i = 0; i < NI; i++)
@@ -573,22 +562,24 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
                     ((float *)(stg + r * F6_EPI_PITCH))[l32] =
                         act_apply<ACT>(acc[i][0][v], acc[i][1][v]);
                 }
-            {
-                const int r = lane, rl = 64 * q + r;
-                if (r < 32 * NI && rl < mrows && col_on) {
-                    float x[32];
+            __syncthreads();
+            const int R = tid >> 2, bb = tid & 3;
+            const int cb = n0 + 32 * bb;
+            if (R < mrows && cb < N) {
+                const uint8_t *src = f6_lds + (4 * (R >> 6) + bb) * (64 * F6_EPI_PITCH) +
+                                     (R & 63) * F6_EPI_PITCH;
+                float x[32];
 #pragma unroll
-                    for (int j = 0; j < 8; j++) {
-                        const f32x4 t = *(const f32x4 *)(stg + r * F6_EPI_PITCH + 16 * j);
-                        x[4 * j] = t[0]; x[4 * j + 1] = t[1]; x[4 * j + 2] = t[2]; x[4 * j + 3] = t[3];
-                    }
-                    uint32_t w[12];
-                    const uint32_t s1 = mxfp6_plane(x, w);
-                    const uint32_t s2 = mxfp6_plane(x, w + 6);
-                    const int b = c0 >> 5;
-                    f6_store_block((uint8_t *)out + (int64_t)(r0 + rl) * 2 * ldo + (b >> 1) * 128,
-                                   b & 1, w, s1, s2);
+                for (int j = 0; j < 8; j++) {
+                    const f32x4 t = *(const f32x4 *)(src + 16 * j);
+                    x[4 * j] = t[0]; x[4 * j + 1] = t[1]; x[4 * j + 2] = t[2]; x[4 * j + 3] = t[3];
                 }
+                uint32_t w[12];
+                const uint32_t s1 = mxfp6_plane(x, w);
+                const uint32_t s2 = mxfp6_plane(x, w + 6);
+                const int b = cb >> 5;
+                f6_store_pair((uint8_t *)out + (int64_t)(r0 + R) * 2 * ldo + (b >> 1) * 128, b & 1, w,
+                              s1, s2);
             }
         } else {
             // one 32-row tile at a time, staged (fp32 for block-int16 rows)
