@@ -154,7 +154,8 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // the fp32 results, row r at out + 2 r ldo bytes, as launch_fp6x2_split
 // writes them; (no activation only) block-int16 rows: int16 [rows][ldo] and
 // one exponent code per 32 columns in out_scales [rows][ldo / 32], the value
-// of q under code e being q 2^(e - 126) / 32767 (ldo % 32 == 0).
+// of q under code e being q 2^(e - 126) / 32767 (ldo % 32 == 0). Non-finite
+// results are not carried: an infinity saturates, a NaN comes out finite.
 enum { F6_OUT_BF16 = 0, F6_OUT_F32 = 1, F6_OUT_RECORDS = 2, F6_OUT_Q16 = 3 };
 hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                  const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
