@@ -346,6 +346,17 @@ def test_fp6x2_layer_block_int16_expert_outputs(m, cfg):
     assert (diff <= lim).all(), (diff - lim).max()
 
 
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2]], ids=lambda c: c.name)
+def test_fp6x2_layer_bf16_output_is_fp32_rounded(m, cfg):
+    """The FP6X2 layer's bf16 output (the block-int16 combine's bf16 store) is
+    exactly its fp32 output rounded to nearest-even, on every element."""
+    inp = make_inputs(cfg).to(DEV)
+    a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, out_dtype=torch.float32)
+    b = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, out_dtype=torch.bfloat16)
+    assert torch.equal(a["idx"], b["idx"])
+    assert torch.equal(b["out"], a["out"].to(torch.bfloat16))
+
+
 def test_fp6x2_layer_determinism_bitwise(m):
     inp = make_inputs(SMALL[4]).to(DEV)
     a = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
