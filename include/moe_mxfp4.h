@@ -390,12 +390,15 @@ typedef struct {
     int precision;    /* enum moe_precision: MOE_PREC_BF16 (the pages' bf16
                          activations), MOE_PREC_MX8 (tokens and h rounded to
                          MXFP8 before each projection; `mode` as in
-                         moe_grouped_gemm_mx8) or MOE_PREC_FP6X2 (where the
-                         schedule resolves to 256-row tiles and d, I <= 4096,
-                         both projections take their activations -- the
-                         tokens, and h from its fp32 value -- as two MXFP6
-                         planes, moe_grouped_gemm_fp6x2; otherwise the bf16
-                         path) */
+                         moe_grouped_gemm_mx8) or MOE_PREC_FP6X2 (with mode
+                         TILE256 or TILE128, or AUTO / TILED at a mean of at
+                         least 128 rows per local expert over T k, and d, I
+                         <= 4096, both projections take their activations --
+                         the tokens, and h from its fp32 value -- as two MXFP6
+                         planes, moe_grouped_gemm_fp6x2, on 256- or 128-row
+                         tiles: TILE256 / TILE128 fix the tile, AUTO / TILED
+                         choose it per projection, and the output does not
+                         depend on it; otherwise the bf16 path) */
 } moe_layer_params;
 
 /* Scratch bytes moe_layer needs for these parameters (0 if invalid). */

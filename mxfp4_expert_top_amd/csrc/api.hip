@@ -6,6 +6,7 @@
 #include "moe_mxfp4.h"
 #include "launch.hpp"
 
+#include <cmath>
 #include <mutex>
 #include <set>
 #include <utility>
@@ -110,6 +111,8 @@ struct LayerWs {
     size_t xq, xs, hq, hs;  // MX8 mode: MXFP8 tokens and h (codes, scales)
     size_t xf, hf;          // FP6X2: the tokens' and h's two MXFP6 planes
     bool f6;                // the FP6X2 gate/up projection runs
+    bool gu128, dn128;      // FP6X2 projections on 128-row tiles (gate/up, down)
+    size_t gws2;            // the down projection's own work plan (tiles differ)
     int splits;
     int router;  // ROUTER_SKINNY, ROUTER_SMALL or ROUTER_TILED
 };
@@ -121,18 +124,44 @@ static int router_kind(int T, int d)
     return T >= ROUTER_TILE_MIN_T && d % 64 == 0 ? ROUTER_TILED : ROUTER_SMALL;
 }
 
-// The FP6X2 precision has the 256-row tile only. It takes it when asked to
-// (MOE_SCHED_TILE256) or, with the schedule left to the library (AUTO or
-// TILED), from a mean of 128 rows per local expert over the row bound T k:
-// EP share (16384 x 16 rows over 112 experts, 24175 local) 1.03 ms against
-// 1.09 ms on the bf16 path's 128-row tiles. Below that, and for the other
-// schedules, the layer runs the bf16 path.
+// The FP6X2 precision runs on 256- or 128-row tiles. It takes them when asked
+// to (MOE_SCHED_TILE256 or TILE128: both projections on those tiles) or, with
+// the schedule left to the library (AUTO or TILED), from a mean of 128 rows
+// per local expert over the row bound T k: EP share (16384 x 16 rows over 112
+// experts, 24175 local) 1.03 ms against 1.09 ms on the bf16 path's 128-row
+// tiles. Below that, and for the streaming schedule, the layer runs the bf16
+// path.
 static bool fp6x2_layer(const moe_layer_params *p)
 {
     if (p->precision != MOE_PREC_FP6X2 || p->d > 4096 || p->I > 4096) return false;
-    if (p->mode == MOE_SCHED_TILE256) return true;
+    if (p->mode == MOE_SCHED_TILE256 || p->mode == MOE_SCHED_TILE128) return true;
     if (p->mode != MOE_SCHED_AUTO && p->mode != MOE_SCHED_TILED) return false;
     return (int64_t)p->T * p->k >= 128 * (int64_t)p->num_local;
+}
+
+// FP6X2 tiles per projection under AUTO / TILED. The 128-row tile lets two
+// workgroups share a CU, so one's prologue, epilogue and launch overlap the
+// other's K loop; it costs a second read of an expert's weights for each extra
+// row tile. Measured (ms, 256-row -> 128-row tiles):
+//   down, I = 1024: prefill 0.944 -> 0.895, EP share 0.180 -> 0.150. Taken
+//     whenever I <= 1024 (three stages still fit two workgroups per CU);
+//   gate/up: EP share 0.291 -> 0.257, but prefill 1.405 -> 1.598 (146-row
+//     experts become a 128-row and an 18-row tile, each streaming the
+//     weights) and long skewed 18.70 -> 18.71-18.83. Taken when the 256-row
+//     grid, estimated from the expected local rows T k num_local / E under
+//     uniform routing, gives fewer than 16 workgroups per CU (256 CUs): there
+//     the finer grid also shortens the tail.
+static void fp6x2_tiles(const moe_layer_params *p, bool *gu128, bool *dn128)
+{
+    if (p->mode == MOE_SCHED_TILE256 || p->mode == MOE_SCHED_TILE128) {
+        *gu128 = *dn128 = p->mode == MOE_SCHED_TILE128;
+        return;
+    }
+    const double rows = (double)p->T * p->k * p->num_local / p->E;
+    const double per_expert = rows / p->num_local;
+    const double wg = (double)p->num_local * std::ceil(per_expert / 256.0) * ((p->I + 127) / 128);
+    *gu128 = wg < 16.0 * 256.0;
+    *dn128 = p->I <= 1024;
 }
 
 LayerWs layer_ws(const moe_layer_params *p)
@@ -157,11 +186,17 @@ LayerWs layer_ws(const moe_layer_params *p)
     L.gws = o;
     const bool mx8 = p->precision == MOE_PREC_MX8;
     L.f6 = fp6x2_layer(p);
+    if (L.f6) fp6x2_tiles(p, &L.gu128, &L.dn128);
     o += round_up(mx8  ? mx8_gemm_ws_bytes(p->num_local, (int)A)
-                  : L.f6 ? grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, MOE_SCHED_TILE256)
+                  : L.f6 ? grouped_gemm_ws_bytes(p->num_local, (int)A, p->I,
+                                                 L.gu128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256)
                          : grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
     // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
     // from there to MXFP8 (hq, hs)
+    L.gws2 = o;
+    if (L.f6 && L.gu128 != L.dn128)
+        o += round_up(grouped_gemm_ws_bytes(p->num_local, (int)A, p->d,
+                                            L.dn128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256));
     L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
     if (L.f6) {
         L.xf = o;  o += round_up(T * (size_t)p->d * 2);
@@ -567,9 +602,12 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
     if (ev) HIP_TRY(hipEventRecord(ev[1], s));
     int32_t *counts = nullptr;
     // one work plan serves both projections (same offsets, bound and schedule;
-    // the FP6X2 projections take 256-row groups)
+    // the FP6X2 gate/up takes 256- or 128-row groups, and a down projection on
+    // the other tile gets a plan of its own)
     const GemmPlanArgs plan =
-        gemm_plan_args(p->num_local, A, L.f6 ? MOE_SCHED_TILE256 : p->mode, base + L.gws);
+        gemm_plan_args(p->num_local, A,
+                       L.f6 ? (L.gu128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256) : p->mode,
+                       base + L.gws);
     if (p->precision == MOE_PREC_MX8) {
         const GemmPlanArgs pm = mx8_plan_args(p->num_local, A, p->mode, base + L.gws);
         HIP_TRY(launch_permute(idx, counts, p->T, p->k, p->expert_begin, p->num_local, off, perm,
@@ -616,7 +654,7 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
         HIP_TRY(launch_gemm_fp6x2_run(xf, p->d, perm, gate_codes, gate_scales, up_codes,
                                       up_scales, p->num_local, A, p->I, p->d, p->act,
                                       base + L.hf, F6_OUT_RECORDS, p->I, base + L.gws, packed,
-                                      s));
+                                      s, nullptr, L.gu128));
     } else {
         HIP_TRY(launch_gemm_run((const bf16 *)x, p->d, perm, gate_codes, gate_scales, up_codes,
                                 up_scales, p->num_local, A, p->I, p->d, p->act, h, 0, p->I,
@@ -629,10 +667,17 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
     int16_t *yq = (int16_t *)y;
     uint8_t *ys = (uint8_t *)(base + L.y) + (size_t)A * p->d * 2;
     if (L.f6) {
+        const bool own_plan = L.gu128 != L.dn128;
+        if (own_plan)
+            HIP_TRY(launch_gemm_plan_into(
+                off, p->num_local,
+                gemm_plan_args(p->num_local, A, L.dn128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256,
+                               base + L.gws2), s));
         HIP_TRY(launch_gemm_fp6x2_run((const uint8_t *)(base + L.hf), p->I, nullptr,
                                       down_codes, down_scales, nullptr, nullptr, p->num_local, A,
                                       p->d, p->I, MOE_ACT_NONE, yq, F6_OUT_Q16, p->d,
-                                      base + L.gws, packed, s, ys));
+                                      base + (own_plan ? L.gws2 : L.gws), packed, s, ys,
+                                      L.dn128));
     } else {
         HIP_TRY(launch_gemm_run(h, p->I, nullptr, down_codes, down_scales, nullptr, nullptr,
                                 p->num_local, A, p->d, p->I, MOE_ACT_NONE, y, 1, p->d, p->mode,

@@ -254,9 +254,12 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // ---------------------------------------------------------------------------
 // Grouped projection on the block-scaled matrix cores, 256-row tiles.
 //
-// Workgroup tile: up to 256 permuted rows of one expert (a work item of the
-// 256-row plan) x 256 weight rows, K step 64 (two MX blocks, one 128-byte
-// record of a split row), 16 waves (4 per SIMD). Wave w: row block q = w / 4
+// Workgroup tile: up to 16 NW permuted rows of one expert (a work item of the
+// 256- or 128-row plan) x 256 weight rows, K step 64 (two MX blocks, one
+// 128-byte record of a split row), NW waves: 16 (one workgroup per CU), or 8
+// with 128-row tiles, whose 80 KB of LDS and at most 128 VGPRs let two
+// workgroups share a CU, so that one's prologue, epilogue and launch overlap
+// the other's K loop. Wave w: row block q = w / 4
 // (row tiles 2 q, 2 q + 1 of 32) and slot c = w % 4 (gate and up rows of
 // output columns 32 c .. + 32, or weight rows 64 c .. + 64); per K step and
 // (row tile, weight tile) two 32 x 32 x 64 MFMAs, one per plane, into the
@@ -270,9 +273,12 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 //     MX block g.
 //
 // LDS: a three-stage ring filled by global_load_lds_dwordx4 (each stage:
-// 256 rows x 128 bytes of records, 256 weight rows x 32 code bytes), one
+// 16 NW rows x 128 bytes of records, 256 weight rows x 32 code bytes), one
 // barrier per K step publishing step k and freeing the stage that step k + 2
-// overwrites; the tile's weight scales (256 x K / 32 bytes) loaded once, in
+// overwrites (128-row tiles whose weight scales leave no room for a third
+// stage in 80 KB, K > 1024: two stages, loads one step ahead, the barrier
+// publishing step k and freeing the stage step k + 1 overwrites); the tile's
+// weight scales (256 x K / 32 bytes) loaded once, in
 // the streaming layout's order (16 groups of 16 weight rows, each group as
 // the layout stores it), by the same DMA ahead of the first two stages. Chunk c (16 bytes) of a row's record
 // sits at position c ^ ((r / 2) % 8), so the 16 rows of a 16-lane read
@@ -282,11 +288,10 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // sat at bytes 0 and 48).
 // ---------------------------------------------------------------------------
 constexpr int F6_BN = 256, F6_BK = 64, F6_ROW = 128;
-constexpr int F6_STAGES = 3;
-constexpr int F6_A_BYTES = 256 * F6_ROW;         // 32 KB of records
 constexpr int F6_W_BYTES = F6_BN * F6_BK / 2;    // 8 KB of E2M1 codes
-constexpr int F6_STAGE = F6_A_BYTES + F6_W_BYTES;
-constexpr int F6_THREADS = 1024;
+// NW waves: 16 (256-row tiles, 32 KB of records per stage) or 8 (128-row tiles)
+__host__ __device__ constexpr int f6_a_bytes(int NW) { return 16 * NW * F6_ROW; }
+__host__ __device__ constexpr int f6_stage(int NW) { return f6_a_bytes(NW) + F6_W_BYTES; }
 constexpr int F6_MAX_K = 4096;
 
 // Weight scales of 16 weight rows in the streaming layout: K / 512 groups
@@ -297,15 +302,19 @@ __host__ __device__ constexpr int f6_scale_chunk(int K)
 }
 
 // the epilogue's staging: per wave 64 rows of up to 256 bytes, padded by 16
-constexpr int F6_EPI_PITCH = 144, F6_EPI_BYTES = 16 * 64 * F6_EPI_PITCH;
+constexpr int F6_EPI_PITCH = 144;
+// LDS per workgroup that lets two 128-row workgroups share a CU's 160 KB
+constexpr int F6_LDS_HALF = 80 * 1024;
 
-__host__ __device__ constexpr int f6_lds_bytes(int K)
+__host__ __device__ constexpr int f6_lds_bytes(int K, int NW, int STG)
 {
-    return F6_STAGES * F6_STAGE + 16 * f6_scale_chunk(K) > F6_EPI_BYTES
-               ? F6_STAGES * F6_STAGE + 16 * f6_scale_chunk(K)
-               : F6_EPI_BYTES;
+    return STG * f6_stage(NW) + 16 * f6_scale_chunk(K) > NW * 64 * F6_EPI_PITCH
+               ? STG * f6_stage(NW) + 16 * f6_scale_chunk(K)
+               : NW * 64 * F6_EPI_PITCH;
 }
-static_assert(f6_lds_bytes(F6_MAX_K) <= 160 * 1024, "LDS of the FP6X2 tile");
+static_assert(f6_lds_bytes(F6_MAX_K, 16, 3) <= 160 * 1024, "LDS of the FP6X2 tile");
+static_assert(f6_lds_bytes(1024, 8, 3) <= F6_LDS_HALF, "three stages of 128 rows at K <= 1024");
+static_assert(f6_lds_bytes(F6_MAX_K, 8, 2) <= F6_LDS_HALF, "two stages of 128 rows at any K");
 
 // Output kinds of the projection: OutT = float or bf16 rows, uint8_t for
 // split records (the next projection's input, written as moe_fp6x2_split
@@ -320,8 +329,8 @@ constexpr bool f6_records = std::is_same<OutT, uint8_t>::value;
 template <typename OutT>
 constexpr bool f6_q16 = std::is_same<OutT, int16_t>::value;
 
-template <int ACT, typename OutT, bool PACKED>
-__global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
+template <int ACT, typename OutT, bool PACKED, int NW, int F6_STAGES>
+__global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
     const uint8_t *__restrict__ ad, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
@@ -333,6 +342,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     static_assert(!(GLU && f6_q16<OutT>), "block-int16 rows come from the down projection");
     extern __shared__ __attribute__((aligned(16))) uint8_t f6_lds[];
     const int chunk_b = f6_scale_chunk(K);
+    constexpr int F6_THREADS = NW * 64, F6_A_BYTES = f6_a_bytes(NW), F6_STAGE = f6_stage(NW);
     uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [16][chunk_b] weight scales
 
     const int nblk = (N + COLS - 1) / COLS;
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
         }
     }
     issue(0, 0);
-    issue(1, 1);
+    if constexpr (F6_STAGES == 3) issue(1, 1);
 
     // ---- wave tiles
     const int h = lane >> 5, l32 = lane & 31;
@@ -526,14 +536,25 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
             // codes issues three per step and so waits for one of kt + 1's
             // too: one wait for every wave, no branch); the barrier publishes
             // every wave's and ends the reads of step kt - 1
-            if (kt + 1 < nk) {
-                asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // (two stages: only step kt's loads are in flight, all waited for;
+            // with 8 waves every wave issues three loads per step)
+            if (F6_STAGES == 3 && kt + 1 < nk) {
+                if constexpr (NW == 8)
+                    asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             } else {
                 asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
-            const int st = kt % 3;
-            if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
-            compute(st, kt);
+            if constexpr (F6_STAGES == 3) {
+                const int st = kt % 3;
+                if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
+                compute(st, kt);
+            } else {
+                const int st = kt & 1;
+                if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+                compute(st, kt);
+            }
         }
 
         // Epilogue through LDS (the ring is idle once every wave is past its
@@ -666,8 +687,8 @@ __global__ __launch_bounds__(F6_THREADS, 1) void gemm_fp6x2_w16_kernel(
     }
 }
 
-template <int ACT, typename OutT, bool PACKED>
-static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
+template <int ACT, typename OutT, bool PACKED, int NW>
+static hipError_t launch_f6_nw(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                             const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                             const uint8_t *w2s, const int32_t *plan,
                             int max_groups, int hdr, int N, int K, OutT *out, int64_t ldo,
@@ -679,10 +700,16 @@ static hipError_t launch_f6(const uint8_t *ad, int64_t lda, const int32_t *a_row
     // the XCD-aware order maps block b to work (b % 8) * ceil(total / 8) + b / 8;
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
-    auto kern = gemm_fp6x2_w16_kernel<ACT, OutT, PACKED>;
-    const hipError_t err = ensure_dynamic_lds((const void *)kern, f6_lds_bytes(K));
+    // 128-row tiles: three stages where two workgroups still fit a CU, else
+    // two (S2 keeps the 16-wave kernel on three stages only)
+    constexpr int S2 = NW == 8 ? 2 : 3;
+    const bool three = NW == 16 || f6_lds_bytes(K, NW, 3) <= F6_LDS_HALF;
+    auto kern = three ? gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, 3>
+                      : gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, S2>;
+    const int lds = f6_lds_bytes(K, NW, three ? 3 : 2);
+    const hipError_t err = ensure_dynamic_lds((const void *)kern, lds);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(F6_THREADS), f6_lds_bytes(K), s, ad, lda,
+    hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(NW * 64), lds, s, ad, lda,
                        a_rows, w1c, w1s, w2c, w2s, plan, hdr, N, K, out, ldo, osc);
     return hipGetLastError();
 }
@@ -692,17 +719,22 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
                                  const uint8_t *w2s, int num_local, int max_rows, int N, int K,
                                  int act, void *out, int out_kind, int64_t ldo,
                                  const void *plan_ws, int packed, hipStream_t s,
-                                 uint8_t *out_scales)
+                                 uint8_t *out_scales, int rows128)
 {
     if (K % 128 != 0 || K > F6_MAX_K) return hipErrorInvalidValue;
     if (out_kind == F6_OUT_RECORDS && act == ACT_NONE) return hipErrorInvalidValue;
     if (out_kind == F6_OUT_Q16 && (act != ACT_NONE || out_scales == nullptr || ldo % 32 != 0))
         return hipErrorInvalidValue;
-    const GemmPlanArgs pa = gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, nullptr);
+    const GemmPlanArgs pa =
+        gemm_plan_args(num_local, max_rows, rows128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256, nullptr);
+    if (rows128 && out_kind != F6_OUT_Q16 && out_kind != F6_OUT_RECORDS) return hipErrorInvalidValue;
     const int32_t *plan = (const int32_t *)plan_ws;
 #define F6_LAUNCH(A, OT, PK)                                                                   \
-    return launch_f6<A, OT, PK>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,      \
-                                pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
+    return launch_f6_nw<A, OT, PK, 16>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,  \
+                                    pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
+#define F6_LAUNCH8(A, OT, PK)                                                                  \
+    return launch_f6_nw<A, OT, PK, 8>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,   \
+                                   pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
 #define F6_GLU(OT, PK)                                                                         \
     switch (act) {                                                                             \
     case ACT_SILU_MUL: F6_LAUNCH(ACT_SILU_MUL, OT, PK);                                       \
@@ -714,6 +746,17 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
         if (act == ACT_NONE) F6_LAUNCH(ACT_NONE, OT, PK);                                      \
         F6_GLU(OT, PK)                                                                         \
     }
+    if (out_kind == F6_OUT_RECORDS && rows128) {
+        switch (act) {
+        case ACT_SILU_MUL:
+            if (packed) F6_LAUNCH8(ACT_SILU_MUL, uint8_t, true);
+            F6_LAUNCH8(ACT_SILU_MUL, uint8_t, false);
+        case ACT_GELU_TANH_MUL:
+            if (packed) F6_LAUNCH8(ACT_GELU_TANH_MUL, uint8_t, true);
+            F6_LAUNCH8(ACT_GELU_TANH_MUL, uint8_t, false);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (out_kind == F6_OUT_RECORDS) {
         if (packed) F6_GLU(uint8_t, true)
         F6_GLU(uint8_t, false)
@@ -721,6 +764,10 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
     if (out_kind == F6_OUT_F32) {
         if (packed) F6_ANY(float, true)
         F6_ANY(float, false)
+    }
+    if (out_kind == F6_OUT_Q16 && rows128) {
+        if (packed) F6_LAUNCH8(ACT_NONE, int16_t, true);
+        F6_LAUNCH8(ACT_NONE, int16_t, false);
     }
     if (out_kind == F6_OUT_Q16) {
         if (packed) F6_LAUNCH(ACT_NONE, int16_t, true);
@@ -731,6 +778,7 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
 #undef F6_ANY
 #undef F6_GLU
 #undef F6_LAUNCH
+#undef F6_LAUNCH8
 }
 
 hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
@@ -744,7 +792,7 @@ hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32
         off, num_local, gemm_plan_args(num_local, max_rows, MOE_SCHED_TILE256, ws), s);
     if (e != hipSuccess) return e;
     return launch_gemm_fp6x2_run(ad, lda, a_rows, w1c, w1s, w2c, w2s, num_local, max_rows, N,
-                                 K, act, out, out_kind, ldo, ws, packed, s);
+                                 K, act, out, out_kind, ldo, ws, packed, s, nullptr, 0);
 }
 
 }  // namespace moe

@@ -149,7 +149,10 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
                               uint8_t *out, int64_t ldo, hipStream_t s,
                               const int32_t *n_dev = nullptr);
 // The 256-row tile from a 256-row work plan (MOE_SCHED_TILE256) already built
-// in plan_ws; K % 128 == 0, K <= 4096 (hipErrorInvalidValue otherwise).
+// in plan_ws, or with rows128 the 128-row tile (two workgroups per CU) from a
+// 128-row plan (MOE_SCHED_TILE128; records and block-int16 outputs only);
+// K % 128 == 0, K <= 4096 (hipErrorInvalidValue otherwise). Each output
+// element is the same either way.
 // Output kinds: bf16 or fp32 rows [rows][ldo]; (GLU only) split records of
 // the fp32 results, row r at out + 2 r ldo bytes, as launch_fp6x2_split
 // writes them; (no activation only) block-int16 rows: int16 [rows][ldo] and
@@ -162,7 +165,7 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
                                  const uint8_t *w2s, int num_local, int max_rows, int N, int K,
                                  int act, void *out, int out_kind, int64_t ldo,
                                  const void *plan_ws, int packed, hipStream_t s,
-                                 uint8_t *out_scales = nullptr);
+                                 uint8_t *out_scales = nullptr, int rows128 = 0);
 hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                                      const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                                      const uint8_t *w2s, const int32_t *off, int num_local,

@@ -271,8 +271,9 @@ def test_small_layer_fp6x2_vs_oracle(m, cfg, packed):
                                                        bias="normal")], ids=lambda c: c.name)
 def test_auto_schedule_takes_fp6x2(m, cfg):
     """With the schedule left to the library and a mean of 128 or more rows
-    per local expert over the row bound, the FP6X2 layer takes its 256-row
-    tiles (bitwise the explicit choice), here also on a local expert range."""
+    per local expert over the row bound, the FP6X2 layer runs (bitwise the
+    explicit 256-row choice, whatever tiles it picks per projection), here
+    also on a local expert range."""
     inp = make_inputs(cfg).to(DEV)
     a = run_gpu_layer(inp, precision=m.PREC_FP6X2, out_dtype=torch.float32)
     b = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256, out_dtype=torch.float32)
@@ -363,6 +364,32 @@ def test_fp6x2_layer_determinism_bitwise(m):
     b = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE256)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("cfg,act,packed", [
+    # K = 512 and 256: three-stage rings on both tile heights
+    (LayerConfig("h0", T=700, I=256, d=512, E=24, k=6, bias="normal"), 1, False),
+    # K = 1536 (gate/up) and 2048 (down): two stages on 128-row tiles
+    (LayerConfig("h1", T=600, I=2048, d=1536, E=16, k=4, expert_begin=4, num_local=8), 1, True),
+    # K = 3584 (two stages) and 1024 (three), about 300 rows per expert
+    (LayerConfig("h2", T=1200, I=1024, d=3584, E=16, k=4, bias="normal"), 2, True),
+], ids=lambda v: v.name if isinstance(v, LayerConfig) else str(v))
+def test_fp6x2_layer_tile_heights_bitwise(m, cfg, act, packed):
+    """An output element is the same sum on 256- and 128-row tiles (the same
+    K steps and planes in the same order; the tile only decides which
+    workgroup computes it): the layer on 128-row tiles (8 waves, two
+    workgroups per CU, a two-stage ring where three do not fit 80 KB), on
+    256-row tiles and under the automatic per-projection choice agree bit for
+    bit, records, block-int16 rows and all."""
+    inp = make_inputs(cfg).to(DEV)
+    pw = m.prepack_weights(inp.weights) if packed else None
+    runs = [run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=md, act=act, packed=pw,
+                          out_dtype=torch.float32)
+            for md in (m.MODE_TILE256, m.MODE_TILE128, m.MODE_AUTO)]
+    assert runs[0]["out"].abs().max() > 0
+    for r in runs[1:]:
+        for key in r:
+            assert torch.equal(r[key], runs[0][key]), key
 
 
 def test_fp6x2_streaming_shapes_are_the_bf16_layer(m):
