@@ -46,7 +46,7 @@ def parse():
                     help="GEMM schedule (enum moe_sched): 0 auto, 1 stream, 2 tiled, "
                          "3 128-row tiles, 4 256-row tiles")
     ap.add_argument("--precision", default="fp6x2", choices=["fp6x2", "bf16", "mx8"],
-                    help="fp6x2 (default): where the schedule takes 256-row tiles, both "
+                    help="fp6x2 (default): where the schedule tiles the rows, both "
                          "projections take their activations (the bf16 tokens, h from fp32) as "
                          "two MXFP6 planes on the block-scaled fp6 x fp4 instruction, within "
                          "the layer's accuracy contract and nearer the oracle than bf16; "
@@ -350,11 +350,12 @@ def main():
     U = int((counts > 0).sum())
     lb, lf, gb, gf = algorithmic(cfg, A, U, out_bytes=4)
 
-    # The layer's FP6X2 rule: 256-row tiles when asked to, or from a mean of
-    # 128 rows per local expert over the row bound T k (else the bf16 path).
+    # The layer's FP6X2 rule: 256- or 128-row tiles when asked to, or from a
+    # mean of 128 rows per local expert over the row bound T k (else the bf16
+    # path).
     f6_layer = f6 and cfg.d <= 4096 and cfg.I <= 4096 and (
-        args.mode == m.MODE_TILE256 or (args.mode in (m.MODE_AUTO, m.MODE_TILED) and
-                                        cfg.T * cfg.k >= 128 * cfg.num_local))
+        args.mode in (m.MODE_TILE256, m.MODE_TILE128) or
+        (args.mode in (m.MODE_AUTO, m.MODE_TILED) and cfg.T * cfg.k >= 128 * cfg.num_local))
     # The dominant kernel is the gate/up projection: weight streaming (HBM
     # bound) for few rows per expert, a tiled GEMM (MFMA bound) otherwise.
     gu_s = stage_ms["gate_up"] / 1e3
