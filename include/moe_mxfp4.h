@@ -141,7 +141,9 @@ int moe_route(const void *x, const float *w_router, const float *bias, float *lo
  *
  *   topk_idx [T][k] int32, expert_counts [E] int32  (from moe_route; or
  *            NULL: each local expert's rows are then counted from topk_idx,
- *            with no atomics, which suits heavily skewed routing)
+ *            with no atomics, which suits heavily skewed routing; above 256
+ *            tokens they are counted from topk_idx either way, which gives
+ *            the same offsets for a histogram of topk_idx)
  *   local experts are ids [expert_begin, expert_begin + num_local)
  *   expert_offsets [num_local + 1] int32 (out): off[0] = 0,
  *                  off[i+1] = off[i] + expert_counts[expert_begin + i]

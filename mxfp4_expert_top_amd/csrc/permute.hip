@@ -9,8 +9,10 @@
 // built with integer ORs (order-independent). Popcounts of the bitmap give
 // (a) each block's per-expert count, and (b) each assignment's rank among the
 // earlier tokens of its block. A column scan over blocks turns (a) into each
-// block's base row per expert. No step depends on atomic ordering, so the
-// permutation is the same on every run.
+// block's base row per expert (relative to the expert's first row) and the
+// expert's total; every scatter block scans the totals for the experts' first
+// rows. No step depends on atomic ordering, so the permutation is the same on
+// every run.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -51,59 +53,94 @@ __global__ __launch_bounds__(PERM_TB) void permute_count_kernel(
     }
 }
 
-// One workgroup: offsets over the local range, then per expert a scan of the
-// block counts (in place: blk[b][e] becomes block b's first row for e).
-// Expert counts come from `counts` (the histogram) or, when it is NULL, from
-// the block counts themselves. Loading one block count at a time, each load
-// behind the previous store, took 93 us at 256 blocks; one wave per expert
-// (lanes over blocks) was slower still, 16 waves walking 896 experts.
-__global__ __launch_bounds__(1024) void permute_scan_kernel(
-    const int32_t *__restrict__ counts, int e0, int nl, int nblk, int32_t *__restrict__ off,
-    int32_t *__restrict__ blk)
+// Column scan over the blocks, many workgroups: workgroup x takes local
+// experts 64 x .. 64 x + 63 and 16 thread groups, group g summing a
+// contiguous run of the blocks (loads coalesced across the 64 experts, 16 of a
+// run in flight at a time); the runs' sums meet in LDS. In place, blk[b][e]
+// becomes block b's first row for expert e counted from the expert's first
+// row, and tot[e] the expert's rows. (One workgroup scanning every expert's
+// column took 81 us at 256 blocks, its per-expert chain of loads being the
+// whole kernel.)
+constexpr int CS_E = 64, CS_G = 16, CS_CHUNK = 16;
+
+__global__ __launch_bounds__(CS_E * CS_G) void permute_colscan_kernel(int nl, int nblk,
+                                                                      int32_t *__restrict__ blk,
+                                                                      int32_t *__restrict__ tot)
 {
-    __shared__ int32_t part[16];
-    const int tid = threadIdx.x;
-    // each thread owns a contiguous run of at most two experts (nl <= 2048)
-    const int per = (nl + 1023) / 1024;
-    const int lo = tid * per, hi = min(lo + per, nl);
-    auto count = [&](int i) {
-        if (counts) return counts[e0 + i];
-        int c = 0;
-        for (int b = 0; b < nblk; b++) c += blk[(int64_t)b * nl + i];
-        return c;
-    };
-    const int c0 = lo < hi ? count(lo) : 0, c1 = lo + 1 < hi ? count(lo + 1) : 0;
-    int total;
-    const int run = block_exclusive_scan(c0 + c1, part, total);  // exclusive prefix of the run
-    if (lo < hi) off[lo] = run;
-    if (lo + 1 < hi) off[lo + 1] = run + c0;
-    if (tid == 0) off[nl] = total;
-    __syncthreads();
-    // thread per expert (loads coalesce across experts); each chunk of block
-    // counts is loaded before its stores, so 16 loads are in flight per wait
-    for (int le = tid; le < nl; le += 1024) {
-        int r = off[le];
-        for (int b0 = 0; b0 < nblk; b0 += 16) {
-            int c[16];
+    __shared__ int32_t part[CS_G][CS_E];
+    const int el = threadIdx.x % CS_E, g = threadIdx.x / CS_E;
+    const int e = blockIdx.x * CS_E + el;
+    const int per = (nblk + CS_G - 1) / CS_G;
+    const int b0 = min(g * per, nblk), b1 = min(b0 + per, nblk);
+    int sum = 0;
+    if (e < nl)
+        for (int c = b0; c < b1; c += CS_CHUNK) {
+            int v[CS_CHUNK];
 #pragma unroll
-            for (int i = 0; i < 16; i++) c[i] = b0 + i < nblk ? blk[(int64_t)(b0 + i) * nl + le] : 0;
+            for (int i = 0; i < CS_CHUNK; i++)
+                v[i] = c + i < b1 ? blk[(int64_t)(c + i) * nl + e] : 0;
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                if (b0 + i < nblk) {
-                    blk[(int64_t)(b0 + i) * nl + le] = r;
-                    r += c[i];
-                }
+            for (int i = 0; i < CS_CHUNK; i++) sum += v[i];
         }
+    part[g][el] = sum;
+    __syncthreads();
+    int run = 0, all = 0;
+#pragma unroll
+    for (int h = 0; h < CS_G; h++) {
+        const int t = part[h][el];
+        run += h < g ? t : 0;
+        all += t;
+    }
+    if (e >= nl) return;
+    if (g == 0) tot[e] = all;
+    // the run's counts again (its own, unchanged so far), then its bases
+    for (int c = b0; c < b1; c += CS_CHUNK) {
+        int v[CS_CHUNK];
+#pragma unroll
+        for (int i = 0; i < CS_CHUNK; i++) v[i] = c + i < b1 ? blk[(int64_t)(c + i) * nl + e] : 0;
+#pragma unroll
+        for (int i = 0; i < CS_CHUNK; i++)
+            if (c + i < b1) {
+                blk[(int64_t)(c + i) * nl + e] = run;
+                run += v[i];
+            }
     }
 }
 
 __global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
     const int32_t *__restrict__ idx, int T, int k, int e0, int nl,
-    const int32_t *__restrict__ base, int32_t *__restrict__ perm, int32_t *__restrict__ inv)
+    const int32_t *__restrict__ base, const int32_t *__restrict__ tot, int32_t *__restrict__ off,
+    int32_t *__restrict__ perm, int32_t *__restrict__ inv)
 {
     extern __shared__ uint32_t bits[];
+    __shared__ int32_t part[16];
+    __shared__ int32_t soff[MOE_MAX_EXPERTS_DEV];
     const int t0 = blockIdx.x * PERM_TB;
-    build_bitmap(bits, idx, T, k, e0, nl, t0);
+    // the local experts' first rows: an exclusive scan of their totals, each
+    // thread owning a run of at most 8 consecutive experts (nl <= 2048);
+    // block 0 also writes them out
+    {
+        constexpr int RUN = MOE_MAX_EXPERTS_DEV / PERM_TB;
+        const int per = (nl + PERM_TB - 1) / PERM_TB;
+        const int lo = threadIdx.x * per;
+        int c[RUN], sum = 0;
+#pragma unroll
+        for (int i = 0; i < RUN; i++) {
+            c[i] = i < per && lo + i < nl ? tot[lo + i] : 0;
+            sum += c[i];
+        }
+        int total;
+        int run = block_exclusive_scan(sum, part, total);
+#pragma unroll
+        for (int i = 0; i < RUN; i++)
+            if (i < per && lo + i < nl) {
+                soff[lo + i] = run;
+                if (blockIdx.x == 0) off[lo + i] = run;
+                run += c[i];
+            }
+        if (blockIdx.x == 0 && threadIdx.x == 0) off[nl] = total;
+    }
+    build_bitmap(bits, idx, T, k, e0, nl, t0);  // its barriers publish soff
     const int tl = threadIdx.x, t = t0 + tl;
     if (t >= T) return;
     const int64_t cap = (int64_t)T * k;
@@ -122,7 +159,7 @@ __global__ __launch_bounds__(PERM_TB) void permute_scatter_kernel(
                 const uint32_t *row = bits + le * PERM_WORDS;
                 int rank = __popc(row[w] & below);
                 for (int i = 0; i < w; i++) rank += __popc(row[i]);
-                int64_t p = (int64_t)base[(int64_t)blockIdx.x * nl + le] + rank;
+                int64_t p = (int64_t)soff[le] + base[(int64_t)blockIdx.x * nl + le] + rank;
                 if (p >= 0 && p < cap) {
                     pos = (int)p;
                     perm[pos] = t;
@@ -222,9 +259,10 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     if (tid == 0) plan[0] = min(ngroups, max_groups);
 }
 
+// block counts [blocks][num_local], then the experts' totals [num_local]
 size_t permute_ws_bytes(int T, int num_local)
 {
-    size_t n = (size_t)perm_blocks(T) * (size_t)num_local * sizeof(int32_t);
+    size_t n = ((size_t)perm_blocks(T) + 1) * (size_t)num_local * sizeof(int32_t);
     return (n + 255) & ~(size_t)255;
 }
 
@@ -234,6 +272,7 @@ hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int 
 {
     const int nblk = perm_blocks(T);
     int32_t *blk = (int32_t *)ws;
+    int32_t *tot = blk + (size_t)nblk * num_local;
     const size_t lds = (size_t)num_local * PERM_WORDS * sizeof(uint32_t);
     hipError_t e;
     if (nblk == 1 && num_local <= 1024) {  // bitmap <= 32 KB of LDS
@@ -244,20 +283,24 @@ hipError_t launch_permute(const int32_t *idx, const int32_t *counts, int T, int 
                            plan ? plan->hdr : 0);
         return hipGetLastError();
     }
+    // (more than one block: the rows are counted from the dispatch bitmaps,
+    // which give the histogram's offsets for any consistent `counts`)
     if (nblk > 0) {
         hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k, e0,
                            num_local, blk);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, counts, e0, num_local,
-                       nblk, off, blk);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (nblk > 0) {
-        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k,
-                           e0, num_local, (const int32_t *)blk, perm, inv);
+        hipLaunchKernelGGL(permute_colscan_kernel, dim3((num_local + CS_E - 1) / CS_E),
+                           dim3(CS_E * CS_G), 0, s, num_local, nblk, blk, tot);
         e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(PERM_TB), lds, s, idx, T, k,
+                           e0, num_local, (const int32_t *)blk, (const int32_t *)tot, off, perm,
+                           inv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        e = launch_fill_i32(off, (int64_t)num_local + 1, 0, s);  // no tokens: no rows
         if (e != hipSuccess) return e;
     }
     if (plan) return launch_gemm_plan_into(off, num_local, *plan, s);
