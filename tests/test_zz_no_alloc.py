@@ -15,11 +15,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_noalloc(inp, packed, out_dtype):
+def _run_noalloc(inp, packed, out_dtype, precision=m.PREC_BF16, mode=m.MODE_AUTO):
     c = inp.cfg
     p = m.layer_params(c.T, c.d, c.E, c.k, c.I, c.expert_begin, c.num_local,
                        out_dtype=m.DT_F32 if out_dtype == torch.float32 else m.DT_BF16,
-                       weight_layout=m.LAYOUT_PACKED)
+                       mode=mode, weight_layout=m.LAYOUT_PACKED, precision=precision)
     assert m.moe_layer_workspace_size(p) <= m.NOALLOC_SCRATCH_BYTES
     out = torch.empty(c.T, c.d, dtype=out_dtype, device=DEV)
     logits = torch.empty(c.T, c.E, dtype=torch.float32, device=DEV)
@@ -42,6 +42,25 @@ def test_noalloc_equals_moe_layer_two_calls(first, second):
         packed = m.prepack_weights(inp.weights)
         a = _run_noalloc(inp, packed, dt)
         b = run_gpu_layer(inp, packed=packed, out_dtype=dt)
+        for key in ("idx", "w", "logits", "out"):
+            assert torch.equal(a[key], b[key]), (cfg.name, key)
+        assert bool((a["out"] != 0).any())
+        del inp, packed, a, b
+        torch.cuda.empty_cache()
+
+
+def test_noalloc_fp6x2_two_calls():
+    """The FP6X2 layer through the same entry: 128 tokens on 128-row tiles,
+    then 64 tokens on 256-row tiles over a local expert range, each bitwise
+    equal to moe_layer's output and routing."""
+    calls = ((LayerConfig("nf0", T=128, I=256), m.MODE_TILE128, torch.float32),
+             (LayerConfig("nf1", T=64, I=256, expert_begin=100, num_local=300, bias="normal"),
+              m.MODE_TILE256, torch.bfloat16))
+    for cfg, mode, dt in calls:
+        inp = make_inputs(cfg, DEV)
+        packed = m.prepack_weights(inp.weights)
+        a = _run_noalloc(inp, packed, dt, precision=m.PREC_FP6X2, mode=mode)
+        b = run_gpu_layer(inp, packed=packed, out_dtype=dt, precision=m.PREC_FP6X2, mode=mode)
         for key in ("idx", "w", "logits", "out"):
             assert torch.equal(a[key], b[key]), (cfg.name, key)
         assert bool((a["out"] != 0).any())
