@@ -219,7 +219,10 @@ def test_router_scores_and_replay(m, T, d, E, bias):
                                          (1000, 64, 4, 16, 20), (5000, 896, 16, 0, 112),
                                          (700, 896, 16, 784, 112), (513, 32, 32, 0, 32),
                                          (200, 896, 16, 0, 896), (256, 64, 4, 8, 40),
-                                         (256, 1100, 16, 0, 1100), (300, 2048, 32, 0, 2048)])
+                                         (256, 1100, 16, 0, 1100), (300, 2048, 32, 0, 2048),
+                                         # 274 blocks: runs of 18 blocks per column
+                                         # scan thread group, two load chunks each
+                                         (70000, 64, 4, 8, 40)])
 @pytest.mark.parametrize("with_counts", [True, False])
 def test_permute_bitexact(m, T, E, k, e0, nl, with_counts):
     rng = np.random.default_rng(T + E + k)
