@@ -61,7 +61,7 @@ typedef void *moe_stream_t; /* hipStream_t */
 enum moe_status {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1, /* a size out of range or a required pointer NULL */
-    MOE_ERR_UNSUPPORTED = 2, /* a valid request this build does not handle     */
+    MOE_ERR_UNSUPPORTED = 2, /* a valid request the library does not handle    */
     MOE_ERR_WORKSPACE = 3,   /* ws smaller than the queried size, or misaligned */
     MOE_ERR_HIP = 4          /* a HIP runtime call or launch failed              */
 };
@@ -104,7 +104,7 @@ enum moe_sched {
     MOE_SCHED_TILE256 = 4
 };
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MOE_MX_BLOCK 32
 #define MOE_MAX_TOPK 32
 #define MOE_MAX_EXPERTS 2048

@@ -297,7 +297,7 @@ const char *moe_status_string(int status)
     switch (status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARG: return "invalid argument";
-    case MOE_ERR_UNSUPPORTED: return "unsupported by this build";
+    case MOE_ERR_UNSUPPORTED: return "unsupported by the library";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
