@@ -157,8 +157,8 @@ static void fp6x2_tiles(const moe_layer_params *p, bool *gu128, bool *dn128)
         *gu128 = *dn128 = p->mode == MOE_SCHED_TILE128;
         return;
     }
-    const double rows = (double)p->T * p->k * p->num_local / p->E;
-    const double per_expert = rows / p->num_local;
+    // expected rows per local expert under uniform routing: T k / E
+    const double per_expert = (double)p->T * p->k / p->E;
     const double wg = (double)p->num_local * std::ceil(per_expert / 256.0) * ((p->I + 127) / 128);
     *gu128 = wg < 16.0 * 256.0;
     *dn128 = p->I <= 1024;
@@ -191,12 +191,12 @@ LayerWs layer_ws(const moe_layer_params *p)
                   : L.f6 ? grouped_gemm_ws_bytes(p->num_local, (int)A, p->I,
                                                  L.gu128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256)
                          : grouped_gemm_ws_bytes(p->num_local, (int)A, p->I, p->mode));
-    // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
-    // from there to MXFP8 (hq, hs)
     L.gws2 = o;
     if (L.f6 && L.gu128 != L.dn128)
         o += round_up(grouped_gemm_ws_bytes(p->num_local, (int)A, p->d,
                                             L.dn128 ? MOE_SCHED_TILE128 : MOE_SCHED_TILE256));
+    // h: bf16 for the bf16 down projection; in the MX8 mode fp32, quantised
+    // from there to MXFP8 (hq, hs)
     L.h = o;      o += round_up(A * (size_t)p->I * (mx8 ? 4 : 2));
     if (L.f6) {
         L.xf = o;  o += round_up(T * (size_t)p->d * 2);
