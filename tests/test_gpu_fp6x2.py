@@ -118,7 +118,7 @@ def _split_rows(m, rng, R, K):
     return rec, oracle.fp6x2_value(rc, rs), vb.float().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("K", [128, 640, 3584])
 def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
@@ -164,9 +164,17 @@ def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
             w2 = oracle.mxfp4_decode(w2c[e].numpy(), w2s[e].numpy()).astype(np.float64)
             u = xa[r0:r1] @ w2.T
             bu = MMA_TOL * _bound(xa[r0:r1], w2)
-            h = g / (1.0 + np.exp(-g)) * u
-            # first-order propagation: |d silu/dg| <= 1.1, |silu(g)| <= |g| + 0.28
-            tol = 1.1 * np.abs(u) * bg + (np.abs(g) + 0.28) * bu + 1e-5 * np.abs(h) + 1e-30
+            if act == 1:
+                h = g / (1.0 + np.exp(-g)) * u
+                # first-order propagation: |d silu/dg| <= 1.1, |silu(g)| <= |g| + 0.28
+                dmax, off_ = 1.1, 0.28
+            else:
+                # GELU, tanh form: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)));
+                # |d gelu/dg| <= 1.129, |gelu(g)| <= |g|
+                c = np.sqrt(2.0 / np.pi)
+                h = 0.5 * g * (1.0 + np.tanh(c * (g + 0.044715 * g ** 3))) * u
+                dmax, off_ = 1.13, 0.0
+            tol = dmax * np.abs(u) * bg + (np.abs(g) + off_) * bu + 1e-5 * np.abs(h) + 1e-30
             assert (np.abs(got[r0:r1] - h) <= tol).all(), np.abs(got[r0:r1] - h).max()
 
 
