@@ -400,6 +400,24 @@ def test_fp6x2_layer_tile_heights_bitwise(m, cfg, act, packed):
             assert torch.equal(r[key], runs[0][key]), key
 
 
+@pytest.mark.parametrize("act", [1, 2])
+def test_fp6x2_layer_128_row_tiles_vs_oracle(m, act):
+    """The FP6X2 layer on 128-row tiles (MOE_SCHED_TILE128, both projections)
+    with SiLU and GELU-tanh against the oracle's layer of the same activation
+    on the GPU's scores, within the default contract."""
+    cfg = SMALL[4]
+    inp = make_inputs(cfg).to(DEV)
+    g = run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=m.MODE_TILE128, act=act,
+                      packed=m.prepack_weights(inp.weights), out_dtype=torch.float32)
+    lg = np_(g["logits"])
+    r_idx, _ = oracle.topk_softmax(lg, cfg.k)
+    assert np.array_equal(np_(g["idx"]), r_idx)
+    ref = oracle.layer(inp.x, np_(inp.w_router), None if inp.bias is None else np_(inp.bias),
+                       host_weights(inp.weights), E=cfg.E, k=cfg.k, I=cfg.I,
+                       e0=cfg.expert_begin, n_local=cfg.num_local, logits=lg, act=act)
+    assert_close_layer(np_(g["out"]), ref["out"], f"{cfg.name} act={act}")
+
+
 def test_fp6x2_streaming_shapes_are_the_bf16_layer(m):
     """Where the schedule streams the weights (few rows per expert) the FP6X2
     precision runs the bf16 kernels: bitwise the bf16 layer."""
