@@ -120,7 +120,7 @@ def _split_rows(m, rng, R, K):
 
 @pytest.mark.parametrize("act", [0, 1, 2])
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("K", [128, 640, 3584])
+@pytest.mark.parametrize("K", [128, 640, 3584, 4096])
 def test_grouped_gemm_fp6x2_vs_definition(m, act, packed, K):
     """Experts with 37, 0, 513, 1, 257 and 150 rows (empty, one row, ragged,
     several 256-row groups), a column count that is not a tile multiple,
@@ -381,6 +381,8 @@ def test_fp6x2_layer_determinism_bitwise(m):
     (LayerConfig("h1", T=600, I=2048, d=1536, E=16, k=4, expert_begin=4, num_local=8), 1, True),
     # K = 3584 (two stages) and 1024 (three), about 300 rows per expert
     (LayerConfig("h2", T=1200, I=1024, d=3584, E=16, k=4, bias="normal"), 2, True),
+    # K = 4096, the largest taken: 80 KB of LDS on 128-row tiles, 152 KB on 256
+    (LayerConfig("h3", T=300, I=2048, d=4096, E=4, k=2), 1, True),
 ], ids=lambda v: v.name if isinstance(v, LayerConfig) else str(v))
 def test_fp6x2_layer_tile_heights_bitwise(m, cfg, act, packed):
     """An output element is the same sum on 256- and 128-row tiles (the same
