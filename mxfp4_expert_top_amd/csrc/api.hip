@@ -210,8 +210,8 @@ LayerWs layer_ws(const moe_layer_params *p)
     }
     // fp32 expert outputs: bf16 here would spend most of the max-abs error
     // budget of the layer (measured 3.05e-2 rms against the 3e-2 bound). The
-    // FP6X2 layer keeps them as block-int16 rows in the same space (A d
-    // int16, then A d / 32 scale codes)
+    // FP6X2 layer, and the MX8 mode on the 256-row tile, keep them as
+    // block-int16 rows in the same space (A d int16, then A d / 32 scale codes)
     L.y = o;      o += round_up(A * (size_t)p->d * 4);
     L.total = o;
     return L;
@@ -628,15 +628,25 @@ int layer_run(const moe_layer_params *p, const LayerWs &L, char *base, const voi
         if (ev) HIP_TRY(hipEventRecord(ev[3], s));
         // down stage: h to MXFP8 (only the off[num_local] rows it holds: A is
         // the host bound, T k, eight times the local rows on an EP share), then
-        // the projection
+        // the projection; on the 256-row tile Y leaves as block-int16 rows
+        // (half fp32's bytes, within 2^-15 of each 32-column block's largest
+        // magnitude) for the matching combine
         HIP_TRY(launch_mxfp8_quantize(h32, 1, p->I, A, p->I, hq, hs, s, off + p->num_local));
+        const bool q16 = mx8_q16_ok(p->mode, p->num_local, A, p->I);
+        int16_t *yq = (int16_t *)y;
+        uint8_t *ys = (uint8_t *)(base + L.y) + (size_t)A * p->d * 2;
         HIP_TRY(launch_gemm_mx8_run(hq, hs, p->I, nullptr, down_codes, down_scales, nullptr,
-                                    nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE, y,
-                                    MX8_OUT_F32, nullptr, p->d, p->mode, base + L.gws, packed,
-                                    s));
+                                    nullptr, p->num_local, A, p->d, p->I, MOE_ACT_NONE,
+                                    q16 ? (void *)yq : (void *)y,
+                                    q16 ? MX8_OUT_Q16 : MX8_OUT_F32, q16 ? ys : nullptr, p->d,
+                                    p->mode, base + L.gws, packed, s));
         if (ev) HIP_TRY(hipEventRecord(ev[4], s));
-        HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
-                               p->out_dtype == MOE_DT_F32, p->d, s));
+        if (q16)
+            HIP_TRY(launch_combine_q16(yq, ys, p->d, inv, w, p->T, p->d, p->k, out,
+                                       p->out_dtype == MOE_DT_F32, p->d, s));
+        else
+            HIP_TRY(launch_combine(y, 1, p->d, inv, w, p->T, p->d, p->k, out,
+                                   p->out_dtype == MOE_DT_F32, p->d, s));
         if (ev) HIP_TRY(hipEventRecord(ev[5], s));
         return MOE_OK;
     }

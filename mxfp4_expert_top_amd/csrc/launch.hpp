@@ -127,7 +127,11 @@ int mx8_resolve_mode(int mode, int num_local, int max_rows, bool q_out = false);
 GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws, bool q_out = false);
 // A: codes [rows][lda] bytes, scales [rows][lda / 32]. Output kinds: bf16,
 // fp32, or MXFP8 (codes in out [rows][ldo], scales in out_scales [rows][ldo/32]).
-enum { MX8_OUT_BF16 = 0, MX8_OUT_F32 = 1, MX8_OUT_MXFP8 = 2 };
+// MX8_OUT_Q16: block-int16 rows as launch_gemm_fp6x2_run's F6_OUT_Q16 writes
+// them (int16 [rows][ldo], one exponent code per 32 columns in out_scales),
+// no activation, where mx8_q16_ok (the 16-wave 256-row tile) holds.
+enum { MX8_OUT_BF16 = 0, MX8_OUT_F32 = 1, MX8_OUT_MXFP8 = 2, MX8_OUT_Q16 = 3 };
+bool mx8_q16_ok(int mode, int num_local, int max_rows, int K);
 hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda,
                                const int32_t *a_rows, const uint8_t *w1c, const uint8_t *w1s,
                                const uint8_t *w2c, const uint8_t *w2s, int num_local,

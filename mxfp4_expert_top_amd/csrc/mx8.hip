@@ -21,6 +21,8 @@
 
 namespace moe {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
@@ -460,6 +462,14 @@ __host__ __device__ constexpr int m8d_lds_bytes(int K)
 {
     return M8D_STAGES * M8D_STAGE + 16 * m8d_scale_chunk(K) + 256 * m8d_scale_row(K);
 }
+// block-int16 output: a wave stages 32 rows of its 64 fp32 columns at a time,
+// padded by 16 bytes, in the ring once the K loop is done
+constexpr int M8D_Q16_PITCH = 64 * 4 + 16;
+__host__ __device__ constexpr int m8d_lds_bytes_q16(int K)
+{
+    return m8d_lds_bytes(K) > 16 * 32 * M8D_Q16_PITCH ? m8d_lds_bytes(K)
+                                                       : 16 * 32 * M8D_Q16_PITCH;
+}
 
 template <int ACT, typename OutT, bool PACKED>
 __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
@@ -467,10 +477,12 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
     const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ w1c,
     const uint8_t *__restrict__ w1s, const uint8_t *__restrict__ w2c,
     const uint8_t *__restrict__ w2s, const int32_t *__restrict__ plan, int hdr, int N, int K,
-    OutT *__restrict__ out, int64_t ldo)
+    OutT *__restrict__ out, int64_t ldo, uint8_t *__restrict__ osc)
 {
     constexpr bool GLU = ACT != ACT_NONE;
     constexpr int COLS = GLU ? M8_BN / 2 : M8_BN;
+    constexpr bool Q16 = std::is_same<OutT, int16_t>::value;
+    static_assert(!(GLU && Q16), "block-int16 rows come from the down projection");
     extern __shared__ __attribute__((aligned(16))) uint8_t m8d_lds[];
     const int srow = m8d_scale_row(K), chunk_b = m8d_scale_chunk(K);
     uint8_t *const Wsc = m8d_lds + M8D_STAGES * M8D_STAGE;  // [16][chunk_b] weight scales
@@ -682,22 +694,76 @@ __global__ __launch_bounds__(M8D_THREADS, 1) void gemm_mx8_w16_kernel(
         }
 
         // lane holds C[8 (v / 4) + 4 h + v % 4][l32] of each tile
+        if constexpr (Q16) {
+            // Block-int16 rows (the expert outputs inside the layer, read once
+            // by the combine), as the FP6X2 down projection writes them: per 32
+            // columns one code e in osc, the biased exponent of the block's
+            // largest magnitude (at most 252), and each value v as the integer
+            // nearest 32767 v 2^(126 - e). One 32-row tile at a time is staged
+            // as fp32 in the idle ring; then 16 lanes hold a row's 64 columns,
+            // 4 each, and the 8 lanes of a 32-column block take its largest
+            // magnitude with three DPP moves.
+            __syncthreads();  // every wave is past its last step's reads
+            constexpr int LPR = 16, RPI = 64 / LPR;
+            uint8_t *const stg = m8d_lds + wave * (32 * M8D_Q16_PITCH);
+            const int c0 = n0 + 64 * slot;
+            const bool col_on = c0 < N;  // N is a multiple of 64
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
+            for (int i = 0; i < NI; i++) {
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (rl >= mrows) continue;
-                OutT *orow = out + (int64_t)(r0 + rl) * ldo;
-                if constexpr (GLU) {
-                    const int col = n0 + 32 * slot + l32;
-                    if (col < N)
-                        store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
-                } else {
+                for (int v = 0; v < 16; v++) {
+                    float *row = (float *)(stg + (8 * (v >> 2) + 4 * h + (v & 3)) * M8D_Q16_PITCH);
 #pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const int col = n0 + 64 * slot + 32 * j + l32;
-                        if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
+                    for (int j = 0; j < 2; j++) row[32 * j + l32] = acc[i][j][v];
+                }
+                const int64_t r = (int64_t)r0 + 64 * q + 32 * i + lane / LPR;
+                OutT *yrow = out + r * ldo + c0 + 4 * (lane % LPR);
+                uint8_t *srow = osc + r * (ldo / 32) + (c0 + 4 * (lane % LPR)) / 32;
+#pragma unroll
+                for (int it = 0; it < 32 / RPI; it++) {
+                    const int rr = RPI * it + lane / LPR, seg = lane % LPR;
+                    const u32x4 val = *(const u32x4 *)(stg + rr * M8D_Q16_PITCH + 16 * seg);
+                    const int rl = 64 * q + 32 * i + rr;
+                    // magnitudes compared as bit patterns (non-negative floats
+                    // order as their bits)
+                    uint32_t mb = 0;
+#pragma unroll
+                    for (int c = 0; c < 4; c++) mb = max(mb, val[c] & 0x7fffffffu);
+                    mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false));
+                    mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, false));
+                    mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x141, 0xF, 0xF, false));
+                    const int code = min((int)(mb >> 23), 252);
+                    const float inv = __uint_as_float((uint32_t)(253 - code) << 23);  // 2^(126 - e)
+                    if (col_on && rl < mrows) {
+                        float x[4];
+#pragma unroll
+                        for (int c = 0; c < 4; c++) x[c] = __uint_as_float(val[c]) * inv;
+                        const u32x2 pk = {
+                            (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[0], x[1])),
+                            (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[2], x[3]))};
+                        __builtin_nontemporal_store(pk, (u32x2 *)(yrow + (int64_t)it * RPI * ldo));
+                        if ((seg & 7) == 0) srow[(int64_t)it * RPI * (ldo / 32)] = (uint8_t)code;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int rl = 64 * q + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (rl >= mrows) continue;
+                    OutT *orow = out + (int64_t)(r0 + rl) * ldo;
+                    if constexpr (GLU) {
+                        const int col = n0 + 32 * slot + l32;
+                        if (col < N)
+                            store_out<OutT>(orow + col, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 2; j++) {
+                            const int col = n0 + 64 * slot + 32 * j + l32;
+                            if (col < N) store_out_once<OutT>(orow + col, acc[i][j][v]);
+                        }
                     }
                 }
             }
@@ -725,20 +791,27 @@ static hipError_t launch_mx8(const uint8_t *ac, const uint8_t *as, int64_t lda,
     // a grid of 8 * ceil(bound / 8) blocks covers every work item
     const int64_t G = (grid + 7) / 8 * 8;
     // fp32 / bf16 output on the 256-row tile: 16 waves, direct-to-LDS loads
+    constexpr bool Q16 = std::is_same<OutT, int16_t>::value;
     if constexpr (BM == 256 && !std::is_same<OutT, uint8_t>::value) {
         if (K <= M8D_MAX_K) {
             auto kern = gemm_mx8_w16_kernel<ACT, OutT, PACKED>;
-            const hipError_t err = ensure_dynamic_lds((const void *)kern, m8d_lds_bytes(K));
+            const int lds = Q16 ? m8d_lds_bytes_q16(K) : m8d_lds_bytes(K);
+            const hipError_t err = ensure_dynamic_lds((const void *)kern, lds);
             if (err != hipSuccess) return err;
-            hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(M8D_THREADS), m8d_lds_bytes(K), s, ac,
-                               as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out, ldo);
+            hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(M8D_THREADS), lds, s, ac, as, lda,
+                               a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out, ldo,
+                               out_scales);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED, BM>), dim3((unsigned)G), dim3(M8_THREADS),
-                       0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa.plan, pa.hdr, N, K, out,
-                       out_scales, ldo);
-    return hipGetLastError();
+    if constexpr (Q16) {
+        return hipErrorInvalidValue;  // block-int16 rows: the 16-wave 256-row tile only
+    } else {
+        hipLaunchKernelGGL((gemm_mx8_kernel<ACT, OutT, PACKED, BM>), dim3((unsigned)G),
+                           dim3(M8_THREADS), 0, s, ac, as, lda, a_rows, w1c, w1s, w2c, w2s,
+                           pa.plan, pa.hdr, N, K, out, out_scales, ldo);
+        return hipGetLastError();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -961,6 +1034,11 @@ GemmPlanArgs mx8_plan_args(int num_local, int max_rows, int mode, void *ws, bool
                           ws);
 }
 
+bool mx8_q16_ok(int mode, int num_local, int max_rows, int K)
+{
+    return mx8_resolve_mode(mode, num_local, max_rows) == MOE_SCHED_TILE256 && K <= M8D_MAX_K;
+}
+
 size_t mx8_gemm_ws_bytes(int num_local, int max_rows)
 {
     // the streaming schedule's 16-row grouping has the most work items
@@ -1001,6 +1079,18 @@ hipError_t launch_gemm_mx8_run(const uint8_t *ac, const uint8_t *as, int64_t lda
 #undef MX8_STREAM
     }
     const bool t256 = md == MOE_SCHED_TILE256;
+    if (out_kind == MX8_OUT_Q16) {
+        if (!mx8_q16_ok(mode, num_local, max_rows, K) || act != ACT_NONE || !out_scales ||
+            ldo % 32 != 0)
+            return hipErrorInvalidValue;
+        if (packed)
+            return launch_mx8<ACT_NONE, int16_t, true, 256>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s,
+                                                            pa, N, K, (int16_t *)out, out_scales,
+                                                            ldo, s);
+        return launch_mx8<ACT_NONE, int16_t, false, 256>(ac, as, lda, a_rows, w1c, w1s, w2c, w2s,
+                                                         pa, N, K, (int16_t *)out, out_scales, ldo,
+                                                         s);
+    }
 #define MX8_RUN(OT, PK)                                                                        \
     return t256 ? mx8_act<OT, PK, 256>(act, ac, as, lda, a_rows, w1c, w1s, w2c, w2s, pa, N, K, \
                                        (OT *)out, out_scales, ldo, s)                          \
