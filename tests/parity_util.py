@@ -194,3 +194,13 @@ def sample_tokens(cfg, idx, n_total=64, seed=0):
 
 def x_bits(inp):
     return oracle.bf16_bits(inp.x)
+
+
+def block_int16_step(y):
+    """The spacing of the block-int16 codes of fp32 rows y [R, d]: per 32
+    columns, with e the biased exponent of the block's largest magnitude
+    (at most 252), 2^(e - 126) / 32767."""
+    R, d = y.shape
+    mb = (np.abs(y).reshape(R, d // 32, 32).view(np.uint32).max(-1) >> 23).astype(np.int64)
+    e = np.minimum(mb, 252)
+    return np.repeat(np.exp2(e - 126.0) / 32767.0, 32, axis=1)

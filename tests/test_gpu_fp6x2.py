@@ -16,8 +16,8 @@ import torch
 
 import oracle
 from synth import CONFIGS, LayerConfig, make_inputs, quantize_mxfp4
-from tests.parity_util import (assert_close_layer, host_weights, np_, oracle_rows, rel_l2,
-                               run_gpu_layer, sample_tokens)
+from tests.parity_util import (assert_close_layer, block_int16_step, host_weights, np_,
+                               oracle_rows, rel_l2, run_gpu_layer, sample_tokens)
 from tests.test_oracle_fp6x2 import _blocks
 
 pytestmark = pytest.mark.gpu
@@ -294,16 +294,6 @@ def test_auto_schedule_takes_fp6x2(m, cfg):
     assert_close_layer(np_(a["out"]), ref["out"], cfg.name)
 
 
-def _block_int16_step(y):
-    """The spacing of the block-int16 codes of fp32 rows y [R, d]: per 32
-    columns, with e the biased exponent of the block's largest magnitude
-    (at most 252), 2^(e - 126) / 32767."""
-    R, d = y.shape
-    mb = (np.abs(y).reshape(R, d // 32, 32).view(np.uint32).max(-1) >> 23).astype(np.int64)
-    e = np.minimum(mb, 252)
-    return np.repeat(np.exp2(e - 126.0) / 32767.0, 32, axis=1)
-
-
 @pytest.mark.parametrize("cfg", [SMALL[1], SMALL[4]], ids=lambda c: c.name)
 def test_fp6x2_layer_block_int16_expert_outputs(m, cfg):
     """Inside the FP6X2 layer the expert outputs Y travel as block-int16 rows
@@ -336,7 +326,7 @@ def test_fp6x2_layer_block_int16_expert_outputs(m, cfg):
                              y, ws)
     torch.cuda.synchronize()
     yv, iv, wv = np_(y), np_(inv), np_(g["w"])
-    step = _block_int16_step(yv)
+    step = block_int16_step(yv)
     ref = np.zeros((T, d), np.float32)
     bound = np.zeros((T, d), np.float64)
     mag = np.zeros((T, d), np.float64)

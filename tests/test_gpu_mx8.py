@@ -17,8 +17,8 @@ import torch
 
 import oracle
 from synth import CONFIGS, LayerConfig, make_inputs, quantize_mxfp4
-from tests.parity_util import (assert_close_layer, host_weights, np_, oracle_rows, rel_l2,
-                               run_gpu_layer, sample_tokens)
+from tests.parity_util import (assert_close_layer, block_int16_step, host_weights, np_,
+                               oracle_rows, rel_l2, run_gpu_layer, sample_tokens)
 from tests.test_oracle_mx8 import _blocks
 
 pytestmark = pytest.mark.gpu
@@ -292,6 +292,61 @@ def test_mx8_layer_determinism_bitwise(m):
     b = run_gpu_layer(inp, precision=m.PREC_MX8)
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("cfg", [SMALL[1], SMALL[2], SMALL[3]], ids=lambda c: c.name)
+def test_mx8_layer_block_int16_expert_outputs(m, cfg):
+    """On the 256-row tile the MX8 layer carries the expert outputs Y as
+    block-int16 rows (per 32 columns the biased exponent e of the largest
+    magnitude, each value the integer nearest 32767 v 2^(126 - e)). Rebuilt
+    from the standalone entry points -- the permutation, MXFP8 tokens, the
+    gate/up projection's fp32 h, MXFP8 h and the down projection's fp32 rows
+    on the same tile -- and combined in fp32 in slot order, every output
+    element lies within sum_j w_j (0.5 + 2^-9) step_j plus fp32 rounding,
+    step_j the code spacing of row j's block. Rounding toward zero, a wrong
+    exponent or a wrong block would exceed that. x2 is an EP share: h rows
+    past the local ones are never read."""
+    inp = make_inputs(cfg).to(DEV)
+    T, k, d, I, nl = cfg.T, cfg.k, cfg.d, cfg.I, cfg.num_local
+    g = run_gpu_layer(inp, precision=m.PREC_MX8, mode=m.MODE_TILE256, out_dtype=torch.float32)
+    A = T * k
+    off = torch.empty(nl + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(A, dtype=torch.int32, device=DEV)
+    inv = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    pws = m.alloc_workspace(m.moe_permute_workspace_size(T, nl), DEV)
+    m.moe_permute(g["idx"], None, cfg.expert_begin, nl, off, perm, inv, pws, E=cfg.E)
+    W = inp.weights
+    xc, xs = m.moe_mxfp8_quantize(inp.x)
+    ws = m.alloc_workspace(m.moe_grouped_gemm_mx8_workspace_size(nl, A), DEV)
+    h = torch.zeros(A, I, dtype=torch.float32, device=DEV)
+    m.moe_grouped_gemm_mx8(xc, xs, perm, W["gate_codes"], W["gate_scales"], W["up_codes"],
+                           W["up_scales"], off, A, 1, h, ws, mode=m.MODE_TILE256)
+    hc, hs = m.moe_mxfp8_quantize(h)
+    y = torch.zeros(A, d, dtype=torch.float32, device=DEV)
+    m.moe_grouped_gemm_mx8(hc, hs, None, W["down_codes"], W["down_scales"], None, None, off, A, 0,
+                           y, ws, mode=m.MODE_TILE256)
+    torch.cuda.synchronize()
+    yv, iv, wv = np_(y), np_(inv), np_(g["w"])
+    assert (iv < int(np_(off)[nl])).all()
+    step = block_int16_step(yv)
+    ref = np.zeros((T, d), np.float32)
+    bound = np.zeros((T, d), np.float64)
+    mag = np.zeros((T, d), np.float64)
+    for j in range(k):
+        r = iv[:, j]
+        on = r >= 0
+        wj = np.where(on, wv[:, j], 0.0).astype(np.float32)[:, None]
+        rows = np.where(on, r, 0)
+        ref = ref + wj * yv[rows]
+        bound += wj.astype(np.float64) * step[rows]
+        mag += np.abs(wj.astype(np.float64) * yv[rows])
+    got = np_(g["out"]).astype(np.float64)
+    diff = np.abs(got - ref.astype(np.float64))
+    lim = (0.5 + 2.0 ** -9) * bound + 4 * k * 2.0 ** -24 * mag
+    print(f"{cfg.name}: max |out - fp32-Y out| / sum w step = {(diff / np.maximum(bound, 1e-300)).max():.3f}")
+    assert (diff <= lim).all(), (diff - lim).max()
+    # the rounding is visible: the block-int16 output is not the fp32-Y one
+    assert not np.array_equal(got, ref.astype(np.float64))
 
 
 @pytest.mark.parametrize("name", ["prefill", "decode", "ep_share", "long_skewed_prefill"])
