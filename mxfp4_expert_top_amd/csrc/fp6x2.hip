@@ -329,8 +329,8 @@ constexpr bool f6_records = std::is_same<OutT, uint8_t>::value;
 template <typename OutT>
 constexpr bool f6_q16 = std::is_same<OutT, int16_t>::value;
 
-template <int ACT, typename OutT, bool PACKED, int NW, int F6_STAGES>
-__global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
+template <int ACT, typename OutT, bool PACKED, int NW, int F6_STAGES, bool WIDE>
+__global__ __launch_bounds__(NW * 64, WIDE ? 1 : 16 / NW) void gemm_fp6x2_w16_kernel(
     const uint8_t *__restrict__ ad, int64_t lda, const int32_t *__restrict__ a_rows,
     const uint8_t *__restrict__ w1c, const uint8_t *__restrict__ w1s,
     const uint8_t *__restrict__ w2c, const uint8_t *__restrict__ w2s,
@@ -342,7 +342,13 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
     static_assert(!(GLU && f6_q16<OutT>), "block-int16 rows come from the down projection");
     extern __shared__ __attribute__((aligned(16))) uint8_t f6_lds[];
     const int chunk_b = f6_scale_chunk(K);
-    constexpr int F6_THREADS = NW * 64, F6_A_BYTES = f6_a_bytes(NW), F6_STAGE = f6_stage(NW);
+    // WIDE: 8 waves on a 256-row tile, each wave holding two column slots
+    // (64 rows x 2 COLS_W columns): per MFMA a third less LDS read than a
+    // wave per slot, as a wave's A fragments serve four weight fragments
+    constexpr int SPW = WIDE ? 2 : 1, NJ = 2 * SPW;
+    static_assert(!WIDE || NW == 8, "wide waves tile 256 rows with 8 waves");
+    constexpr int F6_THREADS = NW * 64, F6_A_BYTES = f6_a_bytes(NW * SPW),
+                  F6_STAGE = f6_stage(NW * SPW);
     uint8_t *const Wsc = f6_lds + F6_STAGES * F6_STAGE;  // [16][chunk_b] weight scales
 
     const int nblk = (N + COLS - 1) / COLS;
@@ -359,7 +365,8 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int slot = wave & 3, q = wave >> 2;
+    // column slot (the first of the wave's SPW) and 64-row block
+    const int slot0 = WIDE ? 2 * (wave & 1) : (wave & 3), q = WIDE ? wave >> 1 : wave >> 2;
     const int nch = K / 128;
     const int64_t row_b = 2 * lda;  // bytes per split row
 
@@ -377,12 +384,13 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
         return (int64_t)e * N + wrow;
     };
 
-    // ---- DMA sources. Records: instruction j of wave w fills rows 16 w + 8 j
-    // .. + 7 (lane L: chunk position L % 8 of row 16 w + 8 j + L / 8).
-    const uint8_t *ag[2];
+    // ---- DMA sources. Records: instruction j of wave w fills rows
+    // 16 SPW w + 8 j .. + 7 (lane L: chunk position L % 8 of row
+    // 16 SPW w + 8 j + L / 8).
+    const uint8_t *ag[2 * SPW];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int rt = 16 * wave + 8 * j + (lane >> 3);
+    for (int j = 0; j < 2 * SPW; j++) {
+        const int rt = 16 * SPW * wave + 8 * j + (lane >> 3);
         const int rc = min(r0 + rt, rend - 1);
         const int64_t arow = a_rows ? (int64_t)a_rows[rc] : (int64_t)rc;
         ag[j] = ad + arow * row_b + 16 * ((lane & 7) ^ ((rt >> 1) & 7));
@@ -403,7 +411,8 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
     auto issue = [&](int kt, int st) {
         const uint32_t sb = lds0 + st * F6_STAGE;
 #pragma unroll
-        for (int j = 0; j < 2; j++) dma16(ag[j] + kt * F6_ROW, sb + (2 * wave + j) * 1024);
+        for (int j = 0; j < 2 * SPW; j++)
+            dma16(ag[j] + kt * F6_ROW, sb + (2 * SPW * wave + j) * 1024);
         if (wload) {
             const uint8_t *src;
             if constexpr (PACKED)
@@ -450,9 +459,13 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
 
     // ---- wave tiles
     const int h = lane >> 5, l32 = lane & 31;
-    int bt[2];
+    // weight fragment jj: slot slot0 + jj / 2, half jj % 2 (GLU: gate, up)
+    int bt[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; j++) bt[j] = GLU ? 128 * j + 32 * slot : 64 * slot + 32 * j;
+    for (int jj = 0; jj < NJ; jj++) {
+        const int sl = slot0 + jj / 2, j = jj & 1;
+        bt[jj] = GLU ? 128 * j + 32 * sl : 64 * sl + 32 * j;
+    }
     const int n_on = (64 * q < mrows ? 1 : 0) + (64 * q + 32 < mrows ? 1 : 0);
     const int bpos = 16 * (h ^ ((l32 >> 3) & 1));
     // rows 64 q + 32 i + l32 share (row / 2) % 8 = (l32 / 2) % 8; block h is
@@ -461,9 +474,9 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
     const int key = (l32 >> 1) & 7;
     // weight scales: this lane's rows and MX block h; the step adds
     // (k / 8) * 256 + (k % 2) * 128 + (k % 8) / 2 (k-block 2 k + h)
-    int wso[2];
+    int wso[NJ];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < NJ; j++) {
         const int row = bt[j] + l32;
         wso[j] = (row / 16) * chunk_b + (row % 16) * 4 + 64 * h;
     }
@@ -473,11 +486,11 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
 
     auto run = [&](auto ni_c) {
         constexpr int NI = decltype(ni_c)::value;
-        f32x16 acc[NI > 0 ? NI : 1][2];
+        f32x16 acc[NI > 0 ? NI : 1][NJ];
 #pragma unroll
         for (int i = 0; i < NI; i++)
 #pragma unroll
-            for (int j = 0; j < 2; j++)
+            for (int j = 0; j < NJ; j++)
 #pragma unroll
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.f;
 
@@ -485,10 +498,10 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
             if constexpr (NI > 0) {
                 const uint8_t *Ap = f6_lds + st * F6_STAGE;
                 const uint8_t *Bq = Ap + F6_A_BYTES;
-                i32x8 bv[2];
-                int sb[2];
+                i32x8 bv[NJ];
+                int sb[NJ];
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
+                for (int j = 0; j < NJ; j++) {
                     const int row = bt[j] + l32;
                     const u32x4 w = *(const u32x4 *)(Bq + row * 32 + bpos);
                     bv[j] = i32x8{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
@@ -518,13 +531,13 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
 #pragma unroll
                 for (int i = 0; i < NI; i++)
 #pragma unroll
-                    for (int j = 0; j < 2; j++)
+                    for (int j = 0; j < NJ; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             a1[i], bv[j], acc[i][j], 2, 4, 0, sa[i], 0, sb[j]);
 #pragma unroll
                 for (int i = 0; i < NI; i++)
 #pragma unroll
-                    for (int j = 0; j < 2; j++)
+                    for (int j = 0; j < NJ; j++)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             a2[i], bv[j], acc[i][j], 2, 4, 1, sa[i], 0, sb[j]);
             }
@@ -538,8 +551,11 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
             // every wave's and ends the reads of step kt - 1
             // (two stages: only step kt's loads are in flight, all waited for;
             // with 8 waves every wave issues three loads per step)
+            // (wide waves: four record loads and one code load per step)
             if (F6_STAGES == 3 && kt + 1 < nk) {
-                if constexpr (NW == 8)
+                if constexpr (WIDE)
+                    asm volatile("s_waitcnt vmcnt(5)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                else if constexpr (NW == 8)
                     asm volatile("s_waitcnt vmcnt(3)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
                 else
                     asm volatile("s_waitcnt vmcnt(2)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -563,9 +579,8 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
         // columns c0 .. c0 + COLS_W - 1.
         __syncthreads();
         constexpr int COLS_W = GLU ? 32 : 64;
-        const int c0 = n0 + COLS_W * slot;
-        const bool col_on = c0 < N;  // N is a multiple of 64
-        uint8_t *const stg = f6_lds + wave * (64 * F6_EPI_PITCH);
+        // the staging area of row block q, slot sl: 64 rows of F6_EPI_PITCH
+        auto area = [&](int sl) { return f6_lds + (4 * q + sl) * (64 * F6_EPI_PITCH); };
         if constexpr (f6_records<OutT>) {
             // (GLU only: a wave's 32 output columns are one MX block.) The
             // fp32 results of the wave's 64 rows staged, 128 bytes per row.
@@ -576,15 +591,21 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
             // is active together: it shares the row, and N % 64 == 0)
             static_assert(GLU, "records are written by the GLU projection");
 #pragma unroll
-            for (int i = 0; i < NI; i++)
+            for (int s2 = 0; s2 < SPW; s2++) {
+                uint8_t *const stg = area(slot0 + s2);
 #pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-                    ((float *)(stg + r * F6_EPI_PITCH))[l32] =
-                        act_apply<ACT>(acc[i][0][v], acc[i][1][v]);
-                }
+                for (int i = 0; i < NI; i++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) {
+                        const int r = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+                        ((float *)(stg + r * F6_EPI_PITCH))[l32] =
+                            act_apply<ACT>(acc[i][2 * s2][v], acc[i][2 * s2 + 1][v]);
+                    }
+            }
             __syncthreads();
-            const int R = tid >> 2, bb = tid & 3;
+#pragma unroll
+            for (int pass = 0; pass < SPW; pass++) {
+            const int R = (tid >> 2) + pass * (F6_THREADS / 4), bb = tid & 3;
             const int cb = n0 + 32 * bb;
             if (R < mrows && cb < N) {
                 const uint8_t *src = f6_lds + (4 * (R >> 6) + bb) * (64 * F6_EPI_PITCH) +
@@ -602,6 +623,7 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
                 f6_store_pair((uint8_t *)out + (int64_t)(r0 + R) * 2 * ldo + (b >> 1) * 128, b & 1, w,
                               s1, s2);
             }
+            }
         } else {
             // one 32-row tile at a time, staged (fp32 for block-int16 rows)
             // and stored as whole row segments
@@ -611,17 +633,23 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
             constexpr int LPR = ROW_B / 16, RPI = 64 / LPR;    // lanes per row, rows per store
             static_assert(32 * PITCH <= 64 * F6_EPI_PITCH, "staging fits the wave's area");
 #pragma unroll
+            for (int s2 = 0; s2 < SPW; s2++) {
+            const int c0 = n0 + COLS_W * (slot0 + s2);
+            const bool col_on = c0 < N;  // N is a multiple of 64
+            uint8_t *const stg = area(slot0 + s2);
+#pragma unroll
             for (int i = 0; i < NI; i++) {
 #pragma unroll
                 for (int v = 0; v < 16; v++) {
                     const int r = 8 * (v >> 2) + 4 * h + (v & 3);
                     StT *row = (StT *)(stg + r * PITCH);
                     if constexpr (GLU) {
-                        store_out<StT>(row + l32, act_apply<ACT>(acc[i][0][v], acc[i][1][v]));
+                        store_out<StT>(row + l32,
+                                       act_apply<ACT>(acc[i][2 * s2][v], acc[i][2 * s2 + 1][v]));
                     } else {
 #pragma unroll
                         for (int j = 0; j < 2; j++)
-                            store_out<StT>(row + 32 * j + l32, acc[i][j][v]);
+                            store_out<StT>(row + 32 * j + l32, acc[i][2 * s2 + j][v]);
                     }
                 }
                 // block-int16 rows: this lane's row of iteration 0
@@ -677,6 +705,7 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
                     }
                 }
             }
+            }
         }
     };
     // every branch runs the same barriers (nk) and the same loads
@@ -687,7 +716,7 @@ __global__ __launch_bounds__(NW * 64, 16 / NW) void gemm_fp6x2_w16_kernel(
     }
 }
 
-template <int ACT, typename OutT, bool PACKED, int NW>
+template <int ACT, typename OutT, bool PACKED, int NW, bool WIDE = false>
 static hipError_t launch_f6_nw(const uint8_t *ad, int64_t lda, const int32_t *a_rows,
                             const uint8_t *w1c, const uint8_t *w1s, const uint8_t *w2c,
                             const uint8_t *w2s, const int32_t *plan,
@@ -702,11 +731,12 @@ static hipError_t launch_f6_nw(const uint8_t *ad, int64_t lda, const int32_t *a_
     const int64_t G = (grid + 7) / 8 * 8;
     // 128-row tiles: three stages where two workgroups still fit a CU, else
     // two (S2 keeps the 16-wave kernel on three stages only)
-    constexpr int S2 = NW == 8 ? 2 : 3;
-    const bool three = NW == 16 || f6_lds_bytes(K, NW, 3) <= F6_LDS_HALF;
-    auto kern = three ? gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, 3>
-                      : gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, S2>;
-    const int lds = f6_lds_bytes(K, NW, three ? 3 : 2);
+    // (wide waves: the 256-row tile's LDS, three stages)
+    constexpr int S2 = NW == 8 && !WIDE ? 2 : 3, NR = WIDE ? 16 : NW;
+    const bool three = NR == 16 || f6_lds_bytes(K, NW, 3) <= F6_LDS_HALF;
+    auto kern = three ? gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, 3, WIDE>
+                      : gemm_fp6x2_w16_kernel<ACT, OutT, PACKED, NW, S2, WIDE>;
+    const int lds = f6_lds_bytes(K, NR, three ? 3 : 2);
     const hipError_t err = ensure_dynamic_lds((const void *)kern, lds);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(kern, dim3((unsigned)G), dim3(NW * 64), lds, s, ad, lda,
@@ -732,6 +762,10 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
 #define F6_LAUNCH(A, OT, PK)                                                                   \
     return launch_f6_nw<A, OT, PK, 16>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,  \
                                     pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
+#define F6_LAUNCHW(A, OT, PK)                                                                  \
+    return launch_f6_nw<A, OT, PK, 8, true>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan,         \
+                                         pa.max_groups, pa.hdr, N, K, (OT *)out, ldo,          \
+                                         out_scales, s)
 #define F6_LAUNCH8(A, OT, PK)                                                                  \
     return launch_f6_nw<A, OT, PK, 8>(ad, lda, a_rows, w1c, w1s, w2c, w2s, plan, pa.max_groups,   \
                                    pa.hdr, N, K, (OT *)out, ldo, out_scales, s)
@@ -757,6 +791,22 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
         default: return hipErrorInvalidValue;
         }
     }
+    // 256-row gate/up tiles over at least 512 rows per expert on average
+    // (the row bound's): wide waves, which read a third less LDS per MFMA;
+    // over fewer rows the tiles are mostly part-filled, and 16 waves, each
+    // SIMD holding a quarter of every row block's columns, keep the matrix
+    // cores evenly loaded where two 64-row waves per SIMD would not
+    if (out_kind == F6_OUT_RECORDS && (int64_t)max_rows >= 512 * (int64_t)num_local) {
+        switch (act) {
+        case ACT_SILU_MUL:
+            if (packed) F6_LAUNCHW(ACT_SILU_MUL, uint8_t, true);
+            F6_LAUNCHW(ACT_SILU_MUL, uint8_t, false);
+        case ACT_GELU_TANH_MUL:
+            if (packed) F6_LAUNCHW(ACT_GELU_TANH_MUL, uint8_t, true);
+            F6_LAUNCHW(ACT_GELU_TANH_MUL, uint8_t, false);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (out_kind == F6_OUT_RECORDS) {
         if (packed) F6_GLU(uint8_t, true)
         F6_GLU(uint8_t, false)
@@ -779,6 +829,7 @@ hipError_t launch_gemm_fp6x2_run(const uint8_t *ad, int64_t lda, const int32_t *
 #undef F6_GLU
 #undef F6_LAUNCH
 #undef F6_LAUNCH8
+#undef F6_LAUNCHW
 }
 
 hipError_t launch_grouped_gemm_fp6x2(const uint8_t *ad, int64_t lda, const int32_t *a_rows,

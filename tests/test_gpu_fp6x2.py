@@ -202,15 +202,19 @@ def test_grouped_gemm_fp6x2_bf16_out_and_direct_rows(m):
         assert (np.abs(got[r0:r1] - ref) <= 2.0 ** -8 * (np.abs(ref) + b) + b).all()
 
 
+@pytest.mark.parametrize("counts", [[150, 0, 257, 40], [900, 701]], ids=["16waves", "wide"])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("act", [1, 2])
-def test_grouped_gemm_fp6x2_record_output_bitexact(m, act, packed):
+def test_grouped_gemm_fp6x2_record_output_bitexact(m, act, packed, counts):
     """Split-record output (the layer's h): byte for byte the oracle's split
     of the fp32 output of the same launch configuration; rows past each
-    group's end untouched."""
-    rng = np.random.default_rng(30 + act + 2 * packed)
-    nl, N, K, T = 4, 320, 384, 500
-    counts = np.array([150, 0, 257, 40], np.int32)
+    group's end untouched. With at least 512 rows per expert (the row bound
+    over the experts) the records come from the wide-wave tile (8 waves of
+    64 x 128), the fp32 rows from the 16-wave one: the same sums either way."""
+    rng = np.random.default_rng(30 + act + 2 * packed + 5 * len(counts))
+    N, K, T = 320, 384, 500
+    counts = np.array(counts, np.int32)
+    nl = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     A = int(off[-1])
     xd, _, _ = _split_rows(m, rng, T, K)
@@ -373,14 +377,19 @@ def test_fp6x2_layer_determinism_bitwise(m):
     (LayerConfig("h2", T=1200, I=1024, d=3584, E=16, k=4, bias="normal"), 2, True),
     # K = 4096, the largest taken: 80 KB of LDS on 128-row tiles, 152 KB on 256
     (LayerConfig("h3", T=300, I=2048, d=4096, E=4, k=2), 1, True),
+    # 512 rows per expert (the row bound's mean): the 256-row gate/up tiles on
+    # wide waves (8 waves of 64 x 128), streaming and canonical weights
+    (LayerConfig("h4", T=2048, I=256, d=512, E=8, k=2, bias="normal"), 1, True),
+    (LayerConfig("h5", T=1536, I=384, d=640, E=6, k=2), 2, False),
 ], ids=lambda v: v.name if isinstance(v, LayerConfig) else str(v))
 def test_fp6x2_layer_tile_heights_bitwise(m, cfg, act, packed):
     """An output element is the same sum on 256- and 128-row tiles (the same
     K steps and planes in the same order; the tile only decides which
     workgroup computes it): the layer on 128-row tiles (8 waves, two
     workgroups per CU, a two-stage ring where three do not fit 80 KB), on
-    256-row tiles and under the automatic per-projection choice agree bit for
-    bit, records, block-int16 rows and all."""
+    256-row tiles (16 waves of 64 x 64, or for gate/up over 512 rows per
+    expert 8 waves of 64 x 128) and under the automatic per-projection choice
+    agree bit for bit, records, block-int16 rows and all."""
     inp = make_inputs(cfg).to(DEV)
     pw = m.prepack_weights(inp.weights) if packed else None
     runs = [run_gpu_layer(inp, precision=m.PREC_FP6X2, mode=md, act=act, packed=pw,
