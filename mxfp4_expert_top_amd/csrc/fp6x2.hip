@@ -254,16 +254,17 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // ---------------------------------------------------------------------------
 // Grouped projection on the block-scaled matrix cores, 256-row tiles.
 //
-// Workgroup tile: up to 16 NW permuted rows of one expert (a work item of the
-// 256- or 128-row plan) x 256 weight rows, K step 64 (two MX blocks, one
-// 128-byte record of a split row), NW waves: 16 (one workgroup per CU), or 8
-// with 128-row tiles, whose 80 KB of LDS and at most 128 VGPRs let two
-// workgroups share a CU, so that one's prologue, epilogue and launch overlap
-// the other's K loop. Wave w: row block q = w / 4
-// (row tiles 2 q, 2 q + 1 of 32) and slot c = w % 4 (gate and up rows of
-// output columns 32 c .. + 32, or weight rows 64 c .. + 64); per K step and
-// (row tile, weight tile) two 32 x 32 x 64 MFMAs, one per plane, into the
-// same fp32 accumulator.
+// Workgroup tile: up to 256 or 128 permuted rows of one expert (a work item
+// of the 256- or 128-row plan) x 256 weight rows, K step 64 (two MX blocks,
+// one 128-byte record of a split row). NW waves: 16 on 256-row tiles (one
+// workgroup per CU); 8 on 128-row tiles, whose 80 KB of LDS and at most 128
+// VGPRs let two workgroups share a CU, so that one's prologue, epilogue and
+// launch overlap the other's K loop; or 8 wide waves on 256-row tiles (WIDE).
+// Wave w: row block q = w / 4 (row tiles 2 q, 2 q + 1 of 32) and slot
+// c = w % 4 (gate and up rows of output columns 32 c .. + 32, or weight rows
+// 64 c .. + 64); a wide wave: row block w / 2 and slots 2 (w % 2) and
+// 2 (w % 2) + 1. Per K step and (row tile, weight tile) two 32 x 32 x 64
+// MFMAs, one per plane, into the same fp32 accumulator.
 //
 // Operands, as the instruction takes them (lane L, l = L % 32, g = L / 32;
 // checked with a one-wave probe against an fp64 evaluation):
@@ -289,7 +290,8 @@ hipError_t launch_fp6x2_split(const void *v, int v_f32, int64_t ldv, int64_t N, 
 // ---------------------------------------------------------------------------
 constexpr int F6_BN = 256, F6_BK = 64, F6_ROW = 128;
 constexpr int F6_W_BYTES = F6_BN * F6_BK / 2;    // 8 KB of E2M1 codes
-// NW waves: 16 (256-row tiles, 32 KB of records per stage) or 8 (128-row tiles)
+// NW: 16 (256-row tiles, 32 KB of records per stage) or 8 (128-row tiles); the
+// wide-wave 256-row tile sizes its LDS as the 16-wave one (f6_a_bytes(16) ...)
 __host__ __device__ constexpr int f6_a_bytes(int NW) { return 16 * NW * F6_ROW; }
 __host__ __device__ constexpr int f6_stage(int NW) { return f6_a_bytes(NW) + F6_W_BYTES; }
 constexpr int F6_MAX_K = 4096;
