@@ -202,17 +202,19 @@ def test_grouped_gemm_fp6x2_bf16_out_and_direct_rows(m):
         assert (np.abs(got[r0:r1] - ref) <= 2.0 ** -8 * (np.abs(ref) + b) + b).all()
 
 
-@pytest.mark.parametrize("counts", [[150, 0, 257, 40], [900, 701]], ids=["16waves", "wide"])
+@pytest.mark.parametrize("counts,K", [([150, 0, 257, 40], 384), ([900, 701], 384),
+                                      ([900, 701], 4096)], ids=["16waves", "wide", "wide_k4096"])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("act", [1, 2])
-def test_grouped_gemm_fp6x2_record_output_bitexact(m, act, packed, counts):
+def test_grouped_gemm_fp6x2_record_output_bitexact(m, act, packed, counts, K):
     """Split-record output (the layer's h): byte for byte the oracle's split
     of the fp32 output of the same launch configuration; rows past each
     group's end untouched. With at least 512 rows per expert (the row bound
     over the experts) the records come from the wide-wave tile (8 waves of
-    64 x 128), the fp32 rows from the 16-wave one: the same sums either way."""
-    rng = np.random.default_rng(30 + act + 2 * packed + 5 * len(counts))
-    N, K, T = 320, 384, 500
+    64 x 128), the fp32 rows from the 16-wave one: the same sums either way;
+    K = 4096 fills the wide tile's three-stage ring to 152 KB of LDS."""
+    rng = np.random.default_rng(30 + act + 2 * packed + 5 * len(counts) + K)
+    N, T = 320, 500
     counts = np.array(counts, np.int32)
     nl = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
