@@ -607,24 +607,24 @@ __global__ __launch_bounds__(NW * 64, WIDE ? 1 : 16 / NW) void gemm_fp6x2_w16_ke
             __syncthreads();
 #pragma unroll
             for (int pass = 0; pass < SPW; pass++) {
-            const int R = (tid >> 2) + pass * (F6_THREADS / 4), bb = tid & 3;
-            const int cb = n0 + 32 * bb;
-            if (R < mrows && cb < N) {
-                const uint8_t *src = f6_lds + (4 * (R >> 6) + bb) * (64 * F6_EPI_PITCH) +
-                                     (R & 63) * F6_EPI_PITCH;
-                float x[32];
+                const int R = (tid >> 2) + pass * (F6_THREADS / 4), bb = tid & 3;
+                const int cb = n0 + 32 * bb;
+                if (R < mrows && cb < N) {
+                    const uint8_t *src = f6_lds + (4 * (R >> 6) + bb) * (64 * F6_EPI_PITCH) +
+                                         (R & 63) * F6_EPI_PITCH;
+                    float x[32];
 #pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const f32x4 t = *(const f32x4 *)(src + 16 * j);
-                    x[4 * j] = t[0]; x[4 * j + 1] = t[1]; x[4 * j + 2] = t[2]; x[4 * j + 3] = t[3];
+                    for (int j = 0; j < 8; j++) {
+                        const f32x4 t = *(const f32x4 *)(src + 16 * j);
+                        x[4 * j] = t[0]; x[4 * j + 1] = t[1]; x[4 * j + 2] = t[2]; x[4 * j + 3] = t[3];
+                    }
+                    uint32_t w[12];
+                    const uint32_t s1 = mxfp6_plane(x, w);
+                    const uint32_t s2 = mxfp6_plane(x, w + 6);
+                    const int b = cb >> 5;
+                    f6_store_pair((uint8_t *)out + (int64_t)(r0 + R) * 2 * ldo + (b >> 1) * 128, b & 1, w,
+                                  s1, s2);
                 }
-                uint32_t w[12];
-                const uint32_t s1 = mxfp6_plane(x, w);
-                const uint32_t s2 = mxfp6_plane(x, w + 6);
-                const int b = cb >> 5;
-                f6_store_pair((uint8_t *)out + (int64_t)(r0 + R) * 2 * ldo + (b >> 1) * 128, b & 1, w,
-                              s1, s2);
-            }
             }
         } else {
             // one 32-row tile at a time, staged (fp32 for block-int16 rows)
@@ -636,77 +636,77 @@ __global__ __launch_bounds__(NW * 64, WIDE ? 1 : 16 / NW) void gemm_fp6x2_w16_ke
             static_assert(32 * PITCH <= 64 * F6_EPI_PITCH, "staging fits the wave's area");
 #pragma unroll
             for (int s2 = 0; s2 < SPW; s2++) {
-            const int c0 = n0 + COLS_W * (slot0 + s2);
-            const bool col_on = c0 < N;  // N is a multiple of 64
-            uint8_t *const stg = area(slot0 + s2);
+                const int c0 = n0 + COLS_W * (slot0 + s2);
+                const bool col_on = c0 < N;  // N is a multiple of 64
+                uint8_t *const stg = area(slot0 + s2);
 #pragma unroll
-            for (int i = 0; i < NI; i++) {
+                for (int i = 0; i < NI; i++) {
 #pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = 8 * (v >> 2) + 4 * h + (v & 3);
-                    StT *row = (StT *)(stg + r * PITCH);
-                    if constexpr (GLU) {
-                        store_out<StT>(row + l32,
-                                       act_apply<ACT>(acc[i][2 * s2][v], acc[i][2 * s2 + 1][v]));
-                    } else {
+                    for (int v = 0; v < 16; v++) {
+                        const int r = 8 * (v >> 2) + 4 * h + (v & 3);
+                        StT *row = (StT *)(stg + r * PITCH);
+                        if constexpr (GLU) {
+                            store_out<StT>(row + l32,
+                                           act_apply<ACT>(acc[i][2 * s2][v], acc[i][2 * s2 + 1][v]));
+                        } else {
 #pragma unroll
-                        for (int j = 0; j < 2; j++)
-                            store_out<StT>(row + 32 * j + l32, acc[i][2 * s2 + j][v]);
-                    }
-                }
-                // block-int16 rows: this lane's row of iteration 0
-                OutT *yrow = nullptr;
-                uint8_t *srow = nullptr;
-                if constexpr (f6_q16<OutT>) {
-                    const int64_t r = (int64_t)r0 + 64 * q + 32 * i + lane / LPR;
-                    yrow = out + r * ldo + c0 + 4 * (lane % LPR);
-                    srow = osc + r * (ldo / 32) + (c0 + 4 * (lane % LPR)) / 32;
-                }
-#pragma unroll
-                for (int it = 0; it < 32 / RPI; it++) {
-                    const int r = RPI * it + lane / LPR, seg = lane % LPR;
-                    const u32x4 val = *(const u32x4 *)(stg + r * PITCH + 16 * seg);
-                    const int rl = 64 * q + 32 * i + r;
-                    if constexpr (f6_q16<OutT>) {
-                        // columns c0 + 4 seg .. + 3; the 8 lanes with equal
-                        // lane / 8 hold one 32-column block. Magnitudes are
-                        // compared as bit patterns (non-negative floats
-                        // order as their bits)
-                        uint32_t mb = 0;
-#pragma unroll
-                        for (int c = 0; c < 4; c++) mb = max(mb, val[c] & 0x7fffffffu);
-                        // max over the 8 lanes: swap neighbours, then pairs
-                        // (quad_perm 1,0,3,2 and 2,3,0,1), then mirror the
-                        // 8-lane half row (lane i and 7 - i): DPP moves on
-                        // the vector unit, no LDS round trip
-                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false));
-                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, false));
-                        mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x141, 0xF, 0xF, false));
-                        // e: the block's largest biased exponent (at most
-                        // 252: larger blocks saturate); x 2^(126 - e) lies
-                        // in (-1, 1), and v_cvt_pknorm_i16_f32 rounds its
-                        // 32767 multiple to an integer, two values a step
-                        const int code = min((int)(mb >> 23), 252);
-                        const float inv = __uint_as_float((uint32_t)(253 - code) << 23);
-                        if (col_on && rl < mrows) {
-                            float x[4];
-#pragma unroll
-                            for (int c = 0; c < 4; c++) x[c] = __uint_as_float(val[c]) * inv;
-                            const u32x2 pk = {
-                                (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[0], x[1])),
-                                (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[2], x[3]))};
-                            __builtin_nontemporal_store(pk, (u32x2 *)(yrow + (int64_t)it * RPI * ldo));
-                            if ((seg & 7) == 0)
-                                srow[(int64_t)it * RPI * (ldo / 32)] = (uint8_t)code;
+                            for (int j = 0; j < 2; j++)
+                                store_out<StT>(row + 32 * j + l32, acc[i][2 * s2 + j][v]);
                         }
-                    } else if (col_on && rl < mrows) {
-                        u32x4 *dst = (u32x4 *)((uint8_t *)(out + (int64_t)(r0 + rl) * ldo + c0) +
-                                               16 * seg);
-                        if constexpr (!GLU && sizeof(OutT) == 4) __builtin_nontemporal_store(val, dst);
-                        else *dst = val;
+                    }
+                    // block-int16 rows: this lane's row of iteration 0
+                    OutT *yrow = nullptr;
+                    uint8_t *srow = nullptr;
+                    if constexpr (f6_q16<OutT>) {
+                        const int64_t r = (int64_t)r0 + 64 * q + 32 * i + lane / LPR;
+                        yrow = out + r * ldo + c0 + 4 * (lane % LPR);
+                        srow = osc + r * (ldo / 32) + (c0 + 4 * (lane % LPR)) / 32;
+                    }
+#pragma unroll
+                    for (int it = 0; it < 32 / RPI; it++) {
+                        const int r = RPI * it + lane / LPR, seg = lane % LPR;
+                        const u32x4 val = *(const u32x4 *)(stg + r * PITCH + 16 * seg);
+                        const int rl = 64 * q + 32 * i + r;
+                        if constexpr (f6_q16<OutT>) {
+                            // columns c0 + 4 seg .. + 3; the 8 lanes with equal
+                            // lane / 8 hold one 32-column block. Magnitudes are
+                            // compared as bit patterns (non-negative floats
+                            // order as their bits)
+                            uint32_t mb = 0;
+#pragma unroll
+                            for (int c = 0; c < 4; c++) mb = max(mb, val[c] & 0x7fffffffu);
+                            // max over the 8 lanes: swap neighbours, then pairs
+                            // (quad_perm 1,0,3,2 and 2,3,0,1), then mirror the
+                            // 8-lane half row (lane i and 7 - i): DPP moves on
+                            // the vector unit, no LDS round trip
+                            mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, false));
+                            mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, false));
+                            mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x141, 0xF, 0xF, false));
+                            // e: the block's largest biased exponent (at most
+                            // 252: larger blocks saturate); x 2^(126 - e) lies
+                            // in (-1, 1), and v_cvt_pknorm_i16_f32 rounds its
+                            // 32767 multiple to an integer, two values a step
+                            const int code = min((int)(mb >> 23), 252);
+                            const float inv = __uint_as_float((uint32_t)(253 - code) << 23);
+                            if (col_on && rl < mrows) {
+                                float x[4];
+#pragma unroll
+                                for (int c = 0; c < 4; c++) x[c] = __uint_as_float(val[c]) * inv;
+                                const u32x2 pk = {
+                                    (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[0], x[1])),
+                                    (uint32_t)__builtin_bit_cast(int, __builtin_amdgcn_cvt_pknorm_i16(x[2], x[3]))};
+                                __builtin_nontemporal_store(pk, (u32x2 *)(yrow + (int64_t)it * RPI * ldo));
+                                if ((seg & 7) == 0)
+                                    srow[(int64_t)it * RPI * (ldo / 32)] = (uint8_t)code;
+                            }
+                        } else if (col_on && rl < mrows) {
+                            u32x4 *dst = (u32x4 *)((uint8_t *)(out + (int64_t)(r0 + rl) * ldo + c0) +
+                                                   16 * seg);
+                            if constexpr (!GLU && sizeof(OutT) == 4) __builtin_nontemporal_store(val, dst);
+                            else *dst = val;
+                        }
                     }
                 }
-            }
             }
         }
     };
